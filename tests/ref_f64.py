@@ -1,0 +1,118 @@
+"""Independent float64 formulations used to pin the oracle (tests only).
+
+Nothing here shares code with the oracle or with the GPU library.  Each helper
+is a *different* formulation of something the method reduces to:
+
+* RoPE as multiplication of the complex numbers x_j + i x_{j+d/2} by
+  e^{i pos theta_j} (the rotate-half form written as complex arithmetic);
+* dense causal attention (the textbook routine the method must reduce to when
+  every node is selected);
+* the entry set E written as a predicate over *all* nodes ("a node is a
+  candidate iff it is a top node, an orphan, or a child of a selected
+  candidate"), not as the oracle's level-by-level candidate lists;
+* the shared softmax evaluated in float64 over that entry set.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def thetas(d: int, base: float) -> np.ndarray:
+    return base ** (-2.0 * np.arange(d // 2) / d)
+
+
+def rope_c(x: np.ndarray, pos, base: float = 10000.0) -> np.ndarray:
+    """RoPE via complex multiplication; x [..., d], pos broadcastable to x[..., 0]."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    ang = np.asarray(pos, np.float64)[..., None] * thetas(d, base)
+    z = z * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def dense_causal(q: np.ndarray, K: np.ndarray, V: np.ndarray, qpos: int, base=10000.0):
+    """Textbook attention of q [G, d] at absolute position qpos over tokens 0..qpos."""
+    n = qpos + 1
+    qr = rope_c(q, qpos, base)
+    kr = rope_c(K[:n], np.arange(n), base)
+    z = qr @ kr.T / np.sqrt(q.shape[-1])
+    w = np.exp(z - z.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ np.asarray(V[:n], np.float64)
+
+
+def level_counts(L: int, b: int, levels: int) -> list[int]:
+    n = [L]
+    for _ in range(levels):
+        n.append(n[-1] // b)
+    return n
+
+
+def candidates_by_predicate(L: int, b: int, levels: int, sel: list[set]):
+    """Candidate sets per level from the node predicate.
+
+    sel[l] = set of selected node ids at level l (l = 1..levels; sel[0] unused).
+    A level-l node x is a candidate iff l is the top level, or x has no full
+    parent (x >= b * n_{l+1}), or its parent is a candidate and selected.
+    Returns {l: sorted list of candidate ids}.
+    """
+    n = level_counts(L, b, levels)
+    memo = {}
+
+    def is_cand(l: int, x: int) -> bool:
+        key = (l, x)
+        if key in memo:
+            return memo[key]
+        if l == levels or x >= b * n[l + 1]:
+            r = True
+        else:
+            par = x // b
+            r = is_cand(l + 1, par) and par in sel[l + 1]
+        memo[key] = r
+        return r
+
+    return {l: [x for x in range(n[l]) if is_cand(l, x)] for l in range(levels + 1)}
+
+
+def entries_from_candidates(cands: dict, sel: list[set], levels: int):
+    """Entry list (level, node, position) implied by the candidate sets."""
+    ent = []
+    for l in range(levels, 0, -1):
+        for pos, x in enumerate(cands[l]):
+            if x not in sel[l]:
+                ent.append((l, x, pos))
+    for pos, x in enumerate(cands[0]):
+        ent.append((0, x, pos))
+    return ent
+
+
+def covered_tokens(level: int, node: int, b: int) -> range:
+    span = b ** level
+    return range(node * span, (node + 1) * span)
+
+
+def group_scores_f64(q: np.ndarray, keys: np.ndarray, qpos: int, base: float):
+    """Per-head logits [G, m, R] and group scores (max over R of the head mean).
+
+    keys [m, R, d] un-rotated; candidate i at position i, query at qpos.
+    """
+    d = q.shape[-1]
+    qr = rope_c(q, qpos, base)                                         # [G, d]
+    m = keys.shape[0]
+    kr = rope_c(keys, np.arange(m)[:, None], base)                     # [m, R, d]
+    z = np.einsum("gd,mrd->gmr", qr, kr) / np.sqrt(d)
+    gm = z.mean(axis=0)                                                # [m, R]
+    jstar = gm.argmax(axis=1)
+    s = gm[np.arange(m), jstar]
+    zsel = z[:, np.arange(m), jstar]                                   # [G, m]
+    return s, zsel
+
+
+def softmax_over_entries(zs: np.ndarray, vals: np.ndarray):
+    """zs [G, E] logits, vals [E, d] -> out [G, d], lse [G] in float64."""
+    M = zs.max(axis=1, keepdims=True)
+    w = np.exp(zs - M)
+    den = w.sum(axis=1, keepdims=True)
+    return (w @ vals) / den, (M + np.log(den))[:, 0]

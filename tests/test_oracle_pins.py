@@ -1,0 +1,426 @@
+"""Pins of the CPU oracle against facts the pages and mathematics fix.
+
+Each test names the pin it implements:
+  P1 every node selected  -> dense causal attention (textbook routine)
+  P2 mean-pooled values    -> subtree means (closed form)
+  P3 pooler closed forms   -> r = 0 gives the child mean, permutation invariance,
+                              a dominant reference gives its argmax child,
+                              equal children give that child
+  P4 selection certificate -> brute force over all subsets / top-p mass rules
+  P5 entries partition the visible tokens
+  P6 entries read          -> exact count formula, linear in log_b L
+  P7 exhaustive small trees (64 tokens) against the node-predicate formulation
+     of E and a float64 softmax over it
+  P9 prefill with T = 1 is decode; prefill over an empty prefix is causal attention
+  P10 R equal references equal R = 1; top-p with cap 1 equals top-1
+  bf16 node rounding matches torch's round-to-nearest-even
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import hti_workloads as W
+from ref_f64 import (candidates_by_predicate, covered_tokens, dense_causal,
+                     entries_from_candidates, group_scores_f64, level_counts, rope_c,
+                     softmax_over_entries)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16r(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def rand_kv(L, d, seed, bf16=False):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((L, d)).astype(np.float32)
+    V = rng.standard_normal((L, d)).astype(np.float32)
+    if bf16:
+        K, V = bf16r(K), bf16r(V)
+    return K, V, rng
+
+
+def sel_sets(res, levels):
+    s = [set() for _ in range(levels + 1)]
+    for l in range(1, levels + 1):
+        s[l] = {int(x) for x in res["sel"][l - 1] if x >= 0}
+    return s
+
+
+def eval_f64(tree, K, V, q, sel, *, base=10000.0, t=-1, blk_k=None, blk_v=None):
+    """Shared softmax in float64 over the entry set implied by `sel`."""
+    L, b, lv = tree.L, tree.b, tree.levels
+    cands = candidates_by_predicate(L, b, lv, sel)
+    zs, vals = [], []
+    for l in range(lv, 0, -1):
+        C = cands[l]
+        uns = [i for i, x in enumerate(C) if x not in sel[l]]
+        if not uns:
+            continue
+        _, z = group_scores_f64(q, tree.lk[l - 1][C], len(C), base)
+        zs.append(z[:, uns])
+        vals.append(tree.lv[l - 1][[C[i] for i in uns]].astype(np.float64))
+    C0 = list(cands[0])
+    keys0 = K[C0].astype(np.float64)
+    vals0 = V[C0].astype(np.float64)
+    if t >= 0:
+        qp = len(C0) + t
+        keys0 = np.concatenate([keys0, blk_k[: t + 1]])
+        vals0 = np.concatenate([vals0, blk_v[: t + 1]])
+    else:
+        qp = sum(1 for x in C0 if x < L - 1)
+    kr = rope_c(keys0, np.arange(len(keys0)), base)
+    zs.append(rope_c(q, qp, base) @ kr.T / np.sqrt(q.shape[-1]))
+    vals.append(vals0)
+    return softmax_over_entries(np.concatenate(zs, axis=1), np.concatenate(vals))
+
+
+# --------------------------------------------------------------------------- golden
+def test_level_counts_golden():
+    g = json.load(open(os.path.join(GOLDEN, "level_counts.json")))
+    for name, e in g.items():
+        if name.startswith("_"):
+            continue
+        w = W.WORKLOADS[name]
+        assert (w.L, w.b, w.levels) == (e["L"], e["b"], e["levels"])
+        assert w.level_counts() == e["counts"]
+        # the oracle sizes its level arrays with the same rule (tiny tree per
+        # workload geometry: scale the count list by the first level)
+        tr = oracle.Tree(e["L"], 1, e["b"], e["levels"], 1, False)
+        assert [x.shape[0] for x in tr.lk] == e["counts"][1:]
+
+
+# --------------------------------------------------------------------------- P1
+@pytest.mark.parametrize("mode", ["topk", "topp"])
+def test_dense_equivalence_tiny_workload(mode):
+    """P1 on the tiny-decode geometry.  With a per-level budget, every token is
+    reached exactly when each level keeps all of its candidates; the largest
+    candidate list is level 1 (n_1 = 256 nodes), so k = 256 (or top-p with
+    p = 1 and cap = 256)."""
+    w = W.TINY
+    K, V = W.gen_kv(w, Lcap=w.L)
+    refs = W.gen_refs(w)
+    q = W.gen_queries(w)
+    K0, V0 = K[0, 0].numpy(), V[0, 0].numpy()
+    tr = oracle.build_tree(K0, V0, refs[0], w.b, w.levels, bf16=False)
+    for qi in (0, 7, 15):
+        qq = q[0, qi].numpy()                      # [Hq=1, d]
+        if mode == "topk":
+            r = oracle.query(tr, K0, V0, qq, k=256)
+        else:
+            r = oracle.query(tr, K0, V0, qq, mode="topp", p=1.0, cap=256)
+        ref = dense_causal(qq, K0, V0, w.L - 1)
+        assert np.abs(r["out"] - ref).max() < 1e-5
+        # top-p still scores every summary level (16 + 256 keys) before keeping all
+        scored = 0 if mode == "topk" else 16 + 256
+        assert r["counts"][0] == w.L + scored and r["counts"][1] == w.L
+
+
+@pytest.mark.parametrize("L,b,levels,R,G,d", [(700, 4, 3, 2, 4, 32), (1000, 8, 2, 1, 2, 128),
+                                             (257, 2, 6, 3, 1, 16)])
+def test_dense_equivalence_bf16_gqa(L, b, levels, R, G, d):
+    K, V, rng = rand_kv(L, d, seed=L, bf16=True)
+    refs = (rng.standard_normal((R, d)) / np.sqrt(d)).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, levels, bf16=True)
+    q = bf16r(rng.standard_normal((G, d)))
+    r = oracle.query(tr, K, V, q, k=L // b)      # n_1 = largest candidate list
+    ref = dense_causal(q, K, V, L - 1)
+    assert np.abs(r["out"] - ref).max() < 1e-5
+
+
+# --------------------------------------------------------------------------- P2
+@pytest.mark.parametrize("bf16", [False, True])
+def test_values_are_subtree_means(bf16):
+    L, d, b, levels = 4096 + 77, 64, 4, 5
+    K, V, rng = rand_kv(L, d, seed=3, bf16=bf16)
+    refs = (rng.standard_normal((2, d)) / 8).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, levels, bf16=bf16)
+    for l in range(1, levels + 1):
+        n = L // b ** l
+        span = b ** l
+        means = V[: n * span].astype(np.float64).reshape(n, span, d).mean(axis=1)
+        err = np.abs(tr.lv[l - 1] - means).max()
+        # fp32: sequential sums of <= b terms per level; bf16: one rounding of
+        # at most half an ulp (2^-9 relative) per level on values |mean| <= 4
+        bound = 2e-6 * l if not bf16 else l * 2.0 ** -9 * 4.0
+        assert err < bound, (l, err, bound)
+
+
+# --------------------------------------------------------------------------- P3
+def test_pooler_closed_forms():
+    L, d, b, levels = 512, 32, 8, 3
+    K, V, rng = rand_kv(L, d, seed=5)
+    # r = 0: every weight is 1/b -> pooled key = child mean (recursively: subtree mean)
+    tr0 = oracle.build_tree(K, V, np.zeros((1, d), np.float32), b, levels, bf16=False)
+    for l in range(1, levels + 1):
+        n, span = L // b ** l, b ** l
+        means = K[: n * span].astype(np.float64).reshape(n, span, d).mean(axis=1)
+        assert np.abs(tr0.lk[l - 1][:, 0] - means).max() < 2e-6 * l
+
+    # equal children: pooling a node whose children all equal u returns u
+    u = rng.standard_normal(d).astype(np.float32)
+    Ku = np.tile(u, (L, 1))
+    refs = rng.standard_normal((2, d)).astype(np.float32)
+    tru = oracle.build_tree(Ku, V, refs, b, levels, bf16=False)
+    for l in range(levels):
+        assert np.abs(tru.lk[l] - u).max() < 4e-6 * np.abs(u).max()
+
+    # permutation of a node's children leaves its pooled key unchanged (up to
+    # the order of the fp32 sums)
+    r1 = rng.standard_normal((1, d)).astype(np.float32)
+    ta = oracle.build_tree(K, V, r1, b, 1, bf16=False)
+    perm = np.concatenate([np.random.default_rng(1).permutation(b) + i * b for i in range(L // b)])
+    tb = oracle.build_tree(K[perm], V[perm], r1, b, 1, bf16=False)
+    assert np.abs(ta.lk[0] - tb.lk[0]).max() < 1e-5
+    assert np.abs(ta.lv[0] - tb.lv[0]).max() < 1e-5
+
+    # dominant reference: r = lam * k_c* with k_c* the child of largest norm ->
+    # the pooled key is k_c* (softmax saturates)
+    Kd = K.copy()
+    Kd[3] *= 6.0                                   # child 3 of node 0 dominates
+    rd = (60.0 * Kd[3] / np.linalg.norm(Kd[3]) ** 2 * np.sqrt(d)).astype(np.float32)[None]
+    td = oracle.build_tree(Kd, V, rd, b, 1, bf16=False)
+    assert np.abs(td.lk[0][0, 0] - Kd[3]).max() < 1e-4 * np.abs(Kd[3]).max()
+
+
+def test_bf16_node_rounding_is_rne():
+    """b = 2 mean (a + b) / 2 in fp32 then rounded: equals torch's RNE bf16 cast."""
+    rng = np.random.default_rng(11)
+    L, d = 4096, 64
+    V = bf16r(rng.standard_normal((L, d)))
+    K = bf16r(rng.standard_normal((L, d)))
+    tr = oracle.build_tree(K, V, np.zeros((1, d), np.float32), 2, 1, bf16=True)
+    v32 = (torch.from_numpy(V[0::2]) + torch.from_numpy(V[1::2])) / 2.0
+    expect = v32.to(torch.bfloat16).float().numpy()
+    assert np.array_equal(tr.lv[0], expect)
+
+
+# --------------------------------------------------------------------------- P4
+def _check_certificate(s, selected_pos, mode, k, p, cap, tol=2e-5):
+    m = len(s)
+    S = sorted(selected_pos)
+    rest = [i for i in range(m) if i not in set(S)]
+    if mode == "topk":
+        assert len(S) == min(k, m)
+    else:
+        assert 1 <= len(S) <= min(cap, m)
+    if rest and S:
+        assert min(s[i] for i in S) >= max(s[i] for i in rest) - tol
+    if mode == "topk" and m <= 10 and len(S) < m:
+        # brute force: no subset of the same size has a larger total score
+        best = max(sum(s[i] for i in c) for c in itertools.combinations(range(m), len(S)))
+        assert sum(s[i] for i in S) >= best - tol * len(S)
+    if mode == "topp" and len(S) < min(cap, m):
+        pi = np.exp(s - s.max())
+        pi /= pi.sum()
+        mass = pi[S].sum()
+        assert mass >= p - 1e-5
+        assert mass - pi[S].min() < p + 1e-5
+
+
+# --------------------------------------------------------------------------- P6
+@pytest.mark.parametrize("b,k,max_levels", [(2, 1, 20), (4, 2, 10), (16, 4, 5)])
+def test_entries_read_grow_linearly_in_log_L(b, k, max_levels):
+    """L = b^levels (one top node, no orphans): keys and values read follow the
+    closed form and grow by a constant per level, i.e. O(log L)."""
+    d = 8
+    prev = None
+    incs = []
+    for lv in range(2, max_levels + 1):
+        L = b ** lv
+        if L > 1 << 20:
+            break
+        K, V, rng = rand_kv(L, d, seed=lv)
+        refs = (rng.standard_normal((1, d)) / 3).astype(np.float32)
+        tr = oracle.build_tree(K, V, refs, b, lv, bf16=False)
+        q = rng.standard_normal((1, d)).astype(np.float32)
+        r = oracle.query(tr, K, V, q, k=k)
+        keys = b + (lv - 2) * k * b + k * b
+        vals = (b - k) + (lv - 2) * (k * b - k) + k * b
+        assert tuple(r["counts"]) == (keys, vals), (lv, r["counts"], keys, vals)
+        tot = keys + vals
+        if prev is not None:
+            incs.append(tot - prev)
+        prev = tot
+    assert len(set(incs)) == 1 and incs[0] == 2 * k * b - k
+
+
+# --------------------------------------------------------------------------- P7
+def _sweep_cases():
+    """Every (L <= 64, b, levels) geometry, four cases each, rotating the
+    selection rule, R, G, the prefill block length and the seed through
+    decorrelated counters so every value of every knob is hit many times."""
+    cases = []
+    sel_variants = {}
+    for b in (2, 4, 8, 16, 32, 64):
+        v = [("topk", k, 1.0, 0) for k in sorted({1, 2, b - 1, b, b + 1} - {0})]
+        v += [("topp", 0, p, cap) for p in (0.1, 0.5, 0.9, 1.0) for cap in sorted({1, 2, b})]
+        sel_variants[b] = v
+    i = 0
+    for L in range(1, 65):
+        for b in (2, 4, 8, 16, 32, 64):
+            maxlv = 0
+            while b ** (maxlv + 1) <= 64:
+                maxlv += 1
+            for lv in range(0, maxlv + 2):
+                variants = sel_variants[b]
+                for j in range(4):
+                    sv = variants[(i * 5 + j) % len(variants)]
+                    R = 1 + (i // 3 + j) % 2
+                    G = 1 + (i // 7 + j // 2) % 2
+                    T = (0, 1, 3, 8)[(i // 11 + j) % 4]        # 0 = decode
+                    cases.append((L, b, lv, sv, R, G, T, i))
+                    i += 1
+    return cases
+
+
+_CASES = _sweep_cases()
+
+
+@pytest.mark.parametrize("chunk", range(8))
+def test_exhaustive_64_token_trees(chunk):
+    """P4 + P5 + P6 + P7 over every 64-token-or-smaller tree geometry, decode
+    and prefill (blocks of 1, 3 and 8 tokens after the 64-token prefix)."""
+    d = 8
+    for (L, b, lv, (mode, k, p, cap), R, G, T, seed) in _CASES[chunk::8]:
+        K, V, rng = rand_kv(L + T, d, seed=seed)
+        refs = (rng.standard_normal((R, d)) / np.sqrt(d)).astype(np.float32)
+        tr = oracle.build_tree(K, V, refs, b, lv, bf16=False, L=L)
+        q = rng.standard_normal((G, d)).astype(np.float32)
+        kmax = k if mode == "topk" else cap
+        for t in (range(T) if T else [-1]):
+            blk = dict(t=t, blk_k=K[L:], blk_v=V[L:]) if T else {}
+            r = oracle.query(tr, K[:L], V[:L], q, mode=mode, k=k, p=p, cap=cap, kmax=kmax,
+                             entries=True, **blk)
+            sel = sel_sets(r, lv)
+            cands = candidates_by_predicate(L, b, lv, sel)
+            # P7: entry list equals the node-predicate formulation
+            ent = entries_from_candidates(cands, sel, lv)
+            nblk = t + 1 if T else 0
+            ent += [(0, L + j, len(cands[0]) + j) for j in range(nblk)]
+            got = list(zip(*[x.tolist() for x in r["entries"]]))
+            assert got == ent, (L, b, lv, mode, k, p, cap, T, t)
+            # P5: entries partition the visible tokens [0, L + nblk)
+            cover = np.zeros(L + nblk, np.int64)
+            for (l, x, _) in ent:
+                for tkn in covered_tokens(l, x, b):
+                    cover[tkn] += 1
+            assert (cover == 1).all()
+            # P4: per-level certificate on float64 scores
+            thr = k if mode == "topk" else 1
+            nkeys = 0
+            for l in range(lv, 0, -1):
+                C = cands[l]
+                if len(C) <= thr:
+                    assert sel[l] == set(C)
+                    continue
+                nkeys += len(C) * R
+                s, _ = group_scores_f64(q, tr.lk[l - 1][C], len(C), 10000.0)
+                pos = [i for i, x in enumerate(C) if x in sel[l]]
+                _check_certificate(s, pos, mode, k, p, cap)
+            # P6: counters
+            nvals = sum(len(cands[l]) - len(sel[l] & set(cands[l])) for l in range(1, lv + 1))
+            n0 = len(cands[0]) + nblk
+            assert tuple(r["counts"]) == (nkeys + n0, nvals + n0)
+            # P7: output equals a float64 softmax over E
+            kw = dict(t=t, blk_k=K[L:].astype(np.float64), blk_v=V[L:].astype(np.float64)) if T else {}
+            out, lse = eval_f64(tr, K, V, q, sel, **kw)
+            assert np.abs(r["out"] - out).max() < 2e-5
+            assert np.abs(r["lse"] - lse).max() < 2e-5
+
+
+# --------------------------------------------------------------------------- P9
+@pytest.mark.parametrize("P0,b,levels", [(300, 4, 3), (1000, 8, 2), (76, 2, 5)])
+def test_prefill_T1_equals_decode(P0, b, levels):
+    assert (P0 + 1) % b != 0
+    d, G = 16, 2
+    K, V, rng = rand_kv(P0 + 1, d, seed=P0)
+    refs = (rng.standard_normal((1, d)) / 4).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    tdec = oracle.build_tree(K, V, refs, b, levels, bf16=False, L=P0 + 1)
+    tpre = oracle.build_tree(K, V, refs, b, levels, bf16=False, L=P0)
+    for k in (1, 3):
+        rd = oracle.query(tdec, K, V, q, k=k)
+        rp = oracle.query(tpre, K, V, q, k=k, t=0, blk_k=K[P0:P0 + 1], blk_v=V[P0:P0 + 1])
+        assert np.array_equal(rd["sel"], rp["sel"])
+        assert np.abs(rd["out"] - rp["out"]).max() < 1e-6
+
+
+def test_prefill_empty_prefix_is_causal_attention():
+    d, G, T = 32, 4, 40
+    rng = np.random.default_rng(9)
+    bk = rng.standard_normal((T, d)).astype(np.float32)
+    bv = rng.standard_normal((T, d)).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    empty = np.zeros((0, d), np.float32)
+    tr = oracle.build_tree(empty, empty, np.zeros((1, d), np.float32), 4, 2, bf16=False)
+    for t in (0, 5, T - 1):
+        r = oracle.query(tr, empty, empty, q, k=2, t=t, blk_k=bk, blk_v=bv)
+        ref = dense_causal(q, bk, bv, t)
+        assert np.abs(r["out"] - ref).max() < 1e-5
+
+
+def test_prefill_matches_f64_entry_softmax():
+    """Prefill over a real prefix: output equals the float64 softmax over E."""
+    P0, T, d, G, b, lv = 2000, 24, 16, 4, 8, 3
+    K, V, rng = rand_kv(P0 + T, d, seed=21)
+    refs = (rng.standard_normal((2, d)) / 4).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, lv, bf16=False, L=P0)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    for t in (0, 11, T - 1):
+        r = oracle.query(tr, K, V, q, k=2, t=t, blk_k=K[P0:], blk_v=V[P0:])
+        out, lse = eval_f64(tr, K, V, q, sel_sets(r, lv), t=t,
+                            blk_k=K[P0:].astype(np.float64), blk_v=V[P0:].astype(np.float64))
+        assert np.abs(r["out"] - out).max() < 2e-5
+
+
+# --------------------------------------------------------------------------- P10
+def test_special_cases():
+    L, d, b, lv, G = 3000, 32, 8, 3, 2
+    K, V, rng = rand_kv(L, d, seed=4)
+    r1 = (rng.standard_normal((1, d)) / 4).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    ta = oracle.build_tree(K, V, r1, b, lv, bf16=False)
+    tb = oracle.build_tree(K, V, np.repeat(r1, 3, axis=0), b, lv, bf16=False)
+    ra = oracle.query(ta, K, V, q, k=3)
+    rb = oracle.query(tb, K, V, q, k=3)
+    assert np.array_equal(ra["out"], rb["out"]) and np.array_equal(ra["sel"], rb["sel"])
+    # top-p with cap 1 is top-1
+    rp = oracle.query(ta, K, V, q, mode="topp", p=0.5, cap=1, kmax=1)
+    rk = oracle.query(ta, K, V, q, k=1, kmax=1)
+    assert np.array_equal(rp["out"], rk["out"]) and np.array_equal(rp["sel"], rk["sel"])
+
+
+def test_replay():
+    """Replaying the oracle's own selection reproduces it; replaying another
+    selection equals the float64 evaluation under that selection."""
+    L, d, b, lv, G = 5000, 16, 8, 3, 2
+    K, V, rng = rand_kv(L, d, seed=8)
+    refs = (rng.standard_normal((1, d)) / 4).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, lv, bf16=False)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    r = oracle.query(tr, K, V, q, k=2)
+    rr = oracle.query(tr, K, V, q, k=2, replay=r["sel"])
+    assert np.array_equal(r["out"], rr["out"])
+    # swap the top-level choice for another node
+    alt = r["sel"].copy()
+    ntop = L // b ** lv
+    other = [x for x in range(ntop) if x not in set(alt[lv - 1])][0]
+    alt[lv - 1] = sorted([alt[lv - 1][0], other])
+    cand = sorted(alt[lv - 1])
+    # descend under the new top choice: pick the first two children each level
+    nxt = [c * b for c in cand]
+    alt[lv - 2] = sorted(nxt[:2])
+    alt[lv - 3] = sorted([alt[lv - 2][0] * b, alt[lv - 2][1] * b])
+    ra = oracle.query(tr, K, V, q, k=2, replay=alt)
+    out, _ = eval_f64(tr, K, V, q, sel_sets({"sel": alt}, lv))
+    assert np.abs(ra["out"] - out).max() < 2e-5
+    with pytest.raises(ValueError):
+        bad = alt.copy()
+        bad[0] = [L // b + 5, -1]          # not a candidate
+        oracle.query(tr, K, V, q, k=2, replay=bad)

@@ -1,0 +1,258 @@
+"""Benchmark of the tree-indexed sparse attention hot path on one MI355X.
+
+Headline (value): decode queries/s at 1,048,576 context, batch 4, where one
+step = tree_append of one token per sequence + sparse_decode of one query per
+sequence (32 query heads over 8 KV heads, d 128, bf16, b 32, 4 levels, top-k 8),
+steps issued back to back on one stream.  Reported beside it: achieved HBM
+GB/s of the decode traversal kernel (algorithmic bytes / kernel time) and the
+prefill throughput (tokens/s) of an 8192-token block over a 524,288-token
+prefix including tree_build of the prefix.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import hierarchical_tree_indexed_amd as hti  # noqa: E402
+import hti_workloads as W  # noqa: E402
+
+METRIC = "decode queries/s + achieved HBM GB/s at 1M ctx; prefill tokens/s at 524K"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+DEV = "cuda"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gen_kv_device(w, Lcap):
+    """Seeded N(0,1) caches drawn on the device, one (sequence, head) at a time."""
+    dt = W.TORCH_DTYPE[w.dtype]
+    K = torch.zeros((w.B, w.Hkv, Lcap, w.d), dtype=dt, device=DEV)
+    V = torch.zeros_like(K)
+    g = torch.Generator(device=DEV)
+    for bi in range(w.B):
+        for h in range(w.Hkv):
+            g.manual_seed(1_000_003 * (w.seed + 1) + 4096 * bi + h)
+            K[bi, h, : w.L] = torch.randn((w.L, w.d), generator=g, device=DEV).to(dt)
+            V[bi, h, : w.L] = torch.randn((w.L, w.d), generator=g, device=DEV).to(dt)
+    return K, V
+
+
+def treeset(w, Lcap, K, V, T=0):
+    sel = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap)
+    cfg = hti.make_cfg(w.B, w.Hq, w.Hkv, w.d, w.b, w.levels, w.R, w.dtype, Lcap, w.rope_base, 1)
+    cfg.rope_npos = hti.plan(cfg, sel, T).rope_npos_needed
+    ts = hti.TreeSet(cfg, device=DEV, k_cache=K, v_cache=V)
+    ts.ref_q.copy_(W.gen_refs(w))
+    ts.rope_init()
+    return ts, sel
+
+
+def decode_unit_bytes(w, L):
+    """Algorithmic bytes one (query, KV group) unit must touch at length L:
+    scored keys (x R) + unselected summary values + token keys and values,
+    plus its query and output rows.  Entry = d elements of the cache dtype."""
+    n = w.level_counts(L)
+    keff = w.k if w.mode == "topk" else w.cap
+    thr = w.k if w.mode == "topk" else 1
+    keys = vals = 0
+    m = n[w.levels]
+    for lvl in range(w.levels, 0, -1):
+        if m > thr:
+            nsel = min(keff, m)
+            keys += m * w.R
+            vals += m - nsel
+        else:
+            nsel = m
+        m = nsel * w.b + (n[lvl - 1] - w.b * n[lvl])
+    keys += m
+    vals += m
+    e = w.d * w.elem_bytes
+    return (keys + vals) * e + w.G * w.d * (w.elem_bytes + 4)
+
+
+def bench_decode(args):
+    w = W.DEC1M
+    S, Wm = args.steps, args.warmup
+    Lcap = w.L + Wm + S
+    log(f"[decode] generating {w.B}x{w.Hkv}x{w.L} bf16 K/V on the device")
+    K, V = gen_kv_device(w, Lcap)
+    q0 = W.gen_queries(w, 0, device=DEV)
+    W.plant_needles(w, K, q0)
+    ts, sel = treeset(w, Lcap, K, V)
+    ts.tree_build([w.L] * w.B)
+    torch.cuda.synchronize()
+    log("[decode] tree built")
+    dt = W.TORCH_DTYPE[w.dtype]
+    gq = torch.Generator(device=DEV)
+    gq.manual_seed(12345)
+    nstep = Wm + S
+    qs = torch.randn((nstep, w.B, 1, w.Hq, w.d), generator=gq, device=DEV).to(dt)
+    ak = torch.randn((nstep, w.B, w.Hkv, w.d), generator=gq, device=DEV).to(dt)
+    av = torch.randn((nstep, w.B, w.Hkv, w.d), generator=gq, device=DEV).to(dt)
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, 1, w.Hq), dtype=torch.float32, device=DEV)
+
+    def step(s):
+        ts.tree_append(ak[s], av[s])
+        ts.sparse_decode(sel, qs[s], out, lse)
+
+    for s in range(Wm):
+        step(s)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(S):
+        ts.tree_append(ak[Wm + s], av[Wm + s])
+        ev[s][0].record()
+        ts.sparse_decode(sel, qs[Wm + s], out, lse)
+        ev[s][1].record()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / S
+    bytes_per_launch = sum(decode_unit_bytes(w, w.L + Wm + s + 1) for s in range(S)) / S * w.B * w.Hkv
+    res = dict(ms_per_step=total_ms / S, wall_s=wall, decode_kernel_ms=dec_ms,
+               bytes_per_launch=bytes_per_launch,
+               qps=w.B * S / (total_ms / 1e3),
+               gbs=bytes_per_launch / (dec_ms / 1e3) / 1e9)
+    log(f"[decode] {res}")
+    del K, V, ts
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(args):
+    w = W.PREFILL
+    log(f"[prefill] generating prefix {w.L} and block {w.T}")
+    K, V = gen_kv_device(w, w.L)
+    qb, kb, vb = W.gen_block(w, device=DEV)
+    ts, sel = treeset(w, w.L, K, V, T=w.T)
+    ws = torch.empty(ts.prefill_workspace_bytes(sel, w.T), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, w.T, w.Hq), dtype=torch.float32, device=DEV)
+
+    def run():
+        ts.tree_build([w.L] * w.B)
+        ts.sparse_prefill(sel, qb, kb, vb, out, ws, lse)
+
+    for _ in range(args.prefill_warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.prefill_reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.prefill_reps
+    pairs = w.T * (w.T + 1) // 2
+    inblock_flop = pairs * w.Hq * 4 * w.d
+    res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9)
+    log(f"[prefill] {res}")
+    del K, V, ts, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args):
+    """The oracle, as it stands, on a bounded sample of the decode workload."""
+    import numpy as np
+
+    import oracle
+    w = W.DEC1M
+    groups = (0, 1)
+    nq = 4
+    log("[cpu] building oracle trees for 2 KV heads of one 1M-token sequence (untimed)")
+    K, V = gen_kv_device(w.replace(B=1), w.L)
+    refs = W.gen_refs(w)
+    trees = {}
+    data = {}
+    for g in groups:
+        Kh = K[0, g].float().cpu().numpy()
+        Vh = V[0, g].float().cpu().numpy()
+        trees[g] = oracle.build_tree(Kh, Vh, refs[g], w.b, w.levels, bf16=True)
+        data[g] = (Kh, Vh)
+    del K, V
+    qs = torch.randn((nq, w.Hq, w.d)).to(torch.bfloat16).float().numpy()
+    t0 = time.perf_counter()
+    for i in range(nq):
+        for g in groups:
+            oracle.query(trees[g], data[g][0], data[g][1], qs[i, g * w.G:(g + 1) * w.G], k=w.k)
+    el = time.perf_counter() - t0
+    per_query = el / nq * (w.Hkv / len(groups))       # all 8 groups of one query
+    return dict(value=1.0 / per_query, unit="queries/s", cores=1, kind="oracle",
+                sample=f"{nq} decode queries x {len(groups)} of {w.Hkv} KV groups of one "
+                       f"1,048,576-token sequence, time scaled x{w.Hkv // len(groups)} to all "
+                       f"groups; tree build untimed; single thread")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--prefill-warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "all"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the method's sequences and KV heads are independent "
+              "and this build runs on a single MI355X; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    hti.lib()
+    dec = bench_decode(args) if args.only in ("decode", "all") else None
+    pre = bench_prefill(args) if args.only in ("prefill", "all") else None
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args)
+    w = W.DEC1M
+    line = {
+        "metric": METRIC,
+        "value": dec["qps"] if dec else None,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"] if dec else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "context": w.L, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "d": w.d, "b": w.b, "levels": w.levels, "k": w.k,
+                   "step": "tree_append + sparse_decode",
+                   "prefill_workload": W.PREFILL.name},
+        "hbm_gbs": dec["gbs"] if dec else None,
+        "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
+        "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
+        "roofline": ({"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": dec["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                      "kernel": "k_traverse (decode)",
+                      "kernel_ms": dec["decode_kernel_ms"],
+                      "bytes_per_launch": dec["bytes_per_launch"]} if dec else None),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,389 @@
+// hti_api.hip -- the C ABI: argument validation, buffer plan, launches.
+// Every check happens on the host before anything is enqueued; on error the
+// device state is untouched and hti_last_error() holds the reason.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hti_internal.h"
+
+using namespace hti;
+
+namespace {
+
+thread_local std::string g_err;
+
+hti_status fail(hti_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+hti_status ok()
+{
+    g_err.clear();
+    return HTI_OK;
+}
+
+hti_status check_cfg(const hti_tree_cfg *c)
+{
+    if (!c) return fail(HTI_ERR_INVALID_ARG, "cfg is NULL");
+    if (c->B < 1 || c->Hq < 1 || c->Hkv < 1) return fail(HTI_ERR_INVALID_ARG, "B, Hq, Hkv must be >= 1");
+    if (c->Hq % c->Hkv) return fail(HTI_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", c->Hq, c->Hkv);
+    const int G = c->Hq / c->Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(HTI_ERR_UNSUPPORTED, "group size Hq/Hkv = %d not in {1,2,4,8}", G);
+    if (c->Hkv > 16) return fail(HTI_ERR_UNSUPPORTED, "Hkv = %d > 16", c->Hkv);
+    if (c->d != 64 && c->d != 128) return fail(HTI_ERR_UNSUPPORTED, "head dim %d not in {64,128}", c->d);
+    if (c->b < 2 || c->b > 64) return fail(HTI_ERR_UNSUPPORTED, "branching factor %d not in [2,64]", c->b);
+    if (c->levels < 0 || c->levels > HTI_MAX_LEVELS)
+        return fail(HTI_ERR_INVALID_ARG, "levels %d not in [0,%d]", c->levels, HTI_MAX_LEVELS);
+    if (c->R < 1 || c->R > HTI_MAX_R) return fail(HTI_ERR_UNSUPPORTED, "R = %d not in [1,%d]", c->R, HTI_MAX_R);
+    if (c->dtype != HTI_F32 && c->dtype != HTI_BF16) return fail(HTI_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+    if (c->Lcap < 0 || c->Lcap >= (int64_t(1) << 31))
+        return fail(HTI_ERR_UNSUPPORTED, "Lcap %lld outside [0, 2^31)", (long long)c->Lcap);
+    if (!(c->rope_base > 0.f)) return fail(HTI_ERR_INVALID_ARG, "rope_base must be > 0");
+    if (c->rope_npos < 1) return fail(HTI_ERR_INVALID_ARG, "rope_npos must be >= 1");
+    return HTI_OK;
+}
+
+hti_status check_select(const hti_select *s)
+{
+    if (!s) return fail(HTI_ERR_INVALID_ARG, "select is NULL");
+    if (s->mode == HTI_TOPK) {
+        if (s->k < 1 || s->k > HTI_MAX_SELECT)
+            return fail(HTI_ERR_UNSUPPORTED, "k = %d not in [1,%d]", s->k, HTI_MAX_SELECT);
+    } else if (s->mode == HTI_TOPP) {
+        if (!(s->p > 0.f && s->p <= 1.f)) return fail(HTI_ERR_INVALID_ARG, "p must be in (0,1]");
+        if (s->cap < 1 || s->cap > HTI_MAX_SELECT)
+            return fail(HTI_ERR_UNSUPPORTED, "cap = %d not in [1,%d]", s->cap, HTI_MAX_SELECT);
+    } else {
+        return fail(HTI_ERR_INVALID_ARG, "unknown selection mode %d", s->mode);
+    }
+    return HTI_OK;
+}
+
+int sel_size(const hti_select *s) { return s->mode == HTI_TOPK ? s->k : s->cap; }
+
+void caps(const hti_tree_cfg *c, int64_t *ncap)
+{
+    ncap[0] = c->Lcap;
+    for (int l = 1; l <= HTI_MAX_LEVELS; ++l) ncap[l] = (l <= c->levels) ? ncap[l - 1] / c->b : 0;
+}
+
+// Largest candidate list per level for any length <= Lcap, and the largest
+// RoPE row a traversal can touch (T > 0: prefill block of T tokens).
+struct Bounds {
+    int64_t cand[HTI_MAX_LEVELS + 1];
+    int64_t max_summary;   // largest summary-level list
+    int64_t rope_rows;     // rows needed
+};
+
+Bounds bounds(const hti_tree_cfg *c, const hti_select *s, int32_t T)
+{
+    int64_t ncap[HTI_MAX_LEVELS + 1];
+    caps(c, ncap);
+    Bounds r{};
+    const int64_t keff = s ? sel_size(s) : 1;
+    const int Lv = c->levels;
+    r.max_summary = 0;
+    r.rope_rows = 1;
+    if (Lv == 0) {
+        r.cand[0] = ncap[0];
+    } else {
+        r.cand[Lv] = ncap[Lv];
+        for (int l = Lv - 1; l >= 0; --l) {
+            const int64_t kept = std::min(keff, r.cand[l + 1]);
+            r.cand[l] = std::min(ncap[l], kept * c->b + (c->b - 1));
+        }
+        for (int l = 1; l <= Lv; ++l) {
+            r.max_summary = std::max(r.max_summary, r.cand[l]);
+            r.rope_rows = std::max(r.rope_rows, r.cand[l] + 1);
+        }
+    }
+    // token level: decode query at <= |C_0|; prefill query at |C_0| + T - 1 and
+    // block-local positions < T
+    const int64_t tok = T > 0 ? r.cand[0] + T : r.cand[0] + 1;
+    r.rope_rows = std::max(r.rope_rows, tok);
+    if (T > 0) r.rope_rows = std::max<int64_t>(r.rope_rows, T);
+    return r;
+}
+
+TreeArgs tree_args(const hti_tree *tr)
+{
+    TreeArgs a{};
+    const hti_tree_cfg &c = tr->cfg;
+    a.kc = tr->k_cache;
+    a.vc = tr->v_cache;
+    for (int l = 0; l < HTI_MAX_LEVELS; ++l) {
+        a.lk[l] = tr->lvl_k[l];
+        a.lv[l] = tr->lvl_v[l];
+    }
+    caps(&c, a.ncap);
+    a.refs = tr->ref_q;
+    a.len = tr->len;
+    a.rope = reinterpret_cast<const float2 *>(tr->rope);
+    a.rope_npos = c.rope_npos;
+    a.B = c.B;
+    a.Hq = c.Hq;
+    a.Hkv = c.Hkv;
+    a.D = c.d;
+    a.b = c.b;
+    a.levels = c.levels;
+    a.R = c.R;
+    a.G = c.Hq / c.Hkv;
+    a.scale = 1.0f / sqrtf((float)c.d);
+    a.dtype = c.dtype;
+    return a;
+}
+
+hti_status check_tree(const hti_tree *tr, bool need_refs)
+{
+    if (!tr) return fail(HTI_ERR_INVALID_ARG, "tree is NULL");
+    hti_status st = check_cfg(&tr->cfg);
+    if (st) return st;
+    if (tr->cfg.Lcap > 0 && (!tr->k_cache || !tr->v_cache))
+        return fail(HTI_ERR_INVALID_ARG, "k_cache/v_cache is NULL");
+    if (!tr->len) return fail(HTI_ERR_INVALID_ARG, "len is NULL");
+    if (!tr->rope) return fail(HTI_ERR_INVALID_ARG, "rope is NULL");
+    int64_t ncap[HTI_MAX_LEVELS + 1];
+    caps(&tr->cfg, ncap);
+    for (int l = 0; l < tr->cfg.levels; ++l)   // a level with no capacity is never touched
+        if (ncap[l + 1] > 0 && (!tr->lvl_k[l] || !tr->lvl_v[l]))
+            return fail(HTI_ERR_INVALID_ARG, "level %d buffers are NULL", l + 1);
+    if (need_refs && !tr->ref_q) return fail(HTI_ERR_INVALID_ARG, "ref_q is NULL");
+    return HTI_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+hti_status launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(HTI_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+struct PrefillWs {
+    size_t part_acc, part_ml, qr, kr, total;
+};
+
+PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
+{
+    PrefillWs w{};
+    const size_t rows = (size_t)c->B * (size_t)T;
+    size_t off = 0;
+    w.part_acc = off;
+    off += align256(rows * c->Hq * c->d * sizeof(float));
+    w.part_ml = off;
+    off += align256(rows * c->Hq * 2 * sizeof(float));
+    w.qr = off;
+    off += align256(rows * c->Hq * c->d * 2);
+    w.kr = off;
+    off += align256(rows * c->Hkv * c->d * 2);
+    w.total = off;
+    return w;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *hti_last_error(void) { return g_err.c_str(); }
+
+hti_status hti_plan(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T, hti_plan_out *out)
+{
+    hti_status st = check_cfg(cfg);
+    if (st) return st;
+    if (!out) return fail(HTI_ERR_INVALID_ARG, "out is NULL");
+    if (sel && (st = check_select(sel))) return st;
+    if (T < 0) return fail(HTI_ERR_INVALID_ARG, "T < 0");
+    memset(out, 0, sizeof *out);
+    caps(cfg, out->ncap);
+    const size_t es = cfg->dtype == HTI_BF16 ? 2 : 4;
+    const size_t bh = (size_t)cfg->B * cfg->Hkv;
+    out->cache_bytes = bh * (size_t)cfg->Lcap * cfg->d * es;
+    for (int l = 1; l <= cfg->levels; ++l) {
+        out->lvl_k_bytes[l - 1] = bh * (size_t)out->ncap[l] * cfg->R * cfg->d * es;
+        out->lvl_v_bytes[l - 1] = bh * (size_t)out->ncap[l] * cfg->d * es;
+    }
+    out->rope_bytes = (size_t)cfg->rope_npos * cfg->d * sizeof(float);
+    const Bounds bd = bounds(cfg, sel, T);
+    out->rope_npos_needed = (int32_t)std::min<int64_t>(bd.rope_rows, INT32_MAX);
+    return ok();
+}
+
+hti_status hti_rope_init(const hti_tree *tree, void *stream)
+{
+    if (!tree) return fail(HTI_ERR_INVALID_ARG, "tree is NULL");
+    hti_status st = check_cfg(&tree->cfg);
+    if (st) return st;
+    if (!tree->rope) return fail(HTI_ERR_INVALID_ARG, "rope is NULL");
+    TreeArgs a = tree_args(tree);
+    return launched(launch_rope_init(a, (double)tree->cfg.rope_base, (hipStream_t)stream), "rope_init");
+}
+
+} // extern "C"
+
+namespace hti {
+__global__ void k_set_len(int64_t *len, int base, int n, int64_t v0, int64_t v1, int64_t v2, int64_t v3, int64_t v4, int64_t v5, int64_t v6,
+                          int64_t v7)
+{
+    const int i = threadIdx.x;
+    const int64_t v[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+    if (i < n) len[base + i] = v[i];
+}
+} // namespace hti
+
+extern "C" {
+
+hti_status hti_tree_build(const hti_tree *tree, const int64_t *L_host, void *stream)
+{
+    hti_status st = check_tree(tree, true);
+    if (st) return st;
+    if (!L_host) return fail(HTI_ERR_INVALID_ARG, "L_host is NULL");
+    const hti_tree_cfg &c = tree->cfg;
+    int64_t maxL = 0;
+    for (int s = 0; s < c.B; ++s) {
+        if (L_host[s] < 0 || L_host[s] > c.Lcap)
+            return fail(HTI_ERR_CAPACITY, "L_host[%d] = %lld outside [0, Lcap = %lld]", s,
+                        (long long)L_host[s], (long long)c.Lcap);
+        maxL = std::max(maxL, L_host[s]);
+    }
+    hipStream_t hs = (hipStream_t)stream;
+    // lengths travel as kernel arguments (no host buffer outlives the call)
+    for (int s0 = 0; s0 < c.B; s0 += 8) {
+        int64_t v[8] = {0};
+        const int n = std::min(8, c.B - s0);
+        for (int i = 0; i < n; ++i) v[i] = L_host[s0 + i];
+        hipLaunchKernelGGL(k_set_len, dim3(1), dim3(64), 0, hs, tree->len, s0, n, v[0], v[1],
+                           v[2], v[3], v[4], v[5], v[6], v[7]);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return launched(e, "tree_build(set_len)");
+    }
+    TreeArgs a = tree_args(tree);
+    int64_t n = maxL;
+    for (int l = 1; l <= c.levels; ++l) {
+        n /= c.b;
+        hipError_t e = launch_build_level(a, l, n, hs);
+        if (e != hipSuccess) return launched(e, "tree_build(level)");
+    }
+    return ok();
+}
+
+hti_status hti_tree_append(const hti_tree *tree, const void *k_new, const void *v_new, void *stream)
+{
+    hti_status st = check_tree(tree, true);
+    if (st) return st;
+    if (!k_new || !v_new) return fail(HTI_ERR_INVALID_ARG, "k_new/v_new is NULL");
+    TreeArgs a = tree_args(tree);
+    return launched(launch_append(a, k_new, v_new, (hipStream_t)stream), "tree_append");
+}
+
+static hti_status check_traversal(const hti_tree *tree, const hti_select *sel, int32_t T,
+                                  int32_t *sel_out, int32_t sel_stride)
+{
+    hti_status st = check_tree(tree, false);
+    if (st) return st;
+    if ((st = check_select(sel))) return st;
+    if (sel_out && sel_stride < sel_size(sel))
+        return fail(HTI_ERR_INVALID_ARG, "sel_stride %d < selection size %d", sel_stride, sel_size(sel));
+    const Bounds bd = bounds(&tree->cfg, sel, T);
+    if (bd.max_summary > HTI_MAX_CAND)
+        return fail(HTI_ERR_UNSUPPORTED, "a summary level can hold %lld candidates (> %d)",
+                    (long long)bd.max_summary, HTI_MAX_CAND);
+    if (bd.rope_rows > tree->cfg.rope_npos)
+        return fail(HTI_ERR_CAPACITY, "RoPE table has %d rows, this call can need %lld",
+                    tree->cfg.rope_npos, (long long)bd.rope_rows);
+    return HTI_OK;
+}
+
+hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q, int32_t Nq,
+                             float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *stream)
+{
+    hti_status st = check_traversal(tree, sel, 0, sel_out, sel_stride);
+    if (st) return st;
+    if (!q || !out) return fail(HTI_ERR_INVALID_ARG, "q/out is NULL");
+    if (Nq < 1) return fail(HTI_ERR_INVALID_ARG, "Nq must be >= 1");
+    TravArgs a{};
+    a.t = tree_args(tree);
+    a.mode = sel->mode;
+    a.k = sel->k;
+    a.cap = sel->cap;
+    a.p = sel->p;
+    a.q = q;
+    a.Nq = Nq;
+    a.out = out;
+    a.lse = lse;
+    a.sel = sel_out;
+    a.sel_stride = sel_stride;
+    const int64_t units = (int64_t)tree->cfg.B * Nq * tree->cfg.Hkv;
+    if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
+    return launched(launch_traverse(a, false, units, (hipStream_t)stream), "sparse_decode");
+}
+
+size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T)
+{
+    (void)sel;
+    if (check_cfg(cfg) || T < 0) return 0;
+    return prefill_ws(cfg, T).total;
+}
+
+hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const void *q_blk,
+                              const void *k_blk, const void *v_blk, int32_t T, float *out, float *lse,
+                              int32_t *sel_out, int32_t sel_stride, void *ws, size_t ws_bytes,
+                              void *stream)
+{
+    if (T < 1) return fail(HTI_ERR_INVALID_ARG, "T must be >= 1");
+    hti_status st = check_traversal(tree, sel, T, sel_out, sel_stride);
+    if (st) return st;
+    if (tree->cfg.dtype != HTI_BF16)
+        return fail(HTI_ERR_UNSUPPORTED, "prefill runs on bf16 matrix cores; dtype must be bf16");
+    if (!q_blk || !k_blk || !v_blk || !out) return fail(HTI_ERR_INVALID_ARG, "q/k/v/out is NULL");
+    const PrefillWs w = prefill_ws(&tree->cfg, T);
+    if (!ws || ws_bytes < w.total)
+        return fail(HTI_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
+    const int64_t units = (int64_t)tree->cfg.B * T * tree->cfg.Hkv;
+    if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
+    char *wb = (char *)ws;
+    hipStream_t hs = (hipStream_t)stream;
+
+    TravArgs ta{};
+    ta.t = tree_args(tree);
+    ta.mode = sel->mode;
+    ta.k = sel->k;
+    ta.cap = sel->cap;
+    ta.p = sel->p;
+    ta.q = q_blk;
+    ta.Nq = T;
+    ta.sel = sel_out;
+    ta.sel_stride = sel_stride;
+    ta.part_acc = (float *)(wb + w.part_acc);
+    ta.part_ml = (float *)(wb + w.part_ml);
+    hipError_t e = launch_traverse(ta, true, units, hs);
+    if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
+
+    PrefillArgs pa{};
+    pa.t = ta.t;
+    pa.q = q_blk;
+    pa.k = k_blk;
+    pa.v = v_blk;
+    pa.T = T;
+    pa.part_acc = ta.part_acc;
+    pa.part_ml = ta.part_ml;
+    pa.out = out;
+    pa.lse = lse;
+    pa.qr = wb + w.qr;
+    pa.kr = wb + w.kr;
+    e = launch_rotate_block(pa, hs);
+    if (e != hipSuccess) return launched(e, "sparse_prefill(rotate)");
+    return launched(launch_inblock_attention(pa, hs), "sparse_prefill(inblock)");
+}
+
+} // extern "C"

@@ -1,0 +1,68 @@
+// hti_internal.h -- kernel argument blocks and launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hti.h"
+
+namespace hti {
+
+constexpr int kMaxCand = HTI_MAX_CAND;
+constexpr int kMaxSel = HTI_MAX_SELECT;
+
+// Device view of one tree set (copied by value into kernel arguments).
+struct TreeArgs {
+    const void *kc, *vc;                 // [B, Hkv, Lcap, D]
+    void *lk[HTI_MAX_LEVELS];            // level l+1 keys [B, Hkv, ncap, R, D]
+    void *lv[HTI_MAX_LEVELS];            // level l+1 values [B, Hkv, ncap, D]
+    int64_t ncap[HTI_MAX_LEVELS + 1];    // ncap[0] = Lcap
+    const float *refs;                   // [Hkv, R, D]
+    int64_t *len;                        // [B]
+    const float2 *rope;                  // [rope_npos, D/2] (cos, sin)
+    int rope_npos;
+    int B, Hq, Hkv, D, b, levels, R, G;
+    float scale;                         // 1 / sqrt(D)
+    int dtype;
+};
+
+// Selection rule and the query-side buffers of one traversal launch.
+struct TravArgs {
+    TreeArgs t;
+    int mode, k, cap;
+    float p;
+    const void *q;     // decode [B, Nq, Hq, D]; prefill [B, T, Hq, D]
+    int Nq;            // queries per sequence (decode) or block length T (prefill)
+    float *out;        // decode [B, Nq, Hq, D]
+    float *lse;        // decode [B, Nq, Hq] (nullable)
+    int *sel;          // [B, Nq, Hkv, levels, sel_stride] (nullable)
+    int sel_stride;
+    // prefill only
+    const float *top_s;  // [B, T, Hkv, ntop_stride] group scores of the top level (nullable)
+    const float *top_z;  // [B, T, Hq, ntop_stride] per-head logits of the top level
+    int ntop_stride;
+    float *part_acc;     // [B, T, Hq, D] unnormalised partial outputs
+    float *part_ml;      // [B, T, Hq, 2] running max and denominator
+};
+
+hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s);
+hipError_t launch_build_level(const TreeArgs &t, int lvl, int64_t max_nodes, hipStream_t s);
+hipError_t launch_append(const TreeArgs &t, const void *k_new, const void *v_new, hipStream_t s);
+hipError_t launch_traverse(const TravArgs &a, bool prefill, int64_t units, hipStream_t s);
+
+// Prefill dense parts (MFMA).
+struct PrefillArgs {
+    TreeArgs t;
+    const void *q, *k, *v;     // block [B, T, Hq|Hkv, D]
+    int T;
+    float *top_s, *top_z;      // outputs of the top-level scoring
+    int ntop_stride;
+    const float *part_acc, *part_ml;
+    float *out, *lse;
+    void *qr, *kr;             // rotated block q/k (bf16 staging) [B, Hq|Hkv, T, D]
+};
+hipError_t launch_top_scores(const PrefillArgs &a, int64_t ntop_max, hipStream_t s);
+hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_inblock_attention(const PrefillArgs &a, hipStream_t s);
+
+} // namespace hti

@@ -1,0 +1,208 @@
+/*
+ * hti.h -- C ABI of the tree-indexed recursive sparse attention library
+ * (gfx950 / MI355X).
+ *
+ * The method (sources cited by page title and element):
+ *   "Recursive Sparse Attention: Million-Token Length Extrapolation at
+ *   Logarithmic Cost", abstract -- a tree over the KV cache whose nodes hold
+ *   one key (from a per-layer pooler shared by every level) and one mean-pooled
+ *   value; each level above the tokens keeps at most k candidates; the
+ *   summaries of the candidates that were not kept share one softmax with the
+ *   exact tokens finally reached; an entry's RoPE position is its index among
+ *   its level's candidates.
+ *   "Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
+ *   Figure 3 caption -- keys of a chunk of contiguous nodes are pooled by
+ *   attention w.r.t. reference queries (R of them, keys stored per reference in
+ *   parallel); routing scores the top level, keeps a top-p set and descends;
+ *   Table VIII -- only full nodes exist, n_l(T) = floor(T / b^l).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller, unless the
+ *     argument says "host".  The library never allocates, frees or retains
+ *     device memory; it keeps no device state between calls.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues work on it and returns; results are valid once the
+ *     stream has reached that point.
+ *   - Every call validates its arguments on the host before enqueuing
+ *     anything.  On error nothing is enqueued, device memory is unchanged, a
+ *     negative hti_status is returned and hti_last_error() describes it.
+ *   - Element types: HTI_F32 = IEEE fp32, HTI_BF16 = bfloat16 (stored as the
+ *     upper 16 bits of an fp32).  Tree nodes are stored in the cache dtype
+ *     (bf16 by round-to-nearest-even); all arithmetic is fp32.
+ *   - Layouts are dense, row-major, innermost dimension last.
+ *   - RoPE: rotate-half pairs (j, j + d/2), angle pos * base^(-2j/d).
+ *   - Pooler: for node i and reference r_j, alpha = softmax over its b
+ *     children of (r_j . k_child / sqrt(d)); pooled key = sum alpha k_child
+ *     (level 1 pools token keys, level l >= 2 pools the level l-1 keys of the
+ *     same reference); value = mean of the children's values.
+ */
+#ifndef HTI_H
+#define HTI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HTI_MAX_LEVELS 12   /* tree levels above the tokens */
+#define HTI_MAX_SELECT 32   /* largest k (top-k) or cap (top-p) */
+#define HTI_MAX_CAND 1024   /* largest candidate list of a summary level */
+#define HTI_MAX_R 8         /* reference queries per KV head */
+
+typedef enum {
+    HTI_OK = 0,
+    HTI_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes */
+    HTI_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle (d, G, ...) */
+    HTI_ERR_CAPACITY = -3,    /* a length exceeds a buffer capacity */
+    HTI_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+    HTI_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
+} hti_status;
+
+typedef enum { HTI_F32 = 0, HTI_BF16 = 1 } hti_dtype;
+typedef enum { HTI_TOPK = 0, HTI_TOPP = 1 } hti_select_mode;
+
+/* Shape of one layer's tree set: B sequences x Hkv KV heads, one tree each. */
+typedef struct {
+    int32_t B;          /* sequences */
+    int32_t Hq;         /* query heads; Hq % Hkv == 0, G = Hq / Hkv in {1,2,4,8} */
+    int32_t Hkv;        /* KV heads */
+    int32_t d;          /* head dim: 64 or 128 */
+    int32_t b;          /* branching factor, 2..64 */
+    int32_t levels;     /* tree levels above the tokens, 0..HTI_MAX_LEVELS */
+    int32_t R;          /* reference queries per KV head, 1..HTI_MAX_R */
+    int32_t dtype;      /* hti_dtype of the caches, tree nodes and q/k/v inputs */
+    int64_t Lcap;       /* token capacity of the cache per (sequence, head) */
+    float rope_base;    /* RoPE base (e.g. 10000) */
+    int32_t rope_npos;  /* rows of the RoPE table (largest position + 1) */
+} hti_tree_cfg;
+
+/* Device buffers of a tree set (all caller-allocated, sizes from hti_plan). */
+typedef struct {
+    hti_tree_cfg cfg;
+    void *k_cache;                    /* [B, Hkv, Lcap, d] un-rotated token keys */
+    void *v_cache;                    /* [B, Hkv, Lcap, d] token values */
+    void *lvl_k[HTI_MAX_LEVELS];      /* level l+1: [B, Hkv, ncap_{l+1}, R, d] pooled keys */
+    void *lvl_v[HTI_MAX_LEVELS];      /* level l+1: [B, Hkv, ncap_{l+1}, d] mean values */
+    const float *ref_q;               /* [Hkv, R, d] fp32 reference queries */
+    int64_t *len;                     /* [B] device: tokens currently in each tree */
+    float *rope;                      /* [rope_npos, d/2, 2] fp32 (cos, sin), see hti_rope_init */
+} hti_tree;
+
+/* Per-call selection rule (RecSA: top-k per level; ZHA: top-p per level). */
+typedef struct {
+    int32_t mode;       /* hti_select_mode */
+    int32_t k;          /* top-k: nodes kept per level, 1..HTI_MAX_SELECT */
+    float p;            /* top-p: probability mass, (0, 1] */
+    int32_t cap;        /* top-p: largest kept set, 1..HTI_MAX_SELECT */
+} hti_select;
+
+/* Sizes for a configuration (all host values). */
+typedef struct {
+    int64_t ncap[HTI_MAX_LEVELS + 1]; /* ncap[0] = Lcap, ncap[l] = floor(ncap[l-1] / b) */
+    size_t cache_bytes;               /* each of k_cache, v_cache */
+    size_t lvl_k_bytes[HTI_MAX_LEVELS];
+    size_t lvl_v_bytes[HTI_MAX_LEVELS];
+    size_t rope_bytes;
+    int32_t rope_npos_needed;         /* rows hti_sparse_decode needs for this cfg and
+                                         the selection passed to hti_plan */
+} hti_plan_out;
+
+/*
+ * hti_plan: capacity of every buffer of `cfg` (host only, no device work).
+ * `sel` (nullable) lets the plan report the RoPE rows decode will need, and
+ * `T` the extra rows of a prefill block (0 for decode only).
+ * Errors: HTI_ERR_INVALID_ARG / HTI_ERR_UNSUPPORTED on a bad cfg.
+ */
+hti_status hti_plan(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T,
+                    hti_plan_out *out);
+
+/*
+ * hti_rope_init: fill tree->rope with cos/sin of pos * base^(-2j/d) for
+ * pos < rope_npos, j < d/2, each formed in double and rounded once to fp32.
+ */
+hti_status hti_rope_init(const hti_tree *tree, void *stream);
+
+/*
+ * hti_tree_build: build every full node of every level over the first
+ * L_host[s] cached tokens of each sequence s and set len[s] = L_host[s]
+ * (a streaming pooling pass over the cache, level by level).
+ *   L_host: host [B], 0 <= L_host[s] <= Lcap.
+ * Source: RecSA abstract (one key, one mean value per node; shared pooler);
+ * ZHA Figure 3 caption (reference-query pooling of contiguous chunks,
+ * recursive); ZHA Table VIII (full nodes only, all built in prefill).
+ */
+hti_status hti_tree_build(const hti_tree *tree, const int64_t *L_host, void *stream);
+
+/*
+ * hti_tree_append: append one token per sequence at row len[s], build every
+ * node that this token completes (level 1 when (len+1) % b == 0, level 2 when
+ * (len+1) % b^2 == 0, ...), then len[s] += 1.
+ *   k_new, v_new: [B, Hkv, d] in the cache dtype.
+ * A sequence whose cache is full (len[s] == Lcap) is left unchanged and its
+ * len is not advanced (the device checks this; callers that track lengths on
+ * the host should check capacity before calling).
+ * Source: ZHA Table VIII (decode maintenance amortised over full-node
+ * completions).
+ */
+hti_status hti_tree_append(const hti_tree *tree, const void *k_new, const void *v_new,
+                           void *stream);
+
+/*
+ * hti_sparse_decode: attention of Nq query tokens per sequence, each at
+ * position len[s] - 1, over that sequence's trees.
+ *   q:   [B, Nq, Hq, d] in the cache dtype (un-rotated)
+ *   out: [B, Nq, Hq, d] fp32 attention output
+ *   lse: [B, Nq, Hq] fp32 log-sum-exp of the logits (nullable)
+ *   sel: [B, Nq, Hkv, levels, sel_stride] int32 (nullable): node ids kept at
+ *        each level (row l-1 = level l), ascending, -1 padded;
+ *        sel_stride >= k (top-k) or cap (top-p).
+ * Per (query, KV group): the top level's nodes are all candidates; at each
+ * level the candidates are scored by the mean over the group's heads of the
+ * RoPE'd logits (candidate i at position i, the query at position |C_l|), the
+ * top-k (or top-p set, capped) is kept and its children, followed by the
+ * level's orphan nodes, form the next level's candidates; the others enter the
+ * per-head softmax with their pooled key and mean value.  At the token level
+ * every candidate enters the softmax exactly.
+ * Source: RecSA abstract; ZHA Figure 3 caption (top-p routing).
+ * Errors additionally: HTI_ERR_CAPACITY if rope_npos is below the positions
+ * this cfg/selection can reach, HTI_ERR_UNSUPPORTED if a summary level can
+ * exceed HTI_MAX_CAND candidates.
+ */
+hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q,
+                             int32_t Nq, float *out, float *lse, int32_t *sel_out,
+                             int32_t sel_stride, void *stream);
+
+/*
+ * hti_prefill_workspace_bytes: device workspace hti_sparse_prefill needs.
+ */
+size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T);
+
+/*
+ * hti_sparse_prefill: attention of a block of T new tokens per sequence,
+ * at positions len[s] .. len[s] + T - 1, over the tree of the prefix
+ * [0, len[s]) plus causal attention inside the block, merged in one softmax.
+ * The tree is not extended by the block.
+ *   q_blk: [B, T, Hq, d], k_blk, v_blk: [B, T, Hkv, d] (cache dtype, un-rotated)
+ *   out:   [B, T, Hq, d] fp32;  lse: [B, T, Hq] fp32 (nullable)
+ *   sel_out: [B, T, Hkv, levels, sel_stride] int32 (nullable), as in decode
+ *   ws, ws_bytes: device workspace of at least hti_prefill_workspace_bytes()
+ * Candidate lists and prefix positions follow decode; at the token level the
+ * prefix candidates are followed by the block tokens 0..t, and query t sits
+ * at position (number of prefix candidates) + t.
+ * Source: RecSA abstract (prefill with the same tree and shared softmax).
+ */
+hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const void *q_blk,
+                              const void *k_blk, const void *v_blk, int32_t T, float *out,
+                              float *lse, int32_t *sel_out, int32_t sel_stride, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char *hti_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HTI_H */

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles, ragged tails and the degenerate cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+import hti_workloads as W
+import oracle
+from gpu_helpers import accept, kmax_of, log, make_treeset, oracle_tree, select_of, tree_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _setup(w, Lcap=None, Ls=None):
+    Lcap = Lcap or w.L
+    K, V = W.gen_kv(w, Lcap=Lcap)
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    Ls = Ls or [w.L] * w.B
+    ts.tree_build(Ls)
+    return ts, K, V, refs, Ls
+
+
+def _decode(ts, w, q):
+    out = torch.empty((w.B, q.shape[1], w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, q.shape[1], w.Hq), dtype=torch.float32, device=DEV)
+    sel = torch.empty((w.B, q.shape[1], w.Hkv, max(w.levels, 1), kmax_of(w)), dtype=torch.int32,
+                      device=DEV)
+    ts.sparse_decode(select_of(w), q.to(DEV).contiguous(), out, lse, sel)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+
+
+def _check_decode(ts, w, K, V, refs, Ls, q, trees=None, upload=False):
+    """Decode every query of every sequence/group and accept against the oracle."""
+    trees = trees or {}
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            if (bi, g) not in trees:
+                trees[(bi, g)] = oracle_tree(w, K[bi, g], V[bi, g], refs[g], Ls[bi])
+            if upload:
+                tr = trees[(bi, g)]
+                for l in range(w.levels):
+                    n = tr.lk[l].shape[0]
+                    ts.lvl_k[l][bi, g, :n] = torch.from_numpy(tr.lk[l]).to(ts.lvl_k[l].dtype).to(DEV)
+                    ts.lvl_v[l][bi, g, :n] = torch.from_numpy(tr.lv[l]).to(ts.lvl_v[l].dtype).to(DEV)
+    out, lse, sel = _decode(ts, w, q)
+    nex, emax = 0, 0.0
+    for bi in range(w.B):
+        for qi in range(q.shape[1]):
+            for g in range(w.Hkv):
+                hs = slice(g * w.G, (g + 1) * w.G)
+                ex, err = accept(w, trees[(bi, g)], K[bi, g, : Ls[bi]], V[bi, g, : Ls[bi]],
+                                 q[bi, qi, hs], out[bi, qi, hs], lse[bi, qi, hs], sel[bi, qi, g])
+                nex += ex
+                emax = max(emax, err)
+    log(f"  {w.name}: units={w.B * q.shape[1] * w.Hkv} exempt={nex} max_err={emax:.2e}")
+    return trees, out, sel
+
+
+# --------------------------------------------------------------------------- build
+BUILD_CASES = [
+    W.TINY,
+    W.DEC128K.replace(name="bf16_b32", L=40000 + 17, B=2, needles=0),
+    W.ZHA2M.replace(name="bf16_r4_b16", L=70000 + 5, levels=4),
+    W.TINY.replace(name="f32_d128_b8", d=128, b=8, levels=4, L=9000 + 3, Hq=4, Hkv=2, R=2),
+    W.DEC128K.replace(name="bf16_d64_b3", d=64, b=3, levels=6, L=3000, Hq=4, Hkv=4),
+]
+
+
+@pytest.mark.parametrize("w", BUILD_CASES, ids=lambda w: w.name)
+def test_build_parity(w):
+    log(f"build parity {w.name} L={w.L} b={w.b} levels={w.levels} R={w.R} {w.dtype}")
+    ts, K, V, refs, Ls = _setup(w)
+    torch.cuda.synchronize()
+    assert ts.len.cpu().tolist() == Ls
+    exact = []
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            tr = oracle_tree(w, K[bi, g], V[bi, g], refs[g], w.L)
+            for l in range(w.levels):
+                n = tr.lk[l].shape[0]
+                exact.append(tree_close(w, ts.lvl_k[l][bi, g, :n], ts.lvl_v[l][bi, g, :n],
+                                        tr.lk[l], tr.lv[l], level=l + 1))
+    log(f"  fraction of bit-exact node elements {np.mean(exact):.5f}")
+    if w.dtype == "bf16":
+        assert np.mean(exact) > 0.99
+
+
+# --------------------------------------------------------------------------- decode
+def test_decode_tiny_workload():
+    """The 4096-token fp32 workload at full size: 16 queries, top-k 4."""
+    w = W.TINY
+    ts, K, V, refs, Ls = _setup(w)
+    q = W.gen_queries(w)
+    _check_decode(ts, w, K, V, refs, Ls, q)
+
+
+DECODE_CASES = [
+    W.DEC128K.replace(name="gqa4_ragged", B=3, L=20000, needles=0, levels=2),
+    W.DEC128K.replace(name="gqa4_orphans", L=32 * 32 * 5 + 32 * 7 + 13, levels=2, Nq=3),
+    W.DEC128K.replace(name="g1_d64", Hq=2, Hkv=2, d=64, L=7777, b=8, levels=3, k=3),
+    W.DEC128K.replace(name="g2_k1", Hq=4, Hkv=2, L=5000, b=16, levels=2, k=1),
+    W.DEC128K.replace(name="g8", Hq=16, Hkv=2, L=6000, b=16, levels=2, k=5),
+    W.DEC128K.replace(name="f32_d128", dtype="f32", Hq=8, Hkv=2, L=9000, b=16, levels=2, k=6),
+    W.ZHA2M.replace(name="topp_r4", L=16 ** 4 * 2 + 300, levels=4),
+    W.ZHA2M.replace(name="topp_p1_cap32", L=3000, levels=2, p=1.0, cap=32, R=2),
+    W.ZHA2M.replace(name="topp_p05", L=20000, levels=3, p=0.5, cap=8, R=1),
+    W.DEC128K.replace(name="k32", L=33000, b=16, levels=3, k=32),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: w.name)
+def test_decode_parity(w):
+    log(f"decode parity {w.name}")
+    Ls = [w.L - 977 * i for i in range(w.B)]
+    ts, K, V, refs, _ = _setup(w, Lcap=w.L, Ls=Ls)
+    q = W.gen_queries(w)
+    trees, _, _ = _check_decode(ts, w, K, V, refs, Ls, q)
+    # the same decode on the oracle's own tree (decode kernel in isolation)
+    _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, upload=True)
+
+
+def test_candidate_capacity_is_enforced():
+    """k = 32 with b = 32 can put 32 * 32 + 31 candidates on a level: more than
+    the kernel's LDS holds, so the call is refused before any launch."""
+    import hierarchical_tree_indexed_amd as hti
+    w = W.DEC128K.replace(name="k32b32", L=33000, levels=2, k=32)
+    K, V = W.gen_kv(w, Lcap=w.L)
+    ts = make_treeset(w, w.L, K.to(DEV), V.to(DEV), W.gen_refs(w).to(DEV))
+    out = torch.empty((1, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    with pytest.raises(hti.HTIError) as ei:
+        ts.sparse_decode(select_of(w), W.gen_queries(w).to(DEV), out)
+    assert ei.value.status == -2
+
+
+def test_decode_is_deterministic():
+    w = DECODE_CASES[0]
+    ts, K, V, refs, Ls = _setup(w)
+    q = W.gen_queries(w)
+    a = _decode(ts, w, q)
+    b = _decode(ts, w, q)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("L,levels", [(1, 2), (5, 2), (31, 1), (32, 1), (33, 3), (1024, 2), (700, 0)])
+def test_decode_edge_lengths(L, levels):
+    """Lengths below one node, exactly one node, a single top node, no tree."""
+    w = W.DEC128K.replace(name=f"edge_{L}_{levels}", L=L, levels=levels, needles=0,
+                          k=32 if levels == 0 else 8)
+    ts, K, V, refs, Ls = _setup(w)
+    q = W.gen_queries(w)
+    _check_decode(ts, w, K, V, refs, Ls, q)
+
+
+def test_dense_equivalence_on_gpu():
+    """Every level keeps all its candidates -> plain causal attention."""
+    from ref_f64 import dense_causal
+    w = W.DEC128K.replace(name="dense", L=1024, b=32, levels=2, k=32, needles=0)
+    ts, K, V, refs, Ls = _setup(w)
+    q = W.gen_queries(w)
+    out, _, _ = _decode(ts, w, q)
+    for g in range(w.Hkv):
+        hs = slice(g * w.G, (g + 1) * w.G)
+        ref = dense_causal(q[0, 0, hs].float().numpy(), K[0, g].float().numpy(),
+                           V[0, g].float().numpy(), w.L - 1)
+        assert np.abs(out[0, 0, hs] - ref).max() < 2e-2
+
+
+# --------------------------------------------------------------------------- append
+def test_append_matches_build_and_oracle():
+    w = W.DEC128K.replace(name="append", B=2, L=32 * 32 * 3 - 5, levels=3, steps=40, needles=0)
+    Lcap = w.L + w.steps
+    K, V = W.gen_kv(w, Lcap=Lcap)
+    refs = W.gen_refs(w)
+    Kd, Vd = K.clone().to(DEV), V.clone().to(DEV)
+    ts = make_treeset(w, Lcap, Kd, Vd, refs.to(DEV))
+    ts.tree_build([w.L] * w.B)
+    for s in range(w.steps):
+        kn, vn = W.gen_append(w, s, device=DEV)
+        ts.tree_append(kn.contiguous(), vn.contiguous())
+        K[:, :, w.L + s] = kn.cpu()
+        V[:, :, w.L + s] = vn.cpu()
+    torch.cuda.synchronize()
+    Lf = w.L + w.steps
+    assert ts.len.cpu().tolist() == [Lf] * w.B
+    assert torch.equal(Kd.cpu(), K) and torch.equal(Vd.cpu(), V)
+    # a fresh build over the final length gives bit-identical nodes
+    ts2 = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    ts2.tree_build([Lf] * w.B)
+    torch.cuda.synchronize()
+    for l in range(w.levels):
+        assert torch.equal(ts.lvl_k[l], ts2.lvl_k[l]) and torch.equal(ts.lvl_v[l], ts2.lvl_v[l])
+    # and the oracle agrees
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            tr = oracle_tree(w, K[bi, g], V[bi, g], refs[g], Lf)
+            for l in range(w.levels):
+                n = tr.lk[l].shape[0]
+                tree_close(w, ts.lvl_k[l][bi, g, :n], ts.lvl_v[l][bi, g, :n], tr.lk[l], tr.lv[l],
+                           level=l + 1)
+    q = W.gen_queries(w)
+    _check_decode(ts, w, K, V, refs, [Lf] * w.B, q)
+
+
+def test_append_full_cache_is_a_no_op():
+    w = W.DEC128K.replace(name="full", B=1, L=64, levels=1, needles=0)
+    K, V = W.gen_kv(w, Lcap=64)
+    ts = make_treeset(w, 64, K.to(DEV), V.to(DEV), W.gen_refs(w).to(DEV))
+    ts.tree_build([64])
+    kn, vn = W.gen_append(w, 0, device=DEV)
+    before = ts.k_cache.clone()
+    ts.tree_append(kn.contiguous(), vn.contiguous())
+    torch.cuda.synchronize()
+    assert ts.len.item() == 64 and torch.equal(before, ts.k_cache)
+
+
+# --------------------------------------------------------------------------- prefill
+def _prefill(ts, w, T, qb, kb, vb):
+    sel = select_of(w)
+    ws = torch.empty(ts.prefill_workspace_bytes(sel, T), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, T, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, T, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, T, w.Hkv, max(w.levels, 1), kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_prefill(sel, qb.to(DEV).contiguous(), kb.to(DEV).contiguous(), vb.to(DEV).contiguous(),
+                      out, ws, lse, so)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
+
+
+def _check_prefill(w, P0, T, ts_list=None, queries=None):
+    w = w.replace(L=P0, T=T)
+    K, V = W.gen_kv(w, Lcap=max(P0, 1))
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, max(P0, 1), K.to(DEV), V.to(DEV), refs.to(DEV), T=T)
+    ts.tree_build([P0] * w.B)
+    qb, kb, vb = W.gen_block(w)
+    out, lse, so = _prefill(ts, w, T, qb, kb, vb)
+    queries = queries if queries is not None else range(T)
+    nex, emax = 0, 0.0
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            tr = oracle_tree(w, K[bi, g], V[bi, g], refs[g], P0)
+            bk = kb[bi, :, g].float().numpy()
+            bv = vb[bi, :, g].float().numpy()
+            for t in queries:
+                hs = slice(g * w.G, (g + 1) * w.G)
+                ex, err = accept(w, tr, K[bi, g, :P0], V[bi, g, :P0], qb[bi, t, hs], out[bi, t, hs],
+                                 lse[bi, t, hs], so[bi, t, g], t=t, blk_k=bk, blk_v=bv)
+                nex += ex
+                emax = max(emax, err)
+    log(f"  prefill P0={P0} T={T}: exempt={nex} max_err={emax:.2e}")
+    return out
+
+
+PF = W.PREFILL.replace(name="pf_small")
+
+
+@pytest.mark.parametrize("P0,T,levels", [(3000, 100, 2), (32 * 32 * 4 + 70, 77, 2), (5000, 1, 2),
+                                         (0, 130, 2), (40, 64, 1), (2000, 33, 0)])
+def test_prefill_parity(P0, T, levels):
+    _check_prefill(PF.replace(levels=levels, k=8 if levels else 32), P0, T)
+
+
+def test_prefill_topp_r4():
+    _check_prefill(W.ZHA2M.replace(name="pf_topp", levels=3), 16 ** 3 * 3 + 50, 48)
+
+
+def test_prefill_T1_equals_decode():
+    """A one-token block at P0 gives the decode result at position P0 when
+    the token completes no node ((P0 + 1) % b != 0)."""
+    w = PF.replace(L=4000, T=1, levels=2)
+    K, V = W.gen_kv(w, Lcap=w.L + 1)
+    refs = W.gen_refs(w)
+    qb, kb, vb = W.gen_block(w)
+    K[:, :, w.L] = kb[:, 0]
+    V[:, :, w.L] = vb[:, 0]
+    ts = make_treeset(w, w.L + 1, K.to(DEV), V.to(DEV), refs.to(DEV), T=1)
+    ts.tree_build([w.L] * w.B)
+    pout, _, psel = _prefill(ts, w, 1, qb, kb, vb)
+    ts.tree_build([w.L + 1] * w.B)
+    dout, _, dsel = _decode(ts, w, qb[:, :1])
+    assert np.array_equal(psel[:, 0], dsel[:, 0])
+    assert np.abs(pout[:, 0] - dout[:, 0]).max() < 2e-2

@@ -27,8 +27,8 @@ STATUS = {0: "HTI_OK", -1: "HTI_ERR_INVALID_ARG", -2: "HTI_ERR_UNSUPPORTED",
           -3: "HTI_ERR_CAPACITY", -4: "HTI_ERR_WORKSPACE", -5: "HTI_ERR_LAUNCH"}
 
 EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append",
-           "hti_sparse_decode", "hti_prefill_workspace_bytes", "hti_sparse_prefill",
-           "hti_last_error"]
+           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_prefill_workspace_bytes",
+           "hti_sparse_prefill", "hti_last_error"]
 
 
 class TreeCfg(C.Structure):
@@ -76,7 +76,8 @@ def lib() -> C.CDLL:
             "hti_rope_init": (C.c_int, [vp, vp]),
             "hti_tree_build": (C.c_int, [vp, vp, vp]),
             "hti_tree_append": (C.c_int, [vp, vp, vp, vp]),
-            "hti_sparse_decode": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, vp]),
+            "hti_decode_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
+            "hti_sparse_decode": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
             "hti_prefill_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
             "hti_sparse_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp,
                                              C.c_size_t, vp]),
@@ -147,6 +148,7 @@ class TreeSet:
         self.ref_q = torch.zeros((cfg.Hkv, cfg.R, cfg.d), dtype=torch.float32, device=device)
         self.len = torch.zeros(cfg.B, dtype=torch.int64, device=device)
         self.rope = torch.zeros((cfg.rope_npos, cfg.d // 2, 2), dtype=torch.float32, device=device)
+        self._dec_ws = {}
         self._refresh()
 
     def _refresh(self):
@@ -169,13 +171,27 @@ class TreeSet:
     def tree_append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
         _check(lib().hti_tree_append(C.byref(self.c), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
+    def decode_workspace(self, sel: Select, Nq: int) -> torch.Tensor:
+        """Zero-filled decode workspace for Nq queries per sequence (kept and
+        reused by every decode call of that shape)."""
+        key = Nq
+        ws = self._dec_ws.get(key)
+        if ws is None:
+            n = lib().hti_decode_workspace_bytes(C.byref(self.cfg), C.byref(sel), Nq)
+            ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=self.k_cache.device)
+            self._dec_ws[key] = ws
+        return ws
+
     def sparse_decode(self, sel: Select, q: torch.Tensor, out: torch.Tensor, lse=None,
-                      sel_out=None, stream=None):
+                      sel_out=None, stream=None, split: bool = True):
         B, Nq, Hq, d = q.shape
         assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
         stride = 0 if sel_out is None else sel_out.shape[-1]
+        ws = self.decode_workspace(sel, Nq) if split else None
+        nbytes = 0 if ws is None else ws.numel()
         _check(lib().hti_sparse_decode(C.byref(self.c), C.byref(sel), _ptr(q), Nq, _ptr(out),
-                                       _ptr(lse), _ptr(sel_out), stride, _stream(stream)))
+                                       _ptr(lse), _ptr(sel_out), stride, _ptr(ws), nbytes,
+                                       _stream(stream)))
 
     def prefill_workspace_bytes(self, sel: Select, T: int) -> int:
         return lib().hti_prefill_workspace_bytes(C.byref(self.cfg), C.byref(sel), T)

@@ -94,7 +94,7 @@ Bounds bounds(const hti_tree_cfg *c, const hti_select *s, int32_t T)
     const int64_t keff = s ? sel_size(s) : 1;
     const int Lv = c->levels;
     r.max_summary = 0;
-    r.rope_rows = 1;
+    r.rope_rows = 2;   // row 1 is the per-position angle step
     if (Lv == 0) {
         r.cand[0] = ncap[0];
     } else {
@@ -163,6 +163,9 @@ hti_status check_tree(const hti_tree *tr, bool need_refs)
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ceil(2^32 / b): for 0 <= i < 2^16 and 2 <= b <= 64, umulhi(i, binv) == i / b
+uint32_t binv_of(int b) { return (uint32_t)(((uint64_t(1) << 32) + (uint64_t)b - 1) / (uint64_t)b); }
 
 hti_status launched(hipError_t e, const char *what)
 {
@@ -304,13 +307,26 @@ static hti_status check_traversal(const hti_tree *tree, const hti_select *sel, i
     return HTI_OK;
 }
 
+size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t Nq)
+{
+    (void)sel;
+    if (check_cfg(cfg) || Nq < 1) return 0;
+    const int64_t units = (int64_t)cfg->B * Nq * cfg->Hkv;
+    return decode_ws_bytes(units, HTI_DECODE_MAX_SPLIT, cfg->levels, cfg->Hq / cfg->Hkv, cfg->d);
+}
+
 hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q, int32_t Nq,
-                             float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *stream)
+                             float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *ws,
+                             size_t ws_bytes, void *stream)
 {
     hti_status st = check_traversal(tree, sel, 0, sel_out, sel_stride);
     if (st) return st;
     if (!q || !out) return fail(HTI_ERR_INVALID_ARG, "q/out is NULL");
     if (Nq < 1) return fail(HTI_ERR_INVALID_ARG, "Nq must be >= 1");
+    const int64_t units_ws = (int64_t)tree->cfg.B * Nq * tree->cfg.Hkv;
+    const int G = tree->cfg.Hq / tree->cfg.Hkv;
+    if (ws && ws_bytes < decode_ws_bytes(units_ws, HTI_DECODE_MAX_SPLIT, tree->cfg.levels, G, tree->cfg.d))
+        return fail(HTI_ERR_WORKSPACE, "decode workspace of %zu bytes is too small", ws_bytes);
     TravArgs a{};
     a.t = tree_args(tree);
     a.mode = sel->mode;
@@ -323,8 +339,21 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
     a.lse = lse;
     a.sel = sel_out;
     a.sel_stride = sel_stride;
-    const int64_t units = (int64_t)tree->cfg.B * Nq * tree->cfg.Hkv;
+    a.binv = binv_of(tree->cfg.b);
+    const int64_t units = units_ws;
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
+    if (ws) {
+        // split each unit over W workgroups when all of them fit on the device
+        // at once; otherwise one workgroup per unit
+        const Bounds bd = bounds(&tree->cfg, sel, 0);
+        int W = 0;
+        hipError_t e = decode_split_plan(a, units, bd.max_summary, &W);
+        if (e != hipSuccess) return launched(e, "sparse_decode(plan)");
+        if (W > 0) {
+            const DecodeWs dw = decode_ws_layout(ws, units, W, tree->cfg.levels, G, tree->cfg.d);
+            return launched(launch_decode_split(a, dw, units, (hipStream_t)stream), "sparse_decode");
+        }
+    }
     return launched(launch_traverse(a, false, units, (hipStream_t)stream), "sparse_decode");
 }
 
@@ -364,6 +393,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     ta.Nq = T;
     ta.sel = sel_out;
     ta.sel_stride = sel_stride;
+    ta.binv = binv_of(tree->cfg.b);
     ta.part_acc = (float *)(wb + w.part_acc);
     ta.part_ml = (float *)(wb + w.part_ml);
     hipError_t e = launch_traverse(ta, true, units, hs);

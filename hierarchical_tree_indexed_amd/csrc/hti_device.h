@@ -108,4 +108,71 @@ __device__ __forceinline__ float group_max(float v)
     return v;
 }
 
+// DPP-based reductions (no LDS round trip).  16-lane all-reduce: quad
+// permutations [1,0,3,2] and [2,3,0,1], then row half-mirror and row mirror;
+// the four 16-lane rows are combined through readlane.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float rlane(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float sum16(float v)
+{
+    v += dppf<0xB1>(v);
+    v += dppf<0x4E>(v);
+    v += dppf<0x141>(v);
+    v += dppf<0x140>(v);
+    return v;
+}
+__device__ __forceinline__ float max16(float v)
+{
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
+    v = fmaxf(v, dppf<0x140>(v));
+    return v;
+}
+__device__ __forceinline__ int min16i(int v)
+{
+    v = min(v, dppi<0xB1>(v));
+    v = min(v, dppi<0x4E>(v));
+    v = min(v, dppi<0x141>(v));
+    v = min(v, dppi<0x140>(v));
+    return v;
+}
+// wave-wide results, uniform across the wave
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = sum16(v);
+    return (rlane(v, 0) + rlane(v, 16)) + (rlane(v, 32) + rlane(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = max16(v);
+    return fmaxf(fmaxf(rlane(v, 0), rlane(v, 16)), fmaxf(rlane(v, 32), rlane(v, 48)));
+}
+__device__ __forceinline__ int wave_min_i(int v)
+{
+    v = min16i(v);
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// One 16-byte-per-lane gather straight into LDS (gfx950 global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds + 16 * l; `lds` must be wave-uniform.
+__device__ __forceinline__ void gather16_to_lds(const void *g, void *lds)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
 } // namespace hti

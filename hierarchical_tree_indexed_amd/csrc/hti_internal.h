@@ -31,6 +31,7 @@ struct TravArgs {
     TreeArgs t;
     int mode, k, cap;
     float p;
+    uint32_t binv;     // ceil(2^32 / b), for division by b in index arithmetic
     const void *q;     // decode [B, Nq, Hq, D]; prefill [B, T, Hq, D]
     int Nq;            // queries per sequence (decode) or block length T (prefill)
     float *out;        // decode [B, Nq, Hq, D]
@@ -44,6 +45,23 @@ struct TravArgs {
     float *part_acc;     // [B, T, Hq, D] unnormalised partial outputs
     float *part_ml;      // [B, T, Hq, 2] running max and denominator
 };
+
+// Workspace of the split decode (zeroed by the caller before first use, then
+// owned by the library): per-unit launch epoch, an error flag, the per-level
+// exchange words and the per-workgroup partial states, all as words tagged
+// with the launch epoch.
+struct DecodeWs {
+    int W;              // workgroups per (query, KV group) unit
+    uint32_t *epoch;    // [units]
+    int *err;           // [1]
+    uint64_t *words;    // [units][levels][W][HTI_MAX_SELECT + 2]
+    uint64_t *part;     // [units][W][G][D + 2]: tag << 32 | fp32 bits
+};
+// W > 0: split each unit over W workgroups; W == 0: one workgroup per unit.
+hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W);
+size_t decode_ws_bytes(int64_t units, int W, int levels, int G, int D);
+DecodeWs decode_ws_layout(void *base, int64_t units, int W, int levels, int G, int D);
+hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s);
 
 hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s);
 hipError_t launch_build_level(const TreeArgs &t, int lvl, int64_t max_nodes, hipStream_t s);

@@ -1,7 +1,8 @@
 // hti_traverse.hip -- fused tree traversal + shared online softmax.
 //
-// One workgroup (256 threads, 4 wavefronts) owns one (query token, KV-head
-// group) unit and walks the tree from the top level to the tokens:
+// One workgroup owns one (query token, KV-head group) unit (decode: 8
+// wavefronts, the level's value rows gathered straight into LDS; prefill: 2
+// wavefronts, many units per compute unit, values through registers) and walks the tree from the top level to the tokens:
 //   "Recursive Sparse Attention", abstract: each level above the tokens keeps
 //   at most k candidates; the summaries of the candidates not kept share one
 //   softmax with the exact tokens finally reached; an entry's RoPE position is
@@ -17,50 +18,86 @@
 // position |C_l| on a summary level and after the tokens before it on the
 // token level; ties keep the lower candidate index.
 //
+// Latency structure.  Each level costs one dependent trip to HBM.  Decode
+// issues, at the start of a level, the key loads of every candidate (into
+// registers) and the value rows of every candidate (straight into LDS with
+// global_load_lds_dwordx4, no registers held), then scores, selects and
+// updates the softmax while the values arrive; the values of the few kept
+// candidates are fetched but not used (about k / |C_l| of the value bytes).
+// Prefill, which runs many units per CU, folds a level's unselected values
+// in with the next level's key loads instead.
+//
 // Per level:
-//   1. score: a quarter-wave (16 lanes) per candidate; each lane holds d/32
-//      rotate-half pairs of the key (two 4..16-byte loads), rotates them with
-//      the RoPE table row of the candidate's index, and dots them with the G
-//      rotated query heads; 16-lane butterfly sums give the G logits;
-//   2. select: wave 0 runs k (or <= cap) rounds of a wavefront arg-max over
-//      the scores held in registers (ties -> lower index), then compacts the
-//      kept positions in ascending order with ballots;
-//   3. accumulate: the unselected candidates update the per-head online
-//      softmax (block max -> rescale -> exp -> per-wave partial sums of the
-//      values, each lane owning d/64 output dims of every head).
-// The token level streams its candidates in chunks of HTI_MAX_CAND.
+//   score:  a quarter-wave (16 lanes) per candidate; each lane holds d/32
+//           rotate-half pairs of the key, rotates them (RoPE row of the
+//           candidate's index: exact table row at the start of each batch,
+//           then an angle-step recurrence over consecutive candidates) and
+//           dots them with the G rotated query heads; 16-lane butterflies
+//           give the G logits;
+//   select: two-level tournament: every wave runs up to k rounds of
+//           wavefront arg-max (DPP max, then the lowest index holding it)
+//           over its contiguous slice of candidates; wave 0 merges the
+//           per-wave lists the same way (top-p: until the running softmax mass
+//           reaches p, at most cap) and compacts the kept positions in
+//           ascending order with ballots;
+//   update: block max over the unselected logits -> rescale -> exp ->
+//           denominators; the values are folded in on the next pass, each
+//           lane owning d/64 output dims of every head.
 #include "hti_device.h"
 #include "hti_internal.h"
+#include "hti_trav_common.h"
 
 namespace hti {
 
 namespace {
 
-constexpr int NT = 256;
-constexpr int NW = NT / kWave;
-constexpr int NQ = NT / 16;     // quarter-waves per block
+constexpr int kVStageBytes = 72 * 1024;   // LDS for one level's value rows (decode)
 
-template <int G>
+template <int G, int NWV>
 struct Smem {
-    float z[G * kMaxCand];       // per-head logits, then probabilities
+    float z[kMaxCand * G];       // [candidate][head]: logits, then probabilities
     float s[kMaxCand];           // group scores
-    uint8_t flag[kMaxCand];      // 1 = kept (selected)
-    float qraw[G * HTI_MAX_LEVELS * 0 + G * 128];
+    uint8_t flag[kMaxCand];      // 1 = kept (not an entry)
+    float qraw[G * 128];
     float q[G * 128];            // rotated query heads
     int sel[2][kMaxSel];
     int nsel[2];
     float M[G], l[G], alpha[G];
-    float red[NW * G];
+    float red[NWV * G];
+    float wl_v[NWV][kMaxSel];    // per-wave selection lists (score, index)
+    int wl_i[NWV][kMaxSel];
+    int wl_n[NWV];
+    float gden;
+    int64_t n[HTI_MAX_LEVELS + 1];
 };
+
 
 } // namespace
 
-template <typename T, int D, int G, bool PREFILL>
-__global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
+template <typename T, int D, int G, bool PREFILL, int NWV, bool STAGE>
+__global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a)
 {
-    constexpr int PPL = D / 32;   // rotate-half pairs per lane when scoring
-    constexpr int DPL = D / 64;   // output dims per lane when accumulating
-    __shared__ Smem<G> sm;
+    constexpr int NT = NWV * 64;
+    constexpr int NQ = NT / 16;                       // quarter-waves (16-lane rows)
+    constexpr int PPL = D / 32;                       // rotate-half pairs per lane
+    constexpr int DPL = D / 64;                       // output dims per lane
+    using KR = typename Raw<T, PPL>::type;
+    using VR = typename Raw<T, DPL>::type;
+    constexpr int KRW = sizeof(KR) / 4 > 0 ? (int)sizeof(KR) / 4 : 1;
+    constexpr int VRW = sizeof(VR) / 4 > 0 ? (int)sizeof(VR) / 4 : 1;
+    // register budget of the in-flight batches: decode keeps a whole level in
+    // flight; prefill keeps them small so that many units share a CU
+    constexpr int KB = (STAGE ? 40 : 24) / (2 * KRW); // key rows per quarter per batch
+    constexpr int VB = 16 / VRW;                      // value rows per wave per batch
+    constexpr int RB = D * (int)sizeof(T);            // bytes of one row
+    constexpr int LPR = RB / 16;                      // lanes per row in a 16-byte gather
+    constexpr int RPI = 64 / LPR;                     // rows per wave gather
+    constexpr int VROWS = STAGE ? kVStageBytes / RB : 1;
+    constexpr int SPL = ceil_div(kMaxCand, 64 * NWV); // selection scores per lane
+    constexpr int MSL = ceil_div(NWV * kMaxSel, 64);  // merge slots per lane
+    __shared__ Smem<G, NWV> sm;
+    extern __shared__ __attribute__((aligned(16))) unsigned char hti_dyn_lds[];
+    T *vst = reinterpret_cast<T *>(hti_dyn_lds);
 
     const TreeArgs &t = a.t;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -73,12 +110,16 @@ __global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
     const int64_t bh = (int64_t)bi * t.Hkv + g;
     const int b = t.b, levels = t.levels, R = t.R;
     const int64_t L = t.len[bi];
+    const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
 
-    int64_t n[HTI_MAX_LEVELS + 1];
-    n[0] = L;
-    for (int l = 1; l <= levels; ++l) n[l] = n[l - 1] / b;
-
-    // load the G query heads of this group (un-rotated)
+    if (tid == 0) {
+        int64_t n = L;
+        sm.n[0] = n;
+        for (int l = 1; l <= levels; ++l) {
+            n /= b;
+            sm.n[l] = n;
+        }
+    }
     const T *qp = (const T *)a.q + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
     for (int i = tid; i < G * D; i += NT) {
         float v;
@@ -88,8 +129,18 @@ __global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
     if (tid < G) {
         sm.M[tid] = -INFINITY;
         sm.l[tid] = 0.f;
+        sm.alpha[tid] = 1.f;
     }
     if (tid == 0) sm.nsel[0] = 0;
+
+    // angle step of one position for this lane's pairs (RoPE table row 1)
+    float st_c[PPL], st_s[PPL];
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        const float2 cs = t.rope[(D / 2) + sub * PPL + e];
+        st_c[e] = cs.x;
+        st_s[e] = cs.y;
+    }
 
     float acc[G][DPL];
 #pragma unroll
@@ -98,97 +149,122 @@ __global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
         for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
     __syncthreads();
 
-    // rotate every query head to RoPE position `pos` (into sm.q)
-    auto rotate_query = [&](int64_t pos) {
-        const float2 *rp = t.rope + pos * (D / 2);
-        for (int i = tid; i < G * (D / 2); i += NT) {
-            const int h = i / (D / 2), j = i % (D / 2);
-            const float2 cs = rp[j];
-            const float x0 = sm.qraw[h * D + j], x1 = sm.qraw[h * D + j + D / 2];
-            sm.q[h * D + j] = x0 * cs.x - x1 * cs.y;
-            sm.q[h * D + j + D / 2] = x0 * cs.y + x1 * cs.x;
+    const T *kc = (const T *)t.kc + bh * t.ncap[0] * D;
+    const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
+
+    // value row of candidate i of a stage (token chunk offset ch, or level)
+    struct StageRef {
+        bool tok;
+        int lvl;
+        int64_t ch;
+        Cands c;
+    };
+    auto val_row = [&](const StageRef &sr, int i) __attribute__((always_inline)) -> const T * {
+        if (sr.tok) return vc + sr.c.id((int)(sr.ch + i)) * D;
+        return (const T *)t.lv[sr.lvl - 1] + (bh * t.ncap[sr.lvl] + sr.c.id(i)) * D;
+    };
+
+    auto rescale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float al = sm.alpha[h];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
+        }
+    };
+    auto add_entry = [&](int i, const float *v) __attribute__((always_inline)) {
+        const float *pz = &sm.z[i * G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = pz[h];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] += p * v[e];
         }
     };
 
-    // score candidates [0, m) whose key for reference j is keyptr(i, j),
-    // RoPE position pos0 + i; writes sm.s (group score) and sm.z (per head)
-    auto score = [&](int m, int nref, int64_t pos0, auto keyptr) {
-        float qa[G][PPL], qb[G][PPL];
+    // ---- values through registers (prefill): entries of a finished stage
+    int pend_m = 0;
+    bool pend_flags = false;
+    StageRef pend{false, 0, 0, {nullptr, 0, b, 0, 0, true}};
+    auto fold_pending = [&]() __attribute__((always_inline)) {
+        if (pend_m == 0) return;
+        rescale();
+        for (int u0 = 0; wave + NWV * u0 < pend_m; u0 += VB) {
+            VR vr[VB];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < PPL; ++e) {
-                qa[h][e] = sm.q[h * D + sub * PPL + e];
-                qb[h][e] = sm.q[h * D + D / 2 + sub * PPL + e];
+            for (int u = 0; u < VB; ++u) {
+                const int i = wave + NWV * (u0 + u);
+                if (i < pend_m && !(pend_flags && sm.flag[i]))
+                    vr[u] = *reinterpret_cast<const VR *>(val_row(pend, i) + lane * DPL);
             }
-        for (int i = quarter; i < m; i += NQ) {
-            const float2 *rp = t.rope + (pos0 + i) * (D / 2) + sub * PPL;
-            float cs_c[PPL], cs_s[PPL];
 #pragma unroll
-            for (int e = 0; e < PPL; ++e) {
-                const float2 cs = rp[e];
-                cs_c[e] = cs.x;
-                cs_s[e] = cs.y;
-            }
-            float best = -INFINITY;
-            float zb[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) zb[h] = 0.f;
-            for (int j = 0; j < nref; ++j) {
-                const T *kp = keyptr(i, j);
-                float k0[PPL], k1[PPL];
-                load_vec<T, PPL>(kp + sub * PPL, k0);
-                load_vec<T, PPL>(kp + D / 2 + sub * PPL, k1);
-                float z[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) z[h] = 0.f;
-#pragma unroll
-                for (int e = 0; e < PPL; ++e) {
-                    const float r0 = k0[e] * cs_c[e] - k1[e] * cs_s[e];
-                    const float r1 = k0[e] * cs_s[e] + k1[e] * cs_c[e];
-#pragma unroll
-                    for (int h = 0; h < G; ++h) z[h] += qa[h][e] * r0 + qb[h][e] * r1;
-                }
-                float gs = 0.f;
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    z[h] = group_sum<16>(z[h]) * t.scale;
-                    gs += z[h];
-                }
-                gs = gs / (float)G;
-                if (gs > best) {
-                    best = gs;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) zb[h] = z[h];
+            for (int u = 0; u < VB; ++u) {
+                const int i = wave + NWV * (u0 + u);
+                if (i < pend_m && !(pend_flags && sm.flag[i])) {
+                    float v[DPL];
+                    cvt(vr[u], v);
+                    add_entry(i, v);
                 }
             }
-            if (sub == 0) {
-                sm.s[i] = best;
+        }
+        pend_m = 0;
+    };
+
+    // ---- values through LDS (decode): rows [r0, r0 + nrows) of a stage
+    constexpr int SIPW = ceil_div(VROWS, RPI * NWV);   // gathers per wave for a full stage
+    auto stage_values = [&](const StageRef &sr, int r0, int nrows) __attribute__((always_inline)) {
+        const int ninst = (nrows + RPI - 1) / RPI;
+        const T *src[SIPW];
 #pragma unroll
-                for (int h = 0; h < G; ++h) sm.z[h * kMaxCand + i] = zb[h];
-            }
+        for (int u = 0; u < SIPW; ++u) {
+            const int row = (wave + u * NWV) * RPI + lane / LPR;
+            src[u] = (row < nrows) ? val_row(sr, r0 + row) + (lane % LPR) * (16 / (int)sizeof(T))
+                                   : nullptr;
+        }
+#pragma unroll
+        for (int u = 0; u < SIPW; ++u) {
+            const int ins = wave + u * NWV;
+            if (ins < ninst && src[u] != nullptr) gather16_to_lds(src[u], vst + (size_t)ins * RPI * D);
+        }
+    };
+    // kept candidates carry probability 0, so every staged row is folded in
+    // without a branch
+    auto fold_staged = [&](int r0, int nrows) __attribute__((always_inline)) {
+        int i = r0 + wave;
+        for (; i + 3 * NWV < r0 + nrows; i += 4 * NWV) {
+            float v[4][DPL];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                load_vec<T, DPL>(vst + (size_t)(i + u * NWV - r0) * D + lane * DPL, v[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) add_entry(i + u * NWV, v[u]);
+        }
+        for (; i < r0 + nrows; i += NWV) {
+            float v[DPL];
+            load_vec<T, DPL>(vst + (size_t)(i - r0) * D + lane * DPL, v);
+            add_entry(i, v);
         }
     };
 
-    // online-softmax update with the candidates of [0, m) whose flag is 0;
-    // value of candidate i at valptr(i)
-    auto accumulate = [&](int m, auto valptr) {
+    // softmax update for the entries of a stage (flag 0): new max, rescale
+    // factor, probabilities written over the logits, denominators
+    auto softmax_update = [&](int m, bool use_flags) __attribute__((always_inline)) {
         float lm[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lm[h] = -INFINITY;
         for (int i = tid; i < m; i += NT)
-            if (!sm.flag[i])
+            if (!(use_flags && sm.flag[i]))
 #pragma unroll
-                for (int h = 0; h < G; ++h) lm[h] = fmaxf(lm[h], sm.z[h * kMaxCand + i]);
+                for (int h = 0; h < G; ++h) lm[h] = fmaxf(lm[h], sm.z[i * G + h]);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            lm[h] = group_max<kWave>(lm[h]);
+            lm[h] = wave_max(lm[h]);
             if (lane == 0) sm.red[wave * G + h] = lm[h];
         }
         __syncthreads();
         if (tid < G) {
             float mm = sm.red[tid];
-            for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sm.red[w * G + tid]);
+            for (int w = 1; w < NWV; ++w) mm = fmaxf(mm, sm.red[w * G + tid]);
             const float Mo = sm.M[tid];
             const float Mn = fmaxf(Mo, mm);
             sm.alpha[tid] = (Mn == -INFINITY) ? 1.f : expf(Mo - Mn);
@@ -199,212 +275,386 @@ __global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
 #pragma unroll
         for (int h = 0; h < G; ++h) ls[h] = 0.f;
         for (int i = tid; i < m; i += NT) {
-            const bool kept = sm.flag[i];
+            const bool kept = use_flags && sm.flag[i];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float pz = kept ? 0.f : expf(sm.z[h * kMaxCand + i] - sm.M[h]);
-                sm.z[h * kMaxCand + i] = pz;
+                const float pz = kept ? 0.f : expf(sm.z[i * G + h] - sm.M[h]);
+                sm.z[i * G + h] = pz;
                 ls[h] += pz;
             }
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            ls[h] = group_sum<kWave>(ls[h]);
+            ls[h] = wave_sum(ls[h]);
             if (lane == 0) sm.red[wave * G + h] = ls[h];
         }
         __syncthreads();
         if (tid < G) {
             float sum = 0.f;
-            for (int w = 0; w < NW; ++w) sum += sm.red[w * G + tid];
+            for (int w = 0; w < NWV; ++w) sum += sm.red[w * G + tid];
             sm.l[tid] = sm.l[tid] * sm.alpha[tid] + sum;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float al = sm.alpha[h];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
-        }
-        for (int i = wave; i < m; i += NW) {
-            if (sm.flag[i]) continue;                       // wave-uniform
-            const T *vp = valptr(i);
-            float v[DPL];
-            load_vec<T, DPL>(vp + lane * DPL, v);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float pz = sm.z[h * kMaxCand + i];
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) acc[h][e] += pz * v[e];
-            }
         }
         __syncthreads();
     };
 
-    auto write_sel = [&](int lvl, int buf) {
+    auto write_sel = [&](int lvl, int buf) __attribute__((always_inline)) {
         if (!a.sel) return;
         const int nsel = sm.nsel[buf];
         int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
         for (int r = tid; r < a.sel_stride; r += NT) o[r] = (r < nsel) ? sm.sel[buf][r] : -1;
     };
 
+    // selection over candidates [0, m) (scores in sm.s): sets sm.flag for the
+    // kept ones and writes their ids, ascending, to sm.sel[nxt].  Order: higher
+    // score first, lower index on ties.  Every wave ranks the candidates of
+    // its contiguous slice against the slice (the global top set lies in the
+    // union of the slices' top sets); wave 0 ranks that union.
+    auto better = [](float va, int ia, float vb, int ib) __attribute__((always_inline)) {
+        return va > vb || (va == vb && ia < ib);
+    };
+    auto select = [&](int m, const Cands &cs, int nxt) __attribute__((always_inline)) {
+        {
+            const int cpw = (m + NWV - 1) / NWV;
+            const int w0 = min(m, wave * cpw), w1 = min(m, w0 + cpw);
+#pragma unroll
+            for (int r = 0; r < SPL; ++r) {
+                const int i = w0 + lane + 64 * r;
+                if (r * 64 >= w1 - w0) break;
+                const float si = (i < w1) ? sm.s[i] : -INFINITY;
+                int rank = 0;
+                int j = w0;
+                for (; j + 4 <= w1; j += 4) {
+                    const float4 v4 = *reinterpret_cast<const float4 *>(&sm.s[j]);
+                    rank += better(v4.x, j, si, i) + better(v4.y, j + 1, si, i) +
+                            better(v4.z, j + 2, si, i) + better(v4.w, j + 3, si, i);
+                }
+                for (; j < w1; ++j) rank += better(sm.s[j], j, si, i);
+                if (i < w1 && rank < keff) {
+                    sm.wl_v[wave][rank] = si;
+                    sm.wl_i[wave][rank] = i;
+                }
+            }
+            if (lane == 0) sm.wl_n[wave] = min(keff, w1 - w0);
+        }
+        __syncthreads();
+        float gmax = 0.f;
+        if (a.mode == HTI_TOPP) {
+            // softmax of the group scores over all candidates
+            gmax = -INFINITY;
+            for (int w = 0; w < NWV; ++w)
+                if (sm.wl_n[w] > 0) gmax = fmaxf(gmax, sm.wl_v[w][0]);
+            float ld = 0.f;
+            for (int i = tid; i < m; i += NT) ld += expf(sm.s[i] - gmax);
+            ld = wave_sum(ld);
+            if (lane == 0) sm.red[wave * G] = ld;
+            __syncthreads();
+            if (tid == 0) {
+                float den = 0.f;
+                for (int w = 0; w < NWV; ++w) den += sm.red[w * G];
+                sm.gden = den;
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+            // rank every listed entry against the union of the lists
+            int myrank[MSL];
+            float myv[MSL];
+            int myi[MSL];
+#pragma unroll
+            for (int q = 0; q < MSL; ++q) {
+                const int slot = lane + 64 * q;
+                const int w = slot / kMaxSel, r = slot % kMaxSel;
+                const bool ok = (w < NWV) && (r < sm.wl_n[w]);
+                myv[q] = ok ? sm.wl_v[w][r] : -INFINITY;
+                myi[q] = ok ? sm.wl_i[w][r] : -1;
+                myrank[q] = 0;
+            }
+            for (int w = 0; w < NWV; ++w) {
+                const int nw = sm.wl_n[w];
+                for (int r = 0; r < nw; ++r) {
+                    const float v = sm.wl_v[w][r];
+                    const int ix = sm.wl_i[w][r];
+#pragma unroll
+                    for (int q = 0; q < MSL; ++q) myrank[q] += better(v, ix, myv[q], myi[q]);
+                }
+            }
+            int nsel = min(keff, m);
+#pragma unroll
+            for (int q = 0; q < MSL; ++q)
+                if (myi[q] < 0) myrank[q] = 0x7fffffff;      // empty slot
+            if (a.mode == HTI_TOPP) {
+                // shortest prefix of the sorted softmax whose running sum reaches p
+                float *sp = sm.wl_v[NWV - 1];            // reuse: sorted probabilities
+#pragma unroll
+                for (int q = 0; q < MSL; ++q)
+                    if (myrank[q] < nsel) sp[myrank[q]] = expf(myv[q] - gmax) / sm.gden;
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                int ns = nsel;
+                if (lane == 0) {
+                    float cum = 0.f;
+                    for (int r = 0; r < nsel; ++r) {
+                        cum += sp[r];
+                        if (cum >= a.p) {
+                            ns = r + 1;
+                            break;
+                        }
+                    }
+                }
+                nsel = __builtin_amdgcn_readfirstlane(ns);
+            }
+            // kept entries: their indices by rank, then ascending positions
+            int *byrank = sm.wl_i[NWV - 1];              // reuse as scratch (rank -> index)
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < MSL; ++q)
+                if (myrank[q] < nsel) byrank[myrank[q]] = myi[q];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            if (lane < nsel) {
+                const int ix = byrank[lane];
+                int pos = 0;
+                for (int r = 0; r < nsel; ++r) pos += byrank[r] < ix;
+                sm.sel[nxt][pos] = (int)cs.id(ix);
+                sm.flag[ix] = 1;
+            }
+            if (lane == 0) sm.nsel[nxt] = nsel;
+        }
+        __syncthreads();
+    };
+
     int cur = 0;
-    for (int lvl = levels; lvl >= 1; --lvl) {
-        const int nprev = sm.nsel[cur];
-        const bool top = (lvl == levels);
-        const int64_t orph0 = top ? 0 : (int64_t)b * n[lvl + 1];
-        const int m = (int)(top ? n[lvl] : (int64_t)nprev * b + (n[lvl] - orph0));
-        const int *selp = sm.sel[cur];
-        auto cand = [&](int i) -> int64_t {
-            if (top) return i;
-            if (i < nprev * b) return (int64_t)selp[i / b] * b + (i % b);
-            return orph0 + (i - nprev * b);
-        };
+    int lvl = levels;
+    int64_t ch = 0;                 // token chunk offset
+    int64_t qpos_tok = 0;
+    while (true) {
+        const bool tok = (lvl == 0);
+        const int nprev = (lvl == levels) ? 0 : sm.nsel[cur];
+        Cands cs;
+        cs.selp = sm.sel[cur];
+        cs.nprev = nprev;
+        cs.b = b;
+        cs.binv = a.binv;
+        cs.top = (lvl == levels);
+        cs.orph0 = cs.top ? 0 : (int64_t)b * sm.n[lvl + 1];
+        const int64_t mfull = cs.top ? sm.n[lvl] : (int64_t)nprev * b + (sm.n[lvl] - cs.orph0);
         const int nxt = cur ^ 1;
-        const bool take_all = (a.mode == HTI_TOPK) ? (m <= a.k) : (m <= 1);
-        if (take_all) {
-            for (int i = tid; i < m; i += NT) sm.sel[nxt][i] = (int)cand(i);
+
+        int m;
+        bool take_all = false, pre = false;
+        int64_t qpos;
+        if (!tok) {
+            m = (int)mfull;
+            take_all = (a.mode == HTI_TOPK) ? (m <= a.k) : (m <= 1);
+            pre = PREFILL && cs.top && a.top_s != nullptr;
+            qpos = m;
+        } else {
+            if (ch == 0) {
+                if (PREFILL) {
+                    qpos_tok = mfull + qi;
+                } else {
+                    // the query token (L - 1) is a candidate iff it is an
+                    // orphan token or its level-1 parent was kept
+                    bool in = (levels == 0) || (L - 1 >= cs.orph0);
+                    if (!in)
+                        for (int r = 0; r < nprev; ++r) in |= ((int64_t)cs.selp[r] == (L - 1) / b);
+                    qpos_tok = mfull - (in ? 1 : 0);
+                }
+            }
+            m = (int)((mfull - ch) < kMaxCand ? (mfull - ch) : kMaxCand);
+            qpos = qpos_tok;
+        }
+        const bool entries = tok ? (m > 0) : !take_all;
+        const bool score_now = entries && !pre;
+        const int nref = tok ? 1 : R;
+        const StageRef sref{tok, lvl, ch, cs};
+
+        if (score_now && (!tok || ch == 0)) {
+            const float2 *rp = t.rope + qpos * (D / 2);
+            for (int i = tid; i < G * (D / 2); i += NT) {
+                const int h = i / (D / 2), j = i % (D / 2);
+                const float2 c2 = rp[j];
+                const float x0 = sm.qraw[h * D + j], x1 = sm.qraw[h * D + j + D / 2];
+                sm.q[h * D + j] = x0 * c2.x - x1 * c2.y;
+                sm.q[h * D + j + D / 2] = x0 * c2.y + x1 * c2.x;
+            }
+        }
+        const int cpq = (m + NQ - 1) / NQ;
+        const int c_beg = min(m, quarter * cpq);
+        const int c_end = min(m, c_beg + cpq);
+        const int nitems = score_now ? (c_end - c_beg) * nref : 0;
+        const int KBR = (KB / nref) * nref;
+        const T *lk = tok ? nullptr : (const T *)t.lk[lvl - 1];
+        const int64_t ncap = tok ? 0 : t.ncap[lvl];
+        const int64_t pos0 = tok ? ch : 0;
+        auto key_row = [&](int ci, int j) __attribute__((always_inline)) -> const T * {
+            if (tok) return kc + cs.id((int)(ch + ci)) * D;
+            return lk + ((bh * ncap + cs.id(ci)) * R + j) * D;
+        };
+
+        KR k0[KB], k1[KB];
+        float rb_c[PPL], rb_s[PPL];
+        auto issue_keys = [&](int item0, int nb) __attribute__((always_inline)) {
+            int ci = c_beg + item0 / nref, j = 0;
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                if (u < nb) {
+                    const T *kp = key_row(ci, j);
+                    k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
+                    k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
+                    if (++j == nref) {
+                        j = 0;
+                        ++ci;
+                    }
+                }
+            }
+            if (nb > 0) {
+                const float2 *rp = t.rope + (pos0 + c_beg + item0 / nref) * (D / 2) + sub * PPL;
+#pragma unroll
+                for (int e = 0; e < PPL; ++e) {
+                    const float2 c2 = rp[e];
+                    rb_c[e] = c2.x;
+                    rb_s[e] = c2.y;
+                }
+            }
+        };
+        issue_keys(0, min(nitems, KBR));
+        const int vfirst = min(m, VROWS);
+        if (STAGE && entries) stage_values(sref, 0, vfirst);
+        if (!STAGE) fold_pending();
+        __syncthreads();
+
+        if (!tok && take_all) {
+            for (int i = tid; i < m; i += NT) sm.sel[nxt][i] = (int)cs.id(i);
             if (tid == 0) sm.nsel[nxt] = m;
             __syncthreads();
             write_sel(lvl, nxt);
             cur = nxt;
+            --lvl;
             continue;
         }
+        if (tok && m <= 0) break;
 
-        rotate_query(m);
-        for (int i = tid; i < m; i += NT) sm.flag[i] = 0;
-        __syncthreads();
-
-        const T *lk = (const T *)t.lk[lvl - 1];
-        const int64_t ncap = t.ncap[lvl];
-        if (PREFILL && top && a.top_s) {
+        // ---- score
+        if (pre) {
             const int64_t srow = (((int64_t)bi * a.Nq + qi) * t.Hkv + g) * a.ntop_stride;
             for (int i = tid; i < m; i += NT) sm.s[i] = a.top_s[srow + i];
             for (int i = tid; i < G * m; i += NT) {
                 const int h = i / m, c = i % m;
-                sm.z[h * kMaxCand + c] =
+                sm.z[c * G + h] =
                     a.top_z[(((int64_t)bi * a.Nq + qi) * t.Hq + g * G + h) * a.ntop_stride + c];
             }
         } else {
-            score(m, R, 0, [&](int i, int j) -> const T * {
-                return lk + ((bh * ncap + cand(i)) * R + j) * D;
-            });
-        }
-        __syncthreads();
-
-        // selection by wave 0: rounds of wavefront arg-max (ties -> lower index)
-        if (wave == 0) {
-            constexpr int RPL = kMaxCand / kWave;
-            float v[RPL];
-            uint32_t kept_bits = 0;
+            float qa[G][PPL], qb[G][PPL];
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-                const int i = lane + kWave * r;
-                v[r] = (i < m) ? sm.s[i] : -INFINITY;
-            }
-            float mx = 0.f, den = 1.f;
-            int rounds;
-            if (a.mode == HTI_TOPK) {
-                rounds = a.k;
-            } else {
-                rounds = a.cap < m ? a.cap : m;
-                float lmx = -INFINITY;
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int r = 0; r < RPL; ++r) lmx = fmaxf(lmx, v[r]);
-                mx = group_max<kWave>(lmx);
-                float ld = 0.f;
+                for (int e = 0; e < PPL; ++e) {
+                    qa[h][e] = sm.q[h * D + sub * PPL + e];
+                    qb[h][e] = sm.q[h * D + D / 2 + sub * PPL + e];
+                }
+            for (int it0 = 0; it0 < nitems; it0 += KBR) {
+                const int nb = min(nitems - it0, KBR);
+                if (it0 > 0) issue_keys(it0, nb);
+                int ci = c_beg + it0 / nref, j = 0;
+                float best = -INFINITY;
+                float zb[G];
 #pragma unroll
-                for (int r = 0; r < RPL; ++r)
-                    if (lane + kWave * r < m) ld += expf(v[r] - mx);
-                den = group_sum<kWave>(ld);
-            }
-            float cum = 0.f;
-            for (int r = 0; r < rounds; ++r) {
-                float bv = -INFINITY;
-                int bix = 0x7fffffff;
+                for (int h = 0; h < G; ++h) zb[h] = 0.f;
+                float cc[PPL], ss[PPL];
 #pragma unroll
-                for (int rr = 0; rr < RPL; ++rr)
-                    if (v[rr] > bv) {
-                        bv = v[rr];
-                        bix = lane + kWave * rr;
-                    }
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) {
-                    const float ov = __shfl_xor(bv, off, kWave);
-                    const int oi = __shfl_xor(bix, off, kWave);
-                    if (ov > bv || (ov == bv && oi < bix)) {
-                        bv = ov;
-                        bix = oi;
-                    }
+                for (int e = 0; e < PPL; ++e) {
+                    cc[e] = rb_c[e];
+                    ss[e] = rb_s[e];
                 }
 #pragma unroll
-                for (int rr = 0; rr < RPL; ++rr)
-                    if (lane + kWave * rr == bix) {
-                        v[rr] = -INFINITY;
-                        kept_bits |= 1u << rr;
+                for (int u = 0; u < KB; ++u) {
+                    if (u < nb) {
+                        float x0[PPL], x1[PPL];
+                        cvt(k0[u], x0);
+                        cvt(k1[u], x1);
+                        float z[G];
+#pragma unroll
+                        for (int h = 0; h < G; ++h) z[h] = 0.f;
+#pragma unroll
+                        for (int e = 0; e < PPL; ++e) {
+                            const float r0 = x0[e] * cc[e] - x1[e] * ss[e];
+                            const float r1 = x0[e] * ss[e] + x1[e] * cc[e];
+#pragma unroll
+                            for (int h = 0; h < G; ++h) z[h] += qa[h][e] * r0 + qb[h][e] * r1;
+                        }
+                        float gs = 0.f;
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            z[h] = sum16(z[h]) * t.scale;
+                            gs += z[h];
+                        }
+                        gs = gs / (float)G;
+                        if (gs > best) {
+                            best = gs;
+#pragma unroll
+                            for (int h = 0; h < G; ++h) zb[h] = z[h];
+                        }
+                        if (++j == nref) {
+                            if (sub == 0) {
+                                sm.s[ci] = best;
+#pragma unroll
+                                for (int h = 0; h < G; ++h) sm.z[ci * G + h] = zb[h];
+                            }
+                            j = 0;
+                            ++ci;
+                            best = -INFINITY;
+#pragma unroll
+                            for (int e = 0; e < PPL; ++e) {   // advance one position
+                                const float c2 = cc[e] * st_c[e] - ss[e] * st_s[e];
+                                const float s2 = cc[e] * st_s[e] + ss[e] * st_c[e];
+                                cc[e] = c2;
+                                ss[e] = s2;
+                            }
+                        }
                     }
-                if (a.mode == HTI_TOPP) {
-                    cum += expf(bv - mx) / den;
-                    if (cum >= a.p) break;
                 }
             }
-            // ascending compaction of the kept positions
-            int base = 0;
-#pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-                if (r * kWave >= m) break;
-                const int i = r * kWave + lane;
-                const bool f = (kept_bits >> r) & 1u;
-                const uint64_t mask = __ballot(f);
-                const int off = __popcll(mask & ((1ull << lane) - 1ull));
-                if (f) sm.sel[nxt][base + off] = (int)cand(i);
-                if (i < m) sm.flag[i] = f ? 1 : 0;
-                base += __popcll(mask);
-            }
-            if (lane == 0) sm.nsel[nxt] = base;
         }
+        for (int i = tid; i < m; i += NT) sm.flag[i] = 0;
         __syncthreads();
 
-        const T *lv = (const T *)t.lv[lvl - 1];
-        accumulate(m, [&](int i) -> const T * { return lv + (bh * ncap + cand(i)) * D; });
+        if (!tok) select(m, cs, nxt);
+        softmax_update(m, !tok);
+
+        if (STAGE) {
+            rescale();
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            fold_staged(0, vfirst);
+            for (int r0 = VROWS; r0 < m; r0 += VROWS) {
+                const int nr = min(VROWS, m - r0);
+                __syncthreads();
+                stage_values(sref, r0, nr);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                fold_staged(r0, nr);
+            }
+            __syncthreads();
+        } else {
+            pend_m = m;
+            pend_flags = !tok;
+            pend = sref;
+        }
+
+        if (tok) {
+            ch += kMaxCand;
+            if (ch >= mfull) break;
+            continue;
+        }
         write_sel(lvl, nxt);
         cur = nxt;
+        --lvl;
     }
-
-    // token level: children of the kept level-1 nodes, then the orphan tokens
-    {
-        const int nsel1 = levels > 0 ? sm.nsel[cur] : 0;
-        const int *selp = sm.sel[cur];
-        const int64_t orph0 = levels > 0 ? (int64_t)b * n[1] : 0;
-        const int64_t m0 = levels > 0 ? (int64_t)nsel1 * b + (L - orph0) : L;
-        auto cand0 = [&](int64_t i) -> int64_t {
-            if (levels == 0) return i;
-            if (i < (int64_t)nsel1 * b) return (int64_t)selp[i / b] * b + (i % b);
-            return orph0 + (i - (int64_t)nsel1 * b);
-        };
-        int64_t qpos;
-        if (PREFILL) {
-            qpos = m0 + qi;
-        } else {
-            // the query token (L - 1) is a candidate iff it is an orphan token
-            // or its level-1 parent was kept
-            bool in = (levels == 0) || (L - 1 >= orph0);
-            if (!in)
-                for (int r = 0; r < nsel1; ++r) in |= ((int64_t)selp[r] == (L - 1) / b);
-            qpos = m0 - (in ? 1 : 0);
-        }
-        rotate_query(qpos);
-        __syncthreads();
-        const T *kc = (const T *)t.kc + bh * t.ncap[0] * D;
-        const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
-        for (int64_t c0 = 0; c0 < m0; c0 += kMaxCand) {
-            const int mc = (int)((m0 - c0) < kMaxCand ? (m0 - c0) : kMaxCand);
-            for (int i = tid; i < mc; i += NT) sm.flag[i] = 0;
-            score(mc, 1, c0, [&](int i, int) -> const T * { return kc + cand0(c0 + i) * D; });
-            __syncthreads();
-            accumulate(mc, [&](int i) -> const T * { return vc + cand0(c0 + i) * D; });
-        }
-    }
+    if (!STAGE) fold_pending();
 
     // combine the per-wave partial sums (reusing the logit buffer)
+    __syncthreads();
     float *red = sm.z;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -415,7 +665,7 @@ __global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
     for (int i = tid; i < G * D; i += NT) {
         const int h = i / D, e = i % D;
         float s = 0.f;
-        for (int w = 0; w < NW; ++w) s += red[(w * G + h) * D + e];
+        for (int w = 0; w < NWV; ++w) s += red[(w * G + h) * D + e];
         if (PREFILL) {
             a.part_acc[(row + h) * D + e] = s;
         } else {
@@ -433,17 +683,35 @@ __global__ __launch_bounds__(NT) void k_traverse(TravArgs a)
     }
 }
 
+// decode: 8 waves per unit, value rows staged in LDS; prefill: 2 waves per
+// unit, values through registers
+template <typename T, int D, int G, bool PF>
+static hipError_t trav_launch(const TravArgs &a, int64_t units, hipStream_t s)
+{
+    constexpr int NWV = PF ? 2 : 8;
+    constexpr bool STAGE = !PF;
+    auto kern = k_traverse<T, D, G, PF, NWV, STAGE>;
+    const size_t dyn = STAGE ? kVStageBytes : 0;
+    static bool attr_set = false;
+    if (!attr_set && dyn > 0) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(NWV * 64), dyn, s, a);
+    return hipGetLastError();
+}
+
 template <typename T, int D, bool PF>
 static hipError_t trav_g(const TravArgs &a, int64_t units, hipStream_t s)
 {
-    dim3 grid((unsigned)units), block(NT);
     switch (a.t.G) {
-    case 1: hipLaunchKernelGGL((k_traverse<T, D, 1, PF>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_traverse<T, D, 2, PF>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_traverse<T, D, 4, PF>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_traverse<T, D, 8, PF>), grid, block, 0, s, a); break;
+    case 1: return trav_launch<T, D, 1, PF>(a, units, s);
+    case 2: return trav_launch<T, D, 2, PF>(a, units, s);
+    case 4: return trav_launch<T, D, 4, PF>(a, units, s);
+    default: return trav_launch<T, D, 8, PF>(a, units, s);
     }
-    return hipGetLastError();
 }
 
 template <typename T, int D>

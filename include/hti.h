@@ -50,6 +50,7 @@ extern "C" {
 #define HTI_MAX_SELECT 32   /* largest k (top-k) or cap (top-p) */
 #define HTI_MAX_CAND 1024   /* largest candidate list of a summary level */
 #define HTI_MAX_R 8         /* reference queries per KV head */
+#define HTI_DECODE_MAX_SPLIT 16  /* most workgroups one decode unit is split over */
 
 typedef enum {
     HTI_OK = 0,
@@ -150,6 +151,12 @@ hti_status hti_tree_append(const hti_tree *tree, const void *k_new, const void *
                            void *stream);
 
 /*
+ * hti_decode_workspace_bytes: size of the workspace hti_sparse_decode uses to
+ * split each (query, KV group) unit over several workgroups.
+ */
+size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t Nq);
+
+/*
  * hti_sparse_decode: attention of Nq query tokens per sequence, each at
  * position len[s] - 1, over that sequence's trees.
  *   q:   [B, Nq, Hq, d] in the cache dtype (un-rotated)
@@ -166,13 +173,20 @@ hti_status hti_tree_append(const hti_tree *tree, const void *k_new, const void *
  * per-head softmax with their pooled key and mean value.  At the token level
  * every candidate enters the softmax exactly.
  * Source: RecSA abstract; ZHA Figure 3 caption (top-p routing).
+ *   ws, ws_bytes: device workspace of hti_decode_workspace_bytes(cfg, sel, Nq)
+ *        bytes, filled with zeros before its first use and then left to the
+ *        library (it keeps per-unit launch counters there).  With a workspace
+ *        each unit is split over up to HTI_DECODE_MAX_SPLIT workgroups that
+ *        cooperate (a cooperative launch); ws = NULL runs one workgroup per
+ *        unit.  One workspace serves one (cfg, Nq) shape and one stream at a
+ *        time: calls that share it must not overlap.
  * Errors additionally: HTI_ERR_CAPACITY if rope_npos is below the positions
  * this cfg/selection can reach, HTI_ERR_UNSUPPORTED if a summary level can
- * exceed HTI_MAX_CAND candidates.
+ * exceed HTI_MAX_CAND candidates, HTI_ERR_WORKSPACE if ws_bytes is too small.
  */
 hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q,
                              int32_t Nq, float *out, float *lse, int32_t *sel_out,
-                             int32_t sel_stride, void *stream);
+                             int32_t sel_stride, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * hti_prefill_workspace_bytes: device workspace hti_sparse_prefill needs.

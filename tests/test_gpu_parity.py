@@ -24,17 +24,17 @@ def _setup(w, Lcap=None, Ls=None):
     return ts, K, V, refs, Ls
 
 
-def _decode(ts, w, q):
+def _decode(ts, w, q, split=True):
     out = torch.empty((w.B, q.shape[1], w.Hq, w.d), dtype=torch.float32, device=DEV)
     lse = torch.empty((w.B, q.shape[1], w.Hq), dtype=torch.float32, device=DEV)
     sel = torch.empty((w.B, q.shape[1], w.Hkv, max(w.levels, 1), kmax_of(w)), dtype=torch.int32,
                       device=DEV)
-    ts.sparse_decode(select_of(w), q.to(DEV).contiguous(), out, lse, sel)
+    ts.sparse_decode(select_of(w), q.to(DEV).contiguous(), out, lse, sel, split=split)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
 
 
-def _check_decode(ts, w, K, V, refs, Ls, q, trees=None, upload=False):
+def _check_decode(ts, w, K, V, refs, Ls, q, trees=None, upload=False, split=True):
     """Decode every query of every sequence/group and accept against the oracle."""
     trees = trees or {}
     for bi in range(w.B):
@@ -47,7 +47,7 @@ def _check_decode(ts, w, K, V, refs, Ls, q, trees=None, upload=False):
                     n = tr.lk[l].shape[0]
                     ts.lvl_k[l][bi, g, :n] = torch.from_numpy(tr.lk[l]).to(ts.lvl_k[l].dtype).to(DEV)
                     ts.lvl_v[l][bi, g, :n] = torch.from_numpy(tr.lv[l]).to(ts.lvl_v[l].dtype).to(DEV)
-    out, lse, sel = _decode(ts, w, q)
+    out, lse, sel = _decode(ts, w, q, split=split)
     nex, emax = 0, 0.0
     for bi in range(w.B):
         for qi in range(q.shape[1]):
@@ -57,7 +57,7 @@ def _check_decode(ts, w, K, V, refs, Ls, q, trees=None, upload=False):
                                  q[bi, qi, hs], out[bi, qi, hs], lse[bi, qi, hs], sel[bi, qi, g])
                 nex += ex
                 emax = max(emax, err)
-    log(f"  {w.name}: units={w.B * q.shape[1] * w.Hkv} exempt={nex} max_err={emax:.2e}")
+    log(f"  {w.name} split={split}: units={w.B * q.shape[1] * w.Hkv} exempt={nex} max_err={emax:.2e}")
     return trees, out, sel
 
 
@@ -91,12 +91,13 @@ def test_build_parity(w):
 
 
 # --------------------------------------------------------------------------- decode
-def test_decode_tiny_workload():
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_tiny_workload(split):
     """The 4096-token fp32 workload at full size: 16 queries, top-k 4."""
     w = W.TINY
     ts, K, V, refs, Ls = _setup(w)
     q = W.gen_queries(w)
-    _check_decode(ts, w, K, V, refs, Ls, q)
+    _check_decode(ts, w, K, V, refs, Ls, q, split=split)
 
 
 DECODE_CASES = [
@@ -120,8 +121,10 @@ def test_decode_parity(w):
     ts, K, V, refs, _ = _setup(w, Lcap=w.L, Ls=Ls)
     q = W.gen_queries(w)
     trees, _, _ = _check_decode(ts, w, K, V, refs, Ls, q)
-    # the same decode on the oracle's own tree (decode kernel in isolation)
+    _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, split=False)
+    # the same decode on the oracle's own tree (decode kernels in isolation)
     _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, upload=True)
+    _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, upload=True, split=False)
 
 
 def test_candidate_capacity_is_enforced():
@@ -137,14 +140,31 @@ def test_candidate_capacity_is_enforced():
     assert ei.value.status == -2
 
 
-def test_decode_is_deterministic():
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_is_deterministic(split):
+    """Repeated launches give bit-identical results (the split path also
+    reuses its workspace across launches)."""
     w = DECODE_CASES[0]
     ts, K, V, refs, Ls = _setup(w)
     q = W.gen_queries(w)
-    a = _decode(ts, w, q)
-    b = _decode(ts, w, q)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    a = _decode(ts, w, q, split=split)
+    for _ in range(3):
+        b = _decode(ts, w, q, split=split)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    ws = ts.decode_workspace(select_of(w), 1)
+    assert int(ws[0:4].view(torch.int32).item()) >= 0
+
+
+def test_split_decode_matches_unsplit():
+    """Both decode paths keep the same nodes and agree on the output."""
+    w = W.DEC128K.replace(name="split_vs_unsplit", L=60000, levels=3, needles=0, B=2, Nq=2)
+    ts, K, V, refs, Ls = _setup(w)
+    q = W.gen_queries(w)
+    o1, l1, s1 = _decode(ts, w, q, split=True)
+    o2, l2, s2 = _decode(ts, w, q, split=False)
+    assert np.array_equal(s1, s2)
+    assert np.abs(o1 - o2).max() < 1e-5 and np.abs(l1 - l2).max() < 1e-5
 
 
 @pytest.mark.parametrize("L,levels", [(1, 2), (5, 2), (31, 1), (32, 1), (33, 3), (1024, 2), (700, 0)])
@@ -155,6 +175,7 @@ def test_decode_edge_lengths(L, levels):
     ts, K, V, refs, Ls = _setup(w)
     q = W.gen_queries(w)
     _check_decode(ts, w, K, V, refs, Ls, q)
+    _check_decode(ts, w, K, V, refs, Ls, q, split=False)
 
 
 def test_dense_equivalence_on_gpu():

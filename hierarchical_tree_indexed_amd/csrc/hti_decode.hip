@@ -12,8 +12,8 @@
 //
 //   * every workgroup derives the level's candidate list (identical in all of
 //     them) and takes a contiguous slice of it: it gathers the slice's keys
-//     (registers) and values (straight into LDS), scores them, and ranks them
-//     inside the slice;
+//     and values into registers, scores the keys and ranks them inside the
+//     slice;
 //   * it publishes its slice's best k (score, index) as 64-bit words carrying
 //     a per-launch tag, written and read with agent-scope atomics, so a word
 //     is valid exactly when its tag matches -- no fences, no counters;
@@ -21,14 +21,15 @@
 //     over the whole slice (the running max may include candidates that turn
 //     out to be kept; any upper bound is a valid reference point);
 //   * every workgroup merges the same W lists into the same kept set, drops
-//     the kept candidates' probabilities and folds its staged values in;
+//     the kept candidates' probabilities and folds its values in;
 //   * the token level is sliced the same way, without an exchange;
-//   * each workgroup leaves its partial state (max, denominator, unnormalised
-//     output per head); the last to finish (an atomic counter) merges them.
+//   * each workgroup publishes its partial state (max, denominator,
+//     unnormalised output per head) the same way, and every workgroup merges
+//     all of them for a slice of the output columns.
 //
-// All workgroups of a launch must be resident together (they wait on each
-// other): the launch is cooperative, and every wait is bounded -- on timeout a
-// flag is raised in the workspace and the missing entries count as absent.
+// The workgroups of a launch wait on each other, so they must be resident
+// together: the grid is kept within one workgroup per compute unit, and every
+// wait is bounded -- on timeout the unit's output is NaN.
 #include <algorithm>
 
 #include "hti_device.h"
@@ -66,7 +67,7 @@ struct DSmem {
     int nkeep;
     int64_t n[HTI_MAX_LEVELS + 1];
     uint32_t tag;
-    int last;
+    int bad;                          // a wait of this workgroup timed out
 };
 
 __device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t idx, float v)
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     constexpr int KRW = sizeof(KR) / 4 > 0 ? (int)sizeof(KR) / 4 : 1;
     constexpr int KB = 40 / (2 * KRW);                 // key rows per quarter per batch
     using VR = typename Raw<T, DPL>::type;
-    constexpr int VBS = 16;                            // value rows per wave held in registers
+    constexpr int VBS = 8;                             // value rows per wave held in registers
     __shared__ DSmem<G> sm;
     extern __shared__ __attribute__((aligned(16))) unsigned char hti_dec_lds[];
 
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
         sm.tag = (ws.epoch[unit] % 0xffffeu) + 1u;
         sm.nsel[0] = 0;
+        sm.bad = 0;
     }
     const T *qp = (const T *)a.q + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
     for (int i = tid; i < G * D; i += DNT) {
@@ -162,6 +164,39 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // Score slice candidates [0, ms) (global index s0 + i, RoPE position
     // pos0 + s0 + i): keys gathered by quarter-waves in batches, best of the
     // nref reference keys kept.  Writes sm.s, sm.z.
+    // one batch of a quarter-wave's keys (items it0.., item = candidate x
+    // reference key) plus the RoPE row of its first candidate
+    auto load_batch = [&](int ms, int s0, int64_t pos0, int nref, auto key_row, int it0,
+                          KR (&k0)[KB], KR (&k1)[KB], float (&rb_c)[PPL],
+                          float (&rb_s)[PPL]) __attribute__((always_inline)) {
+        const int cpq = (ms + DNQ - 1) / DNQ;
+        const int c_beg = min(ms, quarter * cpq);
+        const int c_end = min(ms, c_beg + cpq);
+        const int nitems = (c_end - c_beg) * nref;
+        const int KBR = (KB / nref) * nref;
+        const int nb = min(nitems - it0, KBR);
+        int ci = c_beg + it0 / nref, j = 0;
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+            if (u < nb) {
+                const T *kp = key_row(s0 + ci, j);
+                k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
+                k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
+                if (++j == nref) {
+                    j = 0;
+                    ++ci;
+                }
+            }
+        if (nb > 0) {
+            const float2 *rp = t.rope + (pos0 + s0 + c_beg + it0 / nref) * (D / 2) + sub * PPL;
+#pragma unroll
+            for (int e = 0; e < PPL; ++e) {
+                const float2 c2 = rp[e];
+                rb_c[e] = c2.x;
+                rb_s[e] = c2.y;
+            }
+        }
+    };
     auto score_slice = [&](int ms, int s0, int64_t pos0, int nref, auto key_row,
                            bool keys_issued, KR (&k0)[KB], KR (&k1)[KB], float (&rb_c)[PPL],
                            float (&rb_s)[PPL]) __attribute__((always_inline)) {
@@ -180,27 +215,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
         for (int it0 = 0; it0 < nitems; it0 += KBR) {
             const int nb = min(nitems - it0, KBR);
-            if (it0 > 0 || !keys_issued) {
-                int ci = c_beg + it0 / nref, j = 0;
-#pragma unroll
-                for (int u = 0; u < KB; ++u)
-                    if (u < nb) {
-                        const T *kp = key_row(s0 + ci, j);
-                        k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
-                        k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
-                        if (++j == nref) {
-                            j = 0;
-                            ++ci;
-                        }
-                    }
-                const float2 *rp = t.rope + (pos0 + s0 + c_beg + it0 / nref) * (D / 2) + sub * PPL;
-#pragma unroll
-                for (int e = 0; e < PPL; ++e) {
-                    const float2 c2 = rp[e];
-                    rb_c[e] = c2.x;
-                    rb_s[e] = c2.y;
-                }
-            }
+            if (it0 > 0 || !keys_issued) load_batch(ms, s0, pos0, nref, key_row, it0, k0, k1, rb_c, rb_s);
             int ci = c_beg + it0 / nref, j = 0;
             float best = -INFINITY;
             float zb[G];
@@ -264,11 +279,13 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 
     // value rows of the slice's candidates, wave w owning rows w, w + DNW, ...:
     // the first VBS per wave are loaded with the keys and held in registers
+    // (every load is issued, rows past the slice re-reading its last row, so
+    // that each writes its register unconditionally and none waits on another)
     auto issue_values = [&](int ms, auto val_row, VR (&vr)[VBS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < VBS; ++u) {
-            const int i = wave + DNW * u;
-            if (i < ms) vr[u] = *reinterpret_cast<const VR *>(val_row(i) + lane * DPL);
+            const int i = min(wave + DNW * u, ms - 1);
+            vr[u] = *reinterpret_cast<const VR *>(val_row(i) + lane * DPL);
         }
     };
 
@@ -394,14 +411,17 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             auto val_row = [&](int i) __attribute__((always_inline)) -> const T * {
                 return lv + (bh * ncap + cs.id(s0 + i)) * D;
             };
-            rotate_query(m);
-            VR vr[VBS];
-            issue_values(ms, val_row, vr);
-            for (int i = tid; i < ms; i += DNT) sm.flag[i] = 0;
-            __syncthreads();
+            // gathers first (they depend only on the candidate list), then the
+            // query rotation while they are in flight
             KR k0[KB], k1[KB];
             float rb_c[PPL], rb_s[PPL];
-            score_slice(ms, s0, 0, R, key_row, false, k0, k1, rb_c, rb_s);
+            load_batch(ms, s0, 0, R, key_row, 0, k0, k1, rb_c, rb_s);
+            VR vr[VBS];
+            if (ms > 0) issue_values(ms, val_row, vr);
+            rotate_query(m);
+            for (int i = tid; i < ms; i += DNT) sm.flag[i] = 0;
+            __syncthreads();
+            score_slice(ms, s0, 0, R, key_row, true, k0, k1, rb_c, rb_s);
             __syncthreads();
 
             // rank inside the slice and publish the best keff
@@ -462,7 +482,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 const bool okw = word_tag(word) == tag;
-                if (!okw) __hip_atomic_store(ws.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!okw) {
+                    __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sm.bad = 1;
+                }
                 if (r < keff) {
                     const uint32_t ix = okw ? word_idx(word) : 0xfffu;
                     sm.xv[w * keff + r] = (okw && ix != 0xfffu) ? word_val(word) : -INFINITY;
@@ -488,46 +511,43 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
             // Every list is sorted (slot r holds its slice's rank-r entry), so an
             // entry's global rank is its slot plus, for every other list, the
-            // number of its entries that rank before it -- a binary search.
-            // All lists are searched in the same step: at most 6 dependent
-            // LDS round trips for any W.
-            for (int e = tid; e < ne; e += DNT) {
-                const int wo = e / keff, r = e - wo * keff;
-                const float ve = sm.xv[e];
-                const int ie = sm.xi[e];
-                if (ie == 0x7fffffff) continue;
-                int lo[kMaxW], hi[kMaxW];
-#pragma unroll
-                for (int w2 = 0; w2 < kMaxW; ++w2) {
-                    lo[w2] = 0;
-                    hi[w2] = (w2 < W && w2 != wo) ? keff : 0;
-                }
-                // branch-free: every step reads all lists at once (addresses
-                // clamped into the list), then updates the bounds with selects
-                for (int step = 0; step < 6; ++step) {
-                    float vv[kMaxW];
-                    int ii[kMaxW], mid[kMaxW];
-#pragma unroll
-                    for (int w2 = 0; w2 < kMaxW; ++w2) {
-                        mid[w2] = (lo[w2] + hi[w2]) >> 1;
-                        const int f = (w2 < W ? w2 : 0) * keff + min(mid[w2], keff - 1);
-                        vv[w2] = sm.xv[f];
-                        ii[w2] = sm.xi[f];
+            // number of that list's entries ranking before it.  A group of P
+            // lanes (P = W rounded up to a power of two) takes an entry, lane j
+            // binary-searches list j and the group sums the counts with DPP.
+            {
+                int P = 1;
+                while (P < W) P <<= 1;
+                const int lg = tid & (P - 1);
+                const int ngr = DNT / P;
+                int nsteps = 0;
+                while ((1 << nsteps) <= keff) ++nsteps;
+                const uint32_t kinv = (65536u + keff - 1) / keff;   // e / keff for e < 2^10
+                const int lw = min(lg, W - 1) * keff;
+                for (int e = tid / P; e - tid / P < ne; e += ngr) {
+                    const bool valid = e < ne;
+                    const float ve = valid ? sm.xv[e] : -INFINITY;
+                    const int ie = valid ? sm.xi[e] : 0x7fffffff;
+                    const int wo = (int)(((uint32_t)e * kinv) >> 16);
+                    int lo = 0;
+                    int hi = (lg < W && lg != wo && ie != 0x7fffffff) ? keff : 0;
+                    for (int step = 0; step < nsteps; ++step) {
+                        const int mid = (lo + hi) >> 1;
+                        const int f = lw + min(mid, keff - 1);
+                        const bool active = lo < hi;
+                        const bool bt = better(sm.xv[f], sm.xi[f], ve, ie);
+                        lo = (active && bt) ? mid + 1 : lo;
+                        hi = (active && !bt) ? mid : hi;
                     }
-#pragma unroll
-                    for (int w2 = 0; w2 < kMaxW; ++w2) {
-                        const bool active = lo[w2] < hi[w2];
-                        const bool bt = better(vv[w2], ii[w2], ve, ie);
-                        lo[w2] = (active && bt) ? mid[w2] + 1 : lo[w2];
-                        hi[w2] = (active && !bt) ? mid[w2] : hi[w2];
+                    int cnt = lo;
+                    if (P >= 2) cnt += dppi<0xB1>(cnt);
+                    if (P >= 4) cnt += dppi<0x4E>(cnt);
+                    if (P >= 8) cnt += dppi<0x141>(cnt);
+                    if (P >= 16) cnt += dppi<0x140>(cnt);
+                    const int rank = cnt + (e - wo * keff);
+                    if (lg == 0 && valid && ie != 0x7fffffff && rank < nkeep) {
+                        sm.byrank[rank] = ie;
+                        sm.byv[rank] = ve;
                     }
-                }
-                int rank = r;
-#pragma unroll
-                for (int w2 = 0; w2 < kMaxW; ++w2) rank += lo[w2];
-                if (rank < nkeep) {
-                    sm.byrank[rank] = ie;
-                    sm.byv[rank] = ve;
                 }
             }
             __syncthreads();
@@ -570,6 +590,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < nsel) ? sm.sel[nxt][r] : -1;
         }
         cur = nxt;
+        // Every gather of this level has been consumed: say so to the
+        // compiler, whose wait analysis cannot see through the predicated
+        // loads and would otherwise wait for all memory before each gather of
+        // the next level.
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     // token level: children of the kept level-1 nodes, then the orphan tokens
@@ -590,7 +615,6 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int64_t cpw = (m0 + W - 1) / W;
         const int64_t t0 = min(m0, (int64_t)wg * cpw);
         const int64_t t1 = min(m0, t0 + cpw);
-        rotate_query(qpos);
         for (int64_t c0 = t0; c0 < t1; c0 += kSlice) {
             const int ms = (int)min((int64_t)kSlice, t1 - c0);
             auto key_row = [&](int i, int) __attribute__((always_inline)) -> const T * {
@@ -599,17 +623,20 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             auto val_row = [&](int i) __attribute__((always_inline)) -> const T * {
                 return vc + cs.id((int)(c0 + i)) * D;
             };
-            VR vr[VBS];
-            issue_values(ms, val_row, vr);
-            for (int i = tid; i < ms; i += DNT) sm.flag[i] = 0;
-            __syncthreads();
             KR k0[KB], k1[KB];
             float rb_c[PPL], rb_s[PPL];
-            score_slice(ms, (int)c0, 0, 1, key_row, false, k0, k1, rb_c, rb_s);
+            load_batch(ms, (int)c0, 0, 1, key_row, 0, k0, k1, rb_c, rb_s);
+            VR vr[VBS];
+            issue_values(ms, val_row, vr);
+            if (c0 == t0) rotate_query(qpos);
+            for (int i = tid; i < ms; i += DNT) sm.flag[i] = 0;
+            __syncthreads();
+            score_slice(ms, (int)c0, 0, 1, key_row, true, k0, k1, rb_c, rb_s);
             __syncthreads();
             softmax_ref(ms);
             __syncthreads();
             softmax_fold(ms, val_row, vr);
+            __builtin_amdgcn_s_waitcnt(0);
         }
     }
 
@@ -641,7 +668,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     }
     // Gather n tagged words (word i at src(i)) into LDS dst[i]: every load is
     // issued first, then only words whose tag is not yet current are polled.
-    auto gather_words = [&](int n, auto src, float *dst) __attribute__((always_inline)) {
+    auto gather_words = [&](int n, auto src, auto dst) __attribute__((always_inline)) {
         for (int i0 = 0; i0 < n; i0 += 4 * DNT) {
             uint64_t wv[4];
 #pragma unroll
@@ -660,10 +687,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     wv[u] = __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 if ((uint32_t)(wv[u] >> 32) != tag) {
-                    __hip_atomic_store(ws.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     wv[u] = 0x7fc00000u;          // NaN: the result is visibly invalid
                 }
-                dst[i] = __uint_as_float((uint32_t)wv[u]);
+                *dst(i) = __uint_as_float((uint32_t)wv[u]);
             }
         }
     };
@@ -675,15 +702,22 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     float *mw = sm.z;                                                    // [W][G][2]
     float *aw = reinterpret_cast<float *>(hti_dec_lds) + DNW * G * D;    // [W][G][nc]
     __syncthreads();
-    gather_words(W * G * 2, [&](int i) __attribute__((always_inline)) {
-        const int w = i / (G * 2), r = i % (G * 2);
-        return pw_unit + ((int64_t)w * G + r / 2) * (D + 2) + D + (r % 2);
-    }, mw);
-    gather_words(W * G * nc, [&](int i) __attribute__((always_inline)) {
+    // one round: the (max, denominator) words first, then the columns
+    const int nmw = W * G * 2;
+    gather_words(nmw + W * G * nc, [&](int i) __attribute__((always_inline)) {
+        if (i < nmw) {
+            const int w = i / (G * 2), r = i % (G * 2);
+            return pw_unit + ((int64_t)w * G + r / 2) * (D + 2) + D + (r % 2);
+        }
+        i -= nmw;
         const int w = i / (G * nc), r = i % (G * nc);
         return pw_unit + ((int64_t)w * G + r / nc) * (D + 2) + d0 + (r % nc);
-    }, aw);
+    }, [&](int i) __attribute__((always_inline)) { return i < nmw ? mw + i : aw + (i - nmw); });
     __syncthreads();
+    // a wait that timed out anywhere in this unit (a workgroup that was not
+    // resident in time) makes its output NaN rather than silently wrong
+    const bool failed = sm.bad != 0 ||
+        __hip_atomic_load(&ws.err[unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
     const int64_t row = ((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G;
     for (int i = tid; i < G * nc; i += DNT) {
         const int h = i / nc, c = i % nc;
@@ -697,7 +731,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             num += aw[(w * G + h) * nc + c] * f;
             den += mw[(w * G + h) * 2 + 1] * f;
         }
-        a.out[(row + h) * D + d0 + c] = den > 0.f ? num / den : 0.f;
+        a.out[(row + h) * D + d0 + c] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? num / den : 0.f;
     }
     if (wg == 0 && tid < G && a.lse) {
         const int h = tid;
@@ -732,8 +766,13 @@ static hipError_t dec_launch(const TravArgs &a, const DecodeWs &ws, int64_t unit
     TravArgs aa = a;
     DecodeWs ww = ws;
     void *args[] = {&aa, &ww};
-    return hipLaunchCooperativeKernel((const void *)kern, dim3((unsigned)(units * ws.W)), dim3(DNT),
-                                      args, dyn, s);
+    // A plain launch: the workgroups of a unit wait for each other, which
+    // needs them resident together.  The plan keeps the grid within one
+    // workgroup per compute unit, so they all are whenever the device is not
+    // held by other work; every wait is bounded and a timeout shows as NaN
+    // output (a cooperative launch would guarantee residency but costs more
+    // than the whole kernel to dispatch).
+    return hipLaunchKernel((const void *)kern, dim3((unsigned)(units * ws.W)), dim3(DNT), args, dyn, s);
 }
 
 template <typename T, int D>
@@ -804,7 +843,7 @@ size_t decode_ws_bytes(int64_t units, int W, int levels, int G, int D)
 {
     size_t off = 0;
     off += ((size_t)units * 4 + 255) / 256 * 256;                 // epoch
-    off += 256;                                                   // err
+    off += ((size_t)units * 4 + 255) / 256 * 256;                 // err
     off += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
     off += ((size_t)units * W * G * (D + 2) * 8 + 255) / 256 * 256;
     return off;
@@ -817,8 +856,8 @@ DecodeWs decode_ws_layout(void *base, int64_t units, int W, int levels, int G, i
     w.W = W;
     w.epoch = (uint32_t *)p;
     p += ((size_t)units * 4 + 255) / 256 * 256;
-    w.err = (int *)p;
-    p += 256;
+    w.err = (uint32_t *)p;
+    p += ((size_t)units * 4 + 255) / 256 * 256;
     w.words = (uint64_t *)p;
     p += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
     w.part = (uint64_t *)p;

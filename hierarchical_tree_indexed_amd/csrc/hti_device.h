@@ -149,6 +149,14 @@ __device__ __forceinline__ int min16i(int v)
     v = min(v, dppi<0x140>(v));
     return v;
 }
+__device__ __forceinline__ int sum16i(int v)
+{
+    v += dppi<0xB1>(v);
+    v += dppi<0x4E>(v);
+    v += dppi<0x141>(v);
+    v += dppi<0x140>(v);
+    return v;
+}
 // wave-wide results, uniform across the wave
 __device__ __forceinline__ float wave_sum(float v)
 {

@@ -47,13 +47,13 @@ struct TravArgs {
 };
 
 // Workspace of the split decode (zeroed by the caller before first use, then
-// owned by the library): per-unit launch epoch, an error flag, the per-level
-// exchange words and the per-workgroup partial states, all as words tagged
-// with the launch epoch.
+// owned by the library): per-unit launch epoch, per-unit timeout marks, the
+// per-level exchange words and the per-workgroup partial states, all as words
+// tagged with the launch epoch.
 struct DecodeWs {
     int W;              // workgroups per (query, KV group) unit
     uint32_t *epoch;    // [units]
-    int *err;           // [1]
+    uint32_t *err;      // [units]: tag of the last launch in which a wait timed out
     uint64_t *words;    // [units][levels][W][HTI_MAX_SELECT + 2]
     uint64_t *part;     // [units][W][G][D + 2]: tag << 32 | fp32 bits
 };

@@ -48,14 +48,17 @@ struct Cands {
     uint32_t binv;      // ceil(2^32 / b): i / b == umulhi(i, binv) for i < 2^16
     int64_t orph0;
     bool top;
+    // Branch-free (selects only), so that gathers addressed by it can be
+    // issued back to back: the parent slot is clamped into the kept list and
+    // read even for orphans and at the top level, where it is not used.
     __device__ __forceinline__ int64_t id(int i) const
     {
-        if (top) return i;
-        if (i < nprev * b) {
-            const int q = (int)__umulhi((uint32_t)i, binv);
-            return (int64_t)selp[q] * b + (i - q * b);
-        }
-        return orph0 + (i - nprev * b);
+        const int nb = nprev * b;
+        const int q = (int)__umulhi((uint32_t)i, binv);
+        const int qs = min(q, nprev > 0 ? nprev - 1 : 0);
+        const int64_t child = (int64_t)selp[qs] * b + (i - q * b);
+        const int64_t orphan = orph0 + (i - nb);
+        return top ? (int64_t)i : (i < nb ? child : orphan);
     }
 };
 

@@ -19,7 +19,8 @@
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers owned by the caller, unless the
  *     argument says "host".  The library never allocates, frees or retains
- *     device memory; it keeps no device state between calls.
+ *     device memory; the only device state it keeps between calls is in the
+ *     decode workspace the caller hands it (per-unit launch counters).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *     call only enqueues work on it and returns; results are valid once the
  *     stream has reached that point.
@@ -177,9 +178,13 @@ size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel
  *        bytes, filled with zeros before its first use and then left to the
  *        library (it keeps per-unit launch counters there).  With a workspace
  *        each unit is split over up to HTI_DECODE_MAX_SPLIT workgroups that
- *        cooperate (a cooperative launch); ws = NULL runs one workgroup per
- *        unit.  One workspace serves one (cfg, Nq) shape and one stream at a
- *        time: calls that share it must not overlap.
+ *        wait on each other's partial results; the grid is kept within one
+ *        workgroup per compute unit so that all are resident while the
+ *        device runs nothing else.  Every wait is bounded: if work on other
+ *        streams keeps some workgroups from starting in time, the affected
+ *        outputs are NaN.  ws = NULL runs one independent workgroup per unit.
+ *        One workspace serves one (cfg, Nq) shape and one stream at a time:
+ *        calls that share it must not overlap.
  * Errors additionally: HTI_ERR_CAPACITY if rope_npos is below the positions
  * this cfg/selection can reach, HTI_ERR_UNSUPPORTED if a summary level can
  * exceed HTI_MAX_CAND candidates, HTI_ERR_WORKSPACE if ws_bytes is too small.

@@ -17,15 +17,19 @@
 //   * it publishes its slice's best k (score, index) as 64-bit words carrying
 //     a per-launch tag, written and read with agent-scope atomics, so a word
 //     is valid exactly when its tag matches -- no fences, no counters;
-//   * while the other slices' lists arrive it updates its own online softmax
-//     over the whole slice (the running max may include candidates that turn
-//     out to be kept; any upper bound is a valid reference point);
-//   * every workgroup merges the same W lists into the same kept set, drops
-//     the kept candidates' probabilities and folds its values in;
+//   * every workgroup merges the same W lists into the same kept set; as soon
+//     as the kept set is known the next level's gathers are issued, and the
+//     level's own softmax contribution (unkept candidates) is folded in while
+//     they are in flight;
 //   * the token level is sliced the same way, without an exchange;
 //   * each workgroup publishes its partial state (max, denominator,
 //     unnormalised output per head) the same way, and every workgroup merges
 //     all of them for a slice of the output columns.
+//
+// Softmax state: the running max M is kept identical in every thread (each
+// computes it from the same per-wave maxima); the denominator is kept as a
+// per-thread partial sum and the output as per-wave partial sums, both
+// rescaled by the same factors and reduced once at the end.
 //
 // The workgroups of a launch wait on each other, so they must be resident
 // together: the grid is kept within one workgroup per compute unit, and every
@@ -43,28 +47,27 @@ namespace {
 constexpr int DNT = 256;              // threads per workgroup
 constexpr int DNW = DNT / 64;         // waves
 constexpr int DNQ = DNT / 16;         // quarter-waves (16-lane rows)
-constexpr int kSlice = 128;           // largest slice of a summary level
+constexpr int kSlice = 128;           // largest slice of a summary level / token chunk
 constexpr int kMaxW = 16;             // workgroups per unit
-constexpr int kSlots = kMaxSel + 2;   // words per (level, workgroup): k entries + (max, sum)
+constexpr int kSlots = kMaxSel + 2 * DNW;   // words per (level, workgroup): k entries + per-wave (max, sum)
 constexpr long kSpin = 1L << 22;      // bound on polling for one word
 
 template <int G>
 struct DSmem {
-    float z[kSlice * G];              // [candidate][head]: logits, then probabilities
-    float s[kSlice] __attribute__((aligned(16)));   // group scores of the slice
+    float z[2][kSlice * G];           // [candidate][head]: logits, then probabilities (by step parity)
+    float s[kSlice + 68] __attribute__((aligned(16)));   // group scores of the slice, -inf padded
     uint8_t flag[kSlice];             // 1 = kept
-    float qraw[G * 128];
-    float q[G * 128];
+    float qraw[G * 128] __attribute__((aligned(16)));
     int sel[2][kMaxSel];
     int nsel[2];
-    float M[G], l[G], alpha[G];
-    float red[DNW * G];
-    float xv[kMaxW * kMaxSel + 4] __attribute__((aligned(16)));   // merged lists: score, index
+    float redz[DNW][G];               // per-wave maxima of the logits
+    float xv[kMaxW * kMaxSel + 4] __attribute__((aligned(16)));   // collected lists: score, index
     int xi[kMaxW * kMaxSel + 4] __attribute__((aligned(16)));
-    float xm[kMaxW], xs[kMaxW];       // per-slice max and exp-sum (top-p)
+    float xm[kMaxW * DNW], xs[kMaxW * DNW];    // per-wave max and exp-sum (top-p)
     int byrank[kMaxSel] __attribute__((aligned(16)));   // kept entries by rank: index, score
     float byv[kMaxSel];
     int nkeep;
+    int in_last;                      // the query's own leaf was kept (level 1)
     int64_t n[HTI_MAX_LEVELS + 1];
     uint32_t tag;
     int bad;                          // a wait of this workgroup timed out
@@ -77,6 +80,26 @@ __device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t idx, float 
 __device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 44); }
 __device__ __forceinline__ uint32_t word_idx(uint64_t w) { return (uint32_t)(w >> 32) & 0xfffu; }
 __device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+__device__ __forceinline__ int better(float va, int ia, float vb, int ib)
+{
+    return (int)(va > vb) | ((int)(va == vb) & (int)(ia < ib));
+}
+
+// Candidates of one step (a summary level or the token level) as seen by one
+// workgroup: the list, where its keys and values live, and this workgroup's
+// slice of it.
+template <typename T>
+struct Step {
+    Cands cs;
+    const T *kb, *vb;    // key / value rows of this unit: row r at kb + (r * nref + j) * D
+    int nref;            // keys per row (R at summary levels, 1 at tokens)
+    int m;               // candidates
+    int s0, ms;          // this workgroup's slice (first chunk at the token level)
+    int64_t t1;          // token level: end of this workgroup's range
+    int64_t qpos;        // RoPE position of the query
+    bool take_all;       // every candidate is kept (no scoring)
+};
 
 } // namespace
 
@@ -105,21 +128,25 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const int bi = (int)(rest / a.Nq);
     const int64_t bh = (int64_t)bi * t.Hkv + g;
     const int b = t.b, levels = t.levels, R = t.R;
-    const int64_t L = t.len[bi];
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
-    const int nslot = keff + (a.mode == HTI_TOPP ? 2 : 0);
+    const bool topp = a.mode == HTI_TOPP;
+    const int nslot = keff + (topp ? 2 * DNW : 0);
     uint64_t *xw = ws.words + (int64_t)unit * levels * W * kSlots;
 
     if (tid == 0) {
-        int64_t n = L;
+        const int64_t L0 = t.len[bi];
+        int64_t n = L0;
         sm.n[0] = n;
+        const int bs = __builtin_ctz((unsigned)b);
+        const bool pow2 = (b & (b - 1)) == 0;
         for (int l = 1; l <= levels; ++l) {
-            n /= b;
+            n = pow2 ? (n >> bs) : n / b;
             sm.n[l] = n;
         }
         sm.tag = (ws.epoch[unit] % 0xffffeu) + 1u;
         sm.nsel[0] = 0;
         sm.bad = 0;
+        sm.in_last = 0;
     }
     const T *qp = (const T *)a.q + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
     for (int i = tid; i < G * D; i += DNT) {
@@ -127,48 +154,78 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         load_vec<T, 1>(qp + i, &v);
         sm.qraw[i] = v;
     }
-    if (tid < G) {
-        sm.M[tid] = -INFINITY;
-        sm.l[tid] = 0.f;
-        sm.alpha[tid] = 1.f;
-    }
+    // angle step of each of this lane's RoPE frequencies (row 1 of the table)
     float st_c[PPL], st_s[PPL];
 #pragma unroll
     for (int e = 0; e < PPL; ++e) {
-        const float2 cs = t.rope[(D / 2) + sub * PPL + e];
-        st_c[e] = cs.x;
-        st_s[e] = cs.y;
+        const float2 c2 = t.rope[(D / 2) + sub * PPL + e];
+        st_c[e] = c2.x;
+        st_s[e] = c2.y;
     }
-    float acc[G][DPL];
+    float M[G], lt[G], acc[G][DPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+        M[h] = -INFINITY;
+        lt[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    }
     __syncthreads();
     const uint32_t tag = sm.tag;
+    const int64_t L = sm.n[0];
 
     const T *kc = (const T *)t.kc + bh * t.ncap[0] * D;
     const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
 
-    auto rotate_query = [&](int64_t pos) __attribute__((always_inline)) {
-        const float2 *rp = t.rope + pos * (D / 2);
-        for (int i = tid; i < G * (D / 2); i += DNT) {
-            const int h = i / (D / 2), j = i % (D / 2);
-            const float2 c2 = rp[j];
-            const float x0 = sm.qraw[h * D + j], x1 = sm.qraw[h * D + j + D / 2];
-            sm.q[h * D + j] = x0 * c2.x - x1 * c2.y;
-            sm.q[h * D + j + D / 2] = x0 * c2.y + x1 * c2.x;
+    // ---- the candidates of a step ----
+    // level lvl >= 1 (parents in sm.sel[cur]) or the token level (lvl == 0)
+    auto make_step = [&](int lvl, int cur) __attribute__((always_inline)) -> Step<T> {
+        Step<T> st;
+        const bool top = (lvl == levels);
+        const int nprev = top ? 0 : sm.nsel[cur];
+        st.cs.selp = sm.sel[cur];
+        st.cs.nprev = nprev;
+        st.cs.b = b;
+        st.cs.binv = a.binv;
+        st.cs.top = top;
+        st.cs.orph0 = top ? 0 : (int64_t)b * sm.n[lvl + 1];
+        if (lvl >= 1) {
+            st.m = (int)(top ? sm.n[lvl] : (int64_t)nprev * b + (sm.n[lvl] - st.cs.orph0));
+            st.kb = (const T *)t.lk[lvl - 1] + bh * t.ncap[lvl] * R * D;
+            st.vb = (const T *)t.lv[lvl - 1] + bh * t.ncap[lvl] * D;
+            st.nref = R;
+            st.take_all = (a.mode == HTI_TOPK) ? (st.m <= a.k) : (st.m <= 1);
+            const int cpw = (st.m + W - 1) / W;
+            st.s0 = min(st.m, wg * cpw);
+            st.ms = min(st.m, st.s0 + cpw) - st.s0;
+            st.t1 = st.s0 + st.ms;
+            st.qpos = st.m;
+        } else {
+            // the query token is a candidate when its leaf was kept or it is
+            // an orphan; it then sits last
+            const int64_t m0 = top ? L : (int64_t)nprev * b + (L - st.cs.orph0);
+            const bool in = top || (L - 1 >= st.cs.orph0) || sm.in_last != 0;
+            st.m = (int)m0;
+            st.kb = kc;
+            st.vb = vc;
+            st.nref = 1;
+            st.take_all = false;
+            const int64_t cpw = (m0 + W - 1) / W;
+            const int64_t t0 = min(m0, (int64_t)wg * cpw);
+            st.t1 = min(m0, t0 + cpw);
+            st.s0 = (int)t0;
+            st.ms = (int)min((int64_t)kSlice, st.t1 - t0);
+            st.qpos = m0 - (in ? 1 : 0);
         }
+        return st;
     };
 
-    // Score slice candidates [0, ms) (global index s0 + i, RoPE position
-    // pos0 + s0 + i): keys gathered by quarter-waves in batches, best of the
-    // nref reference keys kept.  Writes sm.s, sm.z.
+    // ---- gathers ----
     // one batch of a quarter-wave's keys (items it0.., item = candidate x
     // reference key) plus the RoPE row of its first candidate
-    auto load_batch = [&](int ms, int s0, int64_t pos0, int nref, auto key_row, int it0,
-                          KR (&k0)[KB], KR (&k1)[KB], float (&rb_c)[PPL],
-                          float (&rb_s)[PPL]) __attribute__((always_inline)) {
+    auto load_batch = [&](const Step<T> &st, int s0, int ms, int it0, KR (&k0)[KB], KR (&k1)[KB],
+                          float (&rb_c)[PPL], float (&rb_s)[PPL]) __attribute__((always_inline)) {
+        const int nref = st.nref;
         const int cpq = (ms + DNQ - 1) / DNQ;
         const int c_beg = min(ms, quarter * cpq);
         const int c_end = min(ms, c_beg + cpq);
@@ -179,7 +236,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 #pragma unroll
         for (int u = 0; u < KB; ++u)
             if (u < nb) {
-                const T *kp = key_row(s0 + ci, j);
+                const T *kp = st.kb + (st.cs.id(s0 + ci) * nref + j) * D;
                 k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
                 k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
                 if (++j == nref) {
@@ -188,7 +245,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 }
             }
         if (nb > 0) {
-            const float2 *rp = t.rope + (pos0 + s0 + c_beg + it0 / nref) * (D / 2) + sub * PPL;
+            const float2 *rp = t.rope + (int64_t)(s0 + c_beg + it0 / nref) * (D / 2) + sub * PPL;
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
                 const float2 c2 = rp[e];
@@ -197,30 +254,69 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
         }
     };
-    auto score_slice = [&](int ms, int s0, int64_t pos0, int nref, auto key_row,
-                           bool keys_issued, KR (&k0)[KB], KR (&k1)[KB], float (&rb_c)[PPL],
-                           float (&rb_s)[PPL]) __attribute__((always_inline)) {
-        const int cpq = (ms + DNQ - 1) / DNQ;
-        const int c_beg = min(ms, quarter * cpq);
-        const int c_end = min(ms, c_beg + cpq);
-        const int nitems = (c_end - c_beg) * nref;
-        const int KBR = (KB / nref) * nref;
+    // value rows of the slice, wave w owning rows w, w + DNW, ...: the first
+    // VBS per wave go to registers.  Every load is issued (rows past the slice
+    // re-read its last row) so that each writes its register unconditionally.
+    auto issue_values = [&](const Step<T> &st, int s0, int ms, VR (&vr)[VBS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < VBS; ++u) {
+            const int i = min(wave + DNW * u, ms - 1);
+            vr[u] = *reinterpret_cast<const VR *>(st.vb + st.cs.id(s0 + i) * D + lane * DPL);
+        }
+    };
+    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&rb_c)[PPL],
+                          float (&rb_s)[PPL], VR (&vr)[VBS], float (&qc)[PPL], float (&qs)[PPL])
+        __attribute__((always_inline)) {
+        if (st.take_all) return;
+        if (st.ms > 0) {
+            load_batch(st, st.s0, st.ms, 0, k0, k1, rb_c, rb_s);
+            issue_values(st, st.s0, st.ms, vr);
+        }
+        const float2 *rp = t.rope + st.qpos * (D / 2) + sub * PPL;
+#pragma unroll
+        for (int e = 0; e < PPL; ++e) {
+            const float2 c2 = rp[e];
+            qc[e] = c2.x;
+            qs[e] = c2.y;
+        }
+    };
+
+    // ---- scoring ----
+    // Rotated query of this lane's elements (sub*PPL.., and the rotate-half
+    // partners), then the slice's keys in quarter-wave batches: logits per
+    // head into sm.z[zb], group scores into sm.s (with -inf padding), kept
+    // flags cleared, per-wave maxima of the logits into sm.redz.
+    auto score = [&](const Step<T> &st, int s0, int ms, int zb, KR (&k0)[KB], KR (&k1)[KB],
+                     float (&rb_c)[PPL], float (&rb_s)[PPL], const float (&qc)[PPL],
+                     const float (&qs)[PPL]) __attribute__((always_inline)) {
         float qa[G][PPL], qb[G][PPL];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
-                qa[h][e] = sm.q[h * D + sub * PPL + e];
-                qb[h][e] = sm.q[h * D + D / 2 + sub * PPL + e];
+                const float x0 = sm.qraw[h * D + sub * PPL + e];
+                const float x1 = sm.qraw[h * D + D / 2 + sub * PPL + e];
+                qa[h][e] = x0 * qc[e] - x1 * qs[e];
+                qb[h][e] = x0 * qs[e] + x1 * qc[e];
             }
+        const int nref = st.nref;
+        const int cpq = (ms + DNQ - 1) / DNQ;
+        const int c_beg = min(ms, quarter * cpq);
+        const int c_end = min(ms, c_beg + cpq);
+        const int nitems = (c_end - c_beg) * nref;
+        const int KBR = (KB / nref) * nref;
+        float zmax[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) zmax[h] = -INFINITY;
+        float *zz = sm.z[zb];
         for (int it0 = 0; it0 < nitems; it0 += KBR) {
             const int nb = min(nitems - it0, KBR);
-            if (it0 > 0 || !keys_issued) load_batch(ms, s0, pos0, nref, key_row, it0, k0, k1, rb_c, rb_s);
+            if (it0 > 0) load_batch(st, s0, ms, it0, k0, k1, rb_c, rb_s);
             int ci = c_beg + it0 / nref, j = 0;
             float best = -INFINITY;
-            float zb[G];
+            float zb_[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) zb[h] = 0.f;
+            for (int h = 0; h < G; ++h) zb_[h] = 0.f;
             float cc[PPL], ss[PPL];
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
@@ -253,14 +349,17 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     if (gs > best) {
                         best = gs;
 #pragma unroll
-                        for (int h = 0; h < G; ++h) zb[h] = z[h];
+                        for (int h = 0; h < G; ++h) zb_[h] = z[h];
                     }
                     if (++j == nref) {
                         if (sub == 0) {
                             sm.s[ci] = best;
+                            sm.flag[ci] = 0;
 #pragma unroll
-                            for (int h = 0; h < G; ++h) sm.z[ci * G + h] = zb[h];
+                            for (int h = 0; h < G; ++h) zz[ci * G + h] = zb_[h];
                         }
+#pragma unroll
+                        for (int h = 0; h < G; ++h) zmax[h] = fmaxf(zmax[h], zb_[h]);
                         j = 0;
                         ++ci;
                         best = -INFINITY;
@@ -275,86 +374,56 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 }
             }
         }
-    };
-
-    // value rows of the slice's candidates, wave w owning rows w, w + DNW, ...:
-    // the first VBS per wave are loaded with the keys and held in registers
-    // (every load is issued, rows past the slice re-reading its last row, so
-    // that each writes its register unconditionally and none waits on another)
-    auto issue_values = [&](int ms, auto val_row, VR (&vr)[VBS]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < VBS; ++u) {
-            const int i = min(wave + DNW * u, ms - 1);
-            vr[u] = *reinterpret_cast<const VR *>(val_row(i) + lane * DPL);
-        }
-    };
-
-    // online-softmax reference update over the slice: running max (over every
-    // slice candidate), rescale factor, probabilities over the logits
-    auto softmax_ref = [&](int ms) __attribute__((always_inline)) {
-        float lm[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) lm[h] = -INFINITY;
-        for (int i = tid; i < ms; i += DNT)
-#pragma unroll
-            for (int h = 0; h < G; ++h) lm[h] = fmaxf(lm[h], sm.z[i * G + h]);
+        if (tid < 68) sm.s[ms + tid] = -INFINITY;
+        // every lane of a quarter holds its quarter's maxima: combine the
+        // wave's four quarters
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            lm[h] = wave_max(lm[h]);
-            if (lane == 0) sm.red[wave * G + h] = lm[h];
-        }
-        __syncthreads();
-        if (tid < G) {
-            float mm = sm.red[tid];
-            for (int w = 1; w < DNW; ++w) mm = fmaxf(mm, sm.red[w * G + tid]);
-            const float Mo = sm.M[tid];
-            const float Mn = fmaxf(Mo, mm);
-            sm.alpha[tid] = (Mn == -INFINITY) ? 1.f : expf(Mo - Mn);
-            sm.M[tid] = Mn;
-        }
-        __syncthreads();
-        for (int i = tid; i < ms * G; i += DNT) {
-            const int h = i % G;
-            sm.z[i] = expf(sm.z[i] - sm.M[h]);
+            const float m4 = fmaxf(fmaxf(rlane(zmax[h], 0), rlane(zmax[h], 16)),
+                                   fmaxf(rlane(zmax[h], 32), rlane(zmax[h], 48)));
+            if (lane == 0) sm.redz[wave][h] = m4;
         }
     };
-    // denominators over the slice's entries (kept candidates' probabilities
-    // zeroed first), then the values staged in LDS
-    auto softmax_fold = [&](int ms, auto val_row, VR (&vr)[VBS]) __attribute__((always_inline)) {
-        float ls[G];
+
+    // new running max from the per-wave maxima (same in every thread), and
+    // the factor that rescales what was accumulated under the old one
+    auto new_max = [&](float (&Mn)[G], float (&alpha)[G]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) ls[h] = 0.f;
-        for (int i = tid; i < ms; i += DNT) {
-            const bool kept = sm.flag[i];
+        for (int h = 0; h < G; ++h) {
+            float mm = M[h];
+#pragma unroll
+            for (int w = 0; w < DNW; ++w) mm = fmaxf(mm, sm.redz[w][h]);
+            Mn[h] = mm;
+            alpha[h] = (mm == -INFINITY) ? 1.f : __expf(M[h] - mm);
+        }
+    };
+    // probabilities of this thread's candidate (kept ones drop out), the
+    // rescaled partial denominator and output
+    auto probs = [&](int ms, int zb, bool use_flags, const float (&Mn)[G], const float (&alpha)[G])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            lt[h] *= alpha[h];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha[h];
+        }
+        if (tid < ms) {
+            const bool kept = use_flags && sm.flag[tid];
+            float *zp = &sm.z[zb][tid * G];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float pz = sm.z[i * G + h];
-                if (kept) {
-                    pz = 0.f;
-                    sm.z[i * G + h] = 0.f;
-                }
-                ls[h] += pz;
+                const float p = kept ? 0.f : __expf(zp[h] - Mn[h]);
+                zp[h] = p;
+                lt[h] += p;
             }
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            ls[h] = wave_sum(ls[h]);
-            if (lane == 0) sm.red[wave * G + h] = ls[h];
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float al = sm.alpha[h];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
-        }
-        __syncthreads();
-        if (tid < G) {
-            float sum = 0.f;
-            for (int w = 0; w < DNW; ++w) sum += sm.red[w * G + tid];
-            sm.l[tid] = sm.l[tid] * sm.alpha[tid] + sum;
-        }
+        for (int h = 0; h < G; ++h) M[h] = Mn[h];
+    };
+    // p * v over the slice's rows: the register batch, then any further rows
+    auto fold = [&](const Step<T> &st, int s0, int ms, int zb, const VR (&vr)[VBS]) __attribute__((always_inline)) {
         auto add_row = [&](int i, const float *v) __attribute__((always_inline)) {
-            const float *pz = &sm.z[i * G];
+            const float *pz = &sm.z[zb][i * G];
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -369,275 +438,249 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 add_row(i, v);
             }
         }
-        for (int i = wave + DNW * VBS; i < ms; i += DNW) {     // rows beyond the batch
+        for (int i = wave + DNW * VBS; i < ms; i += DNW) {
             float v[DPL];
-            load_vec<T, DPL>(val_row(i) + lane * DPL, v);
+            load_vec<T, DPL>(st.vb + st.cs.id(s0 + i) * D + lane * DPL, v);
             add_row(i, v);
         }
-        __syncthreads();
     };
 
-    auto better = [](float va, int ia, float vb, int ib) __attribute__((always_inline)) -> int {
-        return (int)(va > vb) | ((int)(va == vb) & (int)(ia < ib));
-    };
+    // ---- the steps ----
+    int cur = 0, zb = 0;
+    KR k0[KB], k1[KB];
+    float rb_c[PPL], rb_s[PPL], qc[PPL], qs[PPL];
+    VR vr[VBS];
+    Step<T> st = make_step(levels, 0);
+    issue_step(st, k0, k1, rb_c, rb_s, vr, qc, qs);
 
-    int cur = 0;
     for (int lvl = levels; lvl >= 1; --lvl) {
-        const int nprev = (lvl == levels) ? 0 : sm.nsel[cur];
-        Cands cs;
-        cs.selp = sm.sel[cur];
-        cs.nprev = nprev;
-        cs.b = b;
-        cs.binv = a.binv;
-        cs.top = (lvl == levels);
-        cs.orph0 = cs.top ? 0 : (int64_t)b * sm.n[lvl + 1];
-        const int m = (int)(cs.top ? sm.n[lvl] : (int64_t)nprev * b + (sm.n[lvl] - cs.orph0));
         const int nxt = cur ^ 1;
-        const bool take_all = (a.mode == HTI_TOPK) ? (m <= a.k) : (m <= 1);
-        if (take_all) {
-            for (int i = tid; i < m; i += DNT) sm.sel[nxt][i] = (int)cs.id(i);
-            if (tid == 0) sm.nsel[nxt] = m;
+        if (st.take_all) {
+            for (int i = tid; i < st.m; i += DNT) sm.sel[nxt][i] = (int)st.cs.id(i);
+            if (tid == 0) sm.nsel[nxt] = st.m;
+            if (lvl == 1 && tid < st.m && st.cs.id(tid) == (L - 1) / b) sm.in_last = 1;
             __syncthreads();
-        } else {
-            const int cpw = (m + W - 1) / W;
-            const int s0 = min(m, wg * cpw);
-            const int ms = min(m, s0 + cpw) - s0;
-            const T *lk = (const T *)t.lk[lvl - 1];
-            const T *lv = (const T *)t.lv[lvl - 1];
-            const int64_t ncap = t.ncap[lvl];
-            auto key_row = [&](int i, int j) __attribute__((always_inline)) -> const T * {
-                return lk + ((bh * ncap + cs.id(i)) * R + j) * D;
-            };
-            auto val_row = [&](int i) __attribute__((always_inline)) -> const T * {
-                return lv + (bh * ncap + cs.id(s0 + i)) * D;
-            };
-            // gathers first (they depend only on the candidate list), then the
-            // query rotation while they are in flight
-            KR k0[KB], k1[KB];
-            float rb_c[PPL], rb_s[PPL];
-            load_batch(ms, s0, 0, R, key_row, 0, k0, k1, rb_c, rb_s);
-            VR vr[VBS];
-            if (ms > 0) issue_values(ms, val_row, vr);
-            rotate_query(m);
-            for (int i = tid; i < ms; i += DNT) sm.flag[i] = 0;
-            __syncthreads();
-            score_slice(ms, s0, 0, R, key_row, true, k0, k1, rb_c, rb_s);
-            __syncthreads();
-
-            // rank inside the slice and publish the best keff
-            uint64_t *mine = xw + ((int64_t)(lvl - 1) * W + wg) * kSlots;
-            for (int i = tid; i < ms; i += DNT) {
-                const float si = sm.s[i];
-                int rank = 0;
-                int j = 0;
-                for (; j + 4 <= ms; j += 4) {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(&sm.s[j]);
-                    rank += better(v4.x, j, si, i) + better(v4.y, j + 1, si, i) +
-                            better(v4.z, j + 2, si, i) + better(v4.w, j + 3, si, i);
-                }
-                for (; j < ms; ++j) rank += better(sm.s[j], j, si, i);
-                if (rank < keff)
-                    __hip_atomic_store(&mine[rank], pack_word(tag, (uint32_t)(s0 + i), si),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wg == 0 && a.sel) {
+                int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
+                for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < st.m) ? sm.sel[nxt][r] : -1;
             }
-            for (int r = ms + tid; r < keff; r += DNT)
-                __hip_atomic_store(&mine[r], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
+            cur = nxt;
+            st = make_step(lvl - 1, cur);
+            issue_step(st, k0, k1, rb_c, rb_s, vr, qc, qs);
+            continue;
+        }
+        const int s0 = st.s0, ms = st.ms;
+        score(st, s0, ms, zb, k0, k1, rb_c, rb_s, qc, qs);
+        __syncthreads();                                                   // B1
+        float Mn[G], alpha[G];
+        new_max(Mn, alpha);
+
+        // rank inside the slice: Gr threads per candidate, each comparing it
+        // with a run of the (padded) slice, counts summed with DPP
+        uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;
+        uint64_t *mine = lw_words + (int64_t)wg * kSlots;
+        {
+            int Gr = 16;
+            while (Gr > 1 && Gr * ms > DNT) Gr >>= 1;
+            const int ci = tid / Gr, cc = tid & (Gr - 1);
+            const int ch = (((ms + Gr - 1) / Gr) + 3) & ~3;
+            const bool valid = ci < ms;
+            const float si = valid ? sm.s[ci] : -INFINITY;
+            int rank = 0;
+            for (int j = cc * ch; j < cc * ch + ch; j += 4) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(&sm.s[j]);
+                rank += better(v4.x, j, si, ci) + better(v4.y, j + 1, si, ci) +
+                        better(v4.z, j + 2, si, ci) + better(v4.w, j + 3, si, ci);
+            }
+            if (Gr >= 2) rank += dppi<0xB1>(rank);
+            if (Gr >= 4) rank += dppi<0x4E>(rank);
+            if (Gr >= 8) rank += dppi<0x141>(rank);
+            if (Gr >= 16) rank += dppi<0x140>(rank);
+            if (valid && cc == 0 && rank < keff)
+                __hip_atomic_store(&mine[rank], pack_word(tag, (uint32_t)(s0 + ci), si), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            if (a.mode == HTI_TOPP) {
-                // slice max and exp-sum of the group scores
-                float lmx = -INFINITY;
-                for (int i = tid; i < ms; i += DNT) lmx = fmaxf(lmx, sm.s[i]);
-                lmx = wave_max(lmx);
-                if (lane == 0) sm.red[wave * G] = lmx;
-                __syncthreads();
-                float smx = sm.red[0];
-                for (int w = 1; w < DNW; ++w) smx = fmaxf(smx, sm.red[w * G]);
-                float ld = 0.f;
-                for (int i = tid; i < ms; i += DNT) ld += expf(sm.s[i] - smx);
-                ld = wave_sum(ld);
-                __syncthreads();
-                if (lane == 0) sm.red[wave * G] = ld;
-                __syncthreads();
-                if (tid == 0) {
-                    float sum = 0.f;
-                    for (int w = 0; w < DNW; ++w) sum += sm.red[w * G];
-                    __hip_atomic_store(&mine[keff], pack_word(tag, 0, smx), __ATOMIC_RELAXED,
+            if (tid >= ms && tid < keff)
+                __hip_atomic_store(&mine[tid], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (topp) {
+                // this wave's (max, exp-sum) of the group scores it holds
+                const bool own = valid && cc == 0;
+                const float wmax = wave_max(own ? si : -INFINITY);
+                const float wsum = wave_sum(own ? __expf(si - wmax) : 0.f);
+                if (lane == 0) {
+                    __hip_atomic_store(&mine[keff + 2 * wave], pack_word(tag, 0, wmax), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&mine[keff + 1], pack_word(tag, 0, sum), __ATOMIC_RELAXED,
+                    __hip_atomic_store(&mine[keff + 2 * wave + 1], pack_word(tag, 0, wsum), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
+        }
 
-            // own softmax reference while the other slices' lists arrive
-            softmax_ref(ms);
-
-            // collect every slice's list (bounded polling on the tag)
-            for (int e = tid; e < W * nslot; e += DNT) {
-                const int w = e / nslot, r = e % nslot;
-                const uint64_t *src = xw + ((int64_t)(lvl - 1) * W + w) * kSlots + r;
-                uint64_t word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                long spins = 0;
-                while (word_tag(word) != tag && ++spins < kSpin) {
-                    __builtin_amdgcn_s_sleep(1);
-                    word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                const bool okw = word_tag(word) == tag;
-                if (!okw) {
-                    __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    sm.bad = 1;
-                }
-                if (r < keff) {
-                    const uint32_t ix = okw ? word_idx(word) : 0xfffu;
-                    sm.xv[w * keff + r] = (okw && ix != 0xfffu) ? word_val(word) : -INFINITY;
-                    sm.xi[w * keff + r] = (ix == 0xfffu) ? 0x7fffffff : (int)ix;
-                } else if (r == keff) {
-                    sm.xm[w] = okw ? word_val(word) : -INFINITY;
-                } else {
-                    sm.xs[w] = okw ? word_val(word) : 0.f;
-                }
+        // collect every slice's words (bounded polling on the tag)
+        for (int e = tid; e < W * nslot; e += DNT) {
+            const int w = e / nslot, r = e % nslot;
+            const uint64_t *src = lw_words + (int64_t)w * kSlots + r;
+            uint64_t word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            long spins = 0;
+            while (word_tag(word) != tag && ++spins < kSpin) {
+                __builtin_amdgcn_s_sleep(1);
+                word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            __syncthreads();
-
-            // merge: rank every listed entry against all of them
-            const int ne = W * keff;
-            int nkeep = min(keff, m);
-            float gmax = 0.f, den = 1.f;
-            if (a.mode == HTI_TOPP) {
-                gmax = -INFINITY;
-                for (int w = 0; w < W; ++w) gmax = fmaxf(gmax, sm.xm[w]);
-                den = 0.f;
-                for (int w = 0; w < W; ++w)
-                    if (sm.xm[w] > -INFINITY) den += sm.xs[w] * expf(sm.xm[w] - gmax);
+            const bool okw = word_tag(word) == tag;
+            if (!okw) {
+                __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.bad = 1;
             }
-            // Every list is sorted (slot r holds its slice's rank-r entry), so an
-            // entry's global rank is its slot plus, for every other list, the
-            // number of that list's entries ranking before it.  A group of P
-            // lanes (P = W rounded up to a power of two) takes an entry, lane j
-            // binary-searches list j and the group sums the counts with DPP.
-            {
-                int P = 1;
-                while (P < W) P <<= 1;
-                const int lg = tid & (P - 1);
-                const int ngr = DNT / P;
-                int nsteps = 0;
-                while ((1 << nsteps) <= keff) ++nsteps;
-                const uint32_t kinv = (65536u + keff - 1) / keff;   // e / keff for e < 2^10
-                const int lw = min(lg, W - 1) * keff;
-                for (int e = tid / P; e - tid / P < ne; e += ngr) {
+            if (r < keff) {
+                const uint32_t ix = okw ? word_idx(word) : 0xfffu;
+                sm.xv[w * keff + r] = (okw && ix != 0xfffu) ? word_val(word) : -INFINITY;
+                sm.xi[w * keff + r] = (ix == 0xfffu) ? 0x7fffffff : (int)ix;
+            } else {
+                const int q = w * DNW + (r - keff) / 2;
+                if (((r - keff) & 1) == 0) sm.xm[q] = okw ? word_val(word) : -INFINITY;
+                else sm.xs[q] = okw ? word_val(word) : 0.f;
+            }
+        }
+        __syncthreads();                                                   // B2
+
+        // Merge.  Every list is sorted (slot r holds its slice's rank-r
+        // entry), so an entry's global rank is its slot plus, for every other
+        // list, the number of that list's entries ranking before it.  A group
+        // of P lanes (P = W rounded up to a power of two) takes an entry, lane
+        // j binary-searches list j and the group sums the counts with DPP.
+        const int ne = W * keff;
+        int nkeep = min(keff, st.m);
+        {
+            int P = 1;
+            while (P < W) P <<= 1;
+            const int lg = tid & (P - 1);
+            const int ngr = DNT / P;
+            int nsteps = 0;
+            while ((1 << nsteps) <= keff) ++nsteps;
+            const uint32_t kinv = (65536u + keff - 1) / keff;   // e / keff for e < 2^10
+            const int lwo = min(lg, W - 1) * keff;
+            for (int e0 = tid / P; e0 - tid / P < ne; e0 += 2 * ngr) {
+                float ve[2];
+                int ie[2], lo[2], hi[2], wo[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int e = e0 + u * ngr;
                     const bool valid = e < ne;
-                    const float ve = valid ? sm.xv[e] : -INFINITY;
-                    const int ie = valid ? sm.xi[e] : 0x7fffffff;
-                    const int wo = (int)(((uint32_t)e * kinv) >> 16);
-                    int lo = 0;
-                    int hi = (lg < W && lg != wo && ie != 0x7fffffff) ? keff : 0;
-                    for (int step = 0; step < nsteps; ++step) {
-                        const int mid = (lo + hi) >> 1;
-                        const int f = lw + min(mid, keff - 1);
-                        const bool active = lo < hi;
-                        const bool bt = better(sm.xv[f], sm.xi[f], ve, ie);
-                        lo = (active && bt) ? mid + 1 : lo;
-                        hi = (active && !bt) ? mid : hi;
+                    ve[u] = valid ? sm.xv[e] : -INFINITY;
+                    ie[u] = valid ? sm.xi[e] : 0x7fffffff;
+                    wo[u] = (int)(((uint32_t)e * kinv) >> 16);
+                    lo[u] = 0;
+                    hi[u] = (lg < W && lg != wo[u] && ie[u] != 0x7fffffff) ? keff : 0;
+                }
+                for (int step = 0; step < nsteps; ++step) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int mid = (lo[u] + hi[u]) >> 1;
+                        const int f = lwo + min(mid, keff - 1);
+                        const bool active = lo[u] < hi[u];
+                        const bool bt = better(sm.xv[f], sm.xi[f], ve[u], ie[u]);
+                        lo[u] = (active && bt) ? mid + 1 : lo[u];
+                        hi[u] = (active && !bt) ? mid : hi[u];
                     }
-                    int cnt = lo;
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int e = e0 + u * ngr;
+                    int cnt = lo[u];
                     if (P >= 2) cnt += dppi<0xB1>(cnt);
                     if (P >= 4) cnt += dppi<0x4E>(cnt);
                     if (P >= 8) cnt += dppi<0x141>(cnt);
                     if (P >= 16) cnt += dppi<0x140>(cnt);
-                    const int rank = cnt + (e - wo * keff);
-                    if (lg == 0 && valid && ie != 0x7fffffff && rank < nkeep) {
-                        sm.byrank[rank] = ie;
-                        sm.byv[rank] = ve;
+                    const int rank = cnt + (e - wo[u] * keff);
+                    if (lg == 0 && e < ne && ie[u] != 0x7fffffff && rank < nkeep) {
+                        sm.byrank[rank] = ie[u];
+                        sm.byv[rank] = ve[u];
                     }
                 }
             }
-            __syncthreads();
-            if (tid == 0) {
-                int ns = nkeep;
-                if (a.mode == HTI_TOPP) {
-                    // shortest sorted prefix whose softmax mass reaches p
+        }
+        __syncthreads();                                                   // B3
+        if (topp) {
+            // shortest prefix of the sorted kept entries whose softmax mass
+            // (over every candidate of the level) reaches p
+            if (wave == 0) {
+                const int nw = W * DNW;
+                float gmax = -INFINITY;
+                for (int i = lane; i < nw; i += 64) gmax = fmaxf(gmax, sm.xm[i]);
+                gmax = wave_max(gmax);
+                float den = 0.f;
+                for (int i = lane; i < nw; i += 64)
+                    if (sm.xm[i] > -INFINITY) den += sm.xs[i] * __expf(sm.xm[i] - gmax);
+                den = wave_sum(den);
+                if (lane == 0) {
+                    int ns = nkeep;
                     float cum = 0.f;
                     for (int r = 0; r < nkeep; ++r) {
-                        cum += expf(sm.byv[r] - gmax) / den;
+                        cum += __expf(sm.byv[r] - gmax) / den;
                         if (cum >= a.p) {
                             ns = r + 1;
                             break;
                         }
                     }
+                    sm.nkeep = ns;
                 }
-                sm.nkeep = ns;
             }
             __syncthreads();
             nkeep = sm.nkeep;
-            if (tid < nkeep) {
-                const int ix = sm.byrank[tid];
-                int pos = 0;
-                int r = 0;
-                for (; r + 4 <= nkeep; r += 4) {
-                    const int4 b4 = *reinterpret_cast<const int4 *>(&sm.byrank[r]);
-                    pos += (b4.x < ix) + (b4.y < ix) + (b4.z < ix) + (b4.w < ix);
-                }
-                for (; r < nkeep; ++r) pos += sm.byrank[r] < ix;
-                sm.sel[nxt][pos] = (int)cs.id(ix);
-                if (ix >= s0 && ix < s0 + ms) sm.flag[ix - s0] = 1;
+        }
+        // kept set in node order -> next candidate list, kept flags
+        if (tid < nkeep) {
+            const int ix = sm.byrank[tid];
+            int pos = 0;
+            int r = 0;
+            for (; r + 4 <= nkeep; r += 4) {
+                const int4 b4 = *reinterpret_cast<const int4 *>(&sm.byrank[r]);
+                pos += (b4.x < ix) + (b4.y < ix) + (b4.z < ix) + (b4.w < ix);
             }
-            if (tid == 0) sm.nsel[nxt] = nkeep;
-            __syncthreads();
-            softmax_fold(ms, val_row, vr);
+            for (; r < nkeep; ++r) pos += sm.byrank[r] < ix;
+            const int64_t node = st.cs.id(ix);
+            sm.sel[nxt][pos] = (int)node;
+            if (ix >= s0 && ix < s0 + ms) sm.flag[ix - s0] = 1;
+            if (lvl == 1 && node == (L - 1) / b) sm.in_last = 1;
         }
+        if (tid == 0) sm.nsel[nxt] = nkeep;
+        __syncthreads();                                                   // B4
         if (wg == 0 && a.sel) {
-            const int nsel = sm.nsel[nxt];
             int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
-            for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < nsel) ? sm.sel[nxt][r] : -1;
+            for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < nkeep) ? sm.sel[nxt][r] : -1;
         }
+
+        // the next step's gathers go out now; this level's unkept candidates
+        // are folded while they are in flight
+        const Step<T> stc = st;
+        VR vrc[VBS];
+#pragma unroll
+        for (int u = 0; u < VBS; ++u) vrc[u] = vr[u];
         cur = nxt;
-        // Every gather of this level has been consumed: say so to the
-        // compiler, whose wait analysis cannot see through the predicated
-        // loads and would otherwise wait for all memory before each gather of
-        // the next level.
-        __builtin_amdgcn_s_waitcnt(0);
+        st = make_step(lvl - 1, cur);
+        issue_step(st, k0, k1, rb_c, rb_s, vr, qc, qs);
+        probs(ms, zb, true, Mn, alpha);
+        __syncthreads();                                                   // B5
+        fold(stc, s0, ms, zb, vrc);
+        zb ^= 1;
     }
 
-    // token level: children of the kept level-1 nodes, then the orphan tokens
-    {
-        const int nprev = levels > 0 ? sm.nsel[cur] : 0;
-        Cands cs;
-        cs.selp = sm.sel[cur];
-        cs.nprev = nprev;
-        cs.b = b;
-        cs.binv = a.binv;
-        cs.top = (levels == 0);
-        cs.orph0 = levels > 0 ? (int64_t)b * sm.n[1] : 0;
-        const int64_t m0 = levels > 0 ? (int64_t)nprev * b + (L - cs.orph0) : L;
-        bool in = (levels == 0) || (L - 1 >= cs.orph0);
-        if (!in)
-            for (int r = 0; r < nprev; ++r) in |= ((int64_t)cs.selp[r] == (L - 1) / b);
-        const int64_t qpos = m0 - (in ? 1 : 0);
-        const int64_t cpw = (m0 + W - 1) / W;
-        const int64_t t0 = min(m0, (int64_t)wg * cpw);
-        const int64_t t1 = min(m0, t0 + cpw);
-        for (int64_t c0 = t0; c0 < t1; c0 += kSlice) {
-            const int ms = (int)min((int64_t)kSlice, t1 - c0);
-            auto key_row = [&](int i, int) __attribute__((always_inline)) -> const T * {
-                return kc + cs.id((int)(i)) * D;
-            };
-            auto val_row = [&](int i) __attribute__((always_inline)) -> const T * {
-                return vc + cs.id((int)(c0 + i)) * D;
-            };
-            KR k0[KB], k1[KB];
-            float rb_c[PPL], rb_s[PPL];
-            load_batch(ms, (int)c0, 0, 1, key_row, 0, k0, k1, rb_c, rb_s);
-            VR vr[VBS];
-            issue_values(ms, val_row, vr);
-            if (c0 == t0) rotate_query(qpos);
-            for (int i = tid; i < ms; i += DNT) sm.flag[i] = 0;
-            __syncthreads();
-            score_slice(ms, (int)c0, 0, 1, key_row, true, k0, k1, rb_c, rb_s);
-            __syncthreads();
-            softmax_ref(ms);
-            __syncthreads();
-            softmax_fold(ms, val_row, vr);
-            __builtin_amdgcn_s_waitcnt(0);
+    // token level: this workgroup's range of the candidates, in chunks (the
+    // first chunk's gathers were issued with the last level's)
+    for (int c0 = st.s0; c0 < st.t1; c0 += kSlice) {
+        const int ms = (int)min((int64_t)kSlice, st.t1 - c0);
+        if (c0 != st.s0) {
+            load_batch(st, c0, ms, 0, k0, k1, rb_c, rb_s);
+            issue_values(st, c0, ms, vr);
         }
+        score(st, c0, ms, zb, k0, k1, rb_c, rb_s, qc, qs);
+        __syncthreads();
+        float Mn[G], alpha[G];
+        new_max(Mn, alpha);
+        probs(ms, zb, false, Mn, alpha);
+        __syncthreads();
+        fold(st, c0, ms, zb, vr);
+        zb ^= 1;
     }
 
     // Partial state of this slice -> tagged words in the workspace; then every
@@ -646,28 +689,34 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     uint64_t *pw_unit = ws.part + unit * (int64_t)W * G * (D + 2);
     {
         float *red = reinterpret_cast<float *>(hti_dec_lds);     // [DNW][G][D]
+        float lsum[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) lsum[h] = wave_sum(lt[h]);
         __syncthreads();
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e) red[(wave * G + h) * D + lane * DPL + e] = acc[h][e];
+            if (lane == 0) sm.redz[wave][h] = lsum[h];
+        }
         __syncthreads();
         uint64_t *mine = pw_unit + (int64_t)wg * G * (D + 2);
         for (int i = tid; i < G * (D + 2); i += DNT) {
             const int h = i / (D + 2), e = i % (D + 2);
-            float v;
+            float v = 0.f;
             if (e < D) {
-                v = 0.f;
                 for (int w = 0; w < DNW; ++w) v += red[(w * G + h) * D + e];
+            } else if (e == D) {
+                v = M[h];
             } else {
-                v = (e == D) ? sm.M[h] : sm.l[h];
+                for (int w = 0; w < DNW; ++w) v += sm.redz[w][h];
             }
             __hip_atomic_store(&mine[i], ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // Gather n tagged words (word i at src(i)) into LDS dst[i]: every load is
-    // issued first, then only words whose tag is not yet current are polled.
+    // Gather n tagged words (word i at src(i)) into LDS at dst(i): every load
+    // is issued first, then only words whose tag is not yet current are polled.
     auto gather_words = [&](int n, auto src, auto dst) __attribute__((always_inline)) {
         for (int i0 = 0; i0 < n; i0 += 4 * DNT) {
             uint64_t wv[4];
@@ -695,14 +744,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
     };
     // (max, denominator) of every slice per head, and this workgroup's output
-    // columns of every slice's unnormalised output, into LDS
+    // columns of every slice's unnormalised output, into LDS (one round)
     const int cols = (D + W - 1) / W;
     const int d0 = min(D, wg * cols), d1 = min(D, d0 + cols);
     const int nc = d1 - d0;
-    float *mw = sm.z;                                                    // [W][G][2]
-    float *aw = reinterpret_cast<float *>(hti_dec_lds) + DNW * G * D;    // [W][G][nc]
-    __syncthreads();
-    // one round: the (max, denominator) words first, then the columns
+    float *mw = reinterpret_cast<float *>(hti_dec_lds) + DNW * G * D;   // [W][G][2]
+    float *aw = mw + kMaxW * G * 2;                                      // [W][G][nc]
     const int nmw = W * G * 2;
     gather_words(nmw + W * G * nc, [&](int i) __attribute__((always_inline)) {
         if (i < nmw) {
@@ -727,7 +774,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int w = 0; w < W; ++w) {
             const float Mw = mw[(w * G + h) * 2];
             if (Mw == -INFINITY) continue;
-            const float f = expf(Mw - Mx);
+            const float f = __expf(Mw - Mx);
             num += aw[(w * G + h) * nc + c] * f;
             den += mw[(w * G + h) * 2 + 1] * f;
         }
@@ -740,7 +787,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         float den = 0.f;
         for (int w = 0; w < W; ++w) {
             const float Mw = mw[(w * G + h) * 2];
-            if (Mw != -INFINITY) den += mw[(w * G + h) * 2 + 1] * expf(Mw - Mx);
+            if (Mw != -INFINITY) den += mw[(w * G + h) * 2 + 1] * __expf(Mw - Mx);
         }
         a.lse[row + h] = den > 0.f ? Mx + logf(den) : -INFINITY;
     }
@@ -749,13 +796,20 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     if (wg == 0 && tid == 0) ws.epoch[unit] = ws.epoch[unit] + 1u;
 }
 
+template <int G, int D>
+constexpr size_t dec_dyn_bytes()
+{
+    // per-wave partial outputs, then the gathered (max, denominator) and
+    // output columns of every slice
+    return (size_t)(DNW * G * D + kMaxW * G * 2 + kMaxW * G * ((D + kMaxW - 1) / kMaxW) + G * D) *
+           sizeof(float);
+}
+
 template <typename T, int D, int G>
 static hipError_t dec_launch(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
 {
     auto kern = k_decode_split<T, D, G>;
-    // value stage; also holds the final per-wave partial sums
-    // the per-wave partial sums and the gathered output columns of every slice
-    const size_t dyn = (size_t)(DNW * G * D + G * D + kMaxW * G) * sizeof(float);
+    const size_t dyn = dec_dyn_bytes<G, D>();
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -797,8 +851,19 @@ hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t un
 template <typename T, int D, int G>
 static hipError_t dec_capacity(int *blocks_per_cu)
 {
-    const size_t dyn = (size_t)(DNW * G * D + G * D + kMaxW * G) * sizeof(float);
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_decode_split<T, D, G>, DNT, dyn);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_decode_split<T, D, G>, DNT,
+                                                        dec_dyn_bytes<G, D>());
+}
+
+template <typename T, int D>
+static hipError_t dec_capacity_g(int G, int *per_cu)
+{
+    switch (G) {
+    case 1: return dec_capacity<T, D, 1>(per_cu);
+    case 2: return dec_capacity<T, D, 2>(per_cu);
+    case 4: return dec_capacity<T, D, 4>(per_cu);
+    default: return dec_capacity<T, D, 8>(per_cu);
+    }
 }
 
 hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W)
@@ -810,23 +875,10 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        if (a.t.dtype == HTI_BF16) {
-            if (a.t.D == 128) {
-                e = a.t.G == 1 ? dec_capacity<bf16_t, 128, 1>(&per_cu) : a.t.G == 2 ? dec_capacity<bf16_t, 128, 2>(&per_cu)
-                  : a.t.G == 4 ? dec_capacity<bf16_t, 128, 4>(&per_cu) : dec_capacity<bf16_t, 128, 8>(&per_cu);
-            } else {
-                e = a.t.G == 1 ? dec_capacity<bf16_t, 64, 1>(&per_cu) : a.t.G == 2 ? dec_capacity<bf16_t, 64, 2>(&per_cu)
-                  : a.t.G == 4 ? dec_capacity<bf16_t, 64, 4>(&per_cu) : dec_capacity<bf16_t, 64, 8>(&per_cu);
-            }
-        } else {
-            if (a.t.D == 128) {
-                e = a.t.G == 1 ? dec_capacity<float, 128, 1>(&per_cu) : a.t.G == 2 ? dec_capacity<float, 128, 2>(&per_cu)
-                  : a.t.G == 4 ? dec_capacity<float, 128, 4>(&per_cu) : dec_capacity<float, 128, 8>(&per_cu);
-            } else {
-                e = a.t.G == 1 ? dec_capacity<float, 64, 1>(&per_cu) : a.t.G == 2 ? dec_capacity<float, 64, 2>(&per_cu)
-                  : a.t.G == 4 ? dec_capacity<float, 64, 4>(&per_cu) : dec_capacity<float, 64, 8>(&per_cu);
-            }
-        }
+        if (a.t.dtype == HTI_BF16)
+            e = a.t.D == 128 ? dec_capacity_g<bf16_t, 128>(a.t.G, &per_cu) : dec_capacity_g<bf16_t, 64>(a.t.G, &per_cu);
+        else
+            e = a.t.D == 128 ? dec_capacity_g<float, 128>(a.t.G, &per_cu) : dec_capacity_g<float, 64>(a.t.G, &per_cu);
         if (e != hipSuccess) return e;
         cached_key = key;
         // one workgroup per CU keeps every unit's slices on distinct CUs

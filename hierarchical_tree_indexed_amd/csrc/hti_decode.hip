@@ -61,14 +61,16 @@ struct DSmem {
     int sel[2][kMaxSel];
     int nsel[2];
     float redz[DNW][G];               // per-wave maxima of the logits
-    float xv[kMaxW * kMaxSel + 4] __attribute__((aligned(16)));   // collected lists: score, index
-    int xi[kMaxW * kMaxSel + 4] __attribute__((aligned(16)));
+    float xv[kMaxW * kMaxSel] __attribute__((aligned(16)));   // collected lists: score, index
+    int xi[kMaxW * kMaxSel] __attribute__((aligned(16)));
     float xm[kMaxW * DNW], xs[kMaxW * DNW];    // per-wave max and exp-sum (top-p)
     int byrank[kMaxSel] __attribute__((aligned(16)));   // kept entries by rank: index, score
     float byv[kMaxSel];
     int nkeep;
     int in_last;                      // the query's own leaf was kept (level 1)
-    int64_t n[HTI_MAX_LEVELS + 1];
+    int n[HTI_MAX_LEVELS + 1];        // nodes per level (n[0] = tokens; all < 2^31)
+    const void *lkp[HTI_MAX_LEVELS];  // this unit's level keys / values
+    const void *lvp[HTI_MAX_LEVELS];
     uint32_t tag;
     int bad;                          // a wait of this workgroup timed out
 };
@@ -96,8 +98,8 @@ struct Step {
     int nref;            // keys per row (R at summary levels, 1 at tokens)
     int m;               // candidates
     int s0, ms;          // this workgroup's slice (first chunk at the token level)
-    int64_t t1;          // token level: end of this workgroup's range
-    int64_t qpos;        // RoPE position of the query
+    int t1;              // token level: end of this workgroup's range
+    int qpos;            // RoPE position of the query
     bool take_all;       // every candidate is kept (no scoring)
 };
 
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     constexpr int DPL = D / 64;
     using KR = typename Raw<T, PPL>::type;
     constexpr int KRW = sizeof(KR) / 4 > 0 ? (int)sizeof(KR) / 4 : 1;
-    constexpr int KB = 40 / (2 * KRW);                 // key rows per quarter per batch
+    constexpr int KB = (40 / (2 * KRW)) < 16 ? 40 / (2 * KRW) : 16;   // key rows per quarter per batch
     using VR = typename Raw<T, DPL>::type;
     constexpr int VBS = 8;                             // value rows per wave held in registers
     __shared__ DSmem<G> sm;
@@ -130,12 +132,14 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const int b = t.b, levels = t.levels, R = t.R;
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
     const bool topp = a.mode == HTI_TOPP;
-    const int nslot = keff + (topp ? 2 * DNW : 0);
     uint64_t *xw = ws.words + (int64_t)unit * levels * W * kSlots;
 
+    if (tid < levels) {
+        sm.lkp[tid] = (const T *)t.lk[tid] + bh * t.ncap[tid + 1] * R * D;
+        sm.lvp[tid] = (const T *)t.lv[tid] + bh * t.ncap[tid + 1] * D;
+    }
     if (tid == 0) {
-        const int64_t L0 = t.len[bi];
-        int64_t n = L0;
+        int n = (int)t.len[bi];
         sm.n[0] = n;
         const int bs = __builtin_ctz((unsigned)b);
         const bool pow2 = (b & (b - 1)) == 0;
@@ -172,7 +176,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     }
     __syncthreads();
     const uint32_t tag = sm.tag;
-    const int64_t L = sm.n[0];
+    const int L = sm.n[0];
+    const int last_leaf = L > 0 ? (L - 1) / b : -1;   // level-1 node of the query token
 
     const T *kc = (const T *)t.kc + bh * t.ncap[0] * D;
     const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
@@ -188,11 +193,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         st.cs.b = b;
         st.cs.binv = a.binv;
         st.cs.top = top;
-        st.cs.orph0 = top ? 0 : (int64_t)b * sm.n[lvl + 1];
+        const int orph0 = top ? 0 : b * sm.n[lvl + 1];
+        st.cs.orph0 = orph0;
         if (lvl >= 1) {
-            st.m = (int)(top ? sm.n[lvl] : (int64_t)nprev * b + (sm.n[lvl] - st.cs.orph0));
-            st.kb = (const T *)t.lk[lvl - 1] + bh * t.ncap[lvl] * R * D;
-            st.vb = (const T *)t.lv[lvl - 1] + bh * t.ncap[lvl] * D;
+            st.m = top ? sm.n[lvl] : nprev * b + (sm.n[lvl] - orph0);
+            st.kb = (const T *)sm.lkp[lvl - 1];
+            st.vb = (const T *)sm.lvp[lvl - 1];
             st.nref = R;
             st.take_all = (a.mode == HTI_TOPK) ? (st.m <= a.k) : (st.m <= 1);
             const int cpw = (st.m + W - 1) / W;
@@ -203,28 +209,35 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         } else {
             // the query token is a candidate when its leaf was kept or it is
             // an orphan; it then sits last
-            const int64_t m0 = top ? L : (int64_t)nprev * b + (L - st.cs.orph0);
-            const bool in = top || (L - 1 >= st.cs.orph0) || sm.in_last != 0;
-            st.m = (int)m0;
+            const int m0 = top ? L : nprev * b + (L - orph0);
+            const bool in = top || (L - 1 >= orph0) || sm.in_last != 0;
+            st.m = m0;
             st.kb = kc;
             st.vb = vc;
             st.nref = 1;
             st.take_all = false;
-            const int64_t cpw = (m0 + W - 1) / W;
-            const int64_t t0 = min(m0, (int64_t)wg * cpw);
+            const int cpw = (m0 + W - 1) / W;
+            const int t0 = min(m0, wg * cpw);
             st.t1 = min(m0, t0 + cpw);
-            st.s0 = (int)t0;
-            st.ms = (int)min((int64_t)kSlice, st.t1 - t0);
+            st.s0 = t0;
+            st.ms = min(kSlice, (int)st.t1 - t0);
             st.qpos = m0 - (in ? 1 : 0);
         }
         return st;
     };
 
     // ---- gathers ----
-    // one batch of a quarter-wave's keys (items it0.., item = candidate x
-    // reference key) plus the RoPE row of its first candidate
-    auto load_batch = [&](const Step<T> &st, int s0, int ms, int it0, KR (&k0)[KB], KR (&k1)[KB],
-                          float (&rb_c)[PPL], float (&rb_s)[PPL]) __attribute__((always_inline)) {
+    // One batch of a quarter-wave's keys: its items it0.. (item = candidate x
+    // reference key), at most KB of them.  Lane `sub` derives the row of item
+    // it0 + sub (clamped into the batch, so surplus loads re-read a row of
+    // it) and DPP row broadcasts hand row u to the whole quarter: the
+    // address arithmetic is done once per lane instead of once per row, and
+    // every load is issued back to back.  Also the RoPE row of the batch's
+    // first candidate.
+    // With go == false every load reads the (always valid) RoPE table
+    // instead, so that loads never sit behind a branch.
+    auto load_batch = [&](const Step<T> &st, int s0, int ms, int it0, bool go, KR (&k0)[KB], KR (&k1)[KB],
+                          float (&rb)[2 * PPL]) __attribute__((always_inline)) {
         const int nref = st.nref;
         const int cpq = (ms + DNQ - 1) / DNQ;
         const int c_beg = min(ms, quarter * cpq);
@@ -232,52 +245,60 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int nitems = (c_end - c_beg) * nref;
         const int KBR = (KB / nref) * nref;
         const int nb = min(nitems - it0, KBR);
-        int ci = c_beg + it0 / nref, j = 0;
+        const int itl = it0 + (nb > 0 ? min(sub, nb - 1) : 0);
+        const int cl = itl / nref;
+        const int cand = min(c_beg + cl, ms - 1);
+        const uint32_t row = go ? (uint32_t)(st.cs.id(s0 + max(cand, 0)) * nref + (itl - cl * nref)) : 0u;
+        const T *kbase = go ? st.kb : reinterpret_cast<const T *>(t.rope);
 #pragma unroll
-        for (int u = 0; u < KB; ++u)
-            if (u < nb) {
-                const T *kp = st.kb + (st.cs.id(s0 + ci) * nref + j) * D;
-                k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
-                k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
-                if (++j == nref) {
-                    j = 0;
-                    ++ci;
-                }
-            }
-        if (nb > 0) {
-            const float2 *rp = t.rope + (int64_t)(s0 + c_beg + it0 / nref) * (D / 2) + sub * PPL;
+        for (int u = 0; u < KB; ++u) {
+            const uint32_t ru = (uint32_t)row_bcast((int)row, u);
+            const T *kp = kbase + (size_t)ru * D;
+            k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
+            k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
+        }
+        const float4 *rp = reinterpret_cast<const float4 *>(
+            t.rope + (int64_t)max(0, s0 + min(c_beg + it0 / nref, ms - 1)) * (D / 2) + sub * PPL);
 #pragma unroll
-            for (int e = 0; e < PPL; ++e) {
-                const float2 c2 = rp[e];
-                rb_c[e] = c2.x;
-                rb_s[e] = c2.y;
-            }
+        for (int e = 0; e < PPL / 2; ++e) {
+            const float4 c4 = rp[e];
+            rb[4 * e] = c4.x;
+            rb[4 * e + 1] = c4.y;
+            rb[4 * e + 2] = c4.z;
+            rb[4 * e + 3] = c4.w;
         }
     };
     // value rows of the slice, wave w owning rows w, w + DNW, ...: the first
-    // VBS per wave go to registers.  Every load is issued (rows past the slice
-    // re-read its last row) so that each writes its register unconditionally.
-    auto issue_values = [&](const Step<T> &st, int s0, int ms, VR (&vr)[VBS]) __attribute__((always_inline)) {
+    // VBS per wave go to registers.  Lane u of the wave derives the row of its
+    // u-th row (rows past the slice re-read its last row) and hands it to the
+    // wave through a readlane, so the loads go out back to back.
+    auto issue_values = [&](const Step<T> &st, int s0, int ms, bool go, VR (&vr)[VBS]) __attribute__((always_inline)) {
+        const int rl = go ? (int)st.cs.id(s0 + max(0, min(wave + DNW * (lane & (VBS - 1)), ms - 1))) : 0;
+        const T *vbase = go ? st.vb : reinterpret_cast<const T *>(t.rope);
 #pragma unroll
         for (int u = 0; u < VBS; ++u) {
-            const int i = min(wave + DNW * u, ms - 1);
-            vr[u] = *reinterpret_cast<const VR *>(st.vb + st.cs.id(s0 + i) * D + lane * DPL);
+            const uint32_t ru = (uint32_t)__builtin_amdgcn_readlane(rl, u);
+            vr[u] = *reinterpret_cast<const VR *>(vbase + (size_t)ru * D + lane * DPL);
         }
     };
-    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&rb_c)[PPL],
-                          float (&rb_s)[PPL], VR (&vr)[VBS], float (&qc)[PPL], float (&qs)[PPL])
-        __attribute__((always_inline)) {
-        if (st.take_all) return;
-        if (st.ms > 0) {
-            load_batch(st, st.s0, st.ms, 0, k0, k1, rb_c, rb_s);
-            issue_values(st, st.s0, st.ms, vr);
-        }
-        const float2 *rp = t.rope + st.qpos * (D / 2) + sub * PPL;
+    // (RoPE rows stay as loaded, (cos, sin) pairs: splitting them would copy
+    // registers still being loaded and so wait for the gathers right here)
+    // Every load is unconditional (a step with nothing to gather reads the
+    // RoPE table instead): a register that kept its old value on some path
+    // would have to be copied at the loop edge, which waits for its load.
+    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&rb)[2 * PPL], VR (&vr)[VBS],
+                          float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
+        const bool go = !st.take_all && st.ms > 0;
+        load_batch(st, st.s0, st.ms, 0, go, k0, k1, rb);
+        issue_values(st, st.s0, st.ms, go, vr);
+        const float4 *rp = reinterpret_cast<const float4 *>(t.rope + st.qpos * (D / 2) + sub * PPL);
 #pragma unroll
-        for (int e = 0; e < PPL; ++e) {
-            const float2 c2 = rp[e];
-            qc[e] = c2.x;
-            qs[e] = c2.y;
+        for (int e = 0; e < PPL / 2; ++e) {
+            const float4 c4 = rp[e];
+            qcs[4 * e] = c4.x;
+            qcs[4 * e + 1] = c4.y;
+            qcs[4 * e + 2] = c4.z;
+            qcs[4 * e + 3] = c4.w;
         }
     };
 
@@ -287,8 +308,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // head into sm.z[zb], group scores into sm.s (with -inf padding), kept
     // flags cleared, per-wave maxima of the logits into sm.redz.
     auto score = [&](const Step<T> &st, int s0, int ms, int zb, KR (&k0)[KB], KR (&k1)[KB],
-                     float (&rb_c)[PPL], float (&rb_s)[PPL], const float (&qc)[PPL],
-                     const float (&qs)[PPL]) __attribute__((always_inline)) {
+                     float (&rb)[2 * PPL], const float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
         float qa[G][PPL], qb[G][PPL];
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -296,8 +316,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             for (int e = 0; e < PPL; ++e) {
                 const float x0 = sm.qraw[h * D + sub * PPL + e];
                 const float x1 = sm.qraw[h * D + D / 2 + sub * PPL + e];
-                qa[h][e] = x0 * qc[e] - x1 * qs[e];
-                qb[h][e] = x0 * qs[e] + x1 * qc[e];
+                qa[h][e] = x0 * qcs[2 * e] - x1 * qcs[2 * e + 1];
+                qb[h][e] = x0 * qcs[2 * e + 1] + x1 * qcs[2 * e];
             }
         const int nref = st.nref;
         const int cpq = (ms + DNQ - 1) / DNQ;
@@ -311,7 +331,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         float *zz = sm.z[zb];
         for (int it0 = 0; it0 < nitems; it0 += KBR) {
             const int nb = min(nitems - it0, KBR);
-            if (it0 > 0) load_batch(st, s0, ms, it0, k0, k1, rb_c, rb_s);
+            if (it0 > 0) load_batch(st, s0, ms, it0, true, k0, k1, rb);
             int ci = c_beg + it0 / nref, j = 0;
             float best = -INFINITY;
             float zb_[G];
@@ -320,8 +340,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             float cc[PPL], ss[PPL];
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
-                cc[e] = rb_c[e];
-                ss[e] = rb_s[e];
+                cc[e] = rb[2 * e];
+                ss[e] = rb[2 * e + 1];
             }
 #pragma unroll
             for (int u = 0; u < KB; ++u) {
@@ -448,31 +468,28 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // ---- the steps ----
     int cur = 0, zb = 0;
     KR k0[KB], k1[KB];
-    float rb_c[PPL], rb_s[PPL], qc[PPL], qs[PPL];
+    float rb[2 * PPL], qcs[2 * PPL];
     VR vr[VBS];
     Step<T> st = make_step(levels, 0);
-    issue_step(st, k0, k1, rb_c, rb_s, vr, qc, qs);
+    issue_step(st, k0, k1, rb, vr, qcs);
 
     for (int lvl = levels; lvl >= 1; --lvl) {
         const int nxt = cur ^ 1;
-        if (st.take_all) {
+        const bool scored = !st.take_all;
+        const int s0 = st.s0, ms = st.ms;
+        float Mn[G], alpha[G];
+        if (!scored) {
             for (int i = tid; i < st.m; i += DNT) sm.sel[nxt][i] = (int)st.cs.id(i);
             if (tid == 0) sm.nsel[nxt] = st.m;
-            if (lvl == 1 && tid < st.m && st.cs.id(tid) == (L - 1) / b) sm.in_last = 1;
+            if (lvl == 1 && tid < st.m && st.cs.id(tid) == last_leaf) sm.in_last = 1;
             __syncthreads();
             if (wg == 0 && a.sel) {
                 int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
                 for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < st.m) ? sm.sel[nxt][r] : -1;
             }
-            cur = nxt;
-            st = make_step(lvl - 1, cur);
-            issue_step(st, k0, k1, rb_c, rb_s, vr, qc, qs);
-            continue;
-        }
-        const int s0 = st.s0, ms = st.ms;
-        score(st, s0, ms, zb, k0, k1, rb_c, rb_s, qc, qs);
+        } else {
+        score(st, s0, ms, zb, k0, k1, rb, qcs);
         __syncthreads();                                                   // B1
-        float Mn[G], alpha[G];
         new_max(Mn, alpha);
 
         // rank inside the slice: Gr threads per candidate, each comparing it
@@ -516,10 +533,19 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
         }
 
-        // collect every slice's words (bounded polling on the tag)
-        for (int e = tid; e < W * nslot; e += DNT) {
-            const int w = e / nslot, r = e % nslot;
-            const uint64_t *src = lw_words + (int64_t)w * kSlots + r;
+        // collect every slice's words (bounded polling on the tag); list w
+        // lands at xv/xi[w * kp4 ..], padded to a multiple of 4 entries
+        const int kp4 = (keff + 3) & ~3;
+        const int nrow = kp4 + (topp ? 2 * DNW : 0);
+        for (int e = tid; e < W * nrow; e += DNT) {
+            const int w = e / nrow, r = e % nrow;
+            if (r >= keff && r < kp4) {
+                sm.xv[w * kp4 + r] = -INFINITY;
+                sm.xi[w * kp4 + r] = 0x7fffffff;
+                continue;
+            }
+            const int slot = r < keff ? r : r - kp4 + keff;
+            const uint64_t *src = lw_words + (int64_t)w * kSlots + slot;
             uint64_t word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             long spins = 0;
             while (word_tag(word) != tag && ++spins < kSpin) {
@@ -533,11 +559,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
             if (r < keff) {
                 const uint32_t ix = okw ? word_idx(word) : 0xfffu;
-                sm.xv[w * keff + r] = (okw && ix != 0xfffu) ? word_val(word) : -INFINITY;
-                sm.xi[w * keff + r] = (ix == 0xfffu) ? 0x7fffffff : (int)ix;
+                sm.xv[w * kp4 + r] = (okw && ix != 0xfffu) ? word_val(word) : -INFINITY;
+                sm.xi[w * kp4 + r] = (ix == 0xfffu) ? 0x7fffffff : (int)ix;
             } else {
-                const int q = w * DNW + (r - keff) / 2;
-                if (((r - keff) & 1) == 0) sm.xm[q] = okw ? word_val(word) : -INFINITY;
+                const int q = w * DNW + (slot - keff) / 2;
+                if (((slot - keff) & 1) == 0) sm.xm[q] = okw ? word_val(word) : -INFINITY;
                 else sm.xs[q] = okw ? word_val(word) : 0.f;
             }
         }
@@ -546,22 +572,23 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         // Merge.  Every list is sorted (slot r holds its slice's rank-r
         // entry), so an entry's global rank is its slot plus, for every other
         // list, the number of that list's entries ranking before it.  A group
-        // of P lanes (P = W rounded up to a power of two) takes an entry, lane
-        // j binary-searches list j and the group sums the counts with DPP.
-        const int ne = W * keff;
+        // of P lanes (P = W rounded up to a power of two) takes an entry and
+        // lane j counts in list j -- by comparing with all of it for short
+        // lists, by binary search otherwise -- and the group sums the counts
+        // with DPP.
+        const int ne = W * kp4;
         int nkeep = min(keff, st.m);
         {
             int P = 1;
             while (P < W) P <<= 1;
             const int lg = tid & (P - 1);
             const int ngr = DNT / P;
-            int nsteps = 0;
-            while ((1 << nsteps) <= keff) ++nsteps;
-            const uint32_t kinv = (65536u + keff - 1) / keff;   // e / keff for e < 2^10
-            const int lwo = min(lg, W - 1) * keff;
+            const uint32_t kinv = (65536u + kp4 - 1) / kp4;   // e / kp4 for e < 2^10
+            const int lwo = min(lg, W - 1) * kp4;
             for (int e0 = tid / P; e0 - tid / P < ne; e0 += 2 * ngr) {
                 float ve[2];
-                int ie[2], lo[2], hi[2], wo[2];
+                int ie[2], cnt[2], wo[2];
+                bool act[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int e = e0 + u * ngr;
@@ -569,29 +596,45 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     ve[u] = valid ? sm.xv[e] : -INFINITY;
                     ie[u] = valid ? sm.xi[e] : 0x7fffffff;
                     wo[u] = (int)(((uint32_t)e * kinv) >> 16);
-                    lo[u] = 0;
-                    hi[u] = (lg < W && lg != wo[u] && ie[u] != 0x7fffffff) ? keff : 0;
+                    act[u] = lg < W && lg != wo[u] && ie[u] != 0x7fffffff;
+                    cnt[u] = 0;
                 }
-                for (int step = 0; step < nsteps; ++step) {
+                if (kp4 <= 16) {
+                    for (int r = 0; r < kp4; r += 4) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.xv[lwo + r]);
+                        const int4 i4 = *reinterpret_cast<const int4 *>(&sm.xi[lwo + r]);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int mid = (lo[u] + hi[u]) >> 1;
-                        const int f = lwo + min(mid, keff - 1);
-                        const bool active = lo[u] < hi[u];
-                        const bool bt = better(sm.xv[f], sm.xi[f], ve[u], ie[u]);
-                        lo[u] = (active && bt) ? mid + 1 : lo[u];
-                        hi[u] = (active && !bt) ? mid : hi[u];
+                        for (int u = 0; u < 2; ++u)
+                            cnt[u] += better(v4.x, i4.x, ve[u], ie[u]) + better(v4.y, i4.y, ve[u], ie[u]) +
+                                      better(v4.z, i4.z, ve[u], ie[u]) + better(v4.w, i4.w, ve[u], ie[u]);
                     }
+                } else {
+                    int lo[2] = {0, 0}, hi[2] = {kp4, kp4};
+                    int nsteps = 0;
+                    while ((1 << nsteps) <= kp4) ++nsteps;
+                    for (int step = 0; step < nsteps; ++step) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int mid = (lo[u] + hi[u]) >> 1;
+                            const int f = lwo + min(mid, kp4 - 1);
+                            const bool active = lo[u] < hi[u];
+                            const bool bt = better(sm.xv[f], sm.xi[f], ve[u], ie[u]);
+                            lo[u] = (active && bt) ? mid + 1 : lo[u];
+                            hi[u] = (active && !bt) ? mid : hi[u];
+                        }
+                    }
+                    cnt[0] = lo[0];
+                    cnt[1] = lo[1];
                 }
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int e = e0 + u * ngr;
-                    int cnt = lo[u];
-                    if (P >= 2) cnt += dppi<0xB1>(cnt);
-                    if (P >= 4) cnt += dppi<0x4E>(cnt);
-                    if (P >= 8) cnt += dppi<0x141>(cnt);
-                    if (P >= 16) cnt += dppi<0x140>(cnt);
-                    const int rank = cnt + (e - wo[u] * keff);
+                    int c = act[u] ? cnt[u] : 0;
+                    if (P >= 2) c += dppi<0xB1>(c);
+                    if (P >= 4) c += dppi<0x4E>(c);
+                    if (P >= 8) c += dppi<0x141>(c);
+                    if (P >= 16) c += dppi<0x140>(c);
+                    const int rank = c + (e - wo[u] * kp4);
                     if (lg == 0 && e < ne && ie[u] != 0x7fffffff && rank < nkeep) {
                         sm.byrank[rank] = ie[u];
                         sm.byv[rank] = ve[u];
@@ -641,7 +684,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             const int64_t node = st.cs.id(ix);
             sm.sel[nxt][pos] = (int)node;
             if (ix >= s0 && ix < s0 + ms) sm.flag[ix - s0] = 1;
-            if (lvl == 1 && node == (L - 1) / b) sm.in_last = 1;
+            if (lvl == 1 && node == last_leaf) sm.in_last = 1;
         }
         if (tid == 0) sm.nsel[nxt] = nkeep;
         __syncthreads();                                                   // B4
@@ -650,30 +693,34 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < nkeep) ? sm.sel[nxt][r] : -1;
         }
 
-        // the next step's gathers go out now; this level's unkept candidates
-        // are folded while they are in flight
+        }
+        // the next step's gathers go out now (one issue point for both paths,
+        // so the loaded registers carry into the next iteration as they are);
+        // this level's unkept candidates are folded while they are in flight
         const Step<T> stc = st;
         VR vrc[VBS];
 #pragma unroll
         for (int u = 0; u < VBS; ++u) vrc[u] = vr[u];
         cur = nxt;
         st = make_step(lvl - 1, cur);
-        issue_step(st, k0, k1, rb_c, rb_s, vr, qc, qs);
-        probs(ms, zb, true, Mn, alpha);
-        __syncthreads();                                                   // B5
-        fold(stc, s0, ms, zb, vrc);
-        zb ^= 1;
+        issue_step(st, k0, k1, rb, vr, qcs);
+        if (scored) {
+            probs(ms, zb, true, Mn, alpha);
+            __syncthreads();                                               // B5
+            fold(stc, s0, ms, zb, vrc);
+            zb ^= 1;
+        }
     }
 
     // token level: this workgroup's range of the candidates, in chunks (the
     // first chunk's gathers were issued with the last level's)
     for (int c0 = st.s0; c0 < st.t1; c0 += kSlice) {
-        const int ms = (int)min((int64_t)kSlice, st.t1 - c0);
+        const int ms = min(kSlice, st.t1 - c0);
         if (c0 != st.s0) {
-            load_batch(st, c0, ms, 0, k0, k1, rb_c, rb_s);
-            issue_values(st, c0, ms, vr);
+            load_batch(st, c0, ms, 0, true, k0, k1, rb);
+            issue_values(st, c0, ms, true, vr);
         }
-        score(st, c0, ms, zb, k0, k1, rb_c, rb_s, qc, qs);
+        score(st, c0, ms, zb, k0, k1, rb, qcs);
         __syncthreads();
         float Mn[G], alpha[G];
         new_max(Mn, alpha);
@@ -707,7 +754,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             if (e < D) {
                 for (int w = 0; w < DNW; ++w) v += red[(w * G + h) * D + e];
             } else if (e == D) {
-                v = M[h];
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) v = (hh == h) ? M[hh] : v;
             } else {
                 for (int w = 0; w < DNW; ++w) v += sm.redz[w][h];
             }

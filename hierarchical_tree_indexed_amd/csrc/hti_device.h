@@ -157,6 +157,29 @@ __device__ __forceinline__ int sum16i(int v)
     v += dppi<0x140>(v);
     return v;
 }
+// Value of lane n of this lane's 16-lane row (DPP row_newbcast); n must fold
+// to a constant after unrolling.
+__device__ __forceinline__ int row_bcast(int v, int n)
+{
+    switch (n) {
+    case 0: return dppi<0x150>(v);
+    case 1: return dppi<0x151>(v);
+    case 2: return dppi<0x152>(v);
+    case 3: return dppi<0x153>(v);
+    case 4: return dppi<0x154>(v);
+    case 5: return dppi<0x155>(v);
+    case 6: return dppi<0x156>(v);
+    case 7: return dppi<0x157>(v);
+    case 8: return dppi<0x158>(v);
+    case 9: return dppi<0x159>(v);
+    case 10: return dppi<0x15A>(v);
+    case 11: return dppi<0x15B>(v);
+    case 12: return dppi<0x15C>(v);
+    case 13: return dppi<0x15D>(v);
+    case 14: return dppi<0x15E>(v);
+    default: return dppi<0x15F>(v);
+    }
+}
 // wave-wide results, uniform across the wave
 __device__ __forceinline__ float wave_sum(float v)
 {

@@ -174,13 +174,18 @@ hti_status launched(hipError_t e, const char *what)
 }
 
 struct PrefillWs {
-    size_t part_acc, part_ml, qr, kr, total;
+    size_t part_acc, part_ml, qr, kr, top_s, top_z, total;
+    int64_t ntop;       // top-level capacity when the top level is scored on the matrix cores, else 0
 };
 
 PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
 {
     PrefillWs w{};
     const size_t rows = (size_t)c->B * (size_t)T;
+    int64_t ncap[HTI_MAX_LEVELS + 1];
+    caps(c, ncap);
+    w.ntop = (c->levels >= 1 && ncap[c->levels] >= 1 && ncap[c->levels] * c->R <= kTopCols)
+                 ? ncap[c->levels] : 0;
     size_t off = 0;
     w.part_acc = off;
     off += align256(rows * c->Hq * c->d * sizeof(float));
@@ -190,6 +195,10 @@ PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
     off += align256(rows * c->Hq * c->d * 2);
     w.kr = off;
     off += align256(rows * c->Hkv * c->d * 2);
+    w.top_s = off;
+    off += align256(rows * c->Hkv * (size_t)w.ntop * sizeof(float));
+    w.top_z = off;
+    off += align256(rows * c->Hq * (size_t)w.ntop * sizeof(float));
     w.total = off;
     return w;
 }
@@ -396,8 +405,6 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     ta.binv = binv_of(tree->cfg.b);
     ta.part_acc = (float *)(wb + w.part_acc);
     ta.part_ml = (float *)(wb + w.part_ml);
-    hipError_t e = launch_traverse(ta, true, units, hs);
-    if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
 
     PrefillArgs pa{};
     pa.t = ta.t;
@@ -405,6 +412,21 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     pa.k = k_blk;
     pa.v = v_blk;
     pa.T = T;
+    hipError_t e = hipSuccess;
+    if (w.ntop > 0) {
+        // the top level of every query of the block, scored on the matrix cores
+        pa.top_s = (float *)(wb + w.top_s);
+        pa.top_z = (float *)(wb + w.top_z);
+        pa.ntop_stride = (int)w.ntop;
+        e = launch_top_scores(pa, hs);
+        if (e != hipSuccess) return launched(e, "sparse_prefill(top scores)");
+        ta.top_s = pa.top_s;
+        ta.top_z = pa.top_z;
+        ta.ntop_stride = pa.ntop_stride;
+    }
+    e = launch_traverse(ta, true, units, hs);
+    if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
+
     pa.part_acc = ta.part_acc;
     pa.part_ml = ta.part_ml;
     pa.out = out;

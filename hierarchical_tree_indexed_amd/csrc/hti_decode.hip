@@ -112,7 +112,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     constexpr int DPL = D / 64;
     using KR = typename Raw<T, PPL>::type;
     constexpr int KRW = sizeof(KR) / 4 > 0 ? (int)sizeof(KR) / 4 : 1;
-    constexpr int KB = (40 / (2 * KRW)) < 16 ? 40 / (2 * KRW) : 16;   // key rows per quarter per batch
+    // key rows per quarter per batch: at least one candidate's HTI_MAX_R
+    // reference keys (a batch never splits a candidate), at most 16 (DPP row)
+    constexpr int KB0 = 40 / (2 * KRW);
+    constexpr int KB = KB0 < HTI_MAX_R ? HTI_MAX_R : (KB0 > 16 ? 16 : KB0);
+    static_assert(KB >= HTI_MAX_R && KB <= 16, "key batch");
     using VR = typename Raw<T, DPL>::type;
     constexpr int VBS = 8;                             // value rows per wave held in registers
     __shared__ DSmem<G> sm;

@@ -79,7 +79,10 @@ struct PrefillArgs {
     float *out, *lse;
     void *qr, *kr;             // rotated block q/k (bf16 staging) [B, Hq|Hkv, T, D]
 };
-hipError_t launch_top_scores(const PrefillArgs &a, int64_t ntop_max, hipStream_t s);
+// Top-level scoring of a prefill block on the matrix cores; used when the top
+// level has at most kTopCols (node, reference key) columns.
+constexpr int kTopCols = 64;
+hipError_t launch_top_scores(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_inblock_attention(const PrefillArgs &a, hipStream_t s);
 

@@ -250,6 +250,155 @@ hipError_t launch_inblock_attention(const PrefillArgs &a, hipStream_t s)
     return a.t.D == 128 ? inblock_d<128>(a, s) : inblock_d<64>(a, s);
 }
 
-hipError_t launch_top_scores(const PrefillArgs &, int64_t, hipStream_t) { return hipSuccess; }
+// ----------------------------------------------------------------------------
+// Top level of the prefix tree, scored for every query of the block at once.
+//
+// Every query of the block sees the same candidate list at the top (all top
+// nodes, node c at RoPE position c) and sits at the same position n_top, so
+// the logits are one product per KV group: rows = (query, head) pairs with
+// the head's query rotated by n_top, columns = (node, reference key) pairs
+// with the key rotated by its node index.  The product runs on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32): the rotated operands are not bf16 values, and
+// fp32 operands keep the logits, and so the selections, those of fp32
+// arithmetic.  Each lane ends with 4 rows x 1 column of logits; the group
+// score (mean over the group's heads) and the best reference key per node
+// are reduced across lanes with DPP, and the winning lane writes the node's
+// group score and per-head logits for the traversal to pick up.
+// ----------------------------------------------------------------------------
+namespace {
+constexpr int kTopRows = 64;    // (query, head) rows per workgroup: 16 per wave
+
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// (s, j) of the partner lane wins over (best, bj): larger score, then lower j
+__device__ __forceinline__ void top_keep(float &best, int &bj, float s2, int j2)
+{
+    const bool take = (s2 > best) || (s2 == best && j2 < bj);
+    best = take ? s2 : best;
+    bj = take ? j2 : bj;
+}
+} // namespace
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
+{
+    const TreeArgs &t = a.t;
+    const int bi = blockIdx.y / t.Hkv, g = blockIdx.y % t.Hkv;
+    const int T = a.T, R = t.R;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int n = (int)t.len[bi];
+    for (int l = 1; l <= t.levels; ++l) n /= t.b;
+    const int ntop = n, ncol = n * R;
+    if (ncol == 0) return;
+
+    __shared__ float kr[kTopCols][D + 4];   // rotated top keys, [column][element]
+    const int64_t bh = (int64_t)bi * t.Hkv + g;
+    const bf16_t *kb = (const bf16_t *)t.lk[t.levels - 1] + bh * t.ncap[t.levels] * R * D;
+    for (int i = tid; i < ncol * (D / 2); i += 256) {
+        const int col = i / (D / 2), e = i % (D / 2);
+        const int c = col / R;
+        const float x0 = bf2f(kb[(int64_t)col * D + e]), x1 = bf2f(kb[(int64_t)col * D + e + D / 2]);
+        const float2 cs = t.rope[(int64_t)c * (D / 2) + e];
+        kr[col][e] = x0 * cs.x - x1 * cs.y;
+        kr[col][e + D / 2] = x0 * cs.y + x1 * cs.x;
+    }
+
+    // A operand: lane l holds row l % 16 of the wave's tile at k = l / 16 of
+    // every 4-wide k step, i.e. elements d = 4 kk + l / 16 (the rotate-half
+    // partner d + D/2 has the same residue, so each lane rotates its own)
+    const int kq = lane >> 4;
+    const int row = blockIdx.x * kTopRows + wave * 16 + (lane & 15);
+    const bool rvalid = row < T * G;
+    const int tq = rvalid ? row / G : 0, hq = row % G;
+    const bf16_t *qp = (const bf16_t *)a.q + (((int64_t)bi * T + tq) * t.Hq + g * G + hq) * D;
+    const float2 *rq = t.rope + (int64_t)ntop * (D / 2);
+    float qa[D / 4];
+#pragma unroll
+    for (int kk = 0; kk < D / 8; ++kk) {
+        const int d = 4 * kk + kq;
+        const float x0 = bf2f(qp[d]), x1 = bf2f(qp[d + D / 2]);
+        const float2 cs = rq[d];
+        qa[kk] = rvalid ? x0 * cs.x - x1 * cs.y : 0.f;
+        qa[kk + D / 8] = rvalid ? x0 * cs.y + x1 * cs.x : 0.f;
+    }
+    __syncthreads();
+
+    // the rows a lane's accumulators hold: 4 * (lane / 16) + r of the tile
+    const int rbase = blockIdx.x * kTopRows + wave * 16 + 4 * kq;
+    for (int c0 = 0; c0 < ncol; c0 += 16) {
+        const int col = c0 + (lane & 15);
+        const bool cvalid = col < ncol;
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 4; ++kk) {
+            const float bv = cvalid ? kr[col][4 * kk + kq] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], bv, acc, 0, 0, 0);
+        }
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = acc[r] * t.scale;
+        const int j = col % R, c = col / R;
+        // queries held by this lane: G <= 4 -> 4 / G of them (rows grouped by
+        // G); G == 8 -> one query spread over this lane and lane ^ 16
+        constexpr int NQL = G <= 4 ? 4 / G : 1;
+#pragma unroll
+        for (int u = 0; u < NQL; ++u) {
+            float sgrp = 0.f;
+            if (G <= 4) {
+#pragma unroll
+                for (int h = 0; h < (G <= 4 ? G : 1); ++h) sgrp += z[u * G + h];
+            } else {
+                const float own = (z[0] + z[1]) + (z[2] + z[3]);
+                const float oth = __shfl_xor(own, 16);
+                sgrp = (kq & 1) ? oth + own : own + oth;
+            }
+            sgrp = sgrp / (float)G;
+            float best = cvalid ? sgrp : -INFINITY;
+            int bj = j;
+            if (R >= 2) top_keep(best, bj, dppf<0xB1>(best), dppi<0xB1>(bj));
+            if (R >= 4) top_keep(best, bj, dppf<0x4E>(best), dppi<0x4E>(bj));
+            if (R >= 8) top_keep(best, bj, dppf<0x141>(best), dppi<0x141>(bj));
+            const int r0 = rbase + u * (G <= 4 ? G : 4);     // first row of this query
+            const bool writer = cvalid && j == bj && r0 < T * G && (G <= 4 || (kq & 1) == 0);
+            if (writer) {
+                const int tt = r0 / G;
+                a.top_s[(((int64_t)bi * T + tt) * t.Hkv + g) * a.ntop_stride + c] = best;
+                if (G <= 4) {
+#pragma unroll
+                    for (int h = 0; h < (G <= 4 ? G : 1); ++h)
+                        a.top_z[(((int64_t)bi * T + tt) * t.Hq + g * G + h) * a.ntop_stride + c] = z[u * G + h];
+                }
+            }
+            if (G == 8 && cvalid && j == bj && r0 - 4 * (kq & 1) < T * G) {
+                // each half of the lane pair writes its own four heads
+                const int tt = (r0 - 4 * (kq & 1)) / G;
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    a.top_z[(((int64_t)bi * T + tt) * t.Hq + g * G + 4 * (kq & 1) + h) * a.ntop_stride + c] =
+                        z[h];
+            }
+        }
+    }
+}
+
+template <int D>
+static hipError_t top_d(const PrefillArgs &a, hipStream_t s)
+{
+    const int G = a.t.G;
+    dim3 grid((unsigned)((a.T * G + kTopRows - 1) / kTopRows), (unsigned)(a.t.B * a.t.Hkv)), block(256);
+    switch (G) {
+    case 1: hipLaunchKernelGGL((k_top_scores<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_top_scores<D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_top_scores<D, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_top_scores<D, 8>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_top_scores(const PrefillArgs &a, hipStream_t s)
+{
+    if (a.T <= 0 || a.t.levels < 1) return hipSuccess;
+    return a.t.D == 128 ? top_d<128>(a, s) : top_d<64>(a, s);
+}
 
 } // namespace hti

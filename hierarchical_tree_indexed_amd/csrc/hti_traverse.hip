@@ -87,7 +87,11 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
     constexpr int VRW = sizeof(VR) / 4 > 0 ? (int)sizeof(VR) / 4 : 1;
     // register budget of the in-flight batches: decode keeps a whole level in
     // flight; prefill keeps them small so that many units share a CU
-    constexpr int KB = (STAGE ? 40 : 24) / (2 * KRW); // key rows per quarter per batch
+    // key rows per quarter per batch; a batch holds at least one candidate's
+    // HTI_MAX_R reference keys (it never splits a candidate)
+    constexpr int KB0 = (STAGE ? 40 : 24) / (2 * KRW);
+    constexpr int KB = KB0 < HTI_MAX_R ? HTI_MAX_R : KB0;
+    static_assert(KB >= HTI_MAX_R, "key batch");
     constexpr int VB = 16 / VRW;                      // value rows per wave per batch
     constexpr int RB = D * (int)sizeof(T);            // bytes of one row
     constexpr int LPR = RB / 16;                      // lanes per row in a 16-byte gather

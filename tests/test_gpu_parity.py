@@ -111,6 +111,9 @@ DECODE_CASES = [
     W.ZHA2M.replace(name="topp_p1_cap32", L=3000, levels=2, p=1.0, cap=32, R=2),
     W.ZHA2M.replace(name="topp_p05", L=20000, levels=3, p=0.5, cap=8, R=1),
     W.DEC128K.replace(name="k32", L=33000, b=16, levels=3, k=32),
+    # eight reference keys per node in fp32 at d = 128: a key batch must hold
+    # all of a candidate's keys
+    W.DEC128K.replace(name="f32_d128_r8", dtype="f32", Hq=8, Hkv=2, L=6000, b=16, levels=2, k=3, R=8),
 ]
 
 
@@ -285,6 +288,16 @@ PF = W.PREFILL.replace(name="pf_small")
                                          (0, 130, 2), (40, 64, 1), (2000, 33, 0)])
 def test_prefill_parity(P0, T, levels):
     _check_prefill(PF.replace(levels=levels, k=8 if levels else 32), P0, T)
+
+
+@pytest.mark.parametrize("Hq,Hkv,R,k,P0", [(32, 8, 1, 8, 32 * 32 * 12 + 70), (8, 8, 1, 8, 32 * 32 * 12 + 70),
+                                          (16, 8, 2, 8, 32 * 32 * 12 + 31), (64, 8, 1, 8, 32 * 32 * 9 + 3),
+                                          (32, 8, 8, 4, 32 * 32 * 7 + 5)])
+def test_prefill_scored_top_level(Hq, Hkv, R, k, P0):
+    """The top level has more nodes than are kept, so it is scored for the
+    whole block at once on the matrix cores (G = 1, 2, 4, 8; R = 1, 2, 8)."""
+    w = PF.replace(Hq=Hq, Hkv=Hkv, R=R, k=k, levels=2)
+    _check_prefill(w, P0, 40)
 
 
 def test_prefill_topp_r4():

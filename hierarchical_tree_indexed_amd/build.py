@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhti.so")
-SOURCES = ["hti_api.hip", "hti_build.hip", "hti_traverse.hip", "hti_decode.hip", "hti_prefill.hip"]
+SOURCES = ["hti_api.hip", "hti_build.hip", "hti_traverse.hip", "hti_decode.hip", "hti_prefill.hip",
+           "hti_prefill_walk.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-parameter",

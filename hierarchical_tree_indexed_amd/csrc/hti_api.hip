@@ -424,7 +424,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
         ta.top_z = pa.top_z;
         ta.ntop_stride = pa.ntop_stride;
     }
-    e = launch_traverse(ta, true, units, hs);
+    e = launch_prefill_walk(ta, bounds(&tree->cfg, sel, T).max_summary, units, hs);
     if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
 
     pa.part_acc = ta.part_acc;

@@ -73,22 +73,23 @@ __host__ __device__ constexpr size_t pw_wave_words(int G, int D, int MC)
 }
 
 template <int D, int G, int MJ>
-__global__ __launch_bounds__(256) void k_prefill_walk(TravArgs a, int MC)
+__global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 {
     using T = bf16_t;
     constexpr int PPL = D / 32;           // rotate-half pairs per lane (16-lane row per key)
     using KR = typename Raw<T, PPL>::type;
     constexpr int KB = 8;                 // key items per quarter per batch (>= HTI_MAX_R)
     static_assert(KB >= HTI_MAX_R, "a batch holds one candidate's reference keys");
-    constexpr int EPL = D / 16;           // value elements per lane (a quarter holds one row)
-    using VRr = typename Raw<T, 4>::type; // 8 bytes
-    constexpr int VPL = EPL / 4;          // 8-byte pieces per lane per row
-    constexpr int VB = 8;                 // value rows per quarter per batch
+    constexpr int DPL = D / 64;           // value elements per lane (the wave holds one row)
+    using VR = typename Raw<T, DPL>::type;
+    constexpr int VB = 16;                // value rows per batch
     static_assert(MJ <= 32, "kept bits fit one word");
     extern __shared__ __attribute__((aligned(16))) unsigned char pw_lds[];
 
     const TreeArgs &t = a.t;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform in the wave: say so, so that everything the
+    // unit derives from it lives in scalar registers
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane & 15, quarter = lane >> 4;
     const int64_t unit = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
     const int64_t units = (int64_t)t.B * a.Nq * t.Hkv;
@@ -131,13 +132,13 @@ __global__ __launch_bounds__(256) void k_prefill_walk(TravArgs a, int MC)
         st_c[e] = c2.x;
         st_s[e] = c2.y;
     }
-    float M[G], lt[G], acc[G][EPL];
+    float M[G], lt[G], acc[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         M[h] = -INFINITY;
         lt[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+        for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
     }
     wave_sync();
 
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256) void k_prefill_walk(TravArgs a, int MC)
             M[h] = mn;
             lt[h] *= alpha;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+            for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
         }
         for (int jj = 0; jj * 64 < m; ++jj) {
             const int c = jj * 64 + lane;
@@ -289,34 +290,30 @@ __global__ __launch_bounds__(256) void k_prefill_walk(TravArgs a, int MC)
         wave_sync();
     };
 
-    // ---- p * v over candidates [0, m) (values at vb + id * D): quarter q
-    // takes rows q, q + 4, ...; lane `sub` holds elements sub*EPL .. +EPL
+    // ---- p * v over candidates [0, m) (values at vb + id * D): the whole
+    // wave takes one row per load (lane l holds elements l*DPL ..), VB rows
+    // per batch, row ids derived by lanes 0..VB-1 and handed out by readlane
     auto fold = [&](const Cands &cs, const T *vb, int c0, int m) __attribute__((always_inline)) {
-        const int rpq = (m + 3) / 4;
-        for (int r0 = 0; r0 < rpq; r0 += VB) {
-            const int nb = min(rpq - r0, VB);
-            const int il = quarter + 4 * (r0 + min(sub, nb - 1));
-            const uint32_t row = (uint32_t)cs.id(c0 + min(il, m - 1));
-            VRr vr[VB][VPL];
+        for (int r0 = 0; r0 < m; r0 += VB) {
+            const int nb = min(m - r0, VB);
+            const int rl = (int)cs.id(c0 + r0 + min(lane & (VB - 1), nb - 1));
+            VR vr[VB];
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
-                const uint32_t ru = (uint32_t)row_bcast((int)row, u);
-                const T *vp = vb + (size_t)ru * D + sub * EPL;
-#pragma unroll
-                for (int w = 0; w < VPL; ++w) vr[u][w] = *reinterpret_cast<const VRr *>(vp + 4 * w);
+                const uint32_t ru = (uint32_t)__builtin_amdgcn_readlane(rl, u);
+                vr[u] = *reinterpret_cast<const VR *>(vb + (size_t)ru * D + lane * DPL);
             }
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
-                const int i = quarter + 4 * (r0 + u);
-                if (u < nb && i < m) {
-                    float v[EPL];
-#pragma unroll
-                    for (int w = 0; w < VPL; ++w) cvt(vr[u][w], v + 4 * w);
+                if (u < nb) {
+                    float v[DPL];
+                    cvt(vr[u], v);
+                    const float *pz = &sZ[(r0 + u) * G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float p = sZ[i * G + h];
+                        const float p = pz[h];
 #pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[h][e] += p * v[e];
+                        for (int e = 0; e < DPL; ++e) acc[h][e] += p * v[e];
                     }
                 }
             }
@@ -446,23 +443,13 @@ __global__ __launch_bounds__(256) void k_prefill_walk(TravArgs a, int MC)
         }
     }
 
-    // ---- partial state: denominators over the wave, outputs over the four
-    // quarters (each accumulated its own rows)
+    // ---- partial state
     const int64_t row0 = ((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const float l = wave_sum(lt[h]);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float v = acc[h][e];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            acc[h][e] = v;
-        }
-        if (quarter == 0) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) a.part_acc[(row0 + h) * D + sub * EPL + e] = acc[h][e];
-        }
+        for (int e = 0; e < DPL; ++e) a.part_acc[(row0 + h) * D + lane * DPL + e] = acc[h][e];
         if (lane == 0) {
             a.part_ml[(row0 + h) * 2 + 0] = M[h];
             a.part_ml[(row0 + h) * 2 + 1] = l;

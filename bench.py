@@ -153,23 +153,62 @@ def bench_prefill(args):
         ts.tree_build([w.L] * w.B)
         ts.sparse_prefill(sel, qb, kb, vb, out, ws, lse)
 
-    for _ in range(args.prefill_warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.prefill_reps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.prefill_reps
+    def timed(fn, reps):
+        for _ in range(args.prefill_warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(run, args.prefill_reps)
+    # the dense part alone: the same block over an empty prefix leaves only
+    # the in-block causal attention on the matrix cores (plus the rotation
+    # of the block and an empty traversal)
+    ts0, sel0 = treeset(w.replace(L=0), w.L, K, V, T=w.T)
+    ts0.tree_build([0] * w.B)
+    ws0 = torch.empty(ts0.prefill_workspace_bytes(sel0, w.T), dtype=torch.uint8, device=DEV)
+    ms_dense = timed(lambda: ts0.sparse_prefill(sel0, qb, kb, vb, out, ws0, lse), args.prefill_reps)
     pairs = w.T * (w.T + 1) // 2
     inblock_flop = pairs * w.Hq * 4 * w.d
-    res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9)
+    res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9,
+               dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12)
     log(f"[prefill] {res}")
-    del K, V, ts, ws
+    del K, V, ts, ws, ts0, ws0
     torch.cuda.empty_cache()
     return res
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the decode kernel source as it is now (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    src = os.path.join(ROOT, "hierarchical_tree_indexed_amd", "csrc", "hti_decode.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha1") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: 1 GiB read + 1 GiB written per launch."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[copy] 5 copies of {n} bytes")
 
 
 def cpu_baseline(args):
@@ -191,17 +230,21 @@ def cpu_baseline(args):
         trees[g] = oracle.build_tree(Kh, Vh, refs[g], w.b, w.levels, bf16=True)
         data[g] = (Kh, Vh)
     del K, V
-    qs = torch.randn((nq, w.Hq, w.d)).to(torch.bfloat16).float().numpy()
-    t0 = time.perf_counter()
-    for i in range(nq):
+    # as many queries as fit about ten seconds (at least four)
+    gen = torch.Generator().manual_seed(7)
+    budget_s, nq, el = 10.0, 0, 0.0
+    while nq < 4 or (el < budget_s and nq < 100000):
+        q = torch.randn((w.Hq, w.d), generator=gen).to(torch.bfloat16).float().numpy()
+        t0 = time.perf_counter()
         for g in groups:
-            oracle.query(trees[g], data[g][0], data[g][1], qs[i, g * w.G:(g + 1) * w.G], k=w.k)
-    el = time.perf_counter() - t0
+            oracle.query(trees[g], data[g][0], data[g][1], q[g * w.G:(g + 1) * w.G], k=w.k)
+        el += time.perf_counter() - t0
+        nq += 1
     per_query = el / nq * (w.Hkv / len(groups))       # all 8 groups of one query
     return dict(value=1.0 / per_query, unit="queries/s", cores=1, kind="oracle",
                 sample=f"{nq} decode queries x {len(groups)} of {w.Hkv} KV groups of one "
-                       f"1,048,576-token sequence, time scaled x{w.Hkv // len(groups)} to all "
-                       f"groups; tree build untimed; single thread")
+                       f"1,048,576-token sequence ({el:.1f} s), time scaled x{w.Hkv // len(groups)} "
+                       f"to all groups; tree build untimed; single thread")
 
 
 def main():
@@ -213,12 +256,17 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "all"], default="all")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the method's sequences and KV heads are independent "
               "and this build runs on a single MI355X; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     hti.lib()
     dec = bench_decode(args) if args.only in ("decode", "all") else None
     pre = bench_prefill(args) if args.only in ("prefill", "all") else None
@@ -245,10 +293,14 @@ def main():
         "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
         "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
         "roofline": ({"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": dec["gbs"] / HBM_PEAK_GBS, "traffic": None,
-                      "kernel": "k_traverse (decode)",
+                      "frac": dec["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                      "kernel": "k_decode_split",
                       "kernel_ms": dec["decode_kernel_ms"],
                       "bytes_per_launch": dec["bytes_per_launch"]} if dec else None),
+        "prefill_roofline": ({"bound": "mfma", "achieved": pre["dense_tflops"], "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": pre["dense_tflops"] / BF16_PEAK_TFLOPS,
+                              "kernel": "k_inblock (causal in-block attention, bf16 MFMA)",
+                              "dense_ms": pre["dense_ms"], "gflop": pre["inblock_gflop"]} if pre else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -320,3 +320,46 @@ def test_prefill_T1_equals_decode():
     dout, _, dsel = _decode(ts, w, qb[:, :1])
     assert np.array_equal(psel[:, 0], dsel[:, 0])
     assert np.abs(pout[:, 0] - dout[:, 0]).max() < 2e-2
+
+
+# --------------------------------------------------------------------------- graph capture
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_graph_replay_matches_eager(split):
+    """A step of tree_append + sparse_decode captured into a HIP graph gives,
+    on every replay, what the same calls give eagerly: a second tree set
+    runs the calls eagerly between the replays, from the same start."""
+    w = W.DEC128K.replace(name="graph", B=2, L=32 * 156 + 29, levels=2, needles=0)   # completes a node
+    steps = 4
+    Lcap = w.L + steps
+    K, V = W.gen_kv(w, Lcap=Lcap)
+    refs = W.gen_refs(w)
+    tg = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    te = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    tg.tree_build([w.L] * w.B)
+    te.tree_build([w.L] * w.B)
+    sel = select_of(w)
+    q = W.gen_queries(w).to(DEV).contiguous()
+    kn, vn = W.gen_append(w, 0, device=DEV)
+    kn, vn = kn.contiguous(), vn.contiguous()
+    og = torch.empty((w.B, q.shape[1], w.Hq, w.d), dtype=torch.float32, device=DEV)
+    oe = torch.empty_like(og)
+    # workspaces exist before capture (nothing is allocated inside the graph)
+    tg.decode_workspace(sel, q.shape[1])
+    te.decode_workspace(sel, q.shape[1])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            tg.tree_append(kn, vn)
+            tg.sparse_decode(sel, q, og, split=split)
+    torch.cuda.synchronize()
+    for r in range(steps):
+        graph.replay()
+        torch.cuda.synchronize()
+        te.tree_append(kn, vn)
+        te.sparse_decode(sel, q, oe, split=split)
+        torch.cuda.synchronize()
+        assert torch.equal(tg.len, te.len), r
+        assert torch.equal(og, oe), f"replay {r}: max diff {(og - oe).abs().max().item()}"
+        assert torch.equal(tg.k_cache, te.k_cache) and torch.equal(tg.lvl_k[0], te.lvl_k[0]), r

@@ -94,7 +94,7 @@ __device__ __forceinline__ int better(float va, int ia, float vb, int ib)
 template <typename T>
 struct Step {
     Cands cs;
-    const T *kb, *vb;    // key / value rows of this unit: row r at kb + (r * nref + j) * D
+    gptr<T> kb, vb;      // key / value rows of this unit: row r at kb + (r * nref + j) * D
     int nref;            // keys per row (R at summary levels, 1 at tokens)
     int m;               // candidates
     int s0, ms;          // this workgroup's slice (first chunk at the token level)
@@ -156,17 +156,18 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         sm.bad = 0;
         sm.in_last = 0;
     }
-    const T *qp = (const T *)a.q + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
+    const gptr<float2> rope = to_global<float2>(t.rope);
+    const gptr<T> qp = to_global<T>(a.q) + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
     for (int i = tid; i < G * D; i += DNT) {
         float v;
-        load_vec<T, 1>(qp + i, &v);
+        cvt(gload<typename Raw<T, 1>::type>(qp + i), &v);
         sm.qraw[i] = v;
     }
     // angle step of each of this lane's RoPE frequencies (row 1 of the table)
     float st_c[PPL], st_s[PPL];
 #pragma unroll
     for (int e = 0; e < PPL; ++e) {
-        const float2 c2 = t.rope[(D / 2) + sub * PPL + e];
+        const float2 c2 = gload<float2>(rope + (D / 2) + sub * PPL + e);
         st_c[e] = c2.x;
         st_s[e] = c2.y;
     }
@@ -183,8 +184,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const int L = sm.n[0];
     const int last_leaf = L > 0 ? (L - 1) / b : -1;   // level-1 node of the query token
 
-    const T *kc = (const T *)t.kc + bh * t.ncap[0] * D;
-    const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
+    const gptr<T> kc = to_global<T>(t.kc) + bh * t.ncap[0] * D;
+    const gptr<T> vc = to_global<T>(t.vc) + bh * t.ncap[0] * D;
 
     // ---- the candidates of a step ----
     // level lvl >= 1 (parents in sm.sel[cur]) or the token level (lvl == 0)
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         st.cs.orph0 = orph0;
         if (lvl >= 1) {
             st.m = top ? sm.n[lvl] : nprev * b + (sm.n[lvl] - orph0);
-            st.kb = (const T *)sm.lkp[lvl - 1];
-            st.vb = (const T *)sm.lvp[lvl - 1];
+            st.kb = to_global<T>(sm.lkp[lvl - 1]);
+            st.vb = to_global<T>(sm.lvp[lvl - 1]);
             st.nref = R;
             st.take_all = (a.mode == HTI_TOPK) ? (st.m <= a.k) : (st.m <= 1);
             const int cpw = (st.m + W - 1) / W;
@@ -253,19 +254,19 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int cl = itl / nref;
         const int cand = min(c_beg + cl, ms - 1);
         const uint32_t row = go ? (uint32_t)(st.cs.id(s0 + max(cand, 0)) * nref + (itl - cl * nref)) : 0u;
-        const T *kbase = go ? st.kb : reinterpret_cast<const T *>(t.rope);
+        const gptr<T> kbase = go ? st.kb : to_global<T>(t.rope);
 #pragma unroll
         for (int u = 0; u < KB; ++u) {
             const uint32_t ru = (uint32_t)row_bcast((int)row, u);
-            const T *kp = kbase + (size_t)ru * D;
-            k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
-            k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
+            const gptr<T> kp = kbase + (size_t)ru * D;
+            k0[u] = gload<KR>(kp + sub * PPL);
+            k1[u] = gload<KR>(kp + D / 2 + sub * PPL);
         }
-        const float4 *rp = reinterpret_cast<const float4 *>(
-            t.rope + (int64_t)max(0, s0 + min(c_beg + it0 / nref, ms - 1)) * (D / 2) + sub * PPL);
+        const gptr<float4> rp = (gptr<float4>)(
+            rope + (int64_t)max(0, s0 + min(c_beg + it0 / nref, ms - 1)) * (D / 2) + sub * PPL);
 #pragma unroll
         for (int e = 0; e < PPL / 2; ++e) {
-            const float4 c4 = rp[e];
+            const float4 c4 = gload<float4>(rp + e);
             rb[4 * e] = c4.x;
             rb[4 * e + 1] = c4.y;
             rb[4 * e + 2] = c4.z;
@@ -278,11 +279,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // wave through a readlane, so the loads go out back to back.
     auto issue_values = [&](const Step<T> &st, int s0, int ms, bool go, VR (&vr)[VBS]) __attribute__((always_inline)) {
         const int rl = go ? (int)st.cs.id(s0 + max(0, min(wave + DNW * (lane & (VBS - 1)), ms - 1))) : 0;
-        const T *vbase = go ? st.vb : reinterpret_cast<const T *>(t.rope);
+        const gptr<T> vbase = go ? st.vb : to_global<T>(t.rope);
 #pragma unroll
         for (int u = 0; u < VBS; ++u) {
             const uint32_t ru = (uint32_t)__builtin_amdgcn_readlane(rl, u);
-            vr[u] = *reinterpret_cast<const VR *>(vbase + (size_t)ru * D + lane * DPL);
+            vr[u] = gload<VR>(vbase + (size_t)ru * D + lane * DPL);
         }
     };
     // (RoPE rows stay as loaded, (cos, sin) pairs: splitting them would copy
@@ -295,10 +296,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const bool go = !st.take_all && st.ms > 0;
         load_batch(st, st.s0, st.ms, 0, go, k0, k1, rb);
         issue_values(st, st.s0, st.ms, go, vr);
-        const float4 *rp = reinterpret_cast<const float4 *>(t.rope + st.qpos * (D / 2) + sub * PPL);
+        const gptr<float4> rp = (gptr<float4>)(rope + st.qpos * (D / 2) + sub * PPL);
 #pragma unroll
         for (int e = 0; e < PPL / 2; ++e) {
-            const float4 c4 = rp[e];
+            const float4 c4 = gload<float4>(rp + e);
             qcs[4 * e] = c4.x;
             qcs[4 * e + 1] = c4.y;
             qcs[4 * e + 2] = c4.z;
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
         for (int i = wave + DNW * VBS; i < ms; i += DNW) {
             float v[DPL];
-            load_vec<T, DPL>(st.vb + st.cs.id(s0 + i) * D + lane * DPL, v);
+            cvt(gload<VR>(st.vb + st.cs.id(s0 + i) * D + lane * DPL), v);
             add_row(i, v);
         }
     };
@@ -474,10 +475,28 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     KR k0[KB], k1[KB];
     float rb[2 * PPL], qcs[2 * PPL];
     VR vr[VBS];
-    Step<T> st = make_step(levels, 0);
+    // Upper levels that keep every candidate need no gathers: their kept
+    // lists follow from the node counts alone, so they are taken here and the
+    // first gathers are those of the first scored level.
+    int lvl = levels;
+    Step<T> st = make_step(lvl, 0);
+    while (lvl >= 1 && st.take_all) {
+        const int nxt = cur ^ 1;
+        for (int i = tid; i < st.m; i += DNT) sm.sel[nxt][i] = (int)st.cs.id(i);
+        if (tid == 0) sm.nsel[nxt] = st.m;
+        if (lvl == 1 && tid < st.m && st.cs.id(tid) == last_leaf) sm.in_last = 1;
+        __syncthreads();
+        if (wg == 0 && a.sel) {
+            int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
+            for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < st.m) ? sm.sel[nxt][r] : -1;
+        }
+        cur = nxt;
+        --lvl;
+        st = make_step(lvl, cur);
+    }
     issue_step(st, k0, k1, rb, vr, qcs);
 
-    for (int lvl = levels; lvl >= 1; --lvl) {
+    for (; lvl >= 1; --lvl) {
         const int nxt = cur ^ 1;
         const bool scored = !st.take_all;
         const int s0 = st.s0, ms = st.ms;

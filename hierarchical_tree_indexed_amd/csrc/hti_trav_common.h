@@ -64,4 +64,28 @@ struct Cands {
 
 constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Pointer into global memory, so that loads through it are global (not flat)
+// loads even when the pointer itself came through LDS: a flat load also counts
+// against the LDS wait counter, and every later LDS wait would then wait for
+// the gather too.
+template <typename T> using gptr = const __attribute__((address_space(1))) T *;
+template <typename T> __device__ __forceinline__ gptr<T> to_global(const void *p)
+{
+    return (gptr<T>)(const T *)p;
+}
+// loads of the HIP vector types go through the matching native vector type
+template <typename V> struct NativeOf { using type = V; };
+template <> struct NativeOf<uint2> { using type = unsigned __attribute__((ext_vector_type(2))); };
+template <> struct NativeOf<uint4> { using type = unsigned __attribute__((ext_vector_type(4))); };
+template <> struct NativeOf<float2> { using type = float __attribute__((ext_vector_type(2))); };
+template <> struct NativeOf<float4> { using type = float __attribute__((ext_vector_type(4))); };
+template <typename V, typename T> __device__ __forceinline__ V gload(gptr<T> p)
+{
+    using N = typename NativeOf<V>::type;
+    const N n = *(gptr<N>)p;
+    V v;
+    __builtin_memcpy(&v, &n, sizeof(V));
+    return v;
+}
+
 } // namespace hti

@@ -174,9 +174,11 @@ hti_status launched(hipError_t e, const char *what)
 }
 
 struct PrefillWs {
-    size_t part_acc, part_ml, qr, kr, top_s, top_z, total;
+    size_t part_acc, part_ml, qr, kr, vt, top_s, top_z, total;
     int64_t ntop;       // top-level capacity when the top level is scored on the matrix cores, else 0
 };
+
+size_t inblock_tp(int32_t T) { return ((size_t)T + kInblockKeys - 1) / kInblockKeys * kInblockKeys; }
 
 PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
 {
@@ -195,6 +197,8 @@ PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
     off += align256(rows * c->Hq * c->d * 2);
     w.kr = off;
     off += align256(rows * c->Hkv * c->d * 2);
+    w.vt = off;
+    off += align256((size_t)c->B * inblock_tp(T) * c->Hkv * c->d * 2);
     w.top_s = off;
     off += align256(rows * c->Hkv * (size_t)w.ntop * sizeof(float));
     w.top_z = off;
@@ -433,6 +437,8 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     pa.lse = lse;
     pa.qr = wb + w.qr;
     pa.kr = wb + w.kr;
+    pa.vt = wb + w.vt;
+    pa.Tp = (int)inblock_tp(T);
     e = launch_rotate_block(pa, hs);
     if (e != hipSuccess) return launched(e, "sparse_prefill(rotate)");
     return launched(launch_inblock_attention(pa, hs), "sparse_prefill(inblock)");

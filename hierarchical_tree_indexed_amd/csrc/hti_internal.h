@@ -81,10 +81,14 @@ struct PrefillArgs {
     const float *part_acc, *part_ml;
     float *out, *lse;
     void *qr, *kr;             // rotated block q/k (bf16 staging) [B, Hq|Hkv, T, D]
+    void *vt;                  // block v transposed (bf16 staging) [B, Hkv, D, Tp]
+    int Tp;                    // T rounded up to the in-block key tile
 };
 // Top-level scoring of a prefill block on the matrix cores; used when the top
 // level has at most kTopCols (node, reference key) columns.
 constexpr int kTopCols = 64;
+// Key tile of the in-block product; the transposed V rows are padded to it.
+constexpr int kInblockKeys = 64;
 hipError_t launch_top_scores(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_inblock_attention(const PrefillArgs &a, hipStream_t s);

@@ -65,181 +65,302 @@ hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s)
 }
 
 // ----------------------------------------------------------------------------
-// In-block causal attention (flash style) merged with the prefix partials.
-//
-// Work split: a workgroup owns QB*16 consecutive queries of every head of one
-// KV group; wave w handles head g*G + (w % G) and queries q0 + 16*(w / G) ..
-// +15.  Keys advance in tiles of 32 staged through LDS (K row-major, V
-// transposed), shared by all the waves of the group.  Scores are computed
-// transposed, S^T = K Q^T, so a lane's accumulator column is one query: the
-// row statistics of the online softmax need only two cross-lane steps, and the
-// probabilities already sit in the B-operand layout of O^T += V^T P^T.
+// V of the block transposed per KV head for the P V product: vt [B, Hkv, D,
+// Tp] bf16 with Tp = T rounded up to the key tile; keys past T are zero.
+// Within each aligned group of 32 keys the columns are permuted: column
+// 8*j + 4*m + i holds key 16*m + 4*j + i (j, i in 0..3, m in 0..1), the key
+// that the S^T product leaves in quarter-wave j of the 16-key tile m.
 // ----------------------------------------------------------------------------
 namespace {
-constexpr int KT = 32;          // keys per tile
-constexpr int KPAD = 8;         // bf16 padding of a K row in LDS
-constexpr int VPAD = 4;         // bf16 padding of a V^T row in LDS
+constexpr int IKT = kInblockKeys;   // keys per tile of the in-block product
 }
 
-template <int D, int G, int NWV>
-__global__ __launch_bounds__(NWV * 64) void k_inblock(PrefillArgs a)
+template <int D>
+__global__ __launch_bounds__(256) void k_transpose_v(PrefillArgs a)
 {
-    constexpr int NTH = NWV * 64;
-    constexpr int QB = NWV / G;              // 16-query sub-blocks per workgroup
-    constexpr int KS = D / 32;               // k-steps of the QK^T product
-    constexpr int DT = D / 16;               // d-tiles of the PV product
-    __shared__ __attribute__((aligned(16))) bf16_t sK[KT * (D + KPAD)];
-    __shared__ __attribute__((aligned(16))) bf16_t sVt[D * (KT + VPAD)];
+    constexpr int W = D / 2 + 1;                 // padded row of 32-bit words
+    __shared__ uint32_t tw[IKT * W];
+    const TreeArgs &t = a.t;
+    const int kt0 = blockIdx.x * IKT, g = blockIdx.y, bi = blockIdx.z;
+    for (int c = threadIdx.x; c < IKT * D / 8; c += 256) {
+        const int key = c / (D / 8), ch = c % (D / 8);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (kt0 + key < a.T)
+            v = *reinterpret_cast<const uint4 *>(
+                (const bf16_t *)a.v + (((int64_t)bi * a.T + kt0 + key) * t.Hkv + g) * D + 8 * ch);
+        uint32_t *r = tw + key * W + 4 * ch;
+        r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+    }
+    __syncthreads();
+    bf16_t *dst = (bf16_t *)a.vt + ((int64_t)bi * t.Hkv + g) * D * (int64_t)a.Tp + kt0;
+    for (int c = threadIdx.x; c < D * (IKT / 8); c += 256) {
+        const int d = c / (IKT / 8), k8 = c % (IKT / 8);
+        // columns 8*k8 .. 8*k8+7: group k8/4, quarter j = k8%4, then (m, i)
+        const int kbase = 32 * (k8 >> 2) + 4 * (k8 & 3);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key0 = kbase + 16 * (e >> 1) + 2 * (e & 1);   // columns 2e, 2e+1
+            const uint32_t lo = tw[key0 * W + d / 2] >> (16 * (d & 1));
+            const uint32_t hi = tw[(key0 + 1) * W + d / 2] >> (16 * (d & 1));
+            w[e] = (lo & 0xffffu) | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(dst + (int64_t)d * a.Tp + 8 * k8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// In-block causal attention (flash style) merged with the prefix partials.
+//
+// Work split: a workgroup owns QW*NW/G consecutive queries of every head of
+// one KV group; wave w handles head g*G + (w % G) and the QW = 16*QT queries
+// of query block w / G.  Keys advance in tiles of IKT = 64; the K tile
+// (row-major) and the V^T tile are copied from global memory straight into
+// LDS (global_load_lds, 16 bytes per lane, no registers), double-buffered so
+// that the next tile is in flight while the current one is multiplied, with
+// one barrier per tile.  LDS rows carry one 16-byte pad chunk (the copy lanes
+// that map onto a pad chunk are masked off), which puts the rows a
+// quarter-wave reads on distinct bank groups and lets every fragment read
+// use one base address plus an immediate offset.
+//
+// Scores are computed transposed, S^T = K Q^T, so a lane's accumulator column
+// is one query: the running max needs two cross-lane steps per tile, the
+// running denominator stays per lane until the end, and the probabilities
+// already sit in the B-operand layout of O^T += V^T P^T (the V^T columns are
+// permuted to match when V is transposed).  Workgroups are numbered so that
+// one KV group's workgroups share an XCD (and its L2), and the query blocks
+// with the most key tiles start first.
+// ----------------------------------------------------------------------------
+namespace {
+typedef const __attribute__((address_space(1))) void *gvoid_t;
+typedef __attribute__((address_space(3))) void *lvoid_t;
+}
+
+template <int D, int G, int NW, int QT>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
+{
+    constexpr int QW = 16 * QT;                  // queries per wave
+    constexpr int QBW = NW / G;                  // query blocks per workgroup
+    constexpr int KS = D / 32;                   // k-steps of the QK^T product
+    constexpr int DT = D / 16;                   // d-tiles of the PV product
+    constexpr int KCH = D / 8 + 1;               // chunks of a K row in LDS (incl. pad)
+    constexpr int VCH = IKT / 8 + 1;             // chunks of a V^T row in LDS
+    constexpr int KRS = 16 * KCH, VRS = 16 * VCH;
+    constexpr int KCHUNKS = IKT * KCH, CHUNKS = KCHUNKS + D * VCH;
+    constexpr int BUF = 16 * CHUNKS;
+    constexpr int NSEG = (CHUNKS + 63) / 64;     // 1 KB wave copies per tile
+    constexpr int SPW = (NSEG + NW - 1) / NW;
+    __shared__ __attribute__((aligned(1024))) char sb0[NSEG * 1024];
+    __shared__ __attribute__((aligned(1024))) char sb1[NSEG * 1024];
 
     const TreeArgs &t = a.t;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = blockIdx.y, bi = blockIdx.z;
-    const int T = a.T;
-    const int q0blk = blockIdx.x * (QB * 16);
+    const int T = a.T, Tp = a.Tp;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nblk = (T + QW * QBW - 1) / (QW * QBW);
+    int lin = blockIdx.x;
+    const int g = lin % t.Hkv;
+    lin /= t.Hkv;
+    const int bi = lin % t.B;
+    const int q0blk = (nblk - 1 - lin / t.B) * (QW * QBW);
     const int h = g * G + (wave % G);
-    const int q0 = q0blk + 16 * (wave / G);
+    const int q0 = q0blk + QW * (wave / G);      // this wave's first query
     const int col = lane & 15, grp = lane >> 4;
-    const int myq = q0 + col;                       // this lane's query (column)
-    const float c2 = t.scale * 1.4426950408889634f; // scale * log2(e)
+    const float c2 = t.scale * 1.4426950408889634f;   // scale * log2(e)
 
     // Q fragments (B operand of S^T = K Q^T): column = query, k-slots 8*grp..
-    bf16x8 qf[KS];
+    bf16x8 qf[QT][KS];
     {
         const bf16_t *qb = (const bf16_t *)a.qr + (((int64_t)bi * t.Hq + h) * T) * D;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (myq < T)
-                qf[s] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)myq * D + 32 * s + 8 * grp);
-            else
-                qf[s] = bf16x8{};
+        for (int qt = 0; qt < QT; ++qt) {
+            const int qq = min(q0 + 16 * qt + col, T - 1);
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                qf[qt][s] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qq * D + 32 * s + 8 * grp);
         }
     }
 
-    // seed the online softmax with the prefix partial state of this query
-    floatx4 o[DT];
-    float mrow = -INFINITY, lrow = 0.f;
-    if (myq < T) {
-        const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
-        const float M = a.part_ml[row * 2 + 0];
-        lrow = a.part_ml[row * 2 + 1];
-        mrow = (M == -INFINITY) ? -INFINITY : M * 1.4426950408889634f;
-        const float *pa = a.part_acc + row * D;
+    // seed the online softmax with the prefix partial state of each query;
+    // the denominator is kept per lane (the lanes of a query hold disjoint
+    // keys) and summed at the end
+    floatx4 o[QT][DT];
+    float mrow[QT], lrow[QT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const float4 v = *reinterpret_cast<const float4 *>(pa + 16 * dt + 4 * grp);
-            o[dt] = floatx4{v.x, v.y, v.z, v.w};
+    for (int qt = 0; qt < QT; ++qt) {
+        const int myq = q0 + 16 * qt + col;
+        mrow[qt] = -INFINITY;
+        lrow[qt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (myq < T) {
+            const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
+            const float M = a.part_ml[row * 2 + 0];
+            if (grp == 0) lrow[qt] = a.part_ml[row * 2 + 1];
+            mrow[qt] = (M == -INFINITY) ? -INFINITY : M * 1.4426950408889634f;
+            const float *pa = a.part_acc + row * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const float4 v = *reinterpret_cast<const float4 *>(pa + 16 * dt + 4 * grp);
+                o[qt][dt] = floatx4{v.x, v.y, v.z, v.w};
+            }
         }
-    } else {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int qlast = min(T - 1, q0blk + QB * 16 - 1);
-    const int kend = qlast + 1;
+    const int kend = min(T, q0blk + QW * QBW);
+    const int ntiles = (kend + IKT - 1) / IKT;
     const bf16_t *kb = (const bf16_t *)a.kr + (((int64_t)bi * t.Hkv + g) * T) * D;
-    const bf16_t *vb = (const bf16_t *)a.v;
+    const bf16_t *vtb = (const bf16_t *)a.vt + ((int64_t)bi * t.Hkv + g) * D * (int64_t)Tp;
 
-    for (int kt0 = 0; kt0 < kend; kt0 += KT) {
-        __syncthreads();
-        // stage K tile (row-major) and V tile (transposed)
-        for (int c = tid; c < KT * D / 8; c += NTH) {
-            const int key = c / (D / 8), ch = c % (D / 8);
-            uint4 kv = make_uint4(0, 0, 0, 0);
-            if (kt0 + key < T)
-                kv = *reinterpret_cast<const uint4 *>(kb + (int64_t)(kt0 + key) * D + 8 * ch);
-            *reinterpret_cast<uint4 *>(sK + key * (D + KPAD) + 8 * ch) = kv;
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (kt0 + key < T)
-                vv = *reinterpret_cast<const uint4 *>(
-                    vb + (((int64_t)bi * T + kt0 + key) * t.Hkv + g) * D + 8 * ch);
-            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    // copy key tile j into buf: LDS chunk c is written by lane c % 64 of the
+    // copy of segment c / 64; chunks below KCHUNKS are K rows (key, D/8
+    // chunks + pad), the rest V^T rows (d, IKT/8 chunks + pad)
+    auto issue = [&](int j, char *buf) __attribute__((always_inline)) {
+        const int kt0 = j * IKT;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sVt[(8 * ch + 2 * e) * (KT + VPAD) + key] = (bf16_t)(w[e] & 0xffffu);
-                sVt[(8 * ch + 2 * e + 1) * (KT + VPAD) + key] = (bf16_t)(w[e] >> 16);
+        for (int u = 0; u < SPW; ++u) {
+            const int seg = wave + NW * u;
+            if (seg >= NSEG) break;
+            const int ci = seg * 64 + lane;
+            const bf16_t *src = nullptr;
+            if (ci < KCHUNKS) {
+                const int r = ci / KCH, p = ci % KCH;
+                if (p < KCH - 1) src = kb + (int64_t)min(kt0 + r, T - 1) * D + 8 * p;
+            } else if (ci < CHUNKS) {
+                const int r = (ci - KCHUNKS) / VCH, p = (ci - KCHUNKS) % VCH;
+                if (p < VCH - 1) src = vtb + (int64_t)r * Tp + kt0 + 8 * p;
             }
+            if (src) __builtin_amdgcn_global_load_lds((gvoid_t)src, (lvoid_t)(buf + seg * 1024), 16, 0, 0);
         }
-        __syncthreads();
-        if (kt0 > q0 + 15) continue;                // tile entirely in this wave's future
+    };
 
-        // S^T tiles: keys kt0 + 16*mt + 4*grp + i, query myq
-        floatx4 sc[2];
+    const int kbase = col * KRS + 16 * grp;                 // K row col, chunk grp
+    const int vbase = KCHUNKS * 16 + col * VRS + 16 * grp;  // V^T row col, chunk grp
+
+    auto compute = [&](int j, const char *buf) __attribute__((always_inline)) {
+        const int kt0 = j * IKT;
+        if (kt0 > q0 + QW - 1) return;           // tile entirely in this wave's future
+        bool act[QT];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < QT; ++qt) act[qt] = kt0 <= q0 + 16 * qt + 15;
+        // S^T: 16-key tile tm holds keys kt0 + 16*tm + 4*grp + i in lane
+        // (col = query, grp), element i
+        floatx4 sc[QT][4];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(
-                    sK + (16 * mt + col) * (D + KPAD) + 32 * s + 8 * grp);
-                sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[s], sc[mt], 0, 0, 0);
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) sc[qt][tm] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(buf + kbase + 16 * tm * KRS + 64 * s);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt)
+                    if (act[qt]) sc[qt][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qt][s], sc[qt][tm], 0, 0, 0);
+            }
+        // online softmax per query tile; P of 32-key step kg goes to slots
+        // 4*m + i of pf[kg] (tile tm = 2*kg + m)
+        bf16x8 pf[QT][2];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const int myq = q0 + 16 * qt + col;
+            const bool diag = kt0 + IKT - 1 > q0 + 16 * qt;
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kt0 + 16 * tm + 4 * grp + i;
+                    const float x = (!diag || key <= myq) ? sc[qt][tm][i] * c2 : -INFINITY;
+                    sc[qt][tm][i] = x;
+                    tmax = fmaxf(tmax, x);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            const float mnew = fmaxf(mrow[qt], tmax);
+            const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mu);
+            float psum = 0.f;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pz = __builtin_amdgcn_exp2f(sc[qt][tm][i] - mu);
+                    psum += pz;
+                    pf[qt][tm >> 1][4 * (tm & 1) + i] = (__bf16)pz;
+                }
+            lrow[qt] = lrow[qt] * alpha + psum;
+            mrow[qt] = mnew;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
             }
         }
-        float sv[8];
-        float tmax = -INFINITY;
+        // O^T += V^T P^T; V^T row d = 16*dt + col, k-slots 8*grp.. of step kg
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kt0 + 16 * mt + 4 * grp + i;
-                const float x = (key <= myq) ? sc[mt][i] * c2 : -INFINITY;
-                sv[mt * 4 + i] = x;
-                tmax = fmaxf(tmax, x);
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(buf + vbase + 16 * dt * VRS + 64 * kg);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt)
+                    if (act[qt]) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kg], o[qt][dt], 0, 0, 0);
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float mnew = fmaxf(mrow, tmax);
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrow - mnew);
-        float psum = 0.f;
-        bf16x8 pf;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float pz = (mnew == -INFINITY) ? 0.f : exp2f(sv[i] - mnew);
-            psum += pz;
-            pf[i] = (__bf16)pz;
-        }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
-        lrow = lrow * alpha + psum;
-        mrow = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            o[dt] *= alpha;
-            // A = V^T rows d = 16*dt + col, k-slots: keys 4*grp+i (0-3), 16+4*grp+i (4-7)
-            const bf16_t *vr = sVt + (16 * dt + col) * (KT + VPAD);
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr + 4 * grp);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * grp);
-            uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&pk);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
+    };
+    static_assert(BUF <= NSEG * 1024, "tile fits its buffer");
+
+    if (ntiles > 0) issue(0, sb0);
+    for (int j = 0; j < ntiles; j += 2) {
+        __builtin_amdgcn_s_waitcnt(0);           // this wave's copies of tile j landed
+        __syncthreads();                         // everyone's did; tile j-1 is consumed
+        if (j + 1 < ntiles) issue(j + 1, sb1);
+        compute(j, sb0);
+        if (j + 1 < ntiles) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (j + 2 < ntiles) issue(j + 2, sb0);
+            compute(j + 1, sb1);
         }
     }
 
-    if (myq < T) {
-        const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
-        const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-        float *op = a.out + row * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<float4 *>(op + 16 * dt + 4 * grp) =
-                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-        if (a.lse && grp == 0)
-            a.lse[row] = lrow > 0.f ? mrow * 0.6931471805599453f + logf(lrow) : -INFINITY;
+    for (int qt = 0; qt < QT; ++qt) {
+        float l = lrow[qt];
+        l += __shfl_xor(l, 16, kWave);
+        l += __shfl_xor(l, 32, kWave);
+        const int myq = q0 + 16 * qt + col;
+        if (myq < T) {
+            const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            float *op = a.out + row * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<float4 *>(op + 16 * dt + 4 * grp) =
+                    make_float4(o[qt][dt][0] * inv, o[qt][dt][1] * inv, o[qt][dt][2] * inv, o[qt][dt][3] * inv);
+            if (a.lse && grp == 0)
+                a.lse[row] = l > 0.f ? mrow[qt] * 0.6931471805599453f + logf(l) : -INFINITY;
+        }
     }
 }
 
 template <int D>
 static hipError_t inblock_d(const PrefillArgs &a, hipStream_t s)
 {
-    const int G = a.t.G;
-    const int nwv = G == 8 ? 8 : 4;
-    const int qb = nwv / G;
-    dim3 grid((unsigned)((a.T + 16 * qb - 1) / (16 * qb)), (unsigned)a.t.Hkv, (unsigned)a.t.B);
-    dim3 block(64 * nwv);
-    switch (G) {
-    case 1: hipLaunchKernelGGL((k_inblock<D, 1, 4>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_inblock<D, 2, 4>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_inblock<D, 4, 4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_inblock<D, 8, 8>), grid, block, 0, s, a); break;
+    dim3 tgrid((unsigned)(a.Tp / IKT), (unsigned)a.t.Hkv, (unsigned)a.t.B);
+    hipLaunchKernelGGL((k_transpose_v<D>), tgrid, dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    constexpr int QT = 2;
+    // one wave per (head, 32-query block); G heads x (4/G or 1) blocks per workgroup
+    auto grid = [&](int nw, int gg) {
+        const int q = 16 * QT * (nw / gg);
+        return dim3((unsigned)(((a.T + q - 1) / q) * a.t.Hkv * a.t.B));
+    };
+    switch (a.t.G) {
+    case 1: hipLaunchKernelGGL((k_inblock<D, 1, 4, QT>), grid(4, 1), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_inblock<D, 2, 4, QT>), grid(4, 2), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_inblock<D, 4, 4, QT>), grid(4, 4), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_inblock<D, 8, 8, QT>), grid(8, 8), dim3(512), 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -300,6 +300,15 @@ def test_prefill_scored_top_level(Hq, Hkv, R, k, P0):
     _check_prefill(w, P0, 40)
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,P0,T", [(32, 8, 128, 3000, 300), (8, 1, 128, 500, 200),
+                                           (2, 2, 128, 700, 261), (8, 4, 64, 900, 190)])
+def test_prefill_inblock_tiles(Hq, Hkv, d, P0, T):
+    """The causal block product spans several 64-key tiles with a ragged
+    last tile, for head groups G = 4, 8, 1, 2 and head_dim 128 / 64."""
+    w = PF.replace(Hq=Hq, Hkv=Hkv, d=d, levels=2)
+    _check_prefill(w, P0, T)
+
+
 def test_prefill_topp_r4():
     _check_prefill(W.ZHA2M.replace(name="pf_topp", levels=3), 16 ** 3 * 3 + 50, 48)
 

@@ -196,7 +196,7 @@ PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
     w.qr = off;
     off += align256(rows * c->Hq * c->d * 2);
     w.kr = off;
-    off += align256(rows * c->Hkv * c->d * 2);
+    off += align256((size_t)c->B * inblock_tp(T) * c->Hkv * c->d * 2);
     w.vt = off;
     off += align256((size_t)c->B * inblock_tp(T) * c->Hkv * c->d * 2);
     w.top_s = off;

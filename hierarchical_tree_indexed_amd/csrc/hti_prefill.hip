@@ -20,38 +20,58 @@ typedef __attribute__((ext_vector_type(4))) float floatx4;
 
 // ----------------------------------------------------------------------------
 // Rotate the block's q and k by their block-local index and store them as
-// bf16 in head-major layout: qr [B, Hq, T, D], kr [B, Hkv, T, D].
+// bf16 in head-major layout: qr [B, Hq, T, D], kr [B, Hkv, Tp, D] (rows T ..
+// Tp-1 of kr are zero).  A thread rotates 8 consecutive pairs (j, j + D/2).
 // ----------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void k_rotate_block(PrefillArgs a)
+__global__ __launch_bounds__(256) void k_rotate_block(PrefillArgs a)
 {
     const TreeArgs &t = a.t;
     const int H = t.Hq + t.Hkv;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)t.B * a.T * H * (D / 2);
+    const int64_t total = (int64_t)t.B * a.Tp * H * (D / 16);
     if (idx >= total) return;
-    const int j = (int)(idx % (D / 2));
-    int64_t r = idx / (D / 2);
+    const int j = 8 * (int)(idx % (D / 16));
+    int64_t r = idx / (D / 16);
     const int hh = (int)(r % H);
     r /= H;
-    const int tt = (int)(r % a.T);
-    const int bi = (int)(r / a.T);
+    const int tt = (int)(r % a.Tp);
+    const int bi = (int)(r / a.Tp);
     const bool isq = hh < t.Hq;
     const int h = isq ? hh : hh - t.Hq;
     const int nh = isq ? t.Hq : t.Hkv;
+    if (tt >= a.T) {
+        if (!isq) {
+            bf16_t *dst = (bf16_t *)a.kr + (((int64_t)bi * nh + h) * a.Tp + tt) * D;
+            *reinterpret_cast<uint4 *>(dst + j) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(dst + j + D / 2) = make_uint4(0, 0, 0, 0);
+        }
+        return;
+    }
     const T *src = (const T *)(isq ? a.q : a.k) + (((int64_t)bi * a.T + tt) * nh + h) * D;
-    bf16_t *dst = (bf16_t *)(isq ? a.qr : a.kr) + (((int64_t)bi * nh + h) * a.T + tt) * D;
-    float x0, x1;
-    load_vec<T, 1>(src + j, &x0);
-    load_vec<T, 1>(src + j + D / 2, &x1);
-    const float2 cs = t.rope[(int64_t)tt * (D / 2) + j];
-    dst[j] = f2bf(x0 * cs.x - x1 * cs.y);
-    dst[j + D / 2] = f2bf(x0 * cs.y + x1 * cs.x);
+    bf16_t *dst = (bf16_t *)(isq ? a.qr : a.kr) + (((int64_t)bi * nh + h) * (isq ? a.T : a.Tp) + tt) * D;
+    float x0[8], x1[8];
+    load_vec<T, 8>(src + j, x0);
+    load_vec<T, 8>(src + j + D / 2, x1);
+    const float4 *cs4 = reinterpret_cast<const float4 *>(t.rope + (int64_t)tt * (D / 2) + j);
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float4 cs = cs4[e];      // (cos, sin) of pairs j + 2e, j + 2e + 1
+        const float a0 = x0[2 * e] * cs.x - x1[2 * e] * cs.y;
+        const float b0 = x0[2 * e] * cs.y + x1[2 * e] * cs.x;
+        const float a1 = x0[2 * e + 1] * cs.z - x1[2 * e + 1] * cs.w;
+        const float b1 = x0[2 * e + 1] * cs.w + x1[2 * e + 1] * cs.z;
+        lo[e] = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
+        hi[e] = (uint32_t)f2bf(b0) | ((uint32_t)f2bf(b1) << 16);
+    }
+    *reinterpret_cast<uint4 *>(dst + j) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4 *>(dst + j + D / 2) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
 }
 
 hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s)
 {
-    const int64_t total = (int64_t)a.t.B * a.T * (a.t.Hq + a.t.Hkv) * (a.t.D / 2);
+    const int64_t total = (int64_t)a.t.B * a.Tp * (a.t.Hq + a.t.Hkv) * (a.t.D / 16);
     if (total == 0) return hipSuccess;
     dim3 grid((unsigned)((total + 255) / 256)), block(256);
     if (a.t.dtype == HTI_BF16) {
@@ -134,10 +154,11 @@ __global__ __launch_bounds__(256) void k_transpose_v(PrefillArgs a)
 namespace {
 typedef const __attribute__((address_space(1))) void *gvoid_t;
 typedef __attribute__((address_space(3))) void *lvoid_t;
+constexpr float kLazy = 8.f;    // slack of the exponent reference (log2 units)
 }
 
 template <int D, int G, int NW, int QT>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
+__global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 : 8) / NW : 1) void k_inblock(PrefillArgs a)
 {
     constexpr int QW = 16 * QT;                  // queries per wave
     constexpr int QBW = NW / G;                  // query blocks per workgroup
@@ -209,28 +230,41 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
 
     const int kend = min(T, q0blk + QW * QBW);
     const int ntiles = (kend + IKT - 1) / IKT;
-    const bf16_t *kb = (const bf16_t *)a.kr + (((int64_t)bi * t.Hkv + g) * T) * D;
+    const bf16_t *kb = (const bf16_t *)a.kr + (((int64_t)bi * t.Hkv + g) * Tp) * D;
     const bf16_t *vtb = (const bf16_t *)a.vt + ((int64_t)bi * t.Hkv + g) * D * (int64_t)Tp;
 
     // copy key tile j into buf: LDS chunk c is written by lane c % 64 of the
     // copy of segment c / 64; chunks below KCHUNKS are K rows (key, D/8
-    // chunks + pad), the rest V^T rows (d, IKT/8 chunks + pad)
+    // chunks + pad), the rest V^T rows (d, IKT/8 chunks + pad).  The source
+    // offsets relative to the tile are fixed per lane; pad chunks copy nothing.
+    constexpr int KSEG = KCHUNKS / 64;
+    static_assert(KCHUNKS % 64 == 0, "K rows end on a segment boundary");
+    int off[SPW];
+    bool live[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int seg = wave + NW * u;
+        const int ci = seg * 64 + lane;
+        if (seg < KSEG) {
+            const int r = ci / KCH, p = ci % KCH;
+            off[u] = r * D + 8 * p;
+            live[u] = p < KCH - 1;
+        } else {
+            const int r = (ci - KCHUNKS) / VCH, p = (ci - KCHUNKS) % VCH;
+            off[u] = r * Tp + 8 * p;
+            live[u] = p < VCH - 1 && r < D;
+        }
+    }
     auto issue = [&](int j, char *buf) __attribute__((always_inline)) {
         const int kt0 = j * IKT;
+        const bf16_t *kt = kb + (int64_t)kt0 * D, *vt = vtb + kt0;
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int seg = wave + NW * u;
             if (seg >= NSEG) break;
-            const int ci = seg * 64 + lane;
-            const bf16_t *src = nullptr;
-            if (ci < KCHUNKS) {
-                const int r = ci / KCH, p = ci % KCH;
-                if (p < KCH - 1) src = kb + (int64_t)min(kt0 + r, T - 1) * D + 8 * p;
-            } else if (ci < CHUNKS) {
-                const int r = (ci - KCHUNKS) / VCH, p = (ci - KCHUNKS) % VCH;
-                if (p < VCH - 1) src = vtb + (int64_t)r * Tp + kt0 + 8 * p;
-            }
-            if (src) __builtin_amdgcn_global_load_lds((gvoid_t)src, (lvoid_t)(buf + seg * 1024), 16, 0, 0);
+            if (live[u])
+                __builtin_amdgcn_global_load_lds((gvoid_t)((seg < KSEG ? kt : vt) + off[u]),
+                                                 (lvoid_t)(buf + seg * 1024), 16, 0, 0);
         }
     };
 
@@ -240,9 +274,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
     auto compute = [&](int j, const char *buf) __attribute__((always_inline)) {
         const int kt0 = j * IKT;
         if (kt0 > q0 + QW - 1) return;           // tile entirely in this wave's future
-        bool act[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) act[qt] = kt0 <= q0 + 16 * qt + 15;
+        // (a query tile wholly before the tile's keys is multiplied anyway:
+        // the causal mask leaves it zero probabilities)
         // S^T: 16-key tile tm holds keys kt0 + 16*tm + 4*grp + i in lane
         // (col = query, grp), element i
         floatx4 sc[QT][4];
@@ -257,30 +290,39 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
                 const bf16x8 af = *reinterpret_cast<const bf16x8 *>(buf + kbase + 16 * tm * KRS + 64 * s);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-                    if (act[qt]) sc[qt][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qt][s], sc[qt][tm], 0, 0, 0);
+                    sc[qt][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qt][s], sc[qt][tm], 0, 0, 0);
             }
         // online softmax per query tile; P of 32-key step kg goes to slots
-        // 4*m + i of pf[kg] (tile tm = 2*kg + m)
+        // 4*m + i of pf[kg] (tile tm = 2*kg + m).  The exponent reference
+        // mref is the query's running max, raised only when a score exceeds
+        // it by more than kLazy (log2 units): probabilities stay below
+        // 2^kLazy, and the rescale of the accumulators is rare.
+        const bool diag = kt0 + IKT - 1 > q0;    // some key follows some query of the wave
         bf16x8 pf[QT][2];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const int myq = q0 + 16 * qt + col;
-            const bool diag = kt0 + IKT - 1 > q0 + 16 * qt;
-            float tmax = -INFINITY;
+            float lmax = -INFINITY;
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int key = kt0 + 16 * tm + 4 * grp + i;
-                    const float x = (!diag || key <= myq) ? sc[qt][tm][i] * c2 : -INFINITY;
+                    float x = sc[qt][tm][i] * c2;
+                    if (diag) x = (kt0 + 16 * tm + 4 * grp + i <= myq) ? x : -INFINITY;
                     sc[qt][tm][i] = x;
-                    tmax = fmaxf(tmax, x);
+                    lmax = fmaxf(lmax, x);
                 }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-            const float mnew = fmaxf(mrow[qt], tmax);
-            const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mu);
+            if (__builtin_amdgcn_ballot_w64(lmax > mrow[qt] + kLazy)) {
+                float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+                const float mnew = fmaxf(mrow[qt], tmax);
+                const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[qt] - mnew);
+                lrow[qt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
+                mrow[qt] = mnew;
+            }
+            const float mu = (mrow[qt] == -INFINITY) ? 0.f : mrow[qt];
             float psum = 0.f;
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
@@ -290,12 +332,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
                     psum += pz;
                     pf[qt][tm >> 1][4 * (tm & 1) + i] = (__bf16)pz;
                 }
-            lrow[qt] = lrow[qt] * alpha + psum;
-            mrow[qt] = mnew;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
-            }
+            lrow[qt] += psum;
         }
         // O^T += V^T P^T; V^T row d = 16*dt + col, k-slots 8*grp.. of step kg
 #pragma unroll
@@ -305,7 +342,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_inblock(PrefillArgs a)
                 const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(buf + vbase + 16 * dt * VRS + 64 * kg);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-                    if (act[qt]) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kg], o[qt][dt], 0, 0, 0);
+                    o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kg], o[qt][dt], 0, 0, 0);
             }
     };
     static_assert(BUF <= NSEG * 1024, "tile fits its buffer");

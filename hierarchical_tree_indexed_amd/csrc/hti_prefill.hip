@@ -157,8 +157,8 @@ typedef __attribute__((address_space(3))) void *lvoid_t;
 constexpr float kLazy = 8.f;    // slack of the exponent reference (log2 units)
 }
 
-template <int D, int G, int NW, int QT>
-__global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 : 8) / NW : 1) void k_inblock(PrefillArgs a)
+template <int D, int G, int NW, int QT, int NB>
+__global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) void k_inblock(PrefillArgs a)
 {
     constexpr int QW = 16 * QT;                  // queries per wave
     constexpr int QBW = NW / G;                  // query blocks per workgroup
@@ -171,8 +171,10 @@ __global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 
     constexpr int BUF = 16 * CHUNKS;
     constexpr int NSEG = (CHUNKS + 63) / 64;     // 1 KB wave copies per tile
     constexpr int SPW = (NSEG + NW - 1) / NW;
+    static_assert(NB == 2 || NB == 3, "two or three tile buffers");
     __shared__ __attribute__((aligned(1024))) char sb0[NSEG * 1024];
     __shared__ __attribute__((aligned(1024))) char sb1[NSEG * 1024];
+    __shared__ __attribute__((aligned(1024))) char sb2[NB == 3 ? NSEG * 1024 : 16];
 
     const TreeArgs &t = a.t;
     const int T = a.T, Tp = a.Tp;
@@ -203,21 +205,24 @@ __global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 
     }
 
     // seed the online softmax with the prefix partial state of each query;
-    // the denominator is kept per lane (the lanes of a query hold disjoint
-    // keys) and summed at the end
-    floatx4 o[QT][DT];
-    float mrow[QT], lrow[QT];
+    // every element of lacc[qt] holds the query's running denominator
+    floatx4 o[QT][DT], lacc[QT];
+    float mrow[QT];
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int myq = q0 + 16 * qt + col;
         mrow[qt] = -INFINITY;
-        lrow[qt] = 0.f;
+        lacc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
         if (myq < T) {
             const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
             const float M = a.part_ml[row * 2 + 0];
-            if (grp == 0) lrow[qt] = a.part_ml[row * 2 + 1];
+            const float L = a.part_ml[row * 2 + 1];
+            lacc[qt] = floatx4{L, L, L, L};
             mrow[qt] = (M == -INFINITY) ? -INFINITY : M * 1.4426950408889634f;
             const float *pa = a.part_acc + row * D;
 #pragma unroll
@@ -271,18 +276,13 @@ __global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 
     const int kbase = col * KRS + 16 * grp;                 // K row col, chunk grp
     const int vbase = KCHUNKS * 16 + col * VRS + 16 * grp;  // V^T row col, chunk grp
 
-    auto compute = [&](int j, const char *buf) __attribute__((always_inline)) {
-        const int kt0 = j * IKT;
-        if (kt0 > q0 + QW - 1) return;           // tile entirely in this wave's future
-        // (a query tile wholly before the tile's keys is multiplied anyway:
-        // the causal mask leaves it zero probabilities)
+    // one key tile of the product; diag: some key of the tile follows some
+    // query of the wave, so the causal mask applies
+    auto tile = [&](int kt0, const char *buf, bool diag) __attribute__((always_inline)) {
         // S^T: 16-key tile tm holds keys kt0 + 16*tm + 4*grp + i in lane
-        // (col = query, grp), element i
+        // (col = query, grp), element i.  A query tile wholly before the
+        // tile's keys is multiplied anyway: the mask leaves it zero weights.
         floatx4 sc[QT][4];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm) sc[qt][tm] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -290,53 +290,60 @@ __global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 
                 const bf16x8 af = *reinterpret_cast<const bf16x8 *>(buf + kbase + 16 * tm * KRS + 64 * s);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-                    sc[qt][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qt][s], sc[qt][tm], 0, 0, 0);
+                    sc[qt][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        af, qf[qt][s], s == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sc[qt][tm], 0, 0, 0);
             }
-        // online softmax per query tile; P of 32-key step kg goes to slots
-        // 4*m + i of pf[kg] (tile tm = 2*kg + m).  The exponent reference
-        // mref is the query's running max, raised only when a score exceeds
-        // it by more than kLazy (log2 units): probabilities stay below
-        // 2^kLazy, and the rescale of the accumulators is rare.
-        const bool diag = kt0 + IKT - 1 > q0;    // some key follows some query of the wave
+        // online softmax per query tile, in log2 units (c2 = scale*log2 e);
+        // P of 32-key step kg goes to slots 4*m + i of pf[kg] (tm = 2*kg + m).
+        // The exponent reference mrow is the query's running max, raised
+        // only when a score exceeds it by more than kLazy: probabilities stay
+        // below 2^kLazy and the rescale of the accumulators is rare.
+        if (diag) {
+            // (the empty asm keeps this a branch: as selects, the compares
+            // would run on every tile)
+            asm volatile("");
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kt0 + 16 * tm + 4 * grp + i > q0 + 16 * qt + col) sc[qt][tm][i] = -INFINITY;
+        }
         bf16x8 pf[QT][2];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-            const int myq = q0 + 16 * qt + col;
             float lmax = -INFINITY;
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sc[qt][tm][i] * c2;
-                    if (diag) x = (kt0 + 16 * tm + 4 * grp + i <= myq) ? x : -INFINITY;
-                    sc[qt][tm][i] = x;
-                    lmax = fmaxf(lmax, x);
-                }
+                for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sc[qt][tm][i]);
+            lmax *= c2;
             if (__builtin_amdgcn_ballot_w64(lmax > mrow[qt] + kLazy)) {
                 float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
                 const float mnew = fmaxf(mrow[qt], tmax);
                 const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[qt] - mnew);
-                lrow[qt] *= alpha;
+                lacc[qt] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
                 mrow[qt] = mnew;
             }
-            const float mu = (mrow[qt] == -INFINITY) ? 0.f : mrow[qt];
-            float psum = 0.f;
+            const float nmu = (mrow[qt] == -INFINITY) ? 0.f : -mrow[qt];
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pz = __builtin_amdgcn_exp2f(sc[qt][tm][i] - mu);
-                    psum += pz;
-                    pf[qt][tm >> 1][4 * (tm & 1) + i] = (__bf16)pz;
-                }
-            lrow[qt] += psum;
+                for (int i = 0; i < 4; ++i)
+                    pf[qt][tm >> 1][4 * (tm & 1) + i] =
+                        (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][tm][i], c2, nmu));
         }
-        // O^T += V^T P^T; V^T row d = 16*dt + col, k-slots 8*grp.. of step kg
+        // O^T += V^T P^T; V^T row d = 16*dt + col, k-slots 8*grp.. of step kg.
+        // The row sums of P come from the same product with a ones operand.
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
+        for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt][kg], lacc[qt], 0, 0, 0);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(buf + vbase + 16 * dt * VRS + 64 * kg);
@@ -344,28 +351,69 @@ __global__ __launch_bounds__(NW * 64, (QT >= 4 ? 4 : 8) / NW > 0 ? (QT >= 4 ? 4 
                 for (int qt = 0; qt < QT; ++qt)
                     o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kg], o[qt][dt], 0, 0, 0);
             }
+        }
+    };
+    auto compute = [&](int j, const char *buf) __attribute__((always_inline)) {
+        const int kt0 = j * IKT;
+        if (kt0 > q0 + QW - 1) return;           // tile entirely in this wave's future
+        tile(kt0, buf, kt0 + IKT - 1 > q0);
     };
     static_assert(BUF <= NSEG * 1024, "tile fits its buffer");
 
-    if (ntiles > 0) issue(0, sb0);
-    for (int j = 0; j < ntiles; j += 2) {
-        __builtin_amdgcn_s_waitcnt(0);           // this wave's copies of tile j landed
-        __syncthreads();                         // everyone's did; tile j-1 is consumed
-        if (j + 1 < ntiles) issue(j + 1, sb1);
-        compute(j, sb0);
-        if (j + 1 < ntiles) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (j + 2 < ntiles) issue(j + 2, sb0);
+    if constexpr (NB == 2) {
+        // copies run one tile ahead of the product
+        if (ntiles > 0) issue(0, sb0);
+        for (int j = 0; j < ntiles; j += 2) {
+            __builtin_amdgcn_s_waitcnt(0);       // this wave's copies of tile j landed
+            __syncthreads();                     // everyone's did; tile j-1 is consumed
+            if (j + 1 < ntiles) issue(j + 1, sb1);
+            compute(j, sb0);
+            if (j + 1 < ntiles) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (j + 2 < ntiles) issue(j + 2, sb0);
+                compute(j + 1, sb1);
+            }
+        }
+    } else {
+        // copies run two tiles ahead: at the wait for tile j only the copies
+        // of tile j+1 (issued after those of j; vector memory counts retire
+        // in order) may still be in flight -- at least NSEG/NW of them
+        constexpr int VM = NSEG / NW;
+        static_assert(VM < 64, "vmcnt field");
+        constexpr int kWaitNext = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
+        // A plain s_barrier: __syncthreads() adds a workgroup release fence,
+        // which would wait for every copy in flight (LDS writes), tile j+1's
+        // included.  The explicit count wait orders this wave's copies; the
+        // fragment reads of tile j-1 were consumed before the barrier, and
+        // the empty asm keeps the compiler from moving LDS accesses across it.
+        auto wait_tile = [&](int j) __attribute__((always_inline)) {
+            if (j + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitNext);
+            else __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();       // everyone's copies landed; tile j-1 is consumed
+            asm volatile("" ::: "memory");
+        };
+        if (ntiles > 0) issue(0, sb0);
+        if (ntiles > 1) issue(1, sb1);
+        for (int j = 0; j < ntiles; j += 3) {
+            wait_tile(j);
+            if (j + 2 < ntiles) issue(j + 2, sb2);
+            compute(j, sb0);
+            if (j + 1 >= ntiles) break;
+            wait_tile(j + 1);
+            if (j + 3 < ntiles) issue(j + 3, sb0);
             compute(j + 1, sb1);
+            if (j + 2 >= ntiles) break;
+            wait_tile(j + 2);
+            if (j + 4 < ntiles) issue(j + 4, sb1);
+            compute(j + 2, sb2);
         }
     }
 
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-        float l = lrow[qt];
-        l += __shfl_xor(l, 16, kWave);
-        l += __shfl_xor(l, 32, kWave);
+        const float l = lacc[qt][0];
         const int myq = q0 + 16 * qt + col;
         if (myq < T) {
             const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
@@ -387,17 +435,25 @@ static hipError_t inblock_d(const PrefillArgs &a, hipStream_t s)
     dim3 tgrid((unsigned)(a.Tp / IKT), (unsigned)a.t.Hkv, (unsigned)a.t.B);
     hipLaunchKernelGGL((k_transpose_v<D>), tgrid, dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    constexpr int QT = 2;
-    // one wave per (head, 32-query block); G heads x (4/G or 1) blocks per workgroup
-    auto grid = [&](int nw, int gg) {
-        const int q = 16 * QT * (nw / gg);
+#ifndef HTI_IB_QT
+#define HTI_IB_QT 2
+#endif
+    constexpr int QT = HTI_IB_QT;
+#ifndef HTI_IB_NW
+#define HTI_IB_NW 4
+#define HTI_IB_NB 2
+#endif
+    constexpr int NW = HTI_IB_NW, NB = HTI_IB_NB;
+    // one wave per (head, 32-query block); NW/G query blocks per workgroup
+    auto grid = [&](int gg) {
+        const int q = 16 * QT * (NW / gg);
         return dim3((unsigned)(((a.T + q - 1) / q) * a.t.Hkv * a.t.B));
     };
     switch (a.t.G) {
-    case 1: hipLaunchKernelGGL((k_inblock<D, 1, 4, QT>), grid(4, 1), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_inblock<D, 2, 4, QT>), grid(4, 2), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_inblock<D, 4, 4, QT>), grid(4, 4), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_inblock<D, 8, 8, QT>), grid(8, 8), dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_inblock<D, 1, NW, QT, NB>), grid(1), dim3(64 * NW), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_inblock<D, 2, NW, QT, NB>), grid(2), dim3(64 * NW), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_inblock<D, 4, NW, QT, NB>), grid(4), dim3(64 * NW), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_inblock<D, 8, 8, QT, NB>), grid(8), dim3(64 * 8), 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -161,6 +161,7 @@ template <int D, int G, int NW, int QT, int NB>
 __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) void k_inblock(PrefillArgs a)
 {
     constexpr int QW = 16 * QT;                  // queries per wave
+    static_assert(NW >= G && NW % G == 0, "a workgroup holds whole KV groups");
     constexpr int QBW = NW / G;                  // query blocks per workgroup
     constexpr int KS = D / 32;                   // k-steps of the QK^T product
     constexpr int DT = D / 16;                   // d-tiles of the PV product
@@ -185,6 +186,7 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
     const int g = lin % t.Hkv;
     lin /= t.Hkv;
     const int bi = lin % t.B;
+    if (lin / t.B >= nblk) return;               // past the last query block (whole workgroup)
     const int q0blk = (nblk - 1 - lin / t.B) * (QW * QBW);
     const int h = g * G + (wave % G);
     const int q0 = q0blk + QW * (wave / G);      // this wave's first query
@@ -429,6 +431,19 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
     }
 }
 
+// One wave per (head, 16*QT-query block); NW/G query blocks per workgroup.
+// The grid is derived from the same constants as the kernel's own split.
+template <int D, int G, int NW, int QT, int NB>
+static hipError_t inblock_launch(const PrefillArgs &a, hipStream_t s)
+{
+    static_assert(NW >= G && NW % G == 0, "a workgroup holds whole KV groups");
+    constexpr int q = 16 * QT * (NW / G);        // queries per workgroup
+    const int64_t nblk = ((int64_t)a.T + q - 1) / q;
+    hipLaunchKernelGGL((k_inblock<D, G, NW, QT, NB>), dim3((unsigned)(nblk * a.t.Hkv * a.t.B)),
+                       dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t inblock_d(const PrefillArgs &a, hipStream_t s)
 {
@@ -444,16 +459,11 @@ static hipError_t inblock_d(const PrefillArgs &a, hipStream_t s)
 #define HTI_IB_NB 2
 #endif
     constexpr int NW = HTI_IB_NW, NB = HTI_IB_NB;
-    // one wave per (head, 32-query block); NW/G query blocks per workgroup
-    auto grid = [&](int gg) {
-        const int q = 16 * QT * (NW / gg);
-        return dim3((unsigned)(((a.T + q - 1) / q) * a.t.Hkv * a.t.B));
-    };
     switch (a.t.G) {
-    case 1: hipLaunchKernelGGL((k_inblock<D, 1, NW, QT, NB>), grid(1), dim3(64 * NW), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_inblock<D, 2, NW, QT, NB>), grid(2), dim3(64 * NW), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_inblock<D, 4, NW, QT, NB>), grid(4), dim3(64 * NW), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_inblock<D, 8, 8, QT, NB>), grid(8), dim3(64 * 8), 0, s, a); break;
+    case 1: return inblock_launch<D, 1, NW, QT, NB>(a, s);
+    case 2: return inblock_launch<D, 2, NW, QT, NB>(a, s);
+    case 4: return inblock_launch<D, 4, NW, QT, NB>(a, s);
+    default: return inblock_launch<D, 8, (NW > 8 ? NW : 8), QT, NB>(a, s);
     }
     return hipGetLastError();
 }

@@ -138,10 +138,10 @@ __global__ __launch_bounds__(256) void k_transpose_v(PrefillArgs a)
 // (row-major) and the V^T tile are copied from global memory straight into
 // LDS (global_load_lds, 16 bytes per lane, no registers), double-buffered so
 // that the next tile is in flight while the current one is multiplied, with
-// one barrier per tile.  LDS rows carry one 16-byte pad chunk (the copy lanes
-// that map onto a pad chunk are masked off), which puts the rows a
-// quarter-wave reads on distinct bank groups and lets every fragment read
-// use one base address plus an immediate offset.
+// one barrier per tile.  LDS rows carry two 16-byte pad chunks (the copy
+// lanes that map onto a pad chunk are masked off), which keeps the fragment
+// reads free of bank conflicts and lets every fragment read use one base
+// address plus an immediate offset.
 //
 // Scores are computed transposed, S^T = K Q^T, so a lane's accumulator column
 // is one query: the running max needs two cross-lane steps per tile, the
@@ -165,8 +165,13 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
     constexpr int QBW = NW / G;                  // query blocks per workgroup
     constexpr int KS = D / 32;                   // k-steps of the QK^T product
     constexpr int DT = D / 16;                   // d-tiles of the PV product
-    constexpr int KCH = D / 8 + 1;               // chunks of a K row in LDS (incl. pad)
-    constexpr int VCH = IKT / 8 + 1;             // chunks of a V^T row in LDS
+    // LDS rows carry 32 bytes of padding: measured on gfx950, 16-byte reads
+    // of 16 rows (one per lane of a quarter-wave) at a stride of 256+16 or
+    // 128+16 bytes stall about 4 cycles on bank conflicts, at 256+32 and
+    // 128+32 bytes none
+    constexpr int KPADC = 2, VPADC = 2;          // pad chunks per row
+    constexpr int KCH = D / 8 + KPADC;           // chunks of a K row in LDS (incl. pad)
+    constexpr int VCH = IKT / 8 + VPADC;         // chunks of a V^T row in LDS
     constexpr int KRS = 16 * KCH, VRS = 16 * VCH;
     constexpr int KCHUNKS = IKT * KCH, CHUNKS = KCHUNKS + D * VCH;
     constexpr int BUF = 16 * CHUNKS;
@@ -255,11 +260,11 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
         if (seg < KSEG) {
             const int r = ci / KCH, p = ci % KCH;
             off[u] = r * D + 8 * p;
-            live[u] = p < KCH - 1;
+            live[u] = p < D / 8;
         } else {
             const int r = (ci - KCHUNKS) / VCH, p = (ci - KCHUNKS) % VCH;
             off[u] = r * Tp + 8 * p;
-            live[u] = p < VCH - 1 && r < D;
+            live[u] = p < IKT / 8 && r < D;
         }
     }
     auto issue = [&](int j, char *buf) __attribute__((always_inline)) {

@@ -148,11 +148,28 @@ def bench_decode(args):
     g1.record()
     torch.cuda.synchronize()
     total_ms = g0.elapsed_time(g1)
-    res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
-               decode_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
-               qps=w.B * S / (total_ms / 1e3),
-               gbs=bytes_per_launch / (dec_ms / 1e3) / 1e9)
     del graph
+
+    # The decode kernel's own duration: S back-to-back sparse_decode launches
+    # (same tree, same queries) in one graph, so the events bracket kernels
+    # with only the dispatch gaps between them.
+    kgraph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(kgraph, stream=cs):
+            for s in range(S):
+                ts.sparse_decode(sel, qs[Wm + s], out, lse)
+    torch.cuda.synchronize()
+    g0.record()
+    kgraph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    kern_ms = g0.elapsed_time(g1) / S
+    del kgraph
+    res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
+               decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
+               qps=w.B * S / (total_ms / 1e3),
+               gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9)
     log(f"[decode] {res}")
     del K, V, ts
     torch.cuda.empty_cache()

@@ -1,0 +1,123 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: the 131,072-token decode, the 1,048,576-token decode at
+batch 4 (with one appended token), the 2,097,152-token top-p decode with four
+reference keys per node, and the 8192-token prefill block over a
+524,288-token prefix (the 4096-token fp32 workload is checked whole with the
+other decode tests).
+
+The caches are drawn on the device (seeded per sequence and head), the whole
+batch runs through the C ABI, and sampled (sequence, KV group) units -- and,
+for the prefill, sampled block rows -- are checked one by one against the
+oracle, which builds its own tree from the same cache rows copied to the
+host."""
+import numpy as np
+import pytest
+import torch
+
+import hti_workloads as W
+from gpu_helpers import accept, kmax_of, log, make_treeset, oracle_tree, select_of
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _host(x):
+    return x.cpu()
+
+
+def _decode_full(w, units, Lcap, append_steps=0):
+    """Build the tree over the full context, append `append_steps` tokens,
+    decode one query per sequence with the split kernel, and accept the
+    sampled units against the oracle."""
+    log(f"full-size decode {w.name}: B={w.B} L={w.L} Hkv={w.Hkv} levels={w.levels} R={w.R} {w.mode}")
+    K, V = W.gen_kv(w, Lcap=Lcap, device=DEV)
+    q0 = W.gen_queries(w)
+    if w.needles:
+        W.plant_needles(w, K, q0)
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, Lcap, K, V, refs.to(DEV))
+    ts.tree_build([w.L] * w.B)
+    for s in range(append_steps):
+        kn, vn = W.gen_append(w, s, device=DEV)
+        ts.tree_append(kn, vn)
+    L = w.L + append_steps
+    q = q0                     # the query whose direction the needles copy
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, 1, w.Hq), dtype=torch.float32, device=DEV)
+    sel = torch.empty((w.B, 1, w.Hkv, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_decode(select_of(w), q.to(DEV).contiguous(), out, lse, sel, split=True)
+    torch.cuda.synchronize()
+    assert ts.len.cpu().tolist() == [L] * w.B
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    nex, emax = 0, 0.0
+    for bi, g in units:
+        Kh, Vh = _host(K[bi, g, :L]), _host(V[bi, g, :L])
+        tree = oracle_tree(w, Kh, Vh, refs[g], L)
+        hs = slice(g * w.G, (g + 1) * w.G)
+        ex, err = accept(w, tree, Kh, Vh, q[bi, 0, hs], out[bi, 0, hs], lse[bi, 0, hs], sel[bi, 0, g])
+        log(f"  unit (seq {bi}, group {g}): exempt={ex} max_err={err:.2e}")
+        nex += ex
+        emax = max(emax, err)
+    assert np.isfinite(out).all()
+    return nex, emax
+
+
+def test_decode_128k_all_units():
+    """131,072 tokens, 32 query heads on 8 KV heads, 8 planted needles: every
+    unit checked."""
+    w = W.DEC128K
+    _decode_full(w, [(0, g) for g in range(w.Hkv)], Lcap=w.L)
+
+
+def test_decode_1m_batch4_sampled():
+    """1,048,576 tokens x 4 sequences, 16 planted needles each, one appended
+    token, then the decode step; four units sampled across sequences and
+    groups."""
+    w = W.DEC1M
+    _decode_full(w, [(0, 0), (1, 5), (2, 2), (3, 7)], Lcap=w.L + 4, append_steps=1)
+
+
+def test_decode_zha_2m_topp_sampled():
+    """2,097,152 tokens, b = 16, top-p 0.9 capped at 16 nodes, four reference
+    keys per node; both KV groups checked."""
+    w = W.ZHA2M
+    _decode_full(w, [(0, 0), (0, 1)], Lcap=w.L)
+
+
+def test_prefill_524k_block_sampled():
+    """8192-token block over the 524,288-token prefix; block rows at both ends,
+    the middle and a few seeded ones, in two KV groups."""
+    w = W.PREFILL
+    T = w.T
+    log(f"full-size prefill {w.name}: L={w.L} T={T}")
+    K, V = W.gen_kv(w, Lcap=w.L, device=DEV)
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, w.L, K, V, refs.to(DEV), T=T)
+    ts.tree_build([w.L] * w.B)
+    qb, kb, vb = W.gen_block(w)
+    sel = select_of(w)
+    ws = torch.empty(ts.prefill_workspace_bytes(sel, T), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, T, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, T, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, T, w.Hkv, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_prefill(sel, qb.to(DEV).contiguous(), kb.to(DEV).contiguous(), vb.to(DEV).contiguous(),
+                      out, ws, lse, so)
+    torch.cuda.synchronize()
+    out, lse, so = out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 1, 63, 64, T // 2, T - 2, T - 1] + rng.integers(0, T, 5).tolist()))
+    nex, emax = 0, 0.0
+    for g in (0, 5):
+        Kh, Vh = _host(K[0, g, :w.L]), _host(V[0, g, :w.L])
+        tree = oracle_tree(w, Kh, Vh, refs[g], w.L)
+        bk = kb[0, :, g].float().numpy()
+        bv = vb[0, :, g].float().numpy()
+        hs = slice(g * w.G, (g + 1) * w.G)
+        for t in rows:
+            ex, err = accept(w, tree, Kh, Vh, qb[0, t, hs], out[0, t, hs], lse[0, t, hs], so[0, t, g],
+                             t=t, blk_k=bk, blk_v=bv)
+            nex += ex
+            emax = max(emax, err)
+        log(f"  group {g}: {len(rows)} block rows, exempt so far {nex}, max_err {emax:.2e}")

@@ -309,6 +309,13 @@ def test_prefill_inblock_tiles(Hq, Hkv, d, P0, T):
     _check_prefill(w, P0, T)
 
 
+def test_prefill_b24():
+    """A branching factor that is not a power of two (b = 24): candidate
+    positions, orphans and the division by b in the index arithmetic."""
+    w = PF.replace(b=24, levels=2, k=6)
+    _check_prefill(w, 24 * 24 * 3 + 50, 40)
+
+
 def test_prefill_topp_r4():
     _check_prefill(W.ZHA2M.replace(name="pf_topp", levels=3), 16 ** 3 * 3 + 50, 48)
 

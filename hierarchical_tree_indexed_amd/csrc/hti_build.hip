@@ -92,23 +92,30 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
     const int64_t c0 = node * b;                 // first child (level lvl-1 index)
     const int64_t nchild_cap = t.ncap[lvl - 1];
 
+    // Children rg, rg + 4, ...: a slot past the last child reads child b-1
+    // and carries no weight, so that every load is unconditional and all of
+    // them (values included) are in flight together.
+    bool valid[CPL];
+    int64_t crow[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int child = rg + 4 * c;
+        valid[c] = child < b;
+        crow[c] = bh * nchild_cap + c0 + min(child, b - 1);
+    }
+    const T *vbase = (lvl == 1) ? (const T *)t.vc : (const T *)t.lv[lvl - 2];
+    float vx[CPL][EPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
+
     float kx[CPL][EPL];
     for (int j = 0; j < R; ++j) {
         if (lvl >= 2 || j == 0) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const int child = rg + 4 * c;
-                if (child < b) {
-                    const T *kp;
-                    if (lvl == 1)
-                        kp = (const T *)t.kc + ((bh * nchild_cap + c0 + child) * D);
-                    else
-                        kp = (const T *)t.lk[lvl - 2] + (((bh * nchild_cap + c0 + child) * R + j) * D);
-                    load_vec<T, EPL>(kp + sub * EPL, kx[c]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) kx[c][e] = 0.f;
-                }
+                const T *kp = (lvl == 1) ? (const T *)t.kc + crow[c] * D
+                                         : (const T *)t.lk[lvl - 2] + (crow[c] * R + j) * D;
+                load_vec<T, EPL>(kp + sub * EPL, kx[c]);
             }
         }
         float r[EPL];
@@ -123,7 +130,7 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
 #pragma unroll
             for (int e = 0; e < EPL; ++e) dot += r[e] * kx[c][e];
             dot = group_sum<16>(dot) * t.scale;
-            a[c] = (rg + 4 * c < b) ? dot : -INFINITY;
+            a[c] = valid[c] ? dot : -INFINITY;
             mx = fmaxf(mx, a[c]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -131,7 +138,7 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
         float den = 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            a[c] = (rg + 4 * c < b) ? expf(a[c] - mx) : 0.f;
+            a[c] = valid[c] ? expf(a[c] - mx) : 0.f;
             den += a[c];
         }
         den += __shfl_xor(den, 16, kWave);
@@ -163,17 +170,11 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
 #pragma unroll
     for (int e = 0; e < EPL; ++e) vs[e] = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int child = rg + 4 * c;
-        if (child < b) {
-            const T *vp = (lvl == 1) ? (const T *)t.vc + (bh * nchild_cap + c0 + child) * D
-                                     : (const T *)t.lv[lvl - 2] + (bh * nchild_cap + c0 + child) * D;
-            float v[EPL];
-            load_vec<T, EPL>(vp + sub * EPL, v);
+    for (int c = 0; c < CPL; ++c)
+        if (valid[c]) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) vs[e] += v[e];
+            for (int e = 0; e < EPL; ++e) vs[e] += vx[c][e];
         }
-    }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
         vs[e] += __shfl_xor(vs[e], 16, kWave);
@@ -200,9 +201,10 @@ __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl)
     pool_node<T, D, CPL>(t, lvl, bh, h, node, lane);
 }
 
-// Append one token per sequence: one block per sequence, one wave per KV head.
-template <typename T, int D, int CPL>
-__global__ void k_append(TreeArgs t, const T *kn, const T *vn)
+// Append one token per sequence: one block per sequence, one wave per KV head
+// (MAXT: the largest block, 64 * Hkv threads, which sets the register budget).
+template <typename T, int D, int CPL, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const T *vn)
 {
     const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int bi = blockIdx.x;
@@ -251,19 +253,26 @@ hipError_t launch_build_level(const TreeArgs &t, int lvl, int64_t max_nodes, hip
                       : build_level_d<float, 64>(t, lvl, max_nodes, s);
 }
 
+template <typename T, int D, int MAXT>
+static void append_b(const TreeArgs &t, const T *k, const T *v, hipStream_t s)
+{
+    dim3 grid(t.B), block(64 * t.Hkv);
+    if (t.b <= 8)
+        hipLaunchKernelGGL((k_append<T, D, 2, MAXT>), grid, block, 0, s, t, k, v);
+    else if (t.b <= 16)
+        hipLaunchKernelGGL((k_append<T, D, 4, MAXT>), grid, block, 0, s, t, k, v);
+    else if (t.b <= 32)
+        hipLaunchKernelGGL((k_append<T, D, 8, MAXT>), grid, block, 0, s, t, k, v);
+    else
+        hipLaunchKernelGGL((k_append<T, D, 16, MAXT>), grid, block, 0, s, t, k, v);
+}
+
 template <typename T, int D>
 static hipError_t append_d(const TreeArgs &t, const void *kn, const void *vn, hipStream_t s)
 {
-    dim3 grid(t.B), block(64 * t.Hkv);
     const T *k = (const T *)kn, *v = (const T *)vn;
-    if (t.b <= 8)
-        hipLaunchKernelGGL((k_append<T, D, 2>), grid, block, 0, s, t, k, v);
-    else if (t.b <= 16)
-        hipLaunchKernelGGL((k_append<T, D, 4>), grid, block, 0, s, t, k, v);
-    else if (t.b <= 32)
-        hipLaunchKernelGGL((k_append<T, D, 8>), grid, block, 0, s, t, k, v);
-    else
-        hipLaunchKernelGGL((k_append<T, D, 16>), grid, block, 0, s, t, k, v);
+    if (t.Hkv <= 8) append_b<T, D, 512>(t, k, v, s);
+    else append_b<T, D, 1024>(t, k, v, s);
     return hipGetLastError();
 }
 

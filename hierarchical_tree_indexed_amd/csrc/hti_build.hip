@@ -16,6 +16,8 @@
 // elements of each.  Dot products reduce over the 16 lanes of a row group,
 // the softmax and the weighted sums over the 4 row groups.  Every child byte
 // is read from HBM once; the node is written once.
+#include <type_traits>
+
 #include "hti_device.h"
 #include "hti_internal.h"
 
@@ -208,15 +210,32 @@ __global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const 
 {
     const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int bi = blockIdx.x;
-    const int64_t L = t.len[bi];
-    if (L >= t.ncap[0]) return;                        // cache full: unchanged
     const int64_t bh = (int64_t)bi * t.Hkv + h;
-    T *kc = (T *)t.kc + (bh * t.ncap[0] + L) * D;
-    T *vc = (T *)t.vc + (bh * t.ncap[0] + L) * D;
-    for (int e = lane; e < D; e += kWave) {
-        kc[e] = kn[bh * D + e];
-        vc[e] = vn[bh * D + e];
+    // the new row does not depend on the length: its loads go out with the
+    // length's (stores predicated on the length, not behind a branch)
+    constexpr int EPW = (D + 2 * kWave - 1) / (2 * kWave);   // bf16 / fp32 pairs per lane
+    uint64_t kr[EPW], vr[EPW];
+    static_assert(sizeof(T) <= 4, "element size");
+    using W2 = typename std::conditional<sizeof(T) == 2, uint32_t, uint64_t>::type;
+#pragma unroll
+    for (int u = 0; u < EPW; ++u) {
+        const int e = min(2 * (lane + u * kWave), D - 2);
+        kr[u] = *reinterpret_cast<const W2 *>(kn + bh * D + e);
+        vr[u] = *reinterpret_cast<const W2 *>(vn + bh * D + e);
     }
+    const int64_t L = t.len[bi];
+    const bool full = L >= t.ncap[0];                  // cache full: unchanged
+    T *kc = (T *)t.kc + (bh * t.ncap[0] + (full ? 0 : L)) * D;
+    T *vc = (T *)t.vc + (bh * t.ncap[0] + (full ? 0 : L)) * D;
+#pragma unroll
+    for (int u = 0; u < EPW; ++u) {
+        const int e = 2 * (lane + u * kWave);
+        if (!full && e < D) {
+            *reinterpret_cast<W2 *>(kc + e) = (W2)kr[u];
+            *reinterpret_cast<W2 *>(vc + e) = (W2)vr[u];
+        }
+    }
+    if (full) return;
     __syncthreads();
     int64_t idx = L + 1;                               // node count after the append
     for (int lvl = 1; lvl <= t.levels; ++lvl) {

@@ -97,10 +97,13 @@ struct Step {
     gptr<T> kb, vb;      // key / value rows of this unit: row r at kb + (r * nref + j) * D
     int nref;            // keys per row (R at summary levels, 1 at tokens)
     int m;               // candidates
-    int s0, ms;          // this workgroup's slice (first chunk at the token level)
+    int s0, ms;          // candidates this workgroup scores (first chunk at the token level)
     int t1;              // token level: end of this workgroup's range
+    int fs0, fms;        // candidates whose values this workgroup folds (its own slice)
     int qpos;            // RoPE position of the query
     bool take_all;       // every candidate is kept (no scoring)
+    bool local;          // the level fits one slice: every workgroup scores all of it and
+                         // selects on its own, without exchanging lists
 };
 
 } // namespace
@@ -207,8 +210,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             st.nref = R;
             st.take_all = (a.mode == HTI_TOPK) ? (st.m <= a.k) : (st.m <= 1);
             const int cpw = (st.m + W - 1) / W;
-            st.s0 = min(st.m, wg * cpw);
-            st.ms = min(st.m, st.s0 + cpw) - st.s0;
+            st.fs0 = min(st.m, wg * cpw);
+            st.fms = min(st.m, st.fs0 + cpw) - st.fs0;
+            st.local = !st.take_all && st.m <= kSlice;
+            st.s0 = st.local ? 0 : st.fs0;
+            st.ms = st.local ? st.m : st.fms;
             st.t1 = st.s0 + st.ms;
             st.qpos = st.m;
         } else {
@@ -226,6 +232,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             st.t1 = min(m0, t0 + cpw);
             st.s0 = t0;
             st.ms = min(kSlice, (int)st.t1 - t0);
+            st.fs0 = st.s0;
+            st.fms = st.ms;
+            st.local = false;
             st.qpos = m0 - (in ? 1 : 0);
         }
         return st;
@@ -295,7 +304,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                           float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
         const bool go = !st.take_all && st.ms > 0;
         load_batch(st, st.s0, st.ms, 0, go, k0, k1, rb);
-        issue_values(st, st.s0, st.ms, go, vr);
+        issue_values(st, st.fs0, st.fms, !st.take_all && st.fms > 0, vr);
         const gptr<float4> rp = (gptr<float4>)(rope + st.qpos * (D / 2) + sub * PPL);
 #pragma unroll
         for (int e = 0; e < PPL / 2; ++e) {
@@ -422,9 +431,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             alpha[h] = (mm == -INFINITY) ? 1.f : __expf(M[h] - mm);
         }
     };
-    // probabilities of this thread's candidate (kept ones drop out), the
-    // rescaled partial denominator and output
-    auto probs = [&](int ms, int zb, bool use_flags, const float (&Mn)[G], const float (&alpha)[G])
+    // probabilities of this thread's candidate tid in [lo, hi) (kept ones drop
+    // out), the rescaled partial denominator and output
+    auto probs = [&](int lo, int hi, int zb, bool use_flags, const float (&Mn)[G], const float (&alpha)[G])
         __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 #pragma unroll
             for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha[h];
         }
-        if (tid < ms) {
+        if (tid >= lo && tid < hi) {
             const bool kept = use_flags && sm.flag[tid];
             float *zp = &sm.z[zb][tid * G];
 #pragma unroll
@@ -446,9 +455,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int h = 0; h < G; ++h) M[h] = Mn[h];
     };
     // p * v over the slice's rows: the register batch, then any further rows
-    auto fold = [&](const Step<T> &st, int s0, int ms, int zb, const VR (&vr)[VBS]) __attribute__((always_inline)) {
+    // (zo: the z row of the range's first candidate)
+    auto fold = [&](const Step<T> &st, int s0, int ms, int zb, const VR (&vr)[VBS], int zo) __attribute__((always_inline)) {
         auto add_row = [&](int i, const float *v) __attribute__((always_inline)) {
-            const float *pz = &sm.z[zb][i * G];
+            const float *pz = &sm.z[zb][(zo + i) * G];
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -536,13 +546,21 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             if (Gr >= 4) rank += dppi<0x4E>(rank);
             if (Gr >= 8) rank += dppi<0x141>(rank);
             if (Gr >= 16) rank += dppi<0x140>(rank);
+            if (st.local) {
+                // the whole level: the rank is the global rank
+                if (valid && cc == 0 && rank < keff) {
+                    sm.byrank[rank] = ci;
+                    sm.byv[rank] = si;
+                }
+            } else {
             if (valid && cc == 0 && rank < keff)
                 __hip_atomic_store(&mine[rank], pack_word(tag, (uint32_t)(s0 + ci), si), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             if (tid >= ms && tid < keff)
                 __hip_atomic_store(&mine[tid], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            if (topp) {
+            }
+            if (topp && !st.local) {
                 // this wave's (max, exp-sum) of the group scores it holds
                 const bool own = valid && cc == 0;
                 const float wmax = wave_max(own ? si : -INFINITY);
@@ -556,9 +574,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
         }
 
+        const int kp4 = (keff + 3) & ~3;
+        int nkeep = min(keff, st.m);
+        if (!st.local) {
         // collect every slice's words (bounded polling on the tag); list w
         // lands at xv/xi[w * kp4 ..], padded to a multiple of 4 entries
-        const int kp4 = (keff + 3) & ~3;
         const int nrow = kp4 + (topp ? 2 * DNW : 0);
         for (int e = tid; e < W * nrow; e += DNT) {
             const int w = e / nrow, r = e % nrow;
@@ -600,7 +620,6 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         // lists, by binary search otherwise -- and the group sums the counts
         // with DPP.
         const int ne = W * kp4;
-        int nkeep = min(keff, st.m);
         {
             int P = 1;
             while (P < W) P <<= 1;
@@ -665,18 +684,24 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 }
             }
         }
+        }
         __syncthreads();                                                   // B3
         if (topp) {
             // shortest prefix of the sorted kept entries whose softmax mass
             // (over every candidate of the level) reaches p
             if (wave == 0) {
-                const int nw = W * DNW;
-                float gmax = -INFINITY;
-                for (int i = lane; i < nw; i += 64) gmax = fmaxf(gmax, sm.xm[i]);
-                gmax = wave_max(gmax);
-                float den = 0.f;
-                for (int i = lane; i < nw; i += 64)
-                    if (sm.xm[i] > -INFINITY) den += sm.xs[i] * __expf(sm.xm[i] - gmax);
+                float gmax = -INFINITY, den = 0.f;
+                if (st.local) {
+                    for (int i = lane; i < st.m; i += 64) gmax = fmaxf(gmax, sm.s[i]);
+                    gmax = wave_max(gmax);
+                    for (int i = lane; i < st.m; i += 64) den += __expf(sm.s[i] - gmax);
+                } else {
+                    const int nw = W * DNW;
+                    for (int i = lane; i < nw; i += 64) gmax = fmaxf(gmax, sm.xm[i]);
+                    gmax = wave_max(gmax);
+                    for (int i = lane; i < nw; i += 64)
+                        if (sm.xm[i] > -INFINITY) den += sm.xs[i] * __expf(sm.xm[i] - gmax);
+                }
                 den = wave_sum(den);
                 if (lane == 0) {
                     int ns = nkeep;
@@ -728,9 +753,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         st = make_step(lvl - 1, cur);
         issue_step(st, k0, k1, rb, vr, qcs);
         if (scored) {
-            probs(ms, zb, true, Mn, alpha);
+            // this workgroup's own candidates only (a local level was scored
+            // whole by every workgroup)
+            const int zo = stc.local ? stc.fs0 : 0;
+            probs(zo, zo + stc.fms, zb, true, Mn, alpha);
             __syncthreads();                                               // B5
-            fold(stc, s0, ms, zb, vrc);
+            fold(stc, stc.fs0, stc.fms, zb, vrc, zo);
             zb ^= 1;
         }
     }
@@ -747,9 +775,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         __syncthreads();
         float Mn[G], alpha[G];
         new_max(Mn, alpha);
-        probs(ms, zb, false, Mn, alpha);
+        probs(0, ms, zb, false, Mn, alpha);
         __syncthreads();
-        fold(st, c0, ms, zb, vr);
+        fold(st, c0, ms, zb, vr, 0);
         zb ^= 1;
     }
 

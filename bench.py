@@ -109,8 +109,8 @@ def bench_decode(args):
     lse = torch.empty((w.B, 1, w.Hq), dtype=torch.float32, device=DEV)
 
     def step(s):
-        ts.tree_append(ak[s], av[s])
-        ts.sparse_decode(sel, qs[s], out, lse)
+        # append this step's token and attend: one launch (decode_step)
+        ts.decode_step(sel, ak[s], av[s], qs[s], out, lse)
 
     for s in range(Wm):
         step(s)
@@ -121,9 +121,8 @@ def bench_decode(args):
     t0 = time.perf_counter()
     e0.record()
     for s in range(S):
-        ts.tree_append(ak[Wm + s], av[Wm + s])
         ev[s][0].record()
-        ts.sparse_decode(sel, qs[Wm + s], out, lse)
+        step(Wm + s)
         ev[s][1].record()
     e1.record()
     torch.cuda.synchronize()
@@ -133,7 +132,8 @@ def bench_decode(args):
     bytes_per_launch = sum(decode_unit_bytes(w, w.L + Wm + s + 1) for s in range(S)) / S * w.B * w.Hkv
 
     # The next S steps (fresh tokens and queries) captured into one HIP graph
-    # and replayed once: the same kernels, without a host launch per call.
+    # and replayed once: back-to-back launches of the step kernel, so the
+    # events bracket S kernels with only the dispatch gaps between them.
     graph = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -149,23 +149,7 @@ def bench_decode(args):
     torch.cuda.synchronize()
     total_ms = g0.elapsed_time(g1)
     del graph
-
-    # The decode kernel's own duration: S back-to-back sparse_decode launches
-    # (same tree, same queries) in one graph, so the events bracket kernels
-    # with only the dispatch gaps between them.
-    kgraph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(cs):
-        with torch.cuda.graph(kgraph, stream=cs):
-            for s in range(S):
-                ts.sparse_decode(sel, qs[Wm + s], out, lse)
-    torch.cuda.synchronize()
-    g0.record()
-    kgraph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    kern_ms = g0.elapsed_time(g1) / S
-    del kgraph
+    kern_ms = total_ms / S
     res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
                decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
                qps=w.B * S / (total_ms / 1e3),
@@ -324,7 +308,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "context": w.L, "Hq": w.Hq, "Hkv": w.Hkv,
                    "d": w.d, "b": w.b, "levels": w.levels, "k": w.k,
-                   "step": "tree_append + sparse_decode, steps captured in one HIP graph",
+                   "step": "decode_step (tree_append + sparse_decode in one launch), steps captured in one HIP graph",
                    "prefill_workload": W.PREFILL.name},
         "hbm_gbs": dec["gbs"] if dec else None,
         "decode_eager_ms_per_step": dec["eager_ms_per_step"] if dec else None,

@@ -27,8 +27,8 @@ STATUS = {0: "HTI_OK", -1: "HTI_ERR_INVALID_ARG", -2: "HTI_ERR_UNSUPPORTED",
           -3: "HTI_ERR_CAPACITY", -4: "HTI_ERR_WORKSPACE", -5: "HTI_ERR_LAUNCH"}
 
 EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append",
-           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_prefill_workspace_bytes",
-           "hti_sparse_prefill", "hti_last_error"]
+           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_decode_step",
+           "hti_prefill_workspace_bytes", "hti_sparse_prefill", "hti_last_error"]
 
 
 class TreeCfg(C.Structure):
@@ -78,6 +78,7 @@ def lib() -> C.CDLL:
             "hti_tree_append": (C.c_int, [vp, vp, vp, vp]),
             "hti_decode_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
             "hti_sparse_decode": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
+            "hti_decode_step": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
             "hti_prefill_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
             "hti_sparse_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp,
                                              C.c_size_t, vp]),
@@ -192,6 +193,20 @@ class TreeSet:
         _check(lib().hti_sparse_decode(C.byref(self.c), C.byref(sel), _ptr(q), Nq, _ptr(out),
                                        _ptr(lse), _ptr(sel_out), stride, _ptr(ws), nbytes,
                                        _stream(stream)))
+
+    def decode_step(self, sel: Select, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                    out: torch.Tensor, lse=None, sel_out=None, stream=None, split: bool = True):
+        """tree_append(k_new, v_new) followed by sparse_decode(q), in one launch
+        where the split kernel applies."""
+        B, Nq, Hq, d = q.shape
+        assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        stride = 0 if sel_out is None else sel_out.shape[-1]
+        ws = self.decode_workspace(sel, Nq) if split else None
+        nbytes = 0 if ws is None else ws.numel()
+        _check(lib().hti_decode_step(C.byref(self.c), C.byref(sel), _ptr(k_new), _ptr(v_new), _ptr(q), Nq,
+                                     _ptr(out), _ptr(lse), _ptr(sel_out), stride, _ptr(ws), nbytes,
+                                     _stream(stream)))
 
     def prefill_workspace_bytes(self, sel: Select, T: int) -> int:
         return lib().hti_prefill_workspace_bytes(C.byref(self.cfg), C.byref(sel), T)

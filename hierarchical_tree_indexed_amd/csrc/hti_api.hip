@@ -325,12 +325,17 @@ size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel
     (void)sel;
     if (check_cfg(cfg) || Nq < 1) return 0;
     const int64_t units = (int64_t)cfg->B * Nq * cfg->Hkv;
-    return decode_ws_bytes(units, HTI_DECODE_MAX_SPLIT, cfg->levels, cfg->Hq / cfg->Hkv, cfg->d);
+    return decode_ws_bytes(cfg->B, units, HTI_DECODE_MAX_SPLIT, cfg->levels, cfg->Hq / cfg->Hkv, cfg->d);
 }
 
-hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q, int32_t Nq,
-                             float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *ws,
-                             size_t ws_bytes, void *stream)
+} // extern "C"
+
+namespace {
+
+// sparse_decode, and the decode step (k_new != NULL: append, then decode)
+hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select *sel, const void *k_new,
+                       const void *v_new, const void *q, int32_t Nq, float *out, float *lse, int32_t *sel_out,
+                       int32_t sel_stride, void *ws, size_t ws_bytes, void *stream)
 {
     hti_status st = check_traversal(tree, sel, 0, sel_out, sel_stride);
     if (st) return st;
@@ -338,7 +343,7 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
     if (Nq < 1) return fail(HTI_ERR_INVALID_ARG, "Nq must be >= 1");
     const int64_t units_ws = (int64_t)tree->cfg.B * Nq * tree->cfg.Hkv;
     const int G = tree->cfg.Hq / tree->cfg.Hkv;
-    if (ws && ws_bytes < decode_ws_bytes(units_ws, HTI_DECODE_MAX_SPLIT, tree->cfg.levels, G, tree->cfg.d))
+    if (ws && ws_bytes < decode_ws_bytes(tree->cfg.B, units_ws, HTI_DECODE_MAX_SPLIT, tree->cfg.levels, G, tree->cfg.d))
         return fail(HTI_ERR_WORKSPACE, "decode workspace of %zu bytes is too small", ws_bytes);
     TravArgs a{};
     a.t = tree_args(tree);
@@ -355,19 +360,52 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
     a.binv = binv_of(tree->cfg.b);
     const int64_t units = units_ws;
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
+    const hipStream_t hs = (hipStream_t)stream;
+    int W = 0;
     if (ws) {
         // split each unit over W workgroups when all of them fit on the device
         // at once; otherwise one workgroup per unit
         const Bounds bd = bounds(&tree->cfg, sel, 0);
-        int W = 0;
         hipError_t e = decode_split_plan(a, units, bd.max_summary, &W);
-        if (e != hipSuccess) return launched(e, "sparse_decode(plan)");
-        if (W > 0) {
-            const DecodeWs dw = decode_ws_layout(ws, units, W, tree->cfg.levels, G, tree->cfg.d);
-            return launched(launch_decode_split(a, dw, units, (hipStream_t)stream), "sparse_decode");
+        if (e != hipSuccess) return launched(e, what);
+    }
+    if (k_new) {
+        if (W > 0 && tree->cfg.b <= 32) {
+            // the split kernel appends the token itself (one launch)
+            a.k_new = k_new;
+            a.v_new = v_new;
+        } else {
+            hipError_t e = launch_append(a.t, k_new, v_new, hs);
+            if (e != hipSuccess) return launched(e, what);
         }
     }
-    return launched(launch_traverse(a, false, units, (hipStream_t)stream), "sparse_decode");
+    if (W > 0) {
+        const DecodeWs dw = decode_ws_layout(ws, tree->cfg.B, units, W, tree->cfg.levels, G, tree->cfg.d);
+        return launched(launch_decode_split(a, dw, units, hs), what);
+    }
+    return launched(launch_traverse(a, false, units, hs), what);
+}
+
+} // namespace
+
+extern "C" {
+
+hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q, int32_t Nq,
+                             float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    return decode_impl("sparse_decode", tree, sel, nullptr, nullptr, q, Nq, out, lse, sel_out, sel_stride, ws,
+                       ws_bytes, stream);
+}
+
+hti_status hti_decode_step(const hti_tree *tree, const hti_select *sel, const void *k_new, const void *v_new,
+                           const void *q, int32_t Nq, float *out, float *lse, int32_t *sel_out,
+                           int32_t sel_stride, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!k_new || !v_new) return fail(HTI_ERR_INVALID_ARG, "k_new/v_new is NULL");
+    if (hti_status st = check_tree(tree, true)) return st;
+    return decode_impl("decode_step", tree, sel, k_new, v_new, q, Nq, out, lse, sel_out, sel_stride, ws, ws_bytes,
+                       stream);
 }
 
 size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T)

@@ -38,6 +38,7 @@
 
 #include "hti_device.h"
 #include "hti_internal.h"
+#include "hti_pool.h"
 #include "hti_trav_common.h"
 
 namespace hti {
@@ -73,6 +74,8 @@ struct DSmem {
     const void *lvp[HTI_MAX_LEVELS];
     uint32_t tag;
     int bad;                          // a wait of this workgroup timed out
+    int app;                          // decode step: the new token goes in at position lold
+    int lold;                         // sequence length before the step
 };
 
 __device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t idx, float v)
@@ -147,6 +150,16 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     }
     if (tid == 0) {
         int n = (int)t.len[bi];
+        // decode step: this workgroup appends the new token itself (every
+        // workgroup of every query of the sequence writes the same bytes) and
+        // walks the tree with the new length; it counts itself as having read
+        // the old length, which one workgroup replaces at the end
+        const bool app = a.k_new != nullptr && (int64_t)n < t.ncap[0];
+        sm.app = app ? 1 : 0;
+        sm.lold = n;
+        if (a.k_new != nullptr)
+            __hip_atomic_fetch_add(&ws.seqcnt[bi], n >= 0 ? 1u : 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (app) ++n;
         sm.n[0] = n;
         const int bs = __builtin_ctz((unsigned)b);
         const bool pow2 = (b & (b - 1)) == 0;
@@ -183,6 +196,26 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
     }
     __syncthreads();
+    if (sm.app) {
+        // the new row of this unit's KV head at position lold, then every
+        // node it completes, level by level (one wave pools)
+        const int64_t Lold = sm.lold;
+        const T *kn = (const T *)a.k_new + bh * D, *vn = (const T *)a.v_new + bh * D;
+        T *kw = (T *)t.kc + (bh * t.ncap[0] + Lold) * D;
+        T *vw = (T *)t.vc + (bh * t.ncap[0] + Lold) * D;
+        for (int e = tid; e < D; e += DNT) {
+            kw[e] = kn[e];
+            vw[e] = vn[e];
+        }
+        __syncthreads();
+        int64_t idx = Lold + 1;
+        for (int l = 1; l <= levels; ++l) {
+            if (idx % b != 0) break;
+            idx /= b;
+            if (wave == 0) pool_node<T, D, 8>(t, l, bh, g, idx - 1, lane);
+            __syncthreads();
+        }
+    }
     const uint32_t tag = sm.tag;
     const int L = sm.n[0];
     const int last_leaf = L > 0 ? (L - 1) / b : -1;   // level-1 node of the query token
@@ -893,6 +926,19 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // every workgroup of this unit has read the launch tag (they all published
     // their partial state above), so the next launch may move it on
     if (wg == 0 && tid == 0) ws.epoch[unit] = ws.epoch[unit] + 1u;
+    // decode step: once every workgroup of the sequence has read the old
+    // length (bounded wait), the first workgroup of its first unit stores the
+    // new one and clears the count for the next step
+    if (a.k_new != nullptr && wg == 0 && g == 0 && qi == 0 && tid == 0) {
+        const uint32_t need = (uint32_t)W * (uint32_t)t.Hkv * (uint32_t)a.Nq;
+        long spins = 0;
+        while (__hip_atomic_load(&ws.seqcnt[bi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need &&
+               ++spins < kSpin)
+            __builtin_amdgcn_s_sleep(1);
+        if (spins >= kSpin) __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (sm.app) __hip_atomic_store(&t.len[bi], (int64_t)sm.lold + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws.seqcnt[bi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int G, int D>
@@ -990,17 +1036,17 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
     return hipSuccess;
 }
 
-size_t decode_ws_bytes(int64_t units, int W, int levels, int G, int D)
+size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D)
 {
     size_t off = 0;
     off += ((size_t)units * 4 + 255) / 256 * 256;                 // epoch
     off += ((size_t)units * 4 + 255) / 256 * 256;                 // err
     off += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
     off += ((size_t)units * W * G * (D + 2) * 8 + 255) / 256 * 256;
+    off += ((size_t)B * 4 + 255) / 256 * 256;                     // seqcnt
     return off;
 }
-
-DecodeWs decode_ws_layout(void *base, int64_t units, int W, int levels, int G, int D)
+DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, int G, int D)
 {
     DecodeWs w{};
     char *p = (char *)base;
@@ -1012,6 +1058,9 @@ DecodeWs decode_ws_layout(void *base, int64_t units, int W, int levels, int G, i
     w.words = (uint64_t *)p;
     p += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
     w.part = (uint64_t *)p;
+    p += ((size_t)units * W * G * (D + 2) * 8 + 255) / 256 * 256;
+    w.seqcnt = (uint32_t *)p;
+    (void)B;
     return w;
 }
 

@@ -38,6 +38,9 @@ struct TravArgs {
     float *lse;        // decode [B, Nq, Hq] (nullable)
     int *sel;          // [B, Nq, Hkv, levels, sel_stride] (nullable)
     int sel_stride;
+    // decode step: the token appended to every sequence before the queries
+    // attend, [B, Hkv, D] each (nullptr: plain decode)
+    const void *k_new, *v_new;
     // prefill only
     const float *top_s;  // [B, T, Hkv, ntop_stride] group scores of the top level (nullable)
     const float *top_z;  // [B, T, Hq, ntop_stride] per-head logits of the top level
@@ -56,11 +59,12 @@ struct DecodeWs {
     uint32_t *err;      // [units]: tag of the last launch in which a wait timed out
     uint64_t *words;    // [units][levels][W][HTI_MAX_SELECT + 2]
     uint64_t *part;     // [units][W][G][D + 2]: tag << 32 | fp32 bits
+    uint32_t *seqcnt;   // [B]: workgroups of a decode step that have read the sequence length
 };
 // W > 0: split each unit over W workgroups; W == 0: one workgroup per unit.
 hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W);
-size_t decode_ws_bytes(int64_t units, int W, int levels, int G, int D);
-DecodeWs decode_ws_layout(void *base, int64_t units, int W, int levels, int G, int D);
+size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D);
+DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, int G, int D);
 hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s);
 
 hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s);

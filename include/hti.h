@@ -194,6 +194,28 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
                              int32_t sel_stride, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * hti_decode_step: one decode step of every sequence -- append the step's
+ * token (as hti_tree_append) and then attend (as hti_sparse_decode, the
+ * queries at position len[s] - 1 of the grown sequence).  The result, the
+ * caches, the tree levels and len are those of the two calls in that order.
+ *   k_new, v_new: [B, Hkv, d] in the cache dtype; the other arguments as for
+ *   hti_sparse_decode (the same workspace).
+ * With a workspace and b <= 32 this is one kernel launch: every workgroup of
+ * a (sequence, KV group) writes the new row and pools the nodes it completes
+ * itself (identical bytes), and one workgroup per sequence advances len once
+ * every workgroup of that sequence has read the old value (a bounded wait; a
+ * timeout marks the affected outputs NaN as in hti_sparse_decode).  Otherwise
+ * it runs the two calls.  The workspace keeps a per-sequence count between
+ * steps, so steps that share it must not overlap.
+ * Source: RecSA abstract (decoding over the tree); ZHA Table VIII (decode
+ * maintenance amortised over full-node completions).
+ */
+hti_status hti_decode_step(const hti_tree *tree, const hti_select *sel, const void *k_new,
+                           const void *v_new, const void *q, int32_t Nq, float *out, float *lse,
+                           int32_t *sel_out, int32_t sel_stride, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
  * hti_prefill_workspace_bytes: device workspace hti_sparse_prefill needs.
  */
 size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T);

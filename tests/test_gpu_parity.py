@@ -338,12 +338,76 @@ def test_prefill_T1_equals_decode():
     assert np.abs(pout[:, 0] - dout[:, 0]).max() < 2e-2
 
 
+# --------------------------------------------------------------------------- decode step
+STEP_CASES = [
+    # steps 3..4 complete a level-1 and a level-2 node (b = 32)
+    W.DEC128K.replace(name="step_b32", B=2, L=32 * 32 * 3 - 3, levels=2, needles=0),
+    # b = 16, top-p with four reference keys: a level-3 node completes
+    W.ZHA2M.replace(name="step_topp_r4_b16", L=16 ** 3 * 2 - 4, levels=3),
+    # G = 8, d = 64, b = 8, two queries per sequence
+    W.DEC128K.replace(name="step_g8_d64_b8_nq2", Hq=16, Hkv=2, d=64, b=8, levels=3, L=8 ** 3 * 2 - 5,
+                      needles=0, k=3, Nq=2),
+    # b = 64: the two-launch form
+    W.DEC128K.replace(name="step_b64", b=64, levels=2, L=64 * 64 - 3, k=4, needles=0),
+]
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=lambda w: w.name)
+def test_decode_step_matches_append_then_decode(w):
+    """decode_step (one launch where the split kernel applies) against
+    tree_append followed by sparse_decode on a second tree set: outputs,
+    lse, selections, lengths, caches and every tree level bit for bit, over
+    steps that complete nodes; the last step also against the oracle."""
+    steps = 8
+    Lcap = w.L + steps
+    K, V = W.gen_kv(w, Lcap=Lcap)
+    refs = W.gen_refs(w)
+    ta = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    tb = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    ta.tree_build([w.L] * w.B)
+    tb.tree_build([w.L] * w.B)
+    sel = select_of(w)
+    kmax = kmax_of(w)
+    shape = (w.B, w.Nq, w.Hq, w.d)
+    oa, ob = (torch.empty(shape, dtype=torch.float32, device=DEV) for _ in range(2))
+    la, lb = (torch.empty(shape[:3], dtype=torch.float32, device=DEV) for _ in range(2))
+    sa, sb = (torch.empty((w.B, w.Nq, w.Hkv, w.levels, kmax), dtype=torch.int32, device=DEV) for _ in range(2))
+    for s in range(steps):
+        kn, vn = W.gen_append(w, s, device=DEV)
+        q = W.gen_queries(w, step=s + 1).to(DEV).contiguous()
+        ta.decode_step(sel, kn.contiguous(), vn.contiguous(), q, oa, la, sa)
+        tb.tree_append(kn.contiguous(), vn.contiguous())
+        tb.sparse_decode(sel, q, ob, lb, sb)
+        torch.cuda.synchronize()
+        assert torch.equal(ta.len, tb.len), s
+        assert torch.equal(oa, ob), f"step {s}: max diff {(oa - ob).abs().max().item()}"
+        assert torch.equal(la, lb) and torch.equal(sa, sb), s
+    assert ta.len.cpu().tolist() == [w.L + steps] * w.B
+    assert torch.equal(ta.k_cache, tb.k_cache) and torch.equal(ta.v_cache, tb.v_cache)
+    for l in range(w.levels):
+        assert torch.equal(ta.lvl_k[l], tb.lvl_k[l]) and torch.equal(ta.lvl_v[l], tb.lvl_v[l]), l
+    # the last step against the oracle, on the grown caches
+    L = w.L + steps
+    Kh, Vh = ta.k_cache.cpu(), ta.v_cache.cpu()
+    out, lse, so = oa.cpu().numpy(), la.cpu().numpy(), sa.cpu().numpy()
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            tree = oracle_tree(w, Kh[bi, g], Vh[bi, g], refs[g], L)
+            hs = slice(g * w.G, (g + 1) * w.G)
+            for qi in range(w.Nq):
+                accept(w, tree, Kh[bi, g, :L], Vh[bi, g, :L], q.cpu()[bi, qi, hs], out[bi, qi, hs],
+                       lse[bi, qi, hs], so[bi, qi, g])
+    log(f"  {w.name}: {steps} steps, lengths {ta.len.cpu().tolist()}")
+
+
 # --------------------------------------------------------------------------- graph capture
-@pytest.mark.parametrize("split", [True, False])
-def test_decode_graph_replay_matches_eager(split):
-    """A step of tree_append + sparse_decode captured into a HIP graph gives,
-    on every replay, what the same calls give eagerly: a second tree set
-    runs the calls eagerly between the replays, from the same start."""
+@pytest.mark.parametrize("mode", ["split", "unsplit", "step"])
+def test_decode_graph_replay_matches_eager(mode):
+    """A step of tree_append + sparse_decode (or the fused decode_step)
+    captured into a HIP graph gives, on every replay, what tree_append +
+    sparse_decode give eagerly: a second tree set runs those calls eagerly
+    between the replays, from the same start."""
+    split = mode != "unsplit"
     w = W.DEC128K.replace(name="graph", B=2, L=32 * 156 + 29, levels=2, needles=0)   # completes a node
     steps = 4
     Lcap = w.L + steps
@@ -367,8 +431,11 @@ def test_decode_graph_replay_matches_eager(split):
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(graph, stream=stream):
-            tg.tree_append(kn, vn)
-            tg.sparse_decode(sel, q, og, split=split)
+            if mode == "step":
+                tg.decode_step(sel, kn, vn, q, og)
+            else:
+                tg.tree_append(kn, vn)
+                tg.sparse_decode(sel, q, og, split=split)
     torch.cuda.synchronize()
     for r in range(steps):
         graph.replay()

@@ -431,6 +431,16 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
         return fail(HTI_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
     const int64_t units = (int64_t)tree->cfg.B * T * tree->cfg.Hkv;
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
+    {
+        // the traversal addresses rows by 32-bit byte offsets within one
+        // (sequence, KV head) slice of the cache and of each level
+        int64_t ncap[HTI_MAX_LEVELS + 1];
+        caps(&tree->cfg, ncap);
+        int64_t big = ncap[0];
+        for (int l = 1; l <= tree->cfg.levels; ++l) big = std::max(big, ncap[l] * tree->cfg.R);
+        if (big * tree->cfg.d * 2 > (int64_t)0xffffffffll)
+            return fail(HTI_ERR_UNSUPPORTED, "prefill needs each (sequence, KV head) cache slice under 4 GiB");
+    }
     char *wb = (char *)ws;
     hipStream_t hs = (hipStream_t)stream;
 

@@ -20,6 +20,7 @@
 // other's memory latency.  It leaves the unit's partial softmax state
 // (unnormalised output, running max, denominator) for the in-block kernel.
 #include <algorithm>
+#include <type_traits>
 
 #include "hti_device.h"
 #include "hti_internal.h"
@@ -63,13 +64,90 @@ __device__ __forceinline__ void wave_best(float &v, int &i)
     i = i0;
 }
 
+// Sums over the 16 lanes of a row of the G values z[0..G) at once, as a
+// transposed butterfly: at each lane bit from 3 down, the lanes with the bit
+// set keep the upper half of the values still open and swap the other half
+// with their partner.  Lane `sub` ends with the sum of value sub / (16 / G).
+template <int G>
+__device__ __forceinline__ float row_sums(const float (&z)[G], int sub)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1, 2, 4, 8}");
+    float a[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) a[h] = z[h];
+    auto half = [&](auto ctrl, int n, bool hi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < n; ++h) {
+            const float keep = hi ? a[h + n] : a[h];
+            const float send = hi ? a[h] : a[h + n];
+            a[h] = keep + dppf<decltype(ctrl)::value>(send);
+        }
+    };
+    using Mirror = std::integral_constant<int, 0x140>;      // lane i <-> 15 - i
+    using HalfMirror = std::integral_constant<int, 0x141>;  // i <-> 7 - i within each half
+    using Swap2 = std::integral_constant<int, 0x4E>;        // i <-> i ^ 2
+    if constexpr (G >= 2) half(Mirror{}, G / 2, (sub & 8) != 0);
+    else a[0] += dppf<0x140>(a[0]);
+    if constexpr (G >= 4) half(HalfMirror{}, G / 4, (sub & 4) != 0);
+    else a[0] += dppf<0x141>(a[0]);
+    if constexpr (G >= 8) half(Swap2{}, 1, (sub & 2) != 0);
+    else a[0] += dppf<0x4E>(a[0]);
+    a[0] += dppf<0xB1>(a[0]);
+    return a[0];
+}
+
+// Sum over the G values a lane group holds after row_sums (the values differ
+// across lane bits 3, 2, 1 for G = 2, 4, 8 and are equal within a group).
+template <int G>
+__device__ __forceinline__ float head_total(float v)
+{
+    if constexpr (G >= 8) v += dppf<0x4E>(v);
+    if constexpr (G >= 4) v += dppf<0x141>(v);
+    if constexpr (G >= 2) v += dppf<0x140>(v);
+    return v;
+}
+
+// Buffer resource over `base` (raw, unswizzled; reads past `bytes` return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename R> __device__ __forceinline__ R bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <> __device__ __forceinline__ uint16_t bload<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)v, (int)s, 0);
+}
+template <> __device__ __forceinline__ uint32_t bload<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)v, (int)s, 0);
+}
+template <> __device__ __forceinline__ uint2 bload<uint2>(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)v, (int)s, 0);
+    return make_uint2(x[0], x[1]);
+}
+template <> __device__ __forceinline__ uint4 bload<uint4>(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, (int)s, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// acc + a.lo * b.lo + a.hi * b.hi over bf16 pairs, fp32 accumulation
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                           false);
+}
+
 } // namespace
 
-// Per-wave LDS (4-byte words): qraw [G*D], s [MC + 64], z [MC * G],
+// Per-wave LDS (4-byte words): qraw [G*D], probability pairs [MC/2 * G],
+// s [MC + 64] (the last 64 words take discarded stores), z [MC * G],
 // kept-node lists [2][kMaxSel]
 __host__ __device__ constexpr size_t pw_wave_words(int G, int D, int MC)
 {
-    return (size_t)G * D + MC + 64 + (size_t)MC * G + 2 * kMaxSel;
+    return (size_t)G * D + (size_t)(MC / 2) * G + MC + 64 + (size_t)MC * G + 2 * kMaxSel;
 }
 
 template <int D, int G, int MJ>
@@ -82,7 +160,9 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
     static_assert(KB >= HTI_MAX_R, "a batch holds one candidate's reference keys");
     constexpr int DPL = D / 64;           // value elements per lane (the wave holds one row)
     using VR = typename Raw<T, DPL>::type;
-    constexpr int VB = 16;                // value rows per batch
+    constexpr int VB = 16;                // value rows per batch (even: rows go in pairs)
+    constexpr int LPH = 16 / G;           // lanes per head after row_sums
+    constexpr int RB = D / 2 * 8;         // bytes per RoPE table row
     static_assert(MJ <= 32, "kept bits fit one word");
     extern __shared__ __attribute__((aligned(16))) unsigned char pw_lds[];
 
@@ -106,7 +186,8 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 
     float *lds = reinterpret_cast<float *>(pw_lds) + (size_t)wave * pw_wave_words(G, D, MC);
     float *qraw = lds;
-    float *sS = qraw + G * D;
+    uint32_t *sP = reinterpret_cast<uint32_t *>(qraw + G * D);
+    float *sS = reinterpret_cast<float *>(sP + (size_t)(MC / 2) * G);
     float *sZ = sS + MC + 64;
     int *selbuf = reinterpret_cast<int *>(sZ + (size_t)MC * G);
 
@@ -125,13 +206,6 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         }
     }
     const int L = nlev[0];
-    float st_c[PPL], st_s[PPL];
-#pragma unroll
-    for (int e = 0; e < PPL; ++e) {
-        const float2 c2 = t.rope[(D / 2) + sub * PPL + e];
-        st_c[e] = c2.x;
-        st_s[e] = c2.y;
-    }
     float M[G], lt[G], acc[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -140,14 +214,22 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
     }
+    // RoPE table as a buffer: rows past its end read as zeros
+    const __amdgpu_buffer_rsrc_t rope_rs =
+        rsrc(t.rope, (uint32_t)std::min<int64_t>((int64_t)t.rope_npos * RB, 0xffffffffll));
     wave_sync();
 
     // ---- logits of candidates c0 .. c0 + m - 1 of a list (RoPE positions
     // c0 + i; keys at kb + (id * nref + j) * D; the query at qpos) into sZ,
-    // group scores into sS, both indexed from 0.  Quarter q scores a
-    // contiguous run of the list, KB key items per batch.
-    auto score = [&](const Cands &cs, const T *kb, int nref, int c0, int m, int qpos)
+    // and their group scores into sS when WGS, both indexed from 0.  Quarter
+    // q scores a contiguous run of the list, KB key items per batch; the
+    // query is turned to its position and scaled by 1/sqrt(d) once, every key
+    // is turned to its candidate's position, and one transposed butterfly
+    // sums the G heads' partial dot products, leaving head sub / LPH in lane
+    // sub.
+    auto score = [&](auto wgs, const Cands &cs, const T *kb, int nref, int c0, int m, int qpos)
         __attribute__((always_inline)) {
+        constexpr bool WGS = decltype(wgs)::value;
         float qa[G][PPL], qb[G][PPL];
         {
             const float2 *rq = t.rope + (int64_t)qpos * (D / 2) + sub * PPL;
@@ -157,93 +239,156 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const float x0 = qraw[h * D + sub * PPL + e], x1 = qraw[h * D + D / 2 + sub * PPL + e];
-                    qa[h][e] = x0 * cq.x - x1 * cq.y;
-                    qb[h][e] = x0 * cq.y + x1 * cq.x;
+                    qa[h][e] = (x0 * cq.x - x1 * cq.y) * t.scale;
+                    qb[h][e] = (x0 * cq.y + x1 * cq.x) * t.scale;
                 }
             }
         }
+        const __amdgpu_buffer_rsrc_t krs = rsrc(kb, 0xffffffffu);
+        const uint32_t klane = sub * PPL * 2;      // bytes: the lane's pairs within a key half
         const int cpq = (m + 3) / 4;
         const int cb = min(m, quarter * cpq);
         const int ce = min(m, cb + cpq);
         const int nitems = (ce - cb) * nref;
-        const int KBR = (KB / nref) * nref;
-        const int nbatch = (cpq * nref + KBR - 1) / KBR;   // the same in every quarter
-        for (int bt = 0; bt < nbatch; ++bt) {
-            const int it0 = bt * KBR;
-            const int nb = min(nitems - it0, KBR);         // <= 0 for a short quarter
-            // lane `sub` derives the row of item it0 + sub (clamped into the
-            // batch); row u reaches the quarter by a DPP row broadcast
-            const int itl = it0 + (nb > 0 ? min(sub, nb - 1) : 0);
-            const int cl = itl / nref;
-            const int cand = max(0, min(cb + cl, m - 1));
-            const uint32_t row = (uint32_t)(cs.id(c0 + cand) * nref + (itl - cl * nref));
-            KR k0[KB], k1[KB];
+        const int hsel = sub / LPH;
+        const bool wz = (sub % LPH) == 0;          // lanes that store a head's logit
+        const bool ws = WGS && sub == 1;           // the lane that stores the group score
+        // z of one key item: the key turned by (c, s), dotted with the G heads
+        auto logits = [&](const KR &kx0, const KR &kx1, const float (&c)[PPL], const float (&sn)[PPL])
+            __attribute__((always_inline)) {
+            float x0[PPL], x1[PPL];
+            cvt(kx0, x0);
+            cvt(kx1, x1);
+            float z[G];
 #pragma unroll
-            for (int u = 0; u < KB; ++u) {
-                const uint32_t ru = (uint32_t)row_bcast((int)row, u);
-                const T *kp = kb + (size_t)ru * D;
-                k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
-                k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
-            }
-            float cc[PPL], ss[PPL];
-            {
-                const int pos = c0 + max(0, min(cb + it0 / nref, m - 1));
-                const float2 *rp = t.rope + (int64_t)pos * (D / 2) + sub * PPL;
+            for (int e = 0; e < PPL; ++e) {
+                const float r0 = x0[e] * c[e] - x1[e] * sn[e];
+                const float r1 = x0[e] * sn[e] + x1[e] * c[e];
 #pragma unroll
-                for (int e = 0; e < PPL; ++e) {
-                    const float2 c2 = rp[e];
-                    cc[e] = c2.x;
-                    ss[e] = c2.y;
+                for (int h = 0; h < G; ++h) {
+                    z[h] = (e == 0) ? qa[h][0] * r0 : fmaf(qa[h][e], r0, z[h]);
+                    z[h] = fmaf(qb[h][e], r1, z[h]);
                 }
             }
-            int ci = cb + it0 / nref, j = 0;
-            float best = -INFINITY;
-            float zbst[G];
+            return row_sums<G>(z, sub);
+        };
+        if (nref == 1) {
+            // every item is a candidate: no reference-key maximum.  The items
+            // of a quarter's batch sit at consecutive positions: the batch
+            // reads (cos, sin) of its first position and of one position's
+            // step, and turns the rotation on by one step per key.
+            const int nbatch = (cpq + KB - 1) / KB;   // the same in every quarter
+            for (int bt = 0; bt < nbatch; ++bt) {
+                const int it0 = bt * KB;
+                const int nb = min(nitems - it0, KB);  // <= 0 for a short quarter
+                // lane `sub` derives the row of item it0 + sub (clamped into
+                // the batch); row u reaches the quarter by a DPP row broadcast
+                const int cand = max(0, min(cb + it0 + (nb > 0 ? min(sub, nb - 1) : 0), m - 1));
+                const uint32_t roff = (uint32_t)cs.id(c0 + cand) * (D * 2);
+                KR k0[KB], k1[KB];
 #pragma unroll
-            for (int h = 0; h < G; ++h) zbst[h] = 0.f;
+                for (int u = 0; u < KB; ++u) {
+                    const uint32_t o = (uint32_t)row_bcast((int)roff, u) + klane;
+                    k0[u] = bload<KR>(krs, o, 0);
+                    k1[u] = bload<KR>(krs, o + D, 0);
+                }
+                const uint32_t rbase = (uint32_t)(c0 + cb + it0) * RB + sub * PPL * 8;
+                float c[PPL], sn[PPL], stc[PPL], sts[PPL];
 #pragma unroll
-            for (int u = 0; u < KB; ++u) {
-                if (u < nb) {
-                    float x0[PPL], x1[PPL];
-                    cvt(k0[u], x0);
-                    cvt(k1[u], x1);
-                    float z[G];
+                for (int w = 0; w < PPL / 2; ++w) {
+                    const uint4 cs4 = bload<uint4>(rope_rs, rbase + w * 16, 0);
+                    c[2 * w] = __uint_as_float(cs4.x);
+                    sn[2 * w] = __uint_as_float(cs4.y);
+                    c[2 * w + 1] = __uint_as_float(cs4.z);
+                    sn[2 * w + 1] = __uint_as_float(cs4.w);
+                    const uint4 st4 = bload<uint4>(rope_rs, RB + sub * PPL * 8 + w * 16, 0);
+                    stc[2 * w] = __uint_as_float(st4.x);
+                    sts[2 * w] = __uint_as_float(st4.y);
+                    stc[2 * w + 1] = __uint_as_float(st4.z);
+                    sts[2 * w + 1] = __uint_as_float(st4.w);
+                }
 #pragma unroll
-                    for (int h = 0; h < G; ++h) z[h] = 0.f;
-#pragma unroll
-                    for (int e = 0; e < PPL; ++e) {
-                        const float r0 = x0[e] * cc[e] - x1[e] * ss[e];
-                        const float r1 = x0[e] * ss[e] + x1[e] * cc[e];
-#pragma unroll
-                        for (int h = 0; h < G; ++h) z[h] += qa[h][e] * r0 + qb[h][e] * r1;
-                    }
-                    float gs = 0.f;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        z[h] = sum16(z[h]) * t.scale;
-                        gs += z[h];
-                    }
-                    gs = gs / (float)G;
-                    if (gs > best) {
-                        best = gs;
-#pragma unroll
-                        for (int h = 0; h < G; ++h) zbst[h] = z[h];
-                    }
-                    if (++j == nref) {
-                        if (sub == 0) {
-                            sS[ci] = best;
-#pragma unroll
-                            for (int h = 0; h < G; ++h) sZ[ci * G + h] = zbst[h];
-                        }
-                        j = 0;
-                        ++ci;
-                        best = -INFINITY;
+                for (int u = 0; u < KB; ++u) {
+                    if (u > 0) {
 #pragma unroll
                         for (int e = 0; e < PPL; ++e) {
-                            const float c2 = cc[e] * st_c[e] - ss[e] * st_s[e];
-                            const float s2 = cc[e] * st_s[e] + ss[e] * st_c[e];
-                            cc[e] = c2;
-                            ss[e] = s2;
+                            const float c2 = c[e] * stc[e] - sn[e] * sts[e];
+                            const float s2 = c[e] * sts[e] + sn[e] * stc[e];
+                            c[e] = c2;
+                            sn[e] = s2;
+                        }
+                    }
+                    const float zh = logits(k0[u], k1[u], c, sn);
+                    float gs = 0.f;
+                    if constexpr (WGS) gs = head_total<G>(zh) * (1.f / G);
+                    // every lane stores (the others into the spare words past
+                    // sS[MC]), so that the batch stays one basic block
+                    const int ci = cb + it0 + u;
+                    float *dst = (u < nb && (wz || ws)) ? (ws ? &sS[ci] : &sZ[ci * G + hsel]) : &sS[MC + lane];
+                    *dst = ws ? gs : zh;
+                }
+            }
+        } else {
+            // nref reference keys per candidate: its group score is the best
+            // over them, with that key's per-head logits
+            float st_c[PPL], st_s[PPL];
+#pragma unroll
+            for (int e = 0; e < PPL; ++e) {
+                const float2 c2 = t.rope[(D / 2) + sub * PPL + e];
+                st_c[e] = c2.x;
+                st_s[e] = c2.y;
+            }
+            const int KBR = (KB / nref) * nref;
+            const int nbatch = (cpq * nref + KBR - 1) / KBR;
+            for (int bt = 0; bt < nbatch; ++bt) {
+                const int it0 = bt * KBR;
+                const int nb = min(nitems - it0, KBR);
+                const int itl = it0 + (nb > 0 ? min(sub, nb - 1) : 0);
+                const int cl = itl / nref;
+                const int cand = max(0, min(cb + cl, m - 1));
+                const uint32_t roff = ((uint32_t)cs.id(c0 + cand) * nref + (itl - cl * nref)) * (D * 2);
+                KR k0[KB], k1[KB];
+#pragma unroll
+                for (int u = 0; u < KB; ++u) {
+                    const uint32_t o = (uint32_t)row_bcast((int)roff, u) + klane;
+                    k0[u] = bload<KR>(krs, o, 0);
+                    k1[u] = bload<KR>(krs, o + D, 0);
+                }
+                float cc[PPL], ss[PPL];
+                {
+                    const int pos = c0 + max(0, min(cb + it0 / nref, m - 1));
+                    const float2 *rp = t.rope + (int64_t)pos * (D / 2) + sub * PPL;
+#pragma unroll
+                    for (int e = 0; e < PPL; ++e) {
+                        const float2 c2 = rp[e];
+                        cc[e] = c2.x;
+                        ss[e] = c2.y;
+                    }
+                }
+                int ci = cb + it0 / nref, j = 0;
+                float best = -INFINITY, zbst = 0.f;
+#pragma unroll
+                for (int u = 0; u < KB; ++u) {
+                    if (u < nb) {
+                        const float zh = logits(k0[u], k1[u], cc, ss);
+                        const float gs = head_total<G>(zh) * (1.f / G);
+                        if (gs > best) {
+                            best = gs;
+                            zbst = zh;
+                        }
+                        if (++j == nref) {
+                            if (sub == 1) sS[ci] = best;
+                            else if (wz) sZ[ci * G + hsel] = zbst;
+                            j = 0;
+                            ++ci;
+                            best = -INFINITY;
+#pragma unroll
+                            for (int e = 0; e < PPL; ++e) {
+                                const float c2 = cc[e] * st_c[e] - ss[e] * st_s[e];
+                                const float s2 = cc[e] * st_s[e] + ss[e] * st_c[e];
+                                cc[e] = c2;
+                                ss[e] = s2;
+                            }
                         }
                     }
                 }
@@ -254,7 +399,9 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 
     // ---- softmax update over candidates [0, m) of sZ; kept ones (bit jj of
     // `kept` for candidate lane + 64 jj) drop out: new running max, rescale,
-    // probabilities back into sZ, partial denominators
+    // probabilities rounded to bf16 and stored in pairs of consecutive
+    // candidates (zeros up to the next multiple of VB), partial denominators
+    // of the rounded values
     auto softmax_step = [&](int m, uint32_t kept) __attribute__((always_inline)) {
         float mx[G];
 #pragma unroll
@@ -275,16 +422,17 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 #pragma unroll
             for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
         }
-        for (int jj = 0; jj * 64 < m; ++jj) {
+        const int mp = (m + VB - 1) / VB * VB;
+        for (int jj = 0; jj * 64 < mp; ++jj) {
             const int c = jj * 64 + lane;
-            if (c < m) {
-                const bool use = !((kept >> jj) & 1u);
+            const bool use = c < m && !((kept >> jj) & 1u);
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float p = use ? __expf(sZ[c * G + h] - M[h]) : 0.f;
-                    sZ[c * G + h] = p;
-                    lt[h] += p;
-                }
+            for (int h = 0; h < G; ++h) {
+                const float p = use ? __expf(sZ[c * G + h] - M[h]) : 0.f;
+                const uint32_t pb = f2bf(p);
+                lt[h] += bf2f(pb);
+                const uint32_t po = (uint32_t)dppi<0xB1>((int)pb);   // candidate c ^ 1
+                if (!(lane & 1) && c < mp) sP[(c >> 1) * G + h] = pb | (po << 16);
             }
         }
         wave_sync();
@@ -292,30 +440,66 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 
     // ---- p * v over candidates [0, m) (values at vb + id * D): the whole
     // wave takes one row per load (lane l holds elements l*DPL ..), VB rows
-    // per batch, row ids derived by lanes 0..VB-1 and handed out by readlane
+    // per batch, row ids derived by lanes 0..VB-1 and handed out by readlane;
+    // two rows at a time go through bf16 dot products with the probability
+    // pairs (rows past m have probability 0)
     auto fold = [&](const Cands &cs, const T *vb, int c0, int m) __attribute__((always_inline)) {
-        for (int r0 = 0; r0 < m; r0 += VB) {
+        const __amdgpu_buffer_rsrc_t vrs = rsrc(vb, 0xffffffffu);
+        const uint32_t vlane = lane * DPL * 2;
+        auto issue = [&](int r0, VR (&vr)[VB]) __attribute__((always_inline)) {
             const int nb = min(m - r0, VB);
-            const int rl = (int)cs.id(c0 + r0 + min(lane & (VB - 1), nb - 1));
-            VR vr[VB];
+            const uint32_t rl = (uint32_t)cs.id(c0 + r0 + min(lane & (VB - 1), nb - 1)) * (D * 2);
 #pragma unroll
-            for (int u = 0; u < VB; ++u) {
-                const uint32_t ru = (uint32_t)__builtin_amdgcn_readlane(rl, u);
-                vr[u] = *reinterpret_cast<const VR *>(vb + (size_t)ru * D + lane * DPL);
-            }
+            for (int u = 0; u < VB; ++u)
+                vr[u] = bload<VR>(vrs, vlane, (uint32_t)__builtin_amdgcn_readlane((int)rl, u));
+        };
+        auto consume = [&](int r0, const VR (&vr)[VB]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < VB; ++u) {
-                if (u < nb) {
-                    float v[DPL];
-                    cvt(vr[u], v);
-                    const float *pz = &sZ[(r0 + u) * G];
+            for (int u = 0; u < VB; u += 2) {
+                uint32_t pw[G];
+                const uint32_t *pp = &sP[((r0 + u) >> 1) * G];
+                if constexpr (G % 4 == 0) {
+#pragma unroll
+                    for (int h = 0; h < G; h += 4) {
+                        const uint4 x = *reinterpret_cast<const uint4 *>(pp + h);
+                        pw[h] = x.x;
+                        pw[h + 1] = x.y;
+                        pw[h + 2] = x.z;
+                        pw[h + 3] = x.w;
+                    }
+                } else if constexpr (G == 2) {
+                    const uint2 x = *reinterpret_cast<const uint2 *>(pp);
+                    pw[0] = x.x;
+                    pw[1] = x.y;
+                } else {
+                    pw[0] = pp[0];
+                }
+                if constexpr (DPL == 2) {
+                    // (row u, row u+1) of element 0, then of element 1
+                    const uint32_t lo = __builtin_amdgcn_perm(vr[u + 1], vr[u], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(vr[u + 1], vr[u], 0x07060302u);
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float p = pz[h];
-#pragma unroll
-                        for (int e = 0; e < DPL; ++e) acc[h][e] += p * v[e];
+                        acc[h][0] = dot2bf(lo, pw[h], acc[h][0]);
+                        acc[h][1] = dot2bf(hi, pw[h], acc[h][1]);
                     }
+                } else {
+                    const uint32_t pr = (uint32_t)vr[u] | ((uint32_t)vr[u + 1] << 16);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[h][0] = dot2bf(pr, pw[h], acc[h][0]);
                 }
+            }
+        };
+        // two register sets: the next batch's gathers in flight while the
+        // current one is folded
+        VR va[VB], vbb[VB];
+        if (m > 0) issue(0, va);
+        for (int r0 = 0; r0 < m; r0 += 2 * VB) {
+            if (r0 + VB < m) issue(r0 + VB, vbb);
+            consume(r0, va);
+            if (r0 + VB < m) {
+                if (r0 + 2 * VB < m) issue(r0 + 2 * VB, va);
+                consume(r0 + VB, vbb);
             }
         }
         wave_sync();
@@ -350,7 +534,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                 }
                 wave_sync();
             } else {
-                score(cs, kb, R, 0, m, m);
+                score(std::true_type{}, cs, kb, R, 0, m, m);
             }
             // selection (score desc, then lower index): the lane holds
             // candidates lane + 64 jj
@@ -437,7 +621,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
         for (int c0 = 0; c0 < m0; c0 += MC) {
             const int mc = min(MC, m0 - c0);
-            score(cs, kc, 1, c0, mc, qpos);
+            score(std::false_type{}, cs, kc, 1, c0, mc, qpos);
             softmax_step(mc, 0u);
             fold(cs, vc, c0, mc);
         }

@@ -231,7 +231,12 @@ size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *se
  *   ws, ws_bytes: device workspace of at least hti_prefill_workspace_bytes()
  * Candidate lists and prefix positions follow decode; at the token level the
  * prefix candidates are followed by the block tokens 0..t, and query t sits
- * at position (number of prefix candidates) + t.
+ * at position (number of prefix candidates) + t.  Attention weights are
+ * rounded to bf16 before they multiply values (the denominators sum the
+ * rounded weights); scores and the selection are fp32.
+ * Errors: as decode; HTI_ERR_UNSUPPORTED also for dtype other than bf16 and
+ * when one (sequence, KV head) slice of the cache or of a level's keys
+ * reaches 4 GiB.
  * Source: RecSA abstract (prefill with the same tree and shared softmax).
  */
 hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const void *q_blk,

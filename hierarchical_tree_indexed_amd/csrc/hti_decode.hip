@@ -363,27 +363,25 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             for (int e = 0; e < PPL; ++e) {
                 const float x0 = sm.qraw[h * D + sub * PPL + e];
                 const float x1 = sm.qraw[h * D + D / 2 + sub * PPL + e];
-                qa[h][e] = x0 * qcs[2 * e] - x1 * qcs[2 * e + 1];
-                qb[h][e] = x0 * qcs[2 * e + 1] + x1 * qcs[2 * e];
+                qa[h][e] = (x0 * qcs[2 * e] - x1 * qcs[2 * e + 1]) * t.scale;
+                qb[h][e] = (x0 * qcs[2 * e + 1] + x1 * qcs[2 * e]) * t.scale;
             }
         const int nref = st.nref;
+        constexpr int LPH = 16 / G;            // lanes per head after row_sums
+        const int hsel = sub / LPH;
+        const bool wz = (sub % LPH) == 0;
         const int cpq = (ms + DNQ - 1) / DNQ;
         const int c_beg = min(ms, quarter * cpq);
         const int c_end = min(ms, c_beg + cpq);
         const int nitems = (c_end - c_beg) * nref;
         const int KBR = (KB / nref) * nref;
-        float zmax[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) zmax[h] = -INFINITY;
+        float zmaxh = -INFINITY;               // of the lane's head
         float *zz = sm.z[zb];
         for (int it0 = 0; it0 < nitems; it0 += KBR) {
             const int nb = min(nitems - it0, KBR);
             if (it0 > 0) load_batch(st, s0, ms, it0, true, k0, k1, rb);
             int ci = c_beg + it0 / nref, j = 0;
-            float best = -INFINITY;
-            float zb_[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) zb_[h] = 0.f;
+            float best = -INFINITY, zbh = 0.f;
             float cc[PPL], ss[PPL];
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
@@ -398,35 +396,29 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     cvt(k1[u], x1);
                     float z[G];
 #pragma unroll
-                    for (int h = 0; h < G; ++h) z[h] = 0.f;
-#pragma unroll
                     for (int e = 0; e < PPL; ++e) {
                         const float r0 = x0[e] * cc[e] - x1[e] * ss[e];
                         const float r1 = x0[e] * ss[e] + x1[e] * cc[e];
 #pragma unroll
-                        for (int h = 0; h < G; ++h) z[h] += qa[h][e] * r0 + qb[h][e] * r1;
+                        for (int h = 0; h < G; ++h) {
+                            z[h] = (e == 0) ? qa[h][0] * r0 : fmaf(qa[h][e], r0, z[h]);
+                            z[h] = fmaf(qb[h][e], r1, z[h]);
+                        }
                     }
-                    float gs = 0.f;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        z[h] = sum16(z[h]) * t.scale;
-                        gs += z[h];
-                    }
-                    gs = gs / (float)G;
+                    // all heads' row sums at once: lane sub holds head sub / LPH
+                    const float zh = row_sums<G>(z, sub);
+                    const float gs = head_total<G>(zh) * (1.f / G);
                     if (gs > best) {
                         best = gs;
-#pragma unroll
-                        for (int h = 0; h < G; ++h) zb_[h] = z[h];
+                        zbh = zh;
                     }
                     if (++j == nref) {
                         if (sub == 0) {
                             sm.s[ci] = best;
                             sm.flag[ci] = 0;
-#pragma unroll
-                            for (int h = 0; h < G; ++h) zz[ci * G + h] = zb_[h];
                         }
-#pragma unroll
-                        for (int h = 0; h < G; ++h) zmax[h] = fmaxf(zmax[h], zb_[h]);
+                        if (wz) zz[ci * G + hsel] = zbh;
+                        zmaxh = fmaxf(zmaxh, zbh);
                         j = 0;
                         ++ci;
                         best = -INFINITY;
@@ -442,12 +434,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
         }
         if (tid < 68) sm.s[ms + tid] = -INFINITY;
-        // every lane of a quarter holds its quarter's maxima: combine the
-        // wave's four quarters
+        // lane h * LPH of each quarter holds that quarter's maximum of head
+        // h: combine the wave's four quarters
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float m4 = fmaxf(fmaxf(rlane(zmax[h], 0), rlane(zmax[h], 16)),
-                                   fmaxf(rlane(zmax[h], 32), rlane(zmax[h], 48)));
+            const float m4 = fmaxf(fmaxf(rlane(zmaxh, h * LPH), rlane(zmaxh, 16 + h * LPH)),
+                                   fmaxf(rlane(zmaxh, 32 + h * LPH), rlane(zmaxh, 48 + h * LPH)));
             if (lane == 0) sm.redz[wave][h] = m4;
         }
     };

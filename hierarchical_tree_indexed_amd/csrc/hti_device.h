@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hti {
 
 constexpr int kWave = 64;
@@ -180,6 +182,49 @@ __device__ __forceinline__ int row_bcast(int v, int n)
     default: return dppi<0x15F>(v);
     }
 }
+// Sums over the 16 lanes of a row of the G values z[0..G) at once, as a
+// transposed butterfly: at each lane bit from 3 down, the lanes with the bit
+// set keep the upper half of the values still open and swap the other half
+// with their partner.  Lane `sub` ends with the sum of value sub / (16 / G).
+template <int G>
+__device__ __forceinline__ float row_sums(const float (&z)[G], int sub)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1, 2, 4, 8}");
+    float a[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) a[h] = z[h];
+    auto half = [&](auto ctrl, int n, bool hi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < n; ++h) {
+            const float keep = hi ? a[h + n] : a[h];
+            const float send = hi ? a[h] : a[h + n];
+            a[h] = keep + dppf<decltype(ctrl)::value>(send);
+        }
+    };
+    using Mirror = std::integral_constant<int, 0x140>;      // lane i <-> 15 - i
+    using HalfMirror = std::integral_constant<int, 0x141>;  // i <-> 7 - i within each half
+    using Swap2 = std::integral_constant<int, 0x4E>;        // i <-> i ^ 2
+    if constexpr (G >= 2) half(Mirror{}, G / 2, (sub & 8) != 0);
+    else a[0] += dppf<0x140>(a[0]);
+    if constexpr (G >= 4) half(HalfMirror{}, G / 4, (sub & 4) != 0);
+    else a[0] += dppf<0x141>(a[0]);
+    if constexpr (G >= 8) half(Swap2{}, 1, (sub & 2) != 0);
+    else a[0] += dppf<0x4E>(a[0]);
+    a[0] += dppf<0xB1>(a[0]);
+    return a[0];
+}
+
+// Sum over the G values a lane group holds after row_sums (the values differ
+// across lane bits 3, 2, 1 for G = 2, 4, 8 and are equal within a group).
+template <int G>
+__device__ __forceinline__ float head_total(float v)
+{
+    if constexpr (G >= 8) v += dppf<0x4E>(v);
+    if constexpr (G >= 4) v += dppf<0x141>(v);
+    if constexpr (G >= 2) v += dppf<0x140>(v);
+    return v;
+}
+
 // wave-wide results, uniform across the wave
 __device__ __forceinline__ float wave_sum(float v)
 {

@@ -64,49 +64,6 @@ __device__ __forceinline__ void wave_best(float &v, int &i)
     i = i0;
 }
 
-// Sums over the 16 lanes of a row of the G values z[0..G) at once, as a
-// transposed butterfly: at each lane bit from 3 down, the lanes with the bit
-// set keep the upper half of the values still open and swap the other half
-// with their partner.  Lane `sub` ends with the sum of value sub / (16 / G).
-template <int G>
-__device__ __forceinline__ float row_sums(const float (&z)[G], int sub)
-{
-    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1, 2, 4, 8}");
-    float a[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) a[h] = z[h];
-    auto half = [&](auto ctrl, int n, bool hi) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < n; ++h) {
-            const float keep = hi ? a[h + n] : a[h];
-            const float send = hi ? a[h] : a[h + n];
-            a[h] = keep + dppf<decltype(ctrl)::value>(send);
-        }
-    };
-    using Mirror = std::integral_constant<int, 0x140>;      // lane i <-> 15 - i
-    using HalfMirror = std::integral_constant<int, 0x141>;  // i <-> 7 - i within each half
-    using Swap2 = std::integral_constant<int, 0x4E>;        // i <-> i ^ 2
-    if constexpr (G >= 2) half(Mirror{}, G / 2, (sub & 8) != 0);
-    else a[0] += dppf<0x140>(a[0]);
-    if constexpr (G >= 4) half(HalfMirror{}, G / 4, (sub & 4) != 0);
-    else a[0] += dppf<0x141>(a[0]);
-    if constexpr (G >= 8) half(Swap2{}, 1, (sub & 2) != 0);
-    else a[0] += dppf<0x4E>(a[0]);
-    a[0] += dppf<0xB1>(a[0]);
-    return a[0];
-}
-
-// Sum over the G values a lane group holds after row_sums (the values differ
-// across lane bits 3, 2, 1 for G = 2, 4, 8 and are equal within a group).
-template <int G>
-__device__ __forceinline__ float head_total(float v)
-{
-    if constexpr (G >= 8) v += dppf<0x4E>(v);
-    if constexpr (G >= 4) v += dppf<0x141>(v);
-    if constexpr (G >= 2) v += dppf<0x140>(v);
-    return v;
-}
-
 // Buffer resource over `base` (raw, unswizzled; reads past `bytes` return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
 {
@@ -274,9 +231,16 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         };
         if (nref == 1) {
             // every item is a candidate: no reference-key maximum.  The items
-            // of a quarter's batch sit at consecutive positions: the batch
-            // reads (cos, sin) of its first position and of one position's
-            // step, and turns the rotation on by one step per key.
+            // of a quarter's batch sit at consecutive positions p0, p0 + 1, ..:
+            // the batch reads (cos, sin) of p0 and p0 + 1 and steps on with
+            // cos((p+1)t) = 2 cos(t) cos(pt) - cos((p-1)t) (likewise sin).
+            float tc[PPL];   // 2 cos(t) of the lane's pairs
+#pragma unroll
+            for (int w = 0; w < PPL / 2; ++w) {
+                const uint4 st4 = bload<uint4>(rope_rs, RB + sub * PPL * 8 + w * 16, 0);
+                tc[2 * w] = 2.f * __uint_as_float(st4.x);
+                tc[2 * w + 1] = 2.f * __uint_as_float(st4.z);
+            }
             const int nbatch = (cpq + KB - 1) / KB;   // the same in every quarter
             for (int bt = 0; bt < nbatch; ++bt) {
                 const int it0 = bt * KB;
@@ -293,27 +257,38 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                     k1[u] = bload<KR>(krs, o + D, 0);
                 }
                 const uint32_t rbase = (uint32_t)(c0 + cb + it0) * RB + sub * PPL * 8;
-                float c[PPL], sn[PPL], stc[PPL], sts[PPL];
+                float c[PPL], sn[PPL], cq[PPL], sq[PPL];   // position p and p - 1 (or p + 1 before the first step)
 #pragma unroll
                 for (int w = 0; w < PPL / 2; ++w) {
-                    const uint4 cs4 = bload<uint4>(rope_rs, rbase + w * 16, 0);
-                    c[2 * w] = __uint_as_float(cs4.x);
-                    sn[2 * w] = __uint_as_float(cs4.y);
-                    c[2 * w + 1] = __uint_as_float(cs4.z);
-                    sn[2 * w + 1] = __uint_as_float(cs4.w);
-                    const uint4 st4 = bload<uint4>(rope_rs, RB + sub * PPL * 8 + w * 16, 0);
-                    stc[2 * w] = __uint_as_float(st4.x);
-                    sts[2 * w] = __uint_as_float(st4.y);
-                    stc[2 * w + 1] = __uint_as_float(st4.z);
-                    sts[2 * w + 1] = __uint_as_float(st4.w);
+                    const uint4 a4 = bload<uint4>(rope_rs, rbase + w * 16, 0);
+                    c[2 * w] = __uint_as_float(a4.x);
+                    sn[2 * w] = __uint_as_float(a4.y);
+                    c[2 * w + 1] = __uint_as_float(a4.z);
+                    sn[2 * w + 1] = __uint_as_float(a4.w);
+                    const uint4 b4 = bload<uint4>(rope_rs, rbase + RB + w * 16, 0);
+                    cq[2 * w] = __uint_as_float(b4.x);
+                    sq[2 * w] = __uint_as_float(b4.y);
+                    cq[2 * w + 1] = __uint_as_float(b4.z);
+                    sq[2 * w + 1] = __uint_as_float(b4.w);
                 }
 #pragma unroll
                 for (int u = 0; u < KB; ++u) {
-                    if (u > 0) {
+                    if (u == 1) {
 #pragma unroll
                         for (int e = 0; e < PPL; ++e) {
-                            const float c2 = c[e] * stc[e] - sn[e] * sts[e];
-                            const float s2 = c[e] * sts[e] + sn[e] * stc[e];
+                            const float c2 = cq[e], s2 = sq[e];
+                            cq[e] = c[e];
+                            sq[e] = sn[e];
+                            c[e] = c2;
+                            sn[e] = s2;
+                        }
+                    } else if (u > 1) {
+#pragma unroll
+                        for (int e = 0; e < PPL; ++e) {
+                            const float c2 = fmaf(tc[e], c[e], -cq[e]);
+                            const float s2 = fmaf(tc[e], sn[e], -sq[e]);
+                            cq[e] = c[e];
+                            sq[e] = sn[e];
                             c[e] = c2;
                             sn[e] = s2;
                         }

@@ -554,17 +554,17 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
             for (int h = 0; h < G; ++h)
 #pragma unroll
                 for (int e = 0; e < PPL; ++e) {
-                    qa[h][e] = sm.q[h * D + sub * PPL + e];
-                    qb[h][e] = sm.q[h * D + D / 2 + sub * PPL + e];
+                    qa[h][e] = sm.q[h * D + sub * PPL + e] * t.scale;
+                    qb[h][e] = sm.q[h * D + D / 2 + sub * PPL + e] * t.scale;
                 }
+            constexpr int LPH = 16 / G;        // lanes per head after row_sums
+            const int hsel = sub / LPH;
+            const bool wz = (sub % LPH) == 0;
             for (int it0 = 0; it0 < nitems; it0 += KBR) {
                 const int nb = min(nitems - it0, KBR);
                 if (it0 > 0) issue_keys(it0, nb);
                 int ci = c_beg + it0 / nref, j = 0;
-                float best = -INFINITY;
-                float zb[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) zb[h] = 0.f;
+                float best = -INFINITY, zbh = 0.f;
                 float cc[PPL], ss[PPL];
 #pragma unroll
                 for (int e = 0; e < PPL; ++e) {
@@ -579,32 +579,25 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
                         cvt(k1[u], x1);
                         float z[G];
 #pragma unroll
-                        for (int h = 0; h < G; ++h) z[h] = 0.f;
-#pragma unroll
                         for (int e = 0; e < PPL; ++e) {
                             const float r0 = x0[e] * cc[e] - x1[e] * ss[e];
                             const float r1 = x0[e] * ss[e] + x1[e] * cc[e];
 #pragma unroll
-                            for (int h = 0; h < G; ++h) z[h] += qa[h][e] * r0 + qb[h][e] * r1;
+                            for (int h = 0; h < G; ++h) {
+                                z[h] = (e == 0) ? qa[h][0] * r0 : fmaf(qa[h][e], r0, z[h]);
+                                z[h] = fmaf(qb[h][e], r1, z[h]);
+                            }
                         }
-                        float gs = 0.f;
-#pragma unroll
-                        for (int h = 0; h < G; ++h) {
-                            z[h] = sum16(z[h]) * t.scale;
-                            gs += z[h];
-                        }
-                        gs = gs / (float)G;
+                        // all heads' row sums at once: lane sub holds head sub / LPH
+                        const float zh = row_sums<G>(z, sub);
+                        const float gs = head_total<G>(zh) * (1.f / G);
                         if (gs > best) {
                             best = gs;
-#pragma unroll
-                            for (int h = 0; h < G; ++h) zb[h] = z[h];
+                            zbh = zh;
                         }
                         if (++j == nref) {
-                            if (sub == 0) {
-                                sm.s[ci] = best;
-#pragma unroll
-                                for (int h = 0; h < G; ++h) sm.z[ci * G + h] = zb[h];
-                            }
+                            if (sub == 0) sm.s[ci] = best;
+                            if (wz) sm.z[ci * G + hsel] = zbh;
                             j = 0;
                             ++ci;
                             best = -INFINITY;

@@ -37,33 +37,6 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// (v, i) of the best candidate over the wave, in every lane: larger v, then
-// lower i
-__device__ __forceinline__ void wave_best(float &v, int &i)
-{
-    auto take = [&](float v2, int i2) __attribute__((always_inline)) {
-        const bool t = (v2 > v) || (v2 == v && i2 < i);
-        v = t ? v2 : v;
-        i = t ? i2 : i;
-    };
-    take(dppf<0xB1>(v), dppi<0xB1>(i));
-    take(dppf<0x4E>(v), dppi<0x4E>(i));
-    take(dppf<0x141>(v), dppi<0x141>(i));
-    take(dppf<0x140>(v), dppi<0x140>(i));
-    float v0 = rlane(v, 0);
-    int i0 = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const float v2 = rlane(v, r);
-        const int i2 = __builtin_amdgcn_readlane(i, r);
-        const bool t = (v2 > v0) || (v2 == v0 && i2 < i0);
-        v0 = t ? v2 : v0;
-        i0 = t ? i2 : i0;
-    }
-    v = v0;
-    i = i0;
-}
-
 // Buffer resource over `base` (raw, unswizzled; reads past `bytes` return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
 {
@@ -404,10 +377,14 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const float p = use ? __expf(sZ[c * G + h] - M[h]) : 0.f;
-                const uint32_t pb = f2bf(p);
-                lt[h] += bf2f(pb);
-                const uint32_t po = (uint32_t)dppi<0xB1>((int)pb);   // candidate c ^ 1
-                if (!(lane & 1) && c < mp) sP[(c >> 1) * G + h] = pb | (po << 16);
+                const float po = dppf<0xB1>(p);   // candidate c ^ 1
+                // even lanes: candidates (c, c + 1) rounded to bf16 (to
+                // nearest even) as one word, and their rounded sum
+                const bf16x2_t w2 = {(__bf16)p, (__bf16)po};
+                const uint32_t w = __builtin_bit_cast(uint32_t, w2);
+                const float both = __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+                lt[h] += (lane & 1) ? 0.f : both;
+                if (!(lane & 1) && c < mp) sP[(c >> 1) * G + h] = w;
             }
         }
         wave_sync();
@@ -534,20 +511,40 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
             const int nmax = min(keff, m);
             float cum = 0.f;
             for (int r = 0; r < nmax; ++r) {
+                // the lane's best open candidate (candidates are visited in
+                // index order, so the strict > keeps the lower index on ties;
+                // kept ones and those past m hold -inf)
                 float bv = -INFINITY;
-                int bidx = 0x7fffffff;
+                int bj = 0;
 #pragma unroll
                 for (int jj = 0; jj < MJ; ++jj) {
-                    const int c = jj * 64 + lane;
-                    const bool fr = c < m && !((kept >> jj) & 1u);
-                    const bool bt = fr && (sv[jj] > bv || (sv[jj] == bv && c < bidx));
+                    const bool bt = sv[jj] > bv;
                     bv = bt ? sv[jj] : bv;
-                    bidx = bt ? c : bidx;
+                    bj = bt ? jj : bj;
                 }
-                wave_best(bv, bidx);
-                if ((bidx & 63) == lane) kept |= 1u << (bidx >> 6);
+                // the wave's best score, then the lowest candidate index that
+                // holds it
+                float gm = bv;
+                gm = fmaxf(gm, dppf<0xB1>(gm));
+                gm = fmaxf(gm, dppf<0x4E>(gm));
+                gm = fmaxf(gm, dppf<0x141>(gm));
+                gm = fmaxf(gm, dppf<0x140>(gm));
+                gm = fmaxf(fmaxf(rlane(gm, 0), rlane(gm, 16)), fmaxf(rlane(gm, 32), rlane(gm, 48)));
+                const uint64_t hit = __ballot(bv == gm);
+                int win;
+                if (__popcll(hit) == 1) {
+                    const int wl = __ffsll((unsigned long long)hit) - 1;
+                    win = __builtin_amdgcn_readlane(bj, wl) * 64 + wl;
+                } else {
+                    win = wave_min_i(bv == gm ? bj * 64 + lane : 0x7fffffff);
+                }
+                if ((win & 63) == lane) {
+                    kept |= 1u << (win >> 6);
+#pragma unroll
+                    for (int jj = 0; jj < MJ; ++jj) sv[jj] = (jj == (win >> 6)) ? -INFINITY : sv[jj];
+                }
                 if (a.mode == HTI_TOPP) {
-                    cum += __expf(bv - gmax) / den;
+                    cum += __expf(gm - gmax) / den;
                     if (cum >= a.p) break;
                 }
             }

@@ -58,7 +58,7 @@ def _check_decode(ts, w, K, V, refs, Ls, q, trees=None, upload=False, split=True
                 nex += ex
                 emax = max(emax, err)
     log(f"  {w.name} split={split}: units={w.B * q.shape[1] * w.Hkv} exempt={nex} max_err={emax:.2e}")
-    return trees, out, sel
+    return trees, out, sel, nex
 
 
 # --------------------------------------------------------------------------- build
@@ -123,11 +123,30 @@ def test_decode_parity(w):
     Ls = [w.L - 977 * i for i in range(w.B)]
     ts, K, V, refs, _ = _setup(w, Lcap=w.L, Ls=Ls)
     q = W.gen_queries(w)
-    trees, _, _ = _check_decode(ts, w, K, V, refs, Ls, q)
+    trees, _, _, _ = _check_decode(ts, w, K, V, refs, Ls, q)
     _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, split=False)
     # the same decode on the oracle's own tree (decode kernels in isolation)
     _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, upload=True)
     _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, upload=True, split=False)
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_exact_ties(split):
+    """Exactly equal scores: zero keys score 0 at every position.  With all
+    but three level-1 nodes zeroed most candidates tie; the kept sets must be
+    the oracle's (higher score, then lower index) with no exemption."""
+    w = W.DEC128K.replace(name="ties", L=32 * 32 * 4 + 70, levels=2, needles=0, Nq=2)
+    K, V = W.gen_kv(w, Lcap=w.L)
+    keep = torch.zeros(w.L, dtype=torch.bool)
+    for n in (70, 90, 100):
+        keep[n * 32:(n + 1) * 32] = True
+    K[:, :, ~keep] = 0
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, w.L, K.to(DEV), V.to(DEV), refs.to(DEV))
+    ts.tree_build([w.L] * w.B)
+    q = W.gen_queries(w)
+    _, _, _, nex = _check_decode(ts, w, K, V, refs, [w.L] * w.B, q, split=split)
+    assert nex == 0
 
 
 def test_candidate_capacity_is_enforced():
@@ -256,9 +275,11 @@ def _prefill(ts, w, T, qb, kb, vb):
     return out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
 
 
-def _check_prefill(w, P0, T, ts_list=None, queries=None):
+def _check_prefill(w, P0, T, ts_list=None, queries=None, edit_kv=None):
     w = w.replace(L=P0, T=T)
     K, V = W.gen_kv(w, Lcap=max(P0, 1))
+    if edit_kv is not None:
+        edit_kv(K, V)
     refs = W.gen_refs(w)
     ts = make_treeset(w, max(P0, 1), K.to(DEV), V.to(DEV), refs.to(DEV), T=T)
     ts.tree_build([P0] * w.B)
@@ -278,7 +299,7 @@ def _check_prefill(w, P0, T, ts_list=None, queries=None):
                 nex += ex
                 emax = max(emax, err)
     log(f"  prefill P0={P0} T={T}: exempt={nex} max_err={emax:.2e}")
-    return out
+    return out, nex
 
 
 PF = W.PREFILL.replace(name="pf_small")
@@ -307,6 +328,24 @@ def test_prefill_inblock_tiles(Hq, Hkv, d, P0, T):
     last tile, for head groups G = 4, 8, 1, 2 and head_dim 128 / 64."""
     w = PF.replace(Hq=Hq, Hkv=Hkv, d=d, levels=2)
     _check_prefill(w, P0, T)
+
+
+def test_prefill_exact_ties():
+    """Exactly equal scores: keys that are zero score 0 at every position, so
+    with all but three level-1 nodes zeroed most candidates tie.  The kept
+    sets must be those of the oracle (higher score, then lower index) with no
+    exemption, and the outputs must agree."""
+    w = PF.replace(levels=2, k=8)
+    P0 = 32 * 32 * 4 + 70
+
+    def zero_most(K, V):
+        keep = torch.zeros(P0, dtype=torch.bool)
+        for n in (70, 90, 100):
+            keep[n * 32:(n + 1) * 32] = True
+        K[:, :, :P0][:, :, ~keep] = 0
+
+    _, nex = _check_prefill(w, P0, 24, edit_kv=zero_most)
+    assert nex == 0
 
 
 def test_prefill_b24():

@@ -520,7 +520,9 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
     const int ntop = n, ncol = n * R;
     if (ncol == 0) return;
 
-    __shared__ float kr[kTopCols][D + 4];   // rotated top keys, [column][element]
+    // rotated top keys, [column][element]; the row pitch D + 1 puts the 64
+    // (column, k group) reads of one MFMA step in distinct banks
+    __shared__ float kr[kTopCols][D + 1];
     const int64_t bh = (int64_t)bi * t.Hkv + g;
     const bf16_t *kb = (const bf16_t *)t.lk[t.levels - 1] + bh * t.ncap[t.levels] * R * D;
     for (int i = tid; i < ncol * (D / 2); i += 256) {
@@ -533,22 +535,32 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
     }
 
     // A operand: lane l holds row l % 16 of the wave's tile at k = l / 16 of
-    // every 4-wide k step, i.e. elements d = 4 kk + l / 16 (the rotate-half
-    // partner d + D/2 has the same residue, so each lane rotates its own)
+    // every 4-wide k step.  Step kk < D/8 takes element d = (l / 16) * D/8 +
+    // kk of the first half, step kk + D/8 its rotate-half partner d + D/2, so
+    // each lane reads two contiguous runs of D/8 elements and rotates its own
+    // pairs.
+    constexpr int RUN = D / 8;
     const int kq = lane >> 4;
     const int row = blockIdx.x * kTopRows + wave * 16 + (lane & 15);
     const bool rvalid = row < T * G;
     const int tq = rvalid ? row / G : 0, hq = row % G;
-    const bf16_t *qp = (const bf16_t *)a.q + (((int64_t)bi * T + tq) * t.Hq + g * G + hq) * D;
-    const float2 *rq = t.rope + (int64_t)ntop * (D / 2);
+    const bf16_t *qp = (const bf16_t *)a.q + (((int64_t)bi * T + tq) * t.Hq + g * G + hq) * D + kq * RUN;
+    const float2 *rq = t.rope + (int64_t)ntop * (D / 2) + kq * RUN;
     float qa[D / 4];
 #pragma unroll
-    for (int kk = 0; kk < D / 8; ++kk) {
-        const int d = 4 * kk + kq;
-        const float x0 = bf2f(qp[d]), x1 = bf2f(qp[d + D / 2]);
-        const float2 cs = rq[d];
-        qa[kk] = rvalid ? x0 * cs.x - x1 * cs.y : 0.f;
-        qa[kk + D / 8] = rvalid ? x0 * cs.y + x1 * cs.x : 0.f;
+    for (int w8 = 0; w8 < RUN / 8; ++w8) {
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(qp + 8 * w8);
+        const uint4 v1 = *reinterpret_cast<const uint4 *>(qp + D / 2 + 8 * w8);
+        const uint32_t lo[4] = {v0.x, v0.y, v0.z, v0.w}, hi[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = 8 * w8 + i;
+            const float x0 = bf2f((i & 1) ? lo[i >> 1] >> 16 : lo[i >> 1] & 0xffffu);
+            const float x1 = bf2f((i & 1) ? hi[i >> 1] >> 16 : hi[i >> 1] & 0xffffu);
+            const float2 cs = rq[kk];
+            qa[kk] = rvalid ? x0 * cs.x - x1 * cs.y : 0.f;
+            qa[kk + RUN] = rvalid ? x0 * cs.y + x1 * cs.x : 0.f;
+        }
     }
     __syncthreads();
 
@@ -560,7 +572,7 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
-            const float bv = cvalid ? kr[col][4 * kk + kq] : 0.f;
+            const float bv = cvalid ? kr[col][(kk < RUN ? 0 : D / 2) + kq * RUN + kk % RUN] : 0.f;
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], bv, acc, 0, 0, 0);
         }
         float z[4];

@@ -196,10 +196,37 @@ def bench_prefill(args):
     ms_dense = timed(lambda: ts0.sparse_prefill(sel0, qb, kb, vb, out, ws0, lse), args.prefill_reps)
     pairs = w.T * (w.T + 1) // 2
     inblock_flop = pairs * w.Hq * 4 * w.d
+    # the block folded into the tree (tree_extend), so that decoding can
+    # follow the prefill: timed alone, each time after a rebuild of the
+    # prefix tree
+    del ts0, ws0
+    Kx = torch.zeros((w.B, w.Hkv, w.L + w.T, w.d), dtype=K.dtype, device=DEV)
+    Vx = torch.zeros_like(Kx)
+    Kx[:, :, :w.L] = K
+    Vx[:, :, :w.L] = V
+    tsx, _ = treeset(w, w.L + w.T, Kx, Vx, T=w.T)
+    kbc, vbc = kb.contiguous(), vb.contiguous()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ext = []
+    for r in range(args.prefill_warmup + args.prefill_reps):
+        tsx.tree_build([w.L] * w.B)
+        e0.record()
+        tsx.tree_extend(kbc, vbc)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= args.prefill_warmup:
+            ext.append(e0.elapsed_time(e1))
+    ms_ext = sum(ext) / len(ext)
+    # block K and V read, cache rows written, then read again by the pooling
+    # of the nodes they complete, plus those nodes' keys (x R) and values
+    row_bytes = w.B * w.T * w.Hkv * w.d * W.TORCH_DTYPE[w.dtype].itemsize
+    nodes = sum((w.L + w.T) // w.b ** l - w.L // w.b ** l for l in range(1, w.levels + 1))
+    ext_bytes = 3 * 2 * row_bytes + nodes * w.B * w.Hkv * (w.R + 1) * w.d * W.TORCH_DTYPE[w.dtype].itemsize
     res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9,
-               dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12)
+               dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12,
+               extend_ms=ms_ext, extend_gbs=ext_bytes / (ms_ext / 1e3) / 1e9)
     log(f"[prefill] {res}")
-    del K, V, ts, ws, ts0, ws0
+    del K, V, ts, ws, tsx, Kx, Vx
     torch.cuda.empty_cache()
     return res
 
@@ -314,6 +341,8 @@ def main():
         "decode_eager_ms_per_step": dec["eager_ms_per_step"] if dec else None,
         "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
         "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
+        "prefill_extend_ms": pre["extend_ms"] if pre else None,
+        "prefill_extend_gbs": pre["extend_gbs"] if pre else None,
         "roofline": ({"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": dec["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                       "kernel": "k_decode_split",

@@ -26,7 +26,7 @@ TOPK, TOPP = 0, 1
 STATUS = {0: "HTI_OK", -1: "HTI_ERR_INVALID_ARG", -2: "HTI_ERR_UNSUPPORTED",
           -3: "HTI_ERR_CAPACITY", -4: "HTI_ERR_WORKSPACE", -5: "HTI_ERR_LAUNCH"}
 
-EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append",
+EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append", "hti_tree_extend",
            "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_decode_step",
            "hti_prefill_workspace_bytes", "hti_sparse_prefill", "hti_last_error"]
 
@@ -76,6 +76,7 @@ def lib() -> C.CDLL:
             "hti_rope_init": (C.c_int, [vp, vp]),
             "hti_tree_build": (C.c_int, [vp, vp, vp]),
             "hti_tree_append": (C.c_int, [vp, vp, vp, vp]),
+            "hti_tree_extend": (C.c_int, [vp, vp, vp, i32, vp]),
             "hti_decode_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
             "hti_sparse_decode": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
             "hti_decode_step": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
@@ -171,6 +172,12 @@ class TreeSet:
 
     def tree_append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
         _check(lib().hti_tree_append(C.byref(self.c), _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+    def tree_extend(self, k_blk: torch.Tensor, v_blk: torch.Tensor, stream=None):
+        """Append a block [B, T, Hkv, d] to every sequence and build the nodes it completes."""
+        assert k_blk.shape == v_blk.shape and k_blk.dim() == 4 and k_blk.is_contiguous() and v_blk.is_contiguous()
+        _check(lib().hti_tree_extend(C.byref(self.c), _ptr(k_blk), _ptr(v_blk), int(k_blk.shape[1]),
+                                     _stream(stream)))
 
     def decode_workspace(self, sel: Select, Nq: int) -> torch.Tensor:
         """Zero-filled decode workspace for Nq queries per sequence (kept and

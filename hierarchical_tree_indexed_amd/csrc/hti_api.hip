@@ -302,6 +302,17 @@ hti_status hti_tree_append(const hti_tree *tree, const void *k_new, const void *
     return launched(launch_append(a, k_new, v_new, (hipStream_t)stream), "tree_append");
 }
 
+hti_status hti_tree_extend(const hti_tree *tree, const void *k_blk, const void *v_blk, int32_t T,
+                           void *stream)
+{
+    hti_status st = check_tree(tree, true);
+    if (st) return st;
+    if (T < 0) return fail(HTI_ERR_INVALID_ARG, "T must be >= 0");
+    if (T > 0 && (!k_blk || !v_blk)) return fail(HTI_ERR_INVALID_ARG, "k_blk/v_blk is NULL");
+    TreeArgs a = tree_args(tree);
+    return launched(launch_extend(a, k_blk, v_blk, T, (hipStream_t)stream), "tree_extend");
+}
+
 static hti_status check_traversal(const hti_tree *tree, const hti_select *sel, int32_t T,
                                   int32_t *sel_out, int32_t sel_stride)
 {

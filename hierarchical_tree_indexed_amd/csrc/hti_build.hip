@@ -49,17 +49,52 @@ hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s)
 }
 
 // Level `lvl` of every (sequence, head): 4 nodes per 256-thread block.
+// ext == 0: every full node over the first len[s] tokens.  ext > 0: only the
+// nodes that tokens len[s] .. len[s] + ext - 1 (clamped to the cache)
+// complete, len[s] still being the old length.
 template <typename T, int D, int CPL>
-__global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl)
+__global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_t ext)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t node = (int64_t)blockIdx.x * 4 + wave;
     const int64_t bh = blockIdx.y;
     const int bi = (int)(bh / t.Hkv), h = (int)(bh % t.Hkv);
-    int64_t n = t.len[bi];
-    for (int l = 0; l < lvl; ++l) n /= t.b;
-    if (node >= n) return;
+    const int64_t L = t.len[bi];
+    int64_t lo = ext > 0 ? L : 0, hi = ext > 0 ? min(L + ext, t.ncap[0]) : L;
+    for (int l = 0; l < lvl; ++l) {
+        lo /= t.b;
+        hi /= t.b;
+    }
+    const int64_t node = lo + (int64_t)blockIdx.x * 4 + wave;
+    if (node >= hi) return;
     pool_node<T, D, CPL>(t, lvl, bh, h, node, lane);
+}
+
+// Rows of a block of T tokens per sequence ([B, T, Hkv, D], the prefill
+// block layout) into the cache at len[s] .., as far as the cache holds them;
+// 16 bytes per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_extend_rows(TreeArgs t, const T *kb, const T *vb, int T_)
+{
+    constexpr int EPC = 16 / sizeof(T);                 // elements per 16-byte chunk
+    const int cpr = t.D / EPC;                          // chunks per row
+    const int64_t bh = blockIdx.y;
+    const int bi = (int)(bh / t.Hkv), h = (int)(bh % t.Hkv);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)T_ * cpr) return;
+    const int tok = (int)(i / cpr), ch = (int)(i % cpr);
+    const int64_t row = t.len[bi] + tok;
+    if (row >= t.ncap[0]) return;
+    const int64_t src = (((int64_t)bi * T_ + tok) * t.Hkv + h) * t.D + ch * EPC;
+    const int64_t dst = (bh * t.ncap[0] + row) * t.D + ch * EPC;
+    *reinterpret_cast<uint4 *>((T *)t.kc + dst) = *reinterpret_cast<const uint4 *>(kb + src);
+    *reinterpret_cast<uint4 *>((T *)t.vc + dst) = *reinterpret_cast<const uint4 *>(vb + src);
+}
+
+// len[s] += T, clamped to the cache
+__global__ void k_extend_len(int64_t *len, int B, int64_t T_, int64_t cap)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < B) len[s] = min(len[s] + T_, cap);
 }
 
 // Append one token per sequence: one block per sequence, one wave per KV head
@@ -107,28 +142,59 @@ __global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const 
 }
 
 template <typename T, int D>
-static hipError_t build_level_d(const TreeArgs &t, int lvl, int64_t max_nodes, hipStream_t s)
+static hipError_t build_level_d(const TreeArgs &t, int lvl, int64_t max_nodes, int64_t ext, hipStream_t s)
 {
     dim3 grid((unsigned)((max_nodes + 3) / 4), (unsigned)(t.B * t.Hkv));
     if (t.b <= 8)
-        hipLaunchKernelGGL((k_build_level<T, D, 2>), grid, dim3(256), 0, s, t, lvl);
+        hipLaunchKernelGGL((k_build_level<T, D, 2>), grid, dim3(256), 0, s, t, lvl, ext);
     else if (t.b <= 16)
-        hipLaunchKernelGGL((k_build_level<T, D, 4>), grid, dim3(256), 0, s, t, lvl);
+        hipLaunchKernelGGL((k_build_level<T, D, 4>), grid, dim3(256), 0, s, t, lvl, ext);
     else if (t.b <= 32)
-        hipLaunchKernelGGL((k_build_level<T, D, 8>), grid, dim3(256), 0, s, t, lvl);
+        hipLaunchKernelGGL((k_build_level<T, D, 8>), grid, dim3(256), 0, s, t, lvl, ext);
     else
-        hipLaunchKernelGGL((k_build_level<T, D, 16>), grid, dim3(256), 0, s, t, lvl);
+        hipLaunchKernelGGL((k_build_level<T, D, 16>), grid, dim3(256), 0, s, t, lvl, ext);
     return hipGetLastError();
+}
+
+static hipError_t build_level_any(const TreeArgs &t, int lvl, int64_t max_nodes, int64_t ext, hipStream_t s)
+{
+    if (max_nodes <= 0) return hipSuccess;
+    if (t.dtype == HTI_BF16)
+        return t.D == 128 ? build_level_d<bf16_t, 128>(t, lvl, max_nodes, ext, s)
+                          : build_level_d<bf16_t, 64>(t, lvl, max_nodes, ext, s);
+    return t.D == 128 ? build_level_d<float, 128>(t, lvl, max_nodes, ext, s)
+                      : build_level_d<float, 64>(t, lvl, max_nodes, ext, s);
 }
 
 hipError_t launch_build_level(const TreeArgs &t, int lvl, int64_t max_nodes, hipStream_t s)
 {
-    if (max_nodes <= 0) return hipSuccess;
+    return build_level_any(t, lvl, max_nodes, 0, s);
+}
+
+hipError_t launch_extend(const TreeArgs &t, const void *k_blk, const void *v_blk, int T_, hipStream_t s)
+{
+    if (T_ <= 0) return hipSuccess;
+    const int epc = t.dtype == HTI_BF16 ? 8 : 4;
+    const int64_t chunks = (int64_t)T_ * (t.D / epc);
+    const dim3 rgrid((unsigned)((chunks + 255) / 256), (unsigned)(t.B * t.Hkv));
     if (t.dtype == HTI_BF16)
-        return t.D == 128 ? build_level_d<bf16_t, 128>(t, lvl, max_nodes, s)
-                          : build_level_d<bf16_t, 64>(t, lvl, max_nodes, s);
-    return t.D == 128 ? build_level_d<float, 128>(t, lvl, max_nodes, s)
-                      : build_level_d<float, 64>(t, lvl, max_nodes, s);
+        hipLaunchKernelGGL(k_extend_rows<bf16_t>, rgrid, dim3(256), 0, s, t, (const bf16_t *)k_blk,
+                           (const bf16_t *)v_blk, T_);
+    else
+        hipLaunchKernelGGL(k_extend_rows<float>, rgrid, dim3(256), 0, s, t, (const float *)k_blk,
+                           (const float *)v_blk, T_);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // T tokens complete at most floor(T / b^l) + 1 nodes of level l
+    int64_t span = T_;
+    for (int l = 1; l <= t.levels; ++l) {
+        span /= t.b;
+        e = build_level_any(t, l, span + 1, T_, s);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_extend_len, dim3((unsigned)((t.B + 63) / 64)), dim3(64), 0, s, t.len, t.B,
+                       (int64_t)T_, t.ncap[0]);
+    return hipGetLastError();
 }
 
 template <typename T, int D, int MAXT>

@@ -70,6 +70,7 @@ hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t un
 hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s);
 hipError_t launch_build_level(const TreeArgs &t, int lvl, int64_t max_nodes, hipStream_t s);
 hipError_t launch_append(const TreeArgs &t, const void *k_new, const void *v_new, hipStream_t s);
+hipError_t launch_extend(const TreeArgs &t, const void *k_blk, const void *v_blk, int T, hipStream_t s);
 hipError_t launch_traverse(const TravArgs &a, bool prefill, int64_t units, hipStream_t s);
 // Prefill traversal, one wave per (query, KV group) unit; max_summary bounds
 // the candidate list of every summary level.

@@ -152,6 +152,21 @@ hti_status hti_tree_append(const hti_tree *tree, const void *k_new, const void *
                            void *stream);
 
 /*
+ * hti_tree_extend: append a block of T tokens to every sequence (rows
+ * len[s] .. len[s] + T - 1), build every node of every level that these
+ * tokens complete, then len[s] += T -- the tree that hti_tree_build over the
+ * longer prefix gives, bit for bit, so that decoding can follow a prefill
+ * block.  A sequence takes only the tokens its cache still holds (rows past
+ * Lcap are dropped and len[s] stops at Lcap; the device checks this).
+ *   k_blk, v_blk: [B, T, Hkv, d] in the cache dtype (the layout of
+ *   hti_sparse_prefill's block), un-rotated; T >= 0 (0: no-op).
+ * Source: ZHA Table VIII (all full nodes are built in prefill; maintenance
+ * amortised over full-node completions).
+ */
+hti_status hti_tree_extend(const hti_tree *tree, const void *k_blk, const void *v_blk, int32_t T,
+                           void *stream);
+
+/*
  * hti_decode_workspace_bytes: size of the workspace hti_sparse_decode uses to
  * split each (query, KV group) unit over several workgroups.
  */

@@ -121,6 +121,9 @@ def test_build_append_prefill_validation():
     Ls_ok = (C.c_int64 * 2)(10, 10)
     assert L.hti_tree_build(C.byref(t_noref), Ls_ok, None) == -1
     assert L.hti_tree_append(C.byref(t), None, 0x10, None) == -1
+    assert L.hti_tree_extend(C.byref(t), None, 0x10, 8, None) == -1
+    assert L.hti_tree_extend(C.byref(t), 0x10, 0x10, -1, None) == -1
+    assert L.hti_tree_extend(C.byref(t_noref), 0x10, 0x10, 8, None) == -1
     s = hti.make_select("topk", k=8)
     need = L.hti_prefill_workspace_bytes(C.byref(c), C.byref(s), 64)
     assert need > 0

@@ -262,6 +262,76 @@ def test_append_full_cache_is_a_no_op():
     assert ts.len.item() == 64 and torch.equal(before, ts.k_cache)
 
 
+# --------------------------------------------------------------------------- block extension
+def _extend_pair(w, P0, T, Lcap):
+    """Tree A: built over P0[s] tokens, then extended by the next T tokens of
+    each sequence as one block [B, T, Hkv, d]; tree B: built over the longer
+    prefix min(P0[s] + T, Lcap).  Returns both tree sets and the new lengths."""
+    K, V = W.gen_kv(w.replace(L=Lcap), Lcap=Lcap)
+    refs = W.gen_refs(w)
+    KA, VA = K.clone(), V.clone()
+    for s_ in range(w.B):
+        KA[s_, :, P0[s_]:] = 0
+        VA[s_, :, P0[s_]:] = 0
+    ka = torch.zeros((w.B, T, w.Hkv, w.d), dtype=K.dtype)
+    va = torch.zeros_like(ka)
+    for s_ in range(w.B):
+        n = min(T, Lcap - P0[s_])
+        ka[s_, :n] = K[s_, :, P0[s_]:P0[s_] + n].permute(1, 0, 2)
+        va[s_, :n] = V[s_, :, P0[s_]:P0[s_] + n].permute(1, 0, 2)
+    A = make_treeset(w, Lcap, KA.to(DEV), VA.to(DEV), refs.to(DEV))
+    A.tree_build(P0)
+    A.tree_extend(ka.to(DEV).contiguous(), va.to(DEV).contiguous())
+    L1 = [min(p + T, Lcap) for p in P0]
+    B_ = make_treeset(w, Lcap, K.to(DEV), V.to(DEV), refs.to(DEV))
+    B_.tree_build(L1)
+    torch.cuda.synchronize()
+    return A, B_, L1
+
+
+def _same_tree(w, A, B_, L1):
+    assert A.len.cpu().tolist() == L1
+    for s_ in range(w.B):
+        n = L1[s_]
+        assert torch.equal(A.k_cache[s_, :, :n], B_.k_cache[s_, :, :n])
+        assert torch.equal(A.v_cache[s_, :, :n], B_.v_cache[s_, :, :n])
+        for l in range(w.levels):
+            n //= w.b
+            assert torch.equal(A.lvl_k[l][s_, :, :n], B_.lvl_k[l][s_, :, :n]), (s_, l)
+            assert torch.equal(A.lvl_v[l][s_, :, :n], B_.lvl_v[l][s_, :, :n]), (s_, l)
+
+
+EXTEND_CASES = [
+    W.DEC128K.replace(name="ext_bf16_b32", B=2, Hq=8, Hkv=2, L=32 * 32 * 3 + 500, levels=3, needles=0),
+    W.TINY.replace(name="ext_f32_d64_b8", B=2, Hq=2, Hkv=2, b=8, levels=4, L=3000),
+]
+
+
+@pytest.mark.parametrize("w", EXTEND_CASES, ids=lambda w: w.name)
+def test_extend_matches_build(w):
+    """tree_extend of a T-token block (ragged lengths; the block completes
+    nodes at every level) gives the tree tree_build gives over the longer
+    prefix, bit for bit; a decode on it then matches the oracle."""
+    T = 1234
+    P0 = [w.L, w.L - 333]
+    A, B_, L1 = _extend_pair(w, P0, T, Lcap=w.L + T + 7)
+    _same_tree(w, A, B_, L1)
+    K = torch.stack([A.k_cache[s_].cpu() for s_ in range(w.B)])
+    V = torch.stack([A.v_cache[s_].cpu() for s_ in range(w.B)])
+    q = W.gen_queries(w.replace(Nq=2))
+    _check_decode(A, w.replace(Nq=2), K, V, W.gen_refs(w), L1, q)
+
+
+def test_extend_clamps_at_capacity():
+    """A block longer than the free capacity fills the cache and stops there:
+    len = Lcap, and the tree is the one built over Lcap tokens."""
+    w = EXTEND_CASES[0]
+    Lcap = w.L + 100
+    A, B_, L1 = _extend_pair(w, [w.L, Lcap - 3], 300, Lcap)
+    assert L1 == [Lcap, Lcap]
+    _same_tree(w, A, B_, L1)
+
+
 # --------------------------------------------------------------------------- prefill
 def _prefill(ts, w, T, qb, kb, vb):
     sel = select_of(w)

@@ -121,9 +121,6 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
     float *sZ = sS + MC + 64;
     int *selbuf = reinterpret_cast<int *>(sZ + (size_t)MC * G);
 
-    // query of the unit (un-rotated) into LDS
-    const T *qp = (const T *)a.q + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
-    for (int i = lane; i < G * D; i += 64) qraw[i] = bf2f(*reinterpret_cast<const uint16_t *>(qp + i));
     // node counts of the prefix tree
     int nlev[HTI_MAX_LEVELS + 1];
     {
@@ -136,6 +133,18 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         }
     }
     const int L = nlev[0];
+    // query of the unit (un-rotated) into LDS, 8 elements per lane and load;
+    // an empty prefix never reads it
+    if (L > 0) {
+        const T *qp = (const T *)a.q + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
+        for (int i = lane * 8; i < G * D; i += 64 * 8) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(qp + i);
+            *reinterpret_cast<float4 *>(qraw + i) =
+                make_float4(bf2f(v.x & 0xffffu), bf2f(v.x >> 16), bf2f(v.y & 0xffffu), bf2f(v.y >> 16));
+            *reinterpret_cast<float4 *>(qraw + i + 4) =
+                make_float4(bf2f(v.z & 0xffffu), bf2f(v.z >> 16), bf2f(v.w & 0xffffu), bf2f(v.w >> 16));
+        }
+    }
     float M[G], lt[G], acc[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {

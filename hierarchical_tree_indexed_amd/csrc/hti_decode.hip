@@ -144,12 +144,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const bool topp = a.mode == HTI_TOPP;
     uint64_t *xw = ws.words + (int64_t)unit * levels * W * kSlots;
 
-    if (tid < levels) {
-        sm.lkp[tid] = (const T *)t.lk[tid] + bh * t.ncap[tid + 1] * R * D;
-        sm.lvp[tid] = (const T *)t.lv[tid] + bh * t.ncap[tid + 1] * D;
-    }
     if (tid == 0) {
-        int n = (int)t.len[bi];
+        // the length and the launch epoch: both loads go out before either
+        // is used
+        const int64_t len0 = t.len[bi];
+        const uint32_t epoch = ws.epoch[unit];
+        int n = (int)len0;
         // decode step: this workgroup appends the new token itself (every
         // workgroup of every query of the sequence writes the same bytes) and
         // walks the tree with the new length; it counts itself as having read
@@ -167,17 +167,36 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             n = pow2 ? (n >> bs) : n / b;
             sm.n[l] = n;
         }
-        sm.tag = (ws.epoch[unit] % 0xffffeu) + 1u;
+        sm.tag = (epoch % 0xffffeu) + 1u;
         sm.nsel[0] = 0;
         sm.bad = 0;
         sm.in_last = 0;
+        // this unit's level arrays (constant indices into the argument block,
+        // so scalar loads, all issued together; entries past `levels` are
+        // never read)
+#pragma unroll
+        for (int l = 0; l < HTI_MAX_LEVELS; ++l) {
+            sm.lkp[l] = (const T *)t.lk[l] + bh * t.ncap[l + 1] * R * D;
+            sm.lvp[l] = (const T *)t.lv[l] + bh * t.ncap[l + 1] * D;
+        }
     }
     const gptr<float2> rope = to_global<float2>(t.rope);
     const gptr<T> qp = to_global<T>(a.q) + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
-    for (int i = tid; i < G * D; i += DNT) {
-        float v;
-        cvt(gload<typename Raw<T, 1>::type>(qp + i), &v);
-        sm.qraw[i] = v;
+    // the query into LDS, one 16-byte load per thread
+    constexpr int EPC = 16 / (int)sizeof(T);           // elements per 16-byte chunk
+    static_assert(G * D / EPC <= DNT, "one chunk of the query per thread");
+    if (tid < G * D / EPC) {
+        const uint4 x = gload<uint4>(qp + tid * EPC);
+        float *qd = sm.qraw + tid * EPC;
+        if constexpr (sizeof(T) == 2) {
+            cvt(make_uint2(x.x, x.y), qd);
+            cvt(make_uint2(x.z, x.w), qd + 4);
+        } else {
+            qd[0] = __uint_as_float(x.x);
+            qd[1] = __uint_as_float(x.y);
+            qd[2] = __uint_as_float(x.z);
+            qd[3] = __uint_as_float(x.w);
+        }
     }
     // angle step of each of this lane's RoPE frequencies (row 1 of the table)
     float st_c[PPL], st_s[PPL];
@@ -203,9 +222,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const T *kn = (const T *)a.k_new + bh * D, *vn = (const T *)a.v_new + bh * D;
         T *kw = (T *)t.kc + (bh * t.ncap[0] + Lold) * D;
         T *vw = (T *)t.vc + (bh * t.ncap[0] + Lold) * D;
-        for (int e = tid; e < D; e += DNT) {
-            kw[e] = kn[e];
-            vw[e] = vn[e];
+        if (tid < D / EPC) {
+            const uint4 kx = *reinterpret_cast<const uint4 *>(kn + tid * EPC);
+            const uint4 vx = *reinterpret_cast<const uint4 *>(vn + tid * EPC);
+            *reinterpret_cast<uint4 *>(kw + tid * EPC) = kx;
+            *reinterpret_cast<uint4 *>(vw + tid * EPC) = vx;
         }
         __syncthreads();
         int64_t idx = Lold + 1;

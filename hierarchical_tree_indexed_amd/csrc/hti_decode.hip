@@ -171,9 +171,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         sm.nsel[0] = 0;
         sm.bad = 0;
         sm.in_last = 0;
-        // this unit's level arrays (constant indices into the argument block,
-        // so scalar loads, all issued together; entries past `levels` are
-        // never read)
+    }
+    if (tid == 64) {
+        // this unit's level arrays, by another wave than the length's chain
+        // (constant indices into the argument block, so scalar loads, all
+        // issued together; entries past `levels` are never read)
 #pragma unroll
         for (int l = 0; l < HTI_MAX_LEVELS; ++l) {
             sm.lkp[l] = (const T *)t.lk[l] + bh * t.ncap[l + 1] * R * D;

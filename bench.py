@@ -308,8 +308,9 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the method's sequences and KV heads are independent "
-              "and this build runs on a single MI355X; --gpus must be 1", file=sys.stderr)
+        print("bench.py measures one GPU: the method's sequences and KV heads are independent, "
+              "so a multi-GPU run would shard them with no communication; --gpus must be 1",
+              file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.copy_calibration:

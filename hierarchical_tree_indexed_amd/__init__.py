@@ -44,7 +44,8 @@ class Tree(C.Structure):
 
 
 class Select(C.Structure):
-    _fields_ = [("mode", C.c_int32), ("k", C.c_int32), ("p", C.c_float), ("cap", C.c_int32)]
+    _fields_ = [("mode", C.c_int32), ("k", C.c_int32), ("p", C.c_float), ("cap", C.c_int32),
+                ("per_head", C.c_int32)]
 
 
 class PlanOut(C.Structure):
@@ -111,8 +112,11 @@ def _stream(stream=None):
     return stream.cuda_stream
 
 
-def make_select(mode: str = "topk", k: int = 8, p: float = 1.0, cap: int = 16) -> Select:
-    return Select(TOPK if mode == "topk" else TOPP, k, p, cap)
+def make_select(mode: str = "topk", k: int = 8, p: float = 1.0, cap: int = 16,
+                per_head: bool = False) -> Select:
+    """Selection rule; per_head: every query head routes on its own instead of
+    its KV group sharing one selection."""
+    return Select(TOPK if mode == "topk" else TOPP, k, p, cap, 1 if per_head else 0)
 
 
 def make_cfg(B, Hq, Hkv, d, b, levels, R, dtype, Lcap, rope_base=10000.0, rope_npos=1) -> TreeCfg:
@@ -181,8 +185,8 @@ class TreeSet:
 
     def decode_workspace(self, sel: Select, Nq: int) -> torch.Tensor:
         """Zero-filled decode workspace for Nq queries per sequence (kept and
-        reused by every decode call of that shape)."""
-        key = Nq
+        reused by every decode call of that shape and routing)."""
+        key = (Nq, int(sel.per_head))
         ws = self._dec_ws.get(key)
         if ws is None:
             n = lib().hti_decode_workspace_bytes(C.byref(self.cfg), C.byref(sel), Nq)

@@ -67,6 +67,7 @@ hti_status check_select(const hti_select *s)
     } else {
         return fail(HTI_ERR_INVALID_ARG, "unknown selection mode %d", s->mode);
     }
+    if (s->per_head != 0 && s->per_head != 1) return fail(HTI_ERR_INVALID_ARG, "per_head must be 0 or 1");
     return HTI_OK;
 }
 
@@ -139,9 +140,29 @@ TreeArgs tree_args(const hti_tree *tr)
     a.levels = c.levels;
     a.R = c.R;
     a.G = c.Hq / c.Hkv;
+    a.hdiv = 1;
     a.scale = 1.0f / sqrtf((float)c.d);
     a.dtype = c.dtype;
     return a;
+}
+
+// The tree as the traversal kernels see it: per KV group, or (per-head
+// routing) one routing head per query head, a group of one
+TreeArgs routing_args(const hti_tree *tr, const hti_select *sel)
+{
+    TreeArgs a = tree_args(tr);
+    if (sel->per_head) {
+        a.hdiv = a.G;
+        a.Hkv = a.Hq;
+        a.G = 1;
+    }
+    return a;
+}
+
+// routing heads per sequence and query heads per routing head
+int routing_heads(const hti_tree_cfg *c, const hti_select *sel)
+{
+    return sel && sel->per_head ? c->Hq : c->Hkv;
 }
 
 hti_status check_tree(const hti_tree *tr, bool need_refs)
@@ -180,7 +201,7 @@ struct PrefillWs {
 
 size_t inblock_tp(int32_t T) { return ((size_t)T + kInblockKeys - 1) / kInblockKeys * kInblockKeys; }
 
-PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
+PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T, int hu)
 {
     PrefillWs w{};
     const size_t rows = (size_t)c->B * (size_t)T;
@@ -200,7 +221,7 @@ PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T)
     w.vt = off;
     off += align256((size_t)c->B * inblock_tp(T) * c->Hkv * c->d * 2);
     w.top_s = off;
-    off += align256(rows * c->Hkv * (size_t)w.ntop * sizeof(float));
+    off += align256(rows * (size_t)hu * (size_t)w.ntop * sizeof(float));
     w.top_z = off;
     off += align256(rows * c->Hq * (size_t)w.ntop * sizeof(float));
     w.total = off;
@@ -333,10 +354,10 @@ static hti_status check_traversal(const hti_tree *tree, const hti_select *sel, i
 
 size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t Nq)
 {
-    (void)sel;
-    if (check_cfg(cfg) || Nq < 1) return 0;
-    const int64_t units = (int64_t)cfg->B * Nq * cfg->Hkv;
-    return decode_ws_bytes(cfg->B, units, HTI_DECODE_MAX_SPLIT, cfg->levels, cfg->Hq / cfg->Hkv, cfg->d);
+    if (check_cfg(cfg) || Nq < 1 || (sel && check_select(sel))) return 0;
+    const int hu = routing_heads(cfg, sel);
+    const int64_t units = (int64_t)cfg->B * Nq * hu;
+    return decode_ws_bytes(cfg->B, units, HTI_DECODE_MAX_SPLIT, cfg->levels, cfg->Hq / hu, cfg->d);
 }
 
 } // extern "C"
@@ -352,12 +373,13 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     if (st) return st;
     if (!q || !out) return fail(HTI_ERR_INVALID_ARG, "q/out is NULL");
     if (Nq < 1) return fail(HTI_ERR_INVALID_ARG, "Nq must be >= 1");
-    const int64_t units_ws = (int64_t)tree->cfg.B * Nq * tree->cfg.Hkv;
-    const int G = tree->cfg.Hq / tree->cfg.Hkv;
+    const int hu = routing_heads(&tree->cfg, sel);
+    const int64_t units_ws = (int64_t)tree->cfg.B * Nq * hu;
+    const int G = tree->cfg.Hq / hu;
     if (ws && ws_bytes < decode_ws_bytes(tree->cfg.B, units_ws, HTI_DECODE_MAX_SPLIT, tree->cfg.levels, G, tree->cfg.d))
         return fail(HTI_ERR_WORKSPACE, "decode workspace of %zu bytes is too small", ws_bytes);
     TravArgs a{};
-    a.t = tree_args(tree);
+    a.t = routing_args(tree, sel);
     a.mode = sel->mode;
     a.k = sel->k;
     a.cap = sel->cap;
@@ -386,7 +408,7 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
             a.k_new = k_new;
             a.v_new = v_new;
         } else {
-            hipError_t e = launch_append(a.t, k_new, v_new, hs);
+            hipError_t e = launch_append(tree_args(tree), k_new, v_new, hs);
             if (e != hipSuccess) return launched(e, what);
         }
     }
@@ -421,9 +443,8 @@ hti_status hti_decode_step(const hti_tree *tree, const hti_select *sel, const vo
 
 size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T)
 {
-    (void)sel;
-    if (check_cfg(cfg) || T < 0) return 0;
-    return prefill_ws(cfg, T).total;
+    if (check_cfg(cfg) || T < 0 || (sel && check_select(sel))) return 0;
+    return prefill_ws(cfg, T, routing_heads(cfg, sel)).total;
 }
 
 hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const void *q_blk,
@@ -437,10 +458,10 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     if (tree->cfg.dtype != HTI_BF16)
         return fail(HTI_ERR_UNSUPPORTED, "prefill runs on bf16 matrix cores; dtype must be bf16");
     if (!q_blk || !k_blk || !v_blk || !out) return fail(HTI_ERR_INVALID_ARG, "q/k/v/out is NULL");
-    const PrefillWs w = prefill_ws(&tree->cfg, T);
+    const PrefillWs w = prefill_ws(&tree->cfg, T, routing_heads(&tree->cfg, sel));
     if (!ws || ws_bytes < w.total)
         return fail(HTI_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
-    const int64_t units = (int64_t)tree->cfg.B * T * tree->cfg.Hkv;
+    const int64_t units = (int64_t)tree->cfg.B * T * routing_heads(&tree->cfg, sel);
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
     {
         // the traversal addresses rows by 32-bit byte offsets within one
@@ -456,7 +477,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     hipStream_t hs = (hipStream_t)stream;
 
     TravArgs ta{};
-    ta.t = tree_args(tree);
+    ta.t = routing_args(tree, sel);
     ta.mode = sel->mode;
     ta.k = sel->k;
     ta.cap = sel->cap;
@@ -470,7 +491,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     ta.part_ml = (float *)(wb + w.part_ml);
 
     PrefillArgs pa{};
-    pa.t = ta.t;
+    pa.t = ta.t;   // the routing view for the top-level scores; the block kernels take the KV heads
     pa.q = q_blk;
     pa.k = k_blk;
     pa.v = v_blk;
@@ -490,6 +511,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     e = launch_prefill_walk(ta, bounds(&tree->cfg, sel, T).max_summary, units, hs);
     if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
 
+    pa.t = tree_args(tree);
     pa.part_acc = ta.part_acc;
     pa.part_ml = ta.part_ml;
     pa.out = out;

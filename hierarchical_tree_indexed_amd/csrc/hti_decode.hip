@@ -138,7 +138,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const int64_t rest = unit / t.Hkv;
     const int qi = (int)(rest % a.Nq);
     const int bi = (int)(rest / a.Nq);
-    const int64_t bh = (int64_t)bi * t.Hkv + g;
+    const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const int b = t.b, levels = t.levels, R = t.R;
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
     const bool topp = a.mode == HTI_TOPP;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int l = 1; l <= levels; ++l) {
             if (idx % b != 0) break;
             idx /= b;
-            if (wave == 0) pool_node<T, D, 8>(t, l, bh, g, idx - 1, lane);
+            if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, idx - 1, lane);
             __syncthreads();
         }
     }

@@ -22,6 +22,10 @@ struct TreeArgs {
     const float2 *rope;                  // [rope_npos, D/2] (cos, sin)
     int rope_npos;
     int B, Hq, Hkv, D, b, levels, R, G;
+    // Traversals: Hkv routing heads per sequence, G query heads each; the
+    // tree arrays of routing head g are those of KV head g / hdiv, of
+    // Hkv / hdiv per sequence (hdiv > 1: every query head routes on its own)
+    int hdiv;
     float scale;                         // 1 / sqrt(D)
     int dtype;
 };

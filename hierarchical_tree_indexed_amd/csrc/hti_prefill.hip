@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
     // rotated top keys, [column][element]; the row pitch D + 1 puts the 64
     // (column, k group) reads of one MFMA step in distinct banks
     __shared__ float kr[kTopCols][D + 1];
-    const int64_t bh = (int64_t)bi * t.Hkv + g;
+    const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const bf16_t *kb = (const bf16_t *)t.lk[t.levels - 1] + bh * t.ncap[t.levels] * R * D;
     for (int i = tid; i < ncol * (D / 2); i += 256) {
         const int col = i / (D / 2), e = i % (D / 2);

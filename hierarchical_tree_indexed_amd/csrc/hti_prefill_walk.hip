@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
     const int g = (int)(bg % t.Hkv);
     const int bi = (int)(bg / t.Hkv);
     const int64_t uidx = ((int64_t)bi * a.Nq + qi) * t.Hkv + g;   // unit index of the outputs
-    const int64_t bh = (int64_t)bi * t.Hkv + g;
+    const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const int b = t.b, levels = t.levels, R = t.R;
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
 

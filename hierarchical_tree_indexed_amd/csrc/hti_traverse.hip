@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
     const int64_t rest = unit / t.Hkv;
     const int qi = (int)(rest % a.Nq);
     const int bi = (int)(rest / a.Nq);
-    const int64_t bh = (int64_t)bi * t.Hkv + g;
+    const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const int b = t.b, levels = t.levels, R = t.R;
     const int64_t L = t.len[bi];
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;

@@ -98,6 +98,11 @@ typedef struct {
     int32_t k;          /* top-k: nodes kept per level, 1..HTI_MAX_SELECT */
     float p;            /* top-p: probability mass, (0, 1] */
     int32_t cap;        /* top-p: largest kept set, 1..HTI_MAX_SELECT */
+    int32_t per_head;   /* 0: the G query heads of a KV group share one selection,
+                           scored by the mean of their logits; 1: every query
+                           head routes on its own (a group of one) over its KV
+                           head's tree.  sel_out and the units then count query
+                           heads instead of KV groups. */
 } hti_select;
 
 /* Sizes for a configuration (all host values). */

@@ -89,6 +89,16 @@ def test_decode_validation_before_launch():
     # top-p with p outside (0, 1]
     s_p = hti.make_select("topp", p=1.5, cap=16)
     assert L.hti_sparse_decode(C.byref(t), C.byref(s_p), 0x3000, 1, out, None, None, 0, None, 0, None) == -1
+    # routing flag other than 0 / 1
+    s_r = hti.make_select("topk", k=8)
+    s_r.per_head = 2
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s_r), 0x3000, 1, out, None, None, 0, None, 0, None) == -1
+    # per-head routing: the workspace grows with the units (query heads, not KV groups)
+    s_h = hti.make_select("topk", k=8, per_head=True)
+    assert L.hti_decode_workspace_bytes(C.byref(c), C.byref(s_h), 1) > \
+        L.hti_decode_workspace_bytes(C.byref(c), C.byref(s), 1)
+    assert L.hti_prefill_workspace_bytes(C.byref(c), C.byref(s_h), 64) >= \
+        L.hti_prefill_workspace_bytes(C.byref(c), C.byref(s), 64)
     # RoPE table too short for the reachable positions
     t2 = _tree_struct(cfg(rope_npos=100))
     assert L.hti_sparse_decode(C.byref(t2), C.byref(s), 0x3000, 1, out, None, None, 0, None, 0, None) == -3

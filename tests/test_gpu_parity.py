@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import hierarchical_tree_indexed_amd as hti
 import hti_workloads as W
 import oracle
 from gpu_helpers import accept, kmax_of, log, make_treeset, oracle_tree, select_of, tree_close
@@ -260,6 +261,104 @@ def test_append_full_cache_is_a_no_op():
     ts.tree_append(kn.contiguous(), vn.contiguous())
     torch.cuda.synchronize()
     assert ts.len.item() == 64 and torch.equal(before, ts.k_cache)
+
+
+# --------------------------------------------------------------------------- per-head routing
+def _per_head_sel(w):
+    return hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, per_head=True)
+
+
+def _check_per_head(w, trees, K, V, Ls, q, out, lse, so, t_of=None, blk=None):
+    """Each query head against the oracle as a group of one over its KV head's tree."""
+    nex, emax = 0, 0.0
+    for bi in range(w.B):
+        for qi in range(q.shape[1]):
+            for hq in range(w.Hq):
+                g = hq // w.G
+                kw = {}
+                if t_of is not None:
+                    kw = dict(t=t_of(qi), blk_k=blk[0][bi, :, g].float().numpy(),
+                              blk_v=blk[1][bi, :, g].float().numpy())
+                ex, err = accept(w, trees[(bi, g)], K[bi, g, :Ls[bi]], V[bi, g, :Ls[bi]], q[bi, qi, hq:hq + 1],
+                                 out[bi, qi, hq:hq + 1], lse[bi, qi, hq:hq + 1], so[bi, qi, hq], **kw)
+                nex += ex
+                emax = max(emax, err)
+    return nex, emax
+
+
+PER_HEAD_CASES = [
+    W.DEC128K.replace(name="ph_gqa4", B=2, L=20000, needles=0, levels=2, Nq=2),
+    W.ZHA2M.replace(name="ph_topp_r4", L=16 ** 4 + 300, levels=3, Hq=8, Hkv=2),
+]
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("w", PER_HEAD_CASES, ids=lambda w: w.name)
+def test_decode_per_head_routing(w, split):
+    """Every query head routes on its own over its KV head's tree (a group of
+    one): selections per query head and outputs against the oracle."""
+    Ls = [w.L - 977 * i for i in range(w.B)]
+    ts, K, V, refs, _ = _setup(w, Lcap=w.L, Ls=Ls)
+    q = W.gen_queries(w)
+    trees = {(bi, g): oracle_tree(w, K[bi, g], V[bi, g], refs[g], Ls[bi]) for bi in range(w.B) for g in range(w.Hkv)}
+    out = torch.empty((w.B, w.Nq, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, w.Nq, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, w.Nq, w.Hq, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_decode(_per_head_sel(w), q.to(DEV).contiguous(), out, lse, so, split=split)
+    torch.cuda.synchronize()
+    nex, emax = _check_per_head(w, trees, K, V, Ls, q, out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy())
+    log(f"  {w.name} per-head split={split}: exempt={nex} max_err={emax:.2e}")
+
+
+def test_decode_step_per_head_matches_append_then_decode():
+    """decode_step with per-head routing (every query head a unit) equals
+    tree_append followed by sparse_decode, bit for bit, over several steps."""
+    w = W.DEC128K.replace(name="ph_step", B=2, L=32 * 32 * 2 + 29, needles=0, levels=2, Nq=1)
+    Lcap = w.L + 8
+    sel = _per_head_sel(w)
+    res = []
+    for fused in (True, False):
+        ts, K, V, refs, _ = _setup(w, Lcap=Lcap, Ls=[w.L] * w.B)
+        outs = []
+        for step in range(4):
+            kn, vn = W.gen_append(w, step, device=DEV)
+            q = W.gen_queries(w, step=step + 1).to(DEV).contiguous()
+            out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+            if fused:
+                ts.decode_step(sel, kn.contiguous(), vn.contiguous(), q, out)
+            else:
+                ts.tree_append(kn.contiguous(), vn.contiguous())
+                ts.sparse_decode(sel, q, out)
+            outs.append(out.cpu())
+        torch.cuda.synchronize()
+        res.append(outs)
+    for a_, b_ in zip(*res):
+        assert torch.equal(a_, b_)
+
+
+def test_prefill_per_head_routing():
+    """A prefill block with per-head routing (the top level scored per query
+    head on the matrix cores), every query head against the oracle."""
+    w = PF.replace(levels=2, k=8, Hq=8, Hkv=2)
+    P0, T = 32 * 32 * 12 + 70, 40
+    w = w.replace(L=P0, T=T)
+    K, V = W.gen_kv(w, Lcap=P0)
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, P0, K.to(DEV), V.to(DEV), refs.to(DEV), T=T)
+    ts.tree_build([P0] * w.B)
+    qb, kb, vb = W.gen_block(w)
+    sel = _per_head_sel(w)
+    ws = torch.empty(ts.prefill_workspace_bytes(sel, T), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, T, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, T, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, T, w.Hq, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_prefill(sel, qb.to(DEV).contiguous(), kb.to(DEV).contiguous(), vb.to(DEV).contiguous(),
+                      out, ws, lse, so)
+    torch.cuda.synchronize()
+    trees = {(bi, g): oracle_tree(w, K[bi, g], V[bi, g], refs[g], P0) for bi in range(w.B) for g in range(w.Hkv)}
+    nex, emax = _check_per_head(w, trees, K, V, [P0] * w.B, qb, out.cpu().numpy(), lse.cpu().numpy(),
+                                so.cpu().numpy(), t_of=lambda t: t, blk=(kb, vb))
+    log(f"  prefill per-head: exempt={nex} max_err={emax:.2e}")
 
 
 # --------------------------------------------------------------------------- block extension

@@ -150,10 +150,33 @@ def bench_decode(args):
     total_ms = g0.elapsed_time(g1)
     del graph
     kern_ms = total_ms / S
+
+    # per-query-head routing (every query head its own selection): the same
+    # queries at the reached length, sparse_decode without the append, S
+    # calls in one graph
+    sel_ph = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, per_head=True)
+    out_ph = torch.empty_like(out)
+    for s in range(4):
+        ts.sparse_decode(sel_ph, qs[s], out_ph)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            for s in range(S):
+                ts.sparse_decode(sel_ph, qs[Wm + s], out_ph)
+    torch.cuda.synchronize()
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    ph_ms = g0.elapsed_time(g1) / S
+    del graph
     res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
                decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
                qps=w.B * S / (total_ms / 1e3),
-               gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9)
+               gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9,
+               per_head_ms=ph_ms, per_head_qps=w.B / (ph_ms / 1e3),
+               per_head_gbs=decode_unit_bytes(w, w.L + Wm + 2 * S) * w.B * w.Hq / (ph_ms / 1e3) / 1e9)
     log(f"[decode] {res}")
     del K, V, ts
     torch.cuda.empty_cache()
@@ -340,6 +363,9 @@ def main():
                    "prefill_workload": W.PREFILL.name},
         "hbm_gbs": dec["gbs"] if dec else None,
         "decode_eager_ms_per_step": dec["eager_ms_per_step"] if dec else None,
+        "decode_per_head_routing_ms": dec["per_head_ms"] if dec else None,
+        "decode_per_head_routing_qps": dec["per_head_qps"] if dec else None,
+        "decode_per_head_routing_gbs": dec["per_head_gbs"] if dec else None,
         "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
         "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
         "prefill_extend_ms": pre["extend_ms"] if pre else None,

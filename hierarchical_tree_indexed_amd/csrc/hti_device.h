@@ -225,6 +225,29 @@ __device__ __forceinline__ float head_total(float v)
     return v;
 }
 
+// Sum of v over lanes l and l ^ 16 (rows 2r and 2r+1 exchanged by one
+// v_permlane16_swap) and over lanes l and l ^ 32 (halves exchanged by one
+// v_permlane32_swap), in every lane.
+__device__ __forceinline__ float xsum16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xmax16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 // wave-wide results, uniform across the wave
 __device__ __forceinline__ float wave_sum(float v)
 {

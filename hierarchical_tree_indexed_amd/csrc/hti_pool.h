@@ -13,7 +13,8 @@
 // rg = lane / 16) x (slice sub = lane % 16); row group rg holds children rg,
 // rg + 4, ..., slice sub holds d/16 contiguous elements of each.  Dot
 // products reduce over the 16 lanes of a row group, the softmax and the
-// weighted sums over the 4 row groups.
+// weighted sums over the 4 row groups (DPP within a row, lane-swap
+// instructions across rows: no LDS round trips).
 #pragma once
 
 #include "hti_device.h"
@@ -105,20 +106,18 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) dot += r[e] * kx[c][e];
-            dot = group_sum<16>(dot) * t.scale;
+            dot = sum16(dot) * t.scale;
             a[c] = valid[c] ? dot : -INFINITY;
             mx = fmaxf(mx, a[c]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = xmax32(xmax16(mx));
         float den = 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             a[c] = valid[c] ? expf(a[c] - mx) : 0.f;
             den += a[c];
         }
-        den += __shfl_xor(den, 16, kWave);
-        den += __shfl_xor(den, 32, kWave);
+        den = xsum32(xsum16(den));
 
         // pooled key = sum_c softmax_c * k_c
         float acc[EPL];
@@ -131,10 +130,7 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
             for (int e = 0; e < EPL; ++e) acc[e] += w * kx[c][e];
         }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            acc[e] += __shfl_xor(acc[e], 16, kWave);
-            acc[e] += __shfl_xor(acc[e], 32, kWave);
-        }
+        for (int e = 0; e < EPL; ++e) acc[e] = xsum32(xsum16(acc[e]));
         if (rg == 0) {
             T *out = (T *)t.lk[lvl - 1] + (((bh * t.ncap[lvl] + node) * R + j) * D) + sub * EPL;
             store_slice<T, D>(out, acc);
@@ -153,9 +149,7 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
         }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        vs[e] += __shfl_xor(vs[e], 16, kWave);
-        vs[e] += __shfl_xor(vs[e], 32, kWave);
-        vs[e] = vs[e] / (float)b;
+        vs[e] = xsum32(xsum16(vs[e])) / (float)b;
     }
     if (rg == 0) {
         T *out = (T *)t.lv[lvl - 1] + (bh * t.ncap[lvl] + node) * D + sub * EPL;

@@ -231,11 +231,15 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             *reinterpret_cast<uint4 *>(vw + tid * EPC) = vx;
         }
         __syncthreads();
-        int64_t idx = Lold + 1;
+        // (lengths are below 2^31 here: 32-bit index arithmetic, a mask and
+        // a shift when b is a power of two)
+        uint32_t idx = (uint32_t)Lold + 1u;
+        const bool pow2 = (b & (b - 1)) == 0;
+        const int bs = __builtin_ctz((unsigned)b);
         for (int l = 1; l <= levels; ++l) {
-            if (idx % b != 0) break;
-            idx /= b;
-            if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, idx - 1, lane);
+            if (pow2 ? (idx & (uint32_t)(b - 1)) != 0u : idx % (uint32_t)b != 0u) break;
+            idx = pow2 ? idx >> bs : idx / (uint32_t)b;
+            if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, (int64_t)idx - 1, lane);
             __syncthreads();
         }
     }

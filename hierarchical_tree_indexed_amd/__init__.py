@@ -45,7 +45,7 @@ class Tree(C.Structure):
 
 class Select(C.Structure):
     _fields_ = [("mode", C.c_int32), ("k", C.c_int32), ("p", C.c_float), ("cap", C.c_int32),
-                ("per_head", C.c_int32)]
+                ("per_head", C.c_int32), ("leaf_only", C.c_int32)]
 
 
 class PlanOut(C.Structure):
@@ -113,10 +113,12 @@ def _stream(stream=None):
 
 
 def make_select(mode: str = "topk", k: int = 8, p: float = 1.0, cap: int = 16,
-                per_head: bool = False) -> Select:
+                per_head: bool = False, leaf_only: bool = False) -> Select:
     """Selection rule; per_head: every query head routes on its own instead of
-    its KV group sharing one selection."""
-    return Select(TOPK if mode == "topk" else TOPP, k, p, cap, 1 if per_head else 0)
+    its KV group sharing one selection; leaf_only: only the reached tokens are
+    attended (the summaries route but do not join the softmax)."""
+    return Select(TOPK if mode == "topk" else TOPP, k, p, cap, 1 if per_head else 0,
+                  1 if leaf_only else 0)
 
 
 def make_cfg(B, Hq, Hkv, d, b, levels, R, dtype, Lcap, rope_base=10000.0, rope_npos=1) -> TreeCfg:

@@ -68,6 +68,7 @@ hti_status check_select(const hti_select *s)
         return fail(HTI_ERR_INVALID_ARG, "unknown selection mode %d", s->mode);
     }
     if (s->per_head != 0 && s->per_head != 1) return fail(HTI_ERR_INVALID_ARG, "per_head must be 0 or 1");
+    if (s->leaf_only != 0 && s->leaf_only != 1) return fail(HTI_ERR_INVALID_ARG, "leaf_only must be 0 or 1");
     return HTI_OK;
 }
 
@@ -384,6 +385,7 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     a.k = sel->k;
     a.cap = sel->cap;
     a.p = sel->p;
+    a.leaf_only = sel->leaf_only;
     a.q = q;
     a.Nq = Nq;
     a.out = out;
@@ -482,6 +484,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     ta.k = sel->k;
     ta.cap = sel->cap;
     ta.p = sel->p;
+    ta.leaf_only = sel->leaf_only;
     ta.q = q_blk;
     ta.Nq = T;
     ta.sel = sel_out;

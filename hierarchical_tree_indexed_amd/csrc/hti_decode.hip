@@ -107,6 +107,7 @@ struct Step {
     bool take_all;       // every candidate is kept (no scoring)
     bool local;          // the level fits one slice: every workgroup scores all of it and
                          // selects on its own, without exchanging lists
+    bool tok;            // the token level
 };
 
 } // namespace
@@ -254,6 +255,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // level lvl >= 1 (parents in sm.sel[cur]) or the token level (lvl == 0)
     auto make_step = [&](int lvl, int cur) __attribute__((always_inline)) -> Step<T> {
         Step<T> st;
+        st.tok = lvl == 0;
         const bool top = (lvl == levels);
         const int nprev = top ? 0 : sm.nsel[cur];
         st.cs.selp = sm.sel[cur];
@@ -364,7 +366,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                           float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
         const bool go = !st.take_all && st.ms > 0;
         load_batch(st, st.s0, st.ms, 0, go, k0, k1, rb);
-        issue_values(st, st.fs0, st.fms, !st.take_all && st.fms > 0, vr);
+        // (the token level's values, or a summary level's when its unkept
+        // candidates are attended)
+        issue_values(st, st.fs0, st.fms, !st.take_all && st.fms > 0 && (st.tok || !a.leaf_only), vr);
         const gptr<float4> rp = (gptr<float4>)(rope + st.qpos * (D / 2) + sub * PPL);
 #pragma unroll
         for (int e = 0; e < PPL / 2; ++e) {
@@ -804,7 +808,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         cur = nxt;
         st = make_step(lvl - 1, cur);
         issue_step(st, k0, k1, rb, vr, qcs);
-        if (scored) {
+        if (scored && !a.leaf_only) {
             // this workgroup's own candidates only (a local level was scored
             // whole by every workgroup)
             const int zo = stc.local ? stc.fs0 : 0;

@@ -35,6 +35,7 @@ struct TravArgs {
     TreeArgs t;
     int mode, k, cap;
     float p;
+    int leaf_only;     // 1: summaries route but do not join the softmax
     uint32_t binv;     // ceil(2^32 / b), for division by b in index arithmetic
     const void *q;     // decode [B, Nq, Hq, D]; prefill [B, T, Hq, D]
     int Nq;            // queries per sequence (decode) or block length T (prefill)

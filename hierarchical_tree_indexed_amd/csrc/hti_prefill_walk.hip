@@ -575,7 +575,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
             int *o = a.sel + (uidx * levels + (lvl - 1)) * a.sel_stride;
             for (int r = lane; r < a.sel_stride; r += 64) o[r] = (r < nn) ? nsl[r] : -1;
         }
-        if (!take_all) {
+        if (!take_all && !a.leaf_only) {
             softmax_step(m, kept);
             fold(cs, vb, 0, m);     // ids through cs, i.e. the parents' list
         }

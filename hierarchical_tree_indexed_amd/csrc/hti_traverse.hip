@@ -617,24 +617,28 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
         __syncthreads();
 
         if (!tok) select(m, cs, nxt);
-        softmax_update(m, !tok);
+        // leaf_only: a summary level routes and is not attended
+        const bool attend = tok || !a.leaf_only;
+        if (attend) softmax_update(m, !tok);
 
         if (STAGE) {
-            rescale();
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            fold_staged(0, vfirst);
-            for (int r0 = VROWS; r0 < m; r0 += VROWS) {
-                const int nr = min(VROWS, m - r0);
+            __builtin_amdgcn_s_waitcnt(0);       // the staged values landed (attended or not)
+            if (attend) {
+                rescale();
                 __syncthreads();
-                stage_values(sref, r0, nr);
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                fold_staged(r0, nr);
+                fold_staged(0, vfirst);
+                for (int r0 = VROWS; r0 < m; r0 += VROWS) {
+                    const int nr = min(VROWS, m - r0);
+                    __syncthreads();
+                    stage_values(sref, r0, nr);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    fold_staged(r0, nr);
+                }
             }
             __syncthreads();
         } else {
-            pend_m = m;
+            pend_m = attend ? m : 0;
             pend_flags = !tok;
             pend = sref;
         }

@@ -103,6 +103,11 @@ typedef struct {
                            head routes on its own (a group of one) over its KV
                            head's tree.  sel_out and the units then count query
                            heads instead of KV groups. */
+    int32_t leaf_only;  /* 0: the unselected candidates of every level join the
+                           softmax with their summaries (RecSA); 1: only the
+                           reached tokens are attended, the summaries serve the
+                           routing alone (the leaf union the ZHA router
+                           dispatches, ZHA Figure 3 caption) */
 } hti_select;
 
 /* Sizes for a configuration (all host values). */

@@ -45,7 +45,7 @@ class _QArgs(C.Structure):
                 ("K", C.c_void_p), ("V", C.c_void_p),
                 ("lvl_k", C.c_void_p), ("lvl_v", C.c_void_p),
                 ("blk_k", C.c_void_p), ("blk_v", C.c_void_p),
-                ("q", C.c_void_p), ("replay", C.c_void_p), ("kmax", C.c_int)]
+                ("q", C.c_void_p), ("replay", C.c_void_p), ("kmax", C.c_int), ("leaf_only", C.c_int)]
 
 
 class _QOut(C.Structure):
@@ -118,7 +118,7 @@ def build_tree(K, V, refs, b: int, levels: int, bf16: bool, L: int | None = None
 
 def query(tree: Tree, K, V, q, *, mode="topk", k=8, p=1.0, cap=16, rope_base=10000.0,
           qpos: int | None = None, t: int = -1, blk_k=None, blk_v=None, replay=None,
-          kmax: int | None = None, entries: bool = False):
+          kmax: int | None = None, entries: bool = False, leaf_only: bool = False):
     """One query token (G heads of one KV group) over one tree.
 
     Decode: t = -1, query at qpos (default tree.L - 1).
@@ -153,6 +153,7 @@ def query(tree: Tree, K, V, q, *, mode="topk", k=8, p=1.0, cap=16, rope_base=100
         rp = np.ascontiguousarray(replay, dtype=np.int32).reshape(tree.levels, kmax)
     a.replay = _ptr(rp)
     a.kmax = kmax
+    a.leaf_only = 1 if leaf_only else 0
 
     L = tree.levels
     res = dict(out=np.zeros((G, d), np.float32), lse=np.zeros(G, np.float32),

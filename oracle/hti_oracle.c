@@ -184,6 +184,9 @@ typedef struct {
     const float *q;      /* [G][d] the group's query heads */
     const int *replay;   /* [levels][kmax] ascending node ids, -1 padded; or NULL */
     int kmax;
+    int leaf_only;       /* 1: only the reached tokens are attended (the leaf
+                            union the router dispatches, ZHA Figure 3 caption);
+                            0: unselected summaries join the softmax too */
 } orc_query_args;
 
 typedef struct {
@@ -372,9 +375,10 @@ int orc_query(const orc_query_args *A, orc_query_out *O)
             nsel = cnt;
         }
 
-        /* unselected candidates join the shared softmax as summaries */
+        /* unselected candidates join the shared softmax as summaries (not
+         * when only the reached tokens are dispatched) */
         long r = 0;
-        for (long i = 0; i < m; ++i) {
+        for (long i = 0; i < m && !A->leaf_only; ++i) {
             if (r < nsel && sel_pos[r] == i) { ++r; continue; }
             ent_push(&E, G, z + (size_t)i * G, A->lvl_v[l - 1] + (size_t)cand[i] * d);
             rec_entry(O, l, cand[i], i);

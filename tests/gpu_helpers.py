@@ -56,9 +56,10 @@ def oracle_tree(w, K_bh, V_bh, refs_h, L):
     return oracle.build_tree(K_bh[:L], V_bh[:L], refs_h, w.b, w.levels, bf16=(w.dtype == "bf16"), L=L)
 
 
-def accept(w, tree, K_bh, V_bh, q_g, gout, glse, gsel, *, t=-1, blk_k=None, blk_v=None):
+def accept(w, tree, K_bh, V_bh, q_g, gout, glse, gsel, *, t=-1, blk_k=None, blk_v=None, leaf_only=False):
     """Apply the acceptance rule to one (query, group). Returns (exempt, maxerr)."""
-    kw = dict(mode=w.mode, k=w.k, p=w.p, cap=w.cap, rope_base=w.rope_base, kmax=kmax_of(w))
+    kw = dict(mode=w.mode, k=w.k, p=w.p, cap=w.cap, rope_base=w.rope_base, kmax=kmax_of(w),
+              leaf_only=leaf_only)
     if t >= 0:
         kw.update(t=t, blk_k=blk_k, blk_v=blk_v)
     r = oracle.query(tree, K_bh, V_bh, q_g, **kw)

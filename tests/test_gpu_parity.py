@@ -361,6 +361,74 @@ def test_prefill_per_head_routing():
     log(f"  prefill per-head: exempt={nex} max_err={emax:.2e}")
 
 
+# --------------------------------------------------------------------------- leaf-only dispatch
+LEAF_CASES = [
+    W.DEC128K.replace(name="leaf_gqa4", B=2, L=20000, needles=0, levels=2, Nq=2),
+    W.ZHA2M.replace(name="leaf_topp_r4", L=16 ** 4 + 300, levels=3, Hq=8, Hkv=2),
+]
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("w", LEAF_CASES, ids=lambda w: w.name)
+def test_decode_leaf_only(w, split):
+    """Leaf-only dispatch: the summaries route but only the reached tokens are
+    attended; selections and outputs against the oracle's leaf-only variant."""
+    Ls = [w.L - 977 * i for i in range(w.B)]
+    ts, K, V, refs, _ = _setup(w, Lcap=w.L, Ls=Ls)
+    q = W.gen_queries(w)
+    sel = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, leaf_only=True)
+    out = torch.empty((w.B, w.Nq, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, w.Nq, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, w.Nq, w.Hkv, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_decode(sel, q.to(DEV).contiguous(), out, lse, so, split=split)
+    torch.cuda.synchronize()
+    out, lse, so = out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
+    nex, emax = 0, 0.0
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            tr = oracle_tree(w, K[bi, g], V[bi, g], refs[g], Ls[bi])
+            hs = slice(g * w.G, (g + 1) * w.G)
+            for qi in range(w.Nq):
+                ex, err = accept(w, tr, K[bi, g, :Ls[bi]], V[bi, g, :Ls[bi]], q[bi, qi, hs], out[bi, qi, hs],
+                                 lse[bi, qi, hs], so[bi, qi, g], leaf_only=True)
+                nex += ex
+                emax = max(emax, err)
+    log(f"  {w.name} leaf-only split={split}: exempt={nex} max_err={emax:.2e}")
+
+
+def test_prefill_leaf_only():
+    """A prefill block with leaf-only dispatch (the prefix summaries route,
+    the reached prefix tokens and the block are attended), against the oracle."""
+    w = PF.replace(levels=2, k=8)
+    P0, T = 32 * 32 * 12 + 70, 40
+    w = w.replace(L=P0, T=T)
+    K, V = W.gen_kv(w, Lcap=P0)
+    refs = W.gen_refs(w)
+    ts = make_treeset(w, P0, K.to(DEV), V.to(DEV), refs.to(DEV), T=T)
+    ts.tree_build([P0] * w.B)
+    qb, kb, vb = W.gen_block(w)
+    sel = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, leaf_only=True)
+    ws = torch.empty(ts.prefill_workspace_bytes(sel, T), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, T, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, T, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, T, w.Hkv, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_prefill(sel, qb.to(DEV).contiguous(), kb.to(DEV).contiguous(), vb.to(DEV).contiguous(),
+                      out, ws, lse, so)
+    torch.cuda.synchronize()
+    out, lse, so = out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
+    nex, emax = 0, 0.0
+    for g in range(w.Hkv):
+        tr = oracle_tree(w, K[0, g], V[0, g], refs[g], P0)
+        hs = slice(g * w.G, (g + 1) * w.G)
+        bk, bv = kb[0, :, g].float().numpy(), vb[0, :, g].float().numpy()
+        for t in range(T):
+            ex, err = accept(w, tr, K[0, g, :P0], V[0, g, :P0], qb[0, t, hs], out[0, t, hs], lse[0, t, hs],
+                             so[0, t, g], t=t, blk_k=bk, blk_v=bv, leaf_only=True)
+            nex += ex
+            emax = max(emax, err)
+    log(f"  prefill leaf-only: exempt={nex} max_err={emax:.2e}")
+
+
 # --------------------------------------------------------------------------- block extension
 def _extend_pair(w, P0, T, Lcap):
     """Tree A: built over P0[s] tokens, then extended by the next T tokens of

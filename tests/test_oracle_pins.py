@@ -52,12 +52,15 @@ def sel_sets(res, levels):
     return s
 
 
-def eval_f64(tree, K, V, q, sel, *, base=10000.0, t=-1, blk_k=None, blk_v=None):
-    """Shared softmax in float64 over the entry set implied by `sel`."""
+def eval_f64(tree, K, V, q, sel, *, base=10000.0, t=-1, blk_k=None, blk_v=None, leaf_only=False):
+    """Shared softmax in float64 over the entry set implied by `sel` (only the
+    reached tokens when leaf_only)."""
     L, b, lv = tree.L, tree.b, tree.levels
     cands = candidates_by_predicate(L, b, lv, sel)
     zs, vals = [], []
     for l in range(lv, 0, -1):
+        if leaf_only:
+            break
         C = cands[l]
         uns = [i for i, x in enumerate(C) if x not in sel[l]]
         if not uns:
@@ -377,6 +380,45 @@ def test_prefill_matches_f64_entry_softmax():
         out, lse = eval_f64(tr, K, V, q, sel_sets(r, lv), t=t,
                             blk_k=K[P0:].astype(np.float64), blk_v=V[P0:].astype(np.float64))
         assert np.abs(r["out"] - out).max() < 2e-5
+
+
+# --------------------------------------------------------------------------- leaf-only dispatch
+@pytest.mark.parametrize("mode", ["topk", "topp"])
+def test_leaf_only_is_softmax_over_reached_tokens(mode):
+    """Leaf-only dispatch (ZHA Figure 3 caption: the union of the reached
+    leaves is what the main attention sees): the selection is the one of the
+    shared-softmax variant, and the output is the float64 softmax over the
+    reached tokens alone (decode and prefill)."""
+    L, d, G, b, lv = 3000, 32, 4, 8, 3
+    K, V, rng = rand_kv(L + 30, d, seed=31)
+    refs = (rng.standard_normal((2, d)) / np.sqrt(d)).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, lv, bf16=False, L=L)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    kw = dict(k=3) if mode == "topk" else dict(mode="topp", p=0.7, cap=6)
+    ra = oracle.query(tr, K, V, q, **kw)
+    rl = oracle.query(tr, K, V, q, leaf_only=True, **kw)
+    assert np.array_equal(ra["sel"], rl["sel"])
+    out, lse = eval_f64(tr, K, V, q, sel_sets(rl, lv), leaf_only=True)
+    assert np.abs(rl["out"] - out).max() < 2e-5 and np.abs(rl["lse"] - lse).max() < 2e-5
+    assert not np.allclose(rl["out"], ra["out"], atol=1e-3)     # the summaries did matter
+    for t in (0, 17):
+        rl = oracle.query(tr, K, V, q, leaf_only=True, t=t, blk_k=K[L:], blk_v=V[L:], **kw)
+        out, _ = eval_f64(tr, K, V, q, sel_sets(rl, lv), t=t, leaf_only=True,
+                          blk_k=K[L:].astype(np.float64), blk_v=V[L:].astype(np.float64))
+        assert np.abs(rl["out"] - out).max() < 2e-5
+
+
+def test_leaf_only_full_keep_is_dense():
+    """Keeping every candidate reaches every token, and with the summaries out
+    of the softmax the result is textbook causal attention (P1 for the
+    leaf-only variant)."""
+    L, d, G, b, lv = 700, 16, 2, 4, 3
+    K, V, rng = rand_kv(L, d, seed=5)
+    refs = (rng.standard_normal((1, d)) / 4).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, lv, bf16=False)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    r = oracle.query(tr, K, V, q, k=256, kmax=256, leaf_only=True)
+    assert np.abs(r["out"] - dense_causal(q, K, V, L - 1)).max() < 1e-5
 
 
 # --------------------------------------------------------------------------- P10

@@ -171,12 +171,32 @@ def bench_decode(args):
     torch.cuda.synchronize()
     ph_ms = g0.elapsed_time(g1) / S
     del graph
+
+    # leaf-only dispatch (the summaries route, only the reached tokens are
+    # attended): the same queries, timed the same way
+    sel_lf = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, leaf_only=True)
+    for s in range(4):
+        ts.sparse_decode(sel_lf, qs[s], out_ph)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            for s in range(S):
+                ts.sparse_decode(sel_lf, qs[Wm + s], out_ph)
+    torch.cuda.synchronize()
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    lf_ms = g0.elapsed_time(g1) / S
+    del graph
     res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
                decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
                qps=w.B * S / (total_ms / 1e3),
                gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9,
                per_head_ms=ph_ms, per_head_qps=w.B / (ph_ms / 1e3),
-               per_head_gbs=decode_unit_bytes(w, w.L + Wm + 2 * S) * w.B * w.Hq / (ph_ms / 1e3) / 1e9)
+               per_head_gbs=decode_unit_bytes(w, w.L + Wm + 2 * S) * w.B * w.Hq / (ph_ms / 1e3) / 1e9,
+               leaf_only_ms=lf_ms, leaf_only_qps=w.B / (lf_ms / 1e3))
     log(f"[decode] {res}")
     del K, V, ts
     torch.cuda.empty_cache()
@@ -210,6 +230,13 @@ def bench_prefill(args):
         return e0.elapsed_time(e1) / reps
 
     ms = timed(run, args.prefill_reps)
+    sel_lf = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, leaf_only=True)
+
+    def run_lf():
+        ts.tree_build([w.L] * w.B)
+        ts.sparse_prefill(sel_lf, qb, kb, vb, out, ws, lse)
+
+    ms_lf = timed(run_lf, args.prefill_reps)
     # the dense part alone: the same block over an empty prefix leaves only
     # the in-block causal attention on the matrix cores (plus the rotation
     # of the block and an empty traversal)
@@ -247,7 +274,7 @@ def bench_prefill(args):
     ext_bytes = 3 * 2 * row_bytes + nodes * w.B * w.Hkv * (w.R + 1) * w.d * W.TORCH_DTYPE[w.dtype].itemsize
     res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9,
                dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12,
-               extend_ms=ms_ext, extend_gbs=ext_bytes / (ms_ext / 1e3) / 1e9)
+               extend_ms=ms_ext, extend_gbs=ext_bytes / (ms_ext / 1e3) / 1e9, leaf_only_ms=ms_lf)
     log(f"[prefill] {res}")
     del K, V, ts, ws, tsx, Kx, Vx
     torch.cuda.empty_cache()
@@ -366,6 +393,9 @@ def main():
         "decode_per_head_routing_ms": dec["per_head_ms"] if dec else None,
         "decode_per_head_routing_qps": dec["per_head_qps"] if dec else None,
         "decode_per_head_routing_gbs": dec["per_head_gbs"] if dec else None,
+        "decode_leaf_only_ms": dec["leaf_only_ms"] if dec else None,
+        "decode_leaf_only_qps": dec["leaf_only_qps"] if dec else None,
+        "prefill_leaf_only_ms_per_block": pre["leaf_only_ms"] if pre else None,
         "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
         "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
         "prefill_extend_ms": pre["extend_ms"] if pre else None,

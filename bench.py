@@ -151,6 +151,31 @@ def bench_decode(args):
     del graph
     kern_ms = total_ms / S
 
+    ph_ms = lf_ms = float("nan")
+    if not args.no_variants:
+        ph_ms, lf_ms = decode_variants(ts, w, qs, Wm, S, out, cs)
+    res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
+               decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
+               qps=w.B * S / (total_ms / 1e3),
+               gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9,
+               per_head_ms=ph_ms, per_head_qps=w.B / (ph_ms / 1e3),
+               per_head_gbs=decode_unit_bytes(w, w.L + Wm + 2 * S) * w.B * w.Hq / (ph_ms / 1e3) / 1e9,
+               leaf_only_ms=lf_ms, leaf_only_qps=w.B / (lf_ms / 1e3))
+    log(f"[decode] {res}")
+    del K, V, ts
+    torch.cuda.empty_cache()
+    return res
+
+
+def finite(x):
+    """x, or None where a timing was skipped (NaN)"""
+    return None if x != x else x
+
+
+def decode_variants(ts, w, qs, Wm, S, out, cs):
+    """Graph-timed sparse_decode per step under per-query-head routing and
+    under leaf-only dispatch (the tree as the main step left it)."""
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # per-query-head routing (every query head its own selection): the same
     # queries at the reached length, sparse_decode without the append, S
     # calls in one graph
@@ -190,17 +215,7 @@ def bench_decode(args):
     torch.cuda.synchronize()
     lf_ms = g0.elapsed_time(g1) / S
     del graph
-    res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
-               decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
-               qps=w.B * S / (total_ms / 1e3),
-               gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9,
-               per_head_ms=ph_ms, per_head_qps=w.B / (ph_ms / 1e3),
-               per_head_gbs=decode_unit_bytes(w, w.L + Wm + 2 * S) * w.B * w.Hq / (ph_ms / 1e3) / 1e9,
-               leaf_only_ms=lf_ms, leaf_only_qps=w.B / (lf_ms / 1e3))
-    log(f"[decode] {res}")
-    del K, V, ts
-    torch.cuda.empty_cache()
-    return res
+    return ph_ms, lf_ms
 
 
 def bench_prefill(args):
@@ -236,7 +251,7 @@ def bench_prefill(args):
         ts.tree_build([w.L] * w.B)
         ts.sparse_prefill(sel_lf, qb, kb, vb, out, ws, lse)
 
-    ms_lf = timed(run_lf, args.prefill_reps)
+    ms_lf = float("nan") if args.no_variants else timed(run_lf, args.prefill_reps)
     # the dense part alone: the same block over an empty prefix leaves only
     # the in-block causal attention on the matrix cores (plus the rotation
     # of the block and an empty traversal)
@@ -354,6 +369,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "all"], default="all")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the per-head-routing and leaf-only timings (profiled runs of the main step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -390,12 +407,12 @@ def main():
                    "prefill_workload": W.PREFILL.name},
         "hbm_gbs": dec["gbs"] if dec else None,
         "decode_eager_ms_per_step": dec["eager_ms_per_step"] if dec else None,
-        "decode_per_head_routing_ms": dec["per_head_ms"] if dec else None,
-        "decode_per_head_routing_qps": dec["per_head_qps"] if dec else None,
-        "decode_per_head_routing_gbs": dec["per_head_gbs"] if dec else None,
-        "decode_leaf_only_ms": dec["leaf_only_ms"] if dec else None,
-        "decode_leaf_only_qps": dec["leaf_only_qps"] if dec else None,
-        "prefill_leaf_only_ms_per_block": pre["leaf_only_ms"] if pre else None,
+        "decode_per_head_routing_ms": finite(dec["per_head_ms"]) if dec else None,
+        "decode_per_head_routing_qps": finite(dec["per_head_qps"]) if dec else None,
+        "decode_per_head_routing_gbs": finite(dec["per_head_gbs"]) if dec else None,
+        "decode_leaf_only_ms": finite(dec["leaf_only_ms"]) if dec else None,
+        "decode_leaf_only_qps": finite(dec["leaf_only_qps"]) if dec else None,
+        "prefill_leaf_only_ms_per_block": finite(pre["leaf_only_ms"]) if pre else None,
         "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
         "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
         "prefill_extend_ms": pre["extend_ms"] if pre else None,

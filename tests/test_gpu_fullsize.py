@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import hierarchical_tree_indexed_amd as hti
 import hti_workloads as W
 from gpu_helpers import accept, kmax_of, log, make_treeset, oracle_tree, select_of
 
@@ -26,10 +27,12 @@ def _host(x):
     return x.cpu()
 
 
-def _decode_full(w, units, Lcap, append_steps=0):
+def _decode_full(w, units, Lcap, append_steps=0, leaf_only=False, per_head=False):
     """Build the tree over the full context, append `append_steps` tokens,
     decode one query per sequence with the split kernel, and accept the
-    sampled units against the oracle."""
+    sampled units against the oracle (leaf_only / per_head: the selection
+    variants; per_head checks every query head of the sampled KV groups as a
+    group of one)."""
     log(f"full-size decode {w.name}: B={w.B} L={w.L} Hkv={w.Hkv} levels={w.levels} R={w.R} {w.mode}")
     K, V = W.gen_kv(w, Lcap=Lcap, device=DEV)
     q0 = W.gen_queries(w)
@@ -45,8 +48,10 @@ def _decode_full(w, units, Lcap, append_steps=0):
     q = q0                     # the query whose direction the needles copy
     out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
     lse = torch.empty((w.B, 1, w.Hq), dtype=torch.float32, device=DEV)
-    sel = torch.empty((w.B, 1, w.Hkv, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
-    ts.sparse_decode(select_of(w), q.to(DEV).contiguous(), out, lse, sel, split=True)
+    hu = w.Hq if per_head else w.Hkv
+    sel = torch.empty((w.B, 1, hu, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    rule = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, per_head=per_head, leaf_only=leaf_only)
+    ts.sparse_decode(rule, q.to(DEV).contiguous(), out, lse, sel, split=True)
     torch.cuda.synchronize()
     assert ts.len.cpu().tolist() == [L] * w.B
     out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
@@ -54,11 +59,15 @@ def _decode_full(w, units, Lcap, append_steps=0):
     for bi, g in units:
         Kh, Vh = _host(K[bi, g, :L]), _host(V[bi, g, :L])
         tree = oracle_tree(w, Kh, Vh, refs[g], L)
-        hs = slice(g * w.G, (g + 1) * w.G)
-        ex, err = accept(w, tree, Kh, Vh, q[bi, 0, hs], out[bi, 0, hs], lse[bi, 0, hs], sel[bi, 0, g])
-        log(f"  unit (seq {bi}, group {g}): exempt={ex} max_err={err:.2e}")
-        nex += ex
-        emax = max(emax, err)
+        heads = [slice(h, h + 1) for h in range(g * w.G, (g + 1) * w.G)] if per_head else \
+            [slice(g * w.G, (g + 1) * w.G)]
+        for hs in heads:
+            srow = sel[bi, 0, hs.start] if per_head else sel[bi, 0, g]
+            ex, err = accept(w, tree, Kh, Vh, q[bi, 0, hs], out[bi, 0, hs], lse[bi, 0, hs], srow,
+                             leaf_only=leaf_only)
+            nex += ex
+            emax = max(emax, err)
+        log(f"  unit (seq {bi}, group {g}): exempt so far {nex}, max_err {emax:.2e}")
     assert np.isfinite(out).all()
     return nex, emax
 
@@ -76,6 +85,15 @@ def test_decode_1m_batch4_sampled():
     groups."""
     w = W.DEC1M
     _decode_full(w, [(0, 0), (1, 5), (2, 2), (3, 7)], Lcap=w.L + 4, append_steps=1)
+
+
+def test_decode_1m_batch4_variants_sampled():
+    """The 1M-token decode at batch 4 under leaf-only dispatch and under
+    per-query-head routing; sampled units (every query head of them for the
+    per-head run) against the oracle's variants."""
+    w = W.DEC1M
+    _decode_full(w, [(1, 3), (3, 6)], Lcap=w.L, leaf_only=True)
+    _decode_full(w, [(0, 2), (2, 7)], Lcap=w.L, per_head=True)
 
 
 def test_decode_zha_2m_topp_sampled():

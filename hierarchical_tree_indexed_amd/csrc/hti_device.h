@@ -93,23 +93,6 @@ template <> struct VecLoad<bf16_t, 8> {
 template <typename T, int N>
 __device__ __forceinline__ void load_vec(const T *p, float *o) { VecLoad<T, N>::run(p, o); }
 
-// Butterfly reductions over groups of `W` lanes (W a power of two <= 64);
-// every lane of the group ends with the result.
-template <int W>
-__device__ __forceinline__ float group_sum(float v)
-{
-#pragma unroll
-    for (int off = W / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-template <int W>
-__device__ __forceinline__ float group_max(float v)
-{
-#pragma unroll
-    for (int off = W / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
-}
-
 // DPP-based reductions (no LDS round trip).  16-lane all-reduce: quad
 // permutations [1,0,3,2] and [2,3,0,1], then row half-mirror and row mirror;
 // the four 16-lane rows are combined through readlane.

@@ -327,8 +327,7 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
                 for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sc[qt][tm][i]);
             lmax *= c2;
             if (__builtin_amdgcn_ballot_w64(lmax > mrow[qt] + kLazy)) {
-                float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+                const float tmax = xmax32(xmax16(lmax));
                 const float mnew = fmaxf(mrow[qt], tmax);
                 const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[qt] - mnew);
                 lacc[qt] *= alpha;
@@ -590,8 +589,7 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
                 for (int h = 0; h < (G <= 4 ? G : 1); ++h) sgrp += z[u * G + h];
             } else {
                 const float own = (z[0] + z[1]) + (z[2] + z[3]);
-                const float oth = __shfl_xor(own, 16);
-                sgrp = (kq & 1) ? oth + own : own + oth;
+                sgrp = xsum16(own);   // the same sum, in the same order, in both lanes
             }
             sgrp = sgrp / (float)G;
             float best = cvalid ? sgrp : -INFINITY;

@@ -45,7 +45,8 @@ class _QArgs(C.Structure):
                 ("K", C.c_void_p), ("V", C.c_void_p),
                 ("lvl_k", C.c_void_p), ("lvl_v", C.c_void_p),
                 ("blk_k", C.c_void_p), ("blk_v", C.c_void_p),
-                ("q", C.c_void_p), ("replay", C.c_void_p), ("kmax", C.c_int), ("leaf_only", C.c_int)]
+                ("q", C.c_void_p), ("replay", C.c_void_p), ("kmax", C.c_int), ("leaf_only", C.c_int),
+                ("router_fp8", C.c_int)]
 
 
 class _QOut(C.Structure):
@@ -67,6 +68,8 @@ def _load():
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         lib.orc_query.restype = C.c_int
         lib.orc_query.argtypes = [C.POINTER(_QArgs), C.POINTER(_QOut)]
+        lib.orc_router_fp8.restype = None
+        lib.orc_router_fp8.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
         _lib = lib
     return _lib
 
@@ -116,9 +119,23 @@ def build_tree(K, V, refs, b: int, levels: int, bf16: bool, L: int | None = None
     return tr
 
 
+def router_fp8(rows):
+    """E4M3 router copy of key rows [..., d]: (codes uint8 [..., d], scales fp32 [...])."""
+    rows = _f32(rows)
+    d = rows.shape[-1]
+    flat = rows.reshape(-1, d)
+    codes = np.zeros(flat.shape, np.uint8)
+    scales = np.zeros(flat.shape[0], np.float32)
+    lib = _load()
+    for i in range(flat.shape[0]):
+        lib.orc_router_fp8(_ptr(flat[i]), d, codes[i].ctypes.data, scales[i:].ctypes.data)
+    return codes.reshape(rows.shape), scales.reshape(rows.shape[:-1])
+
+
 def query(tree: Tree, K, V, q, *, mode="topk", k=8, p=1.0, cap=16, rope_base=10000.0,
           qpos: int | None = None, t: int = -1, blk_k=None, blk_v=None, replay=None,
-          kmax: int | None = None, entries: bool = False, leaf_only: bool = False):
+          kmax: int | None = None, entries: bool = False, leaf_only: bool = False,
+          router_fp8: bool = False):
     """One query token (G heads of one KV group) over one tree.
 
     Decode: t = -1, query at qpos (default tree.L - 1).
@@ -154,6 +171,7 @@ def query(tree: Tree, K, V, q, *, mode="topk", k=8, p=1.0, cap=16, rope_base=100
     a.replay = _ptr(rp)
     a.kmax = kmax
     a.leaf_only = 1 if leaf_only else 0
+    a.router_fp8 = 1 if router_fp8 else 0
 
     L = tree.levels
     res = dict(out=np.zeros((G, d), np.float32), lse=np.zeros(G, np.float32),

@@ -48,6 +48,16 @@
  *  - a level with no more candidates than the selection size is taken whole
  *    without scoring.
  *  - RoPE: rotate-half pairs (j, j + d/2), theta_j = base^(-2j/d).
+ *  - low-precision router keys [ZHA, Figure 16 caption: router operands,
+ *    reference-key cache and scoring in 4-bit floats while the KV cache and
+ *    the sparse attention stay in bf16]: 8-bit floats here (OCP E4M3, the
+ *    format the target's vector unit converts).  Each stored summary key row
+ *    (one node, one reference) is divided by a power-of-two scale
+ *    2^(e - 8), where amax = f * 2^e with f in [0.5, 1) is the row's largest
+ *    magnitude (scale 1 for an all-zero row), and every element is rounded to
+ *    the nearest E4M3 value, ties to the even code.  Every summary-level logit
+ *    (selection score and, with summaries attended, the summary's softmax
+ *    logit) comes from the dequantised row; tokens and values are untouched.
  */
 #include <math.h>
 #include <stdint.h>
@@ -75,6 +85,56 @@ static float dot_seq(const float *a, const float *b, int d)
     for (int t = 0; t < d; ++t)
         acc += a[t] * b[t];
     return acc;
+}
+
+/* OCP E4M3 magnitude of code c in 0..126 (4 exponent bits, bias 7, 3
+ * mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; code 127
+ * is NaN and never produced here). */
+static double e4m3_value(int c)
+{
+    int e = (c >> 3) & 15, m = c & 7;
+    return e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/* Code of the E4M3 value nearest to x (|x| <= 448), ties to the even code,
+ * found by trying every finite magnitude; the sign bit is x's. */
+static uint8_t e4m3_encode(float x)
+{
+    double a = fabs((double)x), bd = INFINITY;
+    int best = 0;
+    for (int c = 0; c <= 126; ++c) {
+        double dv = fabs(e4m3_value(c) - a);
+        if (dv < bd || (dv == bd && (c & 1) == 0)) {
+            bd = dv;
+            best = c;
+        }
+    }
+    return (uint8_t)((signbit(x) ? 0x80 : 0) | best);
+}
+
+/* Router copy of one key row: codes[d] and its power-of-two scale. */
+void orc_router_fp8(const float *k, int d, uint8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int t = 0; t < d; ++t)
+        if (fabsf(k[t]) > amax) amax = fabsf(k[t]);
+    int e = 8;
+    if (amax > 0.0f) frexpf(amax, &e);
+    *scale = ldexpf(1.0f, e - 8);
+    for (int t = 0; t < d; ++t)
+        codes[t] = e4m3_encode(k[t] / *scale);
+}
+
+/* The key row as the router sees it: codes times scale. */
+static void router_dequant(const float *k, int d, float *y)
+{
+    uint8_t codes[512];   /* d <= 512 */
+    float sc;
+    orc_router_fp8(k, d, codes, &sc);
+    for (int t = 0; t < d; ++t) {
+        double v = e4m3_value(codes[t] & 0x7f);
+        y[t] = (float)((codes[t] & 0x80) ? -v : v) * sc;
+    }
 }
 
 /* y = RoPE(x, pos): rotate-half, angle pos * base^(-2j/d) formed in double. */
@@ -187,6 +247,7 @@ typedef struct {
     int leaf_only;       /* 1: only the reached tokens are attended (the leaf
                             union the router dispatches, ZHA Figure 3 caption);
                             0: unselected summaries join the softmax too */
+    int router_fp8;      /* 1: summary keys are scored through their E4M3 copy */
 } orc_query_args;
 
 typedef struct {
@@ -276,6 +337,7 @@ int orc_query(const orc_query_args *A, orc_query_out *O)
 
     float *qr = (float *)malloc(sizeof(float) * (size_t)G * d);
     float *kr = (float *)malloc(sizeof(float) * (size_t)d);
+    float *kq = (float *)malloc(sizeof(float) * (size_t)d);
     float *zt = (float *)malloc(sizeof(float) * (size_t)G * (R > 0 ? R : 1));
     entry_set E = {0, 0, NULL, NULL};
     O->counts[0] = O->counts[1] = 0;
@@ -315,7 +377,12 @@ int orc_query(const orc_query_args *A, orc_query_out *O)
                 float best = -INFINITY;
                 int jbest = 0;
                 for (int j = 0; j < R; ++j) {
-                    rope(Kl + ((size_t)cand[i] * R + j) * d, d, i, A->rope_base, kr);
+                    const float *krow = Kl + ((size_t)cand[i] * R + j) * d;
+                    if (A->router_fp8) {
+                        router_dequant(krow, d, kq);
+                        krow = kq;
+                    }
+                    rope(krow, d, i, A->rope_base, kr);
                     float gsum = 0.0f;
                     for (int h = 0; h < G; ++h) {
                         zt[j * G + h] = dot_seq(qr + (size_t)h * d, kr, d) * scale;
@@ -467,6 +534,7 @@ int orc_query(const orc_query_args *A, orc_query_out *O)
     free(cand);
     free(qr);
     free(kr);
+    free(kq);
     free(zt);
     free(E.z);
     free(E.v);

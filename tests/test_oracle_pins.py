@@ -14,6 +14,9 @@ Each test names the pin it implements:
   P9 prefill with T = 1 is decode; prefill over an empty prefix is causal attention
   P10 R equal references equal R = 1; top-p with cap 1 equals top-1
   bf16 node rounding matches torch's round-to-nearest-even
+  P11 E4M3 router keys     -> torch's float8_e4m3fn cast (library routine), code
+                              values worked out by hand from the format, and a
+                              tree whose summary keys are the dequantised rows
 """
 import itertools
 import json
@@ -419,6 +422,89 @@ def test_leaf_only_full_keep_is_dense():
     q = rng.standard_normal((G, d)).astype(np.float32)
     r = oracle.query(tr, K, V, q, k=256, kmax=256, leaf_only=True)
     assert np.abs(r["out"] - dense_causal(q, K, V, L - 1)).max() < 1e-5
+
+
+# --------------------------------------------------------------------------- P11 router keys
+def _e4m3_torch(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _dequant_torch(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    v = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    return v * scales[..., None]
+
+
+def test_router_fp8_matches_torch_cast():
+    """The oracle's E4M3 encoder (nearest of all codes, ties to the even one)
+    agrees with torch's float8_e4m3fn conversion of the scaled rows, over rows
+    of every magnitude, with subnormal and zero elements; the scale is
+    2^(e - 8) for amax = f * 2^e, f in [0.5, 1)."""
+    rng = np.random.default_rng(41)
+    rows = [rng.standard_normal(128) * 10.0 ** rng.uniform(-6, 6) for _ in range(300)]
+    x = rng.standard_normal(64)
+    x[::3] *= 1e-4       # elements far below the row maximum: subnormal codes and zeros
+    rows.append(x)
+    rows.append(np.zeros(128))
+    z = np.zeros(128)
+    z[5] = -0.0
+    z[7] = 3.0
+    rows.append(z)
+    for r in rows:
+        r = r.astype(np.float32)
+        codes, sc = oracle.router_fp8(r)
+        sc = float(sc)
+        amax = float(np.abs(r).max())
+        if amax == 0.0:
+            assert sc == 1.0
+        else:
+            m, e = np.frexp(amax)
+            assert sc == 2.0 ** (int(e) - 8) and 128.0 <= amax / sc < 256.0
+        assert np.array_equal(codes, _e4m3_torch(r / np.float32(sc)))
+
+
+def test_router_fp8_codes_by_hand():
+    """Codes worked out from the E4M3 definition (bias 7, 3 mantissa bits,
+    subnormals m/8 * 2^-6): with the row maximum 200 the scale is 1, and
+    1.0625 (halfway 1 | 1.125) -> 1.0 = 0x38, 1.1875 (1.125 | 1.25) -> 1.25 =
+    0x3A, 2^-9 -> 0x01, 2^-10 (0 | 2^-9) -> 0x00, 3 * 2^-10 (2^-9 | 2^-8) ->
+    0x02, -0.0 -> 0x80, 240 -> 0x77, 248 (240 | 256) -> 256 = 0x78, and 200
+    (halfway 192 | 208) -> 192 = 0x74 (exponent field 14, mantissa 4), with
+    the sign bit 0xF4 for -200."""
+    vals = [200.0, 1.0625, 1.1875, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, -0.0, 240.0, 248.0, -200.0]
+    want = [0x74, 0x38, 0x3A, 0x01, 0x00, 0x02, 0x80, 0x77, 0x78, 0xF4]
+    codes, sc = oracle.router_fp8(np.array(vals, np.float32))
+    assert float(sc) == 1.0
+    assert [int(c) for c in codes] == want
+
+
+@pytest.mark.parametrize("R,mode", [(1, "topk"), (2, "topp")])
+def test_router_fp8_is_scoring_on_dequantised_keys(R, mode):
+    """Routing through the E4M3 copy is the plain method on a tree whose
+    summary keys are the dequantised rows (dequantised by torch): identical
+    selections and outputs, bit for bit; tokens and values are untouched.
+    The float64 shared softmax over that tree agrees, and the copy does
+    change the result (the keys are not exactly representable)."""
+    L, d, G, b, lv = 2500, 32, 4, 8, 3
+    K, V, rng = rand_kv(L + 20, d, seed=43, bf16=True)
+    refs = (rng.standard_normal((R, d)) / np.sqrt(d)).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, lv, bf16=True, L=L)
+    tq = oracle.build_tree(K, V, refs, b, lv, bf16=True, L=L)
+    for l in range(lv):
+        codes, sc = oracle.router_fp8(tr.lk[l])
+        tq.lk[l][...] = _dequant_torch(codes, sc)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    kw = dict(k=3) if mode == "topk" else dict(mode="topp", p=0.8, cap=8)
+    for t in (-1, 0, 11):
+        pf = dict(t=t, blk_k=K[L:], blk_v=V[L:]) if t >= 0 else {}
+        r8 = oracle.query(tr, K, V, q, router_fp8=True, **kw, **pf)
+        rq = oracle.query(tq, K, V, q, **kw, **pf)
+        assert np.array_equal(r8["sel"], rq["sel"])
+        assert np.array_equal(r8["out"], rq["out"]) and np.array_equal(r8["lse"], rq["lse"])
+        f64 = dict(t=t, blk_k=K[L:].astype(np.float64), blk_v=V[L:].astype(np.float64)) if t >= 0 else {}
+        out, _ = eval_f64(tq, K, V, q, sel_sets(r8, lv), **f64)
+        assert np.abs(r8["out"] - out).max() < 2e-5
+        r0 = oracle.query(tr, K, V, q, **kw, **pf)
+        assert not np.array_equal(r0["out"], r8["out"])
 
 
 # --------------------------------------------------------------------------- P10

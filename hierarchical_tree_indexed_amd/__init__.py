@@ -34,13 +34,15 @@ EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append", "ht
 class TreeCfg(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32),
                 ("b", C.c_int32), ("levels", C.c_int32), ("R", C.c_int32), ("dtype", C.c_int32),
-                ("Lcap", C.c_int64), ("rope_base", C.c_float), ("rope_npos", C.c_int32)]
+                ("Lcap", C.c_int64), ("rope_base", C.c_float), ("rope_npos", C.c_int32),
+                ("router_fp8", C.c_int32)]
 
 
 class Tree(C.Structure):
     _fields_ = [("cfg", TreeCfg), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
                 ("lvl_k", C.c_void_p * MAX_LEVELS), ("lvl_v", C.c_void_p * MAX_LEVELS),
-                ("ref_q", C.c_void_p), ("len", C.c_void_p), ("rope", C.c_void_p)]
+                ("ref_q", C.c_void_p), ("len", C.c_void_p), ("rope", C.c_void_p),
+                ("lvl_kq", C.c_void_p * MAX_LEVELS), ("lvl_ks", C.c_void_p * MAX_LEVELS)]
 
 
 class Select(C.Structure):
@@ -51,7 +53,8 @@ class Select(C.Structure):
 class PlanOut(C.Structure):
     _fields_ = [("ncap", C.c_int64 * (MAX_LEVELS + 1)), ("cache_bytes", C.c_size_t),
                 ("lvl_k_bytes", C.c_size_t * MAX_LEVELS), ("lvl_v_bytes", C.c_size_t * MAX_LEVELS),
-                ("rope_bytes", C.c_size_t), ("rope_npos_needed", C.c_int32)]
+                ("rope_bytes", C.c_size_t), ("rope_npos_needed", C.c_int32),
+                ("lvl_kq_bytes", C.c_size_t * MAX_LEVELS), ("lvl_ks_bytes", C.c_size_t * MAX_LEVELS)]
 
 
 class HTIError(RuntimeError):
@@ -121,9 +124,10 @@ def make_select(mode: str = "topk", k: int = 8, p: float = 1.0, cap: int = 16,
                   1 if leaf_only else 0)
 
 
-def make_cfg(B, Hq, Hkv, d, b, levels, R, dtype, Lcap, rope_base=10000.0, rope_npos=1) -> TreeCfg:
+def make_cfg(B, Hq, Hkv, d, b, levels, R, dtype, Lcap, rope_base=10000.0, rope_npos=1,
+             router_fp8=False) -> TreeCfg:
     return TreeCfg(B, Hq, Hkv, d, b, levels, R, F32 if dtype in ("f32", F32) else BF16,
-                   Lcap, rope_base, rope_npos)
+                   Lcap, rope_base, rope_npos, int(router_fp8))
 
 
 def plan(cfg: TreeCfg, sel: Select | None = None, T: int = 0) -> PlanOut:
@@ -153,6 +157,13 @@ class TreeSet:
             n = p.ncap[l]
             self.lvl_k.append(torch.zeros((cfg.B, cfg.Hkv, n, cfg.R, cfg.d), dtype=tdt, device=device))
             self.lvl_v.append(torch.zeros((cfg.B, cfg.Hkv, n, cfg.d), dtype=tdt, device=device))
+        # 8-bit router copies of the summary keys (E4M3 codes and row scales)
+        self.lvl_kq, self.lvl_ks = [], []
+        if cfg.router_fp8:
+            for l in range(1, cfg.levels + 1):
+                n = p.ncap[l]
+                self.lvl_kq.append(torch.zeros((cfg.B, cfg.Hkv, n, cfg.R, cfg.d), dtype=torch.uint8, device=device))
+                self.lvl_ks.append(torch.zeros((cfg.B, cfg.Hkv, n, cfg.R), dtype=torch.float32, device=device))
         self.ref_q = torch.zeros((cfg.Hkv, cfg.R, cfg.d), dtype=torch.float32, device=device)
         self.len = torch.zeros(cfg.B, dtype=torch.int64, device=device)
         self.rope = torch.zeros((cfg.rope_npos, cfg.d // 2, 2), dtype=torch.float32, device=device)
@@ -165,6 +176,8 @@ class TreeSet:
         t.k_cache, t.v_cache = _ptr(self.k_cache), _ptr(self.v_cache)
         for i, (k, v) in enumerate(zip(self.lvl_k, self.lvl_v)):
             t.lvl_k[i], t.lvl_v[i] = _ptr(k), _ptr(v)
+        for i, (kq, ks) in enumerate(zip(self.lvl_kq, self.lvl_ks)):
+            t.lvl_kq[i], t.lvl_ks[i] = _ptr(kq), _ptr(ks)
         t.ref_q, t.len, t.rope = _ptr(self.ref_q), _ptr(self.len), _ptr(self.rope)
         self.c = t
 

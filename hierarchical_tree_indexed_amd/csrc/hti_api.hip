@@ -51,6 +51,9 @@ hti_status check_cfg(const hti_tree_cfg *c)
         return fail(HTI_ERR_UNSUPPORTED, "Lcap %lld outside [0, 2^31)", (long long)c->Lcap);
     if (!(c->rope_base > 0.f)) return fail(HTI_ERR_INVALID_ARG, "rope_base must be > 0");
     if (c->rope_npos < 1) return fail(HTI_ERR_INVALID_ARG, "rope_npos must be >= 1");
+    if (c->router_fp8 != 0 && c->router_fp8 != 1) return fail(HTI_ERR_INVALID_ARG, "router_fp8 must be 0 or 1");
+    if (c->router_fp8 && c->dtype != HTI_BF16)
+        return fail(HTI_ERR_UNSUPPORTED, "8-bit router keys need bf16 caches");
     return HTI_OK;
 }
 
@@ -127,7 +130,10 @@ TreeArgs tree_args(const hti_tree *tr)
     for (int l = 0; l < HTI_MAX_LEVELS; ++l) {
         a.lk[l] = tr->lvl_k[l];
         a.lv[l] = tr->lvl_v[l];
+        a.lkq[l] = c.router_fp8 ? tr->lvl_kq[l] : nullptr;
+        a.lks[l] = c.router_fp8 ? tr->lvl_ks[l] : nullptr;
     }
+    a.rfp8 = c.router_fp8;
     caps(&c, a.ncap);
     a.refs = tr->ref_q;
     a.len = tr->len;
@@ -180,6 +186,10 @@ hti_status check_tree(const hti_tree *tr, bool need_refs)
     for (int l = 0; l < tr->cfg.levels; ++l)   // a level with no capacity is never touched
         if (ncap[l + 1] > 0 && (!tr->lvl_k[l] || !tr->lvl_v[l]))
             return fail(HTI_ERR_INVALID_ARG, "level %d buffers are NULL", l + 1);
+    if (tr->cfg.router_fp8)
+        for (int l = 0; l < tr->cfg.levels; ++l)
+            if (ncap[l + 1] > 0 && (!tr->lvl_kq[l] || !tr->lvl_ks[l]))
+                return fail(HTI_ERR_INVALID_ARG, "level %d router-key buffers are NULL", l + 1);
     if (need_refs && !tr->ref_q) return fail(HTI_ERR_INVALID_ARG, "ref_q is NULL");
     return HTI_OK;
 }
@@ -250,6 +260,10 @@ hti_status hti_plan(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T, h
     for (int l = 1; l <= cfg->levels; ++l) {
         out->lvl_k_bytes[l - 1] = bh * (size_t)out->ncap[l] * cfg->R * cfg->d * es;
         out->lvl_v_bytes[l - 1] = bh * (size_t)out->ncap[l] * cfg->d * es;
+        if (cfg->router_fp8) {
+            out->lvl_kq_bytes[l - 1] = bh * (size_t)out->ncap[l] * cfg->R * cfg->d;
+            out->lvl_ks_bytes[l - 1] = bh * (size_t)out->ncap[l] * cfg->R * sizeof(float);
+        }
     }
     out->rope_bytes = (size_t)cfg->rope_npos * cfg->d * sizeof(float);
     const Bounds bd = bounds(cfg, sel, T);

@@ -72,6 +72,8 @@ struct DSmem {
     int n[HTI_MAX_LEVELS + 1];        // nodes per level (n[0] = tokens; all < 2^31)
     const void *lkp[HTI_MAX_LEVELS];  // this unit's level keys / values
     const void *lvp[HTI_MAX_LEVELS];
+    const uint8_t *lkq[HTI_MAX_LEVELS];   // 8-bit router keys and their row scales
+    const float *lks[HTI_MAX_LEVELS];
     uint32_t tag;
     int bad;                          // a wait of this workgroup timed out
     int app;                          // decode step: the new token goes in at position lold
@@ -98,6 +100,8 @@ template <typename T>
 struct Step {
     Cands cs;
     gptr<T> kb, vb;      // key / value rows of this unit: row r at kb + (r * nref + j) * D
+    gptr<uint8_t> kq;    // summary levels with 8-bit router keys: the E4M3 rows, likewise,
+    gptr<float> ks;      // and their scales, row r * nref + j
     int nref;            // keys per row (R at summary levels, 1 at tokens)
     int m;               // candidates
     int s0, ms;          // candidates this workgroup scores (first chunk at the token level)
@@ -112,7 +116,7 @@ struct Step {
 
 } // namespace
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool F8>
 __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 {
     constexpr int PPL = D / 32;
@@ -181,6 +185,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int l = 0; l < HTI_MAX_LEVELS; ++l) {
             sm.lkp[l] = (const T *)t.lk[l] + bh * t.ncap[l + 1] * R * D;
             sm.lvp[l] = (const T *)t.lv[l] + bh * t.ncap[l + 1] * D;
+            if constexpr (F8) {
+                sm.lkq[l] = t.lkq[l] + bh * t.ncap[l + 1] * R * D;
+                sm.lks[l] = t.lks[l] + bh * t.ncap[l + 1] * R;
+            }
         }
     }
     const gptr<float2> rope = to_global<float2>(t.rope);
@@ -269,6 +277,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             st.m = top ? sm.n[lvl] : nprev * b + (sm.n[lvl] - orph0);
             st.kb = to_global<T>(sm.lkp[lvl - 1]);
             st.vb = to_global<T>(sm.lvp[lvl - 1]);
+            if constexpr (F8) {
+                st.kq = to_global<uint8_t>(sm.lkq[lvl - 1]);
+                st.ks = to_global<float>(sm.lks[lvl - 1]);
+            }
             st.nref = R;
             st.take_all = (a.mode == HTI_TOPK) ? (st.m <= a.k) : (st.m <= 1);
             const int cpw = (st.m + W - 1) / W;
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // With go == false every load reads the (always valid) RoPE table
     // instead, so that loads never sit behind a branch.
     auto load_batch = [&](const Step<T> &st, int s0, int ms, int it0, bool go, KR (&k0)[KB], KR (&k1)[KB],
-                          float (&rb)[2 * PPL]) __attribute__((always_inline)) {
+                          float (&sc)[KB], float (&rb)[2 * PPL]) __attribute__((always_inline)) {
         const int nref = st.nref;
         const int cpq = (ms + DNQ - 1) / DNQ;
         const int c_beg = min(ms, quarter * cpq);
@@ -325,13 +337,28 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int cl = itl / nref;
         const int cand = min(c_beg + cl, ms - 1);
         const uint32_t row = go ? (uint32_t)(st.cs.id(s0 + max(cand, 0)) * nref + (itl - cl * nref)) : 0u;
-        const gptr<T> kbase = go ? st.kb : to_global<T>(t.rope);
+        if (F8 && !st.tok) {
+            // E4M3 codes into the low bytes of the key registers, and the row scales
+            using K8 = typename Raw8<PPL>::type;
+            const gptr<uint8_t> k8 = go ? st.kq : to_global<uint8_t>(t.rope);
+            const gptr<float> s8 = go ? st.ks : to_global<float>(t.rope);
 #pragma unroll
-        for (int u = 0; u < KB; ++u) {
-            const uint32_t ru = (uint32_t)row_bcast((int)row, u);
-            const gptr<T> kp = kbase + (size_t)ru * D;
-            k0[u] = gload<KR>(kp + sub * PPL);
-            k1[u] = gload<KR>(kp + D / 2 + sub * PPL);
+            for (int u = 0; u < KB; ++u) {
+                const uint32_t ru = (uint32_t)row_bcast((int)row, u);
+                const gptr<uint8_t> kp = k8 + (size_t)ru * D;
+                put8(k0[u], gload<K8>(kp + sub * PPL));
+                put8(k1[u], gload<K8>(kp + D / 2 + sub * PPL));
+                sc[u] = gload<float>(s8 + ru);
+            }
+        } else {
+            const gptr<T> kbase = go ? st.kb : to_global<T>(t.rope);
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                const uint32_t ru = (uint32_t)row_bcast((int)row, u);
+                const gptr<T> kp = kbase + (size_t)ru * D;
+                k0[u] = gload<KR>(kp + sub * PPL);
+                k1[u] = gload<KR>(kp + D / 2 + sub * PPL);
+            }
         }
         const gptr<float4> rp = (gptr<float4>)(
             rope + (int64_t)max(0, s0 + min(c_beg + it0 / nref, ms - 1)) * (D / 2) + sub * PPL);
@@ -362,10 +389,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // Every load is unconditional (a step with nothing to gather reads the
     // RoPE table instead): a register that kept its old value on some path
     // would have to be copied at the loop edge, which waits for its load.
-    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&rb)[2 * PPL], VR (&vr)[VBS],
+    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&sc)[KB], float (&rb)[2 * PPL],
+                          VR (&vr)[VBS],
                           float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
         const bool go = !st.take_all && st.ms > 0;
-        load_batch(st, st.s0, st.ms, 0, go, k0, k1, rb);
+        load_batch(st, st.s0, st.ms, 0, go, k0, k1, sc, rb);
         // (the token level's values, or a summary level's when its unkept
         // candidates are attended)
         issue_values(st, st.fs0, st.fms, !st.take_all && st.fms > 0 && (st.tok || !a.leaf_only), vr);
@@ -385,8 +413,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // partners), then the slice's keys in quarter-wave batches: logits per
     // head into sm.z[zb], group scores into sm.s (with -inf padding), kept
     // flags cleared, per-wave maxima of the logits into sm.redz.
-    auto score = [&](const Step<T> &st, int s0, int ms, int zb, KR (&k0)[KB], KR (&k1)[KB],
+    auto score = [&](const Step<T> &st, int s0, int ms, int zb, KR (&k0)[KB], KR (&k1)[KB], float (&sc)[KB],
                      float (&rb)[2 * PPL], const float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
+        const bool q8 = F8 && !st.tok;
         float qa[G][PPL], qb[G][PPL];
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -410,7 +439,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         float *zz = sm.z[zb];
         for (int it0 = 0; it0 < nitems; it0 += KBR) {
             const int nb = min(nitems - it0, KBR);
-            if (it0 > 0) load_batch(st, s0, ms, it0, true, k0, k1, rb);
+            if (it0 > 0) load_batch(st, s0, ms, it0, true, k0, k1, sc, rb);
             int ci = c_beg + it0 / nref, j = 0;
             float best = -INFINITY, zbh = 0.f;
             float cc[PPL], ss[PPL];
@@ -423,8 +452,13 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             for (int u = 0; u < KB; ++u) {
                 if (u < nb) {
                     float x0[PPL], x1[PPL];
-                    cvt(k0[u], x0);
-                    cvt(k1[u], x1);
+                    if (q8) {
+                        cvt8<PPL>(get8(k0[u]), x0);
+                        cvt8<PPL>(get8(k1[u]), x1);
+                    } else {
+                        cvt(k0[u], x0);
+                        cvt(k1[u], x1);
+                    }
                     float z[G];
 #pragma unroll
                     for (int e = 0; e < PPL; ++e) {
@@ -437,7 +471,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                         }
                     }
                     // all heads' row sums at once: lane sub holds head sub / LPH
-                    const float zh = row_sums<G>(z, sub);
+                    float zh = row_sums<G>(z, sub);
+                    if (q8) zh *= sc[u];
                     const float gs = head_total<G>(zh) * (1.f / G);
                     if (gs > best) {
                         best = gs;
@@ -539,6 +574,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // ---- the steps ----
     int cur = 0, zb = 0;
     KR k0[KB], k1[KB];
+    float sc[KB];   // row scales of 8-bit router keys
     float rb[2 * PPL], qcs[2 * PPL];
     VR vr[VBS];
     // Upper levels that keep every candidate need no gathers: their kept
@@ -560,7 +596,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         --lvl;
         st = make_step(lvl, cur);
     }
-    issue_step(st, k0, k1, rb, vr, qcs);
+    issue_step(st, k0, k1, sc, rb, vr, qcs);
 
     for (; lvl >= 1; --lvl) {
         const int nxt = cur ^ 1;
@@ -577,7 +613,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < st.m) ? sm.sel[nxt][r] : -1;
             }
         } else {
-        score(st, s0, ms, zb, k0, k1, rb, qcs);
+        score(st, s0, ms, zb, k0, k1, sc, rb, qcs);
         __syncthreads();                                                   // B1
         new_max(Mn, alpha);
 
@@ -807,7 +843,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int u = 0; u < VBS; ++u) vrc[u] = vr[u];
         cur = nxt;
         st = make_step(lvl - 1, cur);
-        issue_step(st, k0, k1, rb, vr, qcs);
+        issue_step(st, k0, k1, sc, rb, vr, qcs);
         if (scored && !a.leaf_only) {
             // this workgroup's own candidates only (a local level was scored
             // whole by every workgroup)
@@ -824,10 +860,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     for (int c0 = st.s0; c0 < st.t1; c0 += kSlice) {
         const int ms = min(kSlice, st.t1 - c0);
         if (c0 != st.s0) {
-            load_batch(st, c0, ms, 0, true, k0, k1, rb);
+            load_batch(st, c0, ms, 0, true, k0, k1, sc, rb);
             issue_values(st, c0, ms, true, vr);
         }
-        score(st, c0, ms, zb, k0, k1, rb, qcs);
+        score(st, c0, ms, zb, k0, k1, sc, rb, qcs);
         __syncthreads();
         float Mn[G], alpha[G];
         new_max(Mn, alpha);
@@ -973,10 +1009,10 @@ constexpr size_t dec_dyn_bytes()
            sizeof(float);
 }
 
-template <typename T, int D, int G>
-static hipError_t dec_launch(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+template <typename T, int D, int G, bool F8>
+static hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
 {
-    auto kern = k_decode_split<T, D, G>;
+    auto kern = k_decode_split<T, D, G, F8>;
     const size_t dyn = dec_dyn_bytes<G, D>();
     static bool attr_set = false;
     if (!attr_set) {
@@ -995,6 +1031,16 @@ static hipError_t dec_launch(const TravArgs &a, const DecodeWs &ws, int64_t unit
     // output (a cooperative launch would guarantee residency but costs more
     // than the whole kernel to dispatch).
     return hipLaunchKernel((const void *)kern, dim3((unsigned)(units * ws.W)), dim3(DNT), args, dyn, s);
+}
+
+// 8-bit router keys: bf16 caches only
+template <typename T, int D, int G>
+static hipError_t dec_launch(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+{
+    if constexpr (std::is_same<T, bf16_t>::value)
+        if (a.t.rfp8) return dec_launch_k<T, D, G, true>(a, ws, units, s);
+    if (a.t.rfp8) return hipErrorInvalidValue;
+    return dec_launch_k<T, D, G, false>(a, ws, units, s);
 }
 
 template <typename T, int D>
@@ -1019,7 +1065,7 @@ hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t un
 template <typename T, int D, int G>
 static hipError_t dec_capacity(int *blocks_per_cu)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_decode_split<T, D, G>, DNT,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_decode_split<T, D, G, false>, DNT,
                                                         dec_dyn_bytes<G, D>());
 }
 

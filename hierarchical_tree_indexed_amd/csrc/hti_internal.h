@@ -16,6 +16,8 @@ struct TreeArgs {
     const void *kc, *vc;                 // [B, Hkv, Lcap, D]
     void *lk[HTI_MAX_LEVELS];            // level l+1 keys [B, Hkv, ncap, R, D]
     void *lv[HTI_MAX_LEVELS];            // level l+1 values [B, Hkv, ncap, D]
+    uint8_t *lkq[HTI_MAX_LEVELS];        // level l+1 E4M3 router keys [B, Hkv, ncap, R, D] (rfp8)
+    float *lks[HTI_MAX_LEVELS];          // their row scales [B, Hkv, ncap, R] (rfp8)
     int64_t ncap[HTI_MAX_LEVELS + 1];    // ncap[0] = Lcap
     const float *refs;                   // [Hkv, R, D]
     int64_t *len;                        // [B]
@@ -28,6 +30,7 @@ struct TreeArgs {
     int hdiv;
     float scale;                         // 1 / sqrt(D)
     int dtype;
+    int rfp8;                            // summary keys are scored through lkq / lks
 };
 
 // Selection rule and the query-side buffers of one traversal launch.

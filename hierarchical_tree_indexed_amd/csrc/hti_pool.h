@@ -60,6 +60,51 @@ __device__ __forceinline__ void store_slice<float, 64>(float *p, const float *v)
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// E4M3 code (OCP 8-bit float: 4 exponent bits, bias 7, 3 mantissa bits) of
+// x, |x| < 256, rounded to the nearest value, ties to even.  With e the
+// binade of |x| (floor(log2 |x|), at least -6, the subnormal binade's) the
+// value is q * 2^(e-3), q = rint(|x| * 2^(3-e)) in [0, 16], and the code is
+// 8 (e + 7) + q - 8: a q of 16 carries into the next binade's exponent field,
+// and the subnormals (e = -6, q < 8) land on codes 0..7.
+__device__ __forceinline__ uint32_t e4m3_code(float x)
+{
+    const float a = fabsf(x);
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    e = e < -6 ? -6 : e;
+    const int q = (int)rintf(ldexpf(a, 3 - e));
+    return (uint32_t)(8 * e + 48 + q) | ((__float_as_uint(x) >> 24) & 0x80u);
+}
+
+// Router copy of one pooled key row, held as EPL elements by each of the 16
+// lanes of a row group (the values as stored: rounded to the cache dtype):
+// the row scale 2^(e-8) for amax = f * 2^e, f in [0.5, 1) (1 when the row is
+// zero), and the codes of the scaled elements.  Lanes of row group 0 store.
+template <int D, int EPL>
+__device__ __forceinline__ void store_router_row(const TreeArgs &t, int lvl, int64_t row, const float *k, int sub,
+                                                 bool store)
+{
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(k[e]));
+    amax = max16(amax);
+    const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 8;
+    uint32_t w[EPL / 4];
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) {
+        w[i] = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[i] |= e4m3_code(ldexpf(k[4 * i + e], 8 - ex)) << (8 * e);
+    }
+    if (store) {
+        uint8_t *q = t.lkq[lvl - 1] + row * D + sub * EPL;
+        if constexpr (EPL == 8)
+            *reinterpret_cast<uint2 *>(q) = make_uint2(w[0], w[1]);
+        else
+            *reinterpret_cast<uint32_t *>(q) = w[0];
+        if (sub == 0) t.lks[lvl - 1][row] = ldexpf(1.f, ex - 8);
+    }
+}
+
 template <typename T, int D, int CPL>
 __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t node, int lane)
 {
@@ -134,6 +179,12 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
         if (rg == 0) {
             T *out = (T *)t.lk[lvl - 1] + (((bh * t.ncap[lvl] + node) * R + j) * D) + sub * EPL;
             store_slice<T, D>(out, acc);
+        }
+        if (t.rfp8) {
+            float kr[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) kr[e] = round_to<T>(acc[e]);
+            store_router_row<D, EPL>(t, lvl, (bh * t.ncap[lvl] + node) * R + j, kr, sub, rg == 0);
         }
     }
 

@@ -524,10 +524,21 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
     __shared__ float kr[kTopCols][D + 1];
     const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const bf16_t *kb = (const bf16_t *)t.lk[t.levels - 1] + bh * t.ncap[t.levels] * R * D;
+    // (8-bit router keys: E4M3 codes times the row scale)
+    const uint8_t *k8 = t.rfp8 ? t.lkq[t.levels - 1] + bh * t.ncap[t.levels] * R * D : nullptr;
+    const float *s8 = t.rfp8 ? t.lks[t.levels - 1] + bh * t.ncap[t.levels] * R : nullptr;
     for (int i = tid; i < ncol * (D / 2); i += 256) {
         const int col = i / (D / 2), e = i % (D / 2);
         const int c = col / R;
-        const float x0 = bf2f(kb[(int64_t)col * D + e]), x1 = bf2f(kb[(int64_t)col * D + e + D / 2]);
+        float x0, x1;
+        if (t.rfp8) {
+            const float sc = s8[col];
+            x0 = __builtin_amdgcn_cvt_f32_fp8((int)k8[(int64_t)col * D + e], 0) * sc;
+            x1 = __builtin_amdgcn_cvt_f32_fp8((int)k8[(int64_t)col * D + e + D / 2], 0) * sc;
+        } else {
+            x0 = bf2f(kb[(int64_t)col * D + e]);
+            x1 = bf2f(kb[(int64_t)col * D + e + D / 2]);
+        }
         const float2 cs = t.rope[(int64_t)c * (D / 2) + e];
         kr[col][e] = x0 * cs.x - x1 * cs.y;
         kr[col][e + D / 2] = x0 * cs.y + x1 * cs.x;

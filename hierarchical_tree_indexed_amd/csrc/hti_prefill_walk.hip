@@ -80,7 +80,7 @@ __host__ __device__ constexpr size_t pw_wave_words(int G, int D, int MC)
     return (size_t)G * D + (size_t)(MC / 2) * G + MC + 64 + (size_t)MC * G + 2 * kMaxSel;
 }
 
-template <int D, int G, int MJ>
+template <int D, int G, int MJ, bool F8>
 __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 {
     using T = bf16_t;
@@ -166,9 +166,14 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
     // is turned to its candidate's position, and one transposed butterfly
     // sums the G heads' partial dot products, leaving head sub / LPH in lane
     // sub.
-    auto score = [&](auto wgs, const Cands &cs, const T *kb, int nref, int c0, int m, int qpos)
-        __attribute__((always_inline)) {
+    auto score = [&](auto wgs, auto f8, const Cands &cs, const void *kb, const float *ks, int nref, int c0, int m,
+                     int qpos) __attribute__((always_inline)) {
         constexpr bool WGS = decltype(wgs)::value;
+        // E4M3 router keys (one byte per element) with a scale per key row
+        constexpr bool Q8 = decltype(f8)::value;
+        using KL = std::conditional_t<Q8, typename Raw8<PPL>::type, KR>;
+        constexpr uint32_t ES = Q8 ? 1 : 2;              // bytes per key element
+        constexpr int RSH = D == 128 ? 5 : 4;            // key row bytes -> scale bytes (E4M3 rows)
         float qa[G][PPL], qb[G][PPL];
         {
             const float2 *rq = t.rope + (int64_t)qpos * (D / 2) + sub * PPL;
@@ -184,7 +189,8 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
             }
         }
         const __amdgpu_buffer_rsrc_t krs = rsrc(kb, 0xffffffffu);
-        const uint32_t klane = sub * PPL * 2;      // bytes: the lane's pairs within a key half
+        const __amdgpu_buffer_rsrc_t srs = rsrc(ks, 0xffffffffu);
+        const uint32_t klane = sub * PPL * ES;     // bytes: the lane's pairs within a key half
         const int cpq = (m + 3) / 4;
         const int cb = min(m, quarter * cpq);
         const int ce = min(m, cb + cpq);
@@ -193,11 +199,16 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         const bool wz = (sub % LPH) == 0;          // lanes that store a head's logit
         const bool ws = WGS && sub == 1;           // the lane that stores the group score
         // z of one key item: the key turned by (c, s), dotted with the G heads
-        auto logits = [&](const KR &kx0, const KR &kx1, const float (&c)[PPL], const float (&sn)[PPL])
+        auto logits = [&](const KL &kx0, const KL &kx1, const float (&c)[PPL], const float (&sn)[PPL], float sc)
             __attribute__((always_inline)) {
             float x0[PPL], x1[PPL];
-            cvt(kx0, x0);
-            cvt(kx1, x1);
+            if constexpr (Q8) {
+                cvt8<PPL>(kx0, x0);
+                cvt8<PPL>(kx1, x1);
+            } else {
+                cvt(kx0, x0);
+                cvt(kx1, x1);
+            }
             float z[G];
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
@@ -209,7 +220,8 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                     z[h] = fmaf(qb[h][e], r1, z[h]);
                 }
             }
-            return row_sums<G>(z, sub);
+            const float zs = row_sums<G>(z, sub);
+            return Q8 ? zs * sc : zs;
         };
         if (nref == 1) {
             // every item is a candidate: no reference-key maximum.  The items
@@ -230,13 +242,15 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                 // lane `sub` derives the row of item it0 + sub (clamped into
                 // the batch); row u reaches the quarter by a DPP row broadcast
                 const int cand = max(0, min(cb + it0 + (nb > 0 ? min(sub, nb - 1) : 0), m - 1));
-                const uint32_t roff = (uint32_t)cs.id(c0 + cand) * (D * 2);
-                KR k0[KB], k1[KB];
+                const uint32_t roff = (uint32_t)cs.id(c0 + cand) * (D * ES);
+                KL k0[KB], k1[KB];
+                float sc[KB];
 #pragma unroll
                 for (int u = 0; u < KB; ++u) {
-                    const uint32_t o = (uint32_t)row_bcast((int)roff, u) + klane;
-                    k0[u] = bload<KR>(krs, o, 0);
-                    k1[u] = bload<KR>(krs, o + D, 0);
+                    const uint32_t rb = (uint32_t)row_bcast((int)roff, u);
+                    k0[u] = bload<KL>(krs, rb + klane, 0);
+                    k1[u] = bload<KL>(krs, rb + klane + D * ES / 2, 0);
+                    sc[u] = Q8 ? __uint_as_float(bload<uint32_t>(srs, rb >> RSH, 0)) : 1.f;
                 }
                 const uint32_t rbase = (uint32_t)(c0 + cb + it0) * RB + sub * PPL * 8;
                 float c[PPL], sn[PPL], cq[PPL], sq[PPL];   // position p and p - 1 (or p + 1 before the first step)
@@ -275,7 +289,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                             sn[e] = s2;
                         }
                     }
-                    const float zh = logits(k0[u], k1[u], c, sn);
+                    const float zh = logits(k0[u], k1[u], c, sn, sc[u]);
                     float gs = 0.f;
                     if constexpr (WGS) gs = head_total<G>(zh) * (1.f / G);
                     // every lane stores (the others into the spare words past
@@ -303,13 +317,15 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                 const int itl = it0 + (nb > 0 ? min(sub, nb - 1) : 0);
                 const int cl = itl / nref;
                 const int cand = max(0, min(cb + cl, m - 1));
-                const uint32_t roff = ((uint32_t)cs.id(c0 + cand) * nref + (itl - cl * nref)) * (D * 2);
-                KR k0[KB], k1[KB];
+                const uint32_t roff = ((uint32_t)cs.id(c0 + cand) * nref + (itl - cl * nref)) * (D * ES);
+                KL k0[KB], k1[KB];
+                float sc[KB];
 #pragma unroll
                 for (int u = 0; u < KB; ++u) {
-                    const uint32_t o = (uint32_t)row_bcast((int)roff, u) + klane;
-                    k0[u] = bload<KR>(krs, o, 0);
-                    k1[u] = bload<KR>(krs, o + D, 0);
+                    const uint32_t rb = (uint32_t)row_bcast((int)roff, u);
+                    k0[u] = bload<KL>(krs, rb + klane, 0);
+                    k1[u] = bload<KL>(krs, rb + klane + D * ES / 2, 0);
+                    sc[u] = Q8 ? __uint_as_float(bload<uint32_t>(srs, rb >> RSH, 0)) : 1.f;
                 }
                 float cc[PPL], ss[PPL];
                 {
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 #pragma unroll
                 for (int u = 0; u < KB; ++u) {
                     if (u < nb) {
-                        const float zh = logits(k0[u], k1[u], cc, ss);
+                        const float zh = logits(k0[u], k1[u], cc, ss, sc[u]);
                         const float gs = head_total<G>(zh) * (1.f / G);
                         if (gs > best) {
                             best = gs;
@@ -495,7 +511,11 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
                 }
                 wave_sync();
             } else {
-                score(std::true_type{}, cs, kb, R, 0, m, m);
+                if constexpr (F8)
+                    score(std::true_type{}, std::true_type{}, cs, t.lkq[lvl - 1] + bh * t.ncap[lvl] * R * D,
+                          t.lks[lvl - 1] + bh * t.ncap[lvl] * R, R, 0, m, m);
+                else
+                    score(std::true_type{}, std::false_type{}, cs, kb, nullptr, R, 0, m, m);
             }
             // selection (score desc, then lower index): the lane holds
             // candidates lane + 64 jj
@@ -602,7 +622,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
         for (int c0 = 0; c0 < m0; c0 += MC) {
             const int mc = min(MC, m0 - c0);
-            score(std::false_type{}, cs, kc, 1, c0, mc, qpos);
+            score(std::false_type{}, std::false_type{}, cs, kc, nullptr, 1, c0, mc, qpos);
             softmax_step(mc, 0u);
             fold(cs, vc, c0, mc);
         }
@@ -622,10 +642,10 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
     }
 }
 
-template <int D, int G, int MJ>
+template <int D, int G, int MJ, bool F8>
 static hipError_t pw_launch(const TravArgs &a, int MC, int64_t units, hipStream_t s)
 {
-    auto kern = k_prefill_walk<D, G, MJ>;
+    auto kern = k_prefill_walk<D, G, MJ, F8>;
     // up to four units per workgroup, as many as fit the LDS
     const size_t per_wave = pw_wave_words(G, D, MC) * 4;
     int nw = (int)std::min<size_t>(4, (size_t)(160 * 1024) / per_wave);
@@ -640,7 +660,11 @@ static hipError_t pw_launch(const TravArgs &a, int MC, int64_t units, hipStream_
 template <int D, int G>
 static hipError_t pw_mj(const TravArgs &a, int MC, int64_t max_summary, int64_t units, hipStream_t s)
 {
-    return max_summary <= 320 ? pw_launch<D, G, 5>(a, MC, units, s) : pw_launch<D, G, 17>(a, MC, units, s);
+    if (a.t.rfp8)
+        return max_summary <= 320 ? pw_launch<D, G, 5, true>(a, MC, units, s)
+                                  : pw_launch<D, G, 17, true>(a, MC, units, s);
+    return max_summary <= 320 ? pw_launch<D, G, 5, false>(a, MC, units, s)
+                              : pw_launch<D, G, 17, false>(a, MC, units, s);
 }
 
 template <int D>

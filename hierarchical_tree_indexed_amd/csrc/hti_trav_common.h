@@ -25,6 +25,30 @@ __device__ __forceinline__ void cvt(uint2 r, float *o)
     cvt(r.x, o);
     cvt(r.y, o + 2);
 }
+// E4M3 router keys: raw images of N consecutive codes, decoded by the vector
+// unit's packed 8-bit float conversion (OCP E4M3 on this target).
+template <int N> struct Raw8;
+template <> struct Raw8<2> { using type = uint16_t; };
+template <> struct Raw8<4> { using type = uint32_t; };
+template <int N> __device__ __forceinline__ void cvt8(uint32_t r, float *o)
+{
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r, false);
+    o[0] = lo[0];
+    o[1] = lo[1];
+    if constexpr (N == 4) {
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r, true);
+        o[2] = hi[0];
+        o[3] = hi[1];
+    }
+}
+// E4M3 codes held in the low bytes of a key register image
+__device__ __forceinline__ void put8(uint2 &k, uint32_t w) { k = make_uint2(w, 0u); }
+__device__ __forceinline__ void put8(uint32_t &k, uint32_t w) { k = w; }
+__device__ __forceinline__ uint32_t get8(const uint2 &k) { return k.x; }
+__device__ __forceinline__ uint32_t get8(const uint32_t &k) { return k; }
+// (fp32 caches: 8-bit router keys are rejected before any launch)
+template <typename K> __device__ __forceinline__ void put8(K &, uint32_t) {}
+template <typename K> __device__ __forceinline__ uint32_t get8(const K &) { return 0u; }
 __device__ __forceinline__ void cvt(float r, float *o) { o[0] = r; }
 __device__ __forceinline__ void cvt(float2 r, float *o)
 {

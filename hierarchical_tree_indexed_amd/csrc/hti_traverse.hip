@@ -74,7 +74,7 @@ struct Smem {
 
 } // namespace
 
-template <typename T, int D, int G, bool PREFILL, int NWV, bool STAGE>
+template <typename T, int D, int G, bool PREFILL, int NWV, bool STAGE, bool F8>
 __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a)
 {
     constexpr int NT = NWV * 64;
@@ -495,17 +495,30 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
             if (tok) return kc + cs.id((int)(ch + ci)) * D;
             return lk + ((bh * ncap + cs.id(ci)) * R + j) * D;
         };
+        // 8-bit router keys at the summary levels: E4M3 codes (in the low
+        // bytes of the key registers) and a scale per key row
+        const bool q8 = F8 && !tok;
+        using K8 = typename Raw8<PPL>::type;
 
         KR k0[KB], k1[KB];
+        float sc[KB];
         float rb_c[PPL], rb_s[PPL];
         auto issue_keys = [&](int item0, int nb) __attribute__((always_inline)) {
             int ci = c_beg + item0 / nref, j = 0;
 #pragma unroll
             for (int u = 0; u < KB; ++u) {
                 if (u < nb) {
-                    const T *kp = key_row(ci, j);
-                    k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
-                    k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
+                    if (q8) {
+                        const int64_t r = (bh * ncap + cs.id(ci)) * R + j;
+                        const uint8_t *kp = t.lkq[lvl - 1] + r * D;
+                        put8(k0[u], *reinterpret_cast<const K8 *>(kp + sub * PPL));
+                        put8(k1[u], *reinterpret_cast<const K8 *>(kp + D / 2 + sub * PPL));
+                        sc[u] = t.lks[lvl - 1][r];
+                    } else {
+                        const T *kp = key_row(ci, j);
+                        k0[u] = *reinterpret_cast<const KR *>(kp + sub * PPL);
+                        k1[u] = *reinterpret_cast<const KR *>(kp + D / 2 + sub * PPL);
+                    }
                     if (++j == nref) {
                         j = 0;
                         ++ci;
@@ -575,8 +588,13 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
                 for (int u = 0; u < KB; ++u) {
                     if (u < nb) {
                         float x0[PPL], x1[PPL];
-                        cvt(k0[u], x0);
-                        cvt(k1[u], x1);
+                        if (q8) {
+                            cvt8<PPL>(get8(k0[u]), x0);
+                            cvt8<PPL>(get8(k1[u]), x1);
+                        } else {
+                            cvt(k0[u], x0);
+                            cvt(k1[u], x1);
+                        }
                         float z[G];
 #pragma unroll
                         for (int e = 0; e < PPL; ++e) {
@@ -589,7 +607,8 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
                             }
                         }
                         // all heads' row sums at once: lane sub holds head sub / LPH
-                        const float zh = row_sums<G>(z, sub);
+                        float zh = row_sums<G>(z, sub);
+                        if (q8) zh *= sc[u];
                         const float gs = head_total<G>(zh) * (1.f / G);
                         if (gs > best) {
                             best = gs;
@@ -686,12 +705,12 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
 
 // decode: 8 waves per unit, value rows staged in LDS; prefill: 2 waves per
 // unit, values through registers
-template <typename T, int D, int G, bool PF>
-static hipError_t trav_launch(const TravArgs &a, int64_t units, hipStream_t s)
+template <typename T, int D, int G, bool PF, bool F8>
+static hipError_t trav_launch_k(const TravArgs &a, int64_t units, hipStream_t s)
 {
     constexpr int NWV = PF ? 2 : 8;
     constexpr bool STAGE = !PF;
-    auto kern = k_traverse<T, D, G, PF, NWV, STAGE>;
+    auto kern = k_traverse<T, D, G, PF, NWV, STAGE, F8>;
     const size_t dyn = STAGE ? kVStageBytes : 0;
     static bool attr_set = false;
     if (!attr_set && dyn > 0) {
@@ -702,6 +721,16 @@ static hipError_t trav_launch(const TravArgs &a, int64_t units, hipStream_t s)
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(NWV * 64), dyn, s, a);
     return hipGetLastError();
+}
+
+// 8-bit router keys: bf16 caches, decode
+template <typename T, int D, int G, bool PF>
+static hipError_t trav_launch(const TravArgs &a, int64_t units, hipStream_t s)
+{
+    if constexpr (std::is_same<T, bf16_t>::value && !PF)
+        if (a.t.rfp8) return trav_launch_k<T, D, G, PF, true>(a, units, s);
+    if (a.t.rfp8) return hipErrorInvalidValue;
+    return trav_launch_k<T, D, G, PF, false>(a, units, s);
 }
 
 template <typename T, int D, bool PF>

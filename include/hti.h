@@ -78,6 +78,20 @@ typedef struct {
     int64_t Lcap;       /* token capacity of the cache per (sequence, head) */
     float rope_base;    /* RoPE base (e.g. 10000) */
     int32_t rope_npos;  /* rows of the RoPE table (largest position + 1) */
+    int32_t router_fp8; /* 0: summary keys are scored as stored.  1 (bf16 caches
+                           only): every summary key row also has an 8-bit float
+                           copy (lvl_kq, lvl_ks) that the build, append and extend
+                           calls write beside it, and the traversals score every
+                           summary candidate through that copy -- its selection
+                           score and, unless leaf_only, its softmax logit.  Token
+                           keys and all values stay in the cache dtype.  The
+                           low-precision router of ZHA Figure 16 (router operands,
+                           reference-key cache and scoring in low precision, the
+                           KV cache and the sparse attention in bf16), here in
+                           OCP E4M3: each row is divided by the power of two
+                           2^(e - 8), amax = f * 2^e with f in [0.5, 1) its
+                           largest magnitude (1 for an all-zero row), and
+                           rounded to the nearest E4M3 value, ties to even. */
 } hti_tree_cfg;
 
 /* Device buffers of a tree set (all caller-allocated, sizes from hti_plan). */
@@ -90,6 +104,9 @@ typedef struct {
     const float *ref_q;               /* [Hkv, R, d] fp32 reference queries */
     int64_t *len;                     /* [B] device: tokens currently in each tree */
     float *rope;                      /* [rope_npos, d/2, 2] fp32 (cos, sin), see hti_rope_init */
+    /* cfg.router_fp8 only (else ignored): */
+    uint8_t *lvl_kq[HTI_MAX_LEVELS];  /* level l+1: [B, Hkv, ncap_{l+1}, R, d] E4M3 codes of lvl_k */
+    float *lvl_ks[HTI_MAX_LEVELS];    /* level l+1: [B, Hkv, ncap_{l+1}, R] their scales */
 } hti_tree;
 
 /* Per-call selection rule (RecSA: top-k per level; ZHA: top-p per level). */
@@ -119,6 +136,8 @@ typedef struct {
     size_t rope_bytes;
     int32_t rope_npos_needed;         /* rows hti_sparse_decode needs for this cfg and
                                          the selection passed to hti_plan */
+    size_t lvl_kq_bytes[HTI_MAX_LEVELS]; /* router copies (0 unless cfg.router_fp8) */
+    size_t lvl_ks_bytes[HTI_MAX_LEVELS];
 } hti_plan_out;
 
 /*

@@ -31,10 +31,11 @@ def log(*a):
     sys.stdout.flush()
 
 
-def make_treeset(w, Lcap, K=None, V=None, refs=None, T=0, rope_npos=None):
+def make_treeset(w, Lcap, K=None, V=None, refs=None, T=0, rope_npos=None, router_fp8=False):
     """TreeSet on cuda:0 for workload w (B, Hq, Hkv, d, b, levels, R, dtype)."""
     sel = select_of(w)
-    cfg = hti.make_cfg(w.B, w.Hq, w.Hkv, w.d, w.b, w.levels, w.R, w.dtype, Lcap, w.rope_base, 1)
+    cfg = hti.make_cfg(w.B, w.Hq, w.Hkv, w.d, w.b, w.levels, w.R, w.dtype, Lcap, w.rope_base, 1,
+                       router_fp8=router_fp8)
     need = hti.plan(cfg, sel, T).rope_npos_needed
     cfg.rope_npos = max(need, rope_npos or 0)
     ts = hti.TreeSet(cfg, device="cuda", k_cache=K, v_cache=V)
@@ -56,10 +57,11 @@ def oracle_tree(w, K_bh, V_bh, refs_h, L):
     return oracle.build_tree(K_bh[:L], V_bh[:L], refs_h, w.b, w.levels, bf16=(w.dtype == "bf16"), L=L)
 
 
-def accept(w, tree, K_bh, V_bh, q_g, gout, glse, gsel, *, t=-1, blk_k=None, blk_v=None, leaf_only=False):
+def accept(w, tree, K_bh, V_bh, q_g, gout, glse, gsel, *, t=-1, blk_k=None, blk_v=None, leaf_only=False,
+           router_fp8=False):
     """Apply the acceptance rule to one (query, group). Returns (exempt, maxerr)."""
     kw = dict(mode=w.mode, k=w.k, p=w.p, cap=w.cap, rope_base=w.rope_base, kmax=kmax_of(w),
-              leaf_only=leaf_only)
+              leaf_only=leaf_only, router_fp8=router_fp8)
     if t >= 0:
         kw.update(t=t, blk_k=blk_k, blk_v=blk_v)
     r = oracle.query(tree, K_bh, V_bh, q_g, **kw)

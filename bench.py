@@ -63,19 +63,21 @@ def treeset(w, Lcap, K, V, T=0):
     return ts, sel
 
 
-def decode_unit_bytes(w, L):
+def decode_unit_bytes(w, L, router_fp8=False):
     """Algorithmic bytes one (query, KV group) unit must touch at length L:
     scored keys (x R) + unselected summary values + token keys and values,
-    plus its query and output rows.  Entry = d elements of the cache dtype."""
+    plus its query and output rows.  Entry = d elements of the cache dtype;
+    with 8-bit router keys a summary key is d bytes and a 4-byte scale."""
     n = w.level_counts(L)
     keff = w.k if w.mode == "topk" else w.cap
     thr = w.k if w.mode == "topk" else 1
     keys = vals = 0
     m = n[w.levels]
+    skeys = 0
     for lvl in range(w.levels, 0, -1):
         if m > thr:
             nsel = min(keff, m)
-            keys += m * w.R
+            skeys += m * w.R
             vals += m - nsel
         else:
             nsel = m
@@ -83,7 +85,8 @@ def decode_unit_bytes(w, L):
     keys += m
     vals += m
     e = w.d * w.elem_bytes
-    return (keys + vals) * e + w.G * w.d * (w.elem_bytes + 4)
+    ek = w.d + 4 if router_fp8 else e
+    return skeys * ek + (keys + vals) * e + w.G * w.d * (w.elem_bytes + 4)
 
 
 def bench_decode(args):
@@ -151,16 +154,22 @@ def bench_decode(args):
     del graph
     kern_ms = total_ms / S
 
-    ph_ms = lf_ms = float("nan")
+    ph_ms = lf_ms = plain_ms = r8_ms = float("nan")
     if not args.no_variants:
-        ph_ms, lf_ms = decode_variants(ts, w, qs, Wm, S, out, cs)
+        ph_ms, lf_ms, plain_ms, r8_ms = decode_variants(ts, w, qs, Wm, S, out, cs)
+    Lr = w.L + Wm + 2 * S
     res = dict(ms_per_step=total_ms / S, eager_ms_per_step=eager_ms / S, wall_s=wall,
                decode_kernel_ms=kern_ms, decode_eager_kernel_ms=dec_ms, bytes_per_launch=bytes_per_launch,
                qps=w.B * S / (total_ms / 1e3),
                gbs=bytes_per_launch / (kern_ms / 1e3) / 1e9,
                per_head_ms=ph_ms, per_head_qps=w.B / (ph_ms / 1e3),
                per_head_gbs=decode_unit_bytes(w, w.L + Wm + 2 * S) * w.B * w.Hq / (ph_ms / 1e3) / 1e9,
-               leaf_only_ms=lf_ms, leaf_only_qps=w.B / (lf_ms / 1e3))
+               leaf_only_ms=lf_ms, leaf_only_qps=w.B / (lf_ms / 1e3),
+               plain_ms=plain_ms, plain_gbs=decode_unit_bytes(w, Lr) * w.B * w.Hkv / (plain_ms / 1e3) / 1e9,
+               r8_ms=r8_ms, r8_qps=w.B / (r8_ms / 1e3),
+               r8_gbs=decode_unit_bytes(w, Lr, True) * w.B * w.Hkv / (r8_ms / 1e3) / 1e9,
+               r8_bytes=decode_unit_bytes(w, Lr, True) * w.B * w.Hkv,
+               plain_bytes=decode_unit_bytes(w, Lr) * w.B * w.Hkv)
     log(f"[decode] {res}")
     del K, V, ts
     torch.cuda.empty_cache()
@@ -173,8 +182,9 @@ def finite(x):
 
 
 def decode_variants(ts, w, qs, Wm, S, out, cs):
-    """Graph-timed sparse_decode per step under per-query-head routing and
-    under leaf-only dispatch (the tree as the main step left it)."""
+    """Graph-timed sparse_decode per step under per-query-head routing, under
+    leaf-only dispatch, plain, and with 8-bit router keys (the tree as the
+    main step left it)."""
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # per-query-head routing (every query head its own selection): the same
     # queries at the reached length, sparse_decode without the append, S
@@ -215,7 +225,37 @@ def decode_variants(ts, w, qs, Wm, S, out, cs):
     torch.cuda.synchronize()
     lf_ms = g0.elapsed_time(g1) / S
     del graph
-    return ph_ms, lf_ms
+
+    # plain sparse_decode on the bf16 keys, then the same call on a second
+    # tree set over the same caches whose summary keys carry the 8-bit router
+    # copy (built at the reached length)
+    def gtime(t_, sel_):
+        for s in range(4):
+            t_.sparse_decode(sel_, qs[s], out_ph)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(gr, stream=cs):
+                for s in range(S):
+                    t_.sparse_decode(sel_, qs[Wm + s], out_ph)
+        torch.cuda.synchronize()
+        g0.record()
+        gr.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / S
+
+    sel = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap)
+    plain_ms = gtime(ts, sel)
+    cfg8 = hti.TreeCfg.from_buffer_copy(ts.cfg)
+    cfg8.router_fp8 = 1
+    ts8 = hti.TreeSet(cfg8, device=DEV, k_cache=ts.k_cache, v_cache=ts.v_cache)
+    ts8.ref_q.copy_(ts.ref_q)
+    ts8.rope_init()
+    ts8.tree_build(ts.len.cpu().tolist())
+    r8_ms = gtime(ts8, sel)
+    del ts8
+    return ph_ms, lf_ms, plain_ms, r8_ms
 
 
 def bench_prefill(args):
@@ -252,6 +292,22 @@ def bench_prefill(args):
         ts.sparse_prefill(sel_lf, qb, kb, vb, out, ws, lse)
 
     ms_lf = float("nan") if args.no_variants else timed(run_lf, args.prefill_reps)
+    # 8-bit router keys: a tree set over the same prefix whose summary keys
+    # carry the E4M3 copy, built and prefilled the same way
+    ms_r8 = float("nan")
+    if not args.no_variants:
+        cfg8 = hti.TreeCfg.from_buffer_copy(ts.cfg)
+        cfg8.router_fp8 = 1
+        ts8 = hti.TreeSet(cfg8, device=DEV, k_cache=K, v_cache=V)
+        ts8.ref_q.copy_(ts.ref_q)
+        ts8.rope_init()
+
+        def run_r8():
+            ts8.tree_build([w.L] * w.B)
+            ts8.sparse_prefill(sel, qb, kb, vb, out, ws, lse)
+
+        ms_r8 = timed(run_r8, args.prefill_reps)
+        del ts8
     # the dense part alone: the same block over an empty prefix leaves only
     # the in-block causal attention on the matrix cores (plus the rotation
     # of the block and an empty traversal)
@@ -289,7 +345,8 @@ def bench_prefill(args):
     ext_bytes = 3 * 2 * row_bytes + nodes * w.B * w.Hkv * (w.R + 1) * w.d * W.TORCH_DTYPE[w.dtype].itemsize
     res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9,
                dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12,
-               extend_ms=ms_ext, extend_gbs=ext_bytes / (ms_ext / 1e3) / 1e9, leaf_only_ms=ms_lf)
+               extend_ms=ms_ext, extend_gbs=ext_bytes / (ms_ext / 1e3) / 1e9, leaf_only_ms=ms_lf,
+               r8_ms=ms_r8)
     log(f"[prefill] {res}")
     del K, V, ts, ws, tsx, Kx, Vx
     torch.cuda.empty_cache()
@@ -413,6 +470,14 @@ def main():
         "decode_leaf_only_ms": finite(dec["leaf_only_ms"]) if dec else None,
         "decode_leaf_only_qps": finite(dec["leaf_only_qps"]) if dec else None,
         "prefill_leaf_only_ms_per_block": finite(pre["leaf_only_ms"]) if pre else None,
+        "decode_plain_ms": finite(dec["plain_ms"]) if dec else None,
+        "decode_plain_gbs": finite(dec["plain_gbs"]) if dec else None,
+        "decode_router_fp8_ms": finite(dec["r8_ms"]) if dec else None,
+        "decode_router_fp8_qps": finite(dec["r8_qps"]) if dec else None,
+        "decode_router_fp8_gbs": finite(dec["r8_gbs"]) if dec else None,
+        "decode_router_fp8_bytes_per_launch": dec["r8_bytes"] if dec else None,
+        "decode_plain_bytes_per_launch": dec["plain_bytes"] if dec else None,
+        "prefill_router_fp8_ms_per_block": finite(pre["r8_ms"]) if pre else None,
         "prefill_tokens_per_s": pre["tokens_per_s"] if pre else None,
         "prefill_ms_per_block": pre["ms_per_block"] if pre else None,
         "prefill_extend_ms": pre["extend_ms"] if pre else None,

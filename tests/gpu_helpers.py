@@ -57,6 +57,31 @@ def oracle_tree(w, K_bh, V_bh, refs_h, L):
     return oracle.build_tree(K_bh[:L], V_bh[:L], refs_h, w.b, w.levels, bf16=(w.dtype == "bf16"), L=L)
 
 
+def oracle_tree_from_device(ts, w, bi, g, L):
+    """The oracle's tree of (sequence bi, KV head g) holding the device's
+    stored levels: for checks of the routing on the keys the device holds
+    (the build itself is checked against the oracle's own build)."""
+    tr = oracle.Tree(L, w.d, w.b, w.levels, w.R, w.dtype == "bf16")
+    for l in range(w.levels):
+        n = tr.lk[l].shape[0]
+        tr.lk[l][...] = ts.lvl_k[l][bi, g, :n].float().cpu().numpy()
+        tr.lv[l][...] = ts.lvl_v[l][bi, g, :n].float().cpu().numpy()
+    return tr
+
+
+def router_copy_matches(ts, w, bi, g, L):
+    """The device's 8-bit router copy of (bi, g) equals the oracle's encoding
+    of the device's stored keys; returns the number of rows compared."""
+    rows = 0
+    for l in range(w.levels):
+        n = L // w.b ** (l + 1)
+        codes, sc = oracle.router_fp8(ts.lvl_k[l][bi, g, :n].float().cpu().numpy())
+        assert np.array_equal(ts.lvl_kq[l][bi, g, :n].cpu().numpy(), codes), f"level {l + 1} codes"
+        assert np.array_equal(ts.lvl_ks[l][bi, g, :n].cpu().numpy(), sc), f"level {l + 1} scales"
+        rows += n * w.R
+    return rows
+
+
 def accept(w, tree, K_bh, V_bh, q_g, gout, glse, gsel, *, t=-1, blk_k=None, blk_v=None, leaf_only=False,
            router_fp8=False):
     """Apply the acceptance rule to one (query, group). Returns (exempt, maxerr)."""

@@ -16,7 +16,8 @@ import torch
 
 import hierarchical_tree_indexed_amd as hti
 import hti_workloads as W
-from gpu_helpers import accept, kmax_of, log, make_treeset, oracle_tree, select_of
+from gpu_helpers import (accept, kmax_of, log, make_treeset, oracle_tree, oracle_tree_from_device,
+                         router_copy_matches, select_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,19 +28,20 @@ def _host(x):
     return x.cpu()
 
 
-def _decode_full(w, units, Lcap, append_steps=0, leaf_only=False, per_head=False):
+def _decode_full(w, units, Lcap, append_steps=0, leaf_only=False, per_head=False, router_fp8=False):
     """Build the tree over the full context, append `append_steps` tokens,
     decode one query per sequence with the split kernel, and accept the
     sampled units against the oracle (leaf_only / per_head: the selection
     variants; per_head checks every query head of the sampled KV groups as a
-    group of one)."""
+    group of one; router_fp8: routing through the 8-bit key copy, checked
+    bit for bit at the sampled units, the oracle on the stored levels)."""
     log(f"full-size decode {w.name}: B={w.B} L={w.L} Hkv={w.Hkv} levels={w.levels} R={w.R} {w.mode}")
     K, V = W.gen_kv(w, Lcap=Lcap, device=DEV)
     q0 = W.gen_queries(w)
     if w.needles:
         W.plant_needles(w, K, q0)
     refs = W.gen_refs(w)
-    ts = make_treeset(w, Lcap, K, V, refs.to(DEV))
+    ts = make_treeset(w, Lcap, K, V, refs.to(DEV), router_fp8=router_fp8)
     ts.tree_build([w.L] * w.B)
     for s in range(append_steps):
         kn, vn = W.gen_append(w, s, device=DEV)
@@ -58,13 +60,18 @@ def _decode_full(w, units, Lcap, append_steps=0, leaf_only=False, per_head=False
     nex, emax = 0, 0.0
     for bi, g in units:
         Kh, Vh = _host(K[bi, g, :L]), _host(V[bi, g, :L])
-        tree = oracle_tree(w, Kh, Vh, refs[g], L)
+        if router_fp8:
+            rows = router_copy_matches(ts, w, bi, g, L)
+            log(f"  unit (seq {bi}, group {g}): {rows} router rows identical")
+            tree = oracle_tree_from_device(ts, w, bi, g, L)
+        else:
+            tree = oracle_tree(w, Kh, Vh, refs[g], L)
         heads = [slice(h, h + 1) for h in range(g * w.G, (g + 1) * w.G)] if per_head else \
             [slice(g * w.G, (g + 1) * w.G)]
         for hs in heads:
             srow = sel[bi, 0, hs.start] if per_head else sel[bi, 0, g]
             ex, err = accept(w, tree, Kh, Vh, q[bi, 0, hs], out[bi, 0, hs], lse[bi, 0, hs], srow,
-                             leaf_only=leaf_only)
+                             leaf_only=leaf_only, router_fp8=router_fp8)
             nex += ex
             emax = max(emax, err)
         log(f"  unit (seq {bi}, group {g}): exempt so far {nex}, max_err {emax:.2e}")
@@ -96,6 +103,15 @@ def test_decode_1m_batch4_variants_sampled():
     _decode_full(w, [(0, 2), (2, 7)], Lcap=w.L, per_head=True)
 
 
+def test_decode_1m_batch4_router_fp8_sampled():
+    """The 1M-token decode at batch 4 with 8-bit router keys, after one
+    appended token (so the append writes the copy of the nodes it
+    completes); sampled units, the copy bit for bit, routing and output
+    against the oracle's 8-bit routing."""
+    w = W.DEC1M
+    _decode_full(w, [(0, 1), (3, 4)], Lcap=w.L + 4, append_steps=1, router_fp8=True)
+
+
 def test_decode_zha_2m_topp_sampled():
     """2,097,152 tokens, b = 16, top-p 0.9 capped at 16 nodes, four reference
     keys per node; both KV groups checked."""
@@ -106,12 +122,22 @@ def test_decode_zha_2m_topp_sampled():
 def test_prefill_524k_block_sampled():
     """8192-token block over the 524,288-token prefix; block rows at both ends,
     the middle and a few seeded ones, in two KV groups."""
+    _prefill_full(router_fp8=False)
+
+
+def test_prefill_524k_block_router_fp8_sampled():
+    """The same block with 8-bit router keys (the walk and the matrix-core top
+    level score through the copy)."""
+    _prefill_full(router_fp8=True)
+
+
+def _prefill_full(router_fp8):
     w = W.PREFILL
     T = w.T
     log(f"full-size prefill {w.name}: L={w.L} T={T}")
     K, V = W.gen_kv(w, Lcap=w.L, device=DEV)
     refs = W.gen_refs(w)
-    ts = make_treeset(w, w.L, K, V, refs.to(DEV), T=T)
+    ts = make_treeset(w, w.L, K, V, refs.to(DEV), T=T, router_fp8=router_fp8)
     ts.tree_build([w.L] * w.B)
     qb, kb, vb = W.gen_block(w)
     sel = select_of(w)
@@ -129,13 +155,17 @@ def test_prefill_524k_block_sampled():
     nex, emax = 0, 0.0
     for g in (0, 5):
         Kh, Vh = _host(K[0, g, :w.L]), _host(V[0, g, :w.L])
-        tree = oracle_tree(w, Kh, Vh, refs[g], w.L)
+        if router_fp8:
+            router_copy_matches(ts, w, 0, g, w.L)
+            tree = oracle_tree_from_device(ts, w, 0, g, w.L)
+        else:
+            tree = oracle_tree(w, Kh, Vh, refs[g], w.L)
         bk = kb[0, :, g].float().numpy()
         bv = vb[0, :, g].float().numpy()
         hs = slice(g * w.G, (g + 1) * w.G)
         for t in rows:
             ex, err = accept(w, tree, Kh, Vh, qb[0, t, hs], out[0, t, hs], lse[0, t, hs], so[0, t, g],
-                             t=t, blk_k=bk, blk_v=bv)
+                             t=t, blk_k=bk, blk_v=bv, router_fp8=router_fp8)
             nex += ex
             emax = max(emax, err)
         log(f"  group {g}: {len(rows)} block rows, exempt so far {nex}, max_err {emax:.2e}")

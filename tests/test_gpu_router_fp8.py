@@ -9,7 +9,7 @@ import torch
 
 import hti_workloads as W
 import oracle
-from gpu_helpers import accept, kmax_of, log, make_treeset, select_of
+from gpu_helpers import accept, kmax_of, log, make_treeset, oracle_tree_from_device, select_of
 
 pytestmark = pytest.mark.gpu
 
@@ -52,17 +52,6 @@ def _check_copy(ts, w, Ls):
     return nodes
 
 
-def _oracle_tree_of(ts, w, bi, g, L):
-    """The oracle's tree with the GPU's stored levels (this file checks the
-    routing; the build is checked against the oracle's own build elsewhere)."""
-    tr = oracle.Tree(L, w.d, w.b, w.levels, w.R, True)
-    for l in range(w.levels):
-        n = tr.lk[l].shape[0]
-        tr.lk[l][...] = ts.lvl_k[l][bi, g, :n].float().cpu().numpy()
-        tr.lv[l][...] = ts.lvl_v[l][bi, g, :n].float().cpu().numpy()
-    return tr
-
-
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_router_copy_matches_oracle(w):
     log(f"router copy {w.name}: build, append, extend")
@@ -102,7 +91,7 @@ def test_decode_router_fp8(w, split):
     nex, emax, e0 = 0, 0.0, 0.0
     for bi in range(w.B):
         for g in range(w.Hkv):
-            tr = _oracle_tree_of(ts, w, bi, g, Ls[bi])
+            tr = oracle_tree_from_device(ts, w, bi, g, Ls[bi])
             for qi in range(q.shape[1]):
                 hs = slice(g * w.G, (g + 1) * w.G)
                 Kb, Vb = K[bi, g, : Ls[bi]], V[bi, g, : Ls[bi]]
@@ -141,7 +130,7 @@ def test_prefill_router_fp8(Hq, Hkv, R, k, levels, P0, T):
     nex, emax = 0, 0.0
     for bi in range(w.B):
         for g in range(w.Hkv):
-            tr = _oracle_tree_of(ts, w, bi, g, P0)
+            tr = oracle_tree_from_device(ts, w, bi, g, P0)
             bk = kb[bi, :, g].float().numpy()
             bv = vb[bi, :, g].float().numpy()
             for t in range(0, T, 3):

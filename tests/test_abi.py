@@ -149,3 +149,30 @@ def test_build_append_prefill_validation():
                                 0x10, 1 << 40, None) == -2
     assert L.hti_sparse_prefill(C.byref(t), C.byref(s), 0x10, 0x10, 0x10, 0, 0x10, None, None, 0,
                                 0x10, 1 << 40, None) == -1
+
+
+def test_router_fp8_cfg_and_buffers():
+    """8-bit router keys: planned sizes, bf16 caches only, 0/1 flag, and the
+    copies' buffers required before anything is enqueued."""
+    L = hti.lib()
+    c = cfg(rope_npos=288)
+    c.router_fp8 = 1
+    p = hti.plan(c, hti.make_select("topk", k=8))
+    assert p.lvl_kq_bytes[0] == 2 * 8 * 4096 * 128 and p.lvl_ks_bytes[0] == 2 * 8 * 4096 * 4
+    assert hti.plan(cfg(), None).lvl_kq_bytes[0] == 0
+    out = hti.PlanOut()
+    c_f32 = cfg(rope_npos=288)
+    c_f32.router_fp8 = 1
+    c_f32.dtype = hti.F32
+    assert L.hti_plan(C.byref(c_f32), None, 0, C.byref(out)) == -2
+    c_bad = cfg(rope_npos=288)
+    c_bad.router_fp8 = 2
+    assert L.hti_plan(C.byref(c_bad), None, 0, C.byref(out)) == -1
+    # the copies' buffers: missing ones are rejected by every call that needs the tree
+    t = _tree_struct(c)
+    s = hti.make_select("topk", k=8)
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, 1, 0x2000, None, None, 0, None, 0, None) == -1
+    Ls = (C.c_int64 * 2)(10, 10)
+    assert L.hti_tree_build(C.byref(t), Ls, None) == -1
+    assert L.hti_tree_append(C.byref(t), 0x3000, 0x3000, None) == -1
+    assert "router" in hti.last_error()

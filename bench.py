@@ -422,8 +422,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--prefill-reps", type=int, default=3)
-    ap.add_argument("--prefill-warmup", type=int, default=1)
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "all"], default="all")
     ap.add_argument("--no-variants", action="store_true",

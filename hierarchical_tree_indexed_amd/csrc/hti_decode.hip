@@ -1082,7 +1082,7 @@ static hipError_t dec_capacity_g(int G, int *per_cu)
 
 hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W)
 {
-    static int cached_key = -1, cached_cap = 0, cached_cap2 = 0;
+    static int cached_key = -1, cached_cus = 0, cached_per_cu = 0;
     const int key = a.t.dtype * 1000 + a.t.D * 10 + a.t.G;
     if (key != cached_key) {
         int dev = 0, cus = 0, per_cu = 0;
@@ -1095,15 +1095,18 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
             e = a.t.D == 128 ? dec_capacity_g<float, 128>(a.t.G, &per_cu) : dec_capacity_g<float, 64>(a.t.G, &per_cu);
         if (e != hipSuccess) return e;
         cached_key = key;
-        // one workgroup per CU keeps every unit's slices on distinct CUs;
-        // two per CU (when they fit) only where one per CU leaves too few
-        // workgroups for the unit's slices
-        cached_cap = cus * (per_cu < 1 ? 0 : 1);
-        cached_cap2 = cus * (per_cu < 2 ? (per_cu < 1 ? 0 : 1) : 2);
+        cached_cus = cus;
+        cached_per_cu = per_cu;
     }
+    // one workgroup per CU keeps every unit's slices on distinct CUs; more
+    // per CU (as many as fit, at most four) only where fewer leave a unit
+    // too few workgroups for its slices
     const int64_t need = (max_summary + kSlice - 1) / kSlice;
-    int64_t w = cached_cap / (units > 0 ? units : 1);
-    if (w < need) w = cached_cap2 / (units > 0 ? units : 1);
+    int64_t w = 0;
+    for (int per = 1; per <= std::min(cached_per_cu, 4); ++per) {
+        w = (int64_t)cached_cus * per / (units > 0 ? units : 1);
+        if (w >= need) break;
+    }
     if (w > kMaxW) w = kMaxW;
     *W = (w >= need && w >= 1 && need <= kMaxW) ? (int)w : 0;
     return hipSuccess;

@@ -1100,12 +1100,14 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
     }
     // one workgroup per CU keeps every unit's slices on distinct CUs; more
     // per CU (as many as fit, at most four) only where fewer leave a unit
-    // too few workgroups for its slices
+    // short of its slices or of eight workgroups (measured at 1M tokens:
+    // eight per unit beat four and sixteen)
     const int64_t need = (max_summary + kSlice - 1) / kSlice;
+    const int64_t want = std::max<int64_t>(need, 8);
     int64_t w = 0;
     for (int per = 1; per <= std::min(cached_per_cu, 4); ++per) {
         w = (int64_t)cached_cus * per / (units > 0 ? units : 1);
-        if (w >= need) break;
+        if (w >= want) break;
     }
     if (w > kMaxW) w = kMaxW;
     *W = (w >= need && w >= 1 && need <= kMaxW) ? (int)w : 0;

@@ -106,13 +106,14 @@ def test_decode_router_fp8(w, split):
     assert emax < e0     # the 8-bit keys were used
 
 
-@pytest.mark.parametrize("Hq,Hkv,R,k,levels,P0,T", [(32, 8, 1, 8, 2, 32 * 32 * 12 + 70, 70),
-                                                    (16, 8, 2, 8, 2, 32 * 32 * 5 + 31, 40),
-                                                    (32, 8, 1, 8, 3, 32 * 32 * 3 + 9, 33)])
-def test_prefill_router_fp8(Hq, Hkv, R, k, levels, P0, T):
+@pytest.mark.parametrize("Hq,Hkv,R,k,levels,P0,T,d", [(32, 8, 1, 8, 2, 32 * 32 * 12 + 70, 70, 128),
+                                                      (16, 8, 2, 8, 2, 32 * 32 * 5 + 31, 40, 128),
+                                                      (32, 8, 1, 8, 3, 32 * 32 * 3 + 9, 33, 128),
+                                                      (8, 2, 2, 4, 2, 32 * 32 * 9 + 17, 50, 64)])
+def test_prefill_router_fp8(Hq, Hkv, R, k, levels, P0, T, d):
     """Summary levels scored through the 8-bit copy in the prefill walk and in
-    the matrix-core scoring of the top level."""
-    w = W.PREFILL.replace(name="r8_pf", Hq=Hq, Hkv=Hkv, R=R, k=k, levels=levels, L=P0, T=T)
+    the matrix-core scoring of the top level (d = 128 and 64)."""
+    w = W.PREFILL.replace(name="r8_pf", Hq=Hq, Hkv=Hkv, R=R, k=k, levels=levels, L=P0, T=T, d=d)
     K, V = W.gen_kv(w, Lcap=P0)
     refs = W.gen_refs(w)
     ts = make_treeset(w, P0, K.to(DEV), V.to(DEV), refs.to(DEV), T=T, router_fp8=True)

@@ -190,6 +190,21 @@ def test_split_decode_matches_unsplit():
     assert np.abs(o1 - o2).max() < 1e-5 and np.abs(l1 - l2).max() < 1e-5
 
 
+@pytest.mark.parametrize("B,Nq", [(8, 1), (4, 4)])
+def test_decode_two_workgroups_per_cu(B, Nq):
+    """64 and 128 (query, group) units: one workgroup per CU would give each
+    unit fewer than eight (four and two), so the plan places two per CU.
+    Against the oracle, and against the one-workgroup-per-unit path."""
+    w = W.DEC128K.replace(name=f"two_per_cu_b{B}_nq{Nq}", L=40000 + 17, needles=0, B=B, Nq=Nq)
+    ts, K, V, refs, Ls = _setup(w)
+    q = W.gen_queries(w)
+    _check_decode(ts, w, K, V, refs, Ls, q, split=True)
+    o1, l1, s1 = _decode(ts, w, q, split=True)
+    o2, l2, s2 = _decode(ts, w, q, split=False)
+    assert np.array_equal(s1, s2)
+    assert np.abs(o1 - o2).max() < 1e-5 and np.abs(l1 - l2).max() < 1e-5
+
+
 @pytest.mark.parametrize("L,levels", [(1, 2), (5, 2), (31, 1), (32, 1), (33, 3), (1024, 2), (700, 0)])
 def test_decode_edge_lengths(L, levels):
     """Lengths below one node, exactly one node, a single top node, no tree."""

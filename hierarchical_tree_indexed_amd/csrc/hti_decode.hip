@@ -1025,9 +1025,10 @@ static hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t un
     DecodeWs ww = ws;
     void *args[] = {&aa, &ww};
     // A plain launch: the workgroups of a unit wait for each other, which
-    // needs them resident together.  The plan keeps the grid within one
-    // workgroup per compute unit, so they all are whenever the device is not
-    // held by other work; every wait is bounded and a timeout shows as NaN
+    // needs them resident together.  The plan keeps the grid within what the
+    // device holds at once (one workgroup per compute unit, or as many as the
+    // occupancy admits), so they all are whenever the device is not held by
+    // other work; every wait is bounded and a timeout shows as NaN
     // output (a cooperative launch would guarantee residency but costs more
     // than the whole kernel to dispatch).
     return hipLaunchKernel((const void *)kern, dim3((unsigned)(units * ws.W)), dim3(DNT), args, dyn, s);

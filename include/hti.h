@@ -222,9 +222,11 @@ size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel
  *        bytes, filled with zeros before its first use and then left to the
  *        library (it keeps per-unit launch counters there).  With a workspace
  *        each unit is split over up to HTI_DECODE_MAX_SPLIT workgroups that
- *        wait on each other's partial results; the grid is kept within one
- *        workgroup per compute unit so that all are resident while the
- *        device runs nothing else.  Every wait is bounded: if work on other
+ *        wait on each other's partial results; the grid is kept within what
+ *        the device holds at once (one workgroup per compute unit, or as many
+ *        as the kernel's occupancy admits, at most four, where one per CU
+ *        would leave a unit fewer than eight) so that all are resident while
+ *        the device runs nothing else.  Every wait is bounded: if work on other
  *        streams keeps some workgroups from starting in time, the affected
  *        outputs are NaN.  ws = NULL runs one independent workgroup per unit.
  *        One workspace serves one (cfg, Nq) shape and one stream at a time:

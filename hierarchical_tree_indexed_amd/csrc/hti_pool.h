@@ -14,7 +14,9 @@
 // rg + 4, ..., slice sub holds d/16 contiguous elements of each.  Dot
 // products reduce over the 16 lanes of a row group, the softmax and the
 // weighted sums over the 4 row groups (DPP within a row, lane-swap
-// instructions across rows: no LDS round trips).
+// instructions across rows: no LDS round trips).  With 8-bit router keys
+// every pooled key row is also written as E4M3 codes with a power-of-two row
+// scale, taken from its stored (cache-dtype) value.
 #pragma once
 
 #include "hti_device.h"

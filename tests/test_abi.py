@@ -176,3 +176,14 @@ def test_router_fp8_cfg_and_buffers():
     assert L.hti_tree_build(C.byref(t), Ls, None) == -1
     assert L.hti_tree_append(C.byref(t), 0x3000, 0x3000, None) == -1
     assert "router" in hti.last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says
+    why, before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and not r.stdout.strip()

@@ -11,6 +11,7 @@ passages each step follows and the readings taken where the pages are silent.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 import subprocess
@@ -62,16 +63,34 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        lib = C.CDLL(compile_oracle(force=False))
-        lib.orc_build.restype = C.c_int
-        lib.orc_build.argtypes = [C.c_long, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
-                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
-        lib.orc_query.restype = C.c_int
-        lib.orc_query.argtypes = [C.POINTER(_QArgs), C.POINTER(_QOut)]
-        lib.orc_router_fp8.restype = None
-        lib.orc_router_fp8.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
-        _lib = lib
+        _lib = _open(compile_oracle(force=False))
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route every call through another build of the oracle source for the
+    duration of the block (the mutation tests compile altered copies of
+    hti_oracle.c to show that a planted mistake turns a pin red)."""
+    global _lib
+    saved = _lib
+    _lib = _open(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _open(path: str):
+    lib = C.CDLL(path)
+    lib.orc_build.restype = C.c_int
+    lib.orc_build.argtypes = [C.c_long, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.orc_query.restype = C.c_int
+    lib.orc_query.argtypes = [C.POINTER(_QArgs), C.POINTER(_QOut)]
+    lib.orc_router_fp8.restype = None
+    lib.orc_router_fp8.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
+    return lib
 
 
 def _f32(x) -> np.ndarray:

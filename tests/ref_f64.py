@@ -10,7 +10,9 @@ is a *different* formulation of something the method reduces to:
 * the entry set E written as a predicate over *all* nodes ("a node is a
   candidate iff it is a top node, an orphan, or a child of a selected
   candidate"), not as the oracle's level-by-level candidate lists;
-* the shared softmax evaluated in float64 over that entry set.
+* the shared softmax evaluated in float64 over that entry set;
+* the tree's pooled keys and mean values as whole-level float64 array
+  operations (log-sum-exp weights), one chain of keys per reference query.
 """
 from __future__ import annotations
 
@@ -116,3 +118,35 @@ def softmax_over_entries(zs: np.ndarray, vals: np.ndarray):
     w = np.exp(zs - M)
     den = w.sum(axis=1, keepdims=True)
     return (w @ vals) / den, (M + np.log(den))[:, 0]
+
+
+def pool_tree_f64(K: np.ndarray, V: np.ndarray, refs: np.ndarray, b: int, levels: int, L: int | None = None):
+    """The tree's levels in float64, written as whole-level array operations.
+
+    Each reference query r_j pools its own chain of keys: level 1 pools the
+    token keys, level l >= 2 pools the level-(l-1) keys of that same
+    reference.  A node's weights are the softmax over its b children of
+    r_j . k_child / sqrt(d) (taken in the log domain: log-sum-exp with the
+    children's maximum), its key the weighted sum of the children's keys and
+    its value the plain mean of the children's values.  Only full nodes.
+    Returns [(keys [n_l, R, d], values [n_l, d]) for l = 1..levels].
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    refs = np.asarray(refs, np.float64)
+    L = K.shape[0] if L is None else L
+    R, d = refs.shape
+    keys = np.repeat(K[:L, None, :], R, axis=1)            # [n, R, d]: level 0, one chain per reference
+    vals = V[:L]
+    out = []
+    for _ in range(levels):
+        n = keys.shape[0] // b
+        ch = keys[: n * b].reshape(n, b, R, d)               # [node, child, ref, d]
+        logit = np.einsum("ncrd,rd->ncr", ch, refs) / np.sqrt(d)
+        lse = logit.max(axis=1, keepdims=True)
+        lse = lse + np.log(np.exp(logit - lse).sum(axis=1, keepdims=True))
+        w = np.exp(logit - lse)                              # [node, child, ref]
+        keys = np.einsum("ncr,ncrd->nrd", w, ch)
+        vals = vals[: n * b].reshape(n, b, d).mean(axis=1)
+        out.append((keys, vals))
+    return out

@@ -5,7 +5,16 @@ Each test names the pin it implements:
   P2 mean-pooled values    -> subtree means (closed form)
   P3 pooler closed forms   -> r = 0 gives the child mean, permutation invariance,
                               a dominant reference gives its argmax child,
-                              equal children give that child
+                              equal children give that child; children whose
+                              logits are ln 3, 0, 0, ln 2 pool with weights
+                              3/7, 1/7, 1/7, 2/7 exactly (the 1/sqrt(d)
+                              temperature, at three head sizes)
+  P3b per-reference chains -> every level of a tree with R distinct reference
+                              queries equals a float64 whole-level pooler in
+                              which each reference pools its own chain
+  P12 exact ties           -> top-k and top-p over exactly equal scores keep
+                              the lowest node indices; a node whose R keys
+                              tie takes the first reference's key
   P4 selection certificate -> brute force over all subsets / top-p mass rules
   P5 entries partition the visible tokens
   P6 entries read          -> exact count formula, linear in log_b L
@@ -29,8 +38,8 @@ import torch
 import oracle
 import hti_workloads as W
 from ref_f64 import (candidates_by_predicate, covered_tokens, dense_causal,
-                     entries_from_candidates, group_scores_f64, level_counts, rope_c,
-                     softmax_over_entries)
+                     entries_from_candidates, group_scores_f64, level_counts, pool_tree_f64,
+                     rope_c, softmax_over_entries)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -192,6 +201,175 @@ def test_pooler_closed_forms():
     rd = (60.0 * Kd[3] / np.linalg.norm(Kd[3]) ** 2 * np.sqrt(d)).astype(np.float32)[None]
     td = oracle.build_tree(Kd, V, rd, b, 1, bf16=False)
     assert np.abs(td.lk[0][0, 0] - Kd[3]).max() < 1e-4 * np.abs(Kd[3]).max()
+
+
+@pytest.mark.parametrize("d", [16, 36, 128])
+def test_pooler_temperature_closed_form(d):
+    """P3: the pooler's weights are softmax(r . k / sqrt(d)) over a node's
+    children.  Four children along orthogonal axes: child c = a_c e_c, and
+    the reference r = sum_c (lambda_c sqrt(d) / a_c) e_c, so that
+    r . k_c / sqrt(d) = lambda_c with lambda = (ln 3, 0, 0, ln 2).  The
+    weights are then 3/7, 1/7, 1/7, 2/7 and the pooled key is
+    (3 a_0 / 7, a_1 / 7, a_2 / 7, 2 a_3 / 7, 0, ...).  The three head sizes
+    tell the 1/sqrt(d) temperature from a missing, halved, doubled or
+    1/d one.  A second node repeats this with the children in another order,
+    and the level above pools the two (its logits are again checked against
+    the closed form)."""
+    b = 4
+    lam = np.array([np.log(3.0), 0.0, 0.0, np.log(2.0)])
+    amp = np.array([2.0, -1.5, 0.75, 3.0])
+    r = np.zeros(d)
+    for c in range(b):
+        r[c] = lam[c] * np.sqrt(d) / amp[c]
+    K = np.zeros((2 * b, d))
+    for c in range(b):
+        K[c, c] = amp[c]
+    order = [2, 0, 3, 1]                       # node 1: the same children permuted
+    K[b:] = K[order]
+    K32 = K.astype(np.float32)
+    V = np.zeros((2 * b, d), np.float32)
+    tr = oracle.build_tree(K32, V, r.astype(np.float32)[None], b, 1, bf16=False)
+    want = np.zeros(d)
+    wts = np.array([3.0, 1.0, 1.0, 2.0]) / 7.0
+    for c in range(b):
+        want[c] = wts[c] * amp[c]
+    for node in range(2):
+        got = tr.lk[0][node, 0].astype(np.float64)
+        assert np.abs(got - want).max() < 2e-6, (d, node, got[:4], want[:4])
+    # level 2 over two children given directly: logits ln 3 and 0 -> 3/4, 1/4
+    u0 = np.zeros(d)
+    u0[0] = 1.0
+    u1 = np.zeros(d)
+    u1[1] = 1.0
+    r2 = np.zeros(d)
+    r2[0] = np.log(3.0) * np.sqrt(d)
+    t2 = oracle.build_tree(np.stack([u0, u1]).astype(np.float32), np.zeros((2, d), np.float32),
+                           r2.astype(np.float32)[None], 2, 1, bf16=False)
+    assert abs(float(t2.lk[0][0, 0, 0]) - 0.75) < 1e-6 and abs(float(t2.lk[0][0, 0, 1]) - 0.25) < 1e-6
+
+
+@pytest.mark.parametrize("L,b,levels,R,d", [(4096 + 300, 4, 5, 3, 32), (2 * 32 ** 2 + 77, 32, 2, 4, 64),
+                                            (1000, 3, 6, 2, 16)])
+def test_pooler_per_reference_chains(L, b, levels, R, d):
+    """P3b: with R distinct reference queries every reference pools its own
+    chain -- level 1 from the tokens, level l >= 2 from its own level-(l-1)
+    keys -- against the float64 whole-level pooler, level by level; values
+    are the plain subtree means.  (A tree that pooled every chain with the
+    first reference, or fed level l a chain of another reference, differs
+    from it by far more than the fp32 rounding of its sums.)"""
+    K, V, rng = rand_kv(L, d, seed=L + R)
+    refs = (rng.standard_normal((R, d)) * (1.5 / np.sqrt(d))).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, levels, bf16=False)
+    ref = pool_tree_f64(K, V, refs, b, levels)
+    for l in range(levels):
+        rk, rv = ref[l]
+        scale = max(1.0, float(np.abs(rk).max()))
+        assert np.abs(tr.lk[l] - rk).max() < 1e-5 * scale * (l + 1), (l + 1, float(np.abs(tr.lk[l] - rk).max()))
+        assert np.abs(tr.lv[l] - rv).max() < 1e-5 * (l + 1)
+        # the chains really differ between references
+        if R > 1:
+            assert np.abs(rk[:, 0] - rk[:, 1]).max() > 1e-2
+    # bf16 storage: each level pools the stored (rounded) children; the
+    # float64 pooler fed the same rounded children one level at a time
+    tb = oracle.build_tree(bf16r(K), bf16r(V), refs, b, levels, bf16=True)
+    for l in range(levels):
+        if l == 0:
+            child = np.repeat(bf16r(K)[:, None, :], R, axis=1)
+        else:
+            child = tb.lk[l - 1]
+        n = child.shape[0] // b
+        for j in range(R):
+            one = pool_tree_f64(child[: n * b, j], np.zeros((n * b, d)), refs[j:j + 1], b, 1)[0][0][:, 0]
+            err = np.abs(tb.lk[l][:, j] - one)
+            # one bf16 rounding (half an ulp: 2^-9 relative) of an fp32 sum
+            assert (err <= 2.0 ** -8 * np.abs(one) + 1e-6).all(), (l + 1, j, float(err.max()))
+
+
+def _tied_setup(L, b, levels, R, d, seed):
+    """A tree with R distinct references, and a group of two query heads
+    q and -q: every per-head logit of head 1 is the exact negative of head
+    0's (rotation commutes with negation), so every group score is exactly 0
+    and every level ties throughout, across nodes and across references."""
+    K, V, rng = rand_kv(L, d, seed=seed)
+    refs = (rng.standard_normal((R, d)) / np.sqrt(d)).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, levels, bf16=False)
+    q0 = rng.standard_normal(d).astype(np.float32)
+    q = np.stack([q0, -q0])
+    return tr, K, V, q
+
+
+def _expected_tied_selection(L, b, levels, count):
+    """Selections under exact ties with the lower-index rule: at each level the
+    `count(m)` lowest node ids among the candidates."""
+    sel = [set() for _ in range(levels + 1)]
+    n = level_counts(L, b, levels)
+    cand = list(range(n[levels]))
+    for l in range(levels, 0, -1):
+        keep = sorted(cand)[: count(len(cand))]
+        sel[l] = set(keep)
+        orph = list(range(b * n[l], n[l - 1]))
+        cand = [c * b + i for c in sorted(keep) for i in range(b)] + orph
+    return sel
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+def test_exact_ties_topk(R):
+    """P12: all group scores exactly equal; top-k keeps the k lowest node ids
+    at every level (reading: ties go to the lower index), and the output is
+    the float64 shared softmax in which every node takes its first
+    reference's key (reading: ties across references go to the lower j)."""
+    L, b, levels, d, k = 4 ** 5 + 37, 4, 5, 16, 3
+    tr, K, V, q = _tied_setup(L, b, levels, R, d, seed=70 + R)
+    r = oracle.query(tr, K, V, q, k=k, entries=True)
+    want = _expected_tied_selection(L, b, levels, lambda m: min(k, m))
+    assert sel_sets(r, levels)[1:] == want[1:]
+    # output under that selection, with key j* = 0 for every summary entry
+    cands = candidates_by_predicate(L, b, levels, want)
+    zs, vals = [], []
+    for l in range(levels, 0, -1):
+        C = cands[l]
+        uns = [i for i, x in enumerate(C) if x not in want[l]]
+        keys0 = tr.lk[l - 1][C][:, 0]                       # the first reference's key
+        kr = rope_c(keys0, np.arange(len(C)))
+        zz = rope_c(q, len(C)) @ kr.T / np.sqrt(d)
+        zs.append(zz[:, uns])
+        vals.append(tr.lv[l - 1][[C[i] for i in uns]].astype(np.float64))
+    C0 = cands[0]
+    kr = rope_c(K[C0], np.arange(len(C0)))
+    qp = sum(1 for x in C0 if x < L - 1)
+    zs.append(rope_c(q, qp) @ kr.T / np.sqrt(d))
+    vals.append(V[C0].astype(np.float64))
+    out, lse = softmax_over_entries(np.concatenate(zs, axis=1), np.concatenate(vals))
+    assert np.abs(r["out"] - out).max() < 2e-5
+    assert np.abs(r["lse"] - lse).max() < 2e-5
+    # every scored level's gap at the boundary is exactly zero (the acceptance
+    # rule exempts such levels); a level taken whole has none
+    fin = np.isfinite(r["gap"])
+    assert fin.sum() >= levels - 1 and (r["gap"][fin] == 0).all()
+
+
+@pytest.mark.parametrize("p,cap", [(0.3, 16), (0.5, 2), (0.9, 16)])
+def test_exact_ties_topp(p, cap):
+    """P12 for top-p: with every score equal, each candidate has softmax mass
+    1/m, so the kept count is the smallest n with n/m >= p (clamped to
+    [1, cap]) and the kept nodes are the n lowest ids."""
+    L, b, levels, d = 4 ** 4 + 9, 4, 4, 16
+    tr, K, V, q = _tied_setup(L, b, levels, 2, d, seed=91)
+
+    def count(m):
+        if m <= 1:
+            return m
+        n = next(i for i in range(1, m + 1) if i / m >= np.float32(p))
+        if m & (m - 1) and n - 1 < cap:
+            # 1/m is inexact in fp32: no running sum may sit near p (unless
+            # the cap decides the count either way)
+            assert min(abs(i / m - p) for i in range(1, m + 1)) > 1e-4
+        # (m a power of two: 1/m and its running sums are exact in fp32)
+        return max(1, min(cap, n))
+
+    r = oracle.query(tr, K, V, q, mode="topp", p=p, cap=cap)
+    want = _expected_tied_selection(L, b, levels, count)
+    assert sel_sets(r, levels)[1:] == want[1:]
 
 
 def test_bf16_node_rounding_is_rne():

@@ -381,40 +381,208 @@ def copy_calibration():
     log(f"[copy] 5 copies of {n} bytes")
 
 
+def measure_floors():
+    """On-device floors from the probe library (hti_probe.hip): dependent-load
+    latency in L2, in the memory-side cache and in HBM; the one-way latency of
+    an exchange between two workgroups through agent-scope atomics (same and
+    different XCD); streaming read and copy bandwidth; bf16 matrix-core
+    throughput.  These are the measured peaks the roofline fractions are also
+    given against."""
+    import ctypes as C
+    path = os.path.join(ROOT, "hierarchical_tree_indexed_amd", "libhti_probe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python hierarchical_tree_indexed_amd/build.py`")
+    P = C.CDLL(path)
+    vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    P.hti_probe_wallclock_khz.argtypes = [vp]
+    P.hti_probe_chase.argtypes = [vp, C.c_uint32, i32, i32, vp, vp]
+    P.hti_probe_pingpong.argtypes = [vp, i32, i32, vp, vp]
+    P.hti_probe_read.argtypes = [vp, i64, vp, i32, vp]
+    P.hti_probe_mfma.argtypes = [vp, i32, i32, vp]
+    khz = C.c_int(0)
+    assert P.hti_probe_wallclock_khz(C.byref(khz)) == 0 and khz.value > 0
+    tick_ns = 1e6 / khz.value
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(2, dtype=torch.int64, device=DEV)
+    res = {"wallclock_khz": khz.value, "cus": cus}
+
+    def chain(nbytes):
+        lines = nbytes // 128
+        perm = torch.randperm(lines, device=DEV)
+        buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+        buf.view(lines, 32)[perm, 0] = (torch.roll(perm, -1) * 32).to(torch.int32)
+        return buf, int(perm[0].item()) * 32, lines
+
+    def chase(buf, start, steps, coherent=0):
+        assert P.hti_probe_chase(buf.data_ptr(), start, steps, coherent, out.data_ptr(), stream) == 0
+        torch.cuda.synchronize()
+        return out[0].item() * tick_ns / steps
+
+    steps = 20000
+    for name, nbytes, warm in (("l2_hit", 1 << 20, True), ("mall_hit", 64 << 20, True),
+                               ("hbm_1gib", 1 << 30, False), ("hbm_8gib", 8 << 30, False)):
+        buf, start, lines = chain(nbytes)
+        if warm:
+            chase(buf, start, lines)
+        res[f"chase_ns_{name}"] = chase(buf, start, steps)
+        if name == "l2_hit":
+            res["chase_ns_l2_agent_scope"] = chase(buf, start, steps, coherent=1)
+        del buf
+        torch.cuda.empty_cache()
+    log(f"[floors] dependent loads (ns): " + ", ".join(f"{k[9:]} {v:.0f}" for k, v in res.items()
+                                                       if k.startswith("chase_ns_")))
+    flags = torch.zeros(64, dtype=torch.int32, device=DEV)
+    for name, other in (("same_xcd", 8), ("other_xcd", 1)):
+        flags.zero_()
+        iters = 2000
+        assert P.hti_probe_pingpong(flags.data_ptr(), iters, other, out.data_ptr(), stream) == 0
+        torch.cuda.synchronize()
+        assert out[1].item() == 0, "ping-pong poll ran out"
+        res[f"exchange_ns_{name}"] = out[0].item() * tick_ns / iters / 2
+    log(f"[floors] one-way exchange (ns): same XCD {res['exchange_ns_same_xcd']:.0f}, "
+        f"other XCD {res['exchange_ns_other_xcd']:.0f}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nbytes = 8 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device=DEV).fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    best = float("inf")
+    for _ in range(4):
+        e0.record()
+        assert P.hti_probe_read(a.data_ptr(), nbytes, sink.data_ptr(), cus * 8, stream) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    res["read_gbs"] = nbytes / (best / 1e3) / 1e9
+    half = nbytes // 2
+    best = float("inf")
+    for _ in range(4):
+        e0.record()
+        a[half:].copy_(a[:half])
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    res["copy_gbs"] = 2 * half / (best / 1e3) / 1e9
+    del a
+    torch.cuda.empty_cache()
+    fsink = torch.zeros(1, dtype=torch.float32, device=DEV)
+    blocks, iters = cus * 8, 20000
+    best = float("inf")
+    for _ in range(3):
+        e0.record()
+        assert P.hti_probe_mfma(fsink.data_ptr(), blocks, iters, stream) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    flop = blocks * 4 * iters * 4 * 2 * 32 * 32 * 16
+    res["mfma_bf16_tflops"] = flop / (best / 1e3) / 1e12
+    log(f"[floors] read {res['read_gbs']:.0f} GB/s, copy {res['copy_gbs']:.0f} GB/s, "
+        f"bf16 MFMA {res['mfma_bf16_tflops']:.0f} TFLOP/s")
+    return res
+
+
+def host_info():
+    """CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return dict(cpu_model=model, nproc=usable, cpu_count=os.cpu_count())
+
+
 def cpu_baseline(args):
-    """The oracle, as it stands, on a bounded sample of the decode workload."""
-    import numpy as np
+    """The oracle, as it stands, on bounded samples of the timed workloads.
+
+    Decode (the headline unit): queries of one 1,048,576-token sequence over
+    2 of its 8 KV groups, timed single-threaded and then with one oracle call
+    per (query, group) on a pool of threads (the oracle's C calls release the
+    interpreter lock), each scaled to all 8 groups.  Also the oracle's tree
+    build over one (sequence, KV head), and rows of the 8192-token prefill
+    block over the 524,288-token prefix (tree build untimed there)."""
+    import concurrent.futures as cf
 
     import oracle
+    hinfo = host_info()
+    threads = max(1, min(16, hinfo["nproc"]))
     w = W.DEC1M
     groups = (0, 1)
-    nq = 4
-    log("[cpu] building oracle trees for 2 KV heads of one 1M-token sequence (untimed)")
+    log("[cpu] oracle trees for 2 KV heads of one 1M-token sequence")
     K, V = gen_kv_device(w.replace(B=1), w.L)
     refs = W.gen_refs(w)
-    trees = {}
-    data = {}
+    trees, data = {}, {}
+    build_s = []
     for g in groups:
         Kh = K[0, g].float().cpu().numpy()
         Vh = V[0, g].float().cpu().numpy()
+        t0 = time.perf_counter()
         trees[g] = oracle.build_tree(Kh, Vh, refs[g], w.b, w.levels, bf16=True)
+        build_s.append(time.perf_counter() - t0)
         data[g] = (Kh, Vh)
     del K, V
-    # as many queries as fit about ten seconds (at least four)
     gen = torch.Generator().manual_seed(7)
-    budget_s, nq, el = 10.0, 0, 0.0
-    while nq < 4 or (el < budget_s and nq < 100000):
+
+    def one(q, g):
+        oracle.query(trees[g], data[g][0], data[g][1], q[g * w.G:(g + 1) * w.G], k=w.k)
+
+    # single thread: as many queries as fit about eight seconds (at least four)
+    budget_s, nq1, el1 = 8.0, 0, 0.0
+    while nq1 < 4 or (el1 < budget_s and nq1 < 100000):
         q = torch.randn((w.Hq, w.d), generator=gen).to(torch.bfloat16).float().numpy()
         t0 = time.perf_counter()
         for g in groups:
-            oracle.query(trees[g], data[g][0], data[g][1], q[g * w.G:(g + 1) * w.G], k=w.k)
-        el += time.perf_counter() - t0
-        nq += 1
-    per_query = el / nq * (w.Hkv / len(groups))       # all 8 groups of one query
-    return dict(value=1.0 / per_query, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{nq} decode queries x {len(groups)} of {w.Hkv} KV groups of one "
-                       f"1,048,576-token sequence ({el:.1f} s), time scaled x{w.Hkv // len(groups)} "
-                       f"to all groups; tree build untimed; single thread")
+            one(q, g)
+        el1 += time.perf_counter() - t0
+        nq1 += 1
+    qps1 = nq1 / el1 / (w.Hkv / len(groups))
+    # a pool of threads over (query, group) units, for about eight seconds
+    nqt = max(4, int(round(qps1 * (w.Hkv / len(groups)) * budget_s * threads * 0.8)))
+    qs = [torch.randn((w.Hq, w.d), generator=gen).to(torch.bfloat16).float().numpy() for _ in range(nqt)]
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda u: one(qs[u[0]], u[1]), [(i, g) for i in range(nqt) for g in groups]))
+    elt = time.perf_counter() - t0
+    qpst = nqt / elt / (w.Hkv / len(groups))
+    # prefill block rows over the 524,288-token prefix (two groups)
+    wp = W.PREFILL
+    Kp, Vp = gen_kv_device(wp, wp.L)
+    qb, kb, vb = W.gen_block(wp)
+    rows = [0, wp.T // 2, wp.T - 1]
+    refsp = W.gen_refs(wp)
+    pre_el, pre_n = 0.0, 0
+    for g in groups:
+        Kh = Kp[0, g].float().cpu().numpy()
+        Vh = Vp[0, g].float().cpu().numpy()
+        tr = oracle.build_tree(Kh, Vh, refsp[g], wp.b, wp.levels, bf16=True)
+        bk, bv = kb[0, :, g].float().numpy(), vb[0, :, g].float().numpy()
+        for t in rows:
+            t0 = time.perf_counter()
+            oracle.query(tr, Kh, Vh, qb[0, t, g * wp.G:(g + 1) * wp.G], k=wp.k, t=t, blk_k=bk, blk_v=bv)
+            pre_el += time.perf_counter() - t0
+            pre_n += 1
+    del Kp, Vp
+    pre_row_s = pre_el / pre_n                                     # one (row, group)
+    pre_block_s_1t = pre_row_s * wp.T * wp.Hkv
+    return dict(value=qpst, unit="queries/s", cores=threads, kind="oracle",
+                sample=(f"decode: {nqt} queries x {len(groups)} of {w.Hkv} KV groups of one 1,048,576-token "
+                        f"sequence on {threads} threads ({elt:.1f} s) and {nq1} queries on one thread "
+                        f"({el1:.1f} s), each scaled x{w.Hkv // len(groups)} to all groups; tree build "
+                        f"timed apart; prefill: {pre_n} (row, group) units of the 8192-token block, "
+                        f"scaled to the block"),
+                single_thread_qps=qps1, threads=threads,
+                build_s_per_head_1m=sum(build_s) / len(build_s),
+                build_s_all_heads_1m_b4_est=sum(build_s) / len(build_s) * w.B * w.Hkv,
+                prefill_s_per_row_group=pre_row_s,
+                prefill_block_s_one_thread_est=pre_block_s_1t,
+                prefill_block_tokens_per_s_one_thread_est=wp.T / pre_block_s_1t,
+                **hinfo)
 
 
 def main():
@@ -428,6 +596,9 @@ def main():
     ap.add_argument("--only", choices=["decode", "prefill", "all"], default="all")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the per-head-routing and leaf-only timings (profiled runs of the main step)")
+    ap.add_argument("--floors", action="store_true",
+                    help="only measure the on-device floors (latency, exchange, bandwidth, matrix-core peak)")
+    ap.add_argument("--no-floors", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -439,6 +610,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.floors:
+        print(json.dumps(measure_floors()), flush=True)
         return
     hti.lib()
     dec = bench_decode(args) if args.only in ("decode", "all") else None

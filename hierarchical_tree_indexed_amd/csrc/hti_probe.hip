@@ -1,0 +1,159 @@
+// hti_probe.hip -- on-device measurements of the floors the decode and
+// prefill kernels are judged against (built as its own library,
+// libhti_probe.so; the attention library does not use it):
+//
+//   * dependent-load latency: one lane follows a chain of indices through a
+//     buffer, each load's address taken from the previous load's value, so
+//     the loads cannot overlap; buffer size and the warm-up decide whether
+//     the chain hits in L2, in the memory-side cache or in HBM;
+//   * exchange latency between two workgroups: a flag passed back and forth
+//     with the same agent-scope relaxed atomic stores and polling loads the
+//     split decode uses for its exchanges;
+//   * read bandwidth: every workgroup streams 16-byte loads over a buffer;
+//   * bf16 matrix-core throughput: every wave issues independent chains of
+//     32x32x16 bf16 products on registers.
+//
+// Times are read from the 100 MHz constant-rate counter (s_memrealtime),
+// whose rate hti_probe_wallclock_khz reports.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr long kSpinMax = 1L << 20;      // polls of one flag (about a second)
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// One lane: steps dependent loads from buf[start]; coherent: agent-scope
+// atomic loads (the form of the decode exchange's polls) instead of plain
+// loads.  out[0] = ticks of the timed chain, out[1] = the last index (keeps
+// the chain live).
+__global__ void k_chase(const uint32_t *buf, uint32_t start, int steps, int coherent, uint64_t *out)
+{
+    if (threadIdx.x != 0) return;
+    uint32_t p = start;
+    const uint64_t t0 = now_ticks();
+    if (coherent) {
+        for (int i = 0; i < steps; ++i)
+            p = __hip_atomic_load(buf + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        for (int i = 0; i < steps; ++i) p = buf[p];
+    }
+    const uint64_t t1 = now_ticks();
+    out[0] = t1 - t0;
+    out[1] = p;
+}
+
+// Two active workgroups, ping (block 0) and pong (block `other`), pass a
+// counter through flags[0] (ping -> pong) and flags[32] (pong -> ping), each
+// write an agent-scope relaxed atomic store, each read a polling agent-scope
+// atomic load.  Blocks other than 0 and `other` exit at once.  Every poll is
+// bounded: out[0] = ticks for `iters` round trips, out[1] = 1 if a poll ran
+// out (the measurement is then void).
+__global__ void k_pingpong(uint32_t *flags, int iters, int other, uint64_t *out)
+{
+    const int bid = (int)blockIdx.x;
+    if ((bid != 0 && bid != other) || threadIdx.x != 0) return;
+    uint32_t *to_pong = flags, *to_ping = flags + 32;
+    int bad = 0;
+    if (bid == 0) {
+        const uint64_t t0 = now_ticks();
+        for (int i = 1; i <= iters && !bad; ++i) {
+            __hip_atomic_store(to_pong, (uint32_t)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            long s = 0;
+            while (__hip_atomic_load(to_ping, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)i)
+                if (++s > kSpinMax) { bad = 1; break; }
+        }
+        const uint64_t t1 = now_ticks();
+        out[0] = t1 - t0;
+        out[1] = (uint64_t)bad;
+    } else {
+        for (int i = 1; i <= iters && !bad; ++i) {
+            long s = 0;
+            while (__hip_atomic_load(to_pong, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)i)
+                if (++s > kSpinMax) { bad = 1; break; }
+            __hip_atomic_store(to_ping, (uint32_t)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (bad) out[1] = 1;
+    }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Grid-stride 16-byte loads over n16 chunks, folded into one word per thread.
+__global__ void k_read(const u32x4 *buf, int64_t n16, uint32_t *sink)
+{
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(buf + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;      // practically never; keeps the loads
+}
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// Four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave
+// (32 * 32 * 16 * 2 FLOP each).
+__global__ __launch_bounds__(256) void k_mfma(float *sink, int iters)
+{
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (short)(0x3f80 + ((threadIdx.x + i) & 7));
+        b[i] = (short)(0x3f80 + ((threadIdx.x * 3 + i) & 7));
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+    if (s == 1.2345f) sink[0] = s;               // practically never; keeps the products
+}
+
+} // namespace
+
+extern "C" {
+
+int hti_probe_wallclock_khz(int *khz)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    return hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess ? 0 : -1;
+}
+
+int hti_probe_chase(const void *buf, uint32_t start, int32_t steps, int32_t coherent, uint64_t *out,
+                    hipStream_t s)
+{
+    if (!buf || !out || steps < 1) return -1;
+    hipLaunchKernelGGL(k_chase, dim3(1), dim3(64), 0, s, (const uint32_t *)buf, start, steps, coherent, out);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int hti_probe_pingpong(uint32_t *flags, int32_t iters, int32_t other_block, uint64_t *out, hipStream_t s)
+{
+    if (!flags || !out || iters < 1 || other_block < 1 || other_block > 255) return -1;
+    hipLaunchKernelGGL(k_pingpong, dim3(other_block + 1), dim3(64), 0, s, flags, iters, other_block, out);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int hti_probe_read(const void *buf, int64_t bytes, uint32_t *sink, int32_t blocks, hipStream_t s)
+{
+    if (!buf || !sink || bytes < 16 || blocks < 1) return -1;
+    hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, s, (const u32x4 *)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int hti_probe_mfma(float *sink, int32_t blocks, int32_t iters, hipStream_t s)
+{
+    if (!sink || blocks < 1 || iters < 1) return -1;
+    hipLaunchKernelGGL(k_mfma, dim3(blocks), dim3(256), 0, s, sink, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+} // extern "C"

@@ -94,6 +94,65 @@ def test_decode_1m_batch4_sampled():
     _decode_full(w, [(0, 0), (1, 5), (2, 2), (3, 7)], Lcap=w.L + 4, append_steps=1)
 
 
+def test_decode_step_1m_batch4_benched_config():
+    """The step the benchmark times, in its configuration: 1,048,575 cached
+    tokens x 4 sequences (16 planted needles each), then two decode_step
+    calls (the append and the split decode in one launch).  The first
+    appended token completes a node at every level (1,048,576 = 32^4), the
+    second completes none.  After each step: output, lse, selections,
+    lengths, cache rows and every level bit for bit against tree_append +
+    sparse_decode on a second tree set; sampled units against the oracle's
+    own tree, built from the grown cache rows."""
+    w = W.DEC1M
+    L0 = w.L - 1
+    Lcap = L0 + 2
+    log(f"decode_step at the benched configuration: B={w.B} L={L0}+2 levels={w.levels}")
+    K, V = W.gen_kv(w.replace(L=L0), Lcap=Lcap, device=DEV)
+    q0 = W.gen_queries(w)
+    W.plant_needles(w.replace(L=L0), K, q0)
+    refs = W.gen_refs(w)
+    ta = make_treeset(w, Lcap, K, V, refs.to(DEV))
+    tb = make_treeset(w, Lcap, K.clone(), V.clone(), refs.to(DEV))
+    ta.tree_build([L0] * w.B)
+    tb.tree_build([L0] * w.B)
+    sel = select_of(w)
+    kmax = kmax_of(w)
+    shape = (w.B, 1, w.Hq, w.d)
+    oa, ob = (torch.empty(shape, dtype=torch.float32, device=DEV) for _ in range(2))
+    la, lb = (torch.empty(shape[:3], dtype=torch.float32, device=DEV) for _ in range(2))
+    sa, sb = (torch.empty((w.B, 1, w.Hkv, w.levels, kmax), dtype=torch.int32, device=DEV) for _ in range(2))
+    units = [(0, 0), (1, 5), (2, 2), (3, 7)]
+    for s in range(2):
+        kn, vn = W.gen_append(w, s, device=DEV)
+        q = (q0 if s == 0 else W.gen_queries(w, step=s)).to(DEV).contiguous()
+        ta.decode_step(sel, kn.contiguous(), vn.contiguous(), q, oa, la, sa)
+        tb.tree_append(kn.contiguous(), vn.contiguous())
+        tb.sparse_decode(sel, q, ob, lb, sb)
+        torch.cuda.synchronize()
+        L = L0 + s + 1
+        assert ta.len.cpu().tolist() == [L] * w.B and torch.equal(ta.len, tb.len)
+        assert torch.equal(oa, ob), f"step {s}: max diff {(oa - ob).abs().max().item()}"
+        assert torch.equal(la, lb) and torch.equal(sa, sb), s
+        assert torch.equal(ta.k_cache[:, :, L - 1], tb.k_cache[:, :, L - 1])
+        assert torch.equal(ta.v_cache[:, :, L - 1], tb.v_cache[:, :, L - 1])
+        for l in range(w.levels):
+            assert torch.equal(ta.lvl_k[l], tb.lvl_k[l]) and torch.equal(ta.lvl_v[l], tb.lvl_v[l]), (s, l)
+        if s == 0:
+            # the top node exists now: a kept top level of one node
+            assert (sa[:, 0, :, w.levels - 1, 0] == 0).all()
+        out, lse, so = oa.cpu().numpy(), la.cpu().numpy(), sa.cpu().numpy()
+        nex, emax = 0, 0.0
+        for bi, g in units:
+            Kh, Vh = ta.k_cache[bi, g, :L].cpu(), ta.v_cache[bi, g, :L].cpu()
+            tree = oracle_tree(w, Kh, Vh, refs[g], L)
+            hs = slice(g * w.G, (g + 1) * w.G)
+            ex, err = accept(w, tree, Kh, Vh, q.cpu()[bi, 0, hs], out[bi, 0, hs], lse[bi, 0, hs], so[bi, 0, g])
+            nex += ex
+            emax = max(emax, err)
+            log(f"  step {s} unit (seq {bi}, group {g}): exempt so far {nex}, max_err {emax:.2e}")
+        assert np.isfinite(out).all()
+
+
 def test_decode_1m_batch4_variants_sampled():
     """The 1M-token decode at batch 4 under leaf-only dispatch and under
     per-query-head routing; sampled units (every query head of them for the

@@ -381,6 +381,67 @@ def copy_calibration():
     log(f"[copy] 5 copies of {n} bytes")
 
 
+PHASES = {1: "entry", 2: "length and query read", 3: "first gathers issued", 4: "scored (B1)",
+          5: "slice ranked (B2)", 6: "slice published", 7: "exchange read (B3)", 8: "exchange ranked (B4)",
+          9: "kept set known", 10: "next gathers issued", 11: "level folded", 12: "tokens scored",
+          13: "tokens folded", 14: "partial published", 15: "partials gathered", 16: "output written"}
+
+
+def decode_timeline(args):
+    """Phase timeline of the split decode step on the headline workload, from
+    the timeline build of the library (libhti_timeline.so, the kernel with
+    clock readings at each phase boundary): per phase, the median over
+    workgroups and steps of the time since the launch's first workgroup
+    started, in microseconds."""
+    import numpy as np
+    hti.LIB_PATH = os.path.join(ROOT, "hierarchical_tree_indexed_amd", "libhti_timeline.so")
+    hti.lib()
+    w = W.DEC1M
+    nst = 40
+    Lcap = w.L + nst + 8
+    K, V = gen_kv_device(w, Lcap)
+    q0 = W.gen_queries(w, 0, device=DEV)
+    W.plant_needles(w, K, q0)
+    ts, sel = treeset(w, Lcap, K, V)
+    ts.tree_build([w.L] * w.B)
+    dt = W.TORCH_DTYPE[w.dtype]
+    gq = torch.Generator(device=DEV)
+    gq.manual_seed(12345)
+    qs = torch.randn((nst, w.B, 1, w.Hq, w.d), generator=gq, device=DEV).to(dt)
+    ak = torch.randn((nst, w.B, w.Hkv, w.d), generator=gq, device=DEV).to(dt)
+    av = torch.randn((nst, w.B, w.Hkv, w.d), generator=gq, device=DEV).to(dt)
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    ws = ts.decode_workspace(sel, 1)
+    tl = ws[256: 256 + 8192 * 64 * 8].view(torch.int64).view(8192, 64)
+    samples = {}
+    ends = []
+    for s in range(nst):
+        ts.decode_step(sel, ak[s], av[s], qs[s], out)
+        torch.cuda.synchronize()
+        if s < 8:
+            continue
+        ev = tl.cpu().numpy()
+        used = ev[(ev[:, 0] != 0)]
+        t0 = (used[:, 0] & ((1 << 48) - 1)).min()
+        for row in used:
+            for e in row:
+                if e == 0:
+                    break
+                ph, lv, tk = int(e >> 52), int((e >> 48) & 15), int(e & ((1 << 48) - 1))
+                samples.setdefault((ph, lv), []).append((tk - t0) * 0.01)      # 100 MHz ticks -> us
+        ends.append(((used & ((1 << 48) - 1)).max() - t0) * 0.01)
+    rows = []
+    for (ph, lv), v in sorted(samples.items(), key=lambda kv: np.median(kv[1])):
+        rows.append(dict(phase=PHASES.get(ph, str(ph)), level=lv, median_us=float(np.median(v)),
+                         p10_us=float(np.percentile(v, 10)), p90_us=float(np.percentile(v, 90)), n=len(v)))
+    res = dict(workload=w.name, steps=nst - 8, kernel_span_us_median=float(np.median(ends)), phases=rows)
+    for r in rows:
+        log(f"[timeline] {r['median_us']:7.2f} us (p10 {r['p10_us']:6.2f}, p90 {r['p90_us']:6.2f})  "
+            f"level {r['level']}  {r['phase']}")
+    log(f"[timeline] kernel span (first entry to last event) median {res['kernel_span_us_median']:.2f} us")
+    return res
+
+
 def measure_floors():
     """On-device floors from the probe library (hti_probe.hip): dependent-load
     latency in L2, in the memory-side cache and in HBM; the one-way latency of
@@ -599,6 +660,8 @@ def main():
     ap.add_argument("--floors", action="store_true",
                     help="only measure the on-device floors (latency, exchange, bandwidth, matrix-core peak)")
     ap.add_argument("--no-floors", action="store_true")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only the phase timeline of the decode step (timeline build of the library)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -613,6 +676,9 @@ def main():
         return
     if args.floors:
         print(json.dumps(measure_floors()), flush=True)
+        return
+    if args.timeline:
+        print(json.dumps(decode_timeline(args)), flush=True)
         return
     hti.lib()
     dec = bench_decode(args) if args.only in ("decode", "all") else None

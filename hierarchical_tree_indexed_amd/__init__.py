@@ -24,10 +24,10 @@ F32, BF16 = 0, 1
 TOPK, TOPP = 0, 1
 
 STATUS = {0: "HTI_OK", -1: "HTI_ERR_INVALID_ARG", -2: "HTI_ERR_UNSUPPORTED",
-          -3: "HTI_ERR_CAPACITY", -4: "HTI_ERR_WORKSPACE", -5: "HTI_ERR_LAUNCH"}
+          -3: "HTI_ERR_CAPACITY", -4: "HTI_ERR_WORKSPACE", -5: "HTI_ERR_LAUNCH", -6: "HTI_ERR_TIMEOUT"}
 
 EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append", "hti_tree_extend",
-           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_decode_step",
+           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_decode_status", "hti_decode_step",
            "hti_prefill_workspace_bytes", "hti_sparse_prefill", "hti_last_error"]
 
 
@@ -82,7 +82,8 @@ def lib() -> C.CDLL:
             "hti_tree_append": (C.c_int, [vp, vp, vp, vp]),
             "hti_tree_extend": (C.c_int, [vp, vp, vp, i32, vp]),
             "hti_decode_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
-            "hti_sparse_decode": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
+            "hti_sparse_decode": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
+            "hti_decode_status": (C.c_int, [vp, C.c_size_t, vp]),
             "hti_decode_step": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
             "hti_prefill_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
             "hti_sparse_prefill": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp,
@@ -210,15 +211,24 @@ class TreeSet:
         return ws
 
     def sparse_decode(self, sel: Select, q: torch.Tensor, out: torch.Tensor, lse=None,
-                      sel_out=None, stream=None, split: bool = True):
+                      sel_out=None, stream=None, split: bool = True, q_pos: torch.Tensor | None = None):
+        """q_pos: [B, Nq] int64 query positions (None: every query at len - 1)."""
         B, Nq, Hq, d = q.shape
         assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        if q_pos is not None:
+            assert q_pos.dtype == torch.int64 and q_pos.is_contiguous() and tuple(q_pos.shape) == (B, Nq)
         stride = 0 if sel_out is None else sel_out.shape[-1]
         ws = self.decode_workspace(sel, Nq) if split else None
         nbytes = 0 if ws is None else ws.numel()
-        _check(lib().hti_sparse_decode(C.byref(self.c), C.byref(sel), _ptr(q), Nq, _ptr(out),
+        _check(lib().hti_sparse_decode(C.byref(self.c), C.byref(sel), _ptr(q), _ptr(q_pos), Nq, _ptr(out),
                                        _ptr(lse), _ptr(sel_out), stride, _ptr(ws), nbytes,
                                        _stream(stream)))
+
+    def decode_status(self, sel: Select, Nq: int, stream=None):
+        """Raise HTIError(HTI_ERR_TIMEOUT) if a split decode with this shape's
+        workspace ran out of a wait (synchronises the stream)."""
+        ws = self.decode_workspace(sel, Nq)
+        _check(lib().hti_decode_status(_ptr(ws), ws.numel(), _stream(stream)))
 
     def decode_step(self, sel: Select, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
                     out: torch.Tensor, lse=None, sel_out=None, stream=None, split: bool = True):

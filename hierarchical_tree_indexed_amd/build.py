@@ -16,6 +16,9 @@ SOURCES = ["hti_api.hip", "hti_build.hip", "hti_traverse.hip", "hti_decode.hip",
 # a library of its own, loaded only by the benchmark
 PROBE_LIB = os.path.join(HERE, "libhti_probe.so")
 PROBE_SOURCES = ["hti_probe.hip"]
+# the same library with the split decode's phase timeline compiled in
+# (HTI_DECODE_TIMELINE): used by `bench.py --timeline` only
+TIMELINE_LIB = os.path.join(HERE, "libhti_timeline.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-parameter",
@@ -23,9 +26,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), "-c",
+def _compile(src: str, defines=()) -> str:
+    tag = "".join("_" + d.lower() for d in defines)
+    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(HERE, "..", "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -44,13 +48,15 @@ def _link(objs, lib):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(srcs))) as ex:
-        objs = dict(zip(srcs, ex.map(_compile, srcs)))
-    _link([objs[s] for s in SOURCES], LIB)
-    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+    jobs = [(s, ()) for s in SOURCES + PROBE_SOURCES] + [("hti_decode.hip", ("HTI_DECODE_TIMELINE",))]
+    with cf.ThreadPoolExecutor(max_workers=min(7, len(jobs))) as ex:
+        objs = dict(zip(jobs, ex.map(lambda j: _compile(*j), jobs)))
+    _link([objs[(s, ())] for s in SOURCES], LIB)
+    _link([objs[(s, ())] for s in PROBE_SOURCES], PROBE_LIB)
+    _link([objs[(s, ("HTI_DECODE_TIMELINE",))] if s == "hti_decode.hip" else objs[(s, ())] for s in SOURCES],
+          TIMELINE_LIB)
     if verbose:
-        print("built", LIB, "and", PROBE_LIB)
+        print("built", LIB, PROBE_LIB, "and", TIMELINE_LIB)
     return LIB
 
 

@@ -5,11 +5,32 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "hti_internal.h"
 
 using namespace hti;
+
+namespace hti {
+
+hipError_t set_dyn_lds_once(const void *kern, size_t bytes)
+{
+    static std::mutex mu;
+    static std::vector<std::pair<int, const void *>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    for (auto &p : done)
+        if (p.first == dev && p.second == kern) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) done.push_back({dev, kern});
+    return e;
+}
+
+} // namespace hti
 
 namespace {
 
@@ -381,8 +402,8 @@ namespace {
 
 // sparse_decode, and the decode step (k_new != NULL: append, then decode)
 hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select *sel, const void *k_new,
-                       const void *v_new, const void *q, int32_t Nq, float *out, float *lse, int32_t *sel_out,
-                       int32_t sel_stride, void *ws, size_t ws_bytes, void *stream)
+                       const void *v_new, const void *q, const int64_t *q_pos, int32_t Nq, float *out, float *lse,
+                       int32_t *sel_out, int32_t sel_stride, void *ws, size_t ws_bytes, void *stream)
 {
     hti_status st = check_traversal(tree, sel, 0, sel_out, sel_stride);
     if (st) return st;
@@ -401,6 +422,7 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     a.p = sel->p;
     a.leaf_only = sel->leaf_only;
     a.q = q;
+    a.q_pos = q_pos;
     a.Nq = Nq;
     a.out = out;
     a.lse = lse;
@@ -439,12 +461,26 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
 
 extern "C" {
 
-hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q, int32_t Nq,
-                             float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *ws,
+hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q, const int64_t *q_pos,
+                             int32_t Nq, float *out, float *lse, int32_t *sel_out, int32_t sel_stride, void *ws,
                              size_t ws_bytes, void *stream)
 {
-    return decode_impl("sparse_decode", tree, sel, nullptr, nullptr, q, Nq, out, lse, sel_out, sel_stride, ws,
-                       ws_bytes, stream);
+    return decode_impl("sparse_decode", tree, sel, nullptr, nullptr, q, q_pos, Nq, out, lse, sel_out, sel_stride,
+                       ws, ws_bytes, stream);
+}
+
+hti_status hti_decode_status(const void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ws || ws_bytes < 4) return fail(HTI_ERR_INVALID_ARG, "ws is NULL or too small");
+    uint32_t st = 0;
+    // the status word is the first word of the workspace
+    hipError_t e = hipMemcpyAsync(&st, ws, 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(HTI_ERR_LAUNCH, "decode_status: %s", hipGetErrorString(e));
+    if (st != 0)
+        return fail(HTI_ERR_TIMEOUT, "a decode launch with this workspace ran out of a wait between workgroups: "
+                                     "its outputs and those of later launches are NaN; zero the workspace");
+    return ok();
 }
 
 hti_status hti_decode_step(const hti_tree *tree, const hti_select *sel, const void *k_new, const void *v_new,
@@ -453,8 +489,8 @@ hti_status hti_decode_step(const hti_tree *tree, const hti_select *sel, const vo
 {
     if (!k_new || !v_new) return fail(HTI_ERR_INVALID_ARG, "k_new/v_new is NULL");
     if (hti_status st = check_tree(tree, true)) return st;
-    return decode_impl("decode_step", tree, sel, k_new, v_new, q, Nq, out, lse, sel_out, sel_stride, ws, ws_bytes,
-                       stream);
+    return decode_impl("decode_step", tree, sel, k_new, v_new, q, nullptr, Nq, out, lse, sel_out, sel_stride, ws,
+                       ws_bytes, stream);
 }
 
 size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T)

@@ -5,36 +5,43 @@
 // summaries sharing one softmax with the exact tokens, candidate-index RoPE;
 // "Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
 // Figure 3 caption: top-p routing, reference-query keys).  Decode has few
-// (query, KV group) units -- 32 at batch 4 with 8 KV heads -- and one compute
-// unit can keep only a few dozen cache lines in flight, so one workgroup per
-// unit would use an eighth of the chip and wait on its own gathers.  Here each
-// unit is split over W workgroups (W * units ~ the CU count):
+// (query, KV group) units -- 32 at batch 4 with 8 KV heads -- so each unit
+// is split over W workgroups (W * units ~ the CU count) that each take a
+// contiguous slice of every level's candidate list:
 //
-//   * every workgroup derives the level's candidate list (identical in all of
-//     them) and takes a contiguous slice of it: it gathers the slice's keys
-//     and values into registers, scores the keys and ranks them inside the
-//     slice;
-//   * it publishes its slice's best k (score, index) as 64-bit words carrying
-//     a per-launch tag, written and read with agent-scope atomics, so a word
-//     is valid exactly when its tag matches -- no fences, no counters;
-//   * every workgroup merges the same W lists into the same kept set; as soon
-//     as the kept set is known the next level's gathers are issued, and the
-//     level's own softmax contribution (unkept candidates) is folded in while
-//     they are in flight;
-//   * the token level is sliced the same way, without an exchange;
-//   * each workgroup publishes its partial state (max, denominator,
-//     unnormalised output per head) the same way, and every workgroup merges
-//     all of them for a slice of the output columns.
+//   * the slice's key rows go straight into registers (16 lanes per row, a
+//     few rows per 16-lane group) and its value rows likewise, all loads of a
+//     level issued back to back as soon as the previous level's kept set is
+//     known;
+//   * scores become 64-bit selection keys (order-preserving score bits over
+//     the complemented candidate index, so that one unsigned comparison is
+//     the tie rule: higher score, then lower index) and ranks are counted,
+//     every wave against its share of the keys, the shares summed in LDS;
+//   * a workgroup publishes its slice's best k as 64-bit words carrying a
+//     per-launch tag (agent-scope atomics: a word is valid exactly when its
+//     tag matches), reads every slice's words, and ranks those the same way;
+//     a level of at most kSlice candidates is scored whole by every
+//     workgroup, which selects on its own;
+//   * every wave derives the kept set in candidate order itself (no further
+//     barrier), issues the next level's loads, and folds the level's unkept
+//     candidates of its own slice while they are in flight;
+//   * each workgroup publishes its partial softmax state the same way and
+//     merges a slice of the output columns from all W of them.
 //
-// Softmax state: the running max M is kept identical in every thread (each
-// computes it from the same per-wave maxima); the denominator is kept as a
-// per-thread partial sum and the output as per-wave partial sums, both
-// rescaled by the same factors and reduced once at the end.
+// Softmax state: one running maximum per head, identical in every thread of
+// the workgroup (taken from per-wave maxima after the scoring barrier); the
+// denominators and outputs are per-thread partial sums rescaled by the same
+// factors and reduced once at the end.
 //
 // The workgroups of a launch wait on each other, so they must be resident
-// together: the grid is kept within one workgroup per compute unit, and every
-// wait is bounded -- on timeout the unit's output is NaN.
+// together: the grid is kept within what the device holds at once, and every
+// wait is bounded.  A wait that runs out sets the workspace's status word:
+// the outputs of that launch and of every later launch with the same
+// workspace are NaN (and no length advances) until the caller zeroes the
+// workspace again; hti_decode_status reads the word.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "hti_device.h"
 #include "hti_internal.h"
@@ -45,39 +52,73 @@ namespace hti {
 
 namespace {
 
-constexpr int DNT = 256;              // threads per workgroup
+constexpr int DNT = 512;              // threads per workgroup (two waves per SIMD)
 constexpr int DNW = DNT / 64;         // waves
-constexpr int DNQ = DNT / 16;         // quarter-waves (16-lane rows)
-constexpr int kSlice = 128;           // largest slice of a summary level / token chunk
-constexpr int kMaxW = 16;             // workgroups per unit
-constexpr int kSlots = kMaxSel + 2 * DNW;   // words per (level, workgroup): k entries + per-wave (max, sum)
-constexpr long kSpin = 1L << 22;      // bound on polling for one word
+constexpr int DNQ = DNT / 16;         // 16-lane rows ("quarters")
+constexpr int kSlice = 128;           // candidates one workgroup scores at once
+constexpr int kMaxW = HTI_DECODE_MAX_SPLIT;
+constexpr int kSlots = kMaxSel + 2;   // words per (level, workgroup): k entries, top-p (max, exp-sum)
+constexpr int kMaxEnt = kMaxW * kMaxSel;   // entries of one exchange
+constexpr int kSelN = kSlice + kMaxEnt;    // selection entries of one level: slice, then exchange
+constexpr int KB = 4;                 // key rows per quarter per batch
+constexpr int VB = kSlice / DNQ;      // value rows per quarter per level (4)
+constexpr long kSpin = 1L << 22;      // polls of one word before a wait gives up
+
+static_assert(VB * DNQ == kSlice, "the value rows of a slice fit one register batch");
+
+// Phase timeline (a separate build of this file with HTI_DECODE_TIMELINE
+// defined, for measurement only): thread 0 of every workgroup notes the
+// constant-rate clock at each phase boundary in LDS and copies the list to
+// the workspace at the end (kTlEvents words per workgroup, after the status
+// word).  Event word: phase << 52 | level << 48 | clock.
+constexpr int kTlEvents = 64;
+constexpr int kTlMaxBlocks = 8192;
+#ifdef HTI_DECODE_TIMELINE
+#define DTL(ph, lv)                                                                                  \
+    do {                                                                                             \
+        if (tid == 0 && tln < kTlEvents)                                                             \
+            sm.tl[tln] = ((uint64_t)(ph) << 52) | ((uint64_t)((lv) & 15) << 48) |                     \
+                         (__builtin_amdgcn_s_memrealtime() & 0xffffffffffffull);                      \
+        ++tln;                                                                                       \
+    } while (0)
+constexpr size_t kTlBytes = (size_t)kTlMaxBlocks * kTlEvents * 8;
+#else
+#define DTL(ph, lv) do {} while (0)
+constexpr size_t kTlBytes = 0;
+#endif
 
 template <int G>
 struct DSmem {
-    float z[2][kSlice * G];           // [candidate][head]: logits, then probabilities (by step parity)
-    float s[kSlice + 68] __attribute__((aligned(16)));   // group scores of the slice, -inf padded
-    uint8_t flag[kSlice];             // 1 = kept
+    // selection entries of the two most recent levels (by parity): keys,
+    // group scores, candidate indices and per-wave partial ranks; entries
+    // [0, kSlice) are the scored slice, [kSlice, kSelN) the exchange
+    uint64_t key[2][kSelN];
+    float esc[2][kSelN];
+    int16_t eix[2][kSelN];
+    uint8_t prt[2][DNW][kSelN];
+    float z[2][kSlice * G];           // [candidate][head] logits of the scored slice / chunk
     float qraw[G * 128] __attribute__((aligned(16)));
-    int sel[2][kMaxSel];
-    int nsel[2];
-    float redz[DNW][G];               // per-wave maxima of the logits
-    float xv[kMaxW * kMaxSel] __attribute__((aligned(16)));   // collected lists: score, index
-    int xi[kMaxW * kMaxSel] __attribute__((aligned(16)));
-    float xm[kMaxW * DNW], xs[kMaxW * DNW];    // per-wave max and exp-sum (top-p)
-    int byrank[kMaxSel] __attribute__((aligned(16)));   // kept entries by rank: index, score
-    float byv[kMaxSel];
-    int nkeep;
-    int in_last;                      // the query's own leaf was kept (level 1)
-    int n[HTI_MAX_LEVELS + 1];        // nodes per level (n[0] = tokens; all < 2^31)
+    float redz[2][DNW][G];            // per-wave maxima of the logits (by the parity of sm.z)
+    // per wave: the kept set in candidate order (node ids, candidate
+    // indices) by level parity, and the kept entries by rank
+    int wsel[2][DNW][kMaxSel];
+    int wcix[2][DNW][kMaxSel];
+    int wrix[DNW][kMaxSel];
+    float wrsc[DNW][kMaxSel];
+    float xm[kMaxW], xs[kMaxW];       // top-p: each slice's (max, exp-sum) of group scores
+    int n[HTI_MAX_LEVELS + 1];        // nodes per level (n[0] = tokens)
     const void *lkp[HTI_MAX_LEVELS];  // this unit's level keys / values
     const void *lvp[HTI_MAX_LEVELS];
     const uint8_t *lkq[HTI_MAX_LEVELS];   // 8-bit router keys and their row scales
     const float *lks[HTI_MAX_LEVELS];
-    uint32_t tag;
-    int bad;                          // a wait of this workgroup timed out
+    uint32_t tag;                     // this launch's tag of the exchange words
+    uint32_t st0;                     // the workspace status at the start
     int app;                          // decode step: the new token goes in at position lold
     int lold;                         // sequence length before the step
+    int bad;                          // a wait of this workgroup ran out
+#ifdef HTI_DECODE_TIMELINE
+    uint64_t tl[kTlEvents];
+#endif
 };
 
 __device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t idx, float v)
@@ -88,14 +129,62 @@ __device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >
 __device__ __forceinline__ uint32_t word_idx(uint64_t w) { return (uint32_t)(w >> 32) & 0xfffu; }
 __device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-__device__ __forceinline__ int better(float va, int ia, float vb, int ib)
+// Selection key: larger means kept first (higher score, then lower index);
+// -0 counts as +0, as in a float comparison.
+__device__ __forceinline__ uint64_t sel_key(float s, int ix)
 {
-    return (int)(va > vb) | ((int)(va == vb) & (int)(ia < ib));
+    uint32_t u = __float_as_uint(s + 0.f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (uint32_t)ix);
 }
+
+// Order this wave's LDS accesses (lanes read what other lanes of the same
+// wave wrote just before): the LDS executes one wave's accesses in order, so
+// only the compiler must be kept from moving them.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Value row slice of one lane: EPL consecutive elements.
+template <typename T, int EPL> struct VRow;
+template <> struct VRow<bf16_t, 8> {
+    uint4 r;
+    __device__ __forceinline__ void load(gptr<bf16_t> p) { r = gload<uint4>(p); }
+    __device__ __forceinline__ void get(float *o) const
+    {
+        cvt(make_uint2(r.x, r.y), o);
+        cvt(make_uint2(r.z, r.w), o + 4);
+    }
+};
+template <> struct VRow<bf16_t, 4> {
+    uint2 r;
+    __device__ __forceinline__ void load(gptr<bf16_t> p) { r = gload<uint2>(p); }
+    __device__ __forceinline__ void get(float *o) const { cvt(r, o); }
+};
+template <> struct VRow<float, 8> {
+    float4 a, b;
+    __device__ __forceinline__ void load(gptr<float> p)
+    {
+        a = gload<float4>(p);
+        b = gload<float4>(p + 4);
+    }
+    __device__ __forceinline__ void get(float *o) const
+    {
+        cvt(a, o);
+        cvt(b, o + 4);
+    }
+};
+template <> struct VRow<float, 4> {
+    float4 a;
+    __device__ __forceinline__ void load(gptr<float> p) { a = gload<float4>(p); }
+    __device__ __forceinline__ void get(float *o) const { cvt(a, o); }
+};
 
 // Candidates of one step (a summary level or the token level) as seen by one
 // workgroup: the list, where its keys and values live, and this workgroup's
-// slice of it.
+// slices of it.
 template <typename T>
 struct Step {
     Cands cs;
@@ -104,7 +193,7 @@ struct Step {
     gptr<float> ks;      // and their scales, row r * nref + j
     int nref;            // keys per row (R at summary levels, 1 at tokens)
     int m;               // candidates
-    int s0, ms;          // candidates this workgroup scores (first chunk at the token level)
+    int s0, ms;          // candidates this workgroup scores (the first chunk at the token level)
     int t1;              // token level: end of this workgroup's range
     int fs0, fms;        // candidates whose values this workgroup folds (its own slice)
     int qpos;            // RoPE position of the query
@@ -119,17 +208,10 @@ struct Step {
 template <typename T, int D, int G, bool F8>
 __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 {
-    constexpr int PPL = D / 32;
-    constexpr int DPL = D / 64;
+    constexpr int PPL = D / 32;                        // rotate-half pairs per lane of a key row
+    constexpr int EPL = D / 16;                        // elements per lane of a value row
     using KR = typename Raw<T, PPL>::type;
-    constexpr int KRW = sizeof(KR) / 4 > 0 ? (int)sizeof(KR) / 4 : 1;
-    // key rows per quarter per batch: at least one candidate's HTI_MAX_R
-    // reference keys (a batch never splits a candidate), at most 16 (DPP row)
-    constexpr int KB0 = 40 / (2 * KRW);
-    constexpr int KB = KB0 < HTI_MAX_R ? HTI_MAX_R : (KB0 > 16 ? 16 : KB0);
-    static_assert(KB >= HTI_MAX_R && KB <= 16, "key batch");
-    using VR = typename Raw<T, DPL>::type;
-    constexpr int VBS = 8;                             // value rows per wave held in registers
+    using VR = VRow<T, EPL>;
     __shared__ DSmem<G> sm;
     extern __shared__ __attribute__((aligned(16))) unsigned char hti_dec_lds[];
 
@@ -148,23 +230,36 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
     const bool topp = a.mode == HTI_TOPP;
     uint64_t *xw = ws.words + (int64_t)unit * levels * W * kSlots;
+    const int64_t orow = ((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G;
+    int tln = 0;
+    (void)tln;
+    DTL(1, 0);
 
+    // ---- start: the length, the launch epoch, the workspace status and
+    // the query position go out together; the query into LDS ----
     if (tid == 0) {
-        // the length and the launch epoch: both loads go out before either
-        // is used
         const int64_t len0 = t.len[bi];
         const uint32_t epoch = ws.epoch[unit];
+        const uint32_t st0 = __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.tag = (epoch % 0xffffeu) + 1u;
+        sm.st0 = st0;
         int n = (int)len0;
         // decode step: this workgroup appends the new token itself (every
         // workgroup of every query of the sequence writes the same bytes) and
         // walks the tree with the new length; it counts itself as having read
         // the old length, which one workgroup replaces at the end
-        const bool app = a.k_new != nullptr && (int64_t)n < t.ncap[0];
+        const bool app = st0 == 0u && a.k_new != nullptr && (int64_t)n < t.ncap[0];
         sm.app = app ? 1 : 0;
         sm.lold = n;
-        if (a.k_new != nullptr)
-            __hip_atomic_fetch_add(&ws.seqcnt[bi], n >= 0 ? 1u : 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.bad = 0;
+        if (a.k_new != nullptr && st0 == 0u)
+            __hip_atomic_fetch_add(&ws.seqcnt[bi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (app) ++n;
+        // a query at position q_pos attends to the tree of tokens 0..q_pos
+        if (a.q_pos) {
+            const int64_t ql = a.q_pos[(int64_t)bi * a.Nq + qi];
+            if (ql < (int64_t)n - 1) n = ql < 0 ? 0 : (int)(ql + 1);
+        }
         sm.n[0] = n;
         const int bs = __builtin_ctz((unsigned)b);
         const bool pow2 = (b & (b - 1)) == 0;
@@ -172,15 +267,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             n = pow2 ? (n >> bs) : n / b;
             sm.n[l] = n;
         }
-        sm.tag = (epoch % 0xffffeu) + 1u;
-        sm.nsel[0] = 0;
-        sm.bad = 0;
-        sm.in_last = 0;
     }
     if (tid == 64) {
-        // this unit's level arrays, by another wave than the length's chain
-        // (constant indices into the argument block, so scalar loads, all
-        // issued together; entries past `levels` are never read)
+        // this unit's level arrays (constant indices into the argument block,
+        // so scalar loads, all issued together; entries past `levels` are
+        // never read)
 #pragma unroll
         for (int l = 0; l < HTI_MAX_LEVELS; ++l) {
             sm.lkp[l] = (const T *)t.lk[l] + bh * t.ncap[l + 1] * R * D;
@@ -192,21 +283,22 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
     }
     const gptr<float2> rope = to_global<float2>(t.rope);
-    const gptr<T> qp = to_global<T>(a.q) + (((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G) * D;
-    // the query into LDS, one 16-byte load per thread
-    constexpr int EPC = 16 / (int)sizeof(T);           // elements per 16-byte chunk
-    static_assert(G * D / EPC <= DNT, "one chunk of the query per thread");
-    if (tid < G * D / EPC) {
-        const uint4 x = gload<uint4>(qp + tid * EPC);
-        float *qd = sm.qraw + tid * EPC;
-        if constexpr (sizeof(T) == 2) {
-            cvt(make_uint2(x.x, x.y), qd);
-            cvt(make_uint2(x.z, x.w), qd + 4);
-        } else {
-            qd[0] = __uint_as_float(x.x);
-            qd[1] = __uint_as_float(x.y);
-            qd[2] = __uint_as_float(x.z);
-            qd[3] = __uint_as_float(x.w);
+    {
+        const gptr<T> qp = to_global<T>(a.q) + orow * D;
+        constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+        static_assert(G * D / EPC <= DNT, "one chunk of the query per thread");
+        if (tid < G * D / EPC) {
+            const uint4 x = gload<uint4>(qp + tid * EPC);
+            float *qd = sm.qraw + tid * EPC;
+            if constexpr (sizeof(T) == 2) {
+                cvt(make_uint2(x.x, x.y), qd);
+                cvt(make_uint2(x.z, x.w), qd + 4);
+            } else {
+                qd[0] = __uint_as_float(x.x);
+                qd[1] = __uint_as_float(x.y);
+                qd[2] = __uint_as_float(x.z);
+                qd[3] = __uint_as_float(x.w);
+            }
         }
     }
     // angle step of each of this lane's RoPE frequencies (row 1 of the table)
@@ -217,19 +309,32 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         st_c[e] = c2.x;
         st_s[e] = c2.y;
     }
-    float M[G], lt[G], acc[G][DPL];
+    float M[G], lt[G], acc[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         M[h] = -INFINITY;
         lt[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
     __syncthreads();
+    DTL(2, 0);
+    const uint32_t tag = sm.tag;
+    if (sm.st0 != 0u) {
+        // an earlier launch with this workspace ran out of a wait: NaN, no
+        // other effect, until the workspace is zeroed
+        const int cols = (D + W - 1) / W;
+        const int d0 = min(D, wg * cols), d1 = min(D, d0 + cols);
+        for (int i = tid; i < G * (d1 - d0); i += DNT)
+            a.out[(orow + i / (d1 - d0)) * D + d0 + i % (d1 - d0)] = __uint_as_float(0x7fc00000u);
+        if (wg == 0 && tid < G && a.lse) a.lse[orow + tid] = __uint_as_float(0x7fc00000u);
+        return;
+    }
     if (sm.app) {
         // the new row of this unit's KV head at position lold, then every
         // node it completes, level by level (one wave pools)
         const int64_t Lold = sm.lold;
+        constexpr int EPC = 16 / (int)sizeof(T);
         const T *kn = (const T *)a.k_new + bh * D, *vn = (const T *)a.v_new + bh * D;
         T *kw = (T *)t.kc + (bh * t.ncap[0] + Lold) * D;
         T *vw = (T *)t.vc + (bh * t.ncap[0] + Lold) * D;
@@ -252,7 +357,6 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             __syncthreads();
         }
     }
-    const uint32_t tag = sm.tag;
     const int L = sm.n[0];
     const int last_leaf = L > 0 ? (L - 1) / b : -1;   // level-1 node of the query token
 
@@ -260,14 +364,14 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const gptr<T> vc = to_global<T>(t.vc) + bh * t.ncap[0] * D;
 
     // ---- the candidates of a step ----
-    // level lvl >= 1 (parents in sm.sel[cur]) or the token level (lvl == 0)
-    auto make_step = [&](int lvl, int cur) __attribute__((always_inline)) -> Step<T> {
+    // level lvl >= 1 (parents: this wave's kept list of parity cur, nprev of
+    // them) or the token level (lvl == 0)
+    auto make_step = [&](int lvl, int cur, int nprev) __attribute__((always_inline)) -> Step<T> {
         Step<T> st;
         st.tok = lvl == 0;
         const bool top = (lvl == levels);
-        const int nprev = top ? 0 : sm.nsel[cur];
-        st.cs.selp = sm.sel[cur];
-        st.cs.nprev = nprev;
+        st.cs.selp = sm.wsel[cur][wave];
+        st.cs.nprev = top ? 0 : nprev;
         st.cs.b = b;
         st.cs.binv = a.binv;
         st.cs.top = top;
@@ -295,7 +399,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             // the query token is a candidate when its leaf was kept or it is
             // an orphan; it then sits last
             const int m0 = top ? L : nprev * b + (L - orph0);
-            const bool in = top || (L - 1 >= orph0) || sm.in_last != 0;
+            bool in = top || (L - 1 >= orph0);
+            for (int r = 0; r < nprev && !in; ++r) in = sm.wsel[cur][wave][r] == last_leaf;
             st.m = m0;
             st.kb = kc;
             st.vb = vc;
@@ -315,15 +420,13 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     };
 
     // ---- gathers ----
-    // One batch of a quarter-wave's keys: its items it0.. (item = candidate x
+    // One batch of a quarter's keys: its items it0.. (item = candidate x
     // reference key), at most KB of them.  Lane `sub` derives the row of item
     // it0 + sub (clamped into the batch, so surplus loads re-read a row of
-    // it) and DPP row broadcasts hand row u to the whole quarter: the
-    // address arithmetic is done once per lane instead of once per row, and
-    // every load is issued back to back.  Also the RoPE row of the batch's
-    // first candidate.
-    // With go == false every load reads the (always valid) RoPE table
-    // instead, so that loads never sit behind a branch.
+    // it) and DPP row broadcasts hand row u to the whole quarter, so the
+    // loads go out back to back.  Also the RoPE row of the batch's first
+    // candidate.  With go == false every load reads the (always valid) RoPE
+    // table instead, so that loads never sit behind a branch.
     auto load_batch = [&](const Step<T> &st, int s0, int ms, int it0, bool go, KR (&k0)[KB], KR (&k1)[KB],
                           float (&sc)[KB], float (&rb)[2 * PPL]) __attribute__((always_inline)) {
         const int nref = st.nref;
@@ -331,8 +434,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int c_beg = min(ms, quarter * cpq);
         const int c_end = min(ms, c_beg + cpq);
         const int nitems = (c_end - c_beg) * nref;
-        const int KBR = (KB / nref) * nref;
-        const int nb = min(nitems - it0, KBR);
+        const int nb = min(nitems - it0, KB);
         const int itl = it0 + (nb > 0 ? min(sub, nb - 1) : 0);
         const int cl = itl / nref;
         const int cand = min(c_beg + cl, ms - 1);
@@ -371,27 +473,23 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             rb[4 * e + 3] = c4.w;
         }
     };
-    // value rows of the slice, wave w owning rows w, w + DNW, ...: the first
-    // VBS per wave go to registers.  Lane u of the wave derives the row of its
-    // u-th row (rows past the slice re-read its last row) and hands it to the
-    // wave through a readlane, so the loads go out back to back.
-    auto issue_values = [&](const Step<T> &st, int s0, int ms, bool go, VR (&vr)[VBS]) __attribute__((always_inline)) {
-        const int rl = go ? (int)st.cs.id(s0 + max(0, min(wave + DNW * (lane & (VBS - 1)), ms - 1))) : 0;
+    // value rows of the fold slice: quarter q owns rows q, q + DNQ, ...
+    // (rows past the slice re-read its last row)
+    auto issue_values = [&](const Step<T> &st, int s0, int ms, bool go, VR (&vr)[VB]) __attribute__((always_inline)) {
         const gptr<T> vbase = go ? st.vb : to_global<T>(t.rope);
 #pragma unroll
-        for (int u = 0; u < VBS; ++u) {
-            const uint32_t ru = (uint32_t)__builtin_amdgcn_readlane(rl, u);
-            vr[u] = gload<VR>(vbase + (size_t)ru * D + lane * DPL);
+        for (int u = 0; u < VB; ++u) {
+            const int i = max(0, min(quarter + DNQ * u, ms - 1));
+            const uint32_t ru = go ? (uint32_t)st.cs.id(s0 + i) : 0u;
+            vr[u].load(vbase + (size_t)ru * D + sub * EPL);
         }
     };
-    // (RoPE rows stay as loaded, (cos, sin) pairs: splitting them would copy
-    // registers still being loaded and so wait for the gathers right here)
-    // Every load is unconditional (a step with nothing to gather reads the
-    // RoPE table instead): a register that kept its old value on some path
-    // would have to be copied at the loop edge, which waits for its load.
+    // every load of a step goes out here, unconditionally (a step with
+    // nothing to gather reads the RoPE table instead): a register that kept
+    // its old value on some path would have to be copied at the loop edge,
+    // which waits for its load
     auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&sc)[KB], float (&rb)[2 * PPL],
-                          VR (&vr)[VBS],
-                          float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
+                          VR (&vr)[VB], float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
         const bool go = !st.take_all && st.ms > 0;
         load_batch(st, st.s0, st.ms, 0, go, k0, k1, sc, rb);
         // (the token level's values, or a summary level's when its unkept
@@ -410,9 +508,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 
     // ---- scoring ----
     // Rotated query of this lane's elements (sub*PPL.., and the rotate-half
-    // partners), then the slice's keys in quarter-wave batches: logits per
-    // head into sm.z[zb], group scores into sm.s (with -inf padding), kept
-    // flags cleared, per-wave maxima of the logits into sm.redz.
+    // partners), then the slice's keys in quarter batches: per-head logits
+    // into sm.z[zb], selection entries (key, score, index) into the level's
+    // slice entries, per-wave maxima of the logits into sm.redz.
     auto score = [&](const Step<T> &st, int s0, int ms, int zb, KR (&k0)[KB], KR (&k1)[KB], float (&sc)[KB],
                      float (&rb)[2 * PPL], const float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
         const bool q8 = F8 && !st.tok;
@@ -434,19 +532,25 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int c_beg = min(ms, quarter * cpq);
         const int c_end = min(ms, c_beg + cpq);
         const int nitems = (c_end - c_beg) * nref;
-        const int KBR = (KB / nref) * nref;
         float zmaxh = -INFINITY;               // of the lane's head
         float *zz = sm.z[zb];
-        for (int it0 = 0; it0 < nitems; it0 += KBR) {
-            const int nb = min(nitems - it0, KBR);
+        uint64_t *ek = sm.key[zb];
+        float *es = sm.esc[zb];
+        int16_t *ei = sm.eix[zb];
+        // the running best over a candidate's reference keys carries across
+        // batches (a batch may end inside a candidate)
+        int ci = c_beg, j = 0;
+        float best = -INFINITY, zbh = 0.f;
+        float cc[PPL], ss[PPL];
+        for (int it0 = 0; it0 < nitems; it0 += KB) {
+            const int nb = min(nitems - it0, KB);
             if (it0 > 0) load_batch(st, s0, ms, it0, true, k0, k1, sc, rb);
-            int ci = c_beg + it0 / nref, j = 0;
-            float best = -INFINITY, zbh = 0.f;
-            float cc[PPL], ss[PPL];
+            if (j == 0) {
 #pragma unroll
-            for (int e = 0; e < PPL; ++e) {
-                cc[e] = rb[2 * e];
-                ss[e] = rb[2 * e + 1];
+                for (int e = 0; e < PPL; ++e) {
+                    cc[e] = rb[2 * e];
+                    ss[e] = rb[2 * e + 1];
+                }
             }
 #pragma unroll
             for (int u = 0; u < KB; ++u) {
@@ -480,8 +584,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     }
                     if (++j == nref) {
                         if (sub == 0) {
-                            sm.s[ci] = best;
-                            sm.flag[ci] = 0;
+                            ek[ci] = sel_key(best, s0 + ci);
+                            es[ci] = best;
+                            ei[ci] = (int16_t)(s0 + ci);
                         }
                         if (wz) zz[ci * G + hsel] = zbh;
                         zmaxh = fmaxf(zmaxh, zbh);
@@ -499,360 +604,287 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 }
             }
         }
-        if (tid < 68) sm.s[ms + tid] = -INFINITY;
         // lane h * LPH of each quarter holds that quarter's maximum of head
         // h: combine the wave's four quarters
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float m4 = fmaxf(fmaxf(rlane(zmaxh, h * LPH), rlane(zmaxh, 16 + h * LPH)),
                                    fmaxf(rlane(zmaxh, 32 + h * LPH), rlane(zmaxh, 48 + h * LPH)));
-            if (lane == 0) sm.redz[wave][h] = m4;
+            if (lane == 0) sm.redz[zb][wave][h] = m4;
         }
+    };
+
+    // ---- selection ----
+    // Partial ranks: entry e (of the n from `base` in the parity-zb arrays)
+    // counted against this wave's share of the same entries; after a barrier
+    // rank(e) = the sum over waves.
+    auto partial_ranks = [&](int zb, int base, int n) __attribute__((always_inline)) {
+        const int j0 = base + n * wave / DNW, j1 = base + n * (wave + 1) / DNW;
+        const uint64_t *kk = sm.key[zb];
+        for (int e = base + lane; e < base + n; e += 64) {
+            const uint64_t ke = kk[e];
+            int c = 0;
+            for (int j = j0; j < j1; ++j) c += (int)(kk[j] > ke);
+            sm.prt[zb][wave][e] = (uint8_t)c;
+        }
+    };
+    auto rank_of = [&](int zb, int e) __attribute__((always_inline)) -> int {
+        int r = 0;
+#pragma unroll
+        for (int w = 0; w < DNW; ++w) r += sm.prt[zb][w][e];
+        return r;
+    };
+    // Kept set from the ranks of n entries (from `base`): the first nav by
+    // rank (top-p: the shortest prefix whose mass over every candidate,
+    // max gmax and denominator den, reaches p), in candidate order, into
+    // this wave's lists of parity nxt.  Returns the kept count.
+    auto finalize = [&](int zb, int base, int n, int m, const Cands &cs, int nxt, float gmax, float den)
+        __attribute__((always_inline)) -> int {
+        const int nav = min(keff, m);
+        for (int e = base + lane; e < base + n; e += 64) {
+            const int r = rank_of(zb, e);
+            if (r < nav) {
+                sm.wrix[wave][r] = sm.eix[zb][e];
+                sm.wrsc[wave][r] = sm.esc[zb][e];
+            }
+        }
+        wave_sync();
+        int nkeep = nav;
+        if (topp) {
+            int ns = nav;
+            if (lane == 0) {
+                float cum = 0.f;
+                for (int r = 0; r < nav; ++r) {
+                    cum += __expf(sm.wrsc[wave][r] - gmax) / den;
+                    if (cum >= a.p) {
+                        ns = r + 1;
+                        break;
+                    }
+                }
+            }
+            nkeep = max(1, min(__builtin_amdgcn_readfirstlane(ns), a.cap));
+        }
+        if (lane < nkeep) {
+            const int ix = sm.wrix[wave][lane];
+            int pos = 0;
+            for (int r = 0; r < nkeep; ++r) pos += (int)(sm.wrix[wave][r] < ix);
+            sm.wcix[nxt][wave][pos] = ix;
+            sm.wsel[nxt][wave][pos] = (int)cs.id(ix);
+        }
+        wave_sync();
+        return nkeep;
+    };
+    auto is_kept = [&](int nxt, int nkeep, int c) __attribute__((always_inline)) -> bool {
+        bool k = false;
+        for (int r = 0; r < nkeep; ++r) k |= sm.wcix[nxt][wave][r] == c;
+        return k;
     };
 
     // new running max from the per-wave maxima (same in every thread), and
     // the factor that rescales what was accumulated under the old one
-    auto new_max = [&](float (&Mn)[G], float (&alpha)[G]) __attribute__((always_inline)) {
+    auto new_max = [&](int zb, float (&Mn)[G], float (&alpha)[G]) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mm = M[h];
 #pragma unroll
-            for (int w = 0; w < DNW; ++w) mm = fmaxf(mm, sm.redz[w][h]);
+            for (int w = 0; w < DNW; ++w) mm = fmaxf(mm, sm.redz[zb][w][h]);
             Mn[h] = mm;
             alpha[h] = (mm == -INFINITY) ? 1.f : __expf(M[h] - mm);
         }
     };
-    // probabilities of this thread's candidate tid in [lo, hi) (kept ones drop
-    // out), the rescaled partial denominator and output
-    auto probs = [&](int lo, int hi, int zb, bool use_flags, const float (&Mn)[G], const float (&alpha)[G])
-        __attribute__((always_inline)) {
+    // softmax terms of this quarter's fold rows (candidates fs0 + quarter +
+    // DNQ u; logits at z index c - zo) times their value rows; kept ones
+    // (when nkeep >= 0) drop out
+    auto fold = [&](int fs0, int fms, int zo, int zb, int nxt, int nkeep, const VR (&vr)[VB],
+                    const float (&Mn)[G], const float (&alpha)[G]) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             lt[h] *= alpha[h];
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha[h];
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+            M[h] = Mn[h];
         }
-        if (tid >= lo && tid < hi) {
-            const bool kept = use_flags && sm.flag[tid];
-            float *zp = &sm.z[zb][tid * G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = kept ? 0.f : __expf(zp[h] - Mn[h]);
-                zp[h] = p;
-                lt[h] += p;
+        for (int u = 0; u < VB; ++u) {
+            const int i = quarter + DNQ * u;
+            if (i < fms) {
+                const int c = fs0 + i;
+                const bool kept = nkeep > 0 && is_kept(nxt, nkeep, c);
+                const float *zp = &sm.z[zb][(c - zo) * G];
+                float v[EPL];
+                vr[u].get(v);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float p = kept ? 0.f : __expf(zp[h] - M[h]);
+                    lt[h] += p;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+                }
             }
         }
-#pragma unroll
-        for (int h = 0; h < G; ++h) M[h] = Mn[h];
     };
-    // p * v over the slice's rows: the register batch, then any further rows
-    // (zo: the z row of the range's first candidate)
-    auto fold = [&](const Step<T> &st, int s0, int ms, int zb, const VR (&vr)[VBS], int zo) __attribute__((always_inline)) {
-        auto add_row = [&](int i, const float *v) __attribute__((always_inline)) {
-            const float *pz = &sm.z[zb][(zo + i) * G];
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) acc[h][e] += pz[h] * v[e];
-        };
-#pragma unroll
-        for (int u = 0; u < VBS; ++u) {
-            const int i = wave + DNW * u;
-            if (i < ms) {
-                float v[DPL];
-                cvt(vr[u], v);
-                add_row(i, v);
-            }
-        }
-        for (int i = wave + DNW * VBS; i < ms; i += DNW) {
-            float v[DPL];
-            cvt(gload<VR>(st.vb + st.cs.id(s0 + i) * D + lane * DPL), v);
-            add_row(i, v);
+    auto write_sel = [&](int lvl, int nxt, int nkeep) __attribute__((always_inline)) {
+        if (wg == 0 && wave == 0 && a.sel) {
+            int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
+            for (int r = lane; r < a.sel_stride; r += 64) o[r] = (r < nkeep) ? sm.wsel[nxt][0][r] : -1;
         }
     };
 
     // ---- the steps ----
-    int cur = 0, zb = 0;
+    int cur = 0, zb = 0, nsel = 0;
     KR k0[KB], k1[KB];
     float sc[KB];   // row scales of 8-bit router keys
     float rb[2 * PPL], qcs[2 * PPL];
-    VR vr[VBS];
+    VR vr[VB];
     // Upper levels that keep every candidate need no gathers: their kept
-    // lists follow from the node counts alone, so they are taken here and the
-    // first gathers are those of the first scored level.
+    // lists follow from the node counts alone (every wave takes them itself).
     int lvl = levels;
-    Step<T> st = make_step(lvl, 0);
+    Step<T> st = make_step(lvl, 0, 0);
     while (lvl >= 1 && st.take_all) {
         const int nxt = cur ^ 1;
-        for (int i = tid; i < st.m; i += DNT) sm.sel[nxt][i] = (int)st.cs.id(i);
-        if (tid == 0) sm.nsel[nxt] = st.m;
-        if (lvl == 1 && tid < st.m && st.cs.id(tid) == last_leaf) sm.in_last = 1;
-        __syncthreads();
-        if (wg == 0 && a.sel) {
-            int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
-            for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < st.m) ? sm.sel[nxt][r] : -1;
+        for (int i = lane; i < st.m; i += 64) {
+            sm.wsel[nxt][wave][i] = (int)st.cs.id(i);
+            sm.wcix[nxt][wave][i] = i;
         }
+        wave_sync();
+        nsel = st.m;
+        write_sel(lvl, nxt, nsel);
         cur = nxt;
         --lvl;
-        st = make_step(lvl, cur);
+        st = make_step(lvl, cur, nsel);
     }
     issue_step(st, k0, k1, sc, rb, vr, qcs);
+    DTL(3, lvl);
 
     for (; lvl >= 1; --lvl) {
         const int nxt = cur ^ 1;
-        const bool scored = !st.take_all;
         const int s0 = st.s0, ms = st.ms;
         float Mn[G], alpha[G];
-        if (!scored) {
-            for (int i = tid; i < st.m; i += DNT) sm.sel[nxt][i] = (int)st.cs.id(i);
-            if (tid == 0) sm.nsel[nxt] = st.m;
-            if (lvl == 1 && tid < st.m && st.cs.id(tid) == last_leaf) sm.in_last = 1;
-            __syncthreads();
-            if (wg == 0 && a.sel) {
-                int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
-                for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < st.m) ? sm.sel[nxt][r] : -1;
+        int nkeep;
+        if (st.take_all) {
+            // (a lower level can keep everything when an upper one kept few)
+            for (int i = lane; i < st.m; i += 64) {
+                sm.wsel[nxt][wave][i] = (int)st.cs.id(i);
+                sm.wcix[nxt][wave][i] = i;
             }
+            wave_sync();
+            nkeep = st.m;
         } else {
-        score(st, s0, ms, zb, k0, k1, sc, rb, qcs);
-        __syncthreads();                                                   // B1
-        new_max(Mn, alpha);
-
-        // rank inside the slice: Gr threads per candidate, each comparing it
-        // with a run of the (padded) slice, counts summed with DPP
-        uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;
-        uint64_t *mine = lw_words + (int64_t)wg * kSlots;
-        {
-            int Gr = 16;
-            while (Gr > 1 && Gr * ms > DNT) Gr >>= 1;
-            const int ci = tid / Gr, cc = tid & (Gr - 1);
-            const int ch = (((ms + Gr - 1) / Gr) + 3) & ~3;
-            const bool valid = ci < ms;
-            const float si = valid ? sm.s[ci] : -INFINITY;
-            int rank = 0;
-            for (int j = cc * ch; j < cc * ch + ch; j += 4) {
-                const float4 v4 = *reinterpret_cast<const float4 *>(&sm.s[j]);
-                rank += better(v4.x, j, si, ci) + better(v4.y, j + 1, si, ci) +
-                        better(v4.z, j + 2, si, ci) + better(v4.w, j + 3, si, ci);
-            }
-            if (Gr >= 2) rank += dppi<0xB1>(rank);
-            if (Gr >= 4) rank += dppi<0x4E>(rank);
-            if (Gr >= 8) rank += dppi<0x141>(rank);
-            if (Gr >= 16) rank += dppi<0x140>(rank);
+            score(st, s0, ms, zb, k0, k1, sc, rb, qcs);
+            __syncthreads();                                           // B1: slice entries, logits
+            DTL(4, lvl);
+            new_max(zb, Mn, alpha);
             if (st.local) {
-                // the whole level: the rank is the global rank
-                if (valid && cc == 0 && rank < keff) {
-                    sm.byrank[rank] = ci;
-                    sm.byv[rank] = si;
-                }
-            } else {
-            if (valid && cc == 0 && rank < keff)
-                __hip_atomic_store(&mine[rank], pack_word(tag, (uint32_t)(s0 + ci), si), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (tid >= ms && tid < keff)
-                __hip_atomic_store(&mine[tid], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-            if (topp && !st.local) {
-                // this wave's (max, exp-sum) of the group scores it holds
-                const bool own = valid && cc == 0;
-                const float wmax = wave_max(own ? si : -INFINITY);
-                const float wsum = wave_sum(own ? __expf(si - wmax) : 0.f);
-                if (lane == 0) {
-                    __hip_atomic_store(&mine[keff + 2 * wave], pack_word(tag, 0, wmax), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&mine[keff + 2 * wave + 1], pack_word(tag, 0, wsum), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        }
-
-        const int kp4 = (keff + 3) & ~3;
-        int nkeep = min(keff, st.m);
-        if (!st.local) {
-        // collect every slice's words (bounded polling on the tag); list w
-        // lands at xv/xi[w * kp4 ..], padded to a multiple of 4 entries
-        const int nrow = kp4 + (topp ? 2 * DNW : 0);
-        for (int e = tid; e < W * nrow; e += DNT) {
-            const int w = e / nrow, r = e % nrow;
-            if (r >= keff && r < kp4) {
-                sm.xv[w * kp4 + r] = -INFINITY;
-                sm.xi[w * kp4 + r] = 0x7fffffff;
-                continue;
-            }
-            const int slot = r < keff ? r : r - kp4 + keff;
-            const uint64_t *src = lw_words + (int64_t)w * kSlots + slot;
-            uint64_t word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            long spins = 0;
-            while (word_tag(word) != tag && ++spins < kSpin) {
-                __builtin_amdgcn_s_sleep(1);
-                word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            const bool okw = word_tag(word) == tag;
-            if (!okw) {
-                __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sm.bad = 1;
-            }
-            if (r < keff) {
-                const uint32_t ix = okw ? word_idx(word) : 0xfffu;
-                sm.xv[w * kp4 + r] = (okw && ix != 0xfffu) ? word_val(word) : -INFINITY;
-                sm.xi[w * kp4 + r] = (ix == 0xfffu) ? 0x7fffffff : (int)ix;
-            } else {
-                const int q = w * DNW + (slot - keff) / 2;
-                if (((slot - keff) & 1) == 0) sm.xm[q] = okw ? word_val(word) : -INFINITY;
-                else sm.xs[q] = okw ? word_val(word) : 0.f;
-            }
-        }
-        __syncthreads();                                                   // B2
-
-        // Merge.  Every list is sorted (slot r holds its slice's rank-r
-        // entry), so an entry's global rank is its slot plus, for every other
-        // list, the number of that list's entries ranking before it.  A group
-        // of P lanes (P = W rounded up to a power of two) takes an entry and
-        // lane j counts in list j -- by comparing with all of it for short
-        // lists, by binary search otherwise -- and the group sums the counts
-        // with DPP.
-        const int ne = W * kp4;
-        {
-            int P = 1;
-            while (P < W) P <<= 1;
-            const int lg = tid & (P - 1);
-            const int ngr = DNT / P;
-            const uint32_t kinv = (65536u + kp4 - 1) / kp4;   // e / kp4 for e < 2^10
-            const int lwo = min(lg, W - 1) * kp4;
-            for (int e0 = tid / P; e0 - tid / P < ne; e0 += 2 * ngr) {
-                float ve[2];
-                int ie[2], cnt[2], wo[2];
-                bool act[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int e = e0 + u * ngr;
-                    const bool valid = e < ne;
-                    ve[u] = valid ? sm.xv[e] : -INFINITY;
-                    ie[u] = valid ? sm.xi[e] : 0x7fffffff;
-                    wo[u] = (int)(((uint32_t)e * kinv) >> 16);
-                    act[u] = lg < W && lg != wo[u] && ie[u] != 0x7fffffff;
-                    cnt[u] = 0;
-                }
-                if (kp4 <= 16) {
-                    for (int r = 0; r < kp4; r += 4) {
-                        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.xv[lwo + r]);
-                        const int4 i4 = *reinterpret_cast<const int4 *>(&sm.xi[lwo + r]);
-#pragma unroll
-                        for (int u = 0; u < 2; ++u)
-                            cnt[u] += better(v4.x, i4.x, ve[u], ie[u]) + better(v4.y, i4.y, ve[u], ie[u]) +
-                                      better(v4.z, i4.z, ve[u], ie[u]) + better(v4.w, i4.w, ve[u], ie[u]);
-                    }
-                } else {
-                    int lo[2] = {0, 0}, hi[2] = {kp4, kp4};
-                    int nsteps = 0;
-                    while ((1 << nsteps) <= kp4) ++nsteps;
-                    for (int step = 0; step < nsteps; ++step) {
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int mid = (lo[u] + hi[u]) >> 1;
-                            const int f = lwo + min(mid, kp4 - 1);
-                            const bool active = lo[u] < hi[u];
-                            const bool bt = better(sm.xv[f], sm.xi[f], ve[u], ie[u]);
-                            lo[u] = (active && bt) ? mid + 1 : lo[u];
-                            hi[u] = (active && !bt) ? mid : hi[u];
-                        }
-                    }
-                    cnt[0] = lo[0];
-                    cnt[1] = lo[1];
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int e = e0 + u * ngr;
-                    int c = act[u] ? cnt[u] : 0;
-                    if (P >= 2) c += dppi<0xB1>(c);
-                    if (P >= 4) c += dppi<0x4E>(c);
-                    if (P >= 8) c += dppi<0x141>(c);
-                    if (P >= 16) c += dppi<0x140>(c);
-                    const int rank = c + (e - wo[u] * kp4);
-                    if (lg == 0 && e < ne && ie[u] != 0x7fffffff && rank < nkeep) {
-                        sm.byrank[rank] = ie[u];
-                        sm.byv[rank] = ve[u];
-                    }
-                }
-            }
-        }
-        }
-        __syncthreads();                                                   // B3
-        if (topp) {
-            // shortest prefix of the sorted kept entries whose softmax mass
-            // (over every candidate of the level) reaches p
-            if (wave == 0) {
+                // the whole level: ranks among all of it, selected locally
+                partial_ranks(zb, 0, ms);
+                __syncthreads();                                       // B2
+                DTL(5, lvl);
                 float gmax = -INFINITY, den = 0.f;
-                if (st.local) {
-                    for (int i = lane; i < st.m; i += 64) gmax = fmaxf(gmax, sm.s[i]);
+                if (topp) {
+                    for (int i = lane; i < ms; i += 64) gmax = fmaxf(gmax, sm.esc[zb][i]);
                     gmax = wave_max(gmax);
-                    for (int i = lane; i < st.m; i += 64) den += __expf(sm.s[i] - gmax);
-                } else {
-                    const int nw = W * DNW;
-                    for (int i = lane; i < nw; i += 64) gmax = fmaxf(gmax, sm.xm[i]);
-                    gmax = wave_max(gmax);
-                    for (int i = lane; i < nw; i += 64)
-                        if (sm.xm[i] > -INFINITY) den += sm.xs[i] * __expf(sm.xm[i] - gmax);
+                    for (int i = lane; i < ms; i += 64) den += __expf(sm.esc[zb][i] - gmax);
+                    den = wave_sum(den);
                 }
-                den = wave_sum(den);
-                if (lane == 0) {
-                    int ns = nkeep;
-                    float cum = 0.f;
-                    for (int r = 0; r < nkeep; ++r) {
-                        cum += __expf(sm.byv[r] - gmax) / den;
-                        if (cum >= a.p) {
-                            ns = r + 1;
-                            break;
+                nkeep = finalize(zb, 0, ms, st.m, st.cs, nxt, gmax, den);
+            } else {
+                uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;
+                partial_ranks(zb, 0, ms);
+                __syncthreads();                                       // B2
+                DTL(5, lvl);
+                if (wave == 0) {
+                    // this slice's best keff, as words at slot = rank
+                    uint64_t *mine = lw_words + (int64_t)wg * kSlots;
+                    for (int e = lane; e < ms; e += 64) {
+                        const int r = rank_of(zb, e);
+                        if (r < keff)
+                            __hip_atomic_store(&mine[r], pack_word(tag, (uint32_t)sm.eix[zb][e], sm.esc[zb][e]),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    for (int r = ms + lane; r < keff; r += 64)
+                        __hip_atomic_store(&mine[r], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    if (topp) {
+                        float wmax = -INFINITY, wsum = 0.f;
+                        for (int i = lane; i < ms; i += 64) wmax = fmaxf(wmax, sm.esc[zb][i]);
+                        wmax = wave_max(wmax);
+                        for (int i = lane; i < ms; i += 64) wsum += __expf(sm.esc[zb][i] - wmax);
+                        wsum = wave_sum(wsum);
+                        if (lane == 0) {
+                            __hip_atomic_store(&mine[keff], pack_word(tag, 0, wmax), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_store(&mine[keff + 1], pack_word(tag, 0, wsum), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
                         }
                     }
-                    sm.nkeep = ns;
                 }
+                DTL(6, lvl);
+                // every slice's words (bounded polling on the tag) -> the
+                // exchange entries at [kSlice, kSlice + W * keff)
+                const int ne = W * keff;
+                const int nw = ne + (topp ? 2 * W : 0);
+                for (int i = tid; i < nw; i += DNT) {
+                    const int w = i < ne ? i / keff : (i - ne) >> 1;
+                    const int slot = i < ne ? i - w * keff : keff + ((i - ne) & 1);
+                    const uint64_t *src = lw_words + (int64_t)w * kSlots + slot;
+                    uint64_t word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    long spins = 0;
+                    while (word_tag(word) != tag && ++spins < kSpin) {
+                        __builtin_amdgcn_s_sleep(1);
+                        word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    const bool okw = word_tag(word) == tag;
+                    if (!okw) sm.bad = 1;
+                    if (i < ne) {
+                        const uint32_t ix = okw ? word_idx(word) : 0xfffu;
+                        const bool real = ix != 0xfffu;
+                        sm.key[zb][kSlice + i] = real ? sel_key(word_val(word), (int)ix) : 0ull;
+                        sm.esc[zb][kSlice + i] = real ? word_val(word) : -INFINITY;
+                        sm.eix[zb][kSlice + i] = (int16_t)(real ? ix : 0);
+                    } else if (slot == keff) {
+                        sm.xm[w] = okw ? word_val(word) : -INFINITY;
+                    } else {
+                        sm.xs[w] = okw ? word_val(word) : 0.f;
+                    }
+                }
+                __syncthreads();                                       // B3
+                DTL(7, lvl);
+                partial_ranks(zb, kSlice, ne);
+                __syncthreads();                                       // B4
+                DTL(8, lvl);
+                float gmax = -INFINITY, den = 0.f;
+                if (topp) {
+                    for (int w = lane; w < W; w += 64) gmax = fmaxf(gmax, sm.xm[w]);
+                    gmax = wave_max(gmax);
+                    for (int w = lane; w < W; w += 64)
+                        if (sm.xm[w] > -INFINITY) den += sm.xs[w] * __expf(sm.xm[w] - gmax);
+                    den = wave_sum(den);
+                }
+                nkeep = finalize(zb, kSlice, ne, st.m, st.cs, nxt, gmax, den);
             }
-            __syncthreads();
-            nkeep = sm.nkeep;
         }
-        // kept set in node order -> next candidate list, kept flags
-        if (tid < nkeep) {
-            const int ix = sm.byrank[tid];
-            int pos = 0;
-            int r = 0;
-            for (; r + 4 <= nkeep; r += 4) {
-                const int4 b4 = *reinterpret_cast<const int4 *>(&sm.byrank[r]);
-                pos += (b4.x < ix) + (b4.y < ix) + (b4.z < ix) + (b4.w < ix);
-            }
-            for (; r < nkeep; ++r) pos += sm.byrank[r] < ix;
-            const int64_t node = st.cs.id(ix);
-            sm.sel[nxt][pos] = (int)node;
-            if (ix >= s0 && ix < s0 + ms) sm.flag[ix - s0] = 1;
-            if (lvl == 1 && node == last_leaf) sm.in_last = 1;
-        }
-        if (tid == 0) sm.nsel[nxt] = nkeep;
-        __syncthreads();                                                   // B4
-        if (wg == 0 && a.sel) {
-            int *o = a.sel + ((int64_t)unit * levels + (lvl - 1)) * a.sel_stride;
-            for (int r = tid; r < a.sel_stride; r += DNT) o[r] = (r < nkeep) ? sm.sel[nxt][r] : -1;
-        }
+        DTL(9, lvl);
+        write_sel(lvl, nxt, nkeep);
 
-        }
-        // the next step's gathers go out now (one issue point for both paths,
-        // so the loaded registers carry into the next iteration as they are);
-        // this level's unkept candidates are folded while they are in flight
+        // the next step's gathers go out now (one issue point for every
+        // path, so that the loaded registers carry into the next iteration
+        // as they are); this level's unkept candidates are folded while they
+        // are in flight
         const Step<T> stc = st;
-        VR vrc[VBS];
+        VR vrc[VB];
 #pragma unroll
-        for (int u = 0; u < VBS; ++u) vrc[u] = vr[u];
-        cur = nxt;
-        st = make_step(lvl - 1, cur);
+        for (int u = 0; u < VB; ++u) vrc[u] = vr[u];
+        st = make_step(lvl - 1, nxt, nkeep);
         issue_step(st, k0, k1, sc, rb, vr, qcs);
-        if (scored && !a.leaf_only) {
+        DTL(10, lvl);
+        if (!stc.take_all && !a.leaf_only) {
             // this workgroup's own candidates only (a local level was scored
-            // whole by every workgroup)
-            const int zo = stc.local ? stc.fs0 : 0;
-            probs(zo, zo + stc.fms, zb, true, Mn, alpha);
-            __syncthreads();                                               // B5
-            fold(stc, stc.fs0, stc.fms, zb, vrc, zo);
-            zb ^= 1;
+            // whole by every workgroup: its logits sit at the candidate index)
+            fold(stc.fs0, stc.fms, stc.local ? 0 : stc.s0, zb, nxt, nkeep, vrc, Mn, alpha);
         }
+        DTL(11, lvl);
+        if (!stc.take_all) zb ^= 1;
+        cur = nxt;
     }
 
     // token level: this workgroup's range of the candidates, in chunks (the
@@ -865,29 +897,31 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
         score(st, c0, ms, zb, k0, k1, sc, rb, qcs);
         __syncthreads();
+        DTL(12, 0);
         float Mn[G], alpha[G];
-        new_max(Mn, alpha);
-        probs(0, ms, zb, false, Mn, alpha);
-        __syncthreads();
-        fold(st, c0, ms, zb, vr, 0);
+        new_max(zb, Mn, alpha);
+        fold(c0, ms, c0, zb, cur, 0, vr, Mn, alpha);
+        DTL(13, 0);
         zb ^= 1;
     }
 
-    // Partial state of this slice -> tagged words in the workspace; then every
-    // workgroup merges a slice of the output columns from all W partials
-    // (same exchange as the levels: a word is valid when its tag matches).
+    // Partial state of this workgroup: the quarters' sums within each wave by
+    // lane swaps, then across waves in LDS; as tagged words in the workspace.
+    // Every workgroup then merges a slice of the output columns from all W.
     uint64_t *pw_unit = ws.part + unit * (int64_t)W * G * (D + 2);
     {
-        float *red = reinterpret_cast<float *>(hti_dec_lds);     // [DNW][G][D]
-        float lsum[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) lsum[h] = wave_sum(lt[h]);
-        __syncthreads();
+        float *red = reinterpret_cast<float *>(hti_dec_lds);     // [DNW][G][D], then [DNW][G] sums
+        float *redl = red + DNW * G * D;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
+            const float l4 = xsum32(xsum16(lt[h]));
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) red[(wave * G + h) * D + lane * DPL + e] = acc[h][e];
-            if (lane == 0) sm.redz[wave][h] = lsum[h];
+            for (int e = 0; e < EPL; ++e) acc[h][e] = xsum32(xsum16(acc[h][e]));
+            if (lane < 16) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) red[(wave * G + h) * D + sub * EPL + e] = acc[h][e];
+            }
+            if (lane == 0) redl[wave * G + h] = l4;
         }
         __syncthreads();
         uint64_t *mine = pw_unit + (int64_t)wg * G * (D + 2);
@@ -895,30 +929,33 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             const int h = i / (D + 2), e = i % (D + 2);
             float v = 0.f;
             if (e < D) {
+#pragma unroll
                 for (int w = 0; w < DNW; ++w) v += red[(w * G + h) * D + e];
             } else if (e == D) {
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) v = (hh == h) ? M[hh] : v;
             } else {
-                for (int w = 0; w < DNW; ++w) v += sm.redz[w][h];
+#pragma unroll
+                for (int w = 0; w < DNW; ++w) v += redl[w * G + h];
             }
             __hip_atomic_store(&mine[i], ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    DTL(14, 0);
     // Gather n tagged words (word i at src(i)) into LDS at dst(i): every load
     // is issued first, then only words whose tag is not yet current are polled.
     auto gather_words = [&](int n, auto src, auto dst) __attribute__((always_inline)) {
-        for (int i0 = 0; i0 < n; i0 += 4 * DNT) {
-            uint64_t wv[4];
+        for (int i0 = 0; i0 < n; i0 += 2 * DNT) {
+            uint64_t wv[2];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 2; ++u) {
                 const int i = i0 + u * DNT + tid;
                 wv[u] = (i < n) ? __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                 : ((uint64_t)tag << 32);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 2; ++u) {
                 const int i = i0 + u * DNT + tid;
                 if (i >= n) continue;
                 long spins = 0;
@@ -927,7 +964,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     wv[u] = __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 if ((uint32_t)(wv[u] >> 32) != tag) {
-                    __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sm.bad = 1;
                     wv[u] = 0x7fc00000u;          // NaN: the result is visibly invalid
                 }
                 *dst(i) = __uint_as_float((uint32_t)wv[u]);
@@ -936,11 +973,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     };
     // (max, denominator) of every slice per head, and this workgroup's output
     // columns of every slice's unnormalised output, into LDS (one round)
+    __syncthreads();
     const int cols = (D + W - 1) / W;
     const int d0 = min(D, wg * cols), d1 = min(D, d0 + cols);
     const int nc = d1 - d0;
-    float *mw = reinterpret_cast<float *>(hti_dec_lds) + DNW * G * D;   // [W][G][2]
-    float *aw = mw + kMaxW * G * 2;                                      // [W][G][nc]
+    float *mw = reinterpret_cast<float *>(hti_dec_lds) + DNW * G * D + DNW * G;   // [W][G][2]
+    float *aw = mw + kMaxW * G * 2;                                               // [W][G][nc]
     const int nmw = W * G * 2;
     gather_words(nmw + W * G * nc, [&](int i) __attribute__((always_inline)) {
         if (i < nmw) {
@@ -952,11 +990,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         return pw_unit + ((int64_t)w * G + r / nc) * (D + 2) + d0 + (r % nc);
     }, [&](int i) __attribute__((always_inline)) { return i < nmw ? mw + i : aw + (i - nmw); });
     __syncthreads();
-    // a wait that timed out anywhere in this unit (a workgroup that was not
-    // resident in time) makes its output NaN rather than silently wrong
+    DTL(15, 0);
+    // a wait that ran out in this workgroup, or anywhere before (the status
+    // word), leaves NaN
+    if (tid == 0 && sm.bad) __hip_atomic_store(ws.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool failed = sm.bad != 0 ||
-        __hip_atomic_load(&ws.err[unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-    const int64_t row = ((int64_t)bi * a.Nq + qi) * t.Hq + (int64_t)g * G;
+        __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
     for (int i = tid; i < G * nc; i += DNT) {
         const int h = i / nc, c = i % nc;
         float Mx = -INFINITY;
@@ -969,7 +1008,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             num += aw[(w * G + h) * nc + c] * f;
             den += mw[(w * G + h) * 2 + 1] * f;
         }
-        a.out[(row + h) * D + d0 + c] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? num / den : 0.f;
+        a.out[(orow + h) * D + d0 + c] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? num / den : 0.f;
     }
     if (wg == 0 && tid < G && a.lse) {
         const int h = tid;
@@ -980,134 +1019,196 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             const float Mw = mw[(w * G + h) * 2];
             if (Mw != -INFINITY) den += mw[(w * G + h) * 2 + 1] * __expf(Mw - Mx);
         }
-        a.lse[row + h] = den > 0.f ? Mx + logf(den) : -INFINITY;
+        a.lse[orow + h] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? Mx + logf(den) : -INFINITY;
     }
+    DTL(16, 0);
+#ifdef HTI_DECODE_TIMELINE
+    if (tid == 0 && blockIdx.x < kTlMaxBlocks) {
+        uint64_t *tr = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws.status) + 256) +
+                       (int64_t)blockIdx.x * kTlEvents;
+        for (int i = 0; i < kTlEvents; ++i) tr[i] = i < tln ? sm.tl[i] : 0ull;
+    }
+#endif
     // every workgroup of this unit has read the launch tag (they all published
     // their partial state above), so the next launch may move it on
     if (wg == 0 && tid == 0) ws.epoch[unit] = ws.epoch[unit] + 1u;
     // decode step: once every workgroup of the sequence has read the old
     // length (bounded wait), the first workgroup of its first unit stores the
-    // new one and clears the count for the next step
+    // new one and clears the count for the next step; if the wait runs out,
+    // the length stays and the status word is set
     if (a.k_new != nullptr && wg == 0 && g == 0 && qi == 0 && tid == 0) {
         const uint32_t need = (uint32_t)W * (uint32_t)t.Hkv * (uint32_t)a.Nq;
         long spins = 0;
         while (__hip_atomic_load(&ws.seqcnt[bi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need &&
                ++spins < kSpin)
             __builtin_amdgcn_s_sleep(1);
-        if (spins >= kSpin) __hip_atomic_store(&ws.err[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (sm.app) __hip_atomic_store(&t.len[bi], (int64_t)sm.lold + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ws.seqcnt[bi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (spins >= kSpin || failed) {
+            __hip_atomic_store(ws.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (sm.app)
+                __hip_atomic_store(&t.len[bi], (int64_t)sm.lold + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ws.seqcnt[bi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
 template <int G, int D>
 constexpr size_t dec_dyn_bytes()
 {
-    // per-wave partial outputs, then the gathered (max, denominator) and
-    // output columns of every slice
-    return (size_t)(DNW * G * D + kMaxW * G * 2 + kMaxW * G * ((D + kMaxW - 1) / kMaxW) + G * D) *
-           sizeof(float);
+    // per-wave partial outputs and sums, then the gathered (max, denominator)
+    // and output columns of every slice
+    // (W * ceil(D / W) <= D + W - 1 columns over all slices)
+    return (size_t)(DNW * G * D + DNW * G + kMaxW * G * 2 + G * (D + kMaxW)) * sizeof(float);
+}
+
+namespace {
+
+// Per-device, per-instance facts the host side caches: whether the dynamic
+// LDS attribute was set and how many workgroups of the instance one CU holds.
+struct DecInstInfo {
+    bool attr = false;
+    int per_cu = 0;
+};
+std::mutex g_dec_mu;
+std::vector<std::pair<std::pair<int, const void *>, DecInstInfo>> g_dec_info;   // (device, kernel) -> info
+std::vector<std::pair<int, int>> g_dev_cus;                                       // device -> CU count
+
+DecInstInfo &dec_info_locked(int dev, const void *kern)
+{
+    for (auto &p : g_dec_info)
+        if (p.first.first == dev && p.first.second == kern) return p.second;
+    g_dec_info.push_back({{dev, kern}, DecInstInfo{}});
+    return g_dec_info.back().second;
 }
 
 template <typename T, int D, int G, bool F8>
-static hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+hipError_t dec_prepare(int dev, DecInstInfo *out)
 {
     auto kern = k_decode_split<T, D, G, F8>;
     const size_t dyn = dec_dyn_bytes<G, D>();
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    std::lock_guard<std::mutex> lk(g_dec_mu);
+    DecInstInfo &info = dec_info_locked(dev, (const void *)kern);
+    if (!info.attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        int per_cu = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, DNT, dyn);
+        if (e != hipSuccess) return e;
+        info.per_cu = per_cu;
+        info.attr = true;
     }
+    *out = info;
+    return hipSuccess;
+}
+
+template <typename T, int D, int G, bool F8>
+hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    DecInstInfo info;
+    if ((e = dec_prepare<T, D, G, F8>(dev, &info)) != hipSuccess) return e;
     TravArgs aa = a;
     DecodeWs ww = ws;
     void *args[] = {&aa, &ww};
     // A plain launch: the workgroups of a unit wait for each other, which
     // needs them resident together.  The plan keeps the grid within what the
-    // device holds at once (one workgroup per compute unit, or as many as the
-    // occupancy admits), so they all are whenever the device is not held by
-    // other work; every wait is bounded and a timeout shows as NaN
-    // output (a cooperative launch would guarantee residency but costs more
+    // device holds at once, so they all are whenever the device is not held
+    // by other work; every wait is bounded and a timeout sets the status
+    // word (a cooperative launch would guarantee residency but costs more
     // than the whole kernel to dispatch).
-    return hipLaunchKernel((const void *)kern, dim3((unsigned)(units * ws.W)), dim3(DNT), args, dyn, s);
+    return hipLaunchKernel((const void *)k_decode_split<T, D, G, F8>, dim3((unsigned)(units * ws.W)), dim3(DNT),
+                           args, dec_dyn_bytes<G, D>(), s);
 }
 
-// 8-bit router keys: bf16 caches only
-template <typename T, int D, int G>
-static hipError_t dec_launch(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+// Dispatch over the instances: 8-bit router keys with bf16 caches only.
+template <typename T, int D, int G, typename Fn>
+hipError_t dec_dispatch_f8(bool rfp8, Fn &&fn)
 {
     if constexpr (std::is_same<T, bf16_t>::value)
-        if (a.t.rfp8) return dec_launch_k<T, D, G, true>(a, ws, units, s);
-    if (a.t.rfp8) return hipErrorInvalidValue;
-    return dec_launch_k<T, D, G, false>(a, ws, units, s);
+        if (rfp8) return fn(std::integral_constant<bool, true>{});
+    if (rfp8) return hipErrorInvalidValue;
+    return fn(std::integral_constant<bool, false>{});
 }
 
-template <typename T, int D>
-static hipError_t dec_g(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+template <typename T, int D, typename Fn>
+hipError_t dec_dispatch_g(int G, bool rfp8, Fn &&fn)
 {
-    switch (a.t.G) {
-    case 1: return dec_launch<T, D, 1>(a, ws, units, s);
-    case 2: return dec_launch<T, D, 2>(a, ws, units, s);
-    case 4: return dec_launch<T, D, 4>(a, ws, units, s);
-    default: return dec_launch<T, D, 8>(a, ws, units, s);
+    auto go = [&](auto gc) {
+        constexpr int GG = decltype(gc)::value;
+        return dec_dispatch_f8<T, D, GG>(rfp8, [&](auto f8) { return fn(std::integral_constant<int, GG>{}, f8); });
+    };
+    switch (G) {
+    case 1: return go(std::integral_constant<int, 1>{});
+    case 2: return go(std::integral_constant<int, 2>{});
+    case 4: return go(std::integral_constant<int, 4>{});
+    default: return go(std::integral_constant<int, 8>{});
     }
 }
+
+template <typename Fn>
+hipError_t dec_dispatch(const TravArgs &a, Fn &&fn)
+{
+    const bool r8 = a.t.rfp8 != 0;
+    auto with = [&](auto tc, auto dc) {
+        using TT = typename decltype(tc)::type;
+        constexpr int DD = decltype(dc)::value;
+        return dec_dispatch_g<TT, DD>(a.t.G, r8, [&](auto gc, auto f8) {
+            return fn(tc, dc, gc, f8);
+        });
+    };
+    struct BF { using type = bf16_t; };
+    struct FP { using type = float; };
+    if (a.t.dtype == HTI_BF16)
+        return a.t.D == 128 ? with(BF{}, std::integral_constant<int, 128>{}) : with(BF{}, std::integral_constant<int, 64>{});
+    return a.t.D == 128 ? with(FP{}, std::integral_constant<int, 128>{}) : with(FP{}, std::integral_constant<int, 64>{});
+}
+
+} // namespace
 
 hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
 {
     if (units <= 0) return hipSuccess;
-    if (a.t.dtype == HTI_BF16)
-        return a.t.D == 128 ? dec_g<bf16_t, 128>(a, ws, units, s) : dec_g<bf16_t, 64>(a, ws, units, s);
-    return a.t.D == 128 ? dec_g<float, 128>(a, ws, units, s) : dec_g<float, 64>(a, ws, units, s);
-}
-
-template <typename T, int D, int G>
-static hipError_t dec_capacity(int *blocks_per_cu)
-{
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_decode_split<T, D, G, false>, DNT,
-                                                        dec_dyn_bytes<G, D>());
-}
-
-template <typename T, int D>
-static hipError_t dec_capacity_g(int G, int *per_cu)
-{
-    switch (G) {
-    case 1: return dec_capacity<T, D, 1>(per_cu);
-    case 2: return dec_capacity<T, D, 2>(per_cu);
-    case 4: return dec_capacity<T, D, 4>(per_cu);
-    default: return dec_capacity<T, D, 8>(per_cu);
-    }
+    return dec_dispatch(a, [&](auto tc, auto dc, auto gc, auto f8) {
+        using TT = typename decltype(tc)::type;
+        return dec_launch_k<TT, decltype(dc)::value, decltype(gc)::value, decltype(f8)::value>(a, ws, units, s);
+    });
 }
 
 hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W)
 {
-    static int cached_key = -1, cached_cus = 0, cached_per_cu = 0;
-    const int key = a.t.dtype * 1000 + a.t.D * 10 + a.t.G;
-    if (key != cached_key) {
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        if (a.t.dtype == HTI_BF16)
-            e = a.t.D == 128 ? dec_capacity_g<bf16_t, 128>(a.t.G, &per_cu) : dec_capacity_g<bf16_t, 64>(a.t.G, &per_cu);
-        else
-            e = a.t.D == 128 ? dec_capacity_g<float, 128>(a.t.G, &per_cu) : dec_capacity_g<float, 64>(a.t.G, &per_cu);
-        if (e != hipSuccess) return e;
-        cached_key = key;
-        cached_cus = cus;
-        cached_per_cu = per_cu;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lk(g_dec_mu);
+        for (auto &p : g_dev_cus)
+            if (p.first == dev) cus = p.second;
     }
+    if (cus == 0) {
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        std::lock_guard<std::mutex> lk(g_dec_mu);
+        g_dev_cus.push_back({dev, cus});
+    }
+    // occupancy of the instance that will be launched
+    int per_cu = 0;
+    e = dec_dispatch(a, [&](auto tc, auto dc, auto gc, auto f8) {
+        using TT = typename decltype(tc)::type;
+        DecInstInfo info;
+        hipError_t r = dec_prepare<TT, decltype(dc)::value, decltype(gc)::value, decltype(f8)::value>(dev, &info);
+        per_cu = info.per_cu;
+        return r;
+    });
+    if (e != hipSuccess) return e;
     // one workgroup per CU keeps every unit's slices on distinct CUs; more
     // per CU (as many as fit, at most four) only where fewer leave a unit
-    // short of its slices or of eight workgroups (measured at 1M tokens:
-    // eight per unit beat four and sixteen)
+    // short of its slices or of eight workgroups
     const int64_t need = (max_summary + kSlice - 1) / kSlice;
     const int64_t want = std::max<int64_t>(need, 8);
     int64_t w = 0;
-    for (int per = 1; per <= std::min(cached_per_cu, 4); ++per) {
-        w = (int64_t)cached_cus * per / (units > 0 ? units : 1);
+    for (int per = 1; per <= std::min(per_cu, 4); ++per) {
+        w = (int64_t)cus * per / (units > 0 ? units : 1);
         if (w >= want) break;
     }
     if (w > kMaxW) w = kMaxW;
@@ -1118,8 +1219,9 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
 size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D)
 {
     size_t off = 0;
+    off += 256;                                                   // status
+    off += kTlBytes;                                              // phase timeline (timeline build)
     off += ((size_t)units * 4 + 255) / 256 * 256;                 // epoch
-    off += ((size_t)units * 4 + 255) / 256 * 256;                 // err
     off += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
     off += ((size_t)units * W * G * (D + 2) * 8 + 255) / 256 * 256;
     off += ((size_t)B * 4 + 255) / 256 * 256;                     // seqcnt
@@ -1130,9 +1232,9 @@ DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, i
     DecodeWs w{};
     char *p = (char *)base;
     w.W = W;
+    w.status = (uint32_t *)p;
+    p += 256 + kTlBytes;
     w.epoch = (uint32_t *)p;
-    p += ((size_t)units * 4 + 255) / 256 * 256;
-    w.err = (uint32_t *)p;
     p += ((size_t)units * 4 + 255) / 256 * 256;
     w.words = (uint64_t *)p;
     p += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;

@@ -41,6 +41,7 @@ struct TravArgs {
     int leaf_only;     // 1: summaries route but do not join the softmax
     uint32_t binv;     // ceil(2^32 / b), for division by b in index arithmetic
     const void *q;     // decode [B, Nq, Hq, D]; prefill [B, T, Hq, D]
+    const int64_t *q_pos;  // decode [B, Nq]: each query attends to tokens 0..q_pos (nullable: len - 1)
     int Nq;            // queries per sequence (decode) or block length T (prefill)
     float *out;        // decode [B, Nq, Hq, D]
     float *lse;        // decode [B, Nq, Hq] (nullable)
@@ -58,13 +59,13 @@ struct TravArgs {
 };
 
 // Workspace of the split decode (zeroed by the caller before first use, then
-// owned by the library): per-unit launch epoch, per-unit timeout marks, the
-// per-level exchange words and the per-workgroup partial states, all as words
-// tagged with the launch epoch.
+// owned by the library): a status word, per-unit launch epochs, the per-level
+// exchange words and the per-workgroup partial states, all as words tagged
+// with the launch epoch.
 struct DecodeWs {
     int W;              // workgroups per (query, KV group) unit
+    uint32_t *status;   // nonzero once a wait ran out (sticky until the workspace is zeroed)
     uint32_t *epoch;    // [units]
-    uint32_t *err;      // [units]: tag of the last launch in which a wait timed out
     uint64_t *words;    // [units][levels][W][HTI_MAX_SELECT + 2]
     uint64_t *part;     // [units][W][G][D + 2]: tag << 32 | fp32 bits
     uint32_t *seqcnt;   // [B]: workgroups of a decode step that have read the sequence length
@@ -74,6 +75,10 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
 size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D);
 DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, int G, int D);
 hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s);
+
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per (device, kernel) (thread-safe).
+hipError_t set_dyn_lds_once(const void *kern, size_t bytes);
 
 hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s);
 hipError_t launch_build_level(const TreeArgs &t, int lvl, int64_t max_nodes, hipStream_t s);

@@ -113,7 +113,12 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
     const int bi = (int)(rest / a.Nq);
     const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const int b = t.b, levels = t.levels, R = t.R;
-    const int64_t L = t.len[bi];
+    int64_t L = t.len[bi];
+    if (!PREFILL && a.q_pos) {
+        // a decode query at position q_pos attends to the tree of tokens 0..q_pos
+        const int64_t ql = a.q_pos[(int64_t)bi * a.Nq + qi];
+        if (ql < L - 1) L = ql < 0 ? 0 : ql + 1;
+    }
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
 
     if (tid == 0) {
@@ -712,12 +717,9 @@ static hipError_t trav_launch_k(const TravArgs &a, int64_t units, hipStream_t s)
     constexpr bool STAGE = !PF;
     auto kern = k_traverse<T, D, G, PF, NWV, STAGE, F8>;
     const size_t dyn = STAGE ? kVStageBytes : 0;
-    static bool attr_set = false;
-    if (!attr_set && dyn > 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (dyn > 0) {
+        hipError_t e = set_dyn_lds_once((const void *)kern, dyn);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(NWV * 64), dyn, s, a);
     return hipGetLastError();

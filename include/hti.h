@@ -20,7 +20,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, unless the
  *     argument says "host".  The library never allocates, frees or retains
  *     device memory; the only device state it keeps between calls is in the
- *     decode workspace the caller hands it (per-unit launch counters).
+ *     decode workspace the caller hands it (a status word, per-unit launch
+ *     counters, per-sequence step counts).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *     call only enqueues work on it and returns; results are valid once the
  *     stream has reached that point.
@@ -59,7 +60,8 @@ typedef enum {
     HTI_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle (d, G, ...) */
     HTI_ERR_CAPACITY = -3,    /* a length exceeds a buffer capacity */
     HTI_ERR_WORKSPACE = -4,   /* workspace missing or too small */
-    HTI_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
+    HTI_ERR_LAUNCH = -5,      /* the HIP runtime refused a launch */
+    HTI_ERR_TIMEOUT = -6      /* a split decode's workgroups ran out of a wait (hti_decode_status) */
 } hti_status;
 
 typedef enum { HTI_F32 = 0, HTI_BF16 = 1 } hti_dtype;
@@ -202,14 +204,20 @@ hti_status hti_tree_extend(const hti_tree *tree, const void *k_blk, const void *
 size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t Nq);
 
 /*
- * hti_sparse_decode: attention of Nq query tokens per sequence, each at
- * position len[s] - 1, over that sequence's trees.
- *   q:   [B, Nq, Hq, d] in the cache dtype (un-rotated)
- *   out: [B, Nq, Hq, d] fp32 attention output
- *   lse: [B, Nq, Hq] fp32 log-sum-exp of the logits (nullable)
- *   sel: [B, Nq, Hkv, levels, sel_stride] int32 (nullable): node ids kept at
- *        each level (row l-1 = level l), ascending, -1 padded;
- *        sel_stride >= k (top-k) or cap (top-p).
+ * hti_sparse_decode: attention of Nq query tokens per sequence over that
+ * sequence's trees.
+ *   q:     [B, Nq, Hq, d] in the cache dtype (un-rotated)
+ *   q_pos: [B, Nq] int64 (nullable): query n of sequence s sits at position
+ *          q_pos[s, n] and attends to the tree of tokens 0..q_pos[s, n] -- the
+ *          nodes wholly inside that prefix, as a decode at length q_pos + 1
+ *          would see them.  NULL puts every query at len[s] - 1.  Values at
+ *          or above len[s] - 1 act as len[s] - 1; a negative value attends to
+ *          nothing (output 0, lse -inf).
+ *   out:   [B, Nq, Hq, d] fp32 attention output
+ *   lse:   [B, Nq, Hq] fp32 log-sum-exp of the logits (nullable)
+ *   sel:   [B, Nq, Hkv, levels, sel_stride] int32 (nullable): node ids kept at
+ *          each level (row l-1 = level l), ascending, -1 padded;
+ *          sel_stride >= k (top-k) or cap (top-p).
  * Per (query, KV group): the top level's nodes are all candidates; at each
  * level the candidates are scored by the mean over the group's heads of the
  * RoPE'd logits (candidate i at position i, the query at position |C_l|), the
@@ -220,24 +228,40 @@ size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel
  * Source: RecSA abstract; ZHA Figure 3 caption (top-p routing).
  *   ws, ws_bytes: device workspace of hti_decode_workspace_bytes(cfg, sel, Nq)
  *        bytes, filled with zeros before its first use and then left to the
- *        library (it keeps per-unit launch counters there).  With a workspace
- *        each unit is split over up to HTI_DECODE_MAX_SPLIT workgroups that
- *        wait on each other's partial results; the grid is kept within what
- *        the device holds at once (one workgroup per compute unit, or as many
- *        as the kernel's occupancy admits, at most four, where one per CU
- *        would leave a unit fewer than eight) so that all are resident while
- *        the device runs nothing else.  Every wait is bounded: if work on other
- *        streams keeps some workgroups from starting in time, the affected
- *        outputs are NaN.  ws = NULL runs one independent workgroup per unit.
- *        One workspace serves one (cfg, Nq) shape and one stream at a time:
- *        calls that share it must not overlap.
+ *        library (it keeps a status word and per-unit launch counters there).
+ *        With a workspace each unit is split over up to HTI_DECODE_MAX_SPLIT
+ *        workgroups that wait on each other's partial results; the grid is
+ *        kept within what the device holds at once (one workgroup per
+ *        compute unit, or as many as the kernel's occupancy admits, at most
+ *        four, where one per CU would leave a unit fewer than eight) so that
+ *        all are resident while the device runs nothing else.  Every wait is
+ *        bounded: if work on other streams keeps some workgroups from starting
+ *        in time, the wait runs out, the launch's outputs are NaN and the
+ *        workspace's status word is set; every later launch with that
+ *        workspace then writes NaN and changes nothing else until the caller
+ *        zeroes the workspace (hti_decode_status reports it).  ws = NULL runs
+ *        one independent workgroup per unit (no waits).  One workspace serves
+ *        one (cfg, Nq) shape and one stream at a time: calls that share it
+ *        must not overlap.
  * Errors additionally: HTI_ERR_CAPACITY if rope_npos is below the positions
  * this cfg/selection can reach, HTI_ERR_UNSUPPORTED if a summary level can
  * exceed HTI_MAX_CAND candidates, HTI_ERR_WORKSPACE if ws_bytes is too small.
  */
 hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const void *q,
-                             int32_t Nq, float *out, float *lse, int32_t *sel_out,
-                             int32_t sel_stride, void *ws, size_t ws_bytes, void *stream);
+                             const int64_t *q_pos, int32_t Nq, float *out, float *lse,
+                             int32_t *sel_out, int32_t sel_stride, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/*
+ * hti_decode_status: whether a split decode with this workspace has run out
+ * of a wait (see hti_sparse_decode).  Synchronises `stream`, reads the
+ * workspace's status word (4 bytes at its start) and returns HTI_OK, or
+ * HTI_ERR_TIMEOUT if the word is set: the outputs of the launch that set it
+ * and of every later one with this workspace are NaN, and no decode step
+ * advanced a length since; the tree itself stays consistent with its stored
+ * lengths.  Zeroing the workspace clears the word.
+ */
+hti_status hti_decode_status(const void *ws, size_t ws_bytes, void *stream);
 
 /*
  * hti_decode_step: one decode step of every sequence -- append the step's
@@ -250,7 +274,9 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
  * a (sequence, KV group) writes the new row and pools the nodes it completes
  * itself (identical bytes), and one workgroup per sequence advances len once
  * every workgroup of that sequence has read the old value (a bounded wait; a
- * timeout marks the affected outputs NaN as in hti_sparse_decode).  Otherwise
+ * timeout sets the status word and leaves the length, as in
+ * hti_sparse_decode).  The queries sit at len[s] - 1 of the grown sequence
+ * (no q_pos).  Otherwise
  * it runs the two calls.  The workspace keeps a per-sequence count between
  * steps, so steps that share it must not overlap.
  * Source: RecSA abstract (decoding over the tree); ZHA Table VIII (decode

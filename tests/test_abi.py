@@ -82,17 +82,17 @@ def test_decode_validation_before_launch():
     s = hti.make_select("topk", k=8)
     out = C.c_void_p(0x2000)
     # NULL q
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s), None, 1, out, None, None, 0, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s), None, None, 1, out, None, None, 0, None, 0, None) == -1
     # k out of range
     s_bad = hti.make_select("topk", k=33)
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s_bad), 0x3000, 1, out, None, None, 0, None, 0, None) == -2
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s_bad), 0x3000, None, 1, out, None, None, 0, None, 0, None) == -2
     # top-p with p outside (0, 1]
     s_p = hti.make_select("topp", p=1.5, cap=16)
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s_p), 0x3000, 1, out, None, None, 0, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s_p), 0x3000, None, 1, out, None, None, 0, None, 0, None) == -1
     # routing flag other than 0 / 1
     s_r = hti.make_select("topk", k=8)
     s_r.per_head = 2
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s_r), 0x3000, 1, out, None, None, 0, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s_r), 0x3000, None, 1, out, None, None, 0, None, 0, None) == -1
     # per-head routing: the workspace grows with the units (query heads, not KV groups)
     s_h = hti.make_select("topk", k=8, per_head=True)
     assert L.hti_decode_workspace_bytes(C.byref(c), C.byref(s_h), 1) > \
@@ -101,22 +101,25 @@ def test_decode_validation_before_launch():
         L.hti_prefill_workspace_bytes(C.byref(c), C.byref(s), 64)
     # RoPE table too short for the reachable positions
     t2 = _tree_struct(cfg(rope_npos=100))
-    assert L.hti_sparse_decode(C.byref(t2), C.byref(s), 0x3000, 1, out, None, None, 0, None, 0, None) == -3
+    assert L.hti_sparse_decode(C.byref(t2), C.byref(s), 0x3000, None, 1, out, None, None, 0, None, 0, None) == -3
     # sel_out with too small a stride
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, 1, out, None, 0x4000, 4, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, None, 1, out, None, 0x4000, 4, None, 0, None) == -1
     # a level with more candidates than the kernel's LDS holds
     t3 = _tree_struct(cfg(levels=1, b=32, rope_npos=1 << 16))      # top level 4096 nodes
-    assert L.hti_sparse_decode(C.byref(t3), C.byref(s), 0x3000, 1, out, None, None, 0, None, 0, None) == -2
+    assert L.hti_sparse_decode(C.byref(t3), C.byref(s), 0x3000, None, 1, out, None, None, 0, None, 0, None) == -2
     # missing level buffer
     t4 = _tree_struct(c)
     t4.lvl_v[2] = None
-    assert L.hti_sparse_decode(C.byref(t4), C.byref(s), 0x3000, 1, out, None, None, 0, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t4), C.byref(s), 0x3000, None, 1, out, None, None, 0, None, 0, None) == -1
     # workspace given but too small
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, 1, out, None, None, 0, 0x5000, 16,
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, None, 1, out, None, None, 0, 0x5000, 16,
                                None) == -4
     assert L.hti_decode_workspace_bytes(C.byref(c), C.byref(s), 1) > 16
     # Nq < 1
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, 0, out, None, None, 0, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, None, 0, out, None, None, 0, None, 0, None) == -1
+    # status query without a workspace
+    assert L.hti_decode_status(None, 0, None) == -1
+    assert L.hti_decode_status(0x5000, 2, None) == -1
 
 
 def test_build_append_prefill_validation():
@@ -171,7 +174,7 @@ def test_router_fp8_cfg_and_buffers():
     # the copies' buffers: missing ones are rejected by every call that needs the tree
     t = _tree_struct(c)
     s = hti.make_select("topk", k=8)
-    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, 1, 0x2000, None, None, 0, None, 0, None) == -1
+    assert L.hti_sparse_decode(C.byref(t), C.byref(s), 0x3000, None, 1, 0x2000, None, None, 0, None, 0, None) == -1
     Ls = (C.c_int64 * 2)(10, 10)
     assert L.hti_tree_build(C.byref(t), Ls, None) == -1
     assert L.hti_tree_append(C.byref(t), 0x3000, 0x3000, None) == -1

@@ -131,6 +131,89 @@ def test_decode_parity(w):
     _check_decode(ts, w, K, V, refs, Ls, q, trees=trees, upload=True, split=False)
 
 
+QPOS_CASES = [
+    W.DEC128K.replace(name="qpos_b32", B=2, L=32 * 32 * 3 + 77, levels=2, needles=0, Nq=5),
+    W.ZHA2M.replace(name="qpos_topp_r4", L=16 ** 3 * 2 + 33, levels=3, Nq=4),
+]
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("w", QPOS_CASES, ids=lambda w: w.name)
+def test_decode_q_pos(w, split):
+    """Queries at their own positions (q_pos): each attends to the tree of
+    tokens 0..q_pos, which the oracle builds over q_pos + 1 tokens.  The
+    positions span a node boundary, an upper-level boundary, the last token,
+    values past it (clamped to len - 1) and a negative one (nothing: 0 out,
+    -inf lse)."""
+    L = w.L
+    ts, K, V, refs, Ls = _setup(w, Lcap=L, Ls=[L] * w.B)
+    q = W.gen_queries(w)
+    pos = np.array([[L - 1, 32 * 32 * 2 - 1, 31, L + 40, 1000][: w.Nq],
+                    [L - 2, 16 ** 3 - 1, 16 ** 2 * 3 + 5, -1, 7][: w.Nq]][: w.B], np.int64)
+    qp = torch.from_numpy(pos).to(DEV)
+    out = torch.empty((w.B, w.Nq, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, w.Nq, w.Hq), dtype=torch.float32, device=DEV)
+    so = torch.empty((w.B, w.Nq, w.Hkv, w.levels, kmax_of(w)), dtype=torch.int32, device=DEV)
+    ts.sparse_decode(select_of(w), q.to(DEV).contiguous(), out, lse, so, split=split, q_pos=qp)
+    torch.cuda.synchronize()
+    out, lse, so = out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
+    nex = 0
+    for bi in range(w.B):
+        for qi in range(w.Nq):
+            p = int(pos[bi, qi])
+            if p < 0:
+                assert (out[bi, qi] == 0).all() and np.isneginf(lse[bi, qi]).all()
+                assert (so[bi, qi] == -1).all()
+                continue
+            Lq = min(p, L - 1) + 1
+            for g in range(w.Hkv):
+                tree = oracle_tree(w, K[bi, g], V[bi, g], refs[g], Lq)
+                hs = slice(g * w.G, (g + 1) * w.G)
+                ex, _ = accept(w, tree, K[bi, g, :Lq], V[bi, g, :Lq], q[bi, qi, hs], out[bi, qi, hs],
+                               lse[bi, qi, hs], so[bi, qi, g])
+                nex += ex
+    log(f"  {w.name} split={split}: positions {pos.tolist()} exempt={nex}")
+
+
+def test_decode_status_is_sticky():
+    """The workspace's status word (set here from the host, standing in for a
+    wait that ran out): the next decode and decode step write NaN, leave the
+    length and the cache alone, and hti_decode_status reports the timeout;
+    after the workspace is zeroed the same calls give the normal results."""
+    w = W.DEC128K.replace(name="status", B=2, L=32 * 40 + 31, levels=2, needles=0)
+    Lcap = w.L + 2
+    ts, K, V, refs, Ls = _setup(w, Lcap=Lcap, Ls=[w.L] * w.B)
+    sel = select_of(w)
+    q = W.gen_queries(w).to(DEV).contiguous()
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    ts.sparse_decode(sel, q, out)
+    ts.decode_status(sel, 1)
+    good = out.clone()
+    ws = ts.decode_workspace(sel, 1)
+    ws[:4] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device=DEV)   # status word
+    ts.sparse_decode(sel, q, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    with pytest.raises(hti.HTIError) as ei:
+        ts.decode_status(sel, 1)
+    assert ei.value.status == -6
+    kn, vn = W.gen_append(w, 0, device=DEV)
+    k_before = ts.k_cache[:, :, w.L].clone()
+    ts.decode_step(sel, kn.contiguous(), vn.contiguous(), q, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    assert ts.len.cpu().tolist() == [w.L] * w.B
+    assert torch.equal(ts.k_cache[:, :, w.L], k_before)
+    ws.zero_()
+    ts.sparse_decode(sel, q, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, good)
+    ts.decode_step(sel, kn.contiguous(), vn.contiguous(), q, out)
+    ts.decode_status(sel, 1)
+    assert ts.len.cpu().tolist() == [w.L + 1] * w.B
+    assert torch.isfinite(out).all()
+
+
 @pytest.mark.parametrize("split", [True, False])
 def test_decode_exact_ties(split):
     """Exactly equal scores: zero keys score 0 at every position.  With all

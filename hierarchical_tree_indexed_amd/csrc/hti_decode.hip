@@ -52,7 +52,7 @@ namespace hti {
 
 namespace {
 
-constexpr int DNT = 512;              // threads per workgroup (two waves per SIMD)
+constexpr int DNT = 256;              // threads per workgroup (one wave per SIMD)
 constexpr int DNW = DNT / 64;         // waves
 constexpr int DNQ = DNT / 16;         // 16-lane rows ("quarters")
 constexpr int kSlice = 128;           // candidates one workgroup scores at once
@@ -61,10 +61,10 @@ constexpr int kSlots = kMaxSel + 2;   // words per (level, workgroup): k entries
 constexpr int kMaxEnt = kMaxW * kMaxSel;   // entries of one exchange
 constexpr int kSelN = kSlice + kMaxEnt;    // selection entries of one level: slice, then exchange
 constexpr int KB = 4;                 // key rows per quarter per batch
-constexpr int VB = kSlice / DNQ;      // value rows per quarter per level (4)
+constexpr int VB = 2;                 // value rows per quarter held in registers (more are loaded at the fold)
 constexpr long kSpin = 1L << 22;      // polls of one word before a wait gives up
 
-static_assert(VB * DNQ == kSlice, "the value rows of a slice fit one register batch");
+
 
 // Phase timeline (a separate build of this file with HTI_DECODE_TIMELINE
 // defined, for measurement only): thread 0 of every workgroup notes the
@@ -105,6 +105,8 @@ struct DSmem {
     int wcix[2][DNW][kMaxSel];
     int wrix[DNW][kMaxSel];
     float wrsc[DNW][kMaxSel];
+    uint8_t wflag[2][DNW][kSlice] __attribute__((aligned(4)));   // per wave: kept flags of its fold slice
+    uint64_t wkx[DNW][128];           // per wave: the exchange keys it read
     float xm[kMaxW], xs[kMaxW];       // top-p: each slice's (max, exp-sum) of group scores
     int n[HTI_MAX_LEVELS + 1];        // nodes per level (n[0] = tokens)
     const void *lkp[HTI_MAX_LEVELS];  // this unit's level keys / values
@@ -216,15 +218,27 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     extern __shared__ __attribute__((aligned(16))) unsigned char hti_dec_lds[];
 
     const TreeArgs &t = a.t;
-    const int W = ws.W;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Every 64-byte line of the argument block goes into the scalar cache in
+    // one round trip, before the first field is used: each launch's arguments
+    // are fresh memory, and fields read later, one line at a time as the code
+    // first needs them, would each wait for their own miss.
+    int W = ws.W;
+    {
+        const uint32_t *kp = (const uint32_t *)__builtin_amdgcn_kernarg_segment_ptr();
+        constexpr int kLines = (int)((sizeof(TravArgs) + sizeof(DecodeWs) + 63) / 64) + 1;
+        uint32_t touch = 0;
+#pragma unroll
+        for (int i = 0; i < kLines; ++i) touch ^= kp[i * 16];
+        asm volatile("" : "+s"(W) : "s"(touch));
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sub = lane & 15, quarter = tid >> 4;
-    const int64_t unit = blockIdx.x / W;
-    const int wg = (int)(blockIdx.x % W);
-    const int g = (int)(unit % t.Hkv);
-    const int64_t rest = unit / t.Hkv;
-    const int qi = (int)(rest % a.Nq);
-    const int bi = (int)(rest / a.Nq);
+    // grid: (workgroup of the unit, routing head, sequence x query)
+    const int wg = (int)blockIdx.x;
+    const int g = (int)blockIdx.y;
+    const int qi = a.Nq == 1 ? 0 : (int)(blockIdx.z % (uint32_t)a.Nq);
+    const int bi = a.Nq == 1 ? (int)blockIdx.z : (int)(blockIdx.z / (uint32_t)a.Nq);
+    const int64_t unit = (int64_t)blockIdx.z * t.Hkv + g;
     const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const int b = t.b, levels = t.levels, R = t.R;
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
@@ -344,21 +358,27 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             *reinterpret_cast<uint4 *>(kw + tid * EPC) = kx;
             *reinterpret_cast<uint4 *>(vw + tid * EPC) = vx;
         }
-        __syncthreads();
         // (lengths are below 2^31 here: 32-bit index arithmetic, a mask and
         // a shift when b is a power of two)
         uint32_t idx = (uint32_t)Lold + 1u;
         const bool pow2 = (b & (b - 1)) == 0;
         const int bs = __builtin_ctz((unsigned)b);
-        for (int l = 1; l <= levels; ++l) {
-            if (pow2 ? (idx & (uint32_t)(b - 1)) != 0u : idx % (uint32_t)b != 0u) break;
-            idx = pow2 ? idx >> bs : idx / (uint32_t)b;
-            if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, (int64_t)idx - 1, lane);
+        // Only a token that completes a node needs the row in place before
+        // anything else (its pooling reads it): otherwise the stores complete
+        // in the background, long before the token level reads the row.
+        if (levels > 0 && (pow2 ? (idx & (uint32_t)(b - 1)) == 0u : idx % (uint32_t)b == 0u)) {
             __syncthreads();
+            for (int l = 1; l <= levels; ++l) {
+                if (pow2 ? (idx & (uint32_t)(b - 1)) != 0u : idx % (uint32_t)b != 0u) break;
+                idx = pow2 ? idx >> bs : idx / (uint32_t)b;
+                if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, (int64_t)idx - 1, lane);
+                __syncthreads();
+            }
         }
     }
     const int L = sm.n[0];
     const int last_leaf = L > 0 ? (L - 1) / b : -1;   // level-1 node of the query token
+    DTL(19, 0);
 
     const gptr<T> kc = to_global<T>(t.kc) + bh * t.ncap[0] * D;
     const gptr<T> vc = to_global<T>(t.vc) + bh * t.ncap[0] * D;
@@ -425,8 +445,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // it0 + sub (clamped into the batch, so surplus loads re-read a row of
     // it) and DPP row broadcasts hand row u to the whole quarter, so the
     // loads go out back to back.  Also the RoPE row of the batch's first
-    // candidate.  With go == false every load reads the (always valid) RoPE
-    // table instead, so that loads never sit behind a branch.
+    // candidate.  The number of loads is fixed (go == false reads the RoPE
+    // table instead): the compiler then knows exactly how many loads each
+    // later wait may leave in flight.
     auto load_batch = [&](const Step<T> &st, int s0, int ms, int it0, bool go, KR (&k0)[KB], KR (&k1)[KB],
                           float (&sc)[KB], float (&rb)[2 * PPL]) __attribute__((always_inline)) {
         const int nref = st.nref;
@@ -440,7 +461,6 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int cand = min(c_beg + cl, ms - 1);
         const uint32_t row = go ? (uint32_t)(st.cs.id(s0 + max(cand, 0)) * nref + (itl - cl * nref)) : 0u;
         if (F8 && !st.tok) {
-            // E4M3 codes into the low bytes of the key registers, and the row scales
             using K8 = typename Raw8<PPL>::type;
             const gptr<uint8_t> k8 = go ? st.kq : to_global<uint8_t>(t.rope);
             const gptr<float> s8 = go ? st.ks : to_global<float>(t.rope);
@@ -475,26 +495,21 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     };
     // value rows of the fold slice: quarter q owns rows q, q + DNQ, ...
     // (rows past the slice re-read its last row)
+    // (a fixed number of loads: rows past the slice re-read its last row, and
+    // go == false reads the RoPE table)
     auto issue_values = [&](const Step<T> &st, int s0, int ms, bool go, VR (&vr)[VB]) __attribute__((always_inline)) {
+        int64_t rid[VB];
+#pragma unroll
+        for (int u = 0; u < VB; ++u) rid[u] = go ? st.cs.id(s0 + max(0, min(quarter + DNQ * u, ms - 1))) : 0;
         const gptr<T> vbase = go ? st.vb : to_global<T>(t.rope);
 #pragma unroll
-        for (int u = 0; u < VB; ++u) {
-            const int i = max(0, min(quarter + DNQ * u, ms - 1));
-            const uint32_t ru = go ? (uint32_t)st.cs.id(s0 + i) : 0u;
-            vr[u].load(vbase + (size_t)ru * D + sub * EPL);
-        }
+        for (int u = 0; u < VB; ++u) vr[u].load(vbase + (size_t)rid[u] * D + sub * EPL);
     };
-    // every load of a step goes out here, unconditionally (a step with
-    // nothing to gather reads the RoPE table instead): a register that kept
-    // its old value on some path would have to be copied at the loop edge,
-    // which waits for its load
-    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&sc)[KB], float (&rb)[2 * PPL],
-                          VR (&vr)[VB], float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
-        const bool go = !st.take_all && st.ms > 0;
-        load_batch(st, st.s0, st.ms, 0, go, k0, k1, sc, rb);
-        // (the token level's values, or a summary level's when its unkept
-        // candidates are attended)
-        issue_values(st, st.fs0, st.fms, !st.take_all && st.fms > 0 && (st.tok || !a.leaf_only), vr);
+    // the loads of a step: its first key batch and the query's RoPE row
+    // (its value rows go out separately, once the previous step's are folded)
+    auto issue_step = [&](const Step<T> &st, KR (&k0)[KB], KR (&k1)[KB], float (&sc)[KB],
+                          float (&rb)[2 * PPL], float (&qcs)[2 * PPL]) __attribute__((always_inline)) {
+        load_batch(st, st.s0, st.ms, 0, !st.take_all && st.ms > 0, k0, k1, sc, rb);
         const gptr<float4> rp = (gptr<float4>)(rope + st.qpos * (D / 2) + sub * PPL);
 #pragma unroll
         for (int e = 0; e < PPL / 2; ++e) {
@@ -504,6 +519,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             qcs[4 * e + 2] = c4.z;
             qcs[4 * e + 3] = c4.w;
         }
+    };
+
+    // (the token level's values, or a summary level's when its unkept
+    // candidates are attended)
+    auto step_values = [&](const Step<T> &st, VR (&vr)[VB]) __attribute__((always_inline)) {
+        issue_values(st, st.fs0, st.fms, !st.take_all && st.fms > 0 && (st.tok || !a.leaf_only), vr);
     };
 
     // ---- scoring ----
@@ -545,7 +566,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int it0 = 0; it0 < nitems; it0 += KB) {
             const int nb = min(nitems - it0, KB);
             if (it0 > 0) load_batch(st, s0, ms, it0, true, k0, k1, sc, rb);
-            if (j == 0) {
+            if (it0 == 0 || j == 0) {
+                // (a batch that starts a candidate starts at the RoPE row
+                // just loaded; one that continues a candidate keeps its row)
 #pragma unroll
                 for (int e = 0; e < PPL; ++e) {
                     cc[e] = rb[2 * e];
@@ -634,13 +657,107 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int w = 0; w < DNW; ++w) r += sm.prt[zb][w][e];
         return r;
     };
+    // Entries held in registers, two per lane (entry lane and lane + 64): up
+    // to 128 of them, compared by readlane broadcasts with no LDS round trip.
+    struct Ents {
+        uint64_t k[2];
+        int ix[2];
+        float sc[2];
+    };
+    auto ents_from_slice = [&](int zb, int n, Ents &E) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int e = lane + 64 * t;
+            const bool v = e < n;
+            E.k[t] = v ? sm.key[zb][e] : 0ull;
+            E.ix[t] = v ? (int)sm.eix[zb][e] : 0;
+            E.sc[t] = v ? sm.esc[zb][e] : -INFINITY;
+        }
+    };
+    // how many of the keys kk[j0 .. j1) (uniform bounds; LDS, read by every
+    // lane at the same address) beat each entry; eight reads go out before
+    // the first comparison
+    auto count_range = [&](const uint64_t *kk, const Ents &E, int j0, int j1, int (&c)[2])
+        __attribute__((always_inline)) {
+        c[0] = c[1] = 0;
+        j0 = __builtin_amdgcn_readfirstlane(j0);
+        j1 = __builtin_amdgcn_readfirstlane(j1);
+        for (int jb = j0; jb < j1; jb += 8) {
+            uint64_t kj[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kj[u] = kk[min(jb + u, j1 - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool in = jb + u < j1;
+                c[0] += (int)(in && kj[u] > E.k[0]);
+                c[1] += (int)(in && kj[u] > E.k[1]);
+            }
+        }
+    };
+    // Kept set from the ranks of the n entries held in registers: the first
+    // nav by rank (top-p: the shortest prefix reaching mass p), put in
+    // candidate order by walking the kept lanes, into this wave's lists of
+    // parity nxt.  Returns the kept count.
+    auto finalize_regs = [&](const Ents &E, const int (&rank)[2], int n, int m, const Cands &cs, int nxt,
+                             float gmax, float den, int fs0, int fms) __attribute__((always_inline)) -> int {
+        const int nav = min(keff, m);
+        uint32_t *fw = reinterpret_cast<uint32_t *>(sm.wflag[nxt][wave]);
+        if (lane < kSlice / 4) fw[lane] = 0u;
+        int nkeep = nav;
+        if (topp) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (lane + 64 * t < n && rank[t] < nav) sm.wrsc[wave][rank[t]] = E.sc[t];
+            wave_sync();
+            int ns = nav;
+            if (lane == 0) {
+                float cum = 0.f;
+                for (int r = 0; r < nav; ++r) {
+                    cum += __expf(sm.wrsc[wave][r] - gmax) / den;
+                    if (cum >= a.p) {
+                        ns = r + 1;
+                        break;
+                    }
+                }
+            }
+            nkeep = max(1, min(__builtin_amdgcn_readfirstlane(ns), a.cap));
+        }
+        bool kept[2];
+        int pos[2] = {0, 0};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) kept[t] = lane + 64 * t < n && rank[t] < nkeep;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            uint64_t mm = __ballot(kept[t2]);
+            while (mm) {
+                const int l = __builtin_ctzll(mm);
+                mm &= mm - 1;
+                const int ixj = __builtin_amdgcn_readlane(E.ix[t2], l);
+                pos[0] += (int)(ixj < E.ix[0]);
+                pos[1] += (int)(ixj < E.ix[1]);
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            if (kept[t]) {
+                const int ix = E.ix[t];
+                sm.wcix[nxt][wave][pos[t]] = ix;
+                sm.wsel[nxt][wave][pos[t]] = (int)cs.id(ix);
+                if (ix >= fs0 && ix < fs0 + fms) sm.wflag[nxt][wave][ix - fs0] = 1;
+            }
+        wave_sync();
+        return nkeep;
+    };
     // Kept set from the ranks of n entries (from `base`): the first nav by
     // rank (top-p: the shortest prefix whose mass over every candidate,
     // max gmax and denominator den, reaches p), in candidate order, into
     // this wave's lists of parity nxt.  Returns the kept count.
-    auto finalize = [&](int zb, int base, int n, int m, const Cands &cs, int nxt, float gmax, float den)
-        __attribute__((always_inline)) -> int {
+    auto finalize = [&](int zb, int base, int n, int m, const Cands &cs, int nxt, float gmax, float den, int fs0,
+                        int fms) __attribute__((always_inline)) -> int {
         const int nav = min(keff, m);
+        uint32_t *fw = reinterpret_cast<uint32_t *>(sm.wflag[nxt][wave]);
+        if (lane < kSlice / 4) fw[lane] = 0u;
         for (int e = base + lane; e < base + n; e += 64) {
             const int r = rank_of(zb, e);
             if (r < nav) {
@@ -670,57 +787,64 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             for (int r = 0; r < nkeep; ++r) pos += (int)(sm.wrix[wave][r] < ix);
             sm.wcix[nxt][wave][pos] = ix;
             sm.wsel[nxt][wave][pos] = (int)cs.id(ix);
+            if (ix >= fs0 && ix < fs0 + fms) sm.wflag[nxt][wave][ix - fs0] = 1;
         }
         wave_sync();
         return nkeep;
     };
-    auto is_kept = [&](int nxt, int nkeep, int c) __attribute__((always_inline)) -> bool {
-        bool k = false;
-        for (int r = 0; r < nkeep; ++r) k |= sm.wcix[nxt][wave][r] == c;
-        return k;
-    };
 
-    // new running max from the per-wave maxima (same in every thread), and
-    // the factor that rescales what was accumulated under the old one
-    auto new_max = [&](int zb, float (&Mn)[G], float (&alpha)[G]) __attribute__((always_inline)) {
+    // the running max takes in this step's per-wave maxima (the same in
+    // every thread) and what was accumulated under the old one is rescaled;
+    // folds at any later point then take their terms against the current max
+    auto new_max = [&](int zb) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mm = M[h];
 #pragma unroll
             for (int w = 0; w < DNW; ++w) mm = fmaxf(mm, sm.redz[zb][w][h]);
-            Mn[h] = mm;
-            alpha[h] = (mm == -INFINITY) ? 1.f : __expf(M[h] - mm);
+            const float alpha = (mm == -INFINITY) ? 1.f : __expf(M[h] - mm);
+            lt[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+            M[h] = mm;
         }
     };
     // softmax terms of this quarter's fold rows (candidates fs0 + quarter +
     // DNQ u; logits at z index c - zo) times their value rows; kept ones
-    // (when nkeep >= 0) drop out
-    auto fold = [&](int fs0, int fms, int zo, int zb, int nxt, int nkeep, const VR (&vr)[VB],
-                    const float (&Mn)[G], const float (&alpha)[G]) __attribute__((always_inline)) {
+    // (flags of parity nxt, when `kept` is set) drop out.  Each lane takes
+    // the exponential of its own head (head sub / (16 / G)) and the quarter
+    // hands the G of them round by DPP row broadcasts.
+    auto fold = [&](int fs0, int fms, int zo, int zb, int nxt, bool kept, const VR (&vr)[VB], gptr<T> vsrc,
+                    const Cands &vcs) __attribute__((always_inline)) {
+        constexpr int LPH = 16 / G;
+        const int hsel = sub / LPH;
+        // this lane's head's running max, by masks (an indexed pick would put
+        // M in private memory)
+        uint32_t mb = 0u;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            lt[h] *= alpha[h];
+        for (int h = 0; h < G; ++h) mb |= (0u - (uint32_t)(hsel == h)) & __float_as_uint(M[h]);
+        const float Mh = __uint_as_float(mb);
+        auto add_row = [&](int i, const VR &row) __attribute__((always_inline)) {
+            const int c = fs0 + i;
+            const bool k = kept && sm.wflag[nxt][wave][i] != 0;
+            const float pl = k ? 0.f : __expf(sm.z[zb][(c - zo) * G + hsel] - Mh);
+            float v[EPL];
+            row.get(v);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
-            M[h] = Mn[h];
-        }
+            for (int h = 0; h < G; ++h) {
+                const float p = __int_as_float(row_bcast(__float_as_int(pl), h * LPH));
+                lt[h] += p;
 #pragma unroll
-        for (int u = 0; u < VB; ++u) {
-            const int i = quarter + DNQ * u;
-            if (i < fms) {
-                const int c = fs0 + i;
-                const bool kept = nkeep > 0 && is_kept(nxt, nkeep, c);
-                const float *zp = &sm.z[zb][(c - zo) * G];
-                float v[EPL];
-                vr[u].get(v);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float p = kept ? 0.f : __expf(zp[h] - M[h]);
-                    lt[h] += p;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
-                }
+                for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
             }
+        };
+#pragma unroll
+        for (int u = 0; u < VB; ++u)
+            if (quarter + DNQ * u < fms) add_row(quarter + DNQ * u, vr[u]);
+        for (int i = quarter + DNQ * VB; i < fms; i += DNQ) {
+            VR row;
+            row.load(vsrc + (size_t)vcs.id(fs0 + i) * D + sub * EPL);
+            add_row(i, row);
         }
     };
     auto write_sel = [&](int lvl, int nxt, int nkeep) __attribute__((always_inline)) {
@@ -753,13 +877,26 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         --lvl;
         st = make_step(lvl, cur, nsel);
     }
-    issue_step(st, k0, k1, sc, rb, vr, qcs);
+    DTL(17, lvl);
+    issue_step(st, k0, k1, sc, rb, qcs);
+    DTL(18, lvl);
+    step_values(st, vr);
     DTL(3, lvl);
 
+    // A summary level's unkept candidates are folded one level later, while
+    // the next level's exchange is in flight (or before the token level's
+    // fold): the pending level's slice, logits, kept flags and value rows.
+    bool pend = false;
+    int p_fs0 = 0, p_fms = 0, p_zo = 0, p_zb = 0, p_par = 0;
+    Step<T> p_st = st;
+    VR vrp[VB];
+    auto fold_pending = [&]() __attribute__((always_inline)) {
+        if (pend) fold(p_fs0, p_fms, p_zo, p_zb, p_par, true, vrp, p_st.vb, p_st.cs);
+        pend = false;
+    };
     for (; lvl >= 1; --lvl) {
         const int nxt = cur ^ 1;
         const int s0 = st.s0, ms = st.ms;
-        float Mn[G], alpha[G];
         int nkeep;
         if (st.take_all) {
             // (a lower level can keep everything when an upper one kept few)
@@ -773,20 +910,127 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             score(st, s0, ms, zb, k0, k1, sc, rb, qcs);
             __syncthreads();                                           // B1: slice entries, logits
             DTL(4, lvl);
-            new_max(zb, Mn, alpha);
+            if (!a.leaf_only) new_max(zb);
+            const int ne = W * keff;                                   // exchanged entries
             if (st.local) {
-                // the whole level: ranks among all of it, selected locally
-                partial_ranks(zb, 0, ms);
+                fold_pending();
+                // the whole level: ranks among all of it (every wave counts
+                // against its share of the keys), selected locally
+                Ents E;
+                ents_from_slice(zb, ms, E);
+                int c[2];
+                count_range(sm.key[zb], E, ms * wave / DNW, ms * (wave + 1) / DNW, c);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (lane + 64 * t < ms) sm.prt[zb][wave][lane + 64 * t] = (uint8_t)c[t];
                 __syncthreads();                                       // B2
                 DTL(5, lvl);
+                int rk[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) rk[t] = lane + 64 * t < ms ? rank_of(zb, lane + 64 * t) : 1 << 20;
                 float gmax = -INFINITY, den = 0.f;
                 if (topp) {
-                    for (int i = lane; i < ms; i += 64) gmax = fmaxf(gmax, sm.esc[zb][i]);
-                    gmax = wave_max(gmax);
-                    for (int i = lane; i < ms; i += 64) den += __expf(sm.esc[zb][i] - gmax);
-                    den = wave_sum(den);
+                    gmax = wave_max(fmaxf(E.sc[0], E.sc[1]));
+                    den = wave_sum((E.sc[0] > -INFINITY ? __expf(E.sc[0] - gmax) : 0.f) +
+                                   (E.sc[1] > -INFINITY ? __expf(E.sc[1] - gmax) : 0.f));
                 }
-                nkeep = finalize(zb, 0, ms, st.m, st.cs, nxt, gmax, den);
+                nkeep = finalize_regs(E, rk, ms, st.m, st.cs, nxt, gmax, den, st.fs0, st.fms);
+            } else if (ne <= 128) {
+                uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;
+                if (wave == 0) {
+                    // this slice's ranks (wave 0 alone) and its best keff as
+                    // words at slot = rank
+                    Ents S;
+                    ents_from_slice(zb, ms, S);
+                    int c[2];
+                    count_range(sm.key[zb], S, 0, ms, c);
+                    uint64_t *mine = lw_words + (int64_t)wg * kSlots;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        if (lane + 64 * t < ms && c[t] < keff)
+                            __hip_atomic_store(&mine[c[t]], pack_word(tag, (uint32_t)S.ix[t], S.sc[t]),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (lane >= ms && lane < keff)
+                        __hip_atomic_store(&mine[lane], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    if (topp) {
+                        const float wmax = wave_max(fmaxf(S.sc[0], S.sc[1]));
+                        const float wsum = wave_sum((S.sc[0] > -INFINITY ? __expf(S.sc[0] - wmax) : 0.f) +
+                                                    (S.sc[1] > -INFINITY ? __expf(S.sc[1] - wmax) : 0.f));
+                        if (lane == 0) {
+                            __hip_atomic_store(&mine[keff], pack_word(tag, 0, wmax), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_store(&mine[keff + 1], pack_word(tag, 0, wsum), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                    DTL(6, lvl);
+                }
+                // the previous level's fold, while the other slices' words
+                // are on their way
+                fold_pending();
+                // every wave reads all W * keff words itself (lane e: entry
+                // e and e + 64; bounded polling on the tag)
+                auto poll = [&](const uint64_t *src, bool &okw) __attribute__((always_inline)) -> uint64_t {
+                    uint64_t word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    long spins = 0;
+                    while (word_tag(word) != tag && ++spins < kSpin) {
+                        __builtin_amdgcn_s_sleep(1);
+                        word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    okw = word_tag(word) == tag;
+                    if (!okw) sm.bad = 1;
+                    return word;
+                };
+                Ents X;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int e = lane + 64 * t;
+                    X.k[t] = 0ull;
+                    X.ix[t] = 0;
+                    X.sc[t] = -INFINITY;
+                    if (e < ne) {
+                        const int w = e / keff;
+                        bool okw;
+                        const uint64_t word = poll(lw_words + (int64_t)w * kSlots + (e - w * keff), okw);
+                        const uint32_t ix = okw ? word_idx(word) : 0xfffu;
+                        if (ix != 0xfffu) {
+                            X.k[t] = sel_key(word_val(word), (int)ix);
+                            X.ix[t] = (int)ix;
+                            X.sc[t] = word_val(word);
+                        }
+                    }
+                }
+                float gmax = -INFINITY, den = 0.f;
+                if (topp) {
+                    float xm = -INFINITY, xs = 0.f;
+                    if (lane < W) {
+                        bool ok1, ok2;
+                        const uint64_t w1 = poll(lw_words + (int64_t)lane * kSlots + keff, ok1);
+                        const uint64_t w2 = poll(lw_words + (int64_t)lane * kSlots + keff + 1, ok2);
+                        xm = ok1 ? word_val(w1) : -INFINITY;
+                        xs = ok2 ? word_val(w2) : 0.f;
+                    }
+                    gmax = wave_max(xm);
+                    den = wave_sum(xm > -INFINITY ? xs * __expf(xm - gmax) : 0.f);
+                }
+                DTL(7, lvl);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (lane + 64 * t < ne) sm.wkx[wave][lane + 64 * t] = X.k[t];
+                wave_sync();
+                int c[2];
+                count_range(sm.wkx[wave], X, ne * wave / DNW, ne * (wave + 1) / DNW, c);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (lane + 64 * t < ne) sm.prt[zb][wave][kSlice + lane + 64 * t] = (uint8_t)c[t];
+                __syncthreads();                                       // B2
+                DTL(8, lvl);
+                int rk[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    rk[t] = lane + 64 * t < ne ? rank_of(zb, kSlice + lane + 64 * t) : 1 << 20;
+                nkeep = finalize_regs(X, rk, ne, st.m, st.cs, nxt, gmax, den, st.fs0, st.fms);
             } else {
                 uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;
                 partial_ranks(zb, 0, ms);
@@ -819,6 +1063,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     }
                 }
                 DTL(6, lvl);
+                fold_pending();
                 // every slice's words (bounded polling on the tag) -> the
                 // exchange entries at [kSlice, kSlice + W * keff)
                 const int ne = W * keff;
@@ -860,30 +1105,33 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                         if (sm.xm[w] > -INFINITY) den += sm.xs[w] * __expf(sm.xm[w] - gmax);
                     den = wave_sum(den);
                 }
-                nkeep = finalize(zb, kSlice, ne, st.m, st.cs, nxt, gmax, den);
+                nkeep = finalize(zb, kSlice, ne, st.m, st.cs, nxt, gmax, den, st.fs0, st.fms);
             }
         }
         DTL(9, lvl);
         write_sel(lvl, nxt, nkeep);
 
-        // the next step's gathers go out now (one issue point for every
-        // path, so that the loaded registers carry into the next iteration
-        // as they are); this level's unkept candidates are folded while they
-        // are in flight
-        const Step<T> stc = st;
-        VR vrc[VB];
+        // this level's fold becomes pending (its own candidates only; a
+        // local level was scored whole by every workgroup, so its logits sit
+        // at the candidate index), and the next step's keys and value rows
+        // go out
+        if (!st.take_all && !a.leaf_only) {
+            pend = true;
+            p_fs0 = st.fs0;
+            p_fms = st.fms;
+            p_zo = st.local ? 0 : st.s0;
+            p_zb = zb;
+            p_par = nxt;
+            p_st = st;
 #pragma unroll
-        for (int u = 0; u < VB; ++u) vrc[u] = vr[u];
-        st = make_step(lvl - 1, nxt, nkeep);
-        issue_step(st, k0, k1, sc, rb, vr, qcs);
-        DTL(10, lvl);
-        if (!stc.take_all && !a.leaf_only) {
-            // this workgroup's own candidates only (a local level was scored
-            // whole by every workgroup: its logits sit at the candidate index)
-            fold(stc.fs0, stc.fms, stc.local ? 0 : stc.s0, zb, nxt, nkeep, vrc, Mn, alpha);
+            for (int u = 0; u < VB; ++u) vrp[u] = vr[u];
         }
-        DTL(11, lvl);
-        if (!stc.take_all) zb ^= 1;
+        const bool scored = !st.take_all;
+        st = make_step(lvl - 1, nxt, nkeep);
+        issue_step(st, k0, k1, sc, rb, qcs);
+        step_values(st, vr);
+        DTL(10, lvl);
+        if (scored) zb ^= 1;
         cur = nxt;
     }
 
@@ -898,12 +1146,13 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         score(st, c0, ms, zb, k0, k1, sc, rb, qcs);
         __syncthreads();
         DTL(12, 0);
-        float Mn[G], alpha[G];
-        new_max(zb, Mn, alpha);
-        fold(c0, ms, c0, zb, cur, 0, vr, Mn, alpha);
+        new_max(zb);
+        fold_pending();
+        fold(c0, ms, c0, zb, cur, false, vr, st.vb, st.cs);
         DTL(13, 0);
         zb ^= 1;
     }
+    fold_pending();     // (a token level with no candidates for this workgroup)
 
     // Partial state of this workgroup: the quarters' sums within each wave by
     // lane swaps, then across waves in LDS; as tagged words in the workspace.
@@ -998,15 +1247,23 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
     for (int i = tid; i < G * nc; i += DNT) {
         const int h = i / nc, c = i % nc;
+        // (all W slices' values read first, then combined in slice order)
+        float Mw[kMaxW], Lw[kMaxW], Aw[kMaxW];
+#pragma unroll
+        for (int w = 0; w < kMaxW; ++w) {
+            Mw[w] = w < W ? mw[(w * G + h) * 2] : -INFINITY;
+            Lw[w] = w < W ? mw[(w * G + h) * 2 + 1] : 0.f;
+            Aw[w] = w < W ? aw[(w * G + h) * nc + c] : 0.f;
+        }
         float Mx = -INFINITY;
-        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, mw[(w * G + h) * 2]);
+#pragma unroll
+        for (int w = 0; w < kMaxW; ++w) Mx = fmaxf(Mx, Mw[w]);
         float num = 0.f, den = 0.f;
-        for (int w = 0; w < W; ++w) {
-            const float Mw = mw[(w * G + h) * 2];
-            if (Mw == -INFINITY) continue;
-            const float f = __expf(Mw - Mx);
-            num += aw[(w * G + h) * nc + c] * f;
-            den += mw[(w * G + h) * 2 + 1] * f;
+#pragma unroll
+        for (int w = 0; w < kMaxW; ++w) {
+            const float f = Mw[w] == -INFINITY ? 0.f : __expf(Mw[w] - Mx);
+            num += Aw[w] * f;
+            den += Lw[w] * f;
         }
         a.out[(orow + h) * D + d0 + c] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? num / den : 0.f;
     }
@@ -1023,9 +1280,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     }
     DTL(16, 0);
 #ifdef HTI_DECODE_TIMELINE
-    if (tid == 0 && blockIdx.x < kTlMaxBlocks) {
-        uint64_t *tr = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws.status) + 256) +
-                       (int64_t)blockIdx.x * kTlEvents;
+    const int64_t lin = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    if (tid == 0 && lin < kTlMaxBlocks) {
+        uint64_t *tr = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws.status) + 256) + lin * kTlEvents;
         for (int i = 0; i < kTlEvents; ++i) tr[i] = i < tln ? sm.tl[i] : 0ull;
     }
 #endif
@@ -1118,8 +1375,10 @@ hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t units, hi
     // by other work; every wait is bounded and a timeout sets the status
     // word (a cooperative launch would guarantee residency but costs more
     // than the whole kernel to dispatch).
-    return hipLaunchKernel((const void *)k_decode_split<T, D, G, F8>, dim3((unsigned)(units * ws.W)), dim3(DNT),
-                           args, dec_dyn_bytes<G, D>(), s);
+    const unsigned heads = (unsigned)a.t.Hkv;
+    return hipLaunchKernel((const void *)k_decode_split<T, D, G, F8>,
+                           dim3((unsigned)ws.W, heads, (unsigned)(units / heads)), dim3(DNT), args,
+                           dec_dyn_bytes<G, D>(), s);
 }
 
 // Dispatch over the instances: 8-bit router keys with bf16 caches only.

@@ -258,6 +258,93 @@ def decode_variants(ts, w, qs, Wm, S, out, cs):
     return ph_ms, lf_ms, plain_ms, r8_ms
 
 
+def graph_ms(fn, S, warm=4):
+    """Average time of fn() over S calls captured into one HIP graph and
+    replayed once (events on the replay stream)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            for _ in range(S):
+                fn()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    del graph
+    return g0.elapsed_time(g1) / S
+
+
+def build_bytes(w, L):
+    """Algorithmic bytes of tree_build over L tokens of every (sequence, KV
+    head): each level reads its children's keys (one per token at level 1,
+    R per node above) and values, and writes its nodes' R keys and value."""
+    n = w.level_counts(L)
+    row = w.d * w.elem_bytes
+    tot = 0
+    for lvl in range(1, w.levels + 1):
+        tot += n[lvl - 1] * ((1 if lvl == 1 else w.R) + 1) * row
+        tot += n[lvl] * (w.R + 1) * row
+    return tot * w.B * w.Hkv
+
+
+def bench_side_workloads(args):
+    """The 131,072-token decode (one query, 8 KV groups, 8 planted needles)
+    and the 2,097,152-token top-p workload with four reference keys per node
+    (tree_build of the whole context, then one top-p decode query), each
+    against the HBM roofline of its algorithmic bytes."""
+    res = {}
+    reps = max(16, args.steps // 4)
+    w = W.DEC128K
+    K, V = gen_kv_device(w, w.L)
+    q0 = W.gen_queries(w, 0, device=DEV)
+    W.plant_needles(w, K, q0)
+    ts, sel = treeset(w, w.L, K, V)
+    ts.tree_build([w.L] * w.B)
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    ms = graph_ms(lambda: ts.sparse_decode(sel, q0, out), reps)
+    by = decode_unit_bytes(w, w.L) * w.B * w.Hkv
+    res["decode_128k"] = dict(ms=ms, queries_per_s=w.B / (ms / 1e3), bytes=by, gbs=by / (ms / 1e3) / 1e9,
+                              frac_hbm=by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+    log(f"[side] decode_128k {res['decode_128k']}")
+    del K, V, ts
+    torch.cuda.empty_cache()
+    w = W.ZHA2M
+    K, V = gen_kv_device(w, w.L)
+    ts, sel = treeset(w, w.L, K, V)
+    ts.tree_build([w.L] * w.B)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bms = []
+    for r in range(2 + args.prefill_reps):
+        e0.record()
+        ts.tree_build([w.L] * w.B)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            bms.append(e0.elapsed_time(e1))
+    bms = sum(bms) / len(bms)
+    bb = build_bytes(w, w.L)
+    q = W.gen_queries(w, 0, device=DEV)
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    ms = graph_ms(lambda: ts.sparse_decode(sel, q, out), reps)
+    by = decode_unit_bytes(w, w.L) * w.B * w.Hkv
+    res["zha_topp_2m_r4"] = dict(build_ms=bms, build_bytes=bb, build_gbs=bb / (bms / 1e3) / 1e9,
+                                 build_frac_hbm=bb / (bms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                 decode_ms=ms, decode_queries_per_s=w.B / (ms / 1e3),
+                                 decode_bytes_upper=by, decode_gbs_upper=by / (ms / 1e3) / 1e9,
+                                 decode_frac_hbm_upper=by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+    log(f"[side] zha_topp_2m_r4 {res['zha_topp_2m_r4']}")
+    del K, V, ts
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(args):
     w = W.PREFILL
     log(f"[prefill] generating prefix {w.L} and block {w.T}")
@@ -384,7 +471,8 @@ def copy_calibration():
 PHASES = {1: "entry", 2: "length and query read", 3: "first gathers issued", 4: "scored (B1)",
           5: "slice ranked (B2)", 6: "slice published", 7: "exchange read (B3)", 8: "exchange ranked (B4)",
           9: "kept set known", 10: "next gathers issued", 11: "level folded", 12: "tokens scored",
-          13: "tokens folded", 14: "partial published", 15: "partials gathered", 16: "output written"}
+          13: "tokens folded", 14: "partial published", 15: "partials gathered", 16: "output written",
+          17: "take-all levels resolved", 18: "first keys issued", 19: "append checked"}
 
 
 def decode_timeline(args):
@@ -683,6 +771,10 @@ def main():
     hti.lib()
     dec = bench_decode(args) if args.only in ("decode", "all") else None
     pre = bench_prefill(args) if args.only in ("prefill", "all") else None
+    side = bench_side_workloads(args) if args.only == "all" and not args.no_variants else None
+    floors = None
+    if not args.no_floors and args.only == "all":
+        floors = measure_floors()
     cpu = None if args.no_cpu_baseline else cpu_baseline(args)
     w = W.DEC1M
     line = {
@@ -732,7 +824,13 @@ def main():
                               "kernel": "k_inblock (causal in-block attention, bf16 MFMA)",
                               "dense_ms": pre["dense_ms"], "gflop": pre["inblock_gflop"]} if pre else None),
         "cpu_baseline": cpu,
+        "side_workloads": side,
+        "measured_floors": floors,
     }
+    if floors and dec:
+        line["roofline"]["frac_of_measured_read_bw"] = dec["gbs"] / floors["read_gbs"]
+    if floors and pre:
+        line["prefill_roofline"]["frac_of_measured_mfma"] = pre["dense_tflops"] / floors["mfma_bf16_tflops"]
     print(json.dumps(line), flush=True)
 
 

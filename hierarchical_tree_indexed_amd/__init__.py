@@ -27,7 +27,8 @@ STATUS = {0: "HTI_OK", -1: "HTI_ERR_INVALID_ARG", -2: "HTI_ERR_UNSUPPORTED",
           -3: "HTI_ERR_CAPACITY", -4: "HTI_ERR_WORKSPACE", -5: "HTI_ERR_LAUNCH", -6: "HTI_ERR_TIMEOUT"}
 
 EXPORTS = ["hti_plan", "hti_rope_init", "hti_tree_build", "hti_tree_append", "hti_tree_extend",
-           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_decode_status", "hti_decode_step",
+           "hti_decode_workspace_bytes", "hti_sparse_decode", "hti_sparse_decode_static",
+           "hti_decode_status", "hti_decode_step",
            "hti_prefill_workspace_bytes", "hti_sparse_prefill", "hti_last_error"]
 
 
@@ -83,6 +84,7 @@ def lib() -> C.CDLL:
             "hti_tree_extend": (C.c_int, [vp, vp, vp, i32, vp]),
             "hti_decode_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
             "hti_sparse_decode": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
+            "hti_sparse_decode_static": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp]),
             "hti_decode_status": (C.c_int, [vp, C.c_size_t, vp]),
             "hti_decode_step": (C.c_int, [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, C.c_size_t, vp]),
             "hti_prefill_workspace_bytes": (C.c_size_t, [vp, vp, i32]),
@@ -223,6 +225,18 @@ class TreeSet:
         _check(lib().hti_sparse_decode(C.byref(self.c), C.byref(sel), _ptr(q), _ptr(q_pos), Nq, _ptr(out),
                                        _ptr(lse), _ptr(sel_out), stride, _ptr(ws), nbytes,
                                        _stream(stream)))
+
+    def sparse_decode_static(self, sel: Select, q: torch.Tensor, out: torch.Tensor, lse=None,
+                             sel_out=None, stream=None, q_pos: torch.Tensor | None = None):
+        """sparse_decode whose split workspace is the library's static device
+        array (no allocation); calls on one GPU must not overlap."""
+        B, Nq, Hq, d = q.shape
+        assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        if q_pos is not None:
+            assert q_pos.dtype == torch.int64 and q_pos.is_contiguous() and tuple(q_pos.shape) == (B, Nq)
+        stride = 0 if sel_out is None else sel_out.shape[-1]
+        _check(lib().hti_sparse_decode_static(C.byref(self.c), C.byref(sel), _ptr(q), _ptr(q_pos), Nq,
+                                              _ptr(out), _ptr(lse), _ptr(sel_out), stride, _stream(stream)))
 
     def decode_status(self, sel: Select, Nq: int, stream=None):
         """Raise HTIError(HTI_ERR_TIMEOUT) if a split decode with this shape's

@@ -400,10 +400,13 @@ size_t hti_decode_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel
 
 namespace {
 
-// sparse_decode, and the decode step (k_new != NULL: append, then decode)
+// sparse_decode, and the decode step (k_new != NULL: append, then decode);
+// use_static: the split workspace is the library's static device array
+// (zeroed by a fill kernel before the launch), `ws` is ignored
 hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select *sel, const void *k_new,
                        const void *v_new, const void *q, const int64_t *q_pos, int32_t Nq, float *out, float *lse,
-                       int32_t *sel_out, int32_t sel_stride, void *ws, size_t ws_bytes, void *stream)
+                       int32_t *sel_out, int32_t sel_stride, void *ws, size_t ws_bytes, void *stream,
+                       bool use_static = false)
 {
     hti_status st = check_traversal(tree, sel, 0, sel_out, sel_stride);
     if (st) return st;
@@ -433,11 +436,22 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
     const hipStream_t hs = (hipStream_t)stream;
     int W = 0;
-    if (ws) {
+    if (ws || use_static) {
         // split each unit over W workgroups when all of them fit on the device
         // at once; otherwise one workgroup per unit
         const Bounds bd = bounds(&tree->cfg, sel, 0);
         hipError_t e = decode_split_plan(a, units, bd.max_summary, &W);
+        if (e != hipSuccess) return launched(e, what);
+    }
+    if (use_static && W > 0) {
+        // the layout of this call's W, in the static array: checked against
+        // its size, zeroed, and used as the workspace
+        const size_t need = decode_ws_bytes(tree->cfg.B, units, W, tree->cfg.levels, G, tree->cfg.d);
+        if (need > kStaticScratchBytes)
+            return fail(HTI_ERR_WORKSPACE, "%s needs %zu bytes of split workspace, above the static array's %zu",
+                        what, need, kStaticScratchBytes);
+        hipError_t e = decode_static_scratch(&ws);
+        if (e == hipSuccess) e = launch_zero(ws, need, hs);
         if (e != hipSuccess) return launched(e, what);
     }
     if (k_new) {
@@ -467,6 +481,14 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
 {
     return decode_impl("sparse_decode", tree, sel, nullptr, nullptr, q, q_pos, Nq, out, lse, sel_out, sel_stride,
                        ws, ws_bytes, stream);
+}
+
+hti_status hti_sparse_decode_static(const hti_tree *tree, const hti_select *sel, const void *q,
+                                    const int64_t *q_pos, int32_t Nq, float *out, float *lse, int32_t *sel_out,
+                                    int32_t sel_stride, void *stream)
+{
+    return decode_impl("sparse_decode_static", tree, sel, nullptr, nullptr, q, q_pos, Nq, out, lse, sel_out,
+                       sel_stride, nullptr, 0, stream, true);
 }
 
 hti_status hti_decode_status(const void *ws, size_t ws_bytes, void *stream)

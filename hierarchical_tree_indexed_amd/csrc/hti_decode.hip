@@ -1475,6 +1475,56 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// The split decode's workspace for callers that cannot allocate: a static
+// device array (every GPU the library runs on holds its own copy until the
+// process ends).  In host code `scratch` only names the symbol; its device
+// address on the current device comes from hipGetSymbolAddress, taken once
+// per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scr_mu;
+std::vector<std::pair<int, void *>> g_scr_ptr;     // device -> address of its scratch
+
+__global__ void k_fill_zero(uint4 *p, int64_t n16)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+} // namespace
+
+hipError_t decode_static_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    for (auto &p : g_scr_ptr)
+        if (p.first == dev) {
+            *ptr = p.second;
+            return hipSuccess;
+        }
+    void *q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scr_ptr.push_back({dev, q});
+    *ptr = q;
+    return hipSuccess;
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s)
+{
+    const int64_t n16 = (int64_t)((bytes + 15) / 16);
+    if (n16 == 0) return hipSuccess;
+    const int blocks = (int)std::min<int64_t>(1024, (n16 + 255) / 256);
+    hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, (uint4 *)p, n16);
+    return hipGetLastError();
+}
+
 size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D)
 {
     size_t off = 0;

@@ -75,6 +75,12 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
 size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D);
 DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, int G, int D);
 hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s);
+// Static workspace of the split decode for callers that cannot allocate
+// (hti_sparse_decode_static): its size, its device address on the current
+// device, and a fill kernel that zeroes part of it.
+constexpr size_t kStaticScratchBytes = HTI_DECODE_STATIC_SCRATCH_BYTES;
+hipError_t decode_static_scratch(void **ptr);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per (device, kernel) (thread-safe).

@@ -253,6 +253,28 @@ hti_status hti_sparse_decode(const hti_tree *tree, const hti_select *sel, const 
                              void *stream);
 
 /*
+ * hti_sparse_decode_static: hti_sparse_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid hipMalloc, harnesses that own every allocation).  Same arguments,
+ * results and errors as hti_sparse_decode with a workspace, except that the
+ * split workspace is a static device array inside the library
+ * (HTI_DECODE_STATIC_SCRATCH_BYTES, 8 MiB, held by every GPU the library runs
+ * on until the process ends).  The call allocates nothing: before the
+ * decode it zeroes the part of the array this call's shape uses with a fill
+ * kernel on `stream`, so no state carries over between calls (a wait that
+ * runs out makes that call's outputs NaN and leaves nothing sticky).  All
+ * calls on one GPU share its array: calls that overlap in time on that GPU
+ * (other streams, other threads) race and must not be made.
+ * Returns HTI_ERR_WORKSPACE if the shape needs more split workspace than
+ * the array holds (hti_decode_workspace_bytes above the limit gives a bound;
+ * the exact need depends on the split the device allows).
+ */
+#define HTI_DECODE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+hti_status hti_sparse_decode_static(const hti_tree *tree, const hti_select *sel, const void *q,
+                                    const int64_t *q_pos, int32_t Nq, float *out, float *lse,
+                                    int32_t *sel_out, int32_t sel_stride, void *stream);
+
+/*
  * hti_decode_status: whether a split decode with this workspace has run out
  * of a wait (see hti_sparse_decode).  Synchronises `stream`, reads the
  * workspace's status word (4 bytes at its start) and returns HTI_OK, or

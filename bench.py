@@ -351,7 +351,12 @@ def bench_prefill(args):
     K, V = gen_kv_device(w, w.L)
     qb, kb, vb = W.gen_block(w, device=DEV)
     ts, sel = treeset(w, w.L, K, V, T=w.T)
-    ws = torch.empty(ts.prefill_workspace_bytes(sel, w.T), dtype=torch.uint8, device=DEV)
+    # the prefix token level node-inverted (queries grouped by kept level-1
+    # node, each node's token rows read once per block) instead of walked per
+    # query: a variant, with the larger workspace
+    sel_tw = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, token_nodes=True)
+    ws = torch.empty(max(ts.prefill_workspace_bytes(sel, w.T), ts.prefill_workspace_bytes(sel_tw, w.T)),
+                     dtype=torch.uint8, device=DEV)
     out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=torch.float32, device=DEV)
     lse = torch.empty((w.B, w.T, w.Hq), dtype=torch.float32, device=DEV)
 
@@ -379,6 +384,11 @@ def bench_prefill(args):
         ts.sparse_prefill(sel_lf, qb, kb, vb, out, ws, lse)
 
     ms_lf = float("nan") if args.no_variants else timed(run_lf, args.prefill_reps)
+    def run_tw():
+        ts.tree_build([w.L] * w.B)
+        ts.sparse_prefill(sel_tw, qb, kb, vb, out, ws, lse)
+
+    ms_tw = float("nan") if args.no_variants else timed(run_tw, args.prefill_reps)
     # 8-bit router keys: a tree set over the same prefix whose summary keys
     # carry the E4M3 copy, built and prefilled the same way
     ms_r8 = float("nan")
@@ -433,7 +443,7 @@ def bench_prefill(args):
     res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9,
                dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12,
                extend_ms=ms_ext, extend_gbs=ext_bytes / (ms_ext / 1e3) / 1e9, leaf_only_ms=ms_lf,
-               r8_ms=ms_r8)
+               r8_ms=ms_r8, token_nodes_ms=ms_tw)
     log(f"[prefill] {res}")
     del K, V, ts, ws, tsx, Kx, Vx
     torch.cuda.empty_cache()
@@ -802,6 +812,7 @@ def main():
         "decode_leaf_only_ms": finite(dec["leaf_only_ms"]) if dec else None,
         "decode_leaf_only_qps": finite(dec["leaf_only_qps"]) if dec else None,
         "prefill_leaf_only_ms_per_block": finite(pre["leaf_only_ms"]) if pre else None,
+        "prefill_token_nodes_ms_per_block": finite(pre["token_nodes_ms"]) if pre else None,
         "decode_plain_ms": finite(dec["plain_ms"]) if dec else None,
         "decode_plain_gbs": finite(dec["plain_gbs"]) if dec else None,
         "decode_router_fp8_ms": finite(dec["r8_ms"]) if dec else None,

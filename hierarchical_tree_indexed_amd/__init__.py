@@ -48,7 +48,7 @@ class Tree(C.Structure):
 
 class Select(C.Structure):
     _fields_ = [("mode", C.c_int32), ("k", C.c_int32), ("p", C.c_float), ("cap", C.c_int32),
-                ("per_head", C.c_int32), ("leaf_only", C.c_int32)]
+                ("per_head", C.c_int32), ("leaf_only", C.c_int32), ("token_nodes", C.c_int32)]
 
 
 class PlanOut(C.Structure):
@@ -119,12 +119,14 @@ def _stream(stream=None):
 
 
 def make_select(mode: str = "topk", k: int = 8, p: float = 1.0, cap: int = 16,
-                per_head: bool = False, leaf_only: bool = False) -> Select:
+                per_head: bool = False, leaf_only: bool = False, token_nodes: bool = False) -> Select:
     """Selection rule; per_head: every query head routes on its own instead of
     its KV group sharing one selection; leaf_only: only the reached tokens are
-    attended (the summaries route but do not join the softmax)."""
+    attended (the summaries route but do not join the softmax); token_nodes
+    (prefill): the prefix token level runs node-inverted (queries grouped by
+    kept level-1 node) instead of every query gathering its own token rows."""
     return Select(TOPK if mode == "topk" else TOPP, k, p, cap, 1 if per_head else 0,
-                  1 if leaf_only else 0)
+                  1 if leaf_only else 0, 1 if token_nodes else 0)
 
 
 def make_cfg(B, Hq, Hkv, d, b, levels, R, dtype, Lcap, rope_base=10000.0, rope_npos=1,

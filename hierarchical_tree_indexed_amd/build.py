@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhti.so")
 SOURCES = ["hti_api.hip", "hti_build.hip", "hti_traverse.hip", "hti_decode.hip", "hti_prefill.hip",
-           "hti_prefill_walk.hip"]
+           "hti_prefill_walk.hip", "hti_prefill_nodes.hip"]
 # on-device floors for the measurement (latency, bandwidth, matrix-core peak):
 # a library of its own, loaded only by the benchmark
 PROBE_LIB = os.path.join(HERE, "libhti_probe.so")

@@ -93,6 +93,7 @@ hti_status check_select(const hti_select *s)
     }
     if (s->per_head != 0 && s->per_head != 1) return fail(HTI_ERR_INVALID_ARG, "per_head must be 0 or 1");
     if (s->leaf_only != 0 && s->leaf_only != 1) return fail(HTI_ERR_INVALID_ARG, "leaf_only must be 0 or 1");
+    if (s->token_nodes != 0 && s->token_nodes != 1) return fail(HTI_ERR_INVALID_ARG, "token_nodes must be 0 or 1");
     return HTI_OK;
 }
 
@@ -227,15 +228,24 @@ hti_status launched(hipError_t e, const char *what)
 }
 
 struct PrefillWs {
-    size_t part_acc, part_ml, qr, kr, vt, top_s, top_z, total;
+    size_t part_acc, part_ml, qr, kr, vt, top_s, top_z;
+    // node-inverted token level (nodes)
+    size_t kept1, nsel1, cnt, ptot, pairs, po, pml;
+    size_t total;
     int64_t ntop;       // top-level capacity when the top level is scored on the matrix cores, else 0
+    bool nodes;
+    int keff, ntrees;
+    int64_t cap_t, cnt_words;
 };
 
 size_t inblock_tp(int32_t T) { return ((size_t)T + kInblockKeys - 1) / kInblockKeys * kInblockKeys; }
 
-PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T, int hu)
+// sel == NULL sizes for shared routing with the largest kept set and the
+// node-inverted token level
+PrefillWs prefill_ws(const hti_tree_cfg *c, const hti_select *sel, int32_t T)
 {
     PrefillWs w{};
+    const int hu = routing_heads(c, sel);
     const size_t rows = (size_t)c->B * (size_t)T;
     int64_t ncap[HTI_MAX_LEVELS + 1];
     caps(c, ncap);
@@ -256,6 +266,29 @@ PrefillWs prefill_ws(const hti_tree_cfg *c, int32_t T, int hu)
     off += align256(rows * (size_t)hu * (size_t)w.ntop * sizeof(float));
     w.top_z = off;
     off += align256(rows * c->Hq * (size_t)w.ntop * sizeof(float));
+    w.nodes = token_nodes_apply(c, sel);
+    if (w.nodes) {
+        const size_t units = rows * (size_t)hu;
+        const int G = c->Hq / hu;
+        w.keff = sel ? sel_size(sel) : HTI_MAX_SELECT;
+        w.ntrees = c->B * c->Hkv;
+        w.cap_t = (int64_t)T * (hu / c->Hkv) * w.keff;
+        w.cnt_words = (int64_t)w.ntrees * ncap[1];
+        w.kept1 = off;
+        off += align256(units * w.keff * 4);
+        w.nsel1 = off;
+        off += align256(units * 4);
+        w.cnt = off;
+        off += align256((size_t)w.cnt_words * 4);
+        w.ptot = off;
+        off += align256((size_t)w.ntrees * 4);
+        w.pairs = off;
+        off += align256((size_t)w.ntrees * w.cap_t * 16);
+        w.po = off;
+        off += align256(units * w.keff * G * c->d * 2);
+        w.pml = off;
+        off += align256(units * w.keff * G * 2 * sizeof(float));
+    }
     w.total = off;
     return w;
 }
@@ -518,7 +551,7 @@ hti_status hti_decode_step(const hti_tree *tree, const hti_select *sel, const vo
 size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *sel, int32_t T)
 {
     if (check_cfg(cfg) || T < 0 || (sel && check_select(sel))) return 0;
-    return prefill_ws(cfg, T, routing_heads(cfg, sel)).total;
+    return prefill_ws(cfg, sel, T).total;
 }
 
 hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const void *q_blk,
@@ -532,7 +565,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     if (tree->cfg.dtype != HTI_BF16)
         return fail(HTI_ERR_UNSUPPORTED, "prefill runs on bf16 matrix cores; dtype must be bf16");
     if (!q_blk || !k_blk || !v_blk || !out) return fail(HTI_ERR_INVALID_ARG, "q/k/v/out is NULL");
-    const PrefillWs w = prefill_ws(&tree->cfg, T, routing_heads(&tree->cfg, sel));
+    const PrefillWs w = prefill_ws(&tree->cfg, sel, T);
     if (!ws || ws_bytes < w.total)
         return fail(HTI_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
     const int64_t units = (int64_t)tree->cfg.B * T * routing_heads(&tree->cfg, sel);
@@ -583,8 +616,41 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
         ta.top_z = pa.top_z;
         ta.ntop_stride = pa.ntop_stride;
     }
+    if (w.nodes) {
+        if ((int64_t)units * w.keff >= (int64_t(1) << 32) || (int64_t)tree->cfg.B * T * tree->cfg.Hq >= (int64_t(1) << 32))
+            return fail(HTI_ERR_UNSUPPORTED, "too many (query, group, rank) pairs for the node-inverted token level");
+        ta.kept1 = (int *)(wb + w.kept1);
+        ta.nsel1 = (int *)(wb + w.nsel1);
+        ta.node_cnt = (uint32_t *)(wb + w.cnt);
+        e = launch_zero(ta.node_cnt, (size_t)w.cnt_words * 4, hs);
+        if (e != hipSuccess) return launched(e, "sparse_prefill(zero counts)");
+    }
     e = launch_prefill_walk(ta, bounds(&tree->cfg, sel, T).max_summary, units, hs);
     if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
+    if (w.nodes) {
+        NodeArgs na{};
+        na.t = ta.t;
+        na.q = q_blk;
+        na.T = T;
+        na.keff = w.keff;
+        na.cap_t = w.cap_t;
+        na.ntrees = w.ntrees;
+        na.kept1 = ta.kept1;
+        na.nsel1 = ta.nsel1;
+        na.cnt = ta.node_cnt;
+        na.ptot = (uint32_t *)(wb + w.ptot);
+        na.pairs = (uint4 *)(wb + w.pairs);
+        na.po = (uint16_t *)(wb + w.po);
+        na.pml = (float *)(wb + w.pml);
+        na.part_acc = ta.part_acc;
+        na.part_ml = ta.part_ml;
+        e = launch_token_pairs(na, units, hs);
+        if (e != hipSuccess) return launched(e, "sparse_prefill(token pairs)");
+        e = launch_token_nodes(na, hs);
+        if (e != hipSuccess) return launched(e, "sparse_prefill(token nodes)");
+        e = launch_token_merge(na, units, hs);
+        if (e != hipSuccess) return launched(e, "sparse_prefill(token merge)");
+    }
 
     pa.t = tree_args(tree);
     pa.part_acc = ta.part_acc;

@@ -56,6 +56,12 @@ struct TravArgs {
     int ntop_stride;
     float *part_acc;     // [B, T, Hq, D] unnormalised partial outputs
     float *part_ml;      // [B, T, Hq, 2] running max and denominator
+    // prefill with the node-inverted token level (kept1 != nullptr): the
+    // traversal leaves each unit's kept level-1 list, counts the units per
+    // level-1 node, and attends only to the orphan tokens itself
+    int *kept1;          // [units][keff] kept level-1 node ids, in kept order
+    int *nsel1;          // [units] their number
+    uint32_t *node_cnt;  // [trees][ncap1] units per node (zeroed before the traversal)
 };
 
 // Workspace of the split decode (zeroed by the caller before first use, then
@@ -114,6 +120,29 @@ constexpr int kTopCols = 64;
 // Key tile of the in-block product; the transposed V rows are padded to it.
 constexpr int kInblockKeys = 64;
 hipError_t launch_top_scores(const PrefillArgs &a, hipStream_t s);
+
+// Node-inverted token level of a prefill block (the traversal's kept level-1
+// lists grouped by node; each node's token rows read once for all its queries).
+struct NodeArgs {
+    TreeArgs t;                // routing view: Hkv routing heads of G query heads
+    const void *q;             // block queries [B, T, Hq, D] bf16
+    int T, keff;               // block length; largest kept set per level
+    int64_t cap_t;             // pair capacity of one tree (T * hdiv * keff)
+    int ntrees;                // B * Hkv / hdiv
+    const int *kept1;          // [units][keff]
+    const int *nsel1;          // [units]
+    uint32_t *cnt;             // [ntrees][ncap1]: counts, then run offsets (scan), then run ends (scatter)
+    uint32_t *ptot;            // [ntrees] pairs per tree
+    uint4 *pairs;              // [ntrees][cap_t] pairs by node: (node id, unit * keff + rank,
+                               // the query's rotation position P - rank * b, its first q row)
+    uint16_t *po;              // [units * keff][G][D] bf16: each pair's normalised token-level output
+    float *pml;                // [units * keff][G][2] its max and denominator
+    float *part_acc, *part_ml; // the traversal's partial states, merged in place
+};
+bool token_nodes_apply(const hti_tree_cfg *c, const hti_select *sel);
+hipError_t launch_token_pairs(const NodeArgs &a, int64_t units, hipStream_t s);
+hipError_t launch_token_nodes(const NodeArgs &a, hipStream_t s);
+hipError_t launch_token_merge(const NodeArgs &a, int64_t units, hipStream_t s);
 hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_inblock_attention(const PrefillArgs &a, hipStream_t s);
 

@@ -595,6 +595,14 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
             int *o = a.sel + (uidx * levels + (lvl - 1)) * a.sel_stride;
             for (int r = lane; r < a.sel_stride; r += 64) o[r] = (r < nn) ? nsl[r] : -1;
         }
+        if (lvl == 1 && a.kept1) {
+            // the node-inverted token level takes the kept nodes' tokens
+            for (int r = lane; r < nn; r += 64) {
+                a.kept1[uidx * keff + r] = nsl[r];
+                atomicAdd(&a.node_cnt[bh * t.ncap[1] + nsl[r]], 1u);
+            }
+            if (lane == 0) a.nsel1[uidx] = nn;
+        }
         if (!take_all && !a.leaf_only) {
             softmax_step(m, kept);
             fold(cs, vb, 0, m);     // ids through cs, i.e. the parents' list
@@ -605,7 +613,8 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 
     // ---- token level: reached prefix tokens, then orphan prefix tokens; the
     // block tokens follow them (handled by the in-block kernel), so query t
-    // sits at |C_0| + t
+    // sits at |C_0| + t.  With the node-inverted token level (kept1) only the
+    // orphan tokens are attended here.
     {
         Cands cs;
         const bool top = (levels == 0);
@@ -620,7 +629,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         const int qpos = m0 + qi;
         const T *kc = (const T *)t.kc + bh * t.ncap[0] * D;
         const T *vc = (const T *)t.vc + bh * t.ncap[0] * D;
-        for (int c0 = 0; c0 < m0; c0 += MC) {
+        for (int c0 = a.kept1 ? nsel * b : 0; c0 < m0; c0 += MC) {
             const int mc = min(MC, m0 - c0);
             score(std::false_type{}, std::false_type{}, cs, kc, nullptr, 1, c0, mc, qpos);
             softmax_step(mc, 0u);

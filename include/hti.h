@@ -19,9 +19,10 @@
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers owned by the caller, unless the
  *     argument says "host".  The library never allocates, frees or retains
- *     device memory; the only device state it keeps between calls is in the
- *     decode workspace the caller hands it (a status word, per-unit launch
- *     counters, per-sequence step counts).
+ *     device memory, with one exception: the static device array that
+ *     hti_sparse_decode_static uses as its workspace.  The only device state
+ *     it keeps between calls is in the decode workspace the caller hands it
+ *     (a status word, per-unit launch counters, per-sequence step counts).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *     call only enqueues work on it and returns; results are valid once the
  *     stream has reached that point.
@@ -127,6 +128,17 @@ typedef struct {
                            reached tokens are attended, the summaries serve the
                            routing alone (the leaf union the ZHA router
                            dispatches, ZHA Figure 3 caption) */
+    int32_t token_nodes;/* prefill only.  0: every query gathers its own prefix
+                           token rows in the traversal (fp32 logits).  1: the
+                           token level of the prefix runs node-inverted -- the
+                           block's queries are grouped by the level-1 nodes they
+                           kept, and each kept node's b token rows are read once
+                           per block and multiplied with all of its queries on
+                           the matrix cores (bf16 operands, fp32 accumulation;
+                           the token level selects nothing) -- wherever the
+                           geometry allows it (levels >= 1, b <= 32; else as 0).
+                           Selections are the same; outputs agree to the output
+                           tolerance. */
 } hti_select;
 
 /* Sizes for a configuration (all host values). */

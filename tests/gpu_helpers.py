@@ -45,8 +45,8 @@ def make_treeset(w, Lcap, K=None, V=None, refs=None, T=0, rope_npos=None, router
     return ts
 
 
-def select_of(w):
-    return hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap)
+def select_of(w, **kw):
+    return hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap, **kw)
 
 
 def kmax_of(w):

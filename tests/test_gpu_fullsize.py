@@ -190,7 +190,13 @@ def test_prefill_524k_block_router_fp8_sampled():
     _prefill_full(router_fp8=True)
 
 
-def _prefill_full(router_fp8):
+def test_prefill_524k_block_token_nodes_sampled():
+    """The same block with the node-inverted token level (the block's queries
+    grouped by kept level-1 node)."""
+    _prefill_full(router_fp8=False, token_nodes=True)
+
+
+def _prefill_full(router_fp8, token_nodes=False):
     w = W.PREFILL
     T = w.T
     log(f"full-size prefill {w.name}: L={w.L} T={T}")
@@ -199,7 +205,7 @@ def _prefill_full(router_fp8):
     ts = make_treeset(w, w.L, K, V, refs.to(DEV), T=T, router_fp8=router_fp8)
     ts.tree_build([w.L] * w.B)
     qb, kb, vb = W.gen_block(w)
-    sel = select_of(w)
+    sel = select_of(w, token_nodes=token_nodes)
     ws = torch.empty(ts.prefill_workspace_bytes(sel, T), dtype=torch.uint8, device=DEV)
     out = torch.empty((w.B, T, w.Hq, w.d), dtype=torch.float32, device=DEV)
     lse = torch.empty((w.B, T, w.Hq), dtype=torch.float32, device=DEV)

@@ -598,8 +598,8 @@ def test_extend_clamps_at_capacity():
 
 
 # --------------------------------------------------------------------------- prefill
-def _prefill(ts, w, T, qb, kb, vb):
-    sel = select_of(w)
+def _prefill(ts, w, T, qb, kb, vb, token_nodes=False):
+    sel = select_of(w, token_nodes=token_nodes)
     ws = torch.empty(ts.prefill_workspace_bytes(sel, T), dtype=torch.uint8, device=DEV)
     out = torch.empty((w.B, T, w.Hq, w.d), dtype=torch.float32, device=DEV)
     lse = torch.empty((w.B, T, w.Hq), dtype=torch.float32, device=DEV)
@@ -610,7 +610,7 @@ def _prefill(ts, w, T, qb, kb, vb):
     return out.cpu().numpy(), lse.cpu().numpy(), so.cpu().numpy()
 
 
-def _check_prefill(w, P0, T, ts_list=None, queries=None, edit_kv=None):
+def _check_prefill(w, P0, T, ts_list=None, queries=None, edit_kv=None, token_nodes=False):
     w = w.replace(L=P0, T=T)
     K, V = W.gen_kv(w, Lcap=max(P0, 1))
     if edit_kv is not None:
@@ -619,7 +619,7 @@ def _check_prefill(w, P0, T, ts_list=None, queries=None, edit_kv=None):
     ts = make_treeset(w, max(P0, 1), K.to(DEV), V.to(DEV), refs.to(DEV), T=T)
     ts.tree_build([P0] * w.B)
     qb, kb, vb = W.gen_block(w)
-    out, lse, so = _prefill(ts, w, T, qb, kb, vb)
+    out, lse, so = _prefill(ts, w, T, qb, kb, vb, token_nodes=token_nodes)
     queries = queries if queries is not None else range(T)
     nex, emax = 0, 0.0
     for bi in range(w.B):
@@ -633,17 +633,20 @@ def _check_prefill(w, P0, T, ts_list=None, queries=None, edit_kv=None):
                                  lse[bi, t, hs], so[bi, t, g], t=t, blk_k=bk, blk_v=bv)
                 nex += ex
                 emax = max(emax, err)
-    log(f"  prefill P0={P0} T={T}: exempt={nex} max_err={emax:.2e}")
+    log(f"  prefill P0={P0} T={T} token_nodes={token_nodes}: exempt={nex} max_err={emax:.2e}")
     return out, nex
 
 
 PF = W.PREFILL.replace(name="pf_small")
 
 
+@pytest.mark.parametrize("token_nodes", [False, True])
 @pytest.mark.parametrize("P0,T,levels", [(3000, 100, 2), (32 * 32 * 4 + 70, 77, 2), (5000, 1, 2),
                                          (0, 130, 2), (40, 64, 1), (2000, 33, 0)])
-def test_prefill_parity(P0, T, levels):
-    _check_prefill(PF.replace(levels=levels, k=8 if levels else 32), P0, T)
+def test_prefill_parity(P0, T, levels, token_nodes):
+    """token_nodes True: the prefix token level node-inverted (levels >= 1);
+    False: every query gathers its own token rows."""
+    _check_prefill(PF.replace(levels=levels, k=8 if levels else 32), P0, T, token_nodes=token_nodes)
 
 
 @pytest.mark.parametrize("Hq,Hkv,R,k,P0", [(32, 8, 1, 8, 32 * 32 * 12 + 70), (8, 8, 1, 8, 32 * 32 * 12 + 70),
@@ -683,15 +686,29 @@ def test_prefill_exact_ties():
     assert nex == 0
 
 
-def test_prefill_b24():
+@pytest.mark.parametrize("token_nodes", [False, True])
+def test_prefill_b24(token_nodes):
     """A branching factor that is not a power of two (b = 24): candidate
-    positions, orphans and the division by b in the index arithmetic."""
+    positions, orphans and the division by b in the index arithmetic; in the
+    node-inverted token level, tokens 24..31 of the second 16-token tile are
+    masked."""
     w = PF.replace(b=24, levels=2, k=6)
-    _check_prefill(w, 24 * 24 * 3 + 50, 40)
+    _check_prefill(w, 24 * 24 * 3 + 50, 40, token_nodes=token_nodes)
 
 
-def test_prefill_topp_r4():
-    _check_prefill(W.ZHA2M.replace(name="pf_topp", levels=3), 16 ** 3 * 3 + 50, 48)
+@pytest.mark.parametrize("token_nodes", [False, True])
+def test_prefill_topp_r4(token_nodes):
+    """Top-p with four reference keys and b = 16 (one 16-token tile per node
+    in the node-inverted token level; kept sets of varying size)."""
+    _check_prefill(W.ZHA2M.replace(name="pf_topp", levels=3), 16 ** 3 * 3 + 50, 48, token_nodes=token_nodes)
+
+
+def test_prefill_small_b_hot_node():
+    """b = 5 (one partly masked token tile) and every query keeping every
+    level-1 node (take-all at level 1): each node's run spans many waves of
+    the node-inverted token level."""
+    w = PF.replace(b=5, levels=1, k=8)
+    _check_prefill(w, 5 * 7 + 3, 200, token_nodes=True)
 
 
 def test_prefill_T1_equals_decode():

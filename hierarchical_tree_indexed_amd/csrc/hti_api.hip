@@ -228,7 +228,7 @@ hti_status launched(hipError_t e, const char *what)
 }
 
 struct PrefillWs {
-    size_t part_acc, part_ml, qr, kr, vt, top_s, top_z;
+    size_t part_acc, part_ml, kr, vt, top_s, top_z;
     // node-inverted token level (nodes)
     size_t kept1, nsel1, cnt, ptot, pairs, po, pml;
     size_t total;
@@ -256,8 +256,6 @@ PrefillWs prefill_ws(const hti_tree_cfg *c, const hti_select *sel, int32_t T)
     off += align256(rows * c->Hq * c->d * sizeof(float));
     w.part_ml = off;
     off += align256(rows * c->Hq * 2 * sizeof(float));
-    w.qr = off;
-    off += align256(rows * c->Hq * c->d * 2);
     w.kr = off;
     off += align256((size_t)c->B * inblock_tp(T) * c->Hkv * c->d * 2);
     w.vt = off;
@@ -657,7 +655,6 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     pa.part_ml = ta.part_ml;
     pa.out = out;
     pa.lse = lse;
-    pa.qr = wb + w.qr;
     pa.kr = wb + w.kr;
     pa.vt = wb + w.vt;
     pa.Tp = (int)inblock_tp(T);

@@ -110,7 +110,7 @@ struct PrefillArgs {
     int ntop_stride;
     const float *part_acc, *part_ml;
     float *out, *lse;
-    void *qr, *kr;             // rotated block q/k (bf16 staging) [B, Hq|Hkv, T, D]
+    void *kr;                  // rotated block k (bf16 staging) [B, Hkv, Tp, D]
     void *vt;                  // block v transposed (bf16 staging) [B, Hkv, D, Tp]
     int Tp;                    // T rounded up to the in-block key tile
 };

@@ -19,37 +19,31 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float floatx4;
 
 // ----------------------------------------------------------------------------
-// Rotate the block's q and k by their block-local index and store them as
-// bf16 in head-major layout: qr [B, Hq, T, D], kr [B, Hkv, Tp, D] (rows T ..
-// Tp-1 of kr are zero).  A thread rotates 8 consecutive pairs (j, j + D/2).
+// Rotate the block's keys by their block-local index and store them as bf16
+// in head-major layout: kr [B, Hkv, Tp, D] (rows T .. Tp-1 zero).  A thread
+// rotates 8 consecutive pairs (j, j + D/2).  (The queries are rotated by the
+// in-block kernel itself when it loads them.)
 // ----------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_rotate_block(PrefillArgs a)
 {
     const TreeArgs &t = a.t;
-    const int H = t.Hq + t.Hkv;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)t.B * a.Tp * H * (D / 16);
+    const int64_t total = (int64_t)t.B * a.Tp * t.Hkv * (D / 16);
     if (idx >= total) return;
     const int j = 8 * (int)(idx % (D / 16));
     int64_t r = idx / (D / 16);
-    const int hh = (int)(r % H);
-    r /= H;
+    const int h = (int)(r % t.Hkv);
+    r /= t.Hkv;
     const int tt = (int)(r % a.Tp);
     const int bi = (int)(r / a.Tp);
-    const bool isq = hh < t.Hq;
-    const int h = isq ? hh : hh - t.Hq;
-    const int nh = isq ? t.Hq : t.Hkv;
+    bf16_t *dst = (bf16_t *)a.kr + (((int64_t)bi * t.Hkv + h) * a.Tp + tt) * D;
     if (tt >= a.T) {
-        if (!isq) {
-            bf16_t *dst = (bf16_t *)a.kr + (((int64_t)bi * nh + h) * a.Tp + tt) * D;
-            *reinterpret_cast<uint4 *>(dst + j) = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(dst + j + D / 2) = make_uint4(0, 0, 0, 0);
-        }
+        *reinterpret_cast<uint4 *>(dst + j) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(dst + j + D / 2) = make_uint4(0, 0, 0, 0);
         return;
     }
-    const T *src = (const T *)(isq ? a.q : a.k) + (((int64_t)bi * a.T + tt) * nh + h) * D;
-    bf16_t *dst = (bf16_t *)(isq ? a.qr : a.kr) + (((int64_t)bi * nh + h) * (isq ? a.T : a.Tp) + tt) * D;
+    const T *src = (const T *)a.k + (((int64_t)bi * a.T + tt) * t.Hkv + h) * D;
     float x0[8], x1[8];
     load_vec<T, 8>(src + j, x0);
     load_vec<T, 8>(src + j + D / 2, x1);
@@ -71,7 +65,7 @@ __global__ __launch_bounds__(256) void k_rotate_block(PrefillArgs a)
 
 hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s)
 {
-    const int64_t total = (int64_t)a.t.B * a.Tp * (a.t.Hq + a.t.Hkv) * (a.t.D / 16);
+    const int64_t total = (int64_t)a.t.B * a.Tp * a.t.Hkv * (a.t.D / 16);
     if (total == 0) return hipSuccess;
     dim3 grid((unsigned)((total + 255) / 256)), block(256);
     if (a.t.dtype == HTI_BF16) {
@@ -199,15 +193,36 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
     const float c2 = t.scale * 1.4426950408889634f;   // scale * log2(e)
 
     // Q fragments (B operand of S^T = K Q^T): column = query, k-slots 8*grp..
+    // of step s.  Each query is rotated by its block-local index here: the
+    // first-half steps hold x_i c - x_{i+D/2} s, the second-half steps
+    // x_i s + x_{i+D/2} c (i = 32*s + 8*grp + e), rounded to bf16.
     bf16x8 qf[QT][KS];
     {
-        const bf16_t *qb = (const bf16_t *)a.qr + (((int64_t)bi * t.Hq + h) * T) * D;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const int qq = min(q0 + 16 * qt + col, T - 1);
+            const bf16_t *qrow = (const bf16_t *)a.q + (((int64_t)bi * T + qq) * t.Hq + h) * D;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                qf[qt][s] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qq * D + 32 * s + 8 * grp);
+            for (int s = 0; s < KS / 2; ++s) {
+                const int i0 = 32 * s + 8 * grp;
+                float x0[8], x1[8];
+                load_vec<bf16_t, 8>(qrow + i0, x0);
+                load_vec<bf16_t, 8>(qrow + i0 + D / 2, x1);
+                const float4 *cs4 = reinterpret_cast<const float4 *>(t.rope + (int64_t)qq * (D / 2) + i0);
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float4 cs = cs4[e];
+                    const float a0 = x0[2 * e] * cs.x - x1[2 * e] * cs.y;
+                    const float b0 = x0[2 * e] * cs.y + x1[2 * e] * cs.x;
+                    const float a1 = x0[2 * e + 1] * cs.z - x1[2 * e + 1] * cs.w;
+                    const float b1 = x0[2 * e + 1] * cs.w + x1[2 * e + 1] * cs.z;
+                    lo[e] = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
+                    hi[e] = (uint32_t)f2bf(b0) | ((uint32_t)f2bf(b1) << 16);
+                }
+                qf[qt][s] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                qf[qt][s + KS / 2] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            }
         }
     }
 
@@ -232,6 +247,8 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
             lacc[qt] = floatx4{L, L, L, L};
             mrow[qt] = (M == -INFINITY) ? -INFINITY : M * 1.4426950408889634f;
             const float *pa = a.part_acc + row * D;
+            // (a prefix with nothing to attend leaves no output row)
+            if (M != -INFINITY)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const float4 v = *reinterpret_cast<const float4 *>(pa + 16 * dt + 4 * grp);
@@ -251,75 +268,77 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
     // offsets relative to the tile are fixed per lane; pad chunks copy nothing.
     constexpr int KSEG = KCHUNKS / 64;
     static_assert(KCHUNKS % 64 == 0, "K rows end on a segment boundary");
+    // (element offset, or -1 where the lane copies nothing)
     int off[SPW];
-    bool live[SPW];
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
         const int seg = wave + NW * u;
         const int ci = seg * 64 + lane;
         if (seg < KSEG) {
             const int r = ci / KCH, p = ci % KCH;
-            off[u] = r * D + 8 * p;
-            live[u] = p < D / 8;
+            off[u] = p < D / 8 ? r * D + 8 * p : -1;
         } else {
             const int r = (ci - KCHUNKS) / VCH, p = (ci - KCHUNKS) % VCH;
-            off[u] = r * Tp + 8 * p;
-            live[u] = p < IKT / 8 && r < D;
+            off[u] = (p < IKT / 8 && r < D) ? r * Tp + 8 * p : -1;
         }
     }
-    auto issue = [&](int j, char *buf) __attribute__((always_inline)) {
+    // parts: 1 = the K rows, 2 = the V^T rows, 3 = both
+    auto issue_parts = [&](int j, char *buf, int parts) __attribute__((always_inline)) {
         const int kt0 = j * IKT;
         const bf16_t *kt = kb + (int64_t)kt0 * D, *vt = vtb + kt0;
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int seg = wave + NW * u;
             if (seg >= NSEG) break;
-            if (live[u])
+            if (off[u] >= 0 && (parts & (seg < KSEG ? 1 : 2)))
                 __builtin_amdgcn_global_load_lds((gvoid_t)((seg < KSEG ? kt : vt) + off[u]),
                                                  (lvoid_t)(buf + seg * 1024), 16, 0, 0);
         }
     };
+    auto issue = [&](int j, char *buf) __attribute__((always_inline)) { issue_parts(j, buf, 3); };
 
     const int kbase = col * KRS + 16 * grp;                 // K row col, chunk grp
     const int vbase = KCHUNKS * 16 + col * VRS + 16 * grp;  // V^T row col, chunk grp
 
-    // one key tile of the product; diag: some key of the tile follows some
-    // query of the wave, so the causal mask applies
-    auto tile = [&](int kt0, const char *buf, bool diag) __attribute__((always_inline)) {
-        // S^T: 16-key tile tm holds keys kt0 + 16*tm + 4*grp + i in lane
-        // (col = query, grp), element i.  A query tile wholly before the
-        // tile's keys is multiplied anyway: the mask leaves it zero weights.
-        floatx4 sc[QT][4];
+    // One key tile of the product in four parts: scores (S^T MFMAs), prep
+    // (causal mask and the running max), expo (probabilities) and pv (O^T
+    // and the row sums).  diag: some key of the tile follows some query of
+    // the wave, so the causal mask applies.
+    //
+    // S^T: 16-key tile tm holds keys kt0 + 16*tm + 4*grp + i in lane
+    // (col = query, grp), element i.  A query tile wholly before the tile's
+    // keys is multiplied anyway: the mask leaves it zero weights.
+    auto scores = [&](const char *buf, floatx4 (&sc)[QT][4], int q_lo, int q_hi) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm) {
                 const bf16x8 af = *reinterpret_cast<const bf16x8 *>(buf + kbase + 16 * tm * KRS + 64 * s);
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt)
+                for (int qt = q_lo; qt < q_hi; ++qt)
                     sc[qt][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         af, qf[qt][s], s == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sc[qt][tm], 0, 0, 0);
             }
-        // online softmax per query tile, in log2 units (c2 = scale*log2 e);
-        // P of 32-key step kg goes to slots 4*m + i of pf[kg] (tm = 2*kg + m).
-        // The exponent reference mrow is the query's running max, raised
-        // only when a score exceeds it by more than kLazy: probabilities stay
-        // below 2^kLazy and the rescale of the accumulators is rare.
+    };
+    // online softmax per query tile, in log2 units (c2 = scale*log2 e).  The
+    // exponent reference mrow is the query's running max, raised only when a
+    // score exceeds it by more than kLazy: probabilities stay below 2^kLazy
+    // and the rescale of the accumulators is rare.
+    auto prep = [&](int kt0, floatx4 (&sc)[QT][4], bool diag, int q_lo, int q_hi) __attribute__((always_inline)) {
         if (diag) {
             // (the empty asm keeps this a branch: as selects, the compares
             // would run on every tile)
             asm volatile("");
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
+            for (int qt = q_lo; qt < q_hi; ++qt)
 #pragma unroll
                 for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (kt0 + 16 * tm + 4 * grp + i > q0 + 16 * qt + col) sc[qt][tm][i] = -INFINITY;
         }
-        bf16x8 pf[QT][2];
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
+        for (int qt = q_lo; qt < q_hi; ++qt) {
             float lmax = -INFINITY;
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
@@ -335,6 +354,13 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
                 for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
                 mrow[qt] = mnew;
             }
+        }
+    };
+    // P of 32-key step kg goes to slots 4*m + i of pf[kg] (tm = 2*kg + m)
+    auto expo = [&](const floatx4 (&sc)[QT][4], bf16x8 (&pf)[QT][2], int q_lo, int q_hi)
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int qt = q_lo; qt < q_hi; ++qt) {
             const float nmu = (mrow[qt] == -INFINITY) ? 0.f : -mrow[qt];
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
@@ -343,21 +369,31 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
                     pf[qt][tm >> 1][4 * (tm & 1) + i] =
                         (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][tm][i], c2, nmu));
         }
-        // O^T += V^T P^T; V^T row d = 16*dt + col, k-slots 8*grp.. of step kg.
-        // The row sums of P come from the same product with a ones operand.
+    };
+    // O^T += V^T P^T; V^T row d = 16*dt + col, k-slots 8*grp.. of step kg.
+    // The row sums of P come from the same product with a ones operand.
+    auto pv = [&](const char *buf, const bf16x8 (&pf)[QT][2], int q_lo, int q_hi) __attribute__((always_inline)) {
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
+            for (int qt = q_lo; qt < q_hi; ++qt)
                 lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt][kg], lacc[qt], 0, 0, 0);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(buf + vbase + 16 * dt * VRS + 64 * kg);
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt)
+                for (int qt = q_lo; qt < q_hi; ++qt)
                     o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kg], o[qt][dt], 0, 0, 0);
             }
         }
+    };
+    auto tile = [&](int kt0, const char *buf, bool diag) __attribute__((always_inline)) {
+        floatx4 sc[QT][4];
+        bf16x8 pf[QT][2];
+        scores(buf, sc, 0, QT);
+        prep(kt0, sc, diag, 0, QT);
+        expo(sc, pf, 0, QT);
+        pv(buf, pf, 0, QT);
     };
     auto compute = [&](int j, const char *buf) __attribute__((always_inline)) {
         const int kt0 = j * IKT;

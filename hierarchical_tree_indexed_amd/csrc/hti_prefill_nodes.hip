@@ -334,8 +334,9 @@ __global__ __launch_bounds__(256) void k_token_merge(NodeArgs a, int64_t rows)
     const int nsel = a.nsel1[unit];
     float Mn = a.part_ml[row * 2 + 0], Lw = a.part_ml[row * 2 + 1];
     float acc[EPL];
+    // (a state with nothing attended has no output row)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = a.part_acc[row * D + lane * EPL + e];
+    for (int e = 0; e < EPL; ++e) acc[e] = Mn == -INFINITY ? 0.f : a.part_acc[row * D + lane * EPL + e];
     for (int r0 = 0; r0 < nsel; r0 += RG) {
         float m[RG], l[RG], o[RG][EPL];
 #pragma unroll

@@ -642,8 +642,11 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const float l = wave_sum(lt[h]);
+        // a head with nothing attended (M = -inf: an empty prefix) leaves no
+        // output row; its readers take it as zero
+        if (M[h] != -INFINITY)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) a.part_acc[(row0 + h) * D + lane * DPL + e] = acc[h][e];
+            for (int e = 0; e < DPL; ++e) a.part_acc[(row0 + h) * D + lane * DPL + e] = acc[h][e];
         if (lane == 0) {
             a.part_ml[(row0 + h) * 2 + 0] = M[h];
             a.part_ml[(row0 + h) * 2 + 1] = l;

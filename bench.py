@@ -481,7 +481,7 @@ def copy_calibration():
 PHASES = {1: "entry", 2: "length and query read", 3: "first gathers issued", 4: "scored (B1)",
           5: "slice ranked (B2)", 6: "slice published", 7: "exchange read (B3)", 8: "exchange ranked (B4)",
           9: "kept set known", 10: "next gathers issued", 11: "level folded", 12: "tokens scored",
-          13: "tokens folded", 14: "partial published", 15: "partials gathered", 16: "output written",
+          13: "tokens folded", 14: "partial stored", 15: "arrival counted", 16: "output written (last arrival)",
           17: "take-all levels resolved", 18: "first keys issued", 19: "append checked"}
 
 

@@ -118,6 +118,7 @@ struct DSmem {
     int app;                          // decode step: the new token goes in at position lold
     int lold;                         // sequence length before the step
     int bad;                          // a wait of this workgroup ran out
+    int last;                         // this workgroup arrived last at the unit's final merge
 #ifdef HTI_DECODE_TIMELINE
     uint64_t tl[kTlEvents];
 #endif
@@ -1155,9 +1156,11 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     fold_pending();     // (a token level with no candidates for this workgroup)
 
     // Partial state of this workgroup: the quarters' sums within each wave by
-    // lane swaps, then across waves in LDS; as tagged words in the workspace.
-    // Every workgroup then merges a slice of the output columns from all W.
-    uint64_t *pw_unit = ws.part + unit * (int64_t)W * G * (D + 2);
+    // lane swaps, then across waves in LDS; stored (fp32) in the workspace and
+    // released before one arrival count per unit.  The workgroup that arrives
+    // last acquires, merges every output column from all W partial states and
+    // writes the outputs; the others are done.
+    float *pf_unit = ws.part + unit * (int64_t)W * G * (D + 2);
     {
         float *red = reinterpret_cast<float *>(hti_dec_lds);     // [DNW][G][D], then [DNW][G] sums
         float *redl = red + DNW * G * D;
@@ -1173,7 +1176,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             if (lane == 0) redl[wave * G + h] = l4;
         }
         __syncthreads();
-        uint64_t *mine = pw_unit + (int64_t)wg * G * (D + 2);
+        float *mine = pf_unit + (int64_t)wg * G * (D + 2);
         for (int i = tid; i < G * (D + 2); i += DNT) {
             const int h = i / (D + 2), e = i % (D + 2);
             float v = 0.f;
@@ -1187,96 +1190,68 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 #pragma unroll
                 for (int w = 0; w < DNW; ++w) v += redl[w * G + h];
             }
-            __hip_atomic_store(&mine[i], ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+            // (agent-scope stores reach the point where every XCD sees them;
+            // an agent-scope release fence would write back the whole L2)
+            __hip_atomic_store(reinterpret_cast<uint32_t *>(mine + i), __float_as_uint(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    DTL(14, 0);
-    // Gather n tagged words (word i at src(i)) into LDS at dst(i): every load
-    // is issued first, then only words whose tag is not yet current are polled.
-    auto gather_words = [&](int n, auto src, auto dst) __attribute__((always_inline)) {
-        for (int i0 = 0; i0 < n; i0 += 2 * DNT) {
-            uint64_t wv[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = i0 + u * DNT + tid;
-                wv[u] = (i < n) ? __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : ((uint64_t)tag << 32);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = i0 + u * DNT + tid;
-                if (i >= n) continue;
-                long spins = 0;
-                while ((uint32_t)(wv[u] >> 32) != tag && ++spins < kSpin) {
-                    __builtin_amdgcn_s_sleep(1);
-                    wv[u] = __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                if ((uint32_t)(wv[u] >> 32) != tag) {
-                    sm.bad = 1;
-                    wv[u] = 0x7fc00000u;          // NaN: the result is visibly invalid
-                }
-                *dst(i) = __uint_as_float((uint32_t)wv[u]);
-            }
-        }
-    };
-    // (max, denominator) of every slice per head, and this workgroup's output
-    // columns of every slice's unnormalised output, into LDS (one round)
+    // a wait that ran out in this workgroup goes to the status word before
+    // the arrival, so the merging workgroup sees it
+    if (tid == 0 && sm.bad) __hip_atomic_store(ws.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every store of this workgroup has completed before its arrival is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int cols = (D + W - 1) / W;
-    const int d0 = min(D, wg * cols), d1 = min(D, d0 + cols);
-    const int nc = d1 - d0;
-    float *mw = reinterpret_cast<float *>(hti_dec_lds) + DNW * G * D + DNW * G;   // [W][G][2]
-    float *aw = mw + kMaxW * G * 2;                                               // [W][G][nc]
-    const int nmw = W * G * 2;
-    gather_words(nmw + W * G * nc, [&](int i) __attribute__((always_inline)) {
-        if (i < nmw) {
-            const int w = i / (G * 2), r = i % (G * 2);
-            return pw_unit + ((int64_t)w * G + r / 2) * (D + 2) + D + (r % 2);
-        }
-        i -= nmw;
-        const int w = i / (G * nc), r = i % (G * nc);
-        return pw_unit + ((int64_t)w * G + r / nc) * (D + 2) + d0 + (r % nc);
-    }, [&](int i) __attribute__((always_inline)) { return i < nmw ? mw + i : aw + (i - nmw); });
+    DTL(14, 0);
+    if (tid == 0) {
+        const uint32_t n = __hip_atomic_fetch_add(&ws.arrive[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.last = (n == (uint32_t)W - 1u);
+    }
     __syncthreads();
     DTL(15, 0);
-    // a wait that ran out in this workgroup, or anywhere before (the status
-    // word), leaves NaN
-    if (tid == 0 && sm.bad) __hip_atomic_store(ws.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool failed = sm.bad != 0 ||
-        __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-    for (int i = tid; i < G * nc; i += DNT) {
-        const int h = i / nc, c = i % nc;
-        // (all W slices' values read first, then combined in slice order)
-        float Mw[kMaxW], Lw[kMaxW], Aw[kMaxW];
+    bool failed;
+    if (sm.last) {
+        // a wait that ran out in any workgroup of this launch, or before (the
+        // status word), leaves NaN
+        failed = sm.bad != 0 || __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        auto ld = [](const float *p) __attribute__((always_inline)) {
+            return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+        };
+        for (int i = tid; i < G * D; i += DNT) {
+            const int h = i / D, c = i % D;
+            // (all W slices' values read first, then combined in slice order)
+            float Mw[kMaxW], Lw[kMaxW], Aw[kMaxW];
 #pragma unroll
-        for (int w = 0; w < kMaxW; ++w) {
-            Mw[w] = w < W ? mw[(w * G + h) * 2] : -INFINITY;
-            Lw[w] = w < W ? mw[(w * G + h) * 2 + 1] : 0.f;
-            Aw[w] = w < W ? aw[(w * G + h) * nc + c] : 0.f;
-        }
-        float Mx = -INFINITY;
+            for (int w = 0; w < kMaxW; ++w) {
+                const float *pw = pf_unit + ((int64_t)w * G + h) * (D + 2);
+                Mw[w] = w < W ? ld(pw + D) : -INFINITY;
+                Lw[w] = w < W ? ld(pw + D + 1) : 0.f;
+                Aw[w] = w < W ? ld(pw + c) : 0.f;
+            }
+            float Mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kMaxW; ++w) Mx = fmaxf(Mx, Mw[w]);
-        float num = 0.f, den = 0.f;
+            for (int w = 0; w < kMaxW; ++w) Mx = fmaxf(Mx, Mw[w]);
+            float num = 0.f, den = 0.f;
 #pragma unroll
-        for (int w = 0; w < kMaxW; ++w) {
-            const float f = Mw[w] == -INFINITY ? 0.f : __expf(Mw[w] - Mx);
-            num += Aw[w] * f;
-            den += Lw[w] * f;
+            for (int w = 0; w < kMaxW; ++w) {
+                const float f = Mw[w] == -INFINITY ? 0.f : __expf(Mw[w] - Mx);
+                num += Aw[w] * f;
+                den += Lw[w] * f;
+            }
+            a.out[(orow + h) * D + c] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? num / den : 0.f;
+            if (c == 0 && a.lse)
+                a.lse[orow + h] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? Mx + logf(den) : -INFINITY;
         }
-        a.out[(orow + h) * D + d0 + c] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? num / den : 0.f;
-    }
-    if (wg == 0 && tid < G && a.lse) {
-        const int h = tid;
-        float Mx = -INFINITY;
-        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, mw[(w * G + h) * 2]);
-        float den = 0.f;
-        for (int w = 0; w < W; ++w) {
-            const float Mw = mw[(w * G + h) * 2];
-            if (Mw != -INFINITY) den += mw[(w * G + h) * 2 + 1] * __expf(Mw - Mx);
+        // every workgroup of this unit has read the launch tag (each read it
+        // on entry, before its arrival), so the next launch may move it on;
+        // the count starts from zero again
+        if (tid == 0) {
+            ws.epoch[unit] = ws.epoch[unit] + 1u;
+            __hip_atomic_store(&ws.arrive[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        a.lse[orow + h] = failed ? __uint_as_float(0x7fc00000u) : den > 0.f ? Mx + logf(den) : -INFINITY;
+    } else {
+        failed = sm.bad != 0 || __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
     }
     DTL(16, 0);
 #ifdef HTI_DECODE_TIMELINE
@@ -1286,9 +1261,6 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         for (int i = 0; i < kTlEvents; ++i) tr[i] = i < tln ? sm.tl[i] : 0ull;
     }
 #endif
-    // every workgroup of this unit has read the launch tag (they all published
-    // their partial state above), so the next launch may move it on
-    if (wg == 0 && tid == 0) ws.epoch[unit] = ws.epoch[unit] + 1u;
     // decode step: once every workgroup of the sequence has read the old
     // length (bounded wait), the first workgroup of its first unit stores the
     // new one and clears the count for the next step; if the wait runs out,
@@ -1312,10 +1284,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 template <int G, int D>
 constexpr size_t dec_dyn_bytes()
 {
-    // per-wave partial outputs and sums, then the gathered (max, denominator)
-    // and output columns of every slice
-    // (W * ceil(D / W) <= D + W - 1 columns over all slices)
-    return (size_t)(DNW * G * D + DNW * G + kMaxW * G * 2 + G * (D + kMaxW)) * sizeof(float);
+    // per-wave partial outputs and sums
+    return (size_t)(DNW * G * D + DNW * G) * sizeof(float);
 }
 
 namespace {
@@ -1531,8 +1501,9 @@ size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D)
     off += 256;                                                   // status
     off += kTlBytes;                                              // phase timeline (timeline build)
     off += ((size_t)units * 4 + 255) / 256 * 256;                 // epoch
+    off += ((size_t)units * 4 + 255) / 256 * 256;                 // arrival counts
     off += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
-    off += ((size_t)units * W * G * (D + 2) * 8 + 255) / 256 * 256;
+    off += ((size_t)units * W * G * (D + 2) * 4 + 255) / 256 * 256;
     off += ((size_t)B * 4 + 255) / 256 * 256;                     // seqcnt
     return off;
 }
@@ -1545,10 +1516,12 @@ DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, i
     p += 256 + kTlBytes;
     w.epoch = (uint32_t *)p;
     p += ((size_t)units * 4 + 255) / 256 * 256;
+    w.arrive = (uint32_t *)p;
+    p += ((size_t)units * 4 + 255) / 256 * 256;
     w.words = (uint64_t *)p;
     p += ((size_t)units * (levels > 0 ? levels : 1) * W * kSlots * 8 + 255) / 256 * 256;
-    w.part = (uint64_t *)p;
-    p += ((size_t)units * W * G * (D + 2) * 8 + 255) / 256 * 256;
+    w.part = (float *)p;
+    p += ((size_t)units * W * G * (D + 2) * 4 + 255) / 256 * 256;
     w.seqcnt = (uint32_t *)p;
     (void)B;
     return w;

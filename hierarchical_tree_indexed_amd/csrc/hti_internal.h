@@ -65,15 +65,16 @@ struct TravArgs {
 };
 
 // Workspace of the split decode (zeroed by the caller before first use, then
-// owned by the library): a status word, per-unit launch epochs, the per-level
-// exchange words and the per-workgroup partial states, all as words tagged
-// with the launch epoch.
+// owned by the library): a status word, per-unit launch epochs and arrival
+// counts, the per-level exchange words (tagged with the launch epoch) and the
+// per-workgroup partial states.
 struct DecodeWs {
     int W;              // workgroups per (query, KV group) unit
     uint32_t *status;   // nonzero once a wait ran out (sticky until the workspace is zeroed)
     uint32_t *epoch;    // [units]
     uint64_t *words;    // [units][levels][W][HTI_MAX_SELECT + 2]
-    uint64_t *part;     // [units][W][G][D + 2]: tag << 32 | fp32 bits
+    uint32_t *arrive;   // [units]: workgroups of the launch that have stored their partial state
+    float *part;        // [units][W][G][D + 2]: partial output, max, denominator
     uint32_t *seqcnt;   // [B]: workgroups of a decode step that have read the sequence length
 };
 // W > 0: split each unit over W workgroups; W == 0: one workgroup per unit.

@@ -637,6 +637,22 @@ def measure_floors():
     res["mfma_bf16_tflops"] = flop / (best / 1e3) / 1e12
     log(f"[floors] read {res['read_gbs']:.0f} GB/s, copy {res['copy_gbs']:.0f} GB/s, "
         f"bf16 MFMA {res['mfma_bf16_tflops']:.0f} TFLOP/s")
+    # launch ramp: entry-time spread of 256 workgroups (the split decode's
+    # grid) at several workgroup sizes, 40 KB of LDS each
+    P.hti_probe_entry.argtypes = [vp, i32, i32, i32, vp]
+    stamps = torch.zeros(256, dtype=torch.int64, device=DEV)
+    ramp = {}
+    for threads in (64, 128, 256, 512):
+        p90 = []
+        for _ in range(9):
+            assert P.hti_probe_entry(stamps.data_ptr(), 256, threads, 40 * 1024, stream) == 0
+            torch.cuda.synchronize()
+            t = (stamps - stamps.min()).double() * tick_ns / 1e3
+            p90.append(float(torch.quantile(t, 0.9)))
+        ramp[threads] = sorted(p90)[len(p90) // 2]
+        res[f"launch_ramp_us_p90_256wg_{threads}t"] = ramp[threads]
+    log("[floors] launch ramp, p90 of 256 workgroup entries (us): " +
+        ", ".join(f"{k} threads {v:.2f}" for k, v in ramp.items()))
     return res
 
 

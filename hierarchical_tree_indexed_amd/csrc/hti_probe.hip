@@ -11,7 +11,8 @@
 //     split decode uses for its exchanges;
 //   * read bandwidth: every workgroup streams 16-byte loads over a buffer;
 //   * bf16 matrix-core throughput: every wave issues independent chains of
-//     32x32x16 bf16 products on registers.
+//     32x32x16 bf16 products on registers;
+//   * the launch ramp: the spread of the entry times of a grid's workgroups.
 //
 // Times are read from the 100 MHz constant-rate counter (s_memrealtime),
 // whose rate hti_probe_wallclock_khz reports.
@@ -116,6 +117,18 @@ __global__ __launch_bounds__(256) void k_mfma(float *sink, int iters)
     if (s == 1.2345f) sink[0] = s;               // practically never; keeps the products
 }
 
+// Launch ramp: thread 0 of every workgroup stamps the counter on entry
+// (out[block]); the workgroup holds `lds` bytes of dynamic LDS, like the
+// kernels whose start it stands in for.
+__global__ void k_entry(uint64_t *out)
+{
+    extern __shared__ unsigned char entry_lds[];
+    if (threadIdx.x == 0) {
+        entry_lds[0] = 1;
+        out[blockIdx.x] = now_ticks();
+    }
+}
+
 } // namespace
 
 extern "C" {
@@ -146,6 +159,16 @@ int hti_probe_read(const void *buf, int64_t bytes, uint32_t *sink, int32_t block
 {
     if (!buf || !sink || bytes < 16 || blocks < 1) return -1;
     hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, s, (const u32x4 *)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int hti_probe_entry(uint64_t *out, int32_t blocks, int32_t threads, int32_t lds, hipStream_t s)
+{
+    if (!out || blocks < 1 || threads < 64 || threads > 1024 || lds < 1 || lds > 160 * 1024) return -1;
+    if (hipFuncSetAttribute((const void *)k_entry, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+        hipSuccess)
+        return -5;
+    hipLaunchKernelGGL(k_entry, dim3(blocks), dim3(threads), (size_t)lds, s, out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

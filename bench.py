@@ -405,10 +405,11 @@ def bench_prefill(args):
 
         ms_r8 = timed(run_r8, args.prefill_reps)
         del ts8
-    # the dense part alone: the same block over an empty prefix leaves only
-    # the in-block causal attention on the matrix cores (plus the rotation
-    # of the block and an empty traversal)
-    ts0, sel0 = treeset(w.replace(L=0), w.L, K, V, T=w.T)
+    # the dense part alone: the same block in a tree set without prefix
+    # capacity (the first block of a sequence) runs only the in-block causal
+    # attention on the matrix cores, plus the rotation of the block's keys
+    # and the transpose of its values
+    ts0, sel0 = treeset(w.replace(L=0), 0, None, None, T=w.T)
     ts0.tree_build([0] * w.B)
     ws0 = torch.empty(ts0.prefill_workspace_bytes(sel0, w.T), dtype=torch.uint8, device=DEV)
     ms_dense = timed(lambda: ts0.sparse_prefill(sel0, qb, kb, vb, out, ws0, lse), args.prefill_reps)

@@ -603,7 +603,18 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     pa.v = v_blk;
     pa.T = T;
     hipError_t e = hipSuccess;
-    if (w.ntop > 0) {
+    // A tree set without prefix capacity (the first block of a sequence) has
+    // nothing before the block: no traversal, no partial states, and every
+    // selection slot is empty.
+    const bool no_prefix = tree->cfg.Lcap == 0;
+    if (no_prefix) {
+        if (sel_out) {
+            e = launch_fill_u32(sel_out, 0xffffffffu, units * tree->cfg.levels * (int64_t)sel_stride,
+                                hs);
+            if (e != hipSuccess) return launched(e, "sparse_prefill(selections)");
+        }
+    }
+    if (!no_prefix && w.ntop > 0) {
         // the top level of every query of the block, scored on the matrix cores
         pa.top_s = (float *)(wb + w.top_s);
         pa.top_z = (float *)(wb + w.top_z);
@@ -614,7 +625,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
         ta.top_z = pa.top_z;
         ta.ntop_stride = pa.ntop_stride;
     }
-    if (w.nodes) {
+    if (!no_prefix && w.nodes) {
         if ((int64_t)units * w.keff >= (int64_t(1) << 32) || (int64_t)tree->cfg.B * T * tree->cfg.Hq >= (int64_t(1) << 32))
             return fail(HTI_ERR_UNSUPPORTED, "too many (query, group, rank) pairs for the node-inverted token level");
         ta.kept1 = (int *)(wb + w.kept1);
@@ -623,9 +634,11 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
         e = launch_zero(ta.node_cnt, (size_t)w.cnt_words * 4, hs);
         if (e != hipSuccess) return launched(e, "sparse_prefill(zero counts)");
     }
-    e = launch_prefill_walk(ta, bounds(&tree->cfg, sel, T).max_summary, units, hs);
-    if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
-    if (w.nodes) {
+    if (!no_prefix) {
+        e = launch_prefill_walk(ta, bounds(&tree->cfg, sel, T).max_summary, units, hs);
+        if (e != hipSuccess) return launched(e, "sparse_prefill(traverse)");
+    }
+    if (!no_prefix && w.nodes) {
         NodeArgs na{};
         na.t = ta.t;
         na.q = q_blk;
@@ -651,8 +664,8 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     }
 
     pa.t = tree_args(tree);
-    pa.part_acc = ta.part_acc;
-    pa.part_ml = ta.part_ml;
+    pa.part_acc = no_prefix ? nullptr : ta.part_acc;
+    pa.part_ml = no_prefix ? nullptr : ta.part_ml;
     pa.out = out;
     pa.lse = lse;
     pa.kr = wb + w.kr;

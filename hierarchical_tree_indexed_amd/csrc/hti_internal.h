@@ -121,6 +121,7 @@ constexpr int kTopCols = 64;
 // Key tile of the in-block product; the transposed V rows are padded to it.
 constexpr int kInblockKeys = 64;
 hipError_t launch_top_scores(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_fill_u32(void *p, uint32_t v, int64_t n, hipStream_t s);
 
 // Node-inverted token level of a prefill block (the traversal's kept level-1
 // lists grouped by node; each node's token rows read once for all its queries).

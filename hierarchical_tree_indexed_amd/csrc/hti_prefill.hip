@@ -10,6 +10,8 @@
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation) and seeded with the partial
 // softmax state (max, denominator, unnormalised output) left by the traversal
 // of the prefix tree, so the merge is a single online softmax.
+#include <algorithm>
+
 #include "hti_device.h"
 #include "hti_internal.h"
 
@@ -61,6 +63,20 @@ __global__ __launch_bounds__(256) void k_rotate_block(PrefillArgs a)
     }
     *reinterpret_cast<uint4 *>(dst + j) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     *reinterpret_cast<uint4 *>(dst + j + D / 2) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+}
+
+// n 32-bit words at p set to v (grid-stride).
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t *p, uint32_t v, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_u32(void *p, uint32_t v, int64_t n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    const int blocks = (int)std::min<int64_t>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, s, (uint32_t *)p, v, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_rotate_block(const PrefillArgs &a, hipStream_t s)
@@ -240,7 +256,9 @@ __global__ __launch_bounds__(NW * 64, QT >= 4 ? 1 : (8 / NW > 0 ? 8 / NW : 1)) v
         lacc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (myq < T) {
+        // (no partial states: a tree set without prefix capacity, nothing
+        // before the block)
+        if (myq < T && a.part_ml != nullptr) {
             const int64_t row = ((int64_t)bi * T + myq) * t.Hq + h;
             const float M = a.part_ml[row * 2 + 0];
             const float L = a.part_ml[row * 2 + 1];

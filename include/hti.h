@@ -340,6 +340,9 @@ size_t hti_prefill_workspace_bytes(const hti_tree_cfg *cfg, const hti_select *se
  * at position (number of prefix candidates) + t.  Attention weights are
  * rounded to bf16 before they multiply values (the denominators sum the
  * rounded weights); scores and the selection are fp32.
+ * A tree set with cfg.Lcap == 0 (the first block of new sequences) holds no
+ * prefix: the call then runs the causal attention inside the block alone,
+ * with no traversal, and fills sel_out with -1.
  * Errors: as decode; HTI_ERR_UNSUPPORTED also for dtype other than bf16 and
  * when one (sequence, KV head) slice of the cache or of a level's keys
  * reaches 4 GiB.

@@ -668,6 +668,40 @@ def test_prefill_inblock_tiles(Hq, Hkv, d, P0, T):
     _check_prefill(w, P0, T)
 
 
+@pytest.mark.parametrize("token_nodes", [False, True])
+def test_prefill_without_prefix_capacity(token_nodes):
+    """A tree set with Lcap = 0 (the first block of new sequences) holds no
+    prefix, so no traversal runs: the outputs must equal, bit for bit, those
+    of the same block over an empty prefix in a tree set with capacity (the
+    same in-block kernel, seeded with nothing), and the oracle's; every
+    selection slot is -1."""
+    w = PF.replace(levels=2, L=0, T=150)
+    T = w.T
+    qb, kb, vb = W.gen_block(w)
+    K, V = W.gen_kv(w, Lcap=1)
+    refs = W.gen_refs(w)
+    res = []
+    for Lcap in (0, 3000):
+        ts = make_treeset(w, Lcap, refs=refs.to(DEV), T=T)
+        ts.tree_build([0] * w.B)
+        res.append(_prefill(ts, w, T, qb, kb, vb, token_nodes=token_nodes))
+        del ts
+    (o0, l0, s0), (o1, l1, s1) = res
+    assert (s0 == -1).all()
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32))
+    assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
+    for bi in range(w.B):
+        for g in range(w.Hkv):
+            tr = oracle_tree(w, K[bi, g], V[bi, g], refs[g], 0)
+            bk = kb[bi, :, g].float().numpy()
+            bv = vb[bi, :, g].float().numpy()
+            hs = slice(g * w.G, (g + 1) * w.G)
+            for t in (0, 1, 63, 64, T - 1):
+                accept(w, tr, K[bi, g, :0], V[bi, g, :0], qb[bi, t, hs], o0[bi, t, hs], l0[bi, t, hs],
+                       s0[bi, t, g], t=t, blk_k=bk, blk_v=bv)
+    log(f"  prefill without prefix capacity, token_nodes={token_nodes}: T={T} bit-identical")
+
+
 def test_prefill_exact_ties():
     """Exactly equal scores: keys that are zero score 0 at every position, so
     with all but three level-1 nodes zeroed most candidates tie.  The kept

@@ -769,7 +769,7 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "all"], default="all")
+    ap.add_argument("--only", choices=["decode", "prefill", "side", "all"], default="all")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the per-head-routing and leaf-only timings (profiled runs of the main step)")
     ap.add_argument("--floors", action="store_true",
@@ -798,7 +798,7 @@ def main():
     hti.lib()
     dec = bench_decode(args) if args.only in ("decode", "all") else None
     pre = bench_prefill(args) if args.only in ("prefill", "all") else None
-    side = bench_side_workloads(args) if args.only == "all" and not args.no_variants else None
+    side = bench_side_workloads(args) if args.only in ("all", "side") and not args.no_variants else None
     floors = None
     if not args.no_floors and args.only == "all":
         floors = measure_floors()

@@ -1441,6 +1441,14 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
         if (w >= want) break;
     }
     if (w > kMaxW) w = kMaxW;
+    // (few units: no more workgroups than the wanted width)
+    if (w > want) w = want;
+    // every workgroup ranks all W * keff exchanged entries; up to 128 of them
+    // are ranked in registers, more take the slower path through LDS: fewer
+    // workgroups per unit where that still covers the level's slices
+    const int keff = a.mode == HTI_TOPK ? a.k : a.cap;
+    const int64_t fast = 128 / (keff > 0 ? keff : 1);
+    if (fast >= need && w > fast) w = fast;
     *W = (w >= need && w >= 1 && need <= kMaxW) ? (int)w : 0;
     return hipSuccess;
 }

@@ -451,15 +451,27 @@ def bench_prefill(args):
     return res
 
 
+DECODE_SOURCES = ("hierarchical_tree_indexed_amd/csrc/hti_decode.hip", "hierarchical_tree_indexed_amd/csrc/hti_pool.h",
+                  "hierarchical_tree_indexed_amd/csrc/hti_device.h", "hierarchical_tree_indexed_amd/csrc/hti_internal.h",
+                  "hierarchical_tree_indexed_amd/csrc/hti_trav_common.h", "include/hti.h")
+
+
+def decode_source_sha():
+    """sha1 over the decode kernel's source file and the headers it includes."""
+    import hashlib
+    h = hashlib.sha1()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per decode launch from the committed counter summary, if it
     was taken on the decode kernel source as it is now (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    src = os.path.join(ROOT, "hierarchical_tree_indexed_amd", "csrc", "hti_decode.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+        sha = decode_source_sha()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha1") != sha:

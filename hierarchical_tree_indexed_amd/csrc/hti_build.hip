@@ -52,21 +52,30 @@ hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s)
 // ext == 0: every full node over the first len[s] tokens.  ext > 0: only the
 // nodes that tokens len[s] .. len[s] + ext - 1 (clamped to the cache)
 // complete, len[s] still being the old length.
-template <typename T, int D, int CPL>
+template <typename T, int D, int CPL, int LV>
 __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_t ext)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t bh = blockIdx.y;
-    const int bi = (int)(bh / t.Hkv), h = (int)(bh % t.Hkv);
+    const int bhy = (int)blockIdx.y;                   // 32-bit: the divisions stay short
+    const int64_t bh = bhy;
+    const int bi = bhy / t.Hkv, h = bhy % t.Hkv;
     const int64_t L = t.len[bi];
-    int64_t lo = ext > 0 ? L : 0, hi = ext > 0 ? min(L + ext, t.ncap[0]) : L;
-    for (int l = 0; l < lvl; ++l) {
-        lo /= t.b;
-        hi /= t.b;
-    }
+    // node range: floor(floor(x / b) / b) = floor(x / b^2), so one division
+    // by the span b^lvl for each end; both ends are below the cache capacity
+    // (< 2^31), so a span clamped to 2^31 divides them the same, in 32 bits
+    uint32_t span = 1;
+    for (int l = 0; l < lvl; ++l) span = (uint32_t)min((uint64_t)span * (uint64_t)t.b, (uint64_t)1 << 31);
+    const int64_t lo = ext > 0 ? (int64_t)((uint32_t)L / span) : 0;
+    const int64_t hi = (int64_t)((uint32_t)(ext > 0 ? min(L + ext, t.ncap[0]) : L) / span);
+    // the block's four nodes share head h: its reference rows go to LDS once
+    __shared__ __align__(16) float sref[HTI_MAX_R * D];
+    const int nref = t.R * D;
+    for (int i = 4 * (int)threadIdx.x; i < nref; i += 4 * 256)
+        *reinterpret_cast<float4 *>(sref + i) = *reinterpret_cast<const float4 *>(t.refs + (int64_t)h * nref + i);
+    __syncthreads();
     const int64_t node = lo + (int64_t)blockIdx.x * 4 + wave;
     if (node >= hi) return;
-    pool_node<T, D, CPL>(t, lvl, bh, h, node, lane);
+    pool_node_refs<T, D, CPL, LV>(t, lvl, bh, node, lane, sref);
 }
 
 // Rows of a block of T tokens per sequence ([B, T, Hkv, D], the prefill
@@ -141,18 +150,27 @@ __global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const 
     if (threadIdx.x == 0) t.len[bi] = L + 1;
 }
 
+template <typename T, int D, int LV>
+static void build_level_lv(const TreeArgs &t, int lvl, dim3 grid, int64_t ext, hipStream_t s)
+{
+    if (t.b <= 8)
+        hipLaunchKernelGGL((k_build_level<T, D, 2, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+    else if (t.b <= 16)
+        hipLaunchKernelGGL((k_build_level<T, D, 4, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+    else if (t.b <= 32)
+        hipLaunchKernelGGL((k_build_level<T, D, 8, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+    else
+        hipLaunchKernelGGL((k_build_level<T, D, 16, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+}
+
 template <typename T, int D>
 static hipError_t build_level_d(const TreeArgs &t, int lvl, int64_t max_nodes, int64_t ext, hipStream_t s)
 {
     dim3 grid((unsigned)((max_nodes + 3) / 4), (unsigned)(t.B * t.Hkv));
-    if (t.b <= 8)
-        hipLaunchKernelGGL((k_build_level<T, D, 2>), grid, dim3(256), 0, s, t, lvl, ext);
-    else if (t.b <= 16)
-        hipLaunchKernelGGL((k_build_level<T, D, 4>), grid, dim3(256), 0, s, t, lvl, ext);
-    else if (t.b <= 32)
-        hipLaunchKernelGGL((k_build_level<T, D, 8>), grid, dim3(256), 0, s, t, lvl, ext);
+    if (lvl == 1)
+        build_level_lv<T, D, 1>(t, lvl, grid, ext, s);
     else
-        hipLaunchKernelGGL((k_build_level<T, D, 16>), grid, dim3(256), 0, s, t, lvl, ext);
+        build_level_lv<T, D, 2>(t, lvl, grid, ext, s);
     return hipGetLastError();
 }
 

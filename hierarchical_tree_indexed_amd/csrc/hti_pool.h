@@ -12,9 +12,11 @@
 // elements), so a wave streams them with 16-byte loads: lane = (row group
 // rg = lane / 16) x (slice sub = lane % 16); row group rg holds children rg,
 // rg + 4, ..., slice sub holds d/16 contiguous elements of each.  Dot
-// products reduce over the 16 lanes of a row group, the softmax and the
-// weighted sums over the 4 row groups (DPP within a row, lane-swap
-// instructions across rows: no LDS round trips).  With 8-bit router keys
+// products reduce over the 16 lanes of a row group (DPP), the softmax over
+// the 4 row groups (lane swaps), and each weighted sum with a reduce-scatter
+// over the row groups that leaves every lane of the wave a quarter of its
+// slice (EPL/2 + EPL/4 lane swaps instead of 2 EPL), so that all 64 lanes
+// store a quarter of the row: no LDS round trips.  With 8-bit router keys
 // every pooled key row is also written as E4M3 codes with a power-of-two row
 // scale, taken from its stored (cache-dtype) value.
 #pragma once
@@ -24,42 +26,45 @@
 
 namespace hti {
 
-// ----------------------------------------------------------------------------
-// One wave pools node `node` of level `lvl` (children at level lvl-1) for
-// (sequence, KV head) slot bh, head index h.  CPL = children per lane-row
-// (ceil(b / 4)).
-// ----------------------------------------------------------------------------
-template <typename T, int D>
-__device__ __forceinline__ void store_slice(T *p, const float *v);
+// Sums over the four row groups of this lane's EPL partial values, scattered:
+// the lanes of row group rg end with the totals of slice elements
+// rg * EPL/4 + i, i < EPL/4.  A swap of the upper 32 lanes of x with the
+// lower 32 of y, then a sum, leaves rows 0-1 with x summed over rows (0, 2)
+// and (1, 3) and rows 2-3 with y summed likewise; a swap of the odd rows of x
+// with the even rows of y, then a sum, finishes each row's pair.
+template <int EPL>
+__device__ __forceinline__ void rg_reduce_scatter(const float (&x)[EPL], float (&out)[EPL / 4])
+{
+    float h[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[e]), __float_as_uint(x[e + EPL / 2]),
+                                                        false, false);
+        h[e] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL / 4; ++e) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[e]), __float_as_uint(h[e + EPL / 4]),
+                                                        false, false);
+        out[e] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
 
-template <>
-__device__ __forceinline__ void store_slice<bf16_t, 128>(bf16_t *p, const float *v)
+// N contiguous elements of a row (N = 1 or 2), rounded to T.
+template <typename T, int N>
+__device__ __forceinline__ void store_part(T *p, const float (&v)[N])
 {
-    uint4 o;
-    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-    o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
-    *reinterpret_cast<uint4 *>(p) = o;
-}
-template <>
-__device__ __forceinline__ void store_slice<bf16_t, 64>(bf16_t *p, const float *v)
-{
-    uint2 o;
-    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    *reinterpret_cast<uint2 *>(p) = o;
-}
-template <>
-__device__ __forceinline__ void store_slice<float, 128>(float *p, const float *v)
-{
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-template <>
-__device__ __forceinline__ void store_slice<float, 64>(float *p, const float *v)
-{
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    if constexpr (sizeof(T) == 2) {
+        if constexpr (N == 2)
+            *reinterpret_cast<uint32_t *>(p) = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        else
+            *reinterpret_cast<uint16_t *>(p) = f2bf(v[0]);
+    } else {
+        if constexpr (N == 2)
+            *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+        else
+            *reinterpret_cast<float *>(p) = v[0];
+    }
 }
 
 // E4M3 code (OCP 8-bit float: 4 exponent bits, bias 7, 3 mantissa bits) of
@@ -77,41 +82,103 @@ __device__ __forceinline__ uint32_t e4m3_code(float x)
     return (uint32_t)(8 * e + 48 + q) | ((__float_as_uint(x) >> 24) & 0x80u);
 }
 
-// Router copy of one pooled key row, held as EPL elements by each of the 16
-// lanes of a row group (the values as stored: rounded to the cache dtype):
-// the row scale 2^(e-8) for amax = f * 2^e, f in [0.5, 1) (1 when the row is
-// zero), and the codes of the scaled elements.  Lanes of row group 0 store.
-template <int D, int EPL>
-__device__ __forceinline__ void store_router_row(const TreeArgs &t, int lvl, int64_t row, const float *k, int sub,
-                                                 bool store)
+// Router copy of one pooled key row, spread over the wave as N elements per
+// lane at column col (the values as stored: rounded to the cache dtype): the
+// row scale 2^(e-8) for amax = f * 2^e, f in [0.5, 1) (1 when the row is
+// zero), and the codes of the scaled elements.
+template <int D, int N>
+__device__ __forceinline__ void store_router_part(const TreeArgs &t, int lvl, int64_t row, const float (&k)[N],
+                                                  int col, int lane)
 {
     float amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(k[e]));
-    amax = max16(amax);
+    for (int e = 0; e < N; ++e) amax = fmaxf(amax, fabsf(k[e]));
+    amax = xmax32(xmax16(max16(amax)));
     const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 8;
-    uint32_t w[EPL / 4];
+    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < EPL / 4; ++i) {
-        w[i] = 0;
+    for (int e = 0; e < N; ++e) w |= e4m3_code(ldexpf(k[e], 8 - ex)) << (8 * e);
+    uint8_t *q = t.lkq[lvl - 1] + row * D + col;
+    if constexpr (N == 2)
+        *reinterpret_cast<uint16_t *>(q) = (uint16_t)w;
+    else
+        *q = (uint8_t)w;
+    if (lane == 0) t.lks[lvl - 1][row] = ldexpf(1.f, ex - 8);
+}
+
+// This lane's part (NP = EPL/4 elements, see rg_reduce_scatter) of the pooled
+// key sum_c softmax_c(r . k_c * scale) k_c over the node's children c (kx:
+// this lane's slices of the children's keys; a padded slot is invalid and
+// carries no weight).
+template <int D, int CPL>
+__device__ __forceinline__ void pool_key(float scale, const float *r_j, const float (&kx)[CPL][D / 16],
+                                         const bool (&valid)[CPL], int sub, float (&part)[D / 64])
+{
+    constexpr int EPL = D / 16;
+    float r[EPL];
+    load_vec<float, EPL>(r_j + sub * EPL, r);
+    float a[CPL];
+    float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[i] |= e4m3_code(ldexpf(k[4 * i + e], 8 - ex)) << (8 * e);
+    for (int c = 0; c < CPL; ++c) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot += r[e] * kx[c][e];
+        dot = sum16(dot) * scale;
+        a[c] = valid[c] ? dot : -INFINITY;
+        mx = fmaxf(mx, a[c]);
     }
-    if (store) {
-        uint8_t *q = t.lkq[lvl - 1] + row * D + sub * EPL;
-        if constexpr (EPL == 8)
-            *reinterpret_cast<uint2 *>(q) = make_uint2(w[0], w[1]);
-        else
-            *reinterpret_cast<uint32_t *>(q) = w[0];
-        if (sub == 0) t.lks[lvl - 1][row] = ldexpf(1.f, ex - 8);
+    mx = xmax32(xmax16(mx));
+    float den = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        a[c] = valid[c] ? expf(a[c] - mx) : 0.f;
+        den += a[c];
+    }
+    const float inv = 1.f / xsum32(xsum16(den));
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const float w = a[c] * inv;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += w * kx[c][e];
+    }
+    rg_reduce_scatter<EPL>(acc, part);
+}
+
+// Pooled key row `row` of level lvl (and its router copy): each lane stores
+// its part, at column col.
+template <typename T, int D>
+__device__ __forceinline__ void store_key_row(const TreeArgs &t, int lvl, int64_t row, const float (&part)[D / 64],
+                                              int col, int lane)
+{
+    constexpr int NP = D / 64;
+    store_part<T, NP>((T *)t.lk[lvl - 1] + row * D + col, part);
+    if (t.rfp8) {
+        float kr[NP];
+#pragma unroll
+        for (int e = 0; e < NP; ++e) kr[e] = round_to<T>(part[e]);
+        store_router_part<D, NP>(t, lvl, row, kr, col, lane);
     }
 }
 
-template <typename T, int D, int CPL>
-__device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t node, int lane)
+// One wave pools node `node` of level `lvl` (children at level lvl-1) for
+// (sequence, KV head) slot bh; refs_h: the R reference rows of its head
+// ([R, D] fp32), in global memory or staged in LDS by the caller (then the
+// per-reference loop of level 1 issues no global load, and so never waits on
+// the previous reference's stores).  CPL = children per lane-row (ceil(b / 4)).
+// LV: 1 when lvl is 1, 2 when lvl is at least 2, 0 when either (known at run
+// time only).
+template <typename T, int D, int CPL, int LV = 0>
+__device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64_t bh, int64_t node, int lane,
+                                               const float *refs_h)
 {
     constexpr int EPL = D / 16;                  // elements per lane of a child row
+    constexpr int NP = D / 64;                   // elements per lane of a pooled row
     const int sub = lane & 15, rg = lane >> 4;
+    const int col = sub * EPL + rg * NP;         // this lane's column of a pooled row
     const int b = t.b, R = t.R;
     const int64_t c0 = node * b;                 // first child (level lvl-1 index)
     const int64_t nchild_cap = t.ncap[lvl - 1];
@@ -131,83 +198,57 @@ __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t
     float vx[CPL][EPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
-
+    // keys of reference 0 (level 1: the token keys, shared by every reference)
+    // (index clamped: an out-of-range lk[-1], even unselected, makes the
+    // compiler copy the whole argument block to scratch)
+    const T *kbase = lvl == 1 ? (const T *)t.kc : (const T *)t.lk[lvl >= 2 ? lvl - 2 : 0];
+    const int kstride = (lvl == 1) ? 1 : R;      // key rows per child
     float kx[CPL][EPL];
-    for (int j = 0; j < R; ++j) {
-        if (lvl >= 2 || j == 0) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const T *kp = (lvl == 1) ? (const T *)t.kc + crow[c] * D
-                                         : (const T *)t.lk[lvl - 2] + (crow[c] * R + j) * D;
-                load_vec<T, EPL>(kp + sub * EPL, kx[c]);
+    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + crow[c] * kstride * D + sub * EPL, kx[c]);
+
+    // mean-pooled value first: it frees the value registers before the keys
+    {
+        float vs[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vs[e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            if (valid[c]) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) vs[e] += vx[c][e];
             }
-        }
-        float r[EPL];
-        load_vec<float, EPL>(t.refs + ((int64_t)h * R + j) * D + sub * EPL, r);
-
-        // logits of the children against reference j
-        float a[CPL];
-        float mx = -INFINITY;
+        float part[NP];
+        rg_reduce_scatter<EPL>(vs, part);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            float dot = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) dot += r[e] * kx[c][e];
-            dot = sum16(dot) * t.scale;
-            a[c] = valid[c] ? dot : -INFINITY;
-            mx = fmaxf(mx, a[c]);
-        }
-        mx = xmax32(xmax16(mx));
-        float den = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            a[c] = valid[c] ? expf(a[c] - mx) : 0.f;
-            den += a[c];
-        }
-        den = xsum32(xsum16(den));
-
-        // pooled key = sum_c softmax_c * k_c
-        float acc[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float w = a[c] / den;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] += w * kx[c][e];
-        }
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = xsum32(xsum16(acc[e]));
-        if (rg == 0) {
-            T *out = (T *)t.lk[lvl - 1] + (((bh * t.ncap[lvl] + node) * R + j) * D) + sub * EPL;
-            store_slice<T, D>(out, acc);
-        }
-        if (t.rfp8) {
-            float kr[EPL];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) kr[e] = round_to<T>(acc[e]);
-            store_router_row<D, EPL>(t, lvl, (bh * t.ncap[lvl] + node) * R + j, kr, sub, rg == 0);
-        }
+        for (int e = 0; e < NP; ++e) part[e] /= (float)b;
+        store_part<T, NP>((T *)t.lv[lvl - 1] + (bh * t.ncap[lvl] + node) * D + col, part);
     }
 
-    // mean-pooled value
-    float vs[EPL];
+    // pooled keys, one per reference.  Key j - 1 is stored after the child
+    // keys of reference j are requested (levels >= 2; level 1 shares one set
+    // of keys, loaded above), so waiting for those never waits for that store.
+    const bool upper = LV == 2 || (LV == 0 && lvl >= 2);
+    const int64_t row0 = (bh * t.ncap[lvl] + node) * R;
+    float part[NP];
+    for (int j = 0; j < R; ++j) {
+        if (j > 0) {
+            if (upper) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) vs[e] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-        if (valid[c]) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) vs[e] += vx[c][e];
+                for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + (crow[c] * R + j) * D + sub * EPL, kx[c]);
+            }
+            store_key_row<T, D>(t, lvl, row0 + j - 1, part, col, lane);
         }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        vs[e] = xsum32(xsum16(vs[e])) / (float)b;
+        pool_key<D, CPL>(t.scale, refs_h + j * D, kx, valid, sub, part);
     }
-    if (rg == 0) {
-        T *out = (T *)t.lv[lvl - 1] + (bh * t.ncap[lvl] + node) * D + sub * EPL;
-        store_slice<T, D>(out, vs);
-    }
+    store_key_row<T, D>(t, lvl, row0 + R - 1, part, col, lane);
+}
+
+// The same, reading the reference rows of head h from global memory.
+template <typename T, int D, int CPL>
+__device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t node, int lane)
+{
+    pool_node_refs<T, D, CPL>(t, lvl, bh, node, lane, t.refs + (int64_t)h * t.R * D);
 }
 
 } // namespace hti

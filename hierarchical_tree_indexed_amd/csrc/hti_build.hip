@@ -49,10 +49,11 @@ hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s)
 }
 
 // Level `lvl` of every (sequence, head): 4 nodes per 256-thread block.
-// ext == 0: every full node over the first len[s] tokens.  ext > 0: only the
-// nodes that tokens len[s] .. len[s] + ext - 1 (clamped to the cache)
+// EXT false: every full node over the first len[s] tokens (node = the block's
+// offset, so the child loads go out before len[s] arrives).  EXT true: only
+// the nodes that tokens len[s] .. len[s] + ext - 1 (clamped to the cache)
 // complete, len[s] still being the old length.
-template <typename T, int D, int CPL, int LV>
+template <typename T, int D, int CPL, int LV, bool EXT>
 __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_t ext)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -65,17 +66,25 @@ __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_
     // (< 2^31), so a span clamped to 2^31 divides them the same, in 32 bits
     uint32_t span = 1;
     for (int l = 0; l < lvl; ++l) span = (uint32_t)min((uint64_t)span * (uint64_t)t.b, (uint64_t)1 << 31);
-    const int64_t lo = ext > 0 ? (int64_t)((uint32_t)L / span) : 0;
-    const int64_t hi = (int64_t)((uint32_t)(ext > 0 ? min(L + ext, t.ncap[0]) : L) / span);
-    // the block's four nodes share head h: its reference rows go to LDS once
-    __shared__ __align__(16) float sref[HTI_MAX_R * D];
-    const int nref = t.R * D;
-    for (int i = 4 * (int)threadIdx.x; i < nref; i += 4 * 256)
-        *reinterpret_cast<float4 *>(sref + i) = *reinterpret_cast<const float4 *>(t.refs + (int64_t)h * nref + i);
-    __syncthreads();
+    const int64_t lo = EXT ? (int64_t)((uint32_t)L / span) : 0;
+    const int64_t hi = (int64_t)((uint32_t)(EXT ? min(L + ext, t.ncap[0]) : L) / span);
     const int64_t node = lo + (int64_t)blockIdx.x * 4 + wave;
-    if (node >= hi) return;
-    pool_node_refs<T, D, CPL, LV>(t, lvl, bh, node, lane, sref);
+
+    // The block's four nodes share head h: its reference rows (at most
+    // HTI_MAX_R * D floats, one float4 per thread) go to LDS once.  Their
+    // load is issued before the child loads and written to LDS after them,
+    // so the barrier does not hold the child rows back.
+    static_assert(HTI_MAX_R * D <= 4 * 256, "one float4 of reference rows per thread");
+    __shared__ __align__(16) float sref[HTI_MAX_R * D];
+    const int i4 = 4 * (int)threadIdx.x;
+    const bool has = i4 < t.R * D;
+    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has) rv = *reinterpret_cast<const float4 *>(t.refs + (int64_t)h * t.R * D + i4);
+    pool_node_refs<T, D, CPL, LV>(t, lvl, bh, node, lane, node < hi, [&]() {
+        if (has) *reinterpret_cast<float4 *>(sref + i4) = rv;
+        __syncthreads();
+        return (const float *)sref;
+    });
 }
 
 // Rows of a block of T tokens per sequence ([B, T, Hkv, D], the prefill
@@ -150,17 +159,17 @@ __global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const 
     if (threadIdx.x == 0) t.len[bi] = L + 1;
 }
 
-template <typename T, int D, int LV>
+template <typename T, int D, int LV, bool EXT>
 static void build_level_lv(const TreeArgs &t, int lvl, dim3 grid, int64_t ext, hipStream_t s)
 {
     if (t.b <= 8)
-        hipLaunchKernelGGL((k_build_level<T, D, 2, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+        hipLaunchKernelGGL((k_build_level<T, D, 2, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
     else if (t.b <= 16)
-        hipLaunchKernelGGL((k_build_level<T, D, 4, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+        hipLaunchKernelGGL((k_build_level<T, D, 4, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
     else if (t.b <= 32)
-        hipLaunchKernelGGL((k_build_level<T, D, 8, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+        hipLaunchKernelGGL((k_build_level<T, D, 8, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
     else
-        hipLaunchKernelGGL((k_build_level<T, D, 16, LV>), grid, dim3(256), 0, s, t, lvl, ext);
+        hipLaunchKernelGGL((k_build_level<T, D, 16, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
 }
 
 template <typename T, int D>
@@ -168,9 +177,9 @@ static hipError_t build_level_d(const TreeArgs &t, int lvl, int64_t max_nodes, i
 {
     dim3 grid((unsigned)((max_nodes + 3) / 4), (unsigned)(t.B * t.Hkv));
     if (lvl == 1)
-        build_level_lv<T, D, 1>(t, lvl, grid, ext, s);
+        ext > 0 ? build_level_lv<T, D, 1, true>(t, lvl, grid, ext, s) : build_level_lv<T, D, 1, false>(t, lvl, grid, ext, s);
     else
-        build_level_lv<T, D, 2>(t, lvl, grid, ext, s);
+        ext > 0 ? build_level_lv<T, D, 2, true>(t, lvl, grid, ext, s) : build_level_lv<T, D, 2, false>(t, lvl, grid, ext, s);
     return hipGetLastError();
 }
 

@@ -117,6 +117,10 @@ __device__ __forceinline__ void pool_key(float scale, const float *r_j, const fl
     constexpr int EPL = D / 16;
     float r[EPL];
     load_vec<float, EPL>(r_j + sub * EPL, r);
+    // logits in base 2 (scale * log2 e folded into one multiply), so that
+    // each weight is one exp2; the weights' sum is at least 1, so its
+    // hardware reciprocal (1 ulp) needs no range care
+    const float zs = scale * 1.44269504088896340736f;
     float a[CPL];
     float mx = -INFINITY;
 #pragma unroll
@@ -124,7 +128,7 @@ __device__ __forceinline__ void pool_key(float scale, const float *r_j, const fl
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot += r[e] * kx[c][e];
-        dot = sum16(dot) * scale;
+        dot = sum16(dot) * zs;
         a[c] = valid[c] ? dot : -INFINITY;
         mx = fmaxf(mx, a[c]);
     }
@@ -132,10 +136,10 @@ __device__ __forceinline__ void pool_key(float scale, const float *r_j, const fl
     float den = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        a[c] = valid[c] ? expf(a[c] - mx) : 0.f;
+        a[c] = valid[c] ? __builtin_amdgcn_exp2f(a[c] - mx) : 0.f;
         den += a[c];
     }
-    const float inv = 1.f / xsum32(xsum16(den));
+    const float inv = __builtin_amdgcn_rcpf(xsum32(xsum16(den)));
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -165,22 +169,28 @@ __device__ __forceinline__ void store_key_row(const TreeArgs &t, int lvl, int64_
 }
 
 // One wave pools node `node` of level `lvl` (children at level lvl-1) for
-// (sequence, KV head) slot bh; refs_h: the R reference rows of its head
-// ([R, D] fp32), in global memory or staged in LDS by the caller (then the
-// per-reference loop of level 1 issues no global load, and so never waits on
-// the previous reference's stores).  CPL = children per lane-row (ceil(b / 4)).
+// (sequence, KV head) slot bh.  CPL = children per lane-row (ceil(b / 4)).
 // LV: 1 when lvl is 1, 2 when lvl is at least 2, 0 when either (known at run
-// time only).
-template <typename T, int D, int CPL, int LV = 0>
+// time only).  refs() is called by every wave once its child loads are in
+// flight, active or not (so it may hold a block barrier), and returns the R
+// reference rows of the head ([R, D] fp32): from global memory, or staged in
+// LDS (then the per-reference loop of level 1 issues no global load, and so
+// never waits on the previous reference's stores).  An inactive wave stores
+// nothing and returns after refs().
+template <typename T, int D, int CPL, int LV, typename Refs>
 __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64_t bh, int64_t node, int lane,
-                                               const float *refs_h)
+                                               bool active, Refs refs)
 {
     constexpr int EPL = D / 16;                  // elements per lane of a child row
     constexpr int NP = D / 64;                   // elements per lane of a pooled row
     const int sub = lane & 15, rg = lane >> 4;
     const int col = sub * EPL + rg * NP;         // this lane's column of a pooled row
     const int b = t.b, R = t.R;
-    const int64_t c0 = node * b;                 // first child (level lvl-1 index)
+    // An inactive wave reads the children of a node clamped into the level
+    // (every launch has at least one node there) and discards them: the
+    // loads are unconditional, so the compiler keeps the rows packed until
+    // their use, and they need not wait for what decides `active`.
+    const int64_t c0 = min(node, t.ncap[lvl] - 1) * b;   // first child (level lvl-1 index)
     const int64_t nchild_cap = t.ncap[lvl - 1];
 
     // Children rg, rg + 4, ...: a slot past the last child reads child b-1
@@ -195,17 +205,18 @@ __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64
         crow[c] = bh * nchild_cap + c0 + min(child, b - 1);
     }
     const T *vbase = (lvl == 1) ? (const T *)t.vc : (const T *)t.lv[lvl - 2];
-    float vx[CPL][EPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
     // keys of reference 0 (level 1: the token keys, shared by every reference)
     // (index clamped: an out-of-range lk[-1], even unselected, makes the
     // compiler copy the whole argument block to scratch)
     const T *kbase = lvl == 1 ? (const T *)t.kc : (const T *)t.lk[lvl >= 2 ? lvl - 2 : 0];
     const int kstride = (lvl == 1) ? 1 : R;      // key rows per child
-    float kx[CPL][EPL];
+    float vx[CPL][EPL], kx[CPL][EPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + crow[c] * kstride * D + sub * EPL, kx[c]);
+    const float *refs_h = refs();
+    if (!active) return;
 
     // mean-pooled value first: it frees the value registers before the keys
     {
@@ -248,7 +259,8 @@ __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64
 template <typename T, int D, int CPL>
 __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t node, int lane)
 {
-    pool_node_refs<T, D, CPL>(t, lvl, bh, node, lane, t.refs + (int64_t)h * t.R * D);
+    const float *refs_h = t.refs + (int64_t)h * t.R * D;
+    pool_node_refs<T, D, CPL, 0>(t, lvl, bh, node, lane, true, [=]() { return refs_h; });
 }
 
 } // namespace hti

@@ -48,11 +48,12 @@ hipError_t launch_rope_init(const TreeArgs &t, double base, hipStream_t s)
     return hipGetLastError();
 }
 
-// Level `lvl` of every (sequence, head): 4 nodes per 256-thread block.
-// EXT false: every full node over the first len[s] tokens (node = the block's
-// offset, so the child loads go out before len[s] arrives).  EXT true: only
-// the nodes that tokens len[s] .. len[s] + ext - 1 (clamped to the cache)
-// complete, len[s] still being the old length.
+// Level `lvl` of every (sequence, head): 4 nodes per 256-thread block at
+// level 1 (a node's references share its token keys), 4 (node, reference)
+// items above (LV = 2).  EXT false: every full node over the first len[s]
+// tokens (node = the block's offset, so the child loads go out before len[s]
+// arrives).  EXT true: only the nodes that tokens len[s] .. len[s] + ext - 1
+// (clamped to the cache) complete, len[s] still being the old length.
 template <typename T, int D, int CPL, int LV, bool EXT>
 __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_t ext)
 {
@@ -68,6 +69,13 @@ __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_
     for (int l = 0; l < lvl; ++l) span = (uint32_t)min((uint64_t)span * (uint64_t)t.b, (uint64_t)1 << 31);
     const int64_t lo = EXT ? (int64_t)((uint32_t)L / span) : 0;
     const int64_t hi = (int64_t)((uint32_t)(EXT ? min(L + ext, t.ncap[0]) : L) / span);
+    if constexpr (LV == 2) {
+        // levels >= 2: one wave per (node, reference)
+        const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+        const int64_t node = lo + item / t.R;
+        pool_node_one_ref<T, D, CPL>(t, lvl, bh, h, node, (int)(item % t.R), lane, node < hi);
+        return;
+    }
     const int64_t node = lo + (int64_t)blockIdx.x * 4 + wave;
 
     // The block's four nodes share head h: its reference rows (at most
@@ -175,7 +183,9 @@ static void build_level_lv(const TreeArgs &t, int lvl, dim3 grid, int64_t ext, h
 template <typename T, int D>
 static hipError_t build_level_d(const TreeArgs &t, int lvl, int64_t max_nodes, int64_t ext, hipStream_t s)
 {
-    dim3 grid((unsigned)((max_nodes + 3) / 4), (unsigned)(t.B * t.Hkv));
+    // four waves per block: nodes at level 1, (node, reference) items above
+    const int64_t items = lvl == 1 ? max_nodes : max_nodes * t.R;
+    dim3 grid((unsigned)((items + 3) / 4), (unsigned)(t.B * t.Hkv));
     if (lvl == 1)
         ext > 0 ? build_level_lv<T, D, 1, true>(t, lvl, grid, ext, s) : build_level_lv<T, D, 1, false>(t, lvl, grid, ext, s);
     else

@@ -255,6 +255,61 @@ __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64
     store_key_row<T, D>(t, lvl, row0 + R - 1, part, col, lane);
 }
 
+// One wave pools reference j of node `node` of level lvl >= 2, whose
+// children hold R keys each: key j of the node is made from the children's
+// keys j alone, so the R references of a node are independent work (the
+// wave of reference 0 also pools the mean value).  One round trip per wave:
+// the children's keys j, (j = 0) their values and the reference row go out
+// together.  An inactive wave (node past the level's last full node) stores
+// nothing; its loads are clamped into the level.
+template <typename T, int D, int CPL>
+__device__ __forceinline__ void pool_node_one_ref(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t node, int j,
+                                                  int lane, bool active)
+{
+    constexpr int EPL = D / 16;
+    constexpr int NP = D / 64;
+    const int sub = lane & 15, rg = lane >> 4;
+    const int col = sub * EPL + rg * NP;
+    const int b = t.b, R = t.R;
+    const int64_t c0 = min(node, t.ncap[lvl] - 1) * b;
+    const int64_t nchild_cap = t.ncap[lvl - 1];
+    bool valid[CPL];
+    int64_t crow[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int child = rg + 4 * c;
+        valid[c] = child < b;
+        crow[c] = bh * nchild_cap + c0 + min(child, b - 1);
+    }
+    const T *kbase = (const T *)t.lk[lvl >= 2 ? lvl - 2 : 0];
+    float kx[CPL][EPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + (crow[c] * R + j) * D + sub * EPL, kx[c]);
+    if (j == 0) {
+        const T *vbase = (const T *)t.lv[lvl >= 2 ? lvl - 2 : 0];
+        float vx[CPL][EPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
+        float vs[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vs[e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            if (valid[c]) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) vs[e] += vx[c][e];
+            }
+        float part[NP];
+        rg_reduce_scatter<EPL>(vs, part);
+#pragma unroll
+        for (int e = 0; e < NP; ++e) part[e] /= (float)b;
+        if (active) store_part<T, NP>((T *)t.lv[lvl - 1] + (bh * t.ncap[lvl] + node) * D + col, part);
+    }
+    float part[NP];
+    pool_key<D, CPL>(t.scale, t.refs + ((int64_t)h * R + j) * D, kx, valid, sub, part);
+    if (active) store_key_row<T, D>(t, lvl, (bh * t.ncap[lvl] + node) * R + j, part, col, lane);
+}
+
 // The same, reading the reference rows of head h from global memory.
 template <typename T, int D, int CPL>
 __device__ void pool_node(const TreeArgs &t, int lvl, int64_t bh, int h, int64_t node, int lane)

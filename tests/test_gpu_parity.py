@@ -69,6 +69,10 @@ BUILD_CASES = [
     W.ZHA2M.replace(name="bf16_r4_b16", L=70000 + 5, levels=4),
     W.TINY.replace(name="f32_d128_b8", d=128, b=8, levels=4, L=9000 + 3, Hq=4, Hkv=2, R=2),
     W.DEC128K.replace(name="bf16_d64_b3", d=64, b=3, levels=6, L=3000, Hq=4, Hkv=4),
+    # 16 children per lane row (b > 32), two references, a partial last node
+    W.DEC128K.replace(name="bf16_b64_r2", b=64, levels=2, L=64 * 64 * 2 + 77, R=2, Hq=4, Hkv=2, needles=0),
+    # the most references (their rows fill the staged block exactly), fp32, d = 64
+    W.TINY.replace(name="f32_d64_b40_r8", d=64, b=40, levels=2, L=40 * 40 * 2 + 11, R=8, Hq=2, Hkv=2),
 ]
 
 
@@ -569,6 +573,8 @@ def _same_tree(w, A, B_, L1):
 EXTEND_CASES = [
     W.DEC128K.replace(name="ext_bf16_b32", B=2, Hq=8, Hkv=2, L=32 * 32 * 3 + 500, levels=3, needles=0),
     W.TINY.replace(name="ext_f32_d64_b8", B=2, Hq=2, Hkv=2, b=8, levels=4, L=3000),
+    # four references: the levels above the first pool one (node, reference) per wave
+    W.ZHA2M.replace(name="ext_bf16_r4_b16", B=2, L=16 * 16 * 16 + 900, levels=3),
 ]
 
 

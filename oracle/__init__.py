@@ -39,7 +39,7 @@ def compile_oracle(force: bool = True) -> str:
 
 
 class _QArgs(C.Structure):
-    _fields_ = [("d", C.c_int), ("b", C.c_int), ("levels", C.c_int), ("R", C.c_int),
+    _fields_ = [("d", C.c_int), ("b", C.c_int), ("fan", C.c_int), ("levels", C.c_int), ("R", C.c_int),
                 ("G", C.c_int), ("mode", C.c_int), ("k", C.c_int), ("cap", C.c_int),
                 ("p", C.c_float), ("rope_base", C.c_double), ("Ltree", C.c_long),
                 ("qpos", C.c_long), ("t", C.c_long),
@@ -84,7 +84,7 @@ def library(path: str):
 def _open(path: str):
     lib = C.CDLL(path)
     lib.orc_build.restype = C.c_int
-    lib.orc_build.argtypes = [C.c_long, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+    lib.orc_build.argtypes = [C.c_long, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.orc_query.restype = C.c_int
     lib.orc_query.argtypes = [C.POINTER(_QArgs), C.POINTER(_QOut)]
@@ -112,29 +112,34 @@ def _ptr_array(arrs):
 
 
 class Tree:
-    """Levels 1..levels of one (sequence, KV head): keys [n_l, R, d], values [n_l, d]."""
+    """Levels 1..levels of one (sequence, KV head): keys [n_l, R, d], values [n_l, d].
+    b tokens per level-1 node (the chunk size C), fan nodes per node above
+    (the fan F; None: fan = b)."""
 
-    def __init__(self, L, d, b, levels, R, bf16):
-        self.L, self.d, self.b, self.levels, self.R, self.bf16 = L, d, b, levels, R, bf16
+    def __init__(self, L, d, b, levels, R, bf16, fan=None):
+        fan = b if fan is None else fan
+        self.L, self.d, self.b, self.fan, self.levels, self.R, self.bf16 = L, d, b, fan, levels, R, bf16
         self.lk, self.lv = [], []
         n = L
-        for _ in range(levels):
-            n //= b
+        for lvl in range(1, levels + 1):
+            n //= b if lvl == 1 else fan
             self.lk.append(np.zeros((n, R, d), np.float32))
             self.lv.append(np.zeros((n, d), np.float32))
 
 
-def build_tree(K, V, refs, b: int, levels: int, bf16: bool, L: int | None = None) -> Tree:
-    """Tree over the first L tokens of K, V ([*, d]); refs [R, d]."""
+def build_tree(K, V, refs, b: int, levels: int, bf16: bool, L: int | None = None, fan: int | None = None) -> Tree:
+    """Tree over the first L tokens of K, V ([*, d]); refs [R, d]; b tokens
+    per level-1 node, fan nodes per node above (None: fan = b)."""
     K, V, refs = _f32(K), _f32(V), _f32(refs)
     L = K.shape[0] if L is None else L
     d = K.shape[1]
     R = refs.shape[0]
-    assert levels <= MAXLVL and b >= 2
-    tr = Tree(L, d, b, levels, R, bf16)
+    fan = b if fan is None else fan
+    assert levels <= MAXLVL and b >= 2 and fan >= 2
+    tr = Tree(L, d, b, levels, R, bf16, fan)
     lk, lv = _ptr_array(tr.lk), _ptr_array(tr.lv)
     tr._keep = (K, V)
-    _load().orc_build(L, d, b, levels, R, int(bf16), _ptr(K), _ptr(V), _ptr(refs), lk, lv)
+    _load().orc_build(L, d, b, fan, levels, R, int(bf16), _ptr(K), _ptr(V), _ptr(refs), lk, lv)
     return tr
 
 
@@ -169,7 +174,7 @@ def query(tree: Tree, K, V, q, *, mode="topk", k=8, p=1.0, cap=16, rope_base=100
     if kmax is None:
         kmax = k if mode == "topk" else cap
     a = _QArgs()
-    a.d, a.b, a.levels, a.R, a.G = d, tree.b, tree.levels, tree.R, G
+    a.d, a.b, a.fan, a.levels, a.R, a.G = d, tree.b, tree.fan, tree.levels, tree.R, G
     a.mode = 0 if mode == "topk" else 1
     a.k, a.cap, a.p, a.rope_base = k, cap, p, rope_base
     a.Ltree = tree.L

@@ -28,8 +28,13 @@
  *           shared pooler provides both the selection keys and the summary keys.
  *
  * Readings where the pages are silent (each restated where it is used):
- *  - pooler: alpha = softmax_c(r . k_c / sqrt(d)) over a node's b children,
+ *  - pooler: alpha = softmax_c(r . k_c / sqrt(d)) over a node's children,
  *    pooled key = sum_c alpha_c k_c; value = arithmetic mean of the children;
+ *  - tree geometry [ZHA, Figure 4 caption and Table II: chunk size C, fan F,
+ *    levels L, e.g. "C4 F4 L6"]: a level-1 node pools a chunk of b = C
+ *    consecutive tokens, a node above pools fan = F consecutive nodes of the
+ *    level below (every geometry the page lists has C = F, the default);
+ *    n_1 = floor(n_0 / C), n_l = floor(n_{l-1} / F);
  *  - nodes are stored in the cache dtype (bf16 by round-to-nearest-even), and
  *    higher levels pool the stored (rounded) children;
  *  - one selection per (query, KV-head group), scored by the mean over the
@@ -165,15 +170,16 @@ static void rope(const float *x, int d, long pos, double base, float *y)
  *   bf16    : nonzero -> every stored node is rounded to bf16
  * Returns the number of levels built.
  */
-int orc_build(long L, int d, int b, int levels, int R, int bf16,
+int orc_build(long L, int d, int b, int fan, int levels, int R, int bf16,
               const float *K, const float *V, const float *refs,
               float *const *lvl_k, float *const *lvl_v)
 {
     float scale = 1.0f / sqrtf((float)d);
-    float *a = (float *)malloc(sizeof(float) * (size_t)b);
+    float *a = (float *)malloc(sizeof(float) * (size_t)(b > fan ? b : fan));
     long n_prev = L;
     for (int l = 1; l <= levels; ++l) {
-        long n = n_prev / b;                         /* full nodes only [ZHA-T8] */
+        const int fb = (l == 1) ? b : fan;           /* children per node of level l */
+        long n = n_prev / fb;                        /* full nodes only [ZHA-T8] */
         float *Kl = lvl_k[l - 1], *Vl = lvl_v[l - 1];
         for (long i = 0; i < n; ++i) {
             for (int j = 0; j < R; ++j) {
@@ -182,39 +188,39 @@ int orc_build(long L, int d, int b, int levels, int R, int bf16,
                 const float *child0;
                 long cstride;
                 if (l == 1) {
-                    child0 = K + (size_t)(i * b) * d;
+                    child0 = K + (size_t)(i * fb) * d;
                     cstride = d;
                 } else {
-                    child0 = lvl_k[l - 2] + ((size_t)(i * b) * R + j) * d;
+                    child0 = lvl_k[l - 2] + ((size_t)(i * fb) * R + j) * d;
                     cstride = (long)R * d;
                 }
                 const float *r = refs + (size_t)j * d;
                 float mx = -INFINITY;
-                for (int c = 0; c < b; ++c) {
+                for (int c = 0; c < fb; ++c) {
                     a[c] = dot_seq(r, child0 + c * cstride, d) * scale;
                     if (a[c] > mx) mx = a[c];
                 }
                 float den = 0.0f;
-                for (int c = 0; c < b; ++c) {
+                for (int c = 0; c < fb; ++c) {
                     a[c] = expf(a[c] - mx);
                     den += a[c];
                 }
                 float *out = Kl + ((size_t)i * R + j) * d;
                 for (int t = 0; t < d; ++t) {
                     float acc = 0.0f;
-                    for (int c = 0; c < b; ++c)
+                    for (int c = 0; c < fb; ++c)
                         acc += (a[c] / den) * child0[c * cstride + t];
                     out[t] = bf16 ? round_bf16(acc) : acc;
                 }
             }
             /* mean-pooled value [RecSA abstract] */
-            const float *vc = (l == 1) ? V + (size_t)(i * b) * d : lvl_v[l - 2] + (size_t)(i * b) * d;
+            const float *vc = (l == 1) ? V + (size_t)(i * fb) * d : lvl_v[l - 2] + (size_t)(i * fb) * d;
             float *vo = Vl + (size_t)i * d;
             for (int t = 0; t < d; ++t) {
                 float acc = 0.0f;
-                for (int c = 0; c < b; ++c)
+                for (int c = 0; c < fb; ++c)
                     acc += vc[(size_t)c * d + t];
-                acc = acc / (float)b;
+                acc = acc / (float)fb;
                 vo[t] = bf16 ? round_bf16(acc) : acc;
             }
         }
@@ -229,7 +235,7 @@ int orc_build(long L, int d, int b, int levels, int R, int bf16,
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
-    int d, b, levels, R, G;
+    int d, b, fan, levels, R, G;   /* b: tokens per level-1 node; fan: nodes per node above */
     int mode;            /* 0 = top-k, 1 = top-p */
     int k, cap;
     float p;
@@ -321,13 +327,13 @@ static void rec_entry(orc_query_out *o, int level, long node, long pos)
  */
 int orc_query(const orc_query_args *A, orc_query_out *O)
 {
-    const int d = A->d, b = A->b, G = A->G, R = A->R, Lv = A->levels;
+    const int d = A->d, G = A->G, R = A->R, Lv = A->levels;
     const float scale = 1.0f / sqrtf((float)d);
     const int prefill = A->t >= 0;
     long n[ORC_MAXLVL + 1];
     n[0] = A->Ltree;
     for (int l = 1; l <= Lv; ++l)
-        n[l] = n[l - 1] / b;                                    /* [ZHA-T8] */
+        n[l] = n[l - 1] / (l == 1 ? A->b : A->fan);             /* [ZHA-T8] */
 
     long cap_c = 1024;
     long *cand = (long *)malloc(sizeof(long) * cap_c);
@@ -456,13 +462,15 @@ int orc_query(const orc_query_args *A, orc_query_out *O)
                 O->sel[row * A->kmax + q] = (int)cand[sel_pos[q]];
 
         /* next candidates: children of the selected nodes in node order, then
-         * the orphans of level l-1 (indices b*n_l .. n_{l-1}-1) */
-        long orph0 = (long)b * n[l], norph = n[l - 1] - orph0;
-        long m2 = nsel * b + norph;
+         * the orphans of level l-1 (indices fb*n_l .. n_{l-1}-1), fb being the
+         * children per node of level l */
+        const int fb = (l == 1) ? A->b : A->fan;
+        long orph0 = (long)fb * n[l], norph = n[l - 1] - orph0;
+        long m2 = nsel * fb + norph;
         long *nc = (long *)malloc(sizeof(long) * (size_t)(m2 > 0 ? m2 : 1));
         long w = 0;
         for (long q = 0; q < nsel; ++q)
-            for (int c = 0; c < b; ++c) nc[w++] = cand[sel_pos[q]] * b + c;
+            for (int c = 0; c < fb; ++c) nc[w++] = cand[sel_pos[q]] * fb + c;
         for (long i = 0; i < norph; ++i) nc[w++] = orph0 + i;
         free(cand);
         cand = nc;

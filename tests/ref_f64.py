@@ -45,32 +45,39 @@ def dense_causal(q: np.ndarray, K: np.ndarray, V: np.ndarray, qpos: int, base=10
     return w @ np.asarray(V[:n], np.float64)
 
 
-def level_counts(L: int, b: int, levels: int) -> list[int]:
+def fan_in(level: int, b: int, fan: int | None) -> int:
+    """Children per node of `level` (>= 1): b tokens at level 1, fan nodes above."""
+    return b if level == 1 or fan is None else fan
+
+
+def level_counts(L: int, b: int, levels: int, fan: int | None = None) -> list[int]:
     n = [L]
-    for _ in range(levels):
-        n.append(n[-1] // b)
+    for lvl in range(1, levels + 1):
+        n.append(n[-1] // fan_in(lvl, b, fan))
     return n
 
 
-def candidates_by_predicate(L: int, b: int, levels: int, sel: list[set]):
+def candidates_by_predicate(L: int, b: int, levels: int, sel: list[set], fan: int | None = None):
     """Candidate sets per level from the node predicate.
 
     sel[l] = set of selected node ids at level l (l = 1..levels; sel[0] unused).
     A level-l node x is a candidate iff l is the top level, or x has no full
-    parent (x >= b * n_{l+1}), or its parent is a candidate and selected.
+    parent (x >= f * n_{l+1}, f the fan-in of level l + 1), or its parent
+    x // f is a candidate and selected.
     Returns {l: sorted list of candidate ids}.
     """
-    n = level_counts(L, b, levels)
+    n = level_counts(L, b, levels, fan)
     memo = {}
 
     def is_cand(l: int, x: int) -> bool:
         key = (l, x)
         if key in memo:
             return memo[key]
-        if l == levels or x >= b * n[l + 1]:
+        f = fan_in(l + 1, b, fan) if l < levels else 0
+        if l == levels or x >= f * n[l + 1]:
             r = True
         else:
-            par = x // b
+            par = x // f
             r = is_cand(l + 1, par) and par in sel[l + 1]
         memo[key] = r
         return r
@@ -90,8 +97,10 @@ def entries_from_candidates(cands: dict, sel: list[set], levels: int):
     return ent
 
 
-def covered_tokens(level: int, node: int, b: int) -> range:
-    span = b ** level
+def covered_tokens(level: int, node: int, b: int, fan: int | None = None) -> range:
+    span = 1
+    for lvl in range(1, level + 1):
+        span *= fan_in(lvl, b, fan)
     return range(node * span, (node + 1) * span)
 
 
@@ -120,12 +129,14 @@ def softmax_over_entries(zs: np.ndarray, vals: np.ndarray):
     return (w @ vals) / den, (M + np.log(den))[:, 0]
 
 
-def pool_tree_f64(K: np.ndarray, V: np.ndarray, refs: np.ndarray, b: int, levels: int, L: int | None = None):
+def pool_tree_f64(K: np.ndarray, V: np.ndarray, refs: np.ndarray, b: int, levels: int, L: int | None = None,
+                  fan: int | None = None):
     """The tree's levels in float64, written as whole-level array operations.
 
     Each reference query r_j pools its own chain of keys: level 1 pools the
     token keys, level l >= 2 pools the level-(l-1) keys of that same
-    reference.  A node's weights are the softmax over its b children of
+    reference.  A node's weights are the softmax over its children (b tokens
+    at level 1, fan nodes above; fan None means b) of
     r_j . k_child / sqrt(d) (taken in the log domain: log-sum-exp with the
     children's maximum), its key the weighted sum of the children's keys and
     its value the plain mean of the children's values.  Only full nodes.
@@ -139,14 +150,15 @@ def pool_tree_f64(K: np.ndarray, V: np.ndarray, refs: np.ndarray, b: int, levels
     keys = np.repeat(K[:L, None, :], R, axis=1)            # [n, R, d]: level 0, one chain per reference
     vals = V[:L]
     out = []
-    for _ in range(levels):
-        n = keys.shape[0] // b
-        ch = keys[: n * b].reshape(n, b, R, d)               # [node, child, ref, d]
+    for lvl in range(1, levels + 1):
+        f = fan_in(lvl, b, fan)
+        n = keys.shape[0] // f
+        ch = keys[: n * f].reshape(n, f, R, d)               # [node, child, ref, d]
         logit = np.einsum("ncrd,rd->ncr", ch, refs) / np.sqrt(d)
         lse = logit.max(axis=1, keepdims=True)
         lse = lse + np.log(np.exp(logit - lse).sum(axis=1, keepdims=True))
         w = np.exp(logit - lse)                              # [node, child, ref]
         keys = np.einsum("ncr,ncrd->nrd", w, ch)
-        vals = vals[: n * b].reshape(n, b, d).mean(axis=1)
+        vals = vals[: n * f].reshape(n, f, d).mean(axis=1)
         out.append((keys, vals))
     return out

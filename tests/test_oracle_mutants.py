@@ -35,8 +35,8 @@ MUTANTS = [
      "const float *r = refs + (size_t)j * d;",
      "const float *r = refs;", "pooler"),
     ("levels above the first pool the first reference's chain",
-     "child0 = lvl_k[l - 2] + ((size_t)(i * b) * R + j) * d;",
-     "child0 = lvl_k[l - 2] + ((size_t)(i * b) * R + 0) * d;", "pooler"),
+     "child0 = lvl_k[l - 2] + ((size_t)(i * fb) * R + j) * d;",
+     "child0 = lvl_k[l - 2] + ((size_t)(i * fb) * R + 0) * d;", "pooler"),
     ("node ties go to the higher index",
      "return (a->pos < b->pos) ? -1 : (a->pos > b->pos);",
      "return (a->pos > b->pos) ? -1 : (a->pos < b->pos);", "ties"),
@@ -49,6 +49,18 @@ MUTANTS = [
     ("summary values dropped from the shared softmax",
      "for (long i = 0; i < m && !A->leaf_only; ++i) {",
      "for (long i = 0; i < m && 0; ++i) {", "query"),
+    # (fan mutants stay inside the arrays the pins allocate: the value mean of
+    # the build, and traversal mutants checked only on trees where the wrong
+    # fan-in reads fewer nodes than exist)
+    ("values above the first level averaged over the chunk size",
+     "acc = acc / (float)fb;",
+     "acc = acc / (float)b;", "fan_build"),
+    ("traversal descends with the chunk size at every level",
+     "const int fb = (l == 1) ? A->b : A->fan;",
+     "const int fb = A->b;", "fan_up"),
+    ("traversal descends with the fan at level 1 too",
+     "const int fb = (l == 1) ? A->b : A->fan;",
+     "const int fb = A->fan;", "fan_down"),
 ]
 
 PINS = {
@@ -65,6 +77,12 @@ PINS = {
         lambda: P.test_dense_equivalence_tiny_workload("topk"),
         lambda: P.test_prefill_matches_f64_entry_softmax(),
     ],
+    "fan_build": [
+        lambda: P.test_pooler_fanout_chains(3000, 8, 3, 4, 2, 32),
+        lambda: P.test_pooler_fanout_chains(5000, 3, 16, 2, 2, 16),
+    ],
+    "fan_up": [lambda: P.check_fanout_cases(lambda b, fan: b < fan)],
+    "fan_down": [lambda: P.check_fanout_cases(lambda b, fan: fan < b)],
 }
 
 

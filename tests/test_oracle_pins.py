@@ -68,7 +68,7 @@ def eval_f64(tree, K, V, q, sel, *, base=10000.0, t=-1, blk_k=None, blk_v=None, 
     """Shared softmax in float64 over the entry set implied by `sel` (only the
     reached tokens when leaf_only)."""
     L, b, lv = tree.L, tree.b, tree.levels
-    cands = candidates_by_predicate(L, b, lv, sel)
+    cands = candidates_by_predicate(L, b, lv, sel, getattr(tree, "fan", b))
     zs, vals = [], []
     for l in range(lv, 0, -1):
         if leaf_only:
@@ -466,56 +466,131 @@ def _sweep_cases():
 _CASES = _sweep_cases()
 
 
+def _check_small_case(L, b, lv, mode, k, p, cap, R, G, T, seed, fan=None):
+    """P4 + P5 + P6 + P7 on one small tree (b tokens per level-1 node, fan
+    nodes per node above; None: fan = b), decode (T = 0) or every row of a
+    T-token prefill block."""
+    d = 8
+    K, V, rng = rand_kv(L + T, d, seed=seed)
+    refs = (rng.standard_normal((R, d)) / np.sqrt(d)).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, lv, bf16=False, L=L, fan=fan)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    kmax = k if mode == "topk" else cap
+    for t in (range(T) if T else [-1]):
+        blk = dict(t=t, blk_k=K[L:], blk_v=V[L:]) if T else {}
+        r = oracle.query(tr, K[:L], V[:L], q, mode=mode, k=k, p=p, cap=cap, kmax=kmax,
+                         entries=True, **blk)
+        sel = sel_sets(r, lv)
+        cands = candidates_by_predicate(L, b, lv, sel, fan)
+        # P7: entry list equals the node-predicate formulation
+        ent = entries_from_candidates(cands, sel, lv)
+        nblk = t + 1 if T else 0
+        ent += [(0, L + j, len(cands[0]) + j) for j in range(nblk)]
+        got = list(zip(*[x.tolist() for x in r["entries"]]))
+        assert got == ent, (L, b, fan, lv, mode, k, p, cap, T, t)
+        # P5: entries partition the visible tokens [0, L + nblk)
+        cover = np.zeros(L + nblk, np.int64)
+        for (l, x, _) in ent:
+            for tkn in covered_tokens(l, x, b, fan):
+                cover[tkn] += 1
+        assert (cover == 1).all()
+        # P4: per-level certificate on float64 scores
+        thr = k if mode == "topk" else 1
+        nkeys = 0
+        for l in range(lv, 0, -1):
+            C = cands[l]
+            if len(C) <= thr:
+                assert sel[l] == set(C)
+                continue
+            nkeys += len(C) * R
+            s_, _ = group_scores_f64(q, tr.lk[l - 1][C], len(C), 10000.0)
+            pos = [i for i, x in enumerate(C) if x in sel[l]]
+            _check_certificate(s_, pos, mode, k, p, cap)
+        # P6: counters
+        nvals = sum(len(cands[l]) - len(sel[l] & set(cands[l])) for l in range(1, lv + 1))
+        n0 = len(cands[0]) + nblk
+        assert tuple(r["counts"]) == (nkeys + n0, nvals + n0)
+        # P7: output equals a float64 softmax over E
+        kw = dict(t=t, blk_k=K[L:].astype(np.float64), blk_v=V[L:].astype(np.float64)) if T else {}
+        out, lse = eval_f64(tr, K, V, q, sel, **kw)
+        assert np.abs(r["out"] - out).max() < 2e-5
+        assert np.abs(r["lse"] - lse).max() < 2e-5
+
+
 @pytest.mark.parametrize("chunk", range(8))
 def test_exhaustive_64_token_trees(chunk):
     """P4 + P5 + P6 + P7 over every 64-token-or-smaller tree geometry, decode
     and prefill (blocks of 1, 3 and 8 tokens after the 64-token prefix)."""
-    d = 8
     for (L, b, lv, (mode, k, p, cap), R, G, T, seed) in _CASES[chunk::8]:
-        K, V, rng = rand_kv(L + T, d, seed=seed)
-        refs = (rng.standard_normal((R, d)) / np.sqrt(d)).astype(np.float32)
-        tr = oracle.build_tree(K, V, refs, b, lv, bf16=False, L=L)
-        q = rng.standard_normal((G, d)).astype(np.float32)
-        kmax = k if mode == "topk" else cap
-        for t in (range(T) if T else [-1]):
-            blk = dict(t=t, blk_k=K[L:], blk_v=V[L:]) if T else {}
-            r = oracle.query(tr, K[:L], V[:L], q, mode=mode, k=k, p=p, cap=cap, kmax=kmax,
-                             entries=True, **blk)
-            sel = sel_sets(r, lv)
-            cands = candidates_by_predicate(L, b, lv, sel)
-            # P7: entry list equals the node-predicate formulation
-            ent = entries_from_candidates(cands, sel, lv)
-            nblk = t + 1 if T else 0
-            ent += [(0, L + j, len(cands[0]) + j) for j in range(nblk)]
-            got = list(zip(*[x.tolist() for x in r["entries"]]))
-            assert got == ent, (L, b, lv, mode, k, p, cap, T, t)
-            # P5: entries partition the visible tokens [0, L + nblk)
-            cover = np.zeros(L + nblk, np.int64)
-            for (l, x, _) in ent:
-                for tkn in covered_tokens(l, x, b):
-                    cover[tkn] += 1
-            assert (cover == 1).all()
-            # P4: per-level certificate on float64 scores
-            thr = k if mode == "topk" else 1
-            nkeys = 0
-            for l in range(lv, 0, -1):
-                C = cands[l]
-                if len(C) <= thr:
-                    assert sel[l] == set(C)
-                    continue
-                nkeys += len(C) * R
-                s, _ = group_scores_f64(q, tr.lk[l - 1][C], len(C), 10000.0)
-                pos = [i for i, x in enumerate(C) if x in sel[l]]
-                _check_certificate(s, pos, mode, k, p, cap)
-            # P6: counters
-            nvals = sum(len(cands[l]) - len(sel[l] & set(cands[l])) for l in range(1, lv + 1))
-            n0 = len(cands[0]) + nblk
-            assert tuple(r["counts"]) == (nkeys + n0, nvals + n0)
-            # P7: output equals a float64 softmax over E
-            kw = dict(t=t, blk_k=K[L:].astype(np.float64), blk_v=V[L:].astype(np.float64)) if T else {}
-            out, lse = eval_f64(tr, K, V, q, sel, **kw)
-            assert np.abs(r["out"] - out).max() < 2e-5
-            assert np.abs(r["lse"] - lse).max() < 2e-5
+        _check_small_case(L, b, lv, mode, k, p, cap, R, G, T, seed)
+
+
+def _fan_cases():
+    """Trees whose fan above level 1 differs from the chunk size of level 1
+    (ZHA Figure 4 and Table II name them apart, C and F): every L <= 64 for
+    each (C, F) pair, at every depth that leaves a node, selection rule, R, G
+    and block length rotated as in the sweep above."""
+    cases = []
+    i = 0
+    for (b, fan) in ((2, 3), (3, 2), (4, 2), (2, 4), (8, 2), (2, 8), (5, 3), (3, 5)):
+        variants = [("topk", k, 1.0, 0) for k in (1, 2, 3)] + \
+                   [("topp", 0, p, cap) for p in (0.5, 0.9) for cap in (1, 3)]
+        for L in range(1, 65):
+            maxlv = 0
+            n = L // b
+            while n >= 1:
+                maxlv += 1
+                n //= fan
+            for lv in range(0, maxlv + 2):
+                sv = variants[i % len(variants)]
+                R = 1 + (i // 3) % 2
+                G = 1 + (i // 5) % 2
+                T = (0, 1, 3)[(i // 7) % 3]
+                cases.append((L, b, fan, lv, sv, R, G, T, 5000 + i))
+                i += 1
+    return cases
+
+
+_FAN_CASES = _fan_cases()
+
+
+def check_fanout_cases(pred):
+    """The fan-out sweep restricted to the (C, F) pairs pred accepts."""
+    for (L, b, fan, lv, (mode, k, p, cap), R, G, T, seed) in _FAN_CASES:
+        if pred(b, fan):
+            _check_small_case(L, b, lv, mode, k, p, cap, R, G, T, seed, fan=fan)
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_exhaustive_fanout_trees(chunk):
+    """The same checks over trees with a fan F above level 1 other than the
+    chunk size C of level 1: the entries still equal the node predicate
+    (parents are x // F above level 1, x // C at it), partition the tokens,
+    satisfy the per-level certificates and give the float64 softmax."""
+    for (L, b, fan, lv, (mode, k, p, cap), R, G, T, seed) in _FAN_CASES[chunk::4]:
+        _check_small_case(L, b, lv, mode, k, p, cap, R, G, T, seed, fan=fan)
+
+
+@pytest.mark.parametrize("L,b,fan,levels,R,d", [(3000, 8, 3, 4, 2, 32), (5000, 3, 16, 2, 2, 16),
+                                                (2 * 32 * 4 * 4 + 33, 32, 4, 3, 4, 64)])
+def test_pooler_fanout_chains(L, b, fan, levels, R, d):
+    """With a fan F above level 1 other than the chunk size C: level 1 pools
+    C tokens, every level above pools F nodes of the level below, per
+    reference chain -- against the float64 whole-level pooler with the same
+    geometry, level by level (a tree that pooled C children at every level
+    would not even have the same node counts)."""
+    K, V, rng = rand_kv(L, d, seed=L + fan)
+    refs = (rng.standard_normal((R, d)) * (1.5 / np.sqrt(d))).astype(np.float32)
+    tr = oracle.build_tree(K, V, refs, b, levels, bf16=False, fan=fan)
+    ref = pool_tree_f64(K, V, refs, b, levels, fan=fan)
+    n = L // b
+    for l in range(levels):
+        rk, rv = ref[l]
+        assert tr.lk[l].shape[0] == rk.shape[0] == n, (l + 1, tr.lk[l].shape, rk.shape, n)
+        scale = max(1.0, float(np.abs(rk).max()))
+        assert np.abs(tr.lk[l] - rk).max() < 1e-5 * scale * (l + 1), (l + 1, float(np.abs(tr.lk[l] - rk).max()))
+        assert np.abs(tr.lv[l] - rv).max() < 1e-5 * (l + 1)
+        n //= fan
 
 
 # --------------------------------------------------------------------------- P9

@@ -55,7 +55,7 @@ def gen_kv_device(w, Lcap):
 
 def treeset(w, Lcap, K, V, T=0):
     sel = hti.make_select(w.mode, k=w.k, p=w.p, cap=w.cap)
-    cfg = hti.make_cfg(w.B, w.Hq, w.Hkv, w.d, w.b, w.levels, w.R, w.dtype, Lcap, w.rope_base, 1)
+    cfg = hti.make_cfg(w.B, w.Hq, w.Hkv, w.d, w.b, w.levels, w.R, w.dtype, Lcap, w.rope_base, 1, fan=w.fan)
     cfg.rope_npos = hti.plan(cfg, sel, T).rope_npos_needed
     ts = hti.TreeSet(cfg, device=DEV, k_cache=K, v_cache=V)
     ts.ref_q.copy_(W.gen_refs(w))
@@ -81,7 +81,8 @@ def decode_unit_bytes(w, L, router_fp8=False):
             vals += m - nsel
         else:
             nsel = m
-        m = nsel * w.b + (n[lvl - 1] - w.b * n[lvl])
+        f = w.b if lvl == 1 else w.F                     # children per node of level lvl
+        m = nsel * f + (n[lvl - 1] - f * n[lvl])
     keys += m
     vals += m
     e = w.d * w.elem_bytes
@@ -294,8 +295,9 @@ def build_bytes(w, L):
 
 
 def bench_side_workloads(args):
-    """The 131,072-token decode (one query, 8 KV groups, 8 planted needles)
-    and the 2,097,152-token top-p workload with four reference keys per node
+    """The 131,072-token decode (one query, 8 KV groups, 8 planted needles),
+    the 1M-token batch-4 decode on a chunk-32 / fan-8 tree, and the
+    2,097,152-token top-p workload with four reference keys per node
     (tree_build of the whole context, then one top-p decode query), each
     against the HBM roofline of its algorithmic bytes."""
     res = {}
@@ -312,6 +314,24 @@ def bench_side_workloads(args):
     res["decode_128k"] = dict(ms=ms, queries_per_s=w.B / (ms / 1e3), bytes=by, gbs=by / (ms / 1e3) / 1e9,
                               frac_hbm=by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
     log(f"[side] decode_128k {res['decode_128k']}")
+    del K, V, ts
+    torch.cuda.empty_cache()
+    # the 1M-token, batch-4 decode on a tree with chunk size 32 at level 1 and
+    # fan 8 above (five levels) instead of C = F = 32 (four levels): the
+    # depth-for-width trade of the pages' tree geometries
+    w = W.DEC1M.replace(name="decode_1m_b4_c32_f8", fan=8, levels=5)
+    K, V = gen_kv_device(w, w.L)
+    q0 = W.gen_queries(w, 0, device=DEV)
+    W.plant_needles(w, K, q0)
+    ts, sel = treeset(w, w.L, K, V)
+    ts.tree_build([w.L] * w.B)
+    out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
+    ms = graph_ms(lambda: ts.sparse_decode(sel, q0, out), reps)
+    by = decode_unit_bytes(w, w.L) * w.B * w.Hkv
+    res["decode_1m_c32_f8"] = dict(ms=ms, queries_per_s=w.B / (ms / 1e3), bytes=by, gbs=by / (ms / 1e3) / 1e9,
+                                   frac_hbm=by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, levels=w.levels, chunk=w.b,
+                                   fan=w.F)
+    log(f"[side] decode_1m_c32_f8 {res['decode_1m_c32_f8']}")
     del K, V, ts
     torch.cuda.empty_cache()
     w = W.ZHA2M
@@ -439,7 +459,7 @@ def bench_prefill(args):
     # block K and V read, cache rows written, then read again by the pooling
     # of the nodes they complete, plus those nodes' keys (x R) and values
     row_bytes = w.B * w.T * w.Hkv * w.d * W.TORCH_DTYPE[w.dtype].itemsize
-    nodes = sum((w.L + w.T) // w.b ** l - w.L // w.b ** l for l in range(1, w.levels + 1))
+    nodes = sum(a - b for a, b in zip(w.level_counts(w.L + w.T)[1:], w.level_counts(w.L)[1:]))
     ext_bytes = 3 * 2 * row_bytes + nodes * w.B * w.Hkv * (w.R + 1) * w.d * W.TORCH_DTYPE[w.dtype].itemsize
     res = dict(ms_per_block=ms, tokens_per_s=w.T * w.B / (ms / 1e3), inblock_gflop=inblock_flop / 1e9,
                dense_ms=ms_dense, dense_tflops=inblock_flop / (ms_dense / 1e3) / 1e12,

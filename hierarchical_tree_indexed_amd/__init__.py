@@ -36,7 +36,7 @@ class TreeCfg(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32),
                 ("b", C.c_int32), ("levels", C.c_int32), ("R", C.c_int32), ("dtype", C.c_int32),
                 ("Lcap", C.c_int64), ("rope_base", C.c_float), ("rope_npos", C.c_int32),
-                ("router_fp8", C.c_int32)]
+                ("router_fp8", C.c_int32), ("fan", C.c_int32)]
 
 
 class Tree(C.Structure):
@@ -130,9 +130,11 @@ def make_select(mode: str = "topk", k: int = 8, p: float = 1.0, cap: int = 16,
 
 
 def make_cfg(B, Hq, Hkv, d, b, levels, R, dtype, Lcap, rope_base=10000.0, rope_npos=1,
-             router_fp8=False) -> TreeCfg:
+             router_fp8=False, fan=0) -> TreeCfg:
+    """b: tokens per level-1 node (chunk size); fan: children per node above
+    level 1 (0: b)."""
     return TreeCfg(B, Hq, Hkv, d, b, levels, R, F32 if dtype in ("f32", F32) else BF16,
-                   Lcap, rope_base, rope_npos, int(router_fp8))
+                   Lcap, rope_base, rope_npos, int(router_fp8), int(fan))
 
 
 def plan(cfg: TreeCfg, sel: Select | None = None, T: int = 0) -> PlanOut:

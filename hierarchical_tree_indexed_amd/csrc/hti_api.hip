@@ -64,6 +64,8 @@ hti_status check_cfg(const hti_tree_cfg *c)
     if (c->Hkv > 16) return fail(HTI_ERR_UNSUPPORTED, "Hkv = %d > 16", c->Hkv);
     if (c->d != 64 && c->d != 128) return fail(HTI_ERR_UNSUPPORTED, "head dim %d not in {64,128}", c->d);
     if (c->b < 2 || c->b > 64) return fail(HTI_ERR_UNSUPPORTED, "branching factor %d not in [2,64]", c->b);
+    if (c->fan != 0 && (c->fan < 2 || c->fan > 64))
+        return fail(HTI_ERR_UNSUPPORTED, "fan %d not 0 or in [2,64]", c->fan);
     if (c->levels < 0 || c->levels > HTI_MAX_LEVELS)
         return fail(HTI_ERR_INVALID_ARG, "levels %d not in [0,%d]", c->levels, HTI_MAX_LEVELS);
     if (c->R < 1 || c->R > HTI_MAX_R) return fail(HTI_ERR_UNSUPPORTED, "R = %d not in [1,%d]", c->R, HTI_MAX_R);
@@ -102,7 +104,7 @@ int sel_size(const hti_select *s) { return s->mode == HTI_TOPK ? s->k : s->cap; 
 void caps(const hti_tree_cfg *c, int64_t *ncap)
 {
     ncap[0] = c->Lcap;
-    for (int l = 1; l <= HTI_MAX_LEVELS; ++l) ncap[l] = (l <= c->levels) ? ncap[l - 1] / c->b : 0;
+    for (int l = 1; l <= HTI_MAX_LEVELS; ++l) ncap[l] = (l <= c->levels) ? ncap[l - 1] / (l == 1 ? c->b : cfg_fan(c)) : 0;
 }
 
 // Largest candidate list per level for any length <= Lcap, and the largest
@@ -128,7 +130,8 @@ Bounds bounds(const hti_tree_cfg *c, const hti_select *s, int32_t T)
         r.cand[Lv] = ncap[Lv];
         for (int l = Lv - 1; l >= 0; --l) {
             const int64_t kept = std::min(keff, r.cand[l + 1]);
-            r.cand[l] = std::min(ncap[l], kept * c->b + (c->b - 1));
+            const int64_t f = l == 0 ? c->b : cfg_fan(c);   // children per node of level l + 1
+            r.cand[l] = std::min(ncap[l], kept * f + (f - 1));
         }
         for (int l = 1; l <= Lv; ++l) {
             r.max_summary = std::max(r.max_summary, r.cand[l]);
@@ -166,6 +169,7 @@ TreeArgs tree_args(const hti_tree *tr)
     a.Hkv = c.Hkv;
     a.D = c.d;
     a.b = c.b;
+    a.fan = cfg_fan(&c);
     a.levels = c.levels;
     a.R = c.R;
     a.G = c.Hq / c.Hkv;
@@ -374,7 +378,7 @@ hti_status hti_tree_build(const hti_tree *tree, const int64_t *L_host, void *str
     TreeArgs a = tree_args(tree);
     int64_t n = maxL;
     for (int l = 1; l <= c.levels; ++l) {
-        n /= c.b;
+        n /= l == 1 ? c.b : cfg_fan(&c);
         hipError_t e = launch_build_level(a, l, n, hs);
         if (e != hipSuccess) return launched(e, "tree_build(level)");
     }
@@ -463,6 +467,7 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     a.sel = sel_out;
     a.sel_stride = sel_stride;
     a.binv = binv_of(tree->cfg.b);
+    a.finv = binv_of(cfg_fan(&tree->cfg));
     const int64_t units = units_ws;
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
     const hipStream_t hs = (hipStream_t)stream;
@@ -486,7 +491,7 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
         if (e != hipSuccess) return launched(e, what);
     }
     if (k_new) {
-        if (W > 0 && tree->cfg.b <= 32) {
+        if (W > 0 && tree->cfg.b <= 32 && cfg_fan(&tree->cfg) <= 32) {
             // the split kernel appends the token itself (one launch)
             a.k_new = k_new;
             a.v_new = v_new;
@@ -593,6 +598,7 @@ hti_status hti_sparse_prefill(const hti_tree *tree, const hti_select *sel, const
     ta.sel = sel_out;
     ta.sel_stride = sel_stride;
     ta.binv = binv_of(tree->cfg.b);
+    ta.finv = binv_of(cfg_fan(&tree->cfg));
     ta.part_acc = (float *)(wb + w.part_acc);
     ta.part_ml = (float *)(wb + w.part_ml);
 

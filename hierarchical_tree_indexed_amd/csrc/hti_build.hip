@@ -62,11 +62,12 @@ __global__ __launch_bounds__(256) void k_build_level(TreeArgs t, int lvl, int64_
     const int64_t bh = bhy;
     const int bi = bhy / t.Hkv, h = bhy % t.Hkv;
     const int64_t L = t.len[bi];
-    // node range: floor(floor(x / b) / b) = floor(x / b^2), so one division
-    // by the span b^lvl for each end; both ends are below the cache capacity
-    // (< 2^31), so a span clamped to 2^31 divides them the same, in 32 bits
+    // node range: floor(floor(x / f1) / f2) = floor(x / (f1 f2)), so one
+    // division by the span (the product of the fan-ins up to lvl) for each
+    // end; both ends are below the cache capacity (< 2^31), so a span clamped
+    // to 2^31 divides them the same, in 32 bits
     uint32_t span = 1;
-    for (int l = 0; l < lvl; ++l) span = (uint32_t)min((uint64_t)span * (uint64_t)t.b, (uint64_t)1 << 31);
+    for (int l = 1; l <= lvl; ++l) span = (uint32_t)min((uint64_t)span * (uint64_t)fan_in(t, l), (uint64_t)1 << 31);
     const int64_t lo = EXT ? (int64_t)((uint32_t)L / span) : 0;
     const int64_t hi = (int64_t)((uint32_t)(EXT ? min(L + ext, t.ncap[0]) : L) / span);
     if constexpr (LV == 2) {
@@ -159,8 +160,9 @@ __global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const 
     __syncthreads();
     int64_t idx = L + 1;                               // node count after the append
     for (int lvl = 1; lvl <= t.levels; ++lvl) {
-        if (idx % t.b != 0) break;                     // no node completed at this level
-        idx /= t.b;
+        const int f = fan_in(t, lvl);
+        if (idx % f != 0) break;                       // no node completed at this level
+        idx /= f;
         pool_node<T, D, CPL>(t, lvl, bh, h, idx - 1, lane);
         __syncthreads();
     }
@@ -170,11 +172,12 @@ __global__ __launch_bounds__(MAXT) void k_append(TreeArgs t, const T *kn, const 
 template <typename T, int D, int LV, bool EXT>
 static void build_level_lv(const TreeArgs &t, int lvl, dim3 grid, int64_t ext, hipStream_t s)
 {
-    if (t.b <= 8)
+    const int f = fan_in(t, lvl);
+    if (f <= 8)
         hipLaunchKernelGGL((k_build_level<T, D, 2, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
-    else if (t.b <= 16)
+    else if (f <= 16)
         hipLaunchKernelGGL((k_build_level<T, D, 4, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
-    else if (t.b <= 32)
+    else if (f <= 32)
         hipLaunchKernelGGL((k_build_level<T, D, 8, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
     else
         hipLaunchKernelGGL((k_build_level<T, D, 16, LV, EXT>), grid, dim3(256), 0, s, t, lvl, ext);
@@ -222,10 +225,11 @@ hipError_t launch_extend(const TreeArgs &t, const void *k_blk, const void *v_blk
                            (const float *)v_blk, T_);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // T tokens complete at most floor(T / b^l) + 1 nodes of level l
+    // T tokens complete at most floor(T / (span of a level-l node)) + 1
+    // nodes of level l
     int64_t span = T_;
     for (int l = 1; l <= t.levels; ++l) {
-        span /= t.b;
+        span /= fan_in(t, l);
         e = build_level_any(t, l, span + 1, T_, s);
         if (e != hipSuccess) return e;
     }
@@ -238,11 +242,12 @@ template <typename T, int D, int MAXT>
 static void append_b(const TreeArgs &t, const T *k, const T *v, hipStream_t s)
 {
     dim3 grid(t.B), block(64 * t.Hkv);
-    if (t.b <= 8)
+    const int f = t.b > t.fan ? t.b : t.fan;          // the larger fan-in of the levels
+    if (f <= 8)
         hipLaunchKernelGGL((k_append<T, D, 2, MAXT>), grid, block, 0, s, t, k, v);
-    else if (t.b <= 16)
+    else if (f <= 16)
         hipLaunchKernelGGL((k_append<T, D, 4, MAXT>), grid, block, 0, s, t, k, v);
-    else if (t.b <= 32)
+    else if (f <= 32)
         hipLaunchKernelGGL((k_append<T, D, 8, MAXT>), grid, block, 0, s, t, k, v);
     else
         hipLaunchKernelGGL((k_append<T, D, 16, MAXT>), grid, block, 0, s, t, k, v);

@@ -276,10 +276,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             if (ql < (int64_t)n - 1) n = ql < 0 ? 0 : (int)(ql + 1);
         }
         sm.n[0] = n;
-        const int bs = __builtin_ctz((unsigned)b);
-        const bool pow2 = (b & (b - 1)) == 0;
         for (int l = 1; l <= levels; ++l) {
-            n = pow2 ? (n >> bs) : n / b;
+            const int f = l == 1 ? b : t.fan;         // children per node of level l
+            n = (f & (f - 1)) == 0 ? (n >> __builtin_ctz((unsigned)f)) : n / f;
             sm.n[l] = n;
         }
     }
@@ -360,18 +359,20 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             *reinterpret_cast<uint4 *>(vw + tid * EPC) = vx;
         }
         // (lengths are below 2^31 here: 32-bit index arithmetic, a mask and
-        // a shift when b is a power of two)
+        // a shift when a fan-in is a power of two)
         uint32_t idx = (uint32_t)Lold + 1u;
-        const bool pow2 = (b & (b - 1)) == 0;
-        const int bs = __builtin_ctz((unsigned)b);
+        auto completes = [&](uint32_t x, int f) __attribute__((always_inline)) {
+            return (f & (f - 1)) == 0 ? (x & (uint32_t)(f - 1)) == 0u : x % (uint32_t)f == 0u;
+        };
         // Only a token that completes a node needs the row in place before
         // anything else (its pooling reads it): otherwise the stores complete
         // in the background, long before the token level reads the row.
-        if (levels > 0 && (pow2 ? (idx & (uint32_t)(b - 1)) == 0u : idx % (uint32_t)b == 0u)) {
+        if (levels > 0 && completes(idx, b)) {
             __syncthreads();
             for (int l = 1; l <= levels; ++l) {
-                if (pow2 ? (idx & (uint32_t)(b - 1)) != 0u : idx % (uint32_t)b != 0u) break;
-                idx = pow2 ? idx >> bs : idx / (uint32_t)b;
+                const int f = l == 1 ? b : t.fan;     // children per node of level l
+                if (!completes(idx, f)) break;
+                idx = (f & (f - 1)) == 0 ? idx >> __builtin_ctz((unsigned)f) : idx / (uint32_t)f;
                 if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, (int64_t)idx - 1, lane);
                 __syncthreads();
             }
@@ -393,13 +394,15 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const bool top = (lvl == levels);
         st.cs.selp = sm.wsel[cur][wave];
         st.cs.nprev = top ? 0 : nprev;
-        st.cs.b = b;
-        st.cs.binv = a.binv;
+        // children per parent: b tokens under a level-1 node, fan nodes above
+        const int fb = lvl == 0 ? b : t.fan;
+        st.cs.b = fb;
+        st.cs.binv = lvl == 0 ? a.binv : a.finv;
         st.cs.top = top;
-        const int orph0 = top ? 0 : b * sm.n[lvl + 1];
+        const int orph0 = top ? 0 : fb * sm.n[lvl + 1];
         st.cs.orph0 = orph0;
         if (lvl >= 1) {
-            st.m = top ? sm.n[lvl] : nprev * b + (sm.n[lvl] - orph0);
+            st.m = top ? sm.n[lvl] : nprev * fb + (sm.n[lvl] - orph0);
             st.kb = to_global<T>(sm.lkp[lvl - 1]);
             st.vb = to_global<T>(sm.lvp[lvl - 1]);
             if constexpr (F8) {

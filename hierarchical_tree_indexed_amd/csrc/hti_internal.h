@@ -24,6 +24,7 @@ struct TreeArgs {
     const float2 *rope;                  // [rope_npos, D/2] (cos, sin)
     int rope_npos;
     int B, Hq, Hkv, D, b, levels, R, G;
+    int fan;                             // children per node above level 1 (b: tokens per level-1 node)
     // Traversals: Hkv routing heads per sequence, G query heads each; the
     // tree arrays of routing head g are those of KV head g / hdiv, of
     // Hkv / hdiv per sequence (hdiv > 1: every query head routes on its own)
@@ -33,6 +34,11 @@ struct TreeArgs {
     int rfp8;                            // summary keys are scored through lkq / lks
 };
 
+// Children per node of level lvl >= 1: the tokens of a level-1 node (b),
+// the nodes of the level below above it (fan).
+__host__ __device__ inline int fan_in(const TreeArgs &t, int lvl) { return lvl == 1 ? t.b : t.fan; }
+inline int cfg_fan(const hti_tree_cfg *c) { return c->fan > 0 ? c->fan : c->b; }
+
 // Selection rule and the query-side buffers of one traversal launch.
 struct TravArgs {
     TreeArgs t;
@@ -40,6 +46,7 @@ struct TravArgs {
     float p;
     int leaf_only;     // 1: summaries route but do not join the softmax
     uint32_t binv;     // ceil(2^32 / b), for division by b in index arithmetic
+    uint32_t finv;     // ceil(2^32 / fan), likewise
     const void *q;     // decode [B, Nq, Hq, D]; prefill [B, T, Hq, D]
     const int64_t *q_pos;  // decode [B, Nq]: each query attends to tokens 0..q_pos (nullable: len - 1)
     int Nq;            // queries per sequence (decode) or block length T (prefill)

@@ -168,8 +168,9 @@ __device__ __forceinline__ void store_key_row(const TreeArgs &t, int lvl, int64_
     }
 }
 
-// One wave pools node `node` of level `lvl` (children at level lvl-1) for
-// (sequence, KV head) slot bh.  CPL = children per lane-row (ceil(b / 4)).
+// One wave pools node `node` of level `lvl` (children at level lvl-1: b
+// tokens at level 1, fan nodes above) for (sequence, KV head) slot bh.
+// CPL = children per lane-row (ceil(children / 4)).
 // LV: 1 when lvl is 1, 2 when lvl is at least 2, 0 when either (known at run
 // time only).  refs() is called by every wave once its child loads are in
 // flight, active or not (so it may hold a block barrier), and returns the R
@@ -185,7 +186,7 @@ __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64
     constexpr int NP = D / 64;                   // elements per lane of a pooled row
     const int sub = lane & 15, rg = lane >> 4;
     const int col = sub * EPL + rg * NP;         // this lane's column of a pooled row
-    const int b = t.b, R = t.R;
+    const int b = LV == 1 ? t.b : LV == 2 ? t.fan : fan_in(t, lvl), R = t.R;   // children of the node
     // An inactive wave reads the children of a node clamped into the level
     // (every launch has at least one node there) and discards them: the
     // loads are unconditional, so the compiler keeps the rows packed until
@@ -270,7 +271,7 @@ __device__ __forceinline__ void pool_node_one_ref(const TreeArgs &t, int lvl, in
     constexpr int NP = D / 64;
     const int sub = lane & 15, rg = lane >> 4;
     const int col = sub * EPL + rg * NP;
-    const int b = t.b, R = t.R;
+    const int b = t.fan, R = t.R;                // children of a node above level 1
     const int64_t c0 = min(node, t.ncap[lvl] - 1) * b;
     const int64_t nchild_cap = t.ncap[lvl - 1];
     bool valid[CPL];

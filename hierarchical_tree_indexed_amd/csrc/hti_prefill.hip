@@ -569,7 +569,7 @@ __global__ __launch_bounds__(256) void k_top_scores(PrefillArgs a)
     const int T = a.T, R = t.R;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int n = (int)t.len[bi];
-    for (int l = 1; l <= t.levels; ++l) n /= t.b;
+    for (int l = 1; l <= t.levels; ++l) n /= fan_in(t, l);
     const int ntop = n, ncol = n * R;
     if (ncol == 0) return;
 

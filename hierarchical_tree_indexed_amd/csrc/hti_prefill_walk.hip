@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         nlev[0] = n;
 #pragma unroll
         for (int l = 1; l <= HTI_MAX_LEVELS; ++l) {
-            n = (l <= levels) ? n / b : 0;
+            n = (l <= levels) ? n / (l == 1 ? b : t.fan) : 0;
             nlev[l] = n;
         }
     }
@@ -489,12 +489,14 @@ __global__ __launch_bounds__(256, 3) void k_prefill_walk(TravArgs a, int MC)
         const bool top = (lvl == levels);
         cs.selp = selbuf + cur * kMaxSel;
         cs.nprev = top ? 0 : nsel;
-        cs.b = b;
-        cs.binv = a.binv;
+        // (children per parent above level 1: the fan)
+        const int fb = t.fan;
+        cs.b = fb;
+        cs.binv = a.finv;
         cs.top = top;
-        const int orph0 = top ? 0 : b * nlev[lvl + 1];
+        const int orph0 = top ? 0 : fb * nlev[lvl + 1];
         cs.orph0 = orph0;
-        const int m = top ? nlev[lvl] : nsel * b + (nlev[lvl] - orph0);
+        const int m = top ? nlev[lvl] : nsel * fb + (nlev[lvl] - orph0);
         const T *kb = (const T *)t.lk[lvl - 1] + bh * t.ncap[lvl] * R * D;
         const T *vb = (const T *)t.lv[lvl - 1] + bh * t.ncap[lvl] * D;
         const bool take_all = (a.mode == HTI_TOPK) ? (m <= a.k) : (m <= 1);

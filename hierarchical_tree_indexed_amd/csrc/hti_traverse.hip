@@ -125,7 +125,7 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
         int64_t n = L;
         sm.n[0] = n;
         for (int l = 1; l <= levels; ++l) {
-            n /= b;
+            n /= fan_in(t, l);
             sm.n[l] = n;
         }
     }
@@ -442,11 +442,13 @@ __global__ __launch_bounds__(NWV * 64, STAGE ? 1 : 4) void k_traverse(TravArgs a
         Cands cs;
         cs.selp = sm.sel[cur];
         cs.nprev = nprev;
-        cs.b = b;
-        cs.binv = a.binv;
+        // children per parent: b tokens under a level-1 node, fan nodes above
+        const int fb = tok ? b : t.fan;
+        cs.b = fb;
+        cs.binv = tok ? a.binv : a.finv;
         cs.top = (lvl == levels);
-        cs.orph0 = cs.top ? 0 : (int64_t)b * sm.n[lvl + 1];
-        const int64_t mfull = cs.top ? sm.n[lvl] : (int64_t)nprev * b + (sm.n[lvl] - cs.orph0);
+        cs.orph0 = cs.top ? 0 : (int64_t)fb * sm.n[lvl + 1];
+        const int64_t mfull = cs.top ? sm.n[lvl] : (int64_t)nprev * fb + (sm.n[lvl] - cs.orph0);
         const int nxt = cur ^ 1;
 
         int m;

@@ -55,6 +55,7 @@ class Workload:
     steps: int = 0         # decode loop: appended tokens per sequence
     rope_base: float = 10000.0
     seed: int = 0
+    fan: int = 0           # children per node above level 1 (0: b, the chunk size of level 1)
 
     @property
     def G(self) -> int:
@@ -68,11 +69,16 @@ class Workload:
     def elem_bytes(self) -> int:
         return 4 if self.dtype == F32 else 2
 
+    @property
+    def F(self) -> int:
+        """Children per node above level 1."""
+        return self.fan or self.b
+
     def level_counts(self, L: int | None = None) -> list[int]:
-        """Full-node counts n_0 = L, n_l = floor(n_{l-1} / b)."""
+        """Full-node counts n_0 = L, n_1 = floor(L / b), n_l = floor(n_{l-1} / F)."""
         n = [self.L if L is None else L]
-        for _ in range(self.levels):
-            n.append(n[-1] // self.b)
+        for lvl in range(1, self.levels + 1):
+            n.append(n[-1] // (self.b if lvl == 1 else self.F))
         return n
 
     def replace(self, **kw) -> "Workload":

@@ -74,7 +74,9 @@ typedef struct {
     int32_t Hq;         /* query heads; Hq % Hkv == 0, G = Hq / Hkv in {1,2,4,8} */
     int32_t Hkv;        /* KV heads */
     int32_t d;          /* head dim: 64 or 128 */
-    int32_t b;          /* branching factor, 2..64 */
+    int32_t b;          /* tokens per level-1 node (ZHA's chunk size C), 2..64;
+                           also the children per node above level 1 unless
+                           `fan` says otherwise */
     int32_t levels;     /* tree levels above the tokens, 0..HTI_MAX_LEVELS */
     int32_t R;          /* reference queries per KV head, 1..HTI_MAX_R */
     int32_t dtype;      /* hti_dtype of the caches, tree nodes and q/k/v inputs */
@@ -95,6 +97,12 @@ typedef struct {
                            2^(e - 8), amax = f * 2^e with f in [0.5, 1) its
                            largest magnitude (1 for an all-zero row), and
                            rounded to the nearest E4M3 value, ties to even. */
+    int32_t fan;        /* children per node above level 1 (ZHA's fan F, which
+                           Figure 4 and Table II name apart from the chunk size
+                           C; every geometry there has F = C), 2..64; 0 means b.
+                           Level 1 has floor(L / b) nodes, level l > 1
+                           floor(n_{l-1} / fan).  A decode step appends in its
+                           own launch when b and fan are at most 32. */
 } hti_tree_cfg;
 
 /* Device buffers of a tree set (all caller-allocated, sizes from hti_plan). */
@@ -143,7 +151,8 @@ typedef struct {
 
 /* Sizes for a configuration (all host values). */
 typedef struct {
-    int64_t ncap[HTI_MAX_LEVELS + 1]; /* ncap[0] = Lcap, ncap[l] = floor(ncap[l-1] / b) */
+    int64_t ncap[HTI_MAX_LEVELS + 1]; /* ncap[0] = Lcap, ncap[1] = floor(Lcap / b),
+                                         ncap[l] = floor(ncap[l-1] / fan) above */
     size_t cache_bytes;               /* each of k_cache, v_cache */
     size_t lvl_k_bytes[HTI_MAX_LEVELS];
     size_t lvl_v_bytes[HTI_MAX_LEVELS];

@@ -32,10 +32,10 @@ def log(*a):
 
 
 def make_treeset(w, Lcap, K=None, V=None, refs=None, T=0, rope_npos=None, router_fp8=False):
-    """TreeSet on cuda:0 for workload w (B, Hq, Hkv, d, b, levels, R, dtype)."""
+    """TreeSet on cuda:0 for workload w (B, Hq, Hkv, d, b, fan, levels, R, dtype)."""
     sel = select_of(w)
     cfg = hti.make_cfg(w.B, w.Hq, w.Hkv, w.d, w.b, w.levels, w.R, w.dtype, Lcap, w.rope_base, 1,
-                       router_fp8=router_fp8)
+                       router_fp8=router_fp8, fan=w.fan)
     need = hti.plan(cfg, sel, T).rope_npos_needed
     cfg.rope_npos = max(need, rope_npos or 0)
     ts = hti.TreeSet(cfg, device="cuda", k_cache=K, v_cache=V)
@@ -54,14 +54,14 @@ def kmax_of(w):
 
 
 def oracle_tree(w, K_bh, V_bh, refs_h, L):
-    return oracle.build_tree(K_bh[:L], V_bh[:L], refs_h, w.b, w.levels, bf16=(w.dtype == "bf16"), L=L)
+    return oracle.build_tree(K_bh[:L], V_bh[:L], refs_h, w.b, w.levels, bf16=(w.dtype == "bf16"), L=L, fan=w.F)
 
 
 def oracle_tree_from_device(ts, w, bi, g, L):
     """The oracle's tree of (sequence bi, KV head g) holding the device's
     stored levels: for checks of the routing on the keys the device holds
     (the build itself is checked against the oracle's own build)."""
-    tr = oracle.Tree(L, w.d, w.b, w.levels, w.R, w.dtype == "bf16")
+    tr = oracle.Tree(L, w.d, w.b, w.levels, w.R, w.dtype == "bf16", fan=w.F)
     for l in range(w.levels):
         n = tr.lk[l].shape[0]
         tr.lk[l][...] = ts.lvl_k[l][bi, g, :n].float().cpu().numpy()
@@ -74,7 +74,7 @@ def router_copy_matches(ts, w, bi, g, L):
     of the device's stored keys; returns the number of rows compared."""
     rows = 0
     for l in range(w.levels):
-        n = L // w.b ** (l + 1)
+        n = w.level_counts(L)[l + 1]
         codes, sc = oracle.router_fp8(ts.lvl_k[l][bi, g, :n].float().cpu().numpy())
         assert np.array_equal(ts.lvl_kq[l][bi, g, :n].cpu().numpy(), codes), f"level {l + 1} codes"
         assert np.array_equal(ts.lvl_ks[l][bi, g, :n].cpu().numpy(), sc), f"level {l + 1} scales"

@@ -94,6 +94,16 @@ def test_decode_1m_batch4_sampled():
     _decode_full(w, [(0, 0), (1, 5), (2, 2), (3, 7)], Lcap=w.L + 4, append_steps=1)
 
 
+def test_decode_1m_c32_f8_sampled():
+    """The 1,048,576-token decode at batch 4 on a tree with chunk size 32 at
+    level 1 and fan 8 above it (five levels: 32,768 / 4,096 / 512 / 64 / 8
+    nodes), the fan-out geometry the benchmark times beside the C = F = 32
+    tree; one appended token, four units sampled against the oracle's own
+    tree of the same geometry."""
+    w = W.DEC1M.replace(name="decode_1m_b4_c32_f8", fan=8, levels=5)
+    _decode_full(w, [(0, 1), (1, 6), (2, 3), (3, 4)], Lcap=w.L + 4, append_steps=1)
+
+
 def test_decode_step_1m_batch4_benched_config():
     """The step the benchmark times, in its configuration: 1,048,575 cached
     tokens x 4 sequences (16 planted needles each), then two decode_step

@@ -73,6 +73,10 @@ BUILD_CASES = [
     W.DEC128K.replace(name="bf16_b64_r2", b=64, levels=2, L=64 * 64 * 2 + 77, R=2, Hq=4, Hkv=2, needles=0),
     # the most references (their rows fill the staged block exactly), fp32, d = 64
     W.TINY.replace(name="f32_d64_b40_r8", d=64, b=40, levels=2, L=40 * 40 * 2 + 11, R=8, Hq=2, Hkv=2),
+    # a fan above level 1 apart from the chunk size: 16 tokens per level-1
+    # node, 4 nodes per node above (and the reverse, with 2 references)
+    W.DEC128K.replace(name="bf16_c16_f4", b=16, fan=4, levels=3, L=16 * 4 * 4 * 5 + 77, Hq=4, Hkv=2, needles=0),
+    W.TINY.replace(name="f32_c4_f16_r2", b=4, fan=16, levels=3, L=4 * 16 * 16 * 2 + 9, R=2, Hq=2, Hkv=2),
 ]
 
 
@@ -119,6 +123,11 @@ DECODE_CASES = [
     # eight reference keys per node in fp32 at d = 128: a key batch must hold
     # all of a candidate's keys
     W.DEC128K.replace(name="f32_d128_r8", dtype="f32", Hq=8, Hkv=2, L=6000, b=16, levels=2, k=3, R=8),
+    # chunk size 32 at level 1, fan 8 above (ZHA's C and F apart), top-k and
+    # top-p with two references; and fan 48 over chunks of 8
+    W.DEC128K.replace(name="c32_f8", L=32 * 8 * 8 * 3 + 8 * 32 + 17, fan=8, levels=3, B=2, needles=0),
+    W.ZHA2M.replace(name="topp_c16_f4_r2", L=16 * 4 ** 3 * 3 + 70, fan=4, levels=4, R=2),
+    W.DEC128K.replace(name="c8_f48_d64", Hq=4, Hkv=2, d=64, b=8, fan=48, levels=2, L=8 * 48 * 4 + 100, k=3),
 ]
 
 
@@ -565,7 +574,7 @@ def _same_tree(w, A, B_, L1):
         assert torch.equal(A.k_cache[s_, :, :n], B_.k_cache[s_, :, :n])
         assert torch.equal(A.v_cache[s_, :, :n], B_.v_cache[s_, :, :n])
         for l in range(w.levels):
-            n //= w.b
+            n //= w.b if l == 0 else w.F
             assert torch.equal(A.lvl_k[l][s_, :, :n], B_.lvl_k[l][s_, :, :n]), (s_, l)
             assert torch.equal(A.lvl_v[l][s_, :, :n], B_.lvl_v[l][s_, :, :n]), (s_, l)
 
@@ -575,6 +584,7 @@ EXTEND_CASES = [
     W.TINY.replace(name="ext_f32_d64_b8", B=2, Hq=2, Hkv=2, b=8, levels=4, L=3000),
     # four references: the levels above the first pool one (node, reference) per wave
     W.ZHA2M.replace(name="ext_bf16_r4_b16", B=2, L=16 * 16 * 16 + 900, levels=3),
+    W.DEC128K.replace(name="ext_c32_f4", B=2, Hq=8, Hkv=2, L=32 * 4 * 4 * 3 + 500, fan=4, levels=3, needles=0),
 ]
 
 
@@ -653,6 +663,15 @@ def test_prefill_parity(P0, T, levels, token_nodes):
     """token_nodes True: the prefix token level node-inverted (levels >= 1);
     False: every query gathers its own token rows."""
     _check_prefill(PF.replace(levels=levels, k=8 if levels else 32), P0, T, token_nodes=token_nodes)
+
+
+@pytest.mark.parametrize("token_nodes", [False, True])
+@pytest.mark.parametrize("b,fan,levels,P0,T", [(32, 4, 3, 32 * 4 * 4 * 3 + 70, 90), (8, 32, 2, 8 * 32 * 5 + 3, 40)])
+def test_prefill_fanout(b, fan, levels, P0, T, token_nodes):
+    """A tree whose fan above level 1 differs from its chunk size, on both
+    token-level paths (the node-inverted one groups queries by level-1 node,
+    whose b tokens stay contiguous)."""
+    _check_prefill(PF.replace(b=b, fan=fan, levels=levels, k=6), P0, T, token_nodes=token_nodes)
 
 
 @pytest.mark.parametrize("Hq,Hkv,R,k,P0", [(32, 8, 1, 8, 32 * 32 * 12 + 70), (8, 8, 1, 8, 32 * 32 * 12 + 70),
@@ -780,6 +799,10 @@ STEP_CASES = [
                       needles=0, k=3, Nq=2),
     # b = 64: the two-launch form
     W.DEC128K.replace(name="step_b64", b=64, levels=2, L=64 * 64 - 3, k=4, needles=0),
+    # chunk 16, fan 4: steps complete nodes of levels 1 to 3 in the one launch
+    W.DEC128K.replace(name="step_c16_f4", b=16, fan=4, levels=3, L=16 * 4 * 4 * 3 - 3, k=4, needles=0),
+    # fan 48 above chunks of 8: the two-launch form
+    W.DEC128K.replace(name="step_c8_f48", b=8, fan=48, levels=2, L=8 * 48 * 2 - 4, k=3, needles=0),
 ]
 
 

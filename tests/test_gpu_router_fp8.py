@@ -42,7 +42,7 @@ def _check_copy(ts, w, Ls):
         ks = ts.lvl_ks[l].cpu().numpy()
         lk = ts.lvl_k[l].float().cpu().numpy()
         for bi in range(w.B):
-            n = Ls[bi] // w.b ** (l + 1)
+            n = w.level_counts(Ls[bi])[l + 1]
             if n == 0:
                 continue
             codes, sc = oracle.router_fp8(lk[bi, :, :n])

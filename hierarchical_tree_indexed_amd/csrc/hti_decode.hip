@@ -208,6 +208,12 @@ struct Step {
 
 } // namespace
 
+// x is a multiple of f (a mask when f is a power of two)
+__device__ __forceinline__ bool completes(uint32_t x, int f)
+{
+    return (f & (f - 1)) == 0 ? (x & (uint32_t)(f - 1)) == 0u : x % (uint32_t)f == 0u;
+}
+
 template <typename T, int D, int G, bool F8>
 __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
 {
@@ -223,13 +229,38 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     // one round trip, before the first field is used: each launch's arguments
     // are fresh memory, and fields read later, one line at a time as the code
     // first needs them, would each wait for their own miss.
+    // (Written out as one block of scalar loads and a single wait: left to
+    // the compiler, the loads went out in two batches with a wait between,
+    // two round trips.)  The segment also holds the hidden arguments after
+    // the explicit ones, so the fourteenth line is inside it.
     int W = ws.W;
     {
-        const uint32_t *kp = (const uint32_t *)__builtin_amdgcn_kernarg_segment_ptr();
-        constexpr int kLines = (int)((sizeof(TravArgs) + sizeof(DecodeWs) + 63) / 64) + 1;
+        const auto kp = __builtin_amdgcn_kernarg_segment_ptr();
+        static_assert((sizeof(TravArgs) + sizeof(DecodeWs) + 63) / 64 + 1 == 14, "argument block lines");
+        uint32_t x[14];
+        asm volatile("s_load_dword %0, %14, 0x0\n\t"
+                     "s_load_dword %1, %14, 0x40\n\t"
+                     "s_load_dword %2, %14, 0x80\n\t"
+                     "s_load_dword %3, %14, 0xc0\n\t"
+                     "s_load_dword %4, %14, 0x100\n\t"
+                     "s_load_dword %5, %14, 0x140\n\t"
+                     "s_load_dword %6, %14, 0x180\n\t"
+                     "s_load_dword %7, %14, 0x1c0\n\t"
+                     "s_load_dword %8, %14, 0x200\n\t"
+                     "s_load_dword %9, %14, 0x240\n\t"
+                     "s_load_dword %10, %14, 0x280\n\t"
+                     "s_load_dword %11, %14, 0x2c0\n\t"
+                     "s_load_dword %12, %14, 0x300\n\t"
+                     "s_load_dword %13, %14, 0x340\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&s"(x[0]), "=&s"(x[1]), "=&s"(x[2]), "=&s"(x[3]), "=&s"(x[4]), "=&s"(x[5]),
+                       "=&s"(x[6]), "=&s"(x[7]), "=&s"(x[8]), "=&s"(x[9]), "=&s"(x[10]), "=&s"(x[11]),
+                       "=&s"(x[12]), "=&s"(x[13])
+                     : "s"(kp)
+                     : "memory");
         uint32_t touch = 0;
 #pragma unroll
-        for (int i = 0; i < kLines; ++i) touch ^= kp[i * 16];
+        for (int i = 0; i < 14; ++i) touch ^= x[i];
         asm volatile("" : "+s"(W) : "s"(touch));
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -242,6 +273,8 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     const int64_t unit = (int64_t)blockIdx.z * t.Hkv + g;
     const int64_t bh = (int64_t)bi * (t.Hkv / t.hdiv) + g / t.hdiv;   // tree slot of routing head g
     const int b = t.b, levels = t.levels, R = t.R;
+    const int fan = __builtin_amdgcn_readfirstlane(t.fan);
+    const uint32_t binv = __builtin_amdgcn_readfirstlane(a.binv), finv = __builtin_amdgcn_readfirstlane(a.finv);
     const int keff = (a.mode == HTI_TOPK) ? a.k : a.cap;
     const bool topp = a.mode == HTI_TOPP;
     uint64_t *xw = ws.words + (int64_t)unit * levels * W * kSlots;
@@ -277,7 +310,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
         sm.n[0] = n;
         for (int l = 1; l <= levels; ++l) {
-            const int f = l == 1 ? b : t.fan;         // children per node of level l
+            const int f = l == 1 ? b : fan;           // children per node of level l
             n = (f & (f - 1)) == 0 ? (n >> __builtin_ctz((unsigned)f)) : n / f;
             sm.n[l] = n;
         }
@@ -297,6 +330,15 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
     }
     const gptr<float2> rope = to_global<float2>(t.rope);
+    // decode step: the new row of this unit's KV head does not depend on the
+    // length, so its loads go out with the query's (stored after the length
+    // is known, below)
+    constexpr int EPCN = 16 / (int)sizeof(T);
+    uint4 knx = make_uint4(0u, 0u, 0u, 0u), vnx = knx;
+    if (a.k_new != nullptr && tid < D / EPCN) {
+        knx = gload<uint4>(to_global<T>(a.k_new) + bh * D + tid * EPCN);
+        vnx = gload<uint4>(to_global<T>(a.v_new) + bh * D + tid * EPCN);
+    }
     {
         const gptr<T> qp = to_global<T>(a.q) + orow * D;
         constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
@@ -348,29 +390,22 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         // the new row of this unit's KV head at position lold, then every
         // node it completes, level by level (one wave pools)
         const int64_t Lold = sm.lold;
-        constexpr int EPC = 16 / (int)sizeof(T);
-        const T *kn = (const T *)a.k_new + bh * D, *vn = (const T *)a.v_new + bh * D;
         T *kw = (T *)t.kc + (bh * t.ncap[0] + Lold) * D;
         T *vw = (T *)t.vc + (bh * t.ncap[0] + Lold) * D;
-        if (tid < D / EPC) {
-            const uint4 kx = *reinterpret_cast<const uint4 *>(kn + tid * EPC);
-            const uint4 vx = *reinterpret_cast<const uint4 *>(vn + tid * EPC);
-            *reinterpret_cast<uint4 *>(kw + tid * EPC) = kx;
-            *reinterpret_cast<uint4 *>(vw + tid * EPC) = vx;
+        if (tid < D / EPCN) {
+            *reinterpret_cast<uint4 *>(kw + tid * EPCN) = knx;
+            *reinterpret_cast<uint4 *>(vw + tid * EPCN) = vnx;
         }
         // (lengths are below 2^31 here: 32-bit index arithmetic, a mask and
         // a shift when a fan-in is a power of two)
         uint32_t idx = (uint32_t)Lold + 1u;
-        auto completes = [&](uint32_t x, int f) __attribute__((always_inline)) {
-            return (f & (f - 1)) == 0 ? (x & (uint32_t)(f - 1)) == 0u : x % (uint32_t)f == 0u;
-        };
         // Only a token that completes a node needs the row in place before
         // anything else (its pooling reads it): otherwise the stores complete
         // in the background, long before the token level reads the row.
         if (levels > 0 && completes(idx, b)) {
             __syncthreads();
             for (int l = 1; l <= levels; ++l) {
-                const int f = l == 1 ? b : t.fan;     // children per node of level l
+                const int f = l == 1 ? b : fan;       // children per node of level l
                 if (!completes(idx, f)) break;
                 idx = (f & (f - 1)) == 0 ? idx >> __builtin_ctz((unsigned)f) : idx / (uint32_t)f;
                 if (wave == 0) pool_node<T, D, 8>(t, l, bh, g / t.hdiv, (int64_t)idx - 1, lane);
@@ -395,9 +430,12 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         st.cs.selp = sm.wsel[cur][wave];
         st.cs.nprev = top ? 0 : nprev;
         // children per parent: b tokens under a level-1 node, fan nodes above
-        const int fb = lvl == 0 ? b : t.fan;
+        // (values read once below: a select between two argument fields
+        // would become a load through a selected argument address, which
+        // puts part of the argument block in scratch)
+        const int fb = lvl == 0 ? b : fan;
         st.cs.b = fb;
-        st.cs.binv = lvl == 0 ? a.binv : a.finv;
+        st.cs.binv = lvl == 0 ? binv : finv;
         st.cs.top = top;
         const int orph0 = top ? 0 : fb * sm.n[lvl + 1];
         st.cs.orph0 = orph0;

@@ -147,6 +147,8 @@ def test_decode_parity(w):
 QPOS_CASES = [
     W.DEC128K.replace(name="qpos_b32", B=2, L=32 * 32 * 3 + 77, levels=2, needles=0, Nq=5),
     W.ZHA2M.replace(name="qpos_topp_r4", L=16 ** 3 * 2 + 33, levels=3, Nq=4),
+    # node boundaries of a chunk-8 / fan-16 tree
+    W.DEC128K.replace(name="qpos_c8_f16", B=2, b=8, fan=16, L=8 * 16 * 16 + 77, levels=3, needles=0, Nq=5),
 ]
 
 
@@ -400,6 +402,7 @@ def _check_per_head(w, trees, K, V, Ls, q, out, lse, so, t_of=None, blk=None):
 PER_HEAD_CASES = [
     W.DEC128K.replace(name="ph_gqa4", B=2, L=20000, needles=0, levels=2, Nq=2),
     W.ZHA2M.replace(name="ph_topp_r4", L=16 ** 4 + 300, levels=3, Hq=8, Hkv=2),
+    W.DEC128K.replace(name="ph_c32_f4", L=32 * 4 * 4 * 4 + 99, fan=4, levels=3, needles=0, Nq=2),
 ]
 
 
@@ -476,6 +479,7 @@ def test_prefill_per_head_routing():
 LEAF_CASES = [
     W.DEC128K.replace(name="leaf_gqa4", B=2, L=20000, needles=0, levels=2, Nq=2),
     W.ZHA2M.replace(name="leaf_topp_r4", L=16 ** 4 + 300, levels=3, Hq=8, Hkv=2),
+    W.ZHA2M.replace(name="leaf_topp_c16_f8", L=16 * 8 * 8 * 3 + 41, fan=8, levels=3, Hq=8, Hkv=2),
 ]
 
 

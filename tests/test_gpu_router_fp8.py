@@ -19,6 +19,9 @@ CASES = [
     W.DEC128K.replace(name="r8_b32_g4", L=40000 + 17, B=2, Hq=8, Hkv=2, needles=0, Nq=2),
     W.ZHA2M.replace(name="r8_topp_r4_b16", L=70000 + 5, levels=4, Nq=2),
     W.DEC128K.replace(name="r8_d64_b3_g1", d=64, b=3, levels=6, L=3000, Hq=4, Hkv=4, k=4, needles=0, Nq=2),
+    # chunk 16 at level 1, fan 4 above
+    W.DEC128K.replace(name="r8_c16_f4", b=16, fan=4, levels=3, L=16 * 4 * 4 * 6 + 21, B=2, Hq=8, Hkv=2,
+                      needles=0, Nq=2),
 ]
 
 

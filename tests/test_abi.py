@@ -49,6 +49,39 @@ def test_plan_sizes():
     assert p3.rope_npos_needed == 287 + 8192
 
 
+def test_plan_sizes_with_fan():
+    """A fan above level 1 apart from the chunk size: level 1 holds
+    floor(Lcap / b) nodes, every level above floor(n / fan); the candidate
+    bound of a summary level is k * fan + fan - 1, of the token level
+    k * b + b - 1; fan 0 is the chunk size."""
+    c = cfg(b=32, levels=4, Lcap=1 << 20)
+    c.fan = 8
+    p = hti.plan(c, hti.make_select("topk", k=8))
+    assert list(p.ncap[:5]) == [1 << 20, 1 << 15, 1 << 12, 1 << 9, 1 << 6]
+    assert p.lvl_v_bytes[3] == 2 * 8 * 64 * 128 * 2
+    # summary levels: at most 8 * 8 + 7 = 71 candidates (row 71); token level
+    # 8 * 32 + 31 = 287 (row 287)
+    assert p.rope_npos_needed == 288
+    c.fan = 0
+    p0 = hti.plan(c, hti.make_select("topk", k=8))
+    assert list(p0.ncap[:5]) == [1 << 20, 1 << 15, 1 << 10, 1 << 5, 1]
+    c.b, c.fan = 4, 48
+    p1 = hti.plan(c, hti.make_select("topk", k=8))
+    assert list(p1.ncap[:4]) == [1 << 20, 1 << 18, (1 << 18) // 48, (1 << 18) // 48 // 48]
+    # summary bound 8 * 48 + 47 = 431 (row 431)
+    assert p1.rope_npos_needed == 432
+
+
+@pytest.mark.parametrize("fan", [1, 65, -3])
+def test_plan_rejects_bad_fan(fan):
+    c = cfg()
+    c.fan = fan
+    out = hti.PlanOut()
+    st = hti.lib().hti_plan(C.byref(c), None, 0, C.byref(out))
+    assert st == -2, hti.last_error()
+    assert "fan" in hti.last_error()
+
+
 @pytest.mark.parametrize("bad,status", [
     (dict(Hq=30), -1), (dict(Hq=48, Hkv=8), -2), (dict(d=96), -2), (dict(b=1), -2),
     (dict(levels=13), -1), (dict(R=9), -2), (dict(dtype=7), -1), (dict(Lcap=-1), -2),

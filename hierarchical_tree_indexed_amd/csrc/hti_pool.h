@@ -67,6 +67,29 @@ __device__ __forceinline__ void store_part(T *p, const float (&v)[N])
     }
 }
 
+// EPL elements of a child row read once (the tree build): a non-temporal
+// load, so that the streamed rows do not push other lines out of the caches.
+template <typename T, int EPL, bool NT>
+__device__ __forceinline__ void load_child(const T *p, float *o)
+{
+    if constexpr (NT && sizeof(T) * EPL == 16) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[2 * i] = __uint_as_float(v[i] << 16);
+                o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+        }
+    } else {
+        load_vec<T, EPL>(p, o);
+    }
+}
+
 // E4M3 code (OCP 8-bit float: 4 exponent bits, bias 7, 3 mantissa bits) of
 // x, |x| < 256, rounded to the nearest value, ties to even.  With e the
 // binade of |x| (floor(log2 |x|), at least -6, the subnormal binade's) the
@@ -213,9 +236,9 @@ __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64
     const int kstride = (lvl == 1) ? 1 : R;      // key rows per child
     float vx[CPL][EPL], kx[CPL][EPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
+    for (int c = 0; c < CPL; ++c) load_child<T, EPL, LV != 0>(vbase + crow[c] * D + sub * EPL, vx[c]);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + crow[c] * kstride * D + sub * EPL, kx[c]);
+    for (int c = 0; c < CPL; ++c) load_child<T, EPL, LV != 0>(kbase + crow[c] * kstride * D + sub * EPL, kx[c]);
     const float *refs_h = refs();
     if (!active) return;
 
@@ -247,7 +270,8 @@ __device__ __forceinline__ void pool_node_refs(const TreeArgs &t, int lvl, int64
         if (j > 0) {
             if (upper) {
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + (crow[c] * R + j) * D + sub * EPL, kx[c]);
+                for (int c = 0; c < CPL; ++c)
+                    load_child<T, EPL, LV != 0>(kbase + (crow[c] * R + j) * D + sub * EPL, kx[c]);
             }
             store_key_row<T, D>(t, lvl, row0 + j - 1, part, col, lane);
         }
@@ -285,12 +309,12 @@ __device__ __forceinline__ void pool_node_one_ref(const TreeArgs &t, int lvl, in
     const T *kbase = (const T *)t.lk[lvl >= 2 ? lvl - 2 : 0];
     float kx[CPL][EPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(kbase + (crow[c] * R + j) * D + sub * EPL, kx[c]);
+    for (int c = 0; c < CPL; ++c) load_child<T, EPL, true>(kbase + (crow[c] * R + j) * D + sub * EPL, kx[c]);
     if (j == 0) {
         const T *vbase = (const T *)t.lv[lvl >= 2 ? lvl - 2 : 0];
         float vx[CPL][EPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) load_vec<T, EPL>(vbase + crow[c] * D + sub * EPL, vx[c]);
+        for (int c = 0; c < CPL; ++c) load_child<T, EPL, true>(vbase + crow[c] * D + sub * EPL, vx[c]);
         float vs[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vs[e] = 0.f;

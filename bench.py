@@ -515,21 +515,29 @@ PHASES = {1: "entry", 2: "length and query read", 3: "first gathers issued", 4: 
           5: "slice ranked (B2)", 6: "slice published", 7: "exchange read (B3)", 8: "exchange ranked (B4)",
           9: "kept set known", 10: "next gathers issued", 11: "level folded", 12: "tokens scored",
           13: "tokens folded", 14: "partial stored", 15: "arrival counted", 16: "output written (last arrival)",
-          17: "take-all levels resolved", 18: "first keys issued", 19: "append checked"}
+          17: "take-all levels resolved", 18: "first keys issued", 19: "append checked",
+          20: "length, epoch and status loaded", 21: "query loaded", 22: "new row stored"}
 
 
 def decode_timeline(args):
     """Phase timeline of the split decode step on the headline workload, from
     the timeline build of the library (libhti_timeline.so, the kernel with
     clock readings at each phase boundary): per phase, the median over
-    workgroups and steps of the time since the launch's first workgroup
-    started, in microseconds."""
+    workgroups and launches of the time since the launch's first workgroup
+    started, in microseconds.  The launches sampled are the last of a run of
+    back-to-back steps in one HIP graph, as the benchmark runs them; the
+    entry spread of launches made one at a time, each after a
+    synchronisation, is reported beside it."""
     import numpy as np
     hti.LIB_PATH = os.path.join(ROOT, "hierarchical_tree_indexed_amd", "libhti_timeline.so")
     hti.lib()
     w = W.DEC1M
-    nst = 40
-    Lcap = w.L + nst + 8
+    # (17 steps per graph, 32 replays: the sampled launches append at 32
+    # different positions modulo the chunk size, so that the share that
+    # completes a node is the workload's own, 1 in 32)
+    n_eager, n_graph, reps = 16, 17, 32
+    nst = n_eager + n_graph
+    Lcap = w.L + n_eager + n_graph * (reps + 1) + 8
     K, V = gen_kv_device(w, Lcap)
     q0 = W.gen_queries(w, 0, device=DEV)
     W.plant_needles(w, K, q0)
@@ -544,32 +552,58 @@ def decode_timeline(args):
     out = torch.empty((w.B, 1, w.Hq, w.d), dtype=torch.float32, device=DEV)
     ws = ts.decode_workspace(sel, 1)
     tl = ws[256: 256 + 8192 * 64 * 8].view(torch.int64).view(8192, 64)
-    samples = {}
-    ends = []
-    for s in range(nst):
+    mask48 = (1 << 48) - 1
+
+    def launch_events():
+        # the stamps of the most recent launch: [blocks, events], zero-padded
+        ev = tl.cpu().numpy()
+        return ev[(ev[:, 0] != 0)]
+
+    eager_spread = []
+    for s in range(n_eager):
         ts.decode_step(sel, ak[s], av[s], qs[s], out)
         torch.cuda.synchronize()
-        if s < 8:
-            continue
-        ev = tl.cpu().numpy()
-        used = ev[(ev[:, 0] != 0)]
-        t0 = (used[:, 0] & ((1 << 48) - 1)).min()
+        if s >= 4:
+            ent = launch_events()[:, 0] & mask48
+            eager_spread.append(float(np.percentile(ent - ent.min(), 90)) * 0.01)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            for s in range(n_eager, nst):
+                ts.decode_step(sel, ak[s], av[s], qs[s], out)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    samples = {}
+    ends = []
+    for _ in range(reps):
+        graph.replay()
+        torch.cuda.synchronize()
+        used = launch_events()
+        t0 = (used[:, 0] & mask48).min()
         for row in used:
             for e in row:
                 if e == 0:
                     break
-                ph, lv, tk = int(e >> 52), int((e >> 48) & 15), int(e & ((1 << 48) - 1))
+                ph, lv, tk = int(e >> 52), int((e >> 48) & 15), int(e & mask48)
                 samples.setdefault((ph, lv), []).append((tk - t0) * 0.01)      # 100 MHz ticks -> us
-        ends.append(((used & ((1 << 48) - 1)).max() - t0) * 0.01)
+        ends.append(((used & mask48).max() - t0) * 0.01)
+    del graph
     rows = []
     for (ph, lv), v in sorted(samples.items(), key=lambda kv: np.median(kv[1])):
         rows.append(dict(phase=PHASES.get(ph, str(ph)), level=lv, median_us=float(np.median(v)),
                          p10_us=float(np.percentile(v, 10)), p90_us=float(np.percentile(v, 90)), n=len(v)))
-    res = dict(workload=w.name, steps=nst - 8, kernel_span_us_median=float(np.median(ends)), phases=rows)
+    res = dict(workload=w.name, launches="last of %d back-to-back steps in a HIP graph, %d replays" % (n_graph, reps),
+               kernel_span_us_median=float(np.median(ends)),
+               eager_entry_spread_p90_us_median=float(np.median(eager_spread)), phases=rows)
     for r in rows:
         log(f"[timeline] {r['median_us']:7.2f} us (p10 {r['p10_us']:6.2f}, p90 {r['p90_us']:6.2f})  "
             f"level {r['level']}  {r['phase']}")
     log(f"[timeline] kernel span (first entry to last event) median {res['kernel_span_us_median']:.2f} us")
+    log(f"[timeline] entry spread (p90) of launches made one at a time after a synchronisation: "
+        f"median {res['eager_entry_spread_p90_us_median']:.2f} us")
     return res
 
 

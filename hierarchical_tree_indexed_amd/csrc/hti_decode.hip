@@ -283,14 +283,36 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     (void)tln;
     DTL(1, 0);
 
-    // ---- start: the length, the launch epoch, the workspace status and
-    // the query position go out together; the query into LDS ----
+    // ---- start: every load that does not depend on the length goes out
+    // first (the query, the decode step's new row of this unit's KV head,
+    // the RoPE angle steps; unconditional, so the compiler's wait counts
+    // stay exact), then the length, the launch epoch and the workspace
+    // status: one round trip for all of them ----
+    constexpr int EPC = 16 / (int)sizeof(T);           // elements per 16-byte chunk
+    static_assert(G * D / EPC <= DNT, "one chunk of the query per thread");
+    static_assert(D / EPC <= 64, "the new row in one wave");
+    const gptr<T> qsrc = to_global<T>(a.q) + orow * D;
+    const uint4 qx = gload<uint4>(qsrc + (tid < G * D / EPC ? tid : 0) * EPC);
+    // (without a new row, the query stands in as the source: read, not used)
+    const int nl = tid & (D / EPC - 1);
+    const uint4 knx = gload<uint4>((a.k_new ? to_global<T>(a.k_new) + bh * D : qsrc) + nl * EPC);
+    const uint4 vnx = gload<uint4>((a.k_new ? to_global<T>(a.v_new) + bh * D : qsrc) + nl * EPC);
+    const gptr<float2> rope = to_global<float2>(t.rope);
+    // angle step of each of this lane's RoPE frequencies (row 1 of the table)
+    float st_c[PPL], st_s[PPL];
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        const float2 c2 = gload<float2>(rope + (D / 2) + sub * PPL + e);
+        st_c[e] = c2.x;
+        st_s[e] = c2.y;
+    }
     if (tid == 0) {
         const int64_t len0 = t.len[bi];
         const uint32_t epoch = ws.epoch[unit];
         const uint32_t st0 = __hip_atomic_load(ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm.tag = (epoch % 0xffffeu) + 1u;
         sm.st0 = st0;
+        DTL(20, 0);
         int n = (int)len0;
         // decode step: this workgroup appends the new token itself (every
         // workgroup of every query of the sequence writes the same bytes) and
@@ -329,41 +351,19 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             }
         }
     }
-    const gptr<float2> rope = to_global<float2>(t.rope);
-    // decode step: the new row of this unit's KV head does not depend on the
-    // length, so its loads go out with the query's (stored after the length
-    // is known, below)
-    constexpr int EPCN = 16 / (int)sizeof(T);
-    uint4 knx = make_uint4(0u, 0u, 0u, 0u), vnx = knx;
-    if (a.k_new != nullptr && tid < D / EPCN) {
-        knx = gload<uint4>(to_global<T>(a.k_new) + bh * D + tid * EPCN);
-        vnx = gload<uint4>(to_global<T>(a.v_new) + bh * D + tid * EPCN);
-    }
-    {
-        const gptr<T> qp = to_global<T>(a.q) + orow * D;
-        constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
-        static_assert(G * D / EPC <= DNT, "one chunk of the query per thread");
-        if (tid < G * D / EPC) {
-            const uint4 x = gload<uint4>(qp + tid * EPC);
-            float *qd = sm.qraw + tid * EPC;
-            if constexpr (sizeof(T) == 2) {
-                cvt(make_uint2(x.x, x.y), qd);
-                cvt(make_uint2(x.z, x.w), qd + 4);
-            } else {
-                qd[0] = __uint_as_float(x.x);
-                qd[1] = __uint_as_float(x.y);
-                qd[2] = __uint_as_float(x.z);
-                qd[3] = __uint_as_float(x.w);
-            }
+    // the query into LDS
+    if (tid < G * D / EPC) {
+        float *qd = sm.qraw + tid * EPC;
+        if constexpr (sizeof(T) == 2) {
+            cvt(make_uint2(qx.x, qx.y), qd);
+            cvt(make_uint2(qx.z, qx.w), qd + 4);
+        } else {
+            qd[0] = __uint_as_float(qx.x);
+            qd[1] = __uint_as_float(qx.y);
+            qd[2] = __uint_as_float(qx.z);
+            qd[3] = __uint_as_float(qx.w);
         }
-    }
-    // angle step of each of this lane's RoPE frequencies (row 1 of the table)
-    float st_c[PPL], st_s[PPL];
-#pragma unroll
-    for (int e = 0; e < PPL; ++e) {
-        const float2 c2 = gload<float2>(rope + (D / 2) + sub * PPL + e);
-        st_c[e] = c2.x;
-        st_s[e] = c2.y;
+        DTL(21, 0);
     }
     float M[G], lt[G], acc[G][EPL];
 #pragma unroll
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
     __syncthreads();
     DTL(2, 0);
     const uint32_t tag = sm.tag;
-    if (sm.st0 != 0u) {
+    if (__builtin_expect(sm.st0 != 0u, 0)) {
         // an earlier launch with this workspace ran out of a wait: NaN, no
         // other effect, until the workspace is zeroed
         const int cols = (D + W - 1) / W;
@@ -392,17 +392,18 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         const int64_t Lold = sm.lold;
         T *kw = (T *)t.kc + (bh * t.ncap[0] + Lold) * D;
         T *vw = (T *)t.vc + (bh * t.ncap[0] + Lold) * D;
-        if (tid < D / EPCN) {
-            *reinterpret_cast<uint4 *>(kw + tid * EPCN) = knx;
-            *reinterpret_cast<uint4 *>(vw + tid * EPCN) = vnx;
+        if (tid < D / EPC) {
+            *reinterpret_cast<uint4 *>(kw + tid * EPC) = knx;
+            *reinterpret_cast<uint4 *>(vw + tid * EPC) = vnx;
         }
+        DTL(22, 0);
         // (lengths are below 2^31 here: 32-bit index arithmetic, a mask and
         // a shift when a fan-in is a power of two)
         uint32_t idx = (uint32_t)Lold + 1u;
         // Only a token that completes a node needs the row in place before
         // anything else (its pooling reads it): otherwise the stores complete
         // in the background, long before the token level reads the row.
-        if (levels > 0 && completes(idx, b)) {
+        if (__builtin_expect(levels > 0 && completes(idx, b), 0)) {
             __syncthreads();
             for (int l = 1; l <= levels; ++l) {
                 const int f = l == 1 ? b : fan;       // children per node of level l

@@ -516,7 +516,9 @@ PHASES = {1: "entry", 2: "length and query read", 3: "first gathers issued", 4: 
           9: "kept set known", 10: "next gathers issued", 11: "level folded", 12: "tokens scored",
           13: "tokens folded", 14: "partial stored", 15: "arrival counted", 16: "output written (last arrival)",
           17: "take-all levels resolved", 18: "first keys issued", 19: "append checked",
-          20: "length, epoch and status loaded", 21: "query loaded", 22: "new row stored"}
+          20: "length, epoch and status loaded", 21: "query loaded", 22: "new row stored",
+          23: "running max updated", 24: "slice ranked (wave 0)", 25: "slice entries read (wave 0)",
+          26: "vector memory drained (wave 0)"}
 
 
 def decode_timeline(args):

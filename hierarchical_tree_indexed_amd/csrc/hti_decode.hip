@@ -92,7 +92,7 @@ struct DSmem {
     // selection entries of the two most recent levels (by parity): keys,
     // group scores, candidate indices and per-wave partial ranks; entries
     // [0, kSlice) are the scored slice, [kSlice, kSelN) the exchange
-    uint64_t key[2][kSelN];
+    uint64_t key[2][kSelN] __attribute__((aligned(16)));
     float esc[2][kSelN];
     int16_t eix[2][kSelN];
     uint8_t prt[2][DNW][kSelN];
@@ -106,7 +106,7 @@ struct DSmem {
     int wrix[DNW][kMaxSel];
     float wrsc[DNW][kMaxSel];
     uint8_t wflag[2][DNW][kSlice] __attribute__((aligned(4)));   // per wave: kept flags of its fold slice
-    uint64_t wkx[DNW][128];           // per wave: the exchange keys it read
+    uint64_t wkx[DNW][128] __attribute__((aligned(16)));   // per wave: the exchange keys it read
     float xm[kMaxW], xs[kMaxW];       // top-p: each slice's (max, exp-sum) of group scores
     int n[HTI_MAX_LEVELS + 1];        // nodes per level (n[0] = tokens)
     const void *lkp[HTI_MAX_LEVELS];  // this unit's level keys / values
@@ -601,6 +601,9 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         uint64_t *ek = sm.key[zb];
         float *es = sm.esc[zb];
         int16_t *ei = sm.eix[zb];
+        // slots [ms, 64) hold zero keys, which beat nothing (rank_le64 reads
+        // whole 16-key batches)
+        if (tid >= ms && tid < 64) ek[tid] = 0ull;
         // the running best over a candidate's reference keys carries across
         // batches (a batch may end inside a candidate)
         int ci = c_beg, j = 0;
@@ -736,6 +739,37 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 c[1] += (int)(in && kj[u] > E.k[1]);
             }
         }
+    };
+    // Rank of one entry per lane among n <= 64 selection keys kk[0 .. n) in
+    // LDS (how many of them beat it), the slots [n, 64) holding zero keys,
+    // which beat nothing.  Keys are read two per 16-byte LDS access, a batch
+    // of 16 per round trip, with no bounds to test.  With n <= 32 the entry
+    // is lane & 31 and each half of the wave counts 16 of the slots (lanes
+    // 0-31 slots 0-15, lanes 32-63 slots 16-31), the halves summed by one
+    // lane swap; otherwise the entry is `lane` and every lane counts the
+    // first ceil(n / 16) batches.  Lanes past the n entries get a rank of no
+    // meaning.
+    auto rank_le64 = [&](const uint64_t *kk, int n) __attribute__((always_inline)) -> int {
+        n = __builtin_amdgcn_readfirstlane(n);
+        const bool split = n <= 32;
+        const int e = split ? (lane & 31) : lane;
+        const uint64_t ke = kk[max(0, min(e, n - 1))];
+        const int j0 = split ? ((lane & 32) >> 1) : 0;
+        const int nb = split ? 1 : (n + 15) >> 4;
+        int c = 0;
+        for (int bt = 0; bt < nb; ++bt) {
+            const ulonglong2 *kp = reinterpret_cast<const ulonglong2 *>(kk + j0 + 16 * bt);
+            ulonglong2 kj[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kj[u] = kp[u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c += (int)(kj[u].x > ke) + (int)(kj[u].y > ke);
+        }
+        if (split) {
+            const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)c, (uint32_t)c, false, false);
+            c = (int)(r[0] + r[1]);
+        }
+        return c;
     };
     // Kept set from the ranks of the n entries held in registers: the first
     // nav by rank (top-p: the shortest prefix reaching mass p), put in
@@ -954,6 +988,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             __syncthreads();                                           // B1: slice entries, logits
             DTL(4, lvl);
             if (!a.leaf_only) new_max(zb);
+            DTL(23, lvl);
             const int ne = W * keff;                                   // exchanged entries
             if (st.local) {
                 fold_pending();
@@ -961,16 +996,23 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 // against its share of the keys), selected locally
                 Ents E;
                 ents_from_slice(zb, ms, E);
-                int c[2];
-                count_range(sm.key[zb], E, ms * wave / DNW, ms * (wave + 1) / DNW, c);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    if (lane + 64 * t < ms) sm.prt[zb][wave][lane + 64 * t] = (uint8_t)c[t];
-                __syncthreads();                                       // B2
-                DTL(5, lvl);
                 int rk[2];
+                if (ms <= 64) {
+                    // (every wave ranks all of them itself: no barrier)
+                    rk[0] = rank_le64(sm.key[zb], ms);
+                    rk[1] = 1 << 20;
+                    DTL(5, lvl);
+                } else {
+                    int c[2];
+                    count_range(sm.key[zb], E, ms * wave / DNW, ms * (wave + 1) / DNW, c);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) rk[t] = lane + 64 * t < ms ? rank_of(zb, lane + 64 * t) : 1 << 20;
+                    for (int t = 0; t < 2; ++t)
+                        if (lane + 64 * t < ms) sm.prt[zb][wave][lane + 64 * t] = (uint8_t)c[t];
+                    __syncthreads();                                   // B2
+                    DTL(5, lvl);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) rk[t] = lane + 64 * t < ms ? rank_of(zb, lane + 64 * t) : 1 << 20;
+                }
                 float gmax = -INFINITY, den = 0.f;
                 if (topp) {
                     gmax = wave_max(fmaxf(E.sc[0], E.sc[1]));
@@ -985,8 +1027,19 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     // words at slot = rank
                     Ents S;
                     ents_from_slice(zb, ms, S);
+                    DTL(25, lvl);
+#ifdef HTI_DECODE_TIMELINE
+                    __builtin_amdgcn_s_waitcnt(0x0f70);   // (vector memory drained: measurement only)
+                    DTL(26, lvl);
+#endif
                     int c[2];
-                    count_range(sm.key[zb], S, 0, ms, c);
+                    if (ms <= 64) {
+                        c[0] = rank_le64(sm.key[zb], ms);
+                        c[1] = 1 << 20;
+                    } else {
+                        count_range(sm.key[zb], S, 0, ms, c);
+                    }
+                    DTL(24, lvl);
                     uint64_t *mine = lw_words + (int64_t)wg * kSlots;
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
@@ -1058,21 +1111,31 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     den = wave_sum(xm > -INFINITY ? xs * __expf(xm - gmax) : 0.f);
                 }
                 DTL(7, lvl);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    if (lane + 64 * t < ne) sm.wkx[wave][lane + 64 * t] = X.k[t];
-                wave_sync();
-                int c[2];
-                count_range(sm.wkx[wave], X, ne * wave / DNW, ne * (wave + 1) / DNW, c);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    if (lane + 64 * t < ne) sm.prt[zb][wave][kSlice + lane + 64 * t] = (uint8_t)c[t];
-                __syncthreads();                                       // B2
-                DTL(8, lvl);
                 int rk[2];
+                if (ne <= 64) {
+                    // (X.k is zero past the entries: the slots [ne, 64) are
+                    // zero keys; every wave ranks all of them itself)
+                    sm.wkx[wave][lane] = X.k[0];
+                    wave_sync();
+                    rk[0] = rank_le64(sm.wkx[wave], ne);
+                    rk[1] = 1 << 20;
+                    DTL(8, lvl);
+                } else {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    rk[t] = lane + 64 * t < ne ? rank_of(zb, kSlice + lane + 64 * t) : 1 << 20;
+                    for (int t = 0; t < 2; ++t)
+                        if (lane + 64 * t < ne) sm.wkx[wave][lane + 64 * t] = X.k[t];
+                    wave_sync();
+                    int c[2];
+                    count_range(sm.wkx[wave], X, ne * wave / DNW, ne * (wave + 1) / DNW, c);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        if (lane + 64 * t < ne) sm.prt[zb][wave][kSlice + lane + 64 * t] = (uint8_t)c[t];
+                    __syncthreads();                                   // B2
+                    DTL(8, lvl);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        rk[t] = lane + 64 * t < ne ? rank_of(zb, kSlice + lane + 64 * t) : 1 << 20;
+                }
                 nkeep = finalize_regs(X, rk, ne, st.m, st.cs, nxt, gmax, den, st.fs0, st.fms);
             } else {
                 uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;

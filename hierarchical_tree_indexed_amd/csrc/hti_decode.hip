@@ -61,7 +61,7 @@ constexpr int kSlots = kMaxSel + 2;   // words per (level, workgroup): k entries
 constexpr int kMaxEnt = kMaxW * kMaxSel;   // entries of one exchange
 constexpr int kSelN = kSlice + kMaxEnt;    // selection entries of one level: slice, then exchange
 constexpr int KB = 4;                 // key rows per quarter per batch
-constexpr int VB = 2;                 // value rows per quarter held in registers (more are loaded at the fold)
+constexpr int VB = 3;                 // value rows per quarter held in registers (more are loaded at the fold)
 constexpr long kSpin = 1L << 22;      // polls of one word before a wait gives up
 
 
@@ -771,10 +771,10 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
         }
         return c;
     };
-    // Kept set from the ranks of the n entries held in registers: the first
-    // nav by rank (top-p: the shortest prefix reaching mass p), put in
-    // candidate order by walking the kept lanes, into this wave's lists of
-    // parity nxt.  Returns the kept count.
+    // Kept set from the ranks of the n entries held in registers, which run
+    // in increasing candidate order over (t, lane): the first nav by rank
+    // (top-p: the shortest prefix reaching mass p), in candidate order, into
+    // this wave's lists of parity nxt.  Returns the kept count.
     auto finalize_regs = [&](const Ents &E, const int (&rank)[2], int n, int m, const Cands &cs, int nxt,
                              float gmax, float den, int fs0, int fms) __attribute__((always_inline)) -> int {
         const int nav = min(keff, m);
@@ -800,20 +800,15 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
             nkeep = max(1, min(__builtin_amdgcn_readfirstlane(ns), a.cap));
         }
         bool kept[2];
-        int pos[2] = {0, 0};
 #pragma unroll
         for (int t = 0; t < 2; ++t) kept[t] = lane + 64 * t < n && rank[t] < nkeep;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-            uint64_t mm = __ballot(kept[t2]);
-            while (mm) {
-                const int l = __builtin_ctzll(mm);
-                mm &= mm - 1;
-                const int ixj = __builtin_amdgcn_readlane(E.ix[t2], l);
-                pos[0] += (int)(ixj < E.ix[0]);
-                pos[1] += (int)(ixj < E.ix[1]);
-            }
-        }
+        // the entries run in candidate order over (t, lane): a kept entry's
+        // place is the number of kept entries before it
+        const uint64_t b0 = __ballot(kept[0]), b1 = __ballot(kept[1]);
+        int pos[2];
+        pos[0] = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u));
+        pos[1] = __builtin_popcountll(b0) +
+                 (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u));
         wave_sync();
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -1024,7 +1019,7 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                 uint64_t *lw_words = xw + (int64_t)(lvl - 1) * W * kSlots;
                 if (wave == 0) {
                     // this slice's ranks (wave 0 alone) and its best keff as
-                    // words at slot = rank
+                    // words
                     Ents S;
                     ents_from_slice(zb, ms, S);
                     DTL(25, lvl);
@@ -1041,11 +1036,22 @@ __global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
                     }
                     DTL(24, lvl);
                     uint64_t *mine = lw_words + (int64_t)wg * kSlots;
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        if (lane + 64 * t < ms && c[t] < keff)
-                            __hip_atomic_store(&mine[c[t]], pack_word(tag, (uint32_t)S.ix[t], S.sc[t]),
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    // the best keff go out in candidate order (slot = the
+                    // number of them before it in the slice), so that the
+                    // W lists read back run in candidate order too
+                    const bool pub0 = lane < ms && c[0] < keff, pub1 = lane + 64 < ms && c[1] < keff;
+                    const uint64_t q0 = __ballot(pub0), q1 = __ballot(pub1);
+                    const int slot0 =
+                        (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(q0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)q0, 0u));
+                    const int slot1 = __builtin_popcountll(q0) + (int)__builtin_amdgcn_mbcnt_hi(
+                                                                     (uint32_t)(q1 >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)q1, 0u));
+                    if (pub0)
+                        __hip_atomic_store(&mine[slot0], pack_word(tag, (uint32_t)S.ix[0], S.sc[0]), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    if (pub1)
+                        __hip_atomic_store(&mine[slot1], pack_word(tag, (uint32_t)S.ix[1], S.sc[1]), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                     if (lane >= ms && lane < keff)
                         __hip_atomic_store(&mine[lane], pack_word(tag, 0xfffu, -INFINITY), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);

@@ -471,12 +471,12 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     const int64_t units = units_ws;
     if (units >= (int64_t(1) << 31)) return fail(HTI_ERR_UNSUPPORTED, "too many (query, group) units");
     const hipStream_t hs = (hipStream_t)stream;
-    int W = 0;
+    int W = 0, occ = 1;
     if (ws || use_static) {
         // split each unit over W workgroups when all of them fit on the device
         // at once; otherwise one workgroup per unit
         const Bounds bd = bounds(&tree->cfg, sel, 0);
-        hipError_t e = decode_split_plan(a, units, bd.max_summary, &W);
+        hipError_t e = decode_split_plan(a, units, bd.max_summary, &W, &occ);
         if (e != hipSuccess) return launched(e, what);
     }
     if (use_static && W > 0) {
@@ -502,7 +502,7 @@ hti_status decode_impl(const char *what, const hti_tree *tree, const hti_select 
     }
     if (W > 0) {
         const DecodeWs dw = decode_ws_layout(ws, tree->cfg.B, units, W, tree->cfg.levels, G, tree->cfg.d);
-        return launched(launch_decode_split(a, dw, units, hs), what);
+        return launched(launch_decode_split(a, dw, units, occ, hs), what);
     }
     return launched(launch_traverse(a, false, units, hs), what);
 }

@@ -214,8 +214,13 @@ __device__ __forceinline__ bool completes(uint32_t x, int f)
     return (f & (f - 1)) == 0 ? (x & (uint32_t)(f - 1)) == 0u : x % (uint32_t)f == 0u;
 }
 
-template <typename T, int D, int G, bool F8>
-__global__ __launch_bounds__(DNT) void k_decode_split(TravArgs a, DecodeWs ws)
+// OCC: the waves per SIMD the instance is built for.  OCC = 2 caps it at 256
+// registers per lane (at some spill cost), so that the plan can place two
+// workgroups per CU where one per CU leaves a unit short of workgroups.  At
+// 1M tokens, batch 16 ran W = 2 at 74 us per step and W = 4 at two per CU
+// 47 us.  The plan uses OCC = 1 wherever one workgroup per CU suffices.
+template <typename T, int D, int G, bool F8, int OCC>
+__global__ __launch_bounds__(DNT, OCC) void k_decode_split(TravArgs a, DecodeWs ws)
 {
     constexpr int PPL = D / 32;                        // rotate-half pairs per lane of a key row
     constexpr int EPL = D / 16;                        // elements per lane of a value row
@@ -1419,10 +1424,10 @@ DecInstInfo &dec_info_locked(int dev, const void *kern)
     return g_dec_info.back().second;
 }
 
-template <typename T, int D, int G, bool F8>
+template <typename T, int D, int G, bool F8, int OCC>
 hipError_t dec_prepare(int dev, DecInstInfo *out)
 {
-    auto kern = k_decode_split<T, D, G, F8>;
+    auto kern = k_decode_split<T, D, G, F8, OCC>;
     const size_t dyn = dec_dyn_bytes<G, D>();
     std::lock_guard<std::mutex> lk(g_dec_mu);
     DecInstInfo &info = dec_info_locked(dev, (const void *)kern);
@@ -1439,14 +1444,14 @@ hipError_t dec_prepare(int dev, DecInstInfo *out)
     return hipSuccess;
 }
 
-template <typename T, int D, int G, bool F8>
+template <typename T, int D, int G, bool F8, int OCC>
 hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     DecInstInfo info;
-    if ((e = dec_prepare<T, D, G, F8>(dev, &info)) != hipSuccess) return e;
+    if ((e = dec_prepare<T, D, G, F8, OCC>(dev, &info)) != hipSuccess) return e;
     TravArgs aa = a;
     DecodeWs ww = ws;
     void *args[] = {&aa, &ww};
@@ -1457,7 +1462,7 @@ hipError_t dec_launch_k(const TravArgs &a, const DecodeWs &ws, int64_t units, hi
     // word (a cooperative launch would guarantee residency but costs more
     // than the whole kernel to dispatch).
     const unsigned heads = (unsigned)a.t.Hkv;
-    return hipLaunchKernel((const void *)k_decode_split<T, D, G, F8>,
+    return hipLaunchKernel((const void *)k_decode_split<T, D, G, F8, OCC>,
                            dim3((unsigned)ws.W, heads, (unsigned)(units / heads)), dim3(DNT), args,
                            dec_dyn_bytes<G, D>(), s);
 }
@@ -1507,16 +1512,19 @@ hipError_t dec_dispatch(const TravArgs &a, Fn &&fn)
 
 } // namespace
 
-hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s)
+hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, int occ, hipStream_t s)
 {
     if (units <= 0) return hipSuccess;
     return dec_dispatch(a, [&](auto tc, auto dc, auto gc, auto f8) {
         using TT = typename decltype(tc)::type;
-        return dec_launch_k<TT, decltype(dc)::value, decltype(gc)::value, decltype(f8)::value>(a, ws, units, s);
+        constexpr int DD = decltype(dc)::value, GG = decltype(gc)::value;
+        constexpr bool FF = decltype(f8)::value;
+        return occ == 2 ? dec_launch_k<TT, DD, GG, FF, 2>(a, ws, units, s)
+                        : dec_launch_k<TT, DD, GG, FF, 1>(a, ws, units, s);
     });
 }
 
-hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W)
+hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W, int *occ)
 {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1531,13 +1539,17 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
         std::lock_guard<std::mutex> lk(g_dec_mu);
         g_dev_cus.push_back({dev, cus});
     }
-    // occupancy of the instance that will be launched
-    int per_cu = 0;
+    // occupancy of the two instances (one and two waves per SIMD)
+    int per1 = 0, per2 = 0;
     e = dec_dispatch(a, [&](auto tc, auto dc, auto gc, auto f8) {
         using TT = typename decltype(tc)::type;
-        DecInstInfo info;
-        hipError_t r = dec_prepare<TT, decltype(dc)::value, decltype(gc)::value, decltype(f8)::value>(dev, &info);
-        per_cu = info.per_cu;
+        constexpr int DD = decltype(dc)::value, GG = decltype(gc)::value;
+        constexpr bool FF = decltype(f8)::value;
+        DecInstInfo i1, i2;
+        hipError_t r = dec_prepare<TT, DD, GG, FF, 1>(dev, &i1);
+        if (r == hipSuccess) r = dec_prepare<TT, DD, GG, FF, 2>(dev, &i2);
+        per1 = i1.per_cu;
+        per2 = i2.per_cu;
         return r;
     });
     if (e != hipSuccess) return e;
@@ -1546,6 +1558,13 @@ hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summa
     // short of its slices or of eight workgroups
     const int64_t need = (max_summary + kSlice - 1) / kSlice;
     const int64_t want = std::max<int64_t>(need, 8);
+    // the uncapped instance where one workgroup per CU gives every unit its
+    // wanted width (or the capped one holds no more per CU); else the capped
+    // one, with as many per CU as it holds
+    const bool one_fits = (int64_t)cus / (units > 0 ? units : 1) >= want;
+    const int o = (one_fits || per2 <= per1) ? 1 : 2;
+    const int per_cu = o == 2 ? per2 : per1;
+    *occ = o;
     int64_t w = 0;
     for (int per = 1; per <= std::min(per_cu, 4); ++per) {
         w = (int64_t)cus * per / (units > 0 ? units : 1);

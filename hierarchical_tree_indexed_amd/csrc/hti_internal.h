@@ -85,10 +85,11 @@ struct DecodeWs {
     uint32_t *seqcnt;   // [B]: workgroups of a decode step that have read the sequence length
 };
 // W > 0: split each unit over W workgroups; W == 0: one workgroup per unit.
-hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W);
+hipError_t decode_split_plan(const TravArgs &a, int64_t units, int64_t max_summary, int *W, int *occ);
 size_t decode_ws_bytes(int B, int64_t units, int W, int levels, int G, int D);
 DecodeWs decode_ws_layout(void *base, int B, int64_t units, int W, int levels, int G, int D);
-hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, hipStream_t s);
+// occ: waves per SIMD of the instance launched (1 or 2), as the plan chose it
+hipError_t launch_decode_split(const TravArgs &a, const DecodeWs &ws, int64_t units, int occ, hipStream_t s);
 // Static workspace of the split decode for callers that cannot allocate
 // (hti_sparse_decode_static): its size, its device address on the current
 // device, and a fill kernel that zeroes part of it.

@@ -796,6 +796,10 @@ def test_prefill_T1_equals_decode():
 STEP_CASES = [
     # steps 3..4 complete a level-1 and a level-2 node (b = 32)
     W.DEC128K.replace(name="step_b32", B=2, L=32 * 32 * 3 - 3, levels=2, needles=0),
+    # batch 8 (64 units): one workgroup per CU would leave each unit four, so
+    # the plan launches the two-waves-per-SIMD instance, two per CU; step 3
+    # completes a level-1 and a level-2 node
+    W.DEC128K.replace(name="step_b32_two_per_cu", B=8, L=32 * 32 * 2 - 3, levels=2, needles=0),
     # b = 16, top-p with four reference keys: a level-3 node completes
     W.ZHA2M.replace(name="step_topp_r4_b16", L=16 ** 3 * 2 - 4, levels=3),
     # G = 8, d = 64, b = 8, two queries per sequence
